@@ -1,0 +1,236 @@
+/*
+ * oscar.h — C ABI of liboscar: the OSCAR INT2 KV-cache write and the
+ * mixed-precision paged decode attention over that cache, for AMD gfx950.
+ *
+ * Method: "OSCAR: Offline Spectral Covariance-Aware Rotation for 2-bit KV
+ * Cache Quantization" (arXiv:2605.17757). Passages are cited by page and
+ * section:
+ *   [abs]   the arXiv v2 abstract (paperdot.bitmofang.com listing);
+ *   [nl]    gist.science/nl technical summary ("Technische Samenvatting");
+ *   [fr]    gist.science/fr technical summary ("Résumé technique").
+ *
+ * Every pointer argument is a plain pointer; "device" means memory the HIP
+ * runtime can address on the current device, "host" means CPU memory.
+ * The caller owns every buffer.  The library allocates device memory only in
+ * oscar_calibrate_rotation (freed before it returns) and keeps no state
+ * besides a thread-local error string.  All calls except
+ * oscar_calibrate_rotation are asynchronous on the given stream.
+ *
+ * Return value: OSCAR_OK (0) or a negative code; oscar_last_error() then
+ * holds a message.  Arguments are validated on the host before any launch;
+ * a call that fails validation launches nothing.  No call aborts and no C++
+ * exception crosses this boundary.
+ */
+#ifndef OSCAR_H_
+#define OSCAR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* hipStream_t without the HIP headers: an opaque stream handle (NULL = the
+ * default stream). */
+typedef struct ihipStream_t *oscar_stream_t;
+
+/* ---------------------------------------------------------------------------
+ * Fixed shape of the cache.
+ *   head_dim 128, 16-token pages; the first 16 tokens ("sink") and the last
+ *   128 tokens ("recent") of every request stay BF16, the middle ("history")
+ *   is rotated, clipped and stored as INT2 ([nl] §2.2.B, [fr] §2.2.B; the
+ *   pages give no sizes, these are the values this library fixes).
+ * ------------------------------------------------------------------------- */
+#define OSCAR_HEAD_DIM 128
+#define OSCAR_PAGE 16
+#define OSCAR_N_SINK 16
+#define OSCAR_N_RECENT 128
+/* BF16 pages per request: entry 0 = sink page, entries 1..8 = ring pages. */
+#define OSCAR_BF16_PAGES_PER_REQ 9
+
+enum {
+  OSCAR_OK = 0,
+  OSCAR_EINVAL = -1,       /* null pointer, negative or inconsistent size    */
+  OSCAR_EUNSUPPORTED = -2, /* group not in {32,64,128}, Hq % Hkv != 0, ...   */
+  OSCAR_EWORKSPACE = -3,   /* workspace smaller than the *_workspace_bytes() */
+  OSCAR_EHIP = -4,         /* HIP runtime or launch error (text appended)    */
+  OSCAR_ENODEV = -5        /* no usable gfx950 device                        */
+};
+
+/* Bits a kernel ORs into *status (oscar_layer_cache.status) when it meets
+ * data it must not follow; the offending work item is skipped. */
+#define OSCAR_STATUS_BAD_PAGE 1u   /* page id outside [0, n_pages)          */
+#define OSCAR_STATUS_BAD_LEN 2u    /* seq_len < 1 or > the host bound       */
+
+/* ---------------------------------------------------------------------------
+ * Position → storage (one request of current length L; positions 0..L-1).
+ *   p < 16                         sink:    bf16 page bf16_pt[b][0], row p
+ *   16 <= p < L-128   (L > 144)    history: h = p-16, INT2 page
+ *                                           hist_pt[b][h/16], row h%16
+ *   max(16, L-128) <= p < L        recent:  ring slot s = p % 128, bf16 page
+ *                                           bf16_pt[b][1 + s/16], row s%16
+ * Appending one token at position L moves position L-128 (when >= 16) from
+ * its ring slot into history; the new token takes that same slot.  History
+ * page j always holds positions 16+16j .. 16+16j+15, so a page depends only
+ * on its own tokens and may be shared between requests (prefix caching,
+ * [nl] §2.2.B, [abs]).  Page tables may repeat page ids.
+ *
+ * BF16 pool: uint16 (bf16 bits) [n_bf16_pages][Hkv][2][16][128]; index 0 of
+ * the "2" axis is K, 1 is V.  Rows hold raw, unrotated vectors.
+ *
+ * History pool: uint8 [n_hist_pages][Hkv][B_hist(G)], one block per
+ * (page, KV head):
+ *     [ K codes 512 B | K meta 64*NG B | V codes 512 B | V meta 64*NG B ]
+ *   NG = 128/G groups; B_hist(G) = 1024 + 128*NG  (1536, 1280, 1152 B for
+ *   G = 32, 64, 128).
+ *
+ * Meta: entry (group g, row t) at byte 4*(16*g + t) of the meta area:
+ *   fp16 scale s at +0, fp16 zero z at +2.  Dequantised value of a code c:
+ *   c*s + z, in the rotated basis.
+ *
+ * Codes: 2-bit values 0..3.  A code area is 128 dwords; dword w (byte 4w,
+ * little-endian) belongs to "lane" l = w/2, half d = w%2, with
+ * a = l%16, q = l/16.  Inside a dword, slot u (0..7) holds two codes, the
+ * first at bit LO[u] and the second at bit HI[u] (each 2 bits wide):
+ *     LO = { 8,  6, 12, 10,  4,  2, 16, 14 }
+ *     HI = {24, 22, 28, 26, 20, 18,  0, 30 }
+ *   K code area (token-major): a = row (token) t, q selects channels;
+ *     slot u of half d holds channels  c0 = 32*(2d + u/4) + 8q + 2*(u%4)
+ *     (first) and c0+1 (second), both of token t.
+ *   V code area (channel-major): a = channel offset m inside a block of 16,
+ *     q selects a quad of rows; slot u of half d holds channel
+ *     c = 16*(4d + u/2) + m for rows t0 = 4q + 2*(u%2) (first) and t0+1
+ *     (second).
+ * This order lets the decode expand a dword into eight fp16 pairs with one
+ * AND-OR each (after at most one shift), in exactly the register order the
+ * gfx950 matrix-core instructions read: K in 16x16x32 (tokens x channels)
+ * tiles, V in 16x16x16 (channels x tokens) tiles.
+ * ------------------------------------------------------------------------- */
+
+typedef struct oscar_layer_cache {
+  int32_t n_kv_heads;      /* Hkv >= 1                                       */
+  int32_t group;           /* G: 32, 64 or 128 channels per (scale, zero)    */
+  uint8_t *hist;           /* device history pool, layout above              */
+  int64_t n_hist_pages;
+  uint16_t *bf16;          /* device BF16 pool, layout above                 */
+  int64_t n_bf16_pages;
+  const int32_t *hist_pt;  /* device int32 [batch][hist_pt_stride]          */
+  int32_t hist_pt_stride;  /* >= history pages of the longest request       */
+  const int32_t *bf16_pt;  /* device int32 [batch][9]                        */
+  uint32_t *status;        /* device, may be NULL: OSCAR_STATUS_* bits       */
+} oscar_layer_cache;
+
+/* Device forms of one fixed per-layer rotation R = U*H*P ([nl] §2.2.A
+ * "Formule", [fr] §2.2.A.3; row-vector convention x_rot = x*R) and its clip
+ * threshold ([nl]/[fr] §2.2.A, [abs] "fixed per-layer rotations and clipping
+ * thresholds").  `forms` is written by oscar_prepare_rotation. */
+typedef struct oscar_rotation {
+  const void *forms;       /* device, oscar_rotation_bytes() bytes           */
+  float clip;              /* > 0 and finite; values clamp to [-clip, clip]  */
+} oscar_rotation;
+
+const char *oscar_last_error(void);
+const char *oscar_version(void);
+
+/* Bytes of one history block for group size G (0 if G is unsupported). */
+size_t oscar_hist_block_bytes(int32_t group);
+
+/* Bytes of the device buffer that holds the forms of one rotation. */
+size_t oscar_rotation_bytes(void);
+
+/* Converts R (device fp64 [128][128], row-major, R[i][j]) into the device
+ * forms the kernels read (fp32 R and R^T, and R^T split into an fp16 high
+ * part plus a 2^11-scaled fp16 low part for the matrix cores).
+ * forms: device buffer of oscar_rotation_bytes(). */
+int oscar_prepare_rotation(const double *R, void *forms, oscar_stream_t stream);
+
+/* Offline calibration ([nl] §2.2.A, [fr] §2.2.A, [abs]):
+ *   C_Q = mean over tokens and query heads of the outer product q q^T;
+ *   C_S = mean over tokens and query heads of o o^T, o = S V the causal
+ *         softmax(q K^T / sqrt(128)) attention output of the calibration
+ *         sequence (query head h reads KV head h / (Hq/Hkv));
+ *   U_Q, U_S = eigenbases (eigenvalues descending, each column's
+ *         largest-magnitude entry positive);
+ *   R_K = U_Q H P_br, R_V = U_S H P_br (H = normalised 128-point Sylvester
+ *         Hadamard, P_br = 7-bit bit-reversal permutation);
+ *   clip_K / clip_V = the clip_quantile quantile (linear interpolation
+ *         between order statistics) of |k R_K| / |v R_V| over every
+ *         calibration token, KV head and channel.
+ * q_cal: device bf16 [n_tokens][Hq][128]; k_cal, v_cal: device bf16
+ * [n_tokens][Hkv][128].  Outputs R_K, R_V (host fp64 [128][128]) and
+ * clip_K, clip_V (host).  Synchronises the stream; allocates and frees its
+ * own device scratch.  n_tokens in [1, 65536], clip_quantile in (0, 1]. */
+int oscar_calibrate_rotation(const uint16_t *q_cal, const uint16_t *k_cal,
+                             const uint16_t *v_cal, int64_t n_tokens,
+                             int32_t n_q_heads, int32_t n_kv_heads,
+                             double clip_quantile, double *R_K, double *R_V,
+                             float *clip_K, float *clip_V,
+                             oscar_stream_t stream);
+
+/* Fused KV write ([abs] "fused ... write ... kernels", [nl]/[fr] §2.2.B):
+ * appends new tokens to every request of the batch.  Request b gets
+ * n_b = cu_new[b+1]-cu_new[b] tokens at positions len_before[b] ..
+ * len_before[b]+n_b-1 from rows cu_new[b].. of k_new / v_new (device bf16
+ * [total_tokens][Hkv][128]).  Tokens that end up in the sink or recent
+ * window are stored raw (bf16); tokens that end up in history, including
+ * ring tokens pushed out by this call, are rotated by R (x*R), clamped to
+ * [-clip, clip], split into groups of G consecutive rotated channels, and
+ * stored as codes c = clamp(rint((x - z)/s), 0, 3) with z = fp16(min),
+ * s = fp16((max - min)/3) (all codes 0 when s == 0).
+ * cu_new: device int32 [batch+1]; len_before: device int32 [batch].
+ * max_new: host upper bound of n_b (sizes the grid).  History pages a call
+ * writes must not be shared with another live request (caller's duty). */
+int oscar_write_kv(const oscar_layer_cache *cache, const oscar_rotation *rot_k,
+                   const oscar_rotation *rot_v, const uint16_t *k_new,
+                   const uint16_t *v_new, const int32_t *cu_new,
+                   const int32_t *len_before, int32_t batch,
+                   int64_t total_tokens, int32_t max_new,
+                   oscar_stream_t stream);
+
+/* Workspace for oscar_decode_attn (device, any alignment >= 256 B). */
+size_t oscar_decode_workspace_bytes(int32_t batch, int32_t n_q_heads,
+                                    int32_t n_kv_heads, int32_t max_seq_len);
+
+/* Mixed-precision paged decode attention ([nl]/[fr] §2.2.B "kernel
+ * integration", [abs]): one query per request attends to all seq_lens[b]
+ * cached tokens: BF16 sink/recent tokens directly, INT2 history through
+ * dequantisation.  History keys stay in the rotated basis and are scored
+ * against q*R_K; the history part of the output is brought back with R_V^T
+ * once per (request, query head).  softmax scale sm_scale; query head h uses
+ * KV head h / (Hq/Hkv).
+ * q: device bf16 [batch][Hq][128]; seq_lens: device int32 [batch], each in
+ * [1, max_seq_len]; out: device fp32 [batch][Hq][128]. */
+int oscar_decode_attn(const oscar_layer_cache *cache,
+                      const oscar_rotation *rot_k, const oscar_rotation *rot_v,
+                      const uint16_t *q, int32_t n_q_heads,
+                      const int32_t *seq_lens, int32_t batch,
+                      int32_t max_seq_len, float sm_scale, float *out,
+                      void *workspace, size_t workspace_bytes,
+                      oscar_stream_t stream);
+
+/* Workspace for oscar_bf16_paged_decode. */
+size_t oscar_bf16_decode_workspace_bytes(int32_t batch, int32_t n_q_heads,
+                                         int32_t n_kv_heads,
+                                         int32_t max_seq_len);
+
+/* Plain BF16 paged decode attention (the BF16 baseline the pages compare
+ * against, [abs] "over BF16"): every token raw bf16, no rotation.
+ * kv_pages: device bf16 [n_pages][Hkv][2][16][128] (same page format as
+ * the BF16 pool); pt: device int32 [batch][pt_stride] — token p of request
+ * b is row p%16 of page pt[b][p/16]; other arguments as oscar_decode_attn.
+ * status: device uint32 or NULL (OSCAR_STATUS_* bits). */
+int oscar_bf16_paged_decode(const uint16_t *q, const uint16_t *kv_pages,
+                            int64_t n_pages, const int32_t *pt,
+                            int32_t pt_stride, const int32_t *seq_lens,
+                            int32_t batch, int32_t max_seq_len,
+                            int32_t n_q_heads, int32_t n_kv_heads,
+                            float sm_scale, float *out, uint32_t *status,
+                            void *workspace, size_t workspace_bytes,
+                            oscar_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSCAR_H_ */

@@ -1,0 +1,488 @@
+"""Plain fp64 CPU oracle of the OSCAR KV write and mixed-precision decode.
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's CPU
+baseline may import this module.  It shares no code with the GPU library and
+imports nothing from it; it is slow and written to be checked by eye.
+
+Sources (cited by page and section):
+  [abs] arXiv:2605.17757 v2 abstract ("OSCAR: Offline Spectral
+        Covariance-Aware Rotation for 2-bit KV Cache Quantization");
+  [nl]  gist.science/nl technical summary, sections 1-2;
+  [fr]  gist.science/fr technical summary, sections 1-2.
+
+Readings where the pages are silent or garbled (each is listed in the design
+notes of this repository):
+  * row vectors: x_rot = x R, inverse x_rot R^T;
+  * C_Q is the uncentred mean outer product q q^T, pooled over all query heads
+    of the layer (the pages print "q_n^T q_n", which as written is a scalar);
+  * S in C_S holds causal softmax probabilities (scale 1/sqrt(128)); query
+    head h reads KV head h // (Hq/Hkv); C_S is pooled over query heads;
+  * eigenvalues descending; each eigenvector's largest-|entry| positive
+    (lowest index on ties);
+  * H is the Sylvester Hadamard matrix divided by sqrt(128); P_br[i][j] = 1
+    iff i = bitrev7(j);
+  * one symmetric clip per layer and tensor: the 0.999 quantile (linear
+    interpolation, "type 7") of |x R| over calibration tokens, heads and
+    channels;
+  * clip first, then per-token groups of G consecutive rotated channels,
+    asymmetric min-max INT2 with fp16 scale and zero, codes from the stored
+    (fp16-rounded) scale and zero, round half to even, all codes 0 when the
+    fp16 scale is 0;
+  * sink = first 16 tokens, recent = last 128 tokens (exact sliding window),
+    both raw bf16 and unrotated; history in between;
+  * decode: one query per request over all cached tokens, no mask, fp64.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+D = 128
+PAGE = 16
+N_SINK = 16
+N_RECENT = 128
+BF16_PAGES_PER_REQ = 9
+
+
+# --------------------------------------------------------------------------
+# number formats
+# --------------------------------------------------------------------------
+
+def bf16_to_f64(u) -> np.ndarray:
+    """bf16 bit patterns (uint16) to float64, exactly."""
+    u = np.asarray(u, dtype=np.uint16)
+    return (u.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def f16_round(x) -> np.ndarray:
+    """Round float64 to the nearest fp16 (ties to even), returned as float16."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16)
+
+
+# --------------------------------------------------------------------------
+# the fixed factors of the rotation  ([nl] §2.2.A, [fr] §2.2.A.3)
+# --------------------------------------------------------------------------
+
+def hadamard(n: int = D) -> np.ndarray:
+    """Normalised Sylvester Hadamard matrix: H[i][j] = (-1)^popcount(i&j)/sqrt(n).
+
+    [nl]/[fr] §2.2.A: the Hadamard factor equalises the importance metric
+    over channels and spreads outlier energy.
+    """
+    i = np.arange(n)
+    parity = np.zeros((n, n), dtype=np.int64)
+    anded = i[:, None] & i[None, :]
+    for b in range(int(np.log2(n))):
+        parity ^= (anded >> b) & 1
+    return np.where(parity == 1, -1.0, 1.0) / np.sqrt(n)
+
+
+def bitrev(i: int, bits: int = 7) -> int:
+    """Reverse the low `bits` bits of i."""
+    r = 0
+    for _ in range(bits):
+        r = (r << 1) | (i & 1)
+        i >>= 1
+    return r
+
+
+def bitrev_permutation(n: int = D) -> np.ndarray:
+    """P_br with P[i][j] = 1 iff i = bitrev(j) ([nl]/[fr] §2.2.A: interleaves
+    high- and low-variance channels so every quantisation group sees a
+    balanced range)."""
+    bits = int(np.log2(n))
+    P = np.zeros((n, n))
+    for j in range(n):
+        P[bitrev(j, bits), j] = 1.0
+    return P
+
+
+# --------------------------------------------------------------------------
+# offline calibration  ([nl] §2.1-2.2.A, [fr] §2.1-2.2.A, [abs])
+# --------------------------------------------------------------------------
+
+def query_covariance(q: np.ndarray) -> np.ndarray:
+    """C_Q: mean over tokens and query heads of the outer product q q^T.
+
+    q: float64 [N][Hq][d].  Logit distortion is governed by the query second
+    moment ([nl]/[fr] §2.1; estimate in §2.2.A).
+    """
+    x = q.reshape(-1, q.shape[-1])
+    return x.T @ x / x.shape[0]
+
+
+def causal_attention_outputs(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                             sm_scale: float | None = None) -> np.ndarray:
+    """O = S V per query head, S the causal softmax(q K^T * sm_scale).
+
+    q: [N][Hq][d], k, v: [N][Hkv][d]; query head h reads KV head
+    h // (Hq/Hkv).  Returns [N][Hq][d].
+    """
+    n, hq, d = q.shape
+    hkv = k.shape[1]
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    out = np.empty_like(q)
+    future = np.triu(np.ones((n, n), dtype=bool), k=1)
+    for h in range(hq):
+        g = h // (hq // hkv)
+        logits = (q[:, h, :] @ k[:, g, :].T) * sm_scale
+        logits[future] = -np.inf
+        logits -= logits.max(axis=1, keepdims=True)
+        p = np.exp(logits)
+        p /= p.sum(axis=1, keepdims=True)
+        out[:, h, :] = p @ v[:, g, :]
+    return out
+
+
+def score_covariance(q, k, v, sm_scale=None) -> np.ndarray:
+    """C_S = (1/N) V^T S^T S V, pooled over query heads: the mean outer
+    product of the attention outputs S V ([nl]/[fr] §2.1 value target,
+    §2.2.A estimate)."""
+    o = causal_attention_outputs(q, k, v, sm_scale)
+    x = o.reshape(-1, o.shape[-1])
+    return x.T @ x / x.shape[0]
+
+
+def eigenbasis(C: np.ndarray) -> np.ndarray:
+    """Eigenbasis U of a symmetric C ([nl]/[fr] §2.2.A "rotation derivation"):
+    columns sorted by descending eigenvalue, each column's largest-magnitude
+    entry made positive (first index on ties)."""
+    w, U = np.linalg.eigh(C)
+    order = np.argsort(-w, kind="stable")
+    U = U[:, order].copy()
+    for j in range(U.shape[1]):
+        i = int(np.argmax(np.abs(U[:, j])))
+        if U[i, j] < 0:
+            U[:, j] = -U[:, j]
+    return U
+
+
+def compose_rotation(U: np.ndarray) -> np.ndarray:
+    """R = U H P_br ([nl] §2.2.A "Formule", [fr] §2.2.A.3)."""
+    n = U.shape[0]
+    return U @ hadamard(n) @ bitrev_permutation(n)
+
+
+def quantile_linear(values: np.ndarray, p: float) -> float:
+    """Quantile with linear interpolation between order statistics (type 7):
+    h = (n-1) p, result = x[floor h] + (h - floor h)(x[floor h + 1] - x[floor h])."""
+    return float(np.quantile(np.asarray(values, dtype=np.float64).ravel(), p, method="linear"))
+
+
+def clip_threshold(x: np.ndarray, R: np.ndarray, quantile: float = 0.999) -> float:
+    """Per-layer clip: quantile of |x R| over all tokens, heads and channels of
+    the calibration set ([nl]/[fr] §2.2.A "clipping thresholds")."""
+    xr = x.reshape(-1, x.shape[-1]) @ R
+    return quantile_linear(np.abs(xr), quantile)
+
+
+def calibrate(q, k, v, clip_quantile: float = 0.999) -> dict:
+    """Full offline calibration of one layer.  q, k, v float64 (bf16 values)."""
+    U_Q = eigenbasis(query_covariance(q))
+    U_S = eigenbasis(score_covariance(q, k, v))
+    R_K = compose_rotation(U_Q)
+    R_V = compose_rotation(U_S)
+    return {"R_K": R_K, "R_V": R_V,
+            "clip_K": clip_threshold(k, R_K, clip_quantile),
+            "clip_V": clip_threshold(v, R_V, clip_quantile)}
+
+
+# --------------------------------------------------------------------------
+# the INT2 quantiser  ([nl]/[fr] §1 four levels, §2.2.B rotate + clip + INT2)
+# --------------------------------------------------------------------------
+
+def quantize(x: np.ndarray, R: np.ndarray, clip: float, G: int) -> dict:
+    """Rotate, clip and quantise vectors.
+
+    x: float64 [n][128] (bf16 values).  Returns codes uint8 [n][128], scale
+    and zero float16 [n][128/G], the clipped rotated values xc [n][128] and
+    t = (xc - zero)/scale in code units (NaN where scale == 0).
+    """
+    n = x.shape[0]
+    ng = D // G
+    xc = np.clip(x @ R, -clip, clip)
+    g = xc.reshape(n, ng, G)
+    lo = g.min(axis=2)
+    hi = g.max(axis=2)
+    zero = f16_round(lo)
+    scale = f16_round((hi - lo) / 3.0)
+    codes, t = codes_from_meta(xc, scale, zero, G)
+    return {"codes": codes, "scale": scale, "zero": zero, "xc": xc, "t": t}
+
+
+def codes_from_meta(xc: np.ndarray, scale: np.ndarray, zero: np.ndarray, G: int):
+    """Codes of clipped rotated values for a given fp16 (scale, zero):
+    clamp(rint((xc - z)/s), 0, 3), 0 where s == 0."""
+    n = xc.shape[0]
+    ng = D // G
+    s = scale.astype(np.float64)[:, :, None]
+    z = zero.astype(np.float64)[:, :, None]
+    g = xc.reshape(n, ng, G)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.where(s > 0, (g - z) / np.where(s > 0, s, 1.0), np.nan)
+    c = np.where(s > 0, np.clip(np.rint(np.nan_to_num(t)), 0, 3), 0).astype(np.uint8)
+    return c.reshape(n, D), t.reshape(n, D)
+
+
+def dequantize(codes: np.ndarray, scale: np.ndarray, zero: np.ndarray, G: int) -> np.ndarray:
+    """Rotated-basis values c*s + z, float64 [n][128]."""
+    n = codes.shape[0]
+    ng = D // G
+    c = codes.reshape(n, ng, G).astype(np.float64)
+    return (c * scale.astype(np.float64)[:, :, None] + zero.astype(np.float64)[:, :, None]).reshape(n, D)
+
+
+# --------------------------------------------------------------------------
+# storage format of a history block (defined in include/oscar.h)
+# --------------------------------------------------------------------------
+
+LO_BIT = (8, 6, 12, 10, 4, 2, 16, 14)
+HI_BIT = (24, 22, 28, 26, 20, 18, 0, 30)
+
+
+def hist_block_bytes(G: int) -> int:
+    return 1024 + 128 * (D // G)
+
+
+def _code_bit_tables(kind: str):
+    """(byte index, shift) [16 rows][128 channels] of every code of a code area."""
+    byte_idx = np.full((PAGE, D), -1, dtype=np.int64)
+    shift = np.full((PAGE, D), -1, dtype=np.int64)
+    for lane in range(64):
+        a, q = lane % 16, lane // 16
+        for d in range(2):
+            word = 2 * lane + d
+            for u in range(8):
+                if kind == "K":
+                    t0, c0 = a, 32 * (2 * d + u // 4) + 8 * q + 2 * (u % 4)
+                    cells = ((t0, c0, LO_BIT[u]), (t0, c0 + 1, HI_BIT[u]))
+                else:
+                    c, t0 = 16 * (4 * d + u // 2) + a, 4 * q + 2 * (u % 2)
+                    cells = ((t0, c, LO_BIT[u]), (t0 + 1, c, HI_BIT[u]))
+                for t, c, bit in cells:
+                    assert byte_idx[t, c] < 0
+                    byte_idx[t, c] = 4 * word + bit // 8
+                    shift[t, c] = bit % 8
+    assert (byte_idx >= 0).all()
+    return byte_idx, shift
+
+
+_K_TABLES = _code_bit_tables("K")
+_V_TABLES = _code_bit_tables("V")
+
+
+def pack_codes(codes: np.ndarray, kind: str) -> np.ndarray:
+    """codes uint8 [..., 16, 128] (0..3) -> code areas uint8 [..., 512]."""
+    byte_idx, shift = _K_TABLES if kind == "K" else _V_TABLES
+    lead = codes.shape[:-2]
+    out = np.zeros(lead + (512,), dtype=np.uint8)
+    flat_out = out.reshape(-1, 512)
+    flat_c = codes.reshape(-1, PAGE, D).astype(np.uint8)
+    for t in range(PAGE):
+        for c in range(D):
+            flat_out[:, byte_idx[t, c]] |= ((flat_c[:, t, c] & 3) << np.uint8(shift[t, c])).astype(np.uint8)
+    return out
+
+
+def unpack_codes(area: np.ndarray, kind: str) -> np.ndarray:
+    """code areas uint8 [..., 512] -> codes uint8 [..., 16, 128]."""
+    byte_idx, shift = _K_TABLES if kind == "K" else _V_TABLES
+    return (area[..., byte_idx] >> shift.astype(np.uint8)) & 3
+
+
+def pack_meta(scale: np.ndarray, zero: np.ndarray) -> np.ndarray:
+    """scale, zero float16 [..., 16 rows, NG] -> meta areas uint8 [..., 64*NG]:
+    entry (g, t) at byte 4*(16 g + t), scale then zero."""
+    s = np.swapaxes(scale.astype(np.float16), -1, -2)  # [..., NG, 16]
+    z = np.swapaxes(zero.astype(np.float16), -1, -2)
+    pair = np.stack([s, z], axis=-1)                  # [..., NG, 16, 2]
+    return pair.view(np.uint8).reshape(scale.shape[:-2] + (-1,))
+
+
+def unpack_meta(area: np.ndarray, G: int):
+    """meta areas uint8 [..., 64*NG] -> (scale, zero) float16 [..., 16, NG]."""
+    ng = D // G
+    pair = np.ascontiguousarray(area).view(np.float16).reshape(area.shape[:-1] + (ng, PAGE, 2))
+    return np.swapaxes(pair[..., 0], -1, -2), np.swapaxes(pair[..., 1], -1, -2)
+
+
+def split_block(block: np.ndarray, G: int) -> dict:
+    """Views of the four areas of history blocks uint8 [..., B_hist(G)]."""
+    m = 64 * (D // G)
+    return {"k_codes": block[..., 0:512], "k_meta": block[..., 512:512 + m],
+            "v_codes": block[..., 512 + m:1024 + m], "v_meta": block[..., 1024 + m:1024 + 2 * m]}
+
+
+# --------------------------------------------------------------------------
+# the mixed-precision paged cache  ([nl]/[fr] §2.2.B)
+# --------------------------------------------------------------------------
+
+def storage_of(p: int, L: int):
+    """Where position p of a request of length L lives: ('sink', row),
+    ('hist', history index h = p - 16) or ('ring', slot)."""
+    if p < N_SINK:
+        return ("sink", p)
+    if p < L - N_RECENT:
+        return ("hist", p - N_SINK)
+    return ("ring", p % N_RECENT)
+
+
+class LayerCacheRef:
+    """One layer's cache as numpy pools with page tables (formats of oscar.h)."""
+
+    def __init__(self, n_kv_heads: int, G: int, n_hist_pages: int, n_bf16_pages: int,
+                 hist_pt: np.ndarray, bf16_pt: np.ndarray):
+        self.hkv, self.G = n_kv_heads, G
+        self.hist = np.zeros((n_hist_pages, n_kv_heads, hist_block_bytes(G)), dtype=np.uint8)
+        self.bf16 = np.zeros((n_bf16_pages, n_kv_heads, 2, PAGE, D), dtype=np.uint16)
+        self.hist_pt = np.asarray(hist_pt, dtype=np.int32)
+        self.bf16_pt = np.asarray(bf16_pt, dtype=np.int32)
+
+    # ---- raw bf16 rows
+    def _bf16_row(self, b: int, where: str, idx: int):
+        if where == "sink":
+            return self.bf16_pt[b, 0], idx
+        return self.bf16_pt[b, 1 + idx // PAGE], idx % PAGE
+
+    def write(self, rot_k: np.ndarray, rot_v: np.ndarray, clip_k: float, clip_v: float,
+              k_new: np.ndarray, v_new: np.ndarray, cu_new, len_before) -> None:
+        """Append tokens (the write of [abs] and [nl]/[fr] §2.2.B).
+
+        k_new, v_new: bf16 bits [T][Hkv][128].  Request b receives rows
+        cu_new[b]..cu_new[b+1]-1 at positions len_before[b]... .  Ring tokens
+        that leave the recent window are quantised into history.
+        """
+        G = self.G
+        for b in range(len(len_before)):
+            L0 = int(len_before[b])
+            n = int(cu_new[b + 1]) - int(cu_new[b])
+            L = L0 + n
+            # tokens whose storage may change: the old ring tokens (positions
+            # max(16, L0-128) .. L0-1) and all new tokens.  Old ring rows are
+            # read before anything is written.
+            src = {}
+            for p in range(max(N_SINK, L0 - N_RECENT), L0):
+                w, idx = storage_of(p, L0)
+                assert w == "ring"
+                pg, row = self._bf16_row(b, "ring", idx)
+                src[p] = (self.bf16[pg, :, 0, row, :].copy(), self.bf16[pg, :, 1, row, :].copy())
+            for i in range(n):
+                r = int(cu_new[b]) + i
+                src[L0 + i] = (k_new[r].copy(), v_new[r].copy())
+            hist_pos = []
+            for p in sorted(src):
+                w, idx = storage_of(p, L)
+                kx, vx = src[p]
+                if w == "hist":
+                    hist_pos.append((p, idx))
+                    continue
+                if p < L0 and w == "ring":
+                    continue  # stays where it is
+                pg, row = self._bf16_row(b, w, idx)
+                self.bf16[pg, :, 0, row, :] = kx
+                self.bf16[pg, :, 1, row, :] = vx
+            if not hist_pos:
+                continue
+            # quantise every history-bound token, then store page by page
+            xs_k = np.stack([bf16_to_f64(src[p][0]) for p, _ in hist_pos])  # [n][Hkv][128]
+            xs_v = np.stack([bf16_to_f64(src[p][1]) for p, _ in hist_pos])
+            for h in range(self.hkv):
+                qk = quantize(xs_k[:, h, :], rot_k, clip_k, G)
+                qv = quantize(xs_v[:, h, :], rot_v, clip_v, G)
+                by_page = {}
+                for j, (_, hidx) in enumerate(hist_pos):
+                    by_page.setdefault(hidx // PAGE, []).append((j, hidx % PAGE))
+                for page, rows in by_page.items():
+                    pid = int(self.hist_pt[b, page])
+                    areas = split_block(self.hist[pid, h], G)
+                    for kind, qq in (("k", qk), ("v", qv)):
+                        codes = unpack_codes(areas[kind + "_codes"], kind.upper())
+                        s, z = unpack_meta(areas[kind + "_meta"], G)
+                        s, z = s.copy(), z.copy()
+                        for j, row in rows:
+                            codes[row] = qq["codes"][j]
+                            s[row] = qq["scale"][j]
+                            z[row] = qq["zero"][j]
+                        areas[kind + "_codes"][:] = pack_codes(codes, kind.upper())
+                        areas[kind + "_meta"][:] = pack_meta(s, z)
+
+    # ---- reconstruction for the decode
+    def gather(self, b: int, L: int, rot_k: np.ndarray, rot_v: np.ndarray):
+        """K, V float64 [L][Hkv][128] of request b, history inverse-rotated
+        back to the original basis (dequantise, then x_rot R^T)."""
+        G = self.G
+        K = np.empty((L, self.hkv, D))
+        V = np.empty((L, self.hkv, D))
+        hist = []
+        for p in range(L):
+            w, idx = storage_of(p, L)
+            if w == "hist":
+                hist.append((p, idx))
+                continue
+            pg, row = self._bf16_row(b, w, idx)
+            K[p] = bf16_to_f64(self.bf16[pg, :, 0, row, :])
+            V[p] = bf16_to_f64(self.bf16[pg, :, 1, row, :])
+        if hist:
+            pages = sorted({idx // PAGE for _, idx in hist})
+            decoded = {}
+            for page in pages:
+                pid = int(self.hist_pt[b, page])
+                for h in range(self.hkv):
+                    areas = split_block(self.hist[pid, h], G)
+                    for kind, R in (("k", rot_k), ("v", rot_v)):
+                        c = unpack_codes(areas[kind + "_codes"], kind.upper())
+                        s, z = unpack_meta(areas[kind + "_meta"], G)
+                        decoded[(page, h, kind)] = dequantize(c, s, z, G) @ R.T
+            for p, idx in hist:
+                for h in range(self.hkv):
+                    K[p, h] = decoded[(idx // PAGE, h, "k")][idx % PAGE]
+                    V[p, h] = decoded[(idx // PAGE, h, "v")][idx % PAGE]
+        return K, V
+
+
+# --------------------------------------------------------------------------
+# attention
+# --------------------------------------------------------------------------
+
+def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float) -> np.ndarray:
+    """softmax(q K^T * sm_scale) V for one request, fp64.
+
+    q: [Hq][128]; K, V: [L][Hkv][128]; query head h reads KV head
+    h // (Hq/Hkv).  Returns [Hq][128].
+    """
+    hq, hkv = q.shape[0], K.shape[1]
+    out = np.empty((hq, q.shape[1]))
+    for h in range(hq):
+        g = h // (hq // hkv)
+        logits = (K[:, g, :] @ q[h]) * sm_scale
+        w = np.exp(logits - logits.max())
+        out[h] = (w / w.sum()) @ V[:, g, :]
+    return out
+
+
+def decode_attn(cache: LayerCacheRef, rot_k, rot_v, q_bits: np.ndarray, seq_lens,
+                sm_scale: float) -> np.ndarray:
+    """Decode attention over the mixed-precision cache ([nl]/[fr] §2.2.B):
+    every history token is dequantised and inverse-rotated, then plain
+    softmax attention over all seq_lens[b] tokens.  Returns [B][Hq][128]."""
+    q = bf16_to_f64(q_bits)
+    out = np.empty(q.shape)
+    for b in range(q.shape[0]):
+        K, V = cache.gather(b, int(seq_lens[b]), rot_k, rot_v)
+        out[b] = attention(q[b], K, V, sm_scale)
+    return out
+
+
+def bf16_paged_decode(q_bits, kv_pages, pt, seq_lens, sm_scale) -> np.ndarray:
+    """Plain BF16 paged decode: token p of request b is row p%16 of page
+    pt[b][p//16] (kv_pages bf16 bits [pages][Hkv][2][16][128])."""
+    q = bf16_to_f64(q_bits)
+    out = np.empty(q.shape)
+    for b in range(q.shape[0]):
+        L = int(seq_lens[b])
+        p = np.arange(L)
+        pages = np.asarray(pt[b])[p // PAGE]
+        K = bf16_to_f64(kv_pages[pages, :, 0, p % PAGE, :])
+        V = bf16_to_f64(kv_pages[pages, :, 1, p % PAGE, :])
+        out[b] = attention(q[b], K, V, sm_scale)
+    return out

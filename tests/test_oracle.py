@@ -1,0 +1,642 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: closed
+forms, invariants of the construction, hand-derived bytes of the documented
+storage format (tests/golden/), brute force in plain Python on tiny inputs, or
+special cases that reduce to a textbook routine.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import oscar_ref as o
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+RNG = np.random.default_rng(1234)
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------- Hadamard
+
+
+def fwht(x):
+    """Textbook fast Walsh-Hadamard butterfly (natural order), unnormalised."""
+    x = np.array(x, dtype=np.float64)
+    n = x.shape[-1]
+    h = 1
+    while h < n:
+        for i in range(0, n, 2 * h):
+            a = x[..., i:i + h].copy()
+            b = x[..., i + h:i + 2 * h].copy()
+            x[..., i:i + h] = a + b
+            x[..., i + h:i + 2 * h] = a - b
+        h *= 2
+    return x
+
+
+def test_hadamard_orthonormal_symmetric():
+    H = o.hadamard()
+    assert np.abs(H @ H.T - np.eye(128)).max() <= 1e-15
+    assert np.array_equal(H, H.T)
+    np.testing.assert_allclose(H[0], 2.0 ** -3.5, rtol=3e-16, atol=0)
+    np.testing.assert_allclose(np.abs(H), 2.0 ** -3.5, rtol=3e-16, atol=0)
+
+
+def test_hadamard_equals_butterfly():
+    x = RNG.standard_normal((5, 128))
+    np.testing.assert_allclose(x @ o.hadamard(), fwht(x) / math.sqrt(128), rtol=0, atol=1e-13)
+
+
+# ------------------------------------------------------------- bit reversal
+
+
+def test_bitrev_table():
+    table = {0: 0, 1: 64, 2: 32, 3: 96, 5: 80, 6: 48, 127: 127, 64: 1}
+    for i, r in table.items():
+        assert o.bitrev(i) == r
+
+
+def test_bitrev_permutation_identities():
+    P = o.bitrev_permutation()
+    H = o.hadamard()
+    assert np.array_equal(P @ P, np.eye(128))      # involution
+    assert np.array_equal(P, P.T)
+    assert P.sum(axis=0).tolist() == [1.0] * 128 and P.sum(axis=1).tolist() == [1.0] * 128
+    assert np.abs(P @ H @ P - H).max() == 0.0
+    assert np.abs(H @ P - P @ H).max() == 0.0
+    # x P moves channel j to position bitrev(j)?  (x P)[j] = sum_i x[i] P[i][j] = x[bitrev(j)]
+    x = np.arange(128.0)
+    assert np.array_equal(x @ P, np.array([o.bitrev(j) for j in range(128)], dtype=float))
+
+
+# -------------------------------------------------------------- calibration
+
+
+def test_query_covariance_closed_form():
+    # q rows are scaled basis vectors: C_Q is diagonal with alpha^2 / (N*Hq)
+    n, hq = 128, 2
+    q = np.zeros((n, hq, 128))
+    alpha = np.arange(1, 129, dtype=float)
+    for i in range(n):
+        q[i, 0, i] = alpha[i]
+    C = o.query_covariance(q)
+    np.testing.assert_allclose(np.diag(C), alpha ** 2 / (n * hq), rtol=1e-15)
+    assert np.abs(C - np.diag(np.diag(C))).max() == 0.0
+
+
+def test_query_covariance_converges_to_sigma():
+    lam = synth.layer_lambda(7, 0)
+    q = RNG.standard_normal((20000, 4, 128)) * np.sqrt(lam)
+    C = o.query_covariance(q)
+    # 80000 samples: relative error of each diagonal entry ~ sqrt(2/80000) = 0.5%
+    np.testing.assert_allclose(np.diag(C), lam, rtol=0.03)
+    assert np.abs(C - np.diag(np.diag(C))).max() < 0.05 * lam.max()
+
+
+def test_score_covariance_single_token():
+    # N = 1: the only probability is 1, so o = v and C_S = mean_h v_g v_g^T
+    hq, hkv = 4, 2
+    q = RNG.standard_normal((1, hq, 128))
+    k = RNG.standard_normal((1, hkv, 128))
+    v = RNG.standard_normal((1, hkv, 128))
+    expect = sum(np.outer(v[0, h // 2], v[0, h // 2]) for h in range(hq)) / hq
+    np.testing.assert_allclose(o.score_covariance(q, k, v), expect, rtol=1e-14, atol=1e-14)
+
+
+def test_causal_attention_two_tokens_by_hand():
+    d = 128
+    q = RNG.standard_normal((2, 1, d))
+    k = RNG.standard_normal((2, 1, d))
+    v = RNG.standard_normal((2, 1, d))
+    out = o.causal_attention_outputs(q, k, v)
+    # token 0 sees only itself; token 1 weighs keys 0 and 1
+    s0 = sum(q[1, 0, i] * k[0, 0, i] for i in range(d)) / math.sqrt(d)
+    s1 = sum(q[1, 0, i] * k[1, 0, i] for i in range(d)) / math.sqrt(d)
+    w0 = 1.0 / (1.0 + math.exp(s1 - s0))
+    np.testing.assert_allclose(out[0, 0], v[0, 0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(out[1, 0], w0 * v[0, 0] + (1 - w0) * v[1, 0], rtol=1e-13, atol=1e-13)
+
+
+def test_causal_attention_gqa_map():
+    n, hq, hkv = 6, 4, 2
+    q = RNG.standard_normal((n, hq, 128))
+    k = RNG.standard_normal((n, hkv, 128))
+    v = RNG.standard_normal((n, hkv, 128))
+    out = o.causal_attention_outputs(q, k, v)
+    for h in range(hq):
+        g = h // 2
+        single = o.causal_attention_outputs(q[:, h:h + 1], k[:, g:g + 1], v[:, g:g + 1])
+        np.testing.assert_allclose(out[:, h], single[:, 0], rtol=1e-14, atol=1e-14)
+
+
+def test_score_covariance_matches_literal_form():
+    # (S V)^T (S V) / N per head equals the page's V^T S^T S V / N with S the
+    # explicit causal probability matrix built in plain loops
+    n = 5
+    q = RNG.standard_normal((n, 1, 128))
+    k = RNG.standard_normal((n, 1, 128))
+    v = RNG.standard_normal((n, 1, 128))
+    S = np.zeros((n, n))
+    for i in range(n):
+        logits = [float(q[i, 0] @ k[j, 0]) / math.sqrt(128) for j in range(i + 1)]
+        m = max(logits)
+        w = [math.exp(x - m) for x in logits]
+        for j in range(i + 1):
+            S[i, j] = w[j] / sum(w)
+    V = v[:, 0, :]
+    np.testing.assert_allclose(o.score_covariance(q, k, v), V.T @ S.T @ S @ V / n, rtol=1e-12, atol=1e-13)
+
+
+def test_eigenbasis_diagonal_sorts_and_signs():
+    vals = RNG.permutation(np.arange(1.0, 129.0))
+    U = o.eigenbasis(np.diag(vals))
+    order = np.argsort(-vals)
+    expect = np.eye(128)[:, order]
+    assert np.array_equal(U, expect)
+
+
+def test_eigenbasis_sign_rule():
+    Q, _ = np.linalg.qr(RNG.standard_normal((128, 128)))
+    lam = np.linspace(10, 1, 128)
+    C = Q @ np.diag(lam) @ Q.T
+    U = o.eigenbasis(C)
+    for j in range(128):
+        col = Q[:, j] * np.sign(Q[np.argmax(np.abs(Q[:, j])), j])
+        np.testing.assert_allclose(U[:, j], col, atol=1e-10)
+        assert U[np.argmax(np.abs(U[:, j])), j] > 0
+
+
+@pytest.fixture(scope="module")
+def calibrated():
+    ld = synth.LayerData(11, 0, 8, 2)
+    qb, kb, vb = ld.calibration(512)
+    q, k, v = (o.bf16_to_f64(x) for x in (qb, kb, vb))
+    cal = o.calibrate(q, k, v)
+    return q, k, v, cal
+
+
+def test_rotation_orthogonal(calibrated):
+    _, _, _, cal = calibrated
+    for R in (cal["R_K"], cal["R_V"]):
+        assert np.abs(R.T @ R - np.eye(128)).max() <= 1e-12
+
+
+def test_rotation_diagonalises_then_mixes(calibrated):
+    # R^T C R = P H Lambda H P, independent of eigenvector signs
+    q, k, v, cal = calibrated
+    H, P = o.hadamard(), o.bitrev_permutation()
+    for C, R in ((o.query_covariance(q), cal["R_K"]), (o.score_covariance(q, k, v), cal["R_V"])):
+        lam = np.sort(np.linalg.eigvalsh(C))[::-1]
+        lhs = R.T @ C @ R
+        rhs = P @ H @ np.diag(lam) @ H @ P
+        assert np.abs(lhs - rhs).max() <= 1e-12 * np.abs(C).max() * 128
+
+
+def test_rotation_equalises_importance(calibrated):
+    # diag(R_K^T C_Q R_K) = tr(C_Q)/128 for every channel (the Hadamard factor
+    # equalises the importance metric, [nl]/[fr] section 2.2.A)
+    q, _, _, cal = calibrated
+    C = o.query_covariance(q)
+    d = np.diag(cal["R_K"].T @ C @ cal["R_K"])
+    np.testing.assert_allclose(d, np.trace(C) / 128, rtol=1e-12)
+
+
+def test_rotation_preserves_dot_products(calibrated):
+    q, k, _, cal = calibrated
+    R = cal["R_K"]
+    a, b = q[:50, 0], k[:50, 0]
+    np.testing.assert_allclose(np.sum((a @ R) * (b @ R), axis=1), np.sum(a * b, axis=1), rtol=1e-12, atol=1e-12)
+
+
+def test_clip_quantile_closed_form():
+    # |values| 1..1024, quantile 0.999: h = 1023*0.999 = 1021.977 -> 1022.977
+    x = -np.arange(1.0, 1025.0).reshape(8, 1, 128)
+    assert abs(o.clip_threshold(x, np.eye(128), 0.999) - (1.0 + 0.999 * 1023.0)) < 1e-9
+    assert o.clip_threshold(x, np.eye(128), 1.0) == 1024.0
+
+
+def test_clip_uses_rotated_values():
+    # with a rotation that maps e_0 to (1,1,..)/sqrt(128) the quantile sees the
+    # rotated magnitudes, not the raw ones
+    x = np.zeros((1, 1, 128))
+    x[0, 0, 0] = math.sqrt(128.0)
+    assert abs(o.clip_threshold(x, o.hadamard(), 0.5) - 1.0) < 1e-12
+
+
+# ---------------------------------------------------------------- quantiser
+
+
+def _group_input(vals, G=32):
+    x = np.zeros((1, 128))
+    x[0, :G] = vals
+    return x
+
+
+def test_quantizer_hand_cases():
+    I = np.eye(128)
+    # levels
+    q = o.quantize(_group_input(np.tile([0, 1, 2, 3], 8)), I, 1000.0, 32)
+    assert q["zero"][0, 0] == 0 and q["scale"][0, 0] == 1
+    assert q["codes"][0, :32].tolist() == [0, 1, 2, 3] * 8
+    # centred
+    q = o.quantize(_group_input(np.tile([-1.5, -0.5, 0.5, 1.5], 8)), I, 1000.0, 32)
+    assert q["zero"][0, 0] == -1.5 and q["scale"][0, 0] == 1
+    assert q["codes"][0, :32].tolist() == [0, 1, 2, 3] * 8
+    # constant group: scale 0, codes 0, dequantised value = zero
+    q = o.quantize(_group_input(np.full(32, 0.75)), I, 1000.0, 32)
+    assert q["scale"][0, 0] == 0 and q["zero"][0, 0] == 0.75
+    assert q["codes"][0, :32].tolist() == [0] * 32
+    assert np.all(o.dequantize(q["codes"], q["scale"], q["zero"], 32)[0, :32] == 0.75)
+    # clipped maximum
+    vals = np.array([50.0] + [float(i % 3) for i in range(31)])
+    q = o.quantize(_group_input(vals), I, 4.0, 32)
+    assert q["xc"][0, 0] == 4.0
+    assert q["zero"][0, 0] == 0.0 and float(q["scale"][0, 0]) == 1.3330078125
+    assert q["codes"][0, 0] == 3
+    # fp16 rounding of the zero
+    q = o.quantize(_group_input(np.array([0.1] + [0.5] * 31)), I, 1000.0, 32)
+    assert float(q["zero"][0, 0]) == 0.0999755859375
+    # ties round to even
+    q = o.quantize(_group_input(np.array([0.0, 3.0, 1.5, 2.5, 0.5] + [1.0] * 27)), I, 1000.0, 32)
+    assert q["codes"][0, 2:5].tolist() == [2, 2, 0]
+
+
+def test_quantizer_golden_file_consistent():
+    g = _golden("quantizer_cases.json")
+    names = [c["name"] for c in g["cases"]]
+    assert names == ["levels", "centered", "constant", "clipped", "fp16 zero", "tie to even"]
+
+
+def test_quantizer_invariants_random():
+    x = synth.bf16_to_f64(synth.bf16_bits(RNG.standard_normal((400, 128)).astype(np.float32) * 3))
+    R, _ = np.linalg.qr(RNG.standard_normal((128, 128)))
+    for G in (32, 64, 128):
+        q = o.quantize(x, R, 5.0, G)
+        c, s, z = q["codes"], q["scale"].astype(float), q["zero"].astype(float)
+        assert c.min() >= 0 and c.max() <= 3
+        xh = o.dequantize(c, q["scale"], q["zero"], G)
+        ng = 128 // G
+        err = np.abs(q["xc"] - xh).reshape(-1, ng, G)
+        # half a step plus fp16 rounding slack of the zero and of the scale (x3)
+        slack = np.abs(q["xc"]).reshape(-1, ng, G).max(axis=2) * 2.0 ** -10
+        assert np.all(err.max(axis=2) <= s / 2 + 4 * slack + 1e-12)
+        g = q["xc"].reshape(-1, ng, G)
+        cg = c.reshape(-1, ng, G)
+        amin = np.argmin(g, axis=2)
+        amax = np.argmax(g, axis=2)
+        assert np.all(np.take_along_axis(cg, amin[..., None], 2) == 0)
+        assert np.all(np.take_along_axis(cg, amax[..., None], 2) == 3)
+
+
+def test_quantizer_identity_is_textbook_minmax():
+    # R = I and no clipping: per-token asymmetric min-max INT2 written out
+    # element by element in plain Python
+    x = synth.bf16_to_f64(synth.bf16_bits(RNG.standard_normal((6, 128)).astype(np.float32)))
+    for G in (32, 64, 128):
+        q = o.quantize(x, np.eye(128), 1e9, G)
+        for n in range(x.shape[0]):
+            for g in range(128 // G):
+                vals = [float(v) for v in x[n, g * G:(g + 1) * G]]
+                lo, hi = min(vals), max(vals)
+                z = float(np.float16(lo))
+                s = float(np.float16((hi - lo) / 3))
+                for i, val in enumerate(vals):
+                    t = (val - z) / s
+                    r = math.floor(t + 0.5)
+                    if t + 0.5 == r and r % 2 == 1:   # exact tie -> even
+                        r -= 1
+                    assert q["codes"][n, g * G + i] == min(3, max(0, r))
+
+
+# ------------------------------------------------------------------ packing
+
+
+def test_pack_roundtrip_and_bijection():
+    c = RNG.integers(0, 4, size=(7, 16, 128)).astype(np.uint8)
+    for kind in "KV":
+        assert np.array_equal(o.unpack_codes(o.pack_codes(c, kind), kind), c)
+        # every bit of the 512-byte area is used by exactly one code
+        ones = np.full((1, 16, 128), 3, dtype=np.uint8)
+        assert np.all(o.pack_codes(ones, kind) == 0xFF)
+
+
+def test_pack_hand_derived_bytes():
+    g = _golden("pack_bytes.json")
+    for case in g["cases"]:
+        c = np.zeros((16, 128), dtype=np.uint8)
+        c[case["row"], case["channel"]] = case["code"]
+        area = o.pack_codes(c, case["kind"])
+        expect = np.zeros(512, dtype=np.uint8)
+        expect[case["byte"]] = case["value"]
+        assert np.array_equal(area, expect), case["derivation"]
+    for case in g["meta_cases"]:
+        ng = 128 // case["G"]
+        s = np.zeros((16, ng), dtype=np.float16)
+        z = np.zeros((16, ng), dtype=np.float16)
+        s[case["row"], case["group"]] = case["scale"]
+        z[case["row"], case["group"]] = case["zero"]
+        area = o.pack_meta(s, z)
+        assert area.shape == (64 * ng,)
+        for k, v in case["bytes"].items():
+            assert area[int(k)] == v
+        s2, z2 = o.unpack_meta(area, case["G"])
+        assert np.array_equal(s2, s) and np.array_equal(z2, z)
+
+
+def test_block_sizes():
+    assert [o.hist_block_bytes(G) for G in (32, 64, 128)] == [1536, 1280, 1152]
+
+
+# ------------------------------------------------------------------- layout
+
+
+def test_storage_of_boundaries():
+    assert o.storage_of(0, 1) == ("sink", 0)
+    assert o.storage_of(15, 16) == ("sink", 15)
+    assert o.storage_of(16, 17) == ("ring", 16)
+    assert o.storage_of(143, 144) == ("ring", 15)
+    assert o.storage_of(16, 145) == ("hist", 0)     # first token to leave the window
+    assert o.storage_of(17, 145) == ("ring", 17)
+    assert o.storage_of(144, 145) == ("ring", 16)   # takes the freed slot
+    assert o.storage_of(31, 160) == ("hist", 15)
+    assert o.storage_of(32, 161) == ("hist", 16)    # second history page
+    for L in (1, 16, 17, 144, 145, 160, 161, 4096):
+        kinds = [o.storage_of(p, L)[0] for p in range(L)]
+        n_ring = min(128, max(0, L - 16))
+        assert kinds.count("sink") == min(L, 16)
+        assert kinds.count("ring") == n_ring
+        assert kinds.count("hist") == max(0, L - 144)
+        slots = [o.storage_of(p, L)[1] for p in range(L) if o.storage_of(p, L)[0] == "ring"]
+        assert len(set(slots)) == len(slots)
+
+
+def _make_cache(L_max, hkv=2, G=32, batch=1, seed=3):
+    n_hist = max(1, (max(0, L_max - 144) + 15) // 16)
+    pt, npool = synth.shuffled_page_tables(seed, 0, [L_max] * batch, n_pool_pages=n_hist * batch + 3)
+    bpt = synth.bf16_page_tables(batch, shuffle_seed=seed)
+    return o.LayerCacheRef(hkv, G, npool, 9 * batch, pt, bpt)
+
+
+def _rot(seed=5):
+    R, _ = np.linalg.qr(np.random.default_rng(seed).standard_normal((128, 128)))
+    return R
+
+
+@pytest.mark.parametrize("L", [1, 16, 17, 144, 145, 160, 161, 300])
+def test_prefill_equals_token_by_token(L):
+    ld = synth.LayerData(21, 0, 4, 2)
+    k, v = ld.cache_kv(L)
+    R = _rot()
+    a = _make_cache(L)
+    a.write(R, R.T, 4.0, 3.0, k, v, [0, L], [0])
+    b = _make_cache(L)
+    for p in range(L):
+        b.write(R, R.T, 4.0, 3.0, k[p:p + 1], v[p:p + 1], [0, 1], [p])
+    assert np.array_equal(a.hist, b.hist)
+    Ka, Va = a.gather(0, L, R, R.T)
+    Kb, Vb = b.gather(0, L, R, R.T)
+    assert np.array_equal(Ka, Kb) and np.array_equal(Va, Vb)
+
+
+def test_chunked_writes_equal_one_shot():
+    L = 500
+    ld = synth.LayerData(22, 0, 4, 2)
+    k, v = ld.cache_kv(L)
+    R = _rot(6)
+    a = _make_cache(L, G=64)
+    a.write(R, R, 5.0, 5.0, k, v, [0, L], [0])
+    b = _make_cache(L, G=64)
+    cuts = [0, 10, 150, 151, 400, 500]   # chunks longer than the window evict many ring tokens
+    for lo, hi in zip(cuts[:-1], cuts[1:]):
+        b.write(R, R, 5.0, 5.0, k[lo:hi], v[lo:hi], [0, hi - lo], [lo])
+    assert np.array_equal(a.hist, b.hist)
+    for L_ in (L,):
+        Ka, Va = a.gather(0, L_, R, R)
+        Kb, Vb = b.gather(0, L_, R, R)
+        assert np.array_equal(Ka, Kb) and np.array_equal(Va, Vb)
+
+
+def test_gather_raw_tokens_exact_and_history_close():
+    L = 200
+    ld = synth.LayerData(23, 0, 4, 2)
+    k, v = ld.cache_kv(L)
+    R = _rot(7)
+    c = _make_cache(L, G=32)
+    c.write(R, R, 1e4, 1e4, k, v, [0, L], [0])
+    K, V = c.gather(0, L, R, R)
+    kf, vf = synth.bf16_to_f64(k), synth.bf16_to_f64(v)
+    raw = [p for p in range(L) if o.storage_of(p, L)[0] != "hist"]
+    hist = [p for p in range(L) if o.storage_of(p, L)[0] == "hist"]
+    assert np.array_equal(K[raw], kf[raw]) and np.array_equal(V[raw], vf[raw])
+    # history: error of each rotated coordinate <= half a step (+ fp16 slack);
+    # an orthogonal R keeps the Euclidean norm of the error
+    for X, Xh in ((kf, K), (vf, V)):
+        err = np.linalg.norm((X[hist] - Xh[hist]).reshape(len(hist), 2, 128), axis=2)
+        q = o.quantize(X[hist].reshape(-1, 128), R, 1e4, 32)
+        bound = np.sqrt(np.sum(((q["scale"].astype(float) / 2 + 0.01) ** 2) * 32, axis=1)).reshape(len(hist), 2)
+        assert np.all(err <= bound)
+
+
+# ------------------------------------------------------------------- decode
+
+
+def _brute_attention(q, K, V, scale):
+    """Plain-Python softmax attention of one head."""
+    logits = [sum(q[i] * K[t][i] for i in range(len(q))) * scale for t in range(len(K))]
+    m = max(logits)
+    w = [math.exp(x - m) for x in logits]
+    tot = sum(w)
+    return [sum(w[t] * V[t][i] for t in range(len(K))) / tot for i in range(len(q))]
+
+
+def test_attention_brute_force_tiny():
+    for L in (1, 2, 7, 20):
+        q = RNG.standard_normal((4, 128))
+        K = RNG.standard_normal((L, 2, 128))
+        V = RNG.standard_normal((L, 2, 128))
+        out = o.attention(q, K, V, 0.1)
+        for h in range(4):
+            ref = _brute_attention(q[h].tolist(), K[:, h // 2].tolist(), V[:, h // 2].tolist(), 0.1)
+            np.testing.assert_allclose(out[h], ref, rtol=1e-12, atol=1e-12)
+
+
+def _filled(L, batch=1, hkv=2, hq=8, G=32, seed=31, R=None, Rv=None, clip=(6.0, 6.0)):
+    ld = synth.LayerData(seed, 0, hq, hkv)
+    k, v = ld.cache_kv(L * batch)
+    R = _rot(8) if R is None else R
+    Rv = R if Rv is None else Rv
+    c = _make_cache(L, hkv=hkv, G=G, batch=batch, seed=seed)
+    cu = [L * i for i in range(batch + 1)]
+    c.write(R, Rv, clip[0], clip[1], k, v, cu, [0] * batch)
+    return c, k, v, ld.decode_q(batch), R, Rv
+
+
+def test_decode_single_token_returns_v():
+    c, k, v, q, R, Rv = _filled(1)
+    out = o.decode_attn(c, R, Rv, q, [1], 0.088)
+    vf = synth.bf16_to_f64(v)
+    for h in range(8):
+        assert np.array_equal(out[0, h], vf[0, h // 4])
+
+
+def test_decode_equal_keys_average_values():
+    L = 40
+    ld = synth.LayerData(32, 0, 8, 2)
+    k, v = ld.cache_kv(L)
+    k[:] = k[0]
+    c = _make_cache(L)
+    R = np.eye(128)
+    c.write(R, R, 1e4, 1e4, k, v, [0, L], [0])
+    out = o.decode_attn(c, R, R, ld.decode_q(1), [L], 0.088)
+    vf = synth.bf16_to_f64(v)
+    for h in range(8):
+        np.testing.assert_allclose(out[0, h], vf[:, h // 4].mean(axis=0), rtol=1e-12, atol=1e-12)
+
+
+def test_decode_without_history_equals_bf16_decode():
+    for L in (1, 16, 17, 100, 144):
+        c, k, v, q, R, Rv = _filled(L)
+        out = o.decode_attn(c, R, Rv, q, [L], 0.088)
+        pages = np.zeros(((L + 15) // 16, 2, 2, 16, 128), dtype=np.uint16)
+        for p in range(L):
+            pages[p // 16, :, 0, p % 16] = k[p]
+            pages[p // 16, :, 1, p % 16] = v[p]
+        pt = np.arange(pages.shape[0], dtype=np.int32)[None]
+        ref = o.bf16_paged_decode(q, pages, pt, [L], 0.088)
+        np.testing.assert_allclose(out, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_decode_lossless_history_pins_rotation_direction():
+    # R = a cyclic channel shift (orthogonal, not symmetric).  Each rotated
+    # group holds only the values {z, z+s, z+2s, z+3s} with fp16-exact s, z,
+    # so quantisation is lossless and the INT2 decode must equal the BF16
+    # decode of the same tokens: a transposed R on either side breaks this.
+    L = 180
+    shift = np.roll(np.eye(128), 5, axis=1)
+    rng = np.random.default_rng(99)
+    k = np.zeros((L, 2, 128), dtype=np.float32)
+    v = np.zeros((L, 2, 128), dtype=np.float32)
+    for X in (k, v):
+        lv = rng.integers(0, 4, size=(L, 2, 128)).astype(np.float32)
+        lv[..., 0::32] = 0
+        lv[..., 1::32] = 3
+        X[:] = (lv * 0.5 - 1.0) @ shift.T  # x R = levels
+    kb, vb = synth.bf16_bits(k), synth.bf16_bits(v)
+    c = _make_cache(L)
+    c.write(shift, shift, 100.0, 100.0, kb, vb, [0, L], [0])
+    q = synth.LayerData(5, 0, 8, 2).decode_q(1)
+    out = o.decode_attn(c, shift, shift, q, [L], 0.088)
+    pages = np.zeros(((L + 15) // 16, 2, 2, 16, 128), dtype=np.uint16)
+    for p in range(L):
+        pages[p // 16, :, 0, p % 16] = kb[p]
+        pages[p // 16, :, 1, p % 16] = vb[p]
+    ref = o.bf16_paged_decode(q, pages, np.arange(pages.shape[0], dtype=np.int32)[None], [L], 0.088)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+    # and the same cache read with R^T in place of R is far off
+    bad = o.decode_attn(c, shift.T, shift.T, q, [L], 0.088)
+    assert np.abs(bad - ref).max() > 0.1
+
+
+def test_decode_mha_and_gqa_agree_when_heads_repeat():
+    L = 200
+    c, k, v, q, R, Rv = _filled(L, hkv=2, hq=2)
+    out_mha = o.decode_attn(c, R, Rv, q, [L], 0.088)
+    # GQA with 4 query heads where heads 0,1 repeat query 0 and heads 2,3 query 1
+    q4 = np.repeat(q, 2, axis=1)
+    out_gqa = o.decode_attn(c, R, Rv, q4, [L], 0.088)
+    np.testing.assert_allclose(out_gqa[0, 0::2], out_mha[0], rtol=0, atol=0)
+
+
+def test_decode_page_permutation_invariant():
+    L = 260
+    c, k, v, q, R, Rv = _filled(L, G=64)
+    out = o.decode_attn(c, R, Rv, q, [L], 0.088)
+    perm = np.random.default_rng(4).permutation(c.hist.shape[0])
+    c2 = o.LayerCacheRef(2, 64, c.hist.shape[0], 9, perm[c.hist_pt], c.bf16_pt)
+    c2.hist[perm] = c.hist
+    c2.bf16[:] = c.bf16
+    out2 = o.decode_attn(c2, R, Rv, q, [L], 0.088)
+    assert np.array_equal(out, out2)
+
+
+def test_decode_shared_prefix_pages():
+    # two requests with the same first 176 tokens share history pages 0-1
+    L = 300
+    ld = synth.LayerData(41, 0, 8, 2)
+    k, v = ld.cache_kv(2 * L)
+    k[L:L + 176] = k[:176]
+    v[L:L + 176] = v[:176]
+    R = _rot(9)
+    n_hist = (L - 144 + 15) // 16
+    pt = np.array([np.arange(n_hist), np.r_[0, 1, np.arange(n_hist, 2 * n_hist - 2)]], dtype=np.int32)
+    bpt = synth.bf16_page_tables(2)
+    shared = o.LayerCacheRef(2, 32, 2 * n_hist, 18, pt, bpt)
+    shared.write(R, R, 6.0, 6.0, k[:L], v[:L], [0, L], [0])
+    shared.write(R, R, 6.0, 6.0, k[L:], v[L:], [0, 0, L], [0, 0])   # request 1 rewrites pages 0-1 identically
+    sep = o.LayerCacheRef(2, 32, 2 * n_hist, 18,
+                          np.array([np.arange(n_hist), np.arange(n_hist, 2 * n_hist)], dtype=np.int32), bpt)
+    sep.write(R, R, 6.0, 6.0, k, v, [0, L, 2 * L], [0, 0])
+    q = ld.decode_q(2)
+    np.testing.assert_array_equal(o.decode_attn(shared, R, R, q, [L, L], 0.088),
+                                  o.decode_attn(sep, R, R, q, [L, L], 0.088))
+
+
+def test_decode_brute_force_with_history():
+    # the whole decode (dequantise + inverse rotation + softmax) against a
+    # plain-Python evaluation that reads codes bit by bit from the bytes
+    L = 170
+    c, k, v, q, R, Rv = _filled(L, hkv=1, hq=2, G=64, clip=(3.0, 2.5))
+    out = o.decode_attn(c, R, Rv, q, [L], 0.1)
+    qf = synth.bf16_to_f64(q)[0]
+    kf, vf = synth.bf16_to_f64(k), synth.bf16_to_f64(v)
+    LO, HI = o.LO_BIT, o.HI_BIT
+
+    def code_at(area, kind, t, ch):
+        for lane in range(64):
+            a, qq = lane % 16, lane // 16
+            for d in range(2):
+                for u in range(8):
+                    if kind == "K":
+                        hits = [(a, 32 * (2 * d + u // 4) + 8 * qq + 2 * (u % 4), LO[u]),
+                                (a, 32 * (2 * d + u // 4) + 8 * qq + 2 * (u % 4) + 1, HI[u])]
+                    else:
+                        cc, t0 = 16 * (4 * d + u // 2) + a, 4 * qq + 2 * (u % 2)
+                        hits = [(t0, cc, LO[u]), (t0 + 1, cc, HI[u])]
+                    for tt, c2, bit in hits:
+                        if tt == t and c2 == ch:
+                            word = int.from_bytes(bytes(area[8 * lane + 4 * d:8 * lane + 4 * d + 4]), "little")
+                            return (word >> bit) & 3
+        raise AssertionError
+
+    def vec(kind, p):
+        h = p - 16
+        blk = c.hist[c.hist_pt[0, h // 16], 0]
+        off = 0 if kind == "K" else 512 + 128
+        meta = blk[off + 512: off + 512 + 128].view(np.float16)
+        xr = []
+        for ch in range(128):
+            g = ch // 64
+            s, z = float(meta[2 * (16 * g + h % 16)]), float(meta[2 * (16 * g + h % 16) + 1])
+            xr.append(code_at(blk[off:off + 512], kind, h % 16, ch) * s + z)
+        Rm = R if kind == "K" else Rv
+        return [sum(xr[j] * Rm[i, j] for j in range(128)) for i in range(128)]
+
+    Ks, Vs = [], []
+    for p in range(L):
+        if o.storage_of(p, L)[0] == "hist":
+            Ks.append(vec("K", p))
+            Vs.append(vec("V", p))
+        else:
+            Ks.append(kf[p, 0].tolist())
+            Vs.append(vf[p, 0].tolist())
+    for h in range(2):
+        ref = _brute_attention(qf[h].tolist(), Ks, Vs, 0.1)
+        np.testing.assert_allclose(out[0, h], ref, rtol=1e-11, atol=1e-11)
