@@ -1,0 +1,191 @@
+"""Thin Python binding over liboscar (argument marshalling only).
+
+Every function turns torch tensors into pointers and sizes and calls the C
+entry point of the same name; all computation runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from ._lib import LayerCacheC, RotationC, check, load
+
+HEAD_DIM = 128
+PAGE = 16
+N_SINK = 16
+N_RECENT = 128
+BF16_PAGES_PER_REQ = 9
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtypes, device=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def hist_block_bytes(group: int) -> int:
+    return int(load().oscar_hist_block_bytes(group))
+
+
+def rotation_bytes() -> int:
+    return int(load().oscar_rotation_bytes())
+
+
+class Rotation:
+    """Device forms of one fixed per-layer rotation R (fp64 [128,128], x_rot = x R)
+    and its clip threshold; built by oscar_prepare_rotation."""
+
+    def __init__(self, R, clip: float, device: torch.device | str = "cuda"):
+        device = torch.device(device)
+        self.R64 = torch.as_tensor(R, dtype=torch.float64).to(device).contiguous()
+        if tuple(self.R64.shape) != (HEAD_DIM, HEAD_DIM):
+            raise ValueError("R must be [128, 128]")
+        self.forms = torch.empty(rotation_bytes(), dtype=torch.uint8, device=device)
+        self.clip = float(clip)
+        check(load().oscar_prepare_rotation(_ptr(self.R64), _ptr(self.forms), _stream(device)))
+
+    def c(self) -> RotationC:
+        return RotationC(self.forms.data_ptr(), self.clip)
+
+
+class LayerCache:
+    """One layer's paged cache in the formats of include/oscar.h.
+
+    hist:   uint8 [n_hist_pages, Hkv, hist_block_bytes(group)]
+    bf16:   bfloat16 [n_bf16_pages, Hkv, 2, 16, 128]
+    hist_pt int32 [B, stride], bf16_pt int32 [B, 9], status int32 [1].
+    """
+
+    def __init__(self, n_kv_heads: int, group: int, n_hist_pages: int, n_bf16_pages: int,
+                 hist_pt: torch.Tensor, bf16_pt: torch.Tensor, device="cuda",
+                 hist: torch.Tensor | None = None, bf16: torch.Tensor | None = None):
+        device = torch.device(device)
+        self.device = device
+        self.n_kv_heads, self.group = int(n_kv_heads), int(group)
+        blk = hist_block_bytes(group)
+        if blk == 0:
+            raise ValueError(f"unsupported group {group}")
+        self.hist = hist if hist is not None else torch.zeros(
+            (max(n_hist_pages, 0), n_kv_heads, blk), dtype=torch.uint8, device=device)
+        self.bf16 = bf16 if bf16 is not None else torch.zeros(
+            (n_bf16_pages, n_kv_heads, 2, PAGE, HEAD_DIM), dtype=torch.bfloat16, device=device)
+        self.hist_pt = torch.as_tensor(hist_pt, dtype=torch.int32).to(device).contiguous()
+        self.bf16_pt = torch.as_tensor(bf16_pt, dtype=torch.int32).to(device).contiguous()
+        self.status = torch.zeros(1, dtype=torch.int32, device=device)
+        _need(self.hist, "hist", (torch.uint8,), device)
+        _need(self.bf16, "bf16", (torch.bfloat16, torch.int16), device)
+
+    def c(self) -> LayerCacheC:
+        return LayerCacheC(self.n_kv_heads, self.group, self.hist.data_ptr(), self.hist.shape[0],
+                           self.bf16.data_ptr(), self.bf16.shape[0], self.hist_pt.data_ptr(),
+                           self.hist_pt.shape[1], self.bf16_pt.data_ptr(), self.status.data_ptr())
+
+
+def write_kv(cache: LayerCache, rot_k: Rotation, rot_v: Rotation, k_new: torch.Tensor,
+             v_new: torch.Tensor, cu_new: torch.Tensor, len_before: torch.Tensor, max_new: int) -> None:
+    """oscar_write_kv: append rows cu_new[b]..cu_new[b+1]-1 of k_new / v_new
+    (bf16 [T, Hkv, 128]) to request b at positions len_before[b]... ."""
+    dev = cache.device
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, n, (torch.bfloat16,), dev)
+    _need(cu_new, "cu_new", (torch.int32,), dev)
+    _need(len_before, "len_before", (torch.int32,), dev)
+    batch = len_before.shape[0]
+    if cu_new.shape[0] != batch + 1:
+        raise ValueError("cu_new must have batch + 1 entries")
+    c = cache.c()
+    rk, rv = rot_k.c(), rot_v.c()
+    check(load().oscar_write_kv(ctypes.byref(c), ctypes.byref(rk), ctypes.byref(rv), _ptr(k_new),
+                                _ptr(v_new), _ptr(cu_new), _ptr(len_before), batch, k_new.shape[0],
+                                int(max_new), _stream(dev)))
+
+
+def decode_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, max_seq_len: int) -> int:
+    return int(load().oscar_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, max_seq_len))
+
+
+def decode_attn(cache: LayerCache, rot_k: Rotation, rot_v: Rotation, q: torch.Tensor,
+                seq_lens: torch.Tensor, max_seq_len: int, sm_scale: float | None = None,
+                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """oscar_decode_attn: q bf16 [B, Hq, 128] -> out fp32 [B, Hq, 128]."""
+    dev = cache.device
+    _need(q, "q", (torch.bfloat16,), dev)
+    _need(seq_lens, "seq_lens", (torch.int32,), dev)
+    batch, hq = q.shape[0], q.shape[1]
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if out is None:
+        out = torch.empty((batch, hq, HEAD_DIM), dtype=torch.float32, device=dev)
+    _need(out, "out", (torch.float32,), dev)
+    need = decode_workspace_bytes(batch, hq, cache.n_kv_heads, max_seq_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    c = cache.c()
+    rk, rv = rot_k.c(), rot_v.c()
+    check(load().oscar_decode_attn(ctypes.byref(c), ctypes.byref(rk), ctypes.byref(rv), _ptr(q), hq,
+                                   _ptr(seq_lens), batch, int(max_seq_len), float(sm_scale), _ptr(out),
+                                   _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out
+
+
+def bf16_decode_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, max_seq_len: int) -> int:
+    return int(load().oscar_bf16_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, max_seq_len))
+
+
+def bf16_paged_decode(q: torch.Tensor, kv_pages: torch.Tensor, pt: torch.Tensor, seq_lens: torch.Tensor,
+                      max_seq_len: int, sm_scale: float | None = None, out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None,
+                      status: torch.Tensor | None = None) -> torch.Tensor:
+    """oscar_bf16_paged_decode over kv_pages bf16 [pages, Hkv, 2, 16, 128]."""
+    dev = q.device
+    _need(q, "q", (torch.bfloat16,), dev)
+    _need(kv_pages, "kv_pages", (torch.bfloat16,), dev)
+    _need(pt, "pt", (torch.int32,), dev)
+    _need(seq_lens, "seq_lens", (torch.int32,), dev)
+    batch, hq = q.shape[0], q.shape[1]
+    hkv = kv_pages.shape[1]
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if out is None:
+        out = torch.empty((batch, hq, HEAD_DIM), dtype=torch.float32, device=dev)
+    need = bf16_decode_workspace_bytes(batch, hq, hkv, max_seq_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    check(load().oscar_bf16_paged_decode(_ptr(q), _ptr(kv_pages), kv_pages.shape[0], _ptr(pt), pt.shape[1],
+                                         _ptr(seq_lens), batch, int(max_seq_len), hq, hkv, float(sm_scale),
+                                         _ptr(out), _ptr(status), _ptr(workspace), workspace.numel(),
+                                         _stream(dev)))
+    return out
+
+
+def calibrate_rotation(q_cal: torch.Tensor, k_cal: torch.Tensor, v_cal: torch.Tensor,
+                       clip_quantile: float = 0.999):
+    """oscar_calibrate_rotation: bf16 [N, Hq, 128], [N, Hkv, 128] x2 on the device ->
+    (R_K, R_V) float64 CPU tensors [128, 128] and (clip_K, clip_V) floats."""
+    dev = q_cal.device
+    for t, n in ((q_cal, "q_cal"), (k_cal, "k_cal"), (v_cal, "v_cal")):
+        _need(t, n, (torch.bfloat16,), dev)
+    R_K = torch.empty((HEAD_DIM, HEAD_DIM), dtype=torch.float64)
+    R_V = torch.empty((HEAD_DIM, HEAD_DIM), dtype=torch.float64)
+    ck, cv = ctypes.c_float(0), ctypes.c_float(0)
+    check(load().oscar_calibrate_rotation(_ptr(q_cal), _ptr(k_cal), _ptr(v_cal), q_cal.shape[0],
+                                          q_cal.shape[1], k_cal.shape[1], float(clip_quantile),
+                                          _ptr(R_K), _ptr(R_V), ctypes.byref(ck), ctypes.byref(cv),
+                                          _stream(dev)))
+    return R_K, R_V, ck.value, cv.value

@@ -1,0 +1,258 @@
+// extern "C" entry points of liboscar: argument validation, workspace sizing,
+// error reporting, and the host side of calibration.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "calib_host.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char *where) {
+  return fail(OSCAR_EHIP, "%s: HIP error %d (%s)", where, int(e), hipGetErrorString(e));
+}
+
+// The current device must be gfx950; the answer is cached per device id.
+int check_device() {
+  static int cached[64] = {0};  // 0 unknown, 1 ok, -1 not gfx950
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) return fail(OSCAR_ENODEV, "no HIP device (%s)", hipGetErrorString(e));
+  if (dev < 64 && cached[dev] == 1) return OSCAR_OK;
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) cached[dev] = ok ? 1 : -1;
+  if (!ok) return fail(OSCAR_ENODEV, "device %d is %s, this library is built for gfx950", dev, prop.gcnArchName);
+  return OSCAR_OK;
+}
+
+bool group_ok(int G) { return G == 32 || G == 64 || G == 128; }
+
+int check_cache(const oscar_layer_cache *c) {
+  if (!c) return fail(OSCAR_EINVAL, "cache is NULL");
+  if (c->n_kv_heads < 1 || c->n_kv_heads > 256)
+    return fail(OSCAR_EINVAL, "n_kv_heads %d outside [1, 256]", c->n_kv_heads);
+  if (!group_ok(c->group)) return fail(OSCAR_EUNSUPPORTED, "group %d not in {32, 64, 128}", c->group);
+  if (c->n_hist_pages < 0 || c->n_bf16_pages < 1)
+    return fail(OSCAR_EINVAL, "page counts must be n_hist_pages >= 0 and n_bf16_pages >= 1");
+  if (c->n_hist_pages > (int64_t(1) << 31) - 1 || c->n_bf16_pages > (int64_t(1) << 31) - 1)
+    return fail(OSCAR_EINVAL, "page counts must fit int32 page ids");
+  if (c->n_hist_pages > 0 && !c->hist) return fail(OSCAR_EINVAL, "hist pool is NULL");
+  if (!c->bf16) return fail(OSCAR_EINVAL, "bf16 pool is NULL");
+  if (!c->hist_pt || c->hist_pt_stride < 1) return fail(OSCAR_EINVAL, "hist_pt NULL or hist_pt_stride < 1");
+  if (!c->bf16_pt) return fail(OSCAR_EINVAL, "bf16_pt is NULL");
+  return OSCAR_OK;
+}
+
+int check_rot(const oscar_rotation *r, const char *name) {
+  if (!r || !r->forms) return fail(OSCAR_EINVAL, "%s: rotation or its forms is NULL", name);
+  if (!std::isfinite(r->clip) || r->clip <= 0.f || r->clip > 65504.f)
+    return fail(OSCAR_EINVAL, "%s: clip %g must be finite, > 0 and <= 65504", name, double(r->clip));
+  return OSCAR_OK;
+}
+
+oscar::RotArg rot_arg(const oscar_rotation *r) {
+  return oscar::RotArg{static_cast<const uint8_t *>(r->forms), r->clip};
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *oscar_last_error(void) { return g_err.c_str(); }
+
+const char *oscar_version(void) { return "oscar-gfx950 0.1"; }
+
+size_t oscar_hist_block_bytes(int32_t group) {
+  return group_ok(group) ? size_t(oscar::hist_block_bytes(group)) : 0;
+}
+
+size_t oscar_rotation_bytes(void) { return oscar::FORM_BYTES; }
+
+int oscar_prepare_rotation(const double *R, void *forms, oscar_stream_t stream) {
+  if (!R || !forms) return fail(OSCAR_EINVAL, "R or forms is NULL");
+  if (int rc = check_device()) return rc;
+  hipError_t e = oscar::launch_prepare_rotation(R, forms, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "prepare_rotation");
+  return OSCAR_OK;
+}
+
+int oscar_write_kv(const oscar_layer_cache *cache, const oscar_rotation *rot_k,
+                   const oscar_rotation *rot_v, const uint16_t *k_new, const uint16_t *v_new,
+                   const int32_t *cu_new, const int32_t *len_before, int32_t batch,
+                   int64_t total_tokens, int32_t max_new, oscar_stream_t stream) {
+  if (int rc = check_cache(cache)) return rc;
+  if (int rc = check_rot(rot_k, "rot_k")) return rc;
+  if (int rc = check_rot(rot_v, "rot_v")) return rc;
+  if (batch < 1 || batch > 65535) return fail(OSCAR_EINVAL, "batch %d outside [1, 65535]", batch);
+  if (total_tokens < 0 || max_new < 0) return fail(OSCAR_EINVAL, "negative token counts");
+  if (int64_t(max_new) > total_tokens) return fail(OSCAR_EINVAL, "max_new %d > total_tokens %lld", max_new, (long long)total_tokens);
+  if (max_new > (1 << 24)) return fail(OSCAR_EINVAL, "max_new %d too large", max_new);
+  if (!cu_new || !len_before) return fail(OSCAR_EINVAL, "cu_new or len_before is NULL");
+  if (total_tokens > 0 && (!k_new || !v_new)) return fail(OSCAR_EINVAL, "k_new or v_new is NULL");
+  if (max_new == 0) return OSCAR_OK;
+  if (int rc = check_device()) return rc;
+  hipError_t e = oscar::launch_write_kv(*cache, rot_arg(rot_k), rot_arg(rot_v), k_new, v_new, cu_new,
+                                        len_before, batch, total_tokens, max_new,
+                                        reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "write_kv");
+  return OSCAR_OK;
+}
+
+size_t oscar_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                    int32_t max_seq_len) {
+  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || max_seq_len < 1) return 0;
+  return oscar::decode_int2_ws_bytes(batch, n_q_heads, n_kv_heads, max_seq_len);
+}
+
+static int check_heads(int32_t hq, int32_t hkv) {
+  if (hq < 1 || hkv < 1) return fail(OSCAR_EINVAL, "head counts must be >= 1");
+  if (hq % hkv) return fail(OSCAR_EUNSUPPORTED, "n_q_heads %d not a multiple of n_kv_heads %d", hq, hkv);
+  if (hq / hkv > 16) return fail(OSCAR_EUNSUPPORTED, "GQA group %d > 16", hq / hkv);
+  return OSCAR_OK;
+}
+
+int oscar_decode_attn(const oscar_layer_cache *cache, const oscar_rotation *rot_k,
+                      const oscar_rotation *rot_v, const uint16_t *q, int32_t n_q_heads,
+                      const int32_t *seq_lens, int32_t batch, int32_t max_seq_len, float sm_scale,
+                      float *out, void *workspace, size_t workspace_bytes, oscar_stream_t stream) {
+  if (int rc = check_cache(cache)) return rc;
+  if (int rc = check_rot(rot_k, "rot_k")) return rc;
+  if (int rc = check_rot(rot_v, "rot_v")) return rc;
+  if (int rc = check_heads(n_q_heads, cache->n_kv_heads)) return rc;
+  if (batch < 1 || batch > 65535) return fail(OSCAR_EINVAL, "batch %d outside [1, 65535]", batch);
+  if (max_seq_len < 1) return fail(OSCAR_EINVAL, "max_seq_len %d < 1", max_seq_len);
+  if (oscar::n_hist_pages(max_seq_len) > cache->hist_pt_stride)
+    return fail(OSCAR_EINVAL, "max_seq_len %d needs %d history pages, hist_pt_stride is %d", max_seq_len,
+                oscar::n_hist_pages(max_seq_len), cache->hist_pt_stride);
+  if (!q || !seq_lens || !out) return fail(OSCAR_EINVAL, "q, seq_lens or out is NULL");
+  if (!std::isfinite(sm_scale) || sm_scale <= 0.f) return fail(OSCAR_EINVAL, "sm_scale must be finite and > 0");
+  const size_t need = oscar::decode_int2_ws_bytes(batch, n_q_heads, cache->n_kv_heads, max_seq_len);
+  if (!workspace || workspace_bytes < need)
+    return fail(OSCAR_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+  if (int rc = check_device()) return rc;
+  hipError_t e = oscar::launch_decode_int2(*cache, rot_arg(rot_k), rot_arg(rot_v), q, n_q_heads, seq_lens,
+                                           batch, max_seq_len, sm_scale, out, workspace,
+                                           reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode_attn");
+  return OSCAR_OK;
+}
+
+size_t oscar_bf16_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                         int32_t max_seq_len) {
+  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || max_seq_len < 1) return 0;
+  return oscar::decode_bf16_ws_bytes(batch, n_q_heads, n_kv_heads, max_seq_len);
+}
+
+int oscar_bf16_paged_decode(const uint16_t *q, const uint16_t *kv_pages, int64_t n_pages,
+                            const int32_t *pt, int32_t pt_stride, const int32_t *seq_lens,
+                            int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
+                            int32_t n_kv_heads, float sm_scale, float *out, uint32_t *status,
+                            void *workspace, size_t workspace_bytes, oscar_stream_t stream) {
+  if (int rc = check_heads(n_q_heads, n_kv_heads)) return rc;
+  if (!q || !kv_pages || !pt || !seq_lens || !out) return fail(OSCAR_EINVAL, "NULL pointer argument");
+  if (n_pages < 1 || n_pages > (int64_t(1) << 31) - 1) return fail(OSCAR_EINVAL, "n_pages %lld invalid", (long long)n_pages);
+  if (batch < 1 || batch > 65535) return fail(OSCAR_EINVAL, "batch %d outside [1, 65535]", batch);
+  if (max_seq_len < 1) return fail(OSCAR_EINVAL, "max_seq_len %d < 1", max_seq_len);
+  if (pt_stride < (max_seq_len + OSCAR_PAGE - 1) / OSCAR_PAGE)
+    return fail(OSCAR_EINVAL, "pt_stride %d too small for max_seq_len %d", pt_stride, max_seq_len);
+  if (!std::isfinite(sm_scale) || sm_scale <= 0.f) return fail(OSCAR_EINVAL, "sm_scale must be finite and > 0");
+  const size_t need = oscar::decode_bf16_ws_bytes(batch, n_q_heads, n_kv_heads, max_seq_len);
+  if (!workspace || workspace_bytes < need)
+    return fail(OSCAR_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+  if (int rc = check_device()) return rc;
+  hipError_t e = oscar::launch_decode_bf16(q, kv_pages, n_pages, pt, pt_stride, seq_lens, batch, max_seq_len,
+                                           n_q_heads, n_kv_heads, sm_scale, out, status, workspace,
+                                           reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "bf16_paged_decode");
+  return OSCAR_OK;
+}
+
+int oscar_calibrate_rotation(const uint16_t *q_cal, const uint16_t *k_cal, const uint16_t *v_cal,
+                             int64_t n_tokens, int32_t n_q_heads, int32_t n_kv_heads,
+                             double clip_quantile, double *R_K, double *R_V, float *clip_K,
+                             float *clip_V, oscar_stream_t stream) {
+  if (!q_cal || !k_cal || !v_cal) return fail(OSCAR_EINVAL, "calibration inputs NULL");
+  if (!R_K || !R_V || !clip_K || !clip_V) return fail(OSCAR_EINVAL, "outputs NULL");
+  if (n_tokens < 1 || n_tokens > 65536) return fail(OSCAR_EINVAL, "n_tokens %lld outside [1, 65536]", (long long)n_tokens);
+  if (n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || n_q_heads > 256)
+    return fail(OSCAR_EUNSUPPORTED, "head counts %d/%d unsupported", n_q_heads, n_kv_heads);
+  if (!(clip_quantile > 0.0 && clip_quantile <= 1.0)) return fail(OSCAR_EINVAL, "clip_quantile must be in (0, 1]");
+  if (int rc = check_device()) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int D = oscar::D;
+  const int64_t nq = n_tokens * n_q_heads, nkv = n_tokens * n_kv_heads;
+  double *cov = nullptr, *o = nullptr, *Rd = nullptr, *y = nullptr;
+  int rc = OSCAR_OK;
+  std::vector<double> cq(D * D), cs(D * D);
+  hipError_t e;
+  auto cleanup = [&]() {
+    if (cov) (void)hipFree(cov);
+    if (o) (void)hipFree(o);
+    if (Rd) (void)hipFree(Rd);
+    if (y) (void)hipFree(y);
+  };
+#define CHECK_HIP(expr, where)       \
+  do {                               \
+    e = (expr);                      \
+    if (e != hipSuccess) {           \
+      rc = hip_fail(e, where);       \
+      cleanup();                     \
+      return rc;                     \
+    }                                \
+  } while (0)
+  CHECK_HIP(hipMalloc(&cov, 2 * D * D * sizeof(double)), "hipMalloc");
+  CHECK_HIP(hipMalloc(&o, size_t(nq) * D * sizeof(double)), "hipMalloc");
+  CHECK_HIP(hipMalloc(&Rd, D * D * sizeof(double)), "hipMalloc");
+  CHECK_HIP(hipMalloc(&y, size_t(nkv) * D * sizeof(double)), "hipMalloc");
+  CHECK_HIP(oscar::launch_calib_outer(q_cal, nullptr, nq, cov, s), "calib C_Q");
+  CHECK_HIP(oscar::launch_calib_attention(q_cal, k_cal, v_cal, n_tokens, n_q_heads, n_kv_heads, o, s), "calib attention");
+  CHECK_HIP(oscar::launch_calib_outer(nullptr, o, nq, cov + D * D, s), "calib C_S");
+  CHECK_HIP(hipMemcpyAsync(cq.data(), cov, D * D * sizeof(double), hipMemcpyDeviceToHost, s), "copy C_Q");
+  CHECK_HIP(hipMemcpyAsync(cs.data(), cov + D * D, D * D * sizeof(double), hipMemcpyDeviceToHost, s), "copy C_S");
+  CHECK_HIP(hipStreamSynchronize(s), "sync");
+  for (auto &x : cq) x /= double(nq);
+  for (auto &x : cs) x /= double(nq);
+  std::vector<double> U, Rk, Rv, absv(size_t(nkv) * D);
+  oscar::eigenbasis(cq, D, U);
+  oscar::compose_rotation(U, Rk);
+  oscar::eigenbasis(cs, D, U);
+  oscar::compose_rotation(U, Rv);
+  double clips[2];
+  const uint16_t *xs[2] = {k_cal, v_cal};
+  const std::vector<double> *Rs[2] = {&Rk, &Rv};
+  for (int t = 0; t < 2; ++t) {
+    CHECK_HIP(hipMemcpyAsync(Rd, Rs[t]->data(), D * D * sizeof(double), hipMemcpyHostToDevice, s), "copy R");
+    CHECK_HIP(oscar::launch_calib_rotate_abs(xs[t], nkv, Rd, y, s), "calib |x R|");
+    CHECK_HIP(hipMemcpyAsync(absv.data(), y, absv.size() * sizeof(double), hipMemcpyDeviceToHost, s), "copy |x R|");
+    CHECK_HIP(hipStreamSynchronize(s), "sync");
+    clips[t] = oscar::quantile_linear(absv, clip_quantile);
+  }
+#undef CHECK_HIP
+  cleanup();
+  std::memcpy(R_K, Rk.data(), D * D * sizeof(double));
+  std::memcpy(R_V, Rv.data(), D * D * sizeof(double));
+  *clip_K = float(clips[0]);
+  *clip_V = float(clips[1]);
+  return OSCAR_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// Internal definitions shared by the liboscar kernels and host code.
+// Storage formats are the ones declared in include/oscar.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "oscar.h"
+
+namespace oscar {
+
+constexpr int D = OSCAR_HEAD_DIM;     // 128
+constexpr int PAGE = OSCAR_PAGE;      // 16
+constexpr int N_SINK = OSCAR_N_SINK;  // 16
+constexpr int N_RECENT = OSCAR_N_RECENT;
+constexpr int N_RAW = N_SINK + N_RECENT;  // 144 raw bf16 tokens at most
+constexpr int BF16_PT = OSCAR_BF16_PAGES_PER_REQ;
+constexpr int CODE_BYTES = 512;       // one code area: 16 rows x 128 codes x 2 bits
+
+// Byte offsets inside the forms buffer of one rotation.
+constexpr size_t FORM_R = 0;                        // fp32 R[i][j]
+constexpr size_t FORM_RT = FORM_R + D * D * 4;      // fp32 RT[j][i] = R[i][j]
+constexpr size_t FORM_RT_HI = FORM_RT + D * D * 4;  // fp16 hi(R[i][j]) at [j][i]
+constexpr size_t FORM_RT_LO = FORM_RT_HI + D * D * 2;  // fp16 2^11 * (R - hi)
+constexpr size_t FORM_BYTES = FORM_RT_LO + D * D * 2;
+
+__host__ __device__ inline int n_groups(int G) { return D / G; }
+__host__ __device__ inline int meta_bytes(int G) { return 64 * (D / G); }
+__host__ __device__ inline int hist_block_bytes(int G) { return 1024 + 128 * (D / G); }
+__host__ __device__ inline int k_codes_off(int) { return 0; }
+__host__ __device__ inline int k_meta_off(int) { return CODE_BYTES; }
+__host__ __device__ inline int v_codes_off(int G) { return CODE_BYTES + meta_bytes(G); }
+__host__ __device__ inline int v_meta_off(int G) { return 2 * CODE_BYTES + meta_bytes(G); }
+
+// Slot bit tables of a code dword (first code at LO[u], second at HI[u]).
+__host__ __device__ inline int slot_lo(int u) {
+  const int t[8] = {8, 6, 12, 10, 4, 2, 16, 14};
+  return t[u];
+}
+__host__ __device__ inline int slot_hi(int u) {
+  const int t[8] = {24, 22, 28, 26, 20, 18, 0, 30};
+  return t[u];
+}
+
+// (word, bit) of the K code of (row t, channel c).
+__host__ __device__ inline void k_code_pos(int t, int c, int &word, int &bit) {
+  const int k = c >> 5, cb = c & 31;
+  const int q = cb >> 3, v = (cb & 7) >> 1;
+  const int d = k >> 1, u = 4 * (k & 1) + v;
+  word = 2 * (16 * q + t) + d;
+  bit = (c & 1) ? slot_hi(u) : slot_lo(u);
+}
+
+// (word, bit) of the V code of (row t, channel c).
+__host__ __device__ inline void v_code_pos(int t, int c, int &word, int &bit) {
+  const int r = c >> 4, m = c & 15;
+  const int d = r >> 2, u = 2 * (r & 3) + ((t & 3) >> 1);
+  const int q = t >> 2;
+  word = 2 * (16 * q + m) + d;
+  bit = (t & 1) ? slot_hi(u) : slot_lo(u);
+}
+
+__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+__device__ inline void flag_status(uint32_t *status, uint32_t bit) {
+  if (status) atomicOr(status, bit);
+}
+
+// history tokens / pages of a request of length L
+__host__ __device__ inline int n_hist_tokens(int L) { return L > N_RAW ? L - N_RAW : 0; }
+__host__ __device__ inline int n_hist_pages(int L) { return (n_hist_tokens(L) + PAGE - 1) / PAGE; }
+
+// Decode split plan shared by the workspace sizing and the launch.
+struct SplitPlan {
+  int pages_per_split;  // history pages per split
+  int n_splits;         // history splits (the BF16 part is one more)
+};
+
+SplitPlan plan_int2_splits(int batch, int n_kv_heads, int max_seq_len);
+SplitPlan plan_bf16_splits(int batch, int n_kv_heads, int max_seq_len);
+
+}  // namespace oscar

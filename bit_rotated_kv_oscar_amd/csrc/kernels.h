@@ -1,0 +1,48 @@
+// Host-side launchers of the liboscar kernels (implemented in the .hip files).
+// They assume validated arguments; api.cpp validates.
+#pragma once
+
+#include "common.h"
+
+namespace oscar {
+
+struct RotArg {
+  const uint8_t *forms;  // device forms of one rotation (FORM_* offsets)
+  float clip;
+};
+
+hipError_t launch_prepare_rotation(const double *R, void *forms, hipStream_t s);
+
+hipError_t launch_write_kv(const oscar_layer_cache &c, RotArg rk, RotArg rv,
+                           const uint16_t *k_new, const uint16_t *v_new,
+                           const int32_t *cu_new, const int32_t *len_before,
+                           int batch, int64_t total_tokens, int max_new, hipStream_t s);
+
+hipError_t launch_decode_int2(const oscar_layer_cache &c, RotArg rk, RotArg rv,
+                              const uint16_t *q, int n_q_heads,
+                              const int32_t *seq_lens, int batch, int max_seq_len,
+                              float sm_scale, float *out, void *ws, hipStream_t s);
+
+size_t decode_int2_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int max_seq_len);
+
+hipError_t launch_decode_bf16(const uint16_t *q, const uint16_t *kv, int64_t n_pages,
+                              const int32_t *pt, int pt_stride, const int32_t *seq_lens,
+                              int batch, int max_seq_len, int n_q_heads, int n_kv_heads,
+                              float sm_scale, float *out, uint32_t *status, void *ws,
+                              hipStream_t s);
+
+size_t decode_bf16_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int max_seq_len);
+
+// Calibration moments (device fp64).
+// cov_q[128][128] += sum over (token, head) of q q^T  (not yet divided by N*Hq)
+hipError_t launch_calib_outer(const uint16_t *x_bf16, const double *x_f64, int64_t n_vec,
+                              double *cov, hipStream_t s);
+// o[N][Hq][128] (fp64) = causal softmax(q k^T / sqrt(128)) v per query head
+hipError_t launch_calib_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                  int64_t n_tokens, int n_q_heads, int n_kv_heads,
+                                  double *o, hipStream_t s);
+// y[n][128] = |x[n] R| (fp64), x bf16 [n][128]
+hipError_t launch_calib_rotate_abs(const uint16_t *x, int64_t n_vec, const double *R,
+                                   double *y, hipStream_t s);
+
+}  // namespace oscar

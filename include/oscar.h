@@ -31,6 +31,12 @@
 extern "C" {
 #endif
 
+#if defined(__GNUC__)
+#define OSCAR_API __attribute__((visibility("default")))
+#else
+#define OSCAR_API
+#endif
+
 /* hipStream_t without the HIP headers: an opaque stream handle (NULL = the
  * default stream). */
 typedef struct ihipStream_t *oscar_stream_t;
@@ -130,20 +136,20 @@ typedef struct oscar_rotation {
   float clip;              /* > 0 and finite; values clamp to [-clip, clip]  */
 } oscar_rotation;
 
-const char *oscar_last_error(void);
-const char *oscar_version(void);
+OSCAR_API const char *oscar_last_error(void);
+OSCAR_API const char *oscar_version(void);
 
 /* Bytes of one history block for group size G (0 if G is unsupported). */
-size_t oscar_hist_block_bytes(int32_t group);
+OSCAR_API size_t oscar_hist_block_bytes(int32_t group);
 
 /* Bytes of the device buffer that holds the forms of one rotation. */
-size_t oscar_rotation_bytes(void);
+OSCAR_API size_t oscar_rotation_bytes(void);
 
 /* Converts R (device fp64 [128][128], row-major, R[i][j]) into the device
  * forms the kernels read (fp32 R and R^T, and R^T split into an fp16 high
  * part plus a 2^11-scaled fp16 low part for the matrix cores).
  * forms: device buffer of oscar_rotation_bytes(). */
-int oscar_prepare_rotation(const double *R, void *forms, oscar_stream_t stream);
+OSCAR_API int oscar_prepare_rotation(const double *R, void *forms, oscar_stream_t stream);
 
 /* Offline calibration ([nl] §2.2.A, [fr] §2.2.A, [abs]):
  *   C_Q = mean over tokens and query heads of the outer product q q^T;
@@ -161,7 +167,7 @@ int oscar_prepare_rotation(const double *R, void *forms, oscar_stream_t stream);
  * [n_tokens][Hkv][128].  Outputs R_K, R_V (host fp64 [128][128]) and
  * clip_K, clip_V (host).  Synchronises the stream; allocates and frees its
  * own device scratch.  n_tokens in [1, 65536], clip_quantile in (0, 1]. */
-int oscar_calibrate_rotation(const uint16_t *q_cal, const uint16_t *k_cal,
+OSCAR_API int oscar_calibrate_rotation(const uint16_t *q_cal, const uint16_t *k_cal,
                              const uint16_t *v_cal, int64_t n_tokens,
                              int32_t n_q_heads, int32_t n_kv_heads,
                              double clip_quantile, double *R_K, double *R_V,
@@ -181,7 +187,7 @@ int oscar_calibrate_rotation(const uint16_t *q_cal, const uint16_t *k_cal,
  * cu_new: device int32 [batch+1]; len_before: device int32 [batch].
  * max_new: host upper bound of n_b (sizes the grid).  History pages a call
  * writes must not be shared with another live request (caller's duty). */
-int oscar_write_kv(const oscar_layer_cache *cache, const oscar_rotation *rot_k,
+OSCAR_API int oscar_write_kv(const oscar_layer_cache *cache, const oscar_rotation *rot_k,
                    const oscar_rotation *rot_v, const uint16_t *k_new,
                    const uint16_t *v_new, const int32_t *cu_new,
                    const int32_t *len_before, int32_t batch,
@@ -189,7 +195,7 @@ int oscar_write_kv(const oscar_layer_cache *cache, const oscar_rotation *rot_k,
                    oscar_stream_t stream);
 
 /* Workspace for oscar_decode_attn (device, any alignment >= 256 B). */
-size_t oscar_decode_workspace_bytes(int32_t batch, int32_t n_q_heads,
+OSCAR_API size_t oscar_decode_workspace_bytes(int32_t batch, int32_t n_q_heads,
                                     int32_t n_kv_heads, int32_t max_seq_len);
 
 /* Mixed-precision paged decode attention ([nl]/[fr] §2.2.B "kernel
@@ -201,7 +207,7 @@ size_t oscar_decode_workspace_bytes(int32_t batch, int32_t n_q_heads,
  * KV head h / (Hq/Hkv).
  * q: device bf16 [batch][Hq][128]; seq_lens: device int32 [batch], each in
  * [1, max_seq_len]; out: device fp32 [batch][Hq][128]. */
-int oscar_decode_attn(const oscar_layer_cache *cache,
+OSCAR_API int oscar_decode_attn(const oscar_layer_cache *cache,
                       const oscar_rotation *rot_k, const oscar_rotation *rot_v,
                       const uint16_t *q, int32_t n_q_heads,
                       const int32_t *seq_lens, int32_t batch,
@@ -210,7 +216,7 @@ int oscar_decode_attn(const oscar_layer_cache *cache,
                       oscar_stream_t stream);
 
 /* Workspace for oscar_bf16_paged_decode. */
-size_t oscar_bf16_decode_workspace_bytes(int32_t batch, int32_t n_q_heads,
+OSCAR_API size_t oscar_bf16_decode_workspace_bytes(int32_t batch, int32_t n_q_heads,
                                          int32_t n_kv_heads,
                                          int32_t max_seq_len);
 
@@ -220,7 +226,7 @@ size_t oscar_bf16_decode_workspace_bytes(int32_t batch, int32_t n_q_heads,
  * the BF16 pool); pt: device int32 [batch][pt_stride] — token p of request
  * b is row p%16 of page pt[b][p/16]; other arguments as oscar_decode_attn.
  * status: device uint32 or NULL (OSCAR_STATUS_* bits). */
-int oscar_bf16_paged_decode(const uint16_t *q, const uint16_t *kv_pages,
+OSCAR_API int oscar_bf16_paged_decode(const uint16_t *q, const uint16_t *kv_pages,
                             int64_t n_pages, const int32_t *pt,
                             int32_t pt_stride, const int32_t *seq_lens,
                             int32_t batch, int32_t max_seq_len,

@@ -383,28 +383,30 @@ class LayerCacheRef:
                 self.bf16[pg, :, 1, row, :] = vx
             if not hist_pos:
                 continue
-            # quantise every history-bound token, then store page by page
-            xs_k = np.stack([bf16_to_f64(src[p][0]) for p, _ in hist_pos])  # [n][Hkv][128]
-            xs_v = np.stack([bf16_to_f64(src[p][1]) for p, _ in hist_pos])
+            # quantise every history-bound token, then store them page by page
+            hidx = np.array([idx for _, idx in hist_pos])
+            pages, rows = hidx // PAGE, hidx % PAGE
+            upages = np.unique(pages)
+            slot = np.searchsorted(upages, pages)
+            pids = self.hist_pt[b, upages]
+            xs = {"k": np.stack([bf16_to_f64(src[p][0]) for p, _ in hist_pos]),  # [n][Hkv][128]
+                  "v": np.stack([bf16_to_f64(src[p][1]) for p, _ in hist_pos])}
+            rot = {"k": (rot_k, clip_k), "v": (rot_v, clip_v)}
             for h in range(self.hkv):
-                qk = quantize(xs_k[:, h, :], rot_k, clip_k, G)
-                qv = quantize(xs_v[:, h, :], rot_v, clip_v, G)
-                by_page = {}
-                for j, (_, hidx) in enumerate(hist_pos):
-                    by_page.setdefault(hidx // PAGE, []).append((j, hidx % PAGE))
-                for page, rows in by_page.items():
-                    pid = int(self.hist_pt[b, page])
-                    areas = split_block(self.hist[pid, h], G)
-                    for kind, qq in (("k", qk), ("v", qv)):
-                        codes = unpack_codes(areas[kind + "_codes"], kind.upper())
-                        s, z = unpack_meta(areas[kind + "_meta"], G)
-                        s, z = s.copy(), z.copy()
-                        for j, row in rows:
-                            codes[row] = qq["codes"][j]
-                            s[row] = qq["scale"][j]
-                            z[row] = qq["zero"][j]
-                        areas[kind + "_codes"][:] = pack_codes(codes, kind.upper())
-                        areas[kind + "_meta"][:] = pack_meta(s, z)
+                blocks = self.hist[pids, h].copy()          # [P][block]
+                areas = split_block(blocks, G)
+                for kind in ("k", "v"):
+                    R, clip = rot[kind]
+                    qq = quantize(xs[kind][:, h, :], R, clip, G)
+                    codes = unpack_codes(areas[kind + "_codes"], kind.upper())
+                    sc, zr = unpack_meta(areas[kind + "_meta"], G)
+                    sc, zr = sc.copy(), zr.copy()
+                    codes[slot, rows] = qq["codes"]
+                    sc[slot, rows] = qq["scale"]
+                    zr[slot, rows] = qq["zero"]
+                    areas[kind + "_codes"][:] = pack_codes(codes, kind.upper())
+                    areas[kind + "_meta"][:] = pack_meta(sc, zr)
+                self.hist[pids, h] = blocks
 
     # ---- reconstruction for the decode
     def gather(self, b: int, L: int, rot_k: np.ndarray, rot_v: np.ndarray):
@@ -413,30 +415,30 @@ class LayerCacheRef:
         G = self.G
         K = np.empty((L, self.hkv, D))
         V = np.empty((L, self.hkv, D))
-        hist = []
-        for p in range(L):
-            w, idx = storage_of(p, L)
-            if w == "hist":
-                hist.append((p, idx))
-                continue
-            pg, row = self._bf16_row(b, w, idx)
-            K[p] = bf16_to_f64(self.bf16[pg, :, 0, row, :])
-            V[p] = bf16_to_f64(self.bf16[pg, :, 1, row, :])
+        where = [storage_of(p, L) for p in range(L)]
+        raw = [(p, self._bf16_row(b, w, idx)) for p, (w, idx) in enumerate(where) if w != "hist"]
+        if raw:
+            pos = np.array([p for p, _ in raw])
+            pg = np.array([r[0] for _, r in raw])
+            row = np.array([r[1] for _, r in raw])
+            K[pos] = bf16_to_f64(self.bf16[pg, :, 0, row, :])
+            V[pos] = bf16_to_f64(self.bf16[pg, :, 1, row, :])
+        hist = [(p, idx) for p, (w, idx) in enumerate(where) if w == "hist"]
         if hist:
-            pages = sorted({idx // PAGE for _, idx in hist})
-            decoded = {}
-            for page in pages:
-                pid = int(self.hist_pt[b, page])
-                for h in range(self.hkv):
-                    areas = split_block(self.hist[pid, h], G)
-                    for kind, R in (("k", rot_k), ("v", rot_v)):
-                        c = unpack_codes(areas[kind + "_codes"], kind.upper())
-                        s, z = unpack_meta(areas[kind + "_meta"], G)
-                        decoded[(page, h, kind)] = dequantize(c, s, z, G) @ R.T
-            for p, idx in hist:
-                for h in range(self.hkv):
-                    K[p, h] = decoded[(idx // PAGE, h, "k")][idx % PAGE]
-                    V[p, h] = decoded[(idx // PAGE, h, "v")][idx % PAGE]
+            pos = np.array([p for p, _ in hist])
+            hidx = np.array([idx for _, idx in hist])
+            pages, rows = hidx // PAGE, hidx % PAGE
+            upages = np.unique(pages)
+            slot = np.searchsorted(upages, pages)
+            pids = self.hist_pt[b, upages]
+            for h in range(self.hkv):
+                areas = split_block(self.hist[pids, h], G)
+                for kind, R, out in (("k", rot_k, K), ("v", rot_v, V)):
+                    c = unpack_codes(areas[kind + "_codes"], kind.upper())      # [P][16][128]
+                    sc, zr = unpack_meta(areas[kind + "_meta"], G)             # [P][16][NG]
+                    n = c.shape[0] * PAGE
+                    x = dequantize(c.reshape(n, D), sc.reshape(n, -1), zr.reshape(n, -1), G) @ R.T
+                    out[pos, h] = x.reshape(-1, PAGE, D)[slot, rows]
         return K, V
 
 

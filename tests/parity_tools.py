@@ -1,0 +1,179 @@
+"""Helpers of the GPU parity tests: build seeded scenarios on both sides and
+compare results under the tolerances of the workload's specification.
+
+Write parity (two levels):
+  1. fp16 scale and zero equal the oracle's, except +-1 fp16 ulp where the
+     oracle's unrounded value lies within 1e-6 (relative) of the midpoint
+     between the two candidates;
+  2. codes equal the oracle's codes recomputed with the GPU's scale and zero,
+     except where the oracle's t = (xc - z)/s lies within 1e-4 code units of
+     a rounding boundary k + 1/2; at most 1e-5 of all codes may differ.
+Decode parity: max |gpu - oracle| <= 2e-2 and ||gpu - oracle||_2 /
+||oracle||_2 <= 5e-3 over all (request, head, channel).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import synth
+from oracle import oscar_ref as o
+
+ABS_TOL = 2e-2
+REL_L2_TOL = 5e-3
+CODE_BAND = 1e-4
+CODE_RATE = 1e-5
+META_REL = 1e-6
+
+
+def to_dev_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def bf16_pool_bits(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def random_rotation(seed: int) -> np.ndarray:
+    R, _ = np.linalg.qr(np.random.default_rng(seed).standard_normal((128, 128)))
+    return R
+
+
+def calibrated(ld: synth.LayerData, n_cal: int = 2048):
+    """Oracle calibration of a layer; clips rounded to fp32 (what the kernels use)."""
+    qc, kc, vc = ld.calibration(n_cal)
+    cal = o.calibrate(o.bf16_to_f64(qc), o.bf16_to_f64(kc), o.bf16_to_f64(vc))
+    return cal["R_K"], cal["R_V"], float(np.float32(cal["clip_K"])), float(np.float32(cal["clip_V"]))
+
+
+def decode_error(gpu: np.ndarray, ref: np.ndarray):
+    d = gpu.astype(np.float64) - ref
+    return float(np.abs(d).max()), float(np.linalg.norm(d) / np.linalg.norm(ref))
+
+
+def assert_decode_close(gpu: np.ndarray, ref: np.ndarray, what: str = "decode"):
+    mx, rel = decode_error(gpu, ref)
+    assert mx <= ABS_TOL and rel <= REL_L2_TOL, f"{what}: max abs {mx:.3e}, rel L2 {rel:.3e}"
+    return mx, rel
+
+
+def _f16_neighbours_ok(gpu: np.ndarray, ref: np.ndarray, unrounded: np.ndarray) -> np.ndarray:
+    """True where gpu == ref, or they are adjacent fp16 values and the
+    unrounded fp64 value is within META_REL of their midpoint."""
+    g = gpu.astype(np.float16)
+    r = ref.astype(np.float16)
+    same = g.view(np.uint16) == r.view(np.uint16)
+    adj = np.abs(g.view(np.uint16).astype(np.int32) - r.view(np.uint16).astype(np.int32)) == 1
+    mid = (g.astype(np.float64) + r.astype(np.float64)) / 2
+    near = np.abs(unrounded - mid) <= META_REL * np.maximum(np.abs(unrounded), 1e-30)
+    return same | (adj & near)
+
+
+def compare_history(gpu_hist: np.ndarray, hist_pt: np.ndarray, tokens_k, tokens_v, lens,
+                    R_K, R_V, clip_k, clip_v, G: int, positions=None) -> dict:
+    """Two-level comparison of every history row of every request.
+
+    tokens_k/v[b]: bf16 bits [L_b][Hkv][128] of request b (all positions).
+    positions[b] (optional): subset of history positions to check.
+    """
+    stats = {"codes": 0, "raw_code_mismatch": 0, "code_out_of_band": 0, "meta": 0,
+             "meta_differ": 0, "meta_out_of_tol": 0}
+    hkv = gpu_hist.shape[1]
+    for b, L in enumerate(lens):
+        hist_p = np.arange(o.N_SINK, max(o.N_SINK, L - o.N_RECENT))
+        if positions is not None:
+            hist_p = np.asarray(positions[b])
+        if hist_p.size == 0:
+            continue
+        hidx = hist_p - o.N_SINK
+        pids = hist_pt[b, hidx // o.PAGE]
+        rows = hidx % o.PAGE
+        for kind, toks, R, clip in (("K", tokens_k[b], R_K, clip_k), ("V", tokens_v[b], R_V, clip_v)):
+            for h in range(hkv):
+                x = o.bf16_to_f64(toks[hist_p, h, :])
+                q = o.quantize(x, R, clip, G)
+                areas = o.split_block(gpu_hist[pids, h], G)
+                codes_all = o.unpack_codes(areas[kind.lower() + "_codes"], kind)   # [n][16][128]
+                s_all, z_all = o.unpack_meta(areas[kind.lower() + "_meta"], G)
+                ar = np.arange(len(rows))
+                gc, gs, gz = codes_all[ar, rows], s_all[ar, rows], z_all[ar, rows]
+                ng = 128 // G
+                xg = q["xc"].reshape(-1, ng, G)
+                lo, hi = xg.min(axis=2), xg.max(axis=2)
+                ok_s = _f16_neighbours_ok(gs, q["scale"], (hi - lo) / 3.0)
+                ok_z = _f16_neighbours_ok(gz, q["zero"], lo)
+                stats["meta"] += 2 * gs.size
+                stats["meta_differ"] += int((gs != q["scale"]).sum() + (gz != q["zero"]).sum())
+                stats["meta_out_of_tol"] += int((~ok_s).sum() + (~ok_z).sum())
+                ref_codes, t = o.codes_from_meta(q["xc"], gs, gz, G)
+                diff = gc != ref_codes
+                frac = t - np.floor(t)
+                near = np.abs(frac - 0.5) < CODE_BAND
+                stats["codes"] += gc.size
+                stats["raw_code_mismatch"] += int((gc != q["codes"]).sum())
+                stats["code_out_of_band"] += int((diff & ~np.nan_to_num(near, nan=False)).sum())
+                stats.setdefault("code_in_band", 0)
+                stats["code_in_band"] += int((diff & np.nan_to_num(near, nan=False)).sum())
+    return stats
+
+
+def assert_history_ok(stats: dict):
+    """No meta outside the midpoint rule, no code flip outside the 1e-4 band,
+    in-band flips at a rate <= 1e-5 (at least one allowed in small cases)."""
+    assert stats["meta_out_of_tol"] == 0, stats
+    assert stats["code_out_of_band"] == 0, stats
+    assert stats.get("code_in_band", 0) <= max(1, CODE_RATE * stats["codes"]), stats
+
+
+class Scenario:
+    """Seeded requests written by the oracle (numpy pools) with shuffled page tables."""
+
+    def __init__(self, seed: int, hq: int, hkv: int, G: int, lens, rot="random", n_cal=2048, layer=0,
+                 spare_pages=3):
+        self.seed, self.hq, self.hkv, self.G = seed, hq, hkv, G
+        self.lens = [int(x) for x in lens]
+        self.ld = synth.LayerData(seed, layer, hq, hkv)
+        if rot == "calibrated":
+            self.R_K, self.R_V, self.clip_k, self.clip_v = calibrated(self.ld, n_cal)
+        else:
+            self.R_K, self.R_V = random_rotation(seed), random_rotation(seed + 1)
+            self.clip_k = self.clip_v = 6.0
+        total = sum(self.lens)
+        k, v = self.ld.cache_kv(total)
+        cu = np.concatenate([[0], np.cumsum(self.lens)]).astype(np.int32)
+        self.k, self.v, self.cu = k, v, cu
+        self.tok_k = [k[cu[b]:cu[b + 1]] for b in range(len(self.lens))]
+        self.tok_v = [v[cu[b]:cu[b + 1]] for b in range(len(self.lens))]
+        need = sum(synth.hist_pages_needed(L) for L in self.lens)
+        self.hist_pt, self.n_hist_pages = synth.shuffled_page_tables(seed, layer, self.lens,
+                                                                     n_pool_pages=need + spare_pages)
+        self.bf16_pt = synth.bf16_page_tables(len(self.lens), shuffle_seed=seed + 7)
+        self.n_bf16_pages = 9 * len(self.lens)
+        self.q = self.ld.decode_q(len(self.lens))
+
+    def oracle_cache(self, chunks=None) -> o.LayerCacheRef:
+        ref = o.LayerCacheRef(self.hkv, self.G, self.n_hist_pages, self.n_bf16_pages, self.hist_pt, self.bf16_pt)
+        for cu, lb, k, v in self.write_calls(chunks):
+            ref.write(self.R_K, self.R_V, self.clip_k, self.clip_v, k, v, cu, lb)
+        return ref
+
+    def write_calls(self, chunks=None):
+        """Write calls (cu_new, len_before, k rows, v rows).  chunks: list of
+        cut lists per call shared by all requests (positions), default one call."""
+        if chunks is None:
+            return [(self.cu, np.zeros(len(self.lens), np.int32), self.k, self.v)]
+        calls = []
+        for lo, hi in zip(chunks[:-1], chunks[1:]):
+            ks, vs, cu, lb = [], [], [0], []
+            for b, L in enumerate(self.lens):
+                a, e = min(lo, L), min(hi, L)
+                ks.append(self.tok_k[b][a:e])
+                vs.append(self.tok_v[b][a:e])
+                cu.append(cu[-1] + (e - a))
+                lb.append(a)
+            calls.append((np.array(cu, np.int32), np.array(lb, np.int32), np.concatenate(ks), np.concatenate(vs)))
+        return calls
+
+    def oracle_decode(self, ref: o.LayerCacheRef, sm_scale=None) -> np.ndarray:
+        sm_scale = sm_scale or 1.0 / np.sqrt(128)
+        return o.decode_attn(ref, self.R_K, self.R_V, self.q, self.lens, sm_scale)

@@ -1,0 +1,183 @@
+"""CPU checks of the C ABI: the library loads, exports every function the
+header declares, the ctypes structs match the C layout, and invalid arguments
+return the documented error codes without launching anything."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import torch
+
+import bit_rotated_kv_oscar_amd as oscar
+from bit_rotated_kv_oscar_amd import _lib
+
+# The calls below pass fake device addresses.  Those with otherwise valid
+# arguments would launch kernels, so they only run where no GPU is visible.
+NO_GPU = not torch.cuda.is_available()
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "oscar.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"OSCAR_API\s+[\w\s\*]*?\b(oscar_\w+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    names = header_functions()
+    for required in ("oscar_calibrate_rotation", "oscar_write_kv", "oscar_decode_attn",
+                     "oscar_bf16_paged_decode", "oscar_prepare_rotation", "oscar_last_error"):
+        assert required in names
+
+
+def test_library_exports_every_header_function():
+    lib = _lib.load()
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (oscar_\w+)", out))
+    for name in header_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    assert {n for n, _, _ in _lib.SIGNATURES} == set(header_functions())
+
+
+def test_struct_layout_matches_c():
+    src = r"""
+    #include <stdio.h>
+    #include <stddef.h>
+    #include "oscar.h"
+    int main(void) {
+      printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(oscar_layer_cache),
+        offsetof(oscar_layer_cache, group), offsetof(oscar_layer_cache, hist),
+        offsetof(oscar_layer_cache, n_hist_pages), offsetof(oscar_layer_cache, bf16),
+        offsetof(oscar_layer_cache, n_bf16_pages), offsetof(oscar_layer_cache, hist_pt),
+        offsetof(oscar_layer_cache, hist_pt_stride), offsetof(oscar_layer_cache, bf16_pt),
+        offsetof(oscar_layer_cache, status), sizeof(oscar_rotation));
+      return 0;
+    }
+    """
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        exe = os.path.join(d, "t")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        vals = [int(x) for x in subprocess.run([exe], capture_output=True, text=True).stdout.split()]
+    L = _lib.LayerCacheC
+    expect = [ctypes.sizeof(L), L.group.offset, L.hist.offset, L.n_hist_pages.offset, L.bf16.offset,
+              L.n_bf16_pages.offset, L.hist_pt.offset, L.hist_pt_stride.offset, L.bf16_pt.offset,
+              L.status.offset, ctypes.sizeof(_lib.RotationC)]
+    assert vals == expect
+
+
+def test_sizes():
+    assert [oscar.hist_block_bytes(g) for g in (32, 64, 128)] == [1536, 1280, 1152]
+    assert oscar.hist_block_bytes(48) == 0
+    assert oscar.rotation_bytes() == 196608
+    assert oscar.decode_workspace_bytes(1, 32, 8, 32768) > 0
+    assert oscar.decode_workspace_bytes(0, 32, 8, 32768) == 0
+    assert oscar.bf16_decode_workspace_bytes(64, 32, 8, 32768) > 0
+
+
+def _cache(**kw):
+    c = _lib.LayerCacheC(2, 32, 0x1000, 4, 0x2000, 9, 0x3000, 1, 0x4000, 0)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+ROT = _lib.RotationC(0x5000, 4.0)
+
+
+def _write(c=None, rk=ROT, rv=ROT, k=0x6000, v=0x7000, cu=0x8000, lb=0x9000, batch=1, total=16, max_new=16):
+    lib = _lib.load()
+    c = c if c is not None else _cache()
+    return lib.oscar_write_kv(ctypes.byref(c), ctypes.byref(rk), ctypes.byref(rv), k, v, cu, lb, batch,
+                              total, max_new, None)
+
+
+def _err():
+    return _lib.load().oscar_last_error().decode()
+
+
+def test_write_validation_codes():
+    E = _lib
+    assert _write(c=_cache(group=48)) == E.OSCAR_EUNSUPPORTED and "group" in _err()
+    assert _write(c=_cache(n_kv_heads=0)) == E.OSCAR_EINVAL
+    assert _write(c=_cache(hist=0)) == E.OSCAR_EINVAL
+    assert _write(c=_cache(bf16_pt=0)) == E.OSCAR_EINVAL
+    assert _write(c=_cache(hist_pt_stride=0)) == E.OSCAR_EINVAL
+    assert _write(rk=_lib.RotationC(0x5000, float("nan"))) == E.OSCAR_EINVAL and "clip" in _err()
+    assert _write(rk=_lib.RotationC(0x5000, -1.0)) == E.OSCAR_EINVAL
+    assert _write(rv=_lib.RotationC(0x5000, 1e6)) == E.OSCAR_EINVAL
+    assert _write(rv=_lib.RotationC(0, 1.0)) == E.OSCAR_EINVAL
+    assert _write(batch=0) == E.OSCAR_EINVAL
+    assert _write(max_new=32, total=16) == E.OSCAR_EINVAL
+    assert _write(k=0) == E.OSCAR_EINVAL
+    assert _write(cu=0) == E.OSCAR_EINVAL
+    # nothing to write: success without touching a device
+    assert _write(max_new=0, total=0, k=0, v=0) == E.OSCAR_OK
+    if NO_GPU:  # valid arguments, no device: refused before any launch
+        assert _write() == E.OSCAR_ENODEV
+
+
+def _decode(c=None, hq=8, batch=1, max_len=150, ws=0xA000, ws_bytes=1 << 30, scale=0.088, q=0xB000):
+    lib = _lib.load()
+    c = c if c is not None else _cache()
+    return lib.oscar_decode_attn(ctypes.byref(c), ctypes.byref(ROT), ctypes.byref(ROT), q, hq, 0xC000, batch,
+                                 max_len, scale, 0xD000, ws, ws_bytes, None)
+
+
+def test_decode_validation_codes():
+    E = _lib
+    assert _decode(hq=7) == E.OSCAR_EUNSUPPORTED and "multiple" in _err()
+    assert _decode(hq=64) == E.OSCAR_EUNSUPPORTED            # GQA 32 > 16
+    assert _decode(max_len=0) == E.OSCAR_EINVAL
+    assert _decode(max_len=10_000) == E.OSCAR_EINVAL and "hist_pt_stride" in _err()
+    assert _decode(q=0) == E.OSCAR_EINVAL
+    assert _decode(scale=0.0) == E.OSCAR_EINVAL
+    assert _decode(ws=0) == E.OSCAR_EWORKSPACE
+    assert _decode(ws_bytes=16) == E.OSCAR_EWORKSPACE and "workspace" in _err()
+    assert _decode(batch=0) == E.OSCAR_EINVAL
+    if NO_GPU:
+        assert _decode() == E.OSCAR_ENODEV
+
+
+def test_bf16_decode_validation_codes():
+    lib = _lib.load()
+    E = _lib
+
+    def call(hq=8, hkv=2, pt_stride=4, max_len=64, n_pages=8, ws_bytes=1 << 30, pt=0x1):
+        return lib.oscar_bf16_paged_decode(0x1000, 0x2000, n_pages, pt, pt_stride, 0x3000, 1, max_len, hq, hkv,
+                                           0.088, 0x4000, None, 0x5000, ws_bytes, None)
+    assert call(hq=6, hkv=4) == E.OSCAR_EUNSUPPORTED
+    assert call(pt_stride=3) == E.OSCAR_EINVAL
+    assert call(n_pages=0) == E.OSCAR_EINVAL
+    assert call(pt=0) == E.OSCAR_EINVAL
+    assert call(ws_bytes=0) == E.OSCAR_EWORKSPACE
+    if NO_GPU:
+        assert call() == E.OSCAR_ENODEV
+
+
+def test_calibrate_and_prepare_validation_codes():
+    lib = _lib.load()
+    E = _lib
+    R = (ctypes.c_double * (128 * 128))()
+    f = ctypes.c_float()
+    assert lib.oscar_calibrate_rotation(0, 0x1, 0x1, 16, 8, 2, 0.999, R, R, ctypes.byref(f), ctypes.byref(f),
+                                        None) == E.OSCAR_EINVAL
+    assert lib.oscar_calibrate_rotation(0x1, 0x1, 0x1, 0, 8, 2, 0.999, R, R, ctypes.byref(f), ctypes.byref(f),
+                                        None) == E.OSCAR_EINVAL
+    assert lib.oscar_calibrate_rotation(0x1, 0x1, 0x1, 16, 8, 3, 0.999, R, R, ctypes.byref(f), ctypes.byref(f),
+                                        None) == E.OSCAR_EUNSUPPORTED
+    assert lib.oscar_calibrate_rotation(0x1, 0x1, 0x1, 16, 8, 2, 1.5, R, R, ctypes.byref(f), ctypes.byref(f),
+                                        None) == E.OSCAR_EINVAL
+    assert lib.oscar_prepare_rotation(0, 0x1, None) == E.OSCAR_EINVAL
+
+
+def test_errors_raise_in_binding():
+    with pytest.raises(_lib.OscarError) as ei:
+        _lib.check(_write(c=_cache(group=16)))
+    assert ei.value.code == _lib.OSCAR_EUNSUPPORTED

@@ -1,0 +1,256 @@
+"""GPU parity of liboscar against the fp64 oracle (through the C ABI).
+
+Every case builds seeded inputs with synth/, runs the oracle on the CPU and the
+HIP kernels on cuda:0, and compares under the rules of tests/parity_tools.py.
+Decode cases feed the oracle-written cache to the GPU, so both sides attend
+over identical bytes; write cases compare the GPU-written pools with the
+oracle-written ones.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import oscar_ref as o
+from tests.parity_tools import (Scenario, assert_decode_close, assert_history_ok, bf16_pool_bits,
+                                compare_history, decode_error, to_dev_bf16)
+
+pytestmark = pytest.mark.gpu
+
+SCALE = 1.0 / math.sqrt(128)
+
+
+@pytest.fixture(scope="module")
+def oscar():
+    import bit_rotated_kv_oscar_amd as m
+    return m
+
+
+def gpu_cache(oscar, sc: Scenario, hist=None, bf16=None):
+    dev = torch.device("cuda:0")
+    c = oscar.LayerCache(sc.hkv, sc.G, sc.n_hist_pages, sc.n_bf16_pages, torch.from_numpy(sc.hist_pt),
+                         torch.from_numpy(sc.bf16_pt), device=dev)
+    if hist is not None:
+        c.hist.copy_(torch.from_numpy(hist))
+    if bf16 is not None:
+        c.bf16.view(torch.int16).copy_(torch.from_numpy(bf16.view(np.int16)))
+    return c
+
+
+def gpu_rotations(oscar, sc: Scenario):
+    return oscar.Rotation(sc.R_K, sc.clip_k), oscar.Rotation(sc.R_V, sc.clip_v)
+
+
+def gpu_write(oscar, sc: Scenario, cache, rk, rv, chunks=None):
+    for cu, lb, k, v in sc.write_calls(chunks):
+        n = np.diff(cu)
+        oscar.write_kv(cache, rk, rv, to_dev_bf16(k), to_dev_bf16(v), torch.from_numpy(cu).cuda(),
+                       torch.from_numpy(lb).cuda(), int(n.max()) if n.size else 0)
+    torch.cuda.synchronize()
+
+
+def gpu_decode(oscar, sc: Scenario, cache, rk, rv):
+    lens = torch.tensor(sc.lens, dtype=torch.int32, device="cuda")
+    out = oscar.decode_attn(cache, rk, rv, to_dev_bf16(sc.q), lens, max(sc.lens), SCALE)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check_raw_rows(sc: Scenario, gpu_bf16: np.ndarray, ref: o.LayerCacheRef):
+    """Sink and ring rows in use must be bit-identical."""
+    for b, L in enumerate(sc.lens):
+        for p in range(L):
+            w, idx = o.storage_of(p, L)
+            if w == "hist":
+                continue
+            pg, row = ref._bf16_row(b, w, idx)
+            assert np.array_equal(gpu_bf16[pg, :, :, row, :], ref.bf16[pg, :, :, row, :]), (b, p)
+
+
+# ------------------------------------------------------------------ forms
+
+
+def test_prepare_rotation_forms(oscar):
+    R = np.linalg.qr(np.random.default_rng(3).standard_normal((128, 128)))[0]
+    rot = oscar.Rotation(R, 5.0)
+    f = rot.forms.cpu().numpy()
+    R32 = f[0:65536].view(np.float32).reshape(128, 128)
+    RT32 = f[65536:131072].view(np.float32).reshape(128, 128)
+    hi = f[131072:163840].view(np.float16).reshape(128, 128).astype(np.float64)
+    lo = f[163840:196608].view(np.float16).reshape(128, 128).astype(np.float64)
+    assert np.array_equal(R32, R.astype(np.float32))
+    assert np.array_equal(RT32, R32.T)
+    assert np.abs(hi.T + lo.T / 2048 - R).max() < 2.0 ** -22
+
+
+# ------------------------------------------------------------------ write
+
+
+def test_write_single_layer_calibrated_g32(oscar):
+    # one layer: 8 query / 2 KV heads, 4096 tokens (16 sink + 128 recent + 3952 history), G = 32
+    sc = Scenario(100, 8, 2, 32, [4096], rot="calibrated")
+    ref = sc.oracle_cache()
+    cache = gpu_cache(oscar, sc)
+    rk, rv = gpu_rotations(oscar, sc)
+    gpu_write(oscar, sc, cache, rk, rv)
+    assert int(cache.status.item()) == 0
+    stats = compare_history(cache.hist.cpu().numpy(), sc.hist_pt, sc.tok_k, sc.tok_v, sc.lens,
+                            sc.R_K, sc.R_V, sc.clip_k, sc.clip_v, sc.G)
+    print("write stats", stats)
+    assert_history_ok(stats)
+    check_raw_rows(sc, bf16_pool_bits(cache.bf16), ref)
+
+
+@pytest.mark.parametrize("G", [32, 64, 128])
+def test_write_ragged_batch(oscar, G):
+    lens = [1, 16, 17, 144, 145, 160, 161, 300, 1000]
+    sc = Scenario(200 + G, 8, 2, G, lens)
+    ref = sc.oracle_cache()
+    cache = gpu_cache(oscar, sc)
+    rk, rv = gpu_rotations(oscar, sc)
+    gpu_write(oscar, sc, cache, rk, rv)
+    assert int(cache.status.item()) == 0
+    stats = compare_history(cache.hist.cpu().numpy(), sc.hist_pt, sc.tok_k, sc.tok_v, sc.lens,
+                            sc.R_K, sc.R_V, sc.clip_k, sc.clip_v, G)
+    assert_history_ok(stats)
+    check_raw_rows(sc, bf16_pool_bits(cache.bf16), ref)
+
+
+def test_write_chunks_and_appends(oscar):
+    # prefill in uneven chunks (one longer than the recent window), then
+    # single-token appends: ring tokens leave the window and are quantised
+    lens = [700, 433]
+    chunks = [0, 100, 250, 400] + list(range(401, 440)) + [600, 700]
+    sc = Scenario(300, 8, 2, 64, lens)
+    ref = sc.oracle_cache(chunks)
+    cache = gpu_cache(oscar, sc)
+    rk, rv = gpu_rotations(oscar, sc)
+    gpu_write(oscar, sc, cache, rk, rv, chunks)
+    assert int(cache.status.item()) == 0
+    stats = compare_history(cache.hist.cpu().numpy(), sc.hist_pt, sc.tok_k, sc.tok_v, sc.lens,
+                            sc.R_K, sc.R_V, sc.clip_k, sc.clip_v, sc.G)
+    assert_history_ok(stats)
+    check_raw_rows(sc, bf16_pool_bits(cache.bf16), ref)
+
+
+# ------------------------------------------------------------------ decode
+
+
+@pytest.mark.parametrize("G", [32, 64, 128])
+def test_decode_ragged_batch(oscar, G):
+    lens = [1, 15, 16, 17, 100, 144, 145, 146, 159, 160, 161, 777, 2049]
+    sc = Scenario(400 + G, 8, 2, G, lens)
+    ref = sc.oracle_cache()
+    cache = gpu_cache(oscar, sc, hist=ref.hist, bf16=ref.bf16)
+    rk, rv = gpu_rotations(oscar, sc)
+    out = gpu_decode(oscar, sc, cache, rk, rv)
+    assert int(cache.status.item()) == 0
+    mx, rel = assert_decode_close(out, sc.oracle_decode(ref))
+    print(f"G={G} max abs {mx:.2e} rel {rel:.2e}")
+
+
+def test_decode_single_layer_calibrated(oscar):
+    sc = Scenario(101, 8, 2, 32, [4096], rot="calibrated")
+    ref = sc.oracle_cache()
+    cache = gpu_cache(oscar, sc, hist=ref.hist, bf16=ref.bf16)
+    rk, rv = gpu_rotations(oscar, sc)
+    out = gpu_decode(oscar, sc, cache, rk, rv)
+    mx, rel = assert_decode_close(out, sc.oracle_decode(ref))
+    print(f"max abs {mx:.2e} rel {rel:.2e}")
+
+
+def test_decode_mha_and_gqa8(oscar):
+    for hq, hkv in ((4, 4), (16, 2)):
+        sc = Scenario(500 + hq, hq, hkv, 64, [300, 1500])
+        ref = sc.oracle_cache()
+        cache = gpu_cache(oscar, sc, hist=ref.hist, bf16=ref.bf16)
+        rk, rv = gpu_rotations(oscar, sc)
+        assert_decode_close(gpu_decode(oscar, sc, cache, rk, rv), sc.oracle_decode(ref), f"{hq}/{hkv}")
+
+
+def test_decode_deterministic(oscar):
+    sc = Scenario(600, 8, 2, 64, [3000, 200])
+    ref = sc.oracle_cache()
+    cache = gpu_cache(oscar, sc, hist=ref.hist, bf16=ref.bf16)
+    rk, rv = gpu_rotations(oscar, sc)
+    a = gpu_decode(oscar, sc, cache, rk, rv)
+    b = gpu_decode(oscar, sc, cache, rk, rv)
+    assert np.array_equal(a, b)
+
+
+def test_decode_shared_prefix_pages(oscar):
+    # request 1 reuses request 0's first two history pages (same tokens)
+    L = 400
+    sc = Scenario(700, 8, 2, 32, [L, L])
+    for arr in (sc.k, sc.v):
+        arr[L:L + 176] = arr[:176]
+    sc.tok_k = [sc.k[:L], sc.k[L:]]
+    sc.tok_v = [sc.v[:L], sc.v[L:]]
+    sc.hist_pt[1, :2] = sc.hist_pt[0, :2]
+    ref = sc.oracle_cache()
+    cache = gpu_cache(oscar, sc, hist=ref.hist, bf16=ref.bf16)
+    rk, rv = gpu_rotations(oscar, sc)
+    assert_decode_close(gpu_decode(oscar, sc, cache, rk, rv), sc.oracle_decode(ref))
+
+
+def test_bad_page_ids_are_flagged_not_followed(oscar):
+    sc = Scenario(800, 8, 2, 64, [600])
+    ref = sc.oracle_cache()
+    cache = gpu_cache(oscar, sc, hist=ref.hist, bf16=ref.bf16)
+    cache.hist_pt[0, 3] = sc.n_hist_pages + 1000   # outside the pool
+    rk, rv = gpu_rotations(oscar, sc)
+    out = gpu_decode(oscar, sc, cache, rk, rv)
+    assert int(cache.status.item()) & 1
+    assert np.isfinite(out).all()
+
+
+# ------------------------------------------------------------------ BF16 baseline
+
+
+def test_bf16_paged_decode(oscar):
+    lens = [1, 16, 17, 300, 1024, 4097]
+    hq, hkv = 8, 2
+    ld = synth.LayerData(900, 0, hq, hkv)
+    k, v = ld.cache_kv(sum(lens))
+    pt, npages = synth.shuffled_page_tables(900, 0, lens, n_pages_fn=lambda L: (L + 15) // 16)
+    pages = np.zeros((npages, hkv, 2, 16, 128), dtype=np.uint16)
+    off = 0
+    for b, L in enumerate(lens):
+        p = np.arange(L)
+        pages[pt[b, p // 16], :, 0, p % 16] = k[off:off + L]
+        pages[pt[b, p // 16], :, 1, p % 16] = v[off:off + L]
+        off += L
+    q = ld.decode_q(len(lens))
+    ref = o.bf16_paged_decode(q, pages, pt, lens, SCALE)
+    import bit_rotated_kv_oscar_amd as m
+    kv = to_dev_bf16(pages)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = m.bf16_paged_decode(to_dev_bf16(q), kv, torch.from_numpy(pt).cuda(),
+                              torch.tensor(lens, dtype=torch.int32, device="cuda"), max(lens), SCALE,
+                              status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert_decode_close(out.cpu().numpy(), ref, "bf16")
+
+
+# ------------------------------------------------------------------ calibration
+
+
+def test_calibration_matches_oracle(oscar):
+    ld = synth.LayerData(1000, 0, 8, 2)
+    qc, kc, vc = ld.calibration(2048)
+    R_K, R_V, ck, cv = oscar.calibrate_rotation(to_dev_bf16(qc), to_dev_bf16(kc), to_dev_bf16(vc), 0.999)
+    R_K, R_V = R_K.numpy(), R_V.numpy()
+    q, k, v = (o.bf16_to_f64(x) for x in (qc, kc, vc))
+    cal = o.calibrate(q, k, v)
+    H, P = o.hadamard(), o.bitrev_permutation()
+    for R, C in ((R_K, o.query_covariance(q)), (R_V, o.score_covariance(q, k, v))):
+        assert np.abs(R.T @ R - np.eye(128)).max() < 1e-12
+        lam = np.sort(np.linalg.eigvalsh(C))[::-1]
+        assert np.abs(R.T @ C @ R - P @ H @ np.diag(lam) @ H @ P).max() < 1e-10 * np.abs(C).max()
+    assert np.abs(R_K - cal["R_K"]).max() < 1e-8
+    assert np.abs(R_V - cal["R_V"]).max() < 1e-8
+    assert abs(ck - cal["clip_K"]) <= 1e-6 * cal["clip_K"]
+    assert abs(cv - cal["clip_V"]) <= 1e-6 * cal["clip_V"]
