@@ -1,0 +1,384 @@
+#!/usr/bin/env python3
+"""Benchmark of the OSCAR INT2 KV-cache hot path on one MI355X.
+
+Default workload (the headline configuration): Qwen3-8B-shaped attention,
+36 layers, each with its own calibrated R_K, R_V and clips; 32 query / 8 KV
+heads, head_dim 128; batch 1 at a 32768-token context (16 sink + 128 recent
+BF16 tokens, the rest INT2 with G = 64, fp16 scale / zero); 16-token pages in
+a shuffled page table.  One step is one generation step of the attention
+stack: for every layer, write-on-append of the new token (the token leaving
+the recent window is rotated, clipped and packed into history) followed by
+the mixed-precision paged decode.  The step is captured once in a HIP graph
+and replayed; sequence lengths advance on the device each replay.
+
+`--workload bs64` runs the batch-64 configuration (per-request lengths
+uniform in [8192, 32768], pages of all requests interleaved in one pool).
+
+Printed: one JSON line (metric, value in GB/s of algorithmic bytes per step,
+tokens/s, the in-run BF16 paged-decode comparison, the roofline of the
+dominant kernel and the CPU oracle baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "INT2 decode-attn KV GB/s (% HBM peak) + tokens/s, 32K ctx bs1 & bs64"
+HBM_PEAK_GBS = 8000.0
+HEAD_DIM = 128
+
+
+def parse_args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", choices=["bs1", "bs64"], default="bs1")
+    p.add_argument("--layers", type=int, default=None, help="override the layer count (testing only)")
+    p.add_argument("--seed", type=int, default=1)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-bf16", action="store_true")
+    p.add_argument("--copy-probe-mb", type=int, default=0,
+                   help="only run a plain device copy of this many MiB (counter scale reference)")
+    return p.parse_args()
+
+
+WORKLOADS = {
+    "bs1": dict(name="qwen3-8b-shaped attention decode, 36 layers, batch 1, context 32768, G 64",
+                layers=36, hq=32, hkv=8, G=64, batch=1, len_lo=32768, len_hi=32768),
+    "bs64": dict(name="qwen3-8b-shaped attention decode, 36 layers, batch 64, contexts U[8192, 32768], G 64",
+                 layers=36, hq=32, hkv=8, G=64, batch=64, len_lo=8192, len_hi=32768),
+}
+
+
+def n_hist_tokens(L):
+    return max(0, L - 144)
+
+
+def decode_bytes(lens, hq, hkv, G):
+    """Algorithmic bytes of one decode call: INT2 codes + fp16 meta of every
+    history token, raw bf16 sink/recent tokens, page-table entries, q, out,
+    and R_K / R_V (fp32) once."""
+    per_tok_int2 = 2 * (32 + 4 * (128 // G))
+    b = 0
+    for L in lens:
+        nh = n_hist_tokens(L)
+        b += nh * hkv * per_tok_int2
+        b += min(L, 144) * hkv * 2 * 256
+        b += ((nh + 15) // 16) * 4 + 9 * 4
+    b += len(lens) * hq * HEAD_DIM * (2 + 4)
+    b += 2 * 128 * 128 * 4
+    return b
+
+
+def append_bytes(batch, hkv, G):
+    """Algorithmic bytes of one append call: the evicted ring token is read
+    and written to history, the new token is read and stored raw, R_K and
+    R_V (fp32) are read once."""
+    per_tok_int2 = 32 + 4 * (128 // G)
+    return batch * hkv * 2 * (256 + per_tok_int2 + 256 + 256) + 2 * 128 * 128 * 4
+
+
+def bf16_bytes(lens, hq, hkv):
+    b = 0
+    for L in lens:
+        b += L * hkv * 2 * 256 + ((L + 15) // 16) * 4
+    return b + len(lens) * hq * HEAD_DIM * (2 + 4)
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the path is single-GPU; "
+              f"see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_rotated_kv_oscar_amd as oscar
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb * (1 << 20)
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty(n, dtype=torch.uint8, device=dev)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n}))
+        return
+
+    W = dict(WORKLOADS[args.workload])
+    if args.layers:
+        W["layers"] = args.layers
+    nl, hq, hkv, G, B = W["layers"], W["hq"], W["hkv"], W["G"], W["batch"]
+    steps, warm = args.steps, args.warmup
+    headroom = steps + warm + 1
+    if W["batch"] == 1:
+        final_lens = np.array([W["len_hi"]], dtype=np.int32)
+    else:
+        final_lens = synth.request_lengths(args.seed, B, W["len_lo"], W["len_hi"])
+    start_lens = final_lens - headroom          # prefill length; each step appends one token
+    max_len = int(final_lens.max())
+    t_setup = time.time()
+
+    # ---------------------------------------------------------------- layers
+    class Layer:
+        pass
+
+    layers = []
+    bf16_layers = []
+    pages_per_req = [synth.hist_pages_needed(int(L)) for L in final_lens]
+    for l in range(nl):
+        ly = Layer()
+        ld = synth.LayerData(args.seed, l, hq, hkv)
+        # calibration on the device (library), 2048 seeded tokens
+        g = synth.device_generator(args.seed, l, synth.S_CAL_Q)
+        qc = synth.q_device(g, 2048, hq, ld.lam, dev)
+        kc = synth.kv_device(synth.device_generator(args.seed, l, synth.S_CAL_K), 2048, ld.outliers, dev)
+        vc = synth.kv_device(synth.device_generator(args.seed, l, synth.S_CAL_V), 2048, ld.outliers, dev)
+        R_K, R_V, ck, cv = oscar.calibrate_rotation(qc, kc, vc, 0.999)
+        ly.rk, ly.rv = oscar.Rotation(R_K, ck, dev), oscar.Rotation(R_V, cv, dev)
+        # page tables: every request's history pages from one shuffled pool
+        hist_pt, n_pool = synth.shuffled_page_tables(args.seed, l, final_lens, n_pool_pages=sum(pages_per_req) + 1)
+        bf16_pt = synth.bf16_page_tables(B, shuffle_seed=args.seed + l)
+        ly.cache = oscar.LayerCache(hkv, G, n_pool, 9 * B, torch.from_numpy(hist_pt), torch.from_numpy(bf16_pt),
+                                    device=dev)
+        # prefill: every request's first start_len tokens in one write call
+        tot = int(start_lens.sum())
+        k = synth.kv_device(synth.device_generator(args.seed, l, synth.S_CACHE_K), tot, ld.outliers, dev)
+        v = synth.kv_device(synth.device_generator(args.seed, l, synth.S_CACHE_V), tot, ld.outliers, dev)
+        cu = torch.from_numpy(np.concatenate([[0], np.cumsum(start_lens)]).astype(np.int32)).to(dev)
+        oscar.write_kv(ly.cache, ly.rk, ly.rv, k, v, cu, torch.zeros(B, dtype=torch.int32, device=dev),
+                       int(start_lens.max()))
+        # per-step inputs (the same new token and query every step)
+        ly.k_new = synth.kv_device(synth.device_generator(args.seed, l, synth.S_NEW_K), B, ld.outliers, dev)
+        ly.v_new = synth.kv_device(synth.device_generator(args.seed, l, synth.S_NEW_V), B, ld.outliers, dev)
+        ly.q = synth.q_device(synth.device_generator(args.seed, l, synth.S_DEC_Q), B, hq, ld.lam, dev)
+        ly.out = torch.empty((B, hq, HEAD_DIM), dtype=torch.float32, device=dev)
+        ly.ws = torch.empty(oscar.decode_workspace_bytes(B, hq, hkv, max_len), dtype=torch.uint8, device=dev)
+        layers.append(ly)
+        if not args.no_bf16:
+            # the same tokens, all raw bf16, for the in-run BF16 baseline
+            bl = Layer()
+            n_pages = [(int(L) + 15) // 16 for L in final_lens]
+            pt, npg = synth.shuffled_page_tables(args.seed + 100, l, final_lens, n_pool_pages=sum(n_pages),
+                                                 n_pages_fn=lambda L: (L + 15) // 16)
+            kv = torch.zeros((npg, hkv, 2, 16, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+            ptd = torch.from_numpy(pt).to(dev)
+            off = 0
+            for bb in range(B):
+                Ls = int(start_lens[bb])
+                pos = torch.arange(Ls, device=dev)
+                pg = ptd[bb, pos // 16]
+                kv[pg, :, 0, pos % 16] = k[off:off + Ls]
+                kv[pg, :, 1, pos % 16] = v[off:off + Ls]
+                off += Ls
+            bl.kv, bl.pt = kv, ptd
+            bl.out = torch.empty((B, hq, HEAD_DIM), dtype=torch.float32, device=dev)
+            bl.ws = torch.empty(oscar.bf16_decode_workspace_bytes(B, hq, hkv, max_len), dtype=torch.uint8,
+                                device=dev)
+            bf16_layers.append(bl)
+        del k, v, qc, kc, vc
+    torch.cuda.synchronize()
+    for ly in layers:
+        assert int(ly.cache.status.item()) == 0, "prefill flagged bad data"
+    setup_s = time.time() - t_setup
+
+    # ---------------------------------------------------------------- the step
+    lens_before = torch.from_numpy(start_lens.astype(np.int32)).to(dev)   # before this step's append
+    lens_after = lens_before + 1
+    cu1 = torch.arange(B + 1, dtype=torch.int32, device=dev)
+
+    def step():
+        for ly in layers:
+            oscar.write_kv(ly.cache, ly.rk, ly.rv, ly.k_new, ly.v_new, cu1, lens_before, 1)
+            oscar.decode_attn(ly.cache, ly.rk, ly.rv, ly.q, lens_after, max_len, 1 / math.sqrt(HEAD_DIM),
+                              out=ly.out, workspace=ly.ws)
+        lens_before.add_(1)
+        lens_after.add_(1)
+
+    def bf16_step():
+        for bl in bf16_layers:
+            oscar.bf16_paged_decode(layers[0].q, bl.kv, bl.pt, lens_after, max_len, 1 / math.sqrt(HEAD_DIM),
+                                    out=bl.out, workspace=bl.ws)
+
+    stream = torch.cuda.Stream(device=dev)
+    torch.cuda.synchronize()
+    # one eager step checks that the launches work before capture; then rewind
+    with torch.cuda.stream(stream):
+        step()
+        lens_before.sub_(1)
+        lens_after.sub_(1)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        step()
+    # capture advanced nothing on the device; replays advance the lengths
+    torch.cuda.synchronize()
+
+    for _ in range(warm):
+        graph.replay()
+    torch.cuda.synchronize()
+    lens_at_timing = lens_before.cpu().numpy().copy()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / steps
+    for ly in layers:
+        assert int(ly.cache.status.item()) == 0, "decode flagged bad data"
+        assert torch.isfinite(ly.out).all(), "non-finite decode output"
+
+    # bytes per step, averaged over the timed steps (lengths grow by one per step)
+    step_bytes = 0.0
+    dec_bytes_mean = 0.0
+    for s in range(steps):
+        lens_s = (lens_at_timing + s + 1).tolist()
+        db = decode_bytes(lens_s, hq, hkv, G)
+        dec_bytes_mean += db / steps
+        step_bytes += nl * (db + append_bytes(B, hkv, G)) / steps
+    gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    tokens_per_s = B / (ms_per_step * 1e-3)
+
+    # ------------------------------------------------ dominant-kernel timing
+    # HIP events on the stream the decode is launched on, around each decode
+    # call of every layer (eager launches, lengths fixed at the final value)
+    dec_ms = []
+    with torch.cuda.stream(stream):
+        for rep in range(3):
+            for ly in layers:
+                a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a0.record(stream)
+                oscar.decode_attn(ly.cache, ly.rk, ly.rv, ly.q, lens_before, max_len, 1 / math.sqrt(HEAD_DIM),
+                                  out=ly.out, workspace=ly.ws)
+                a1.record(stream)
+                dec_ms.append((a0, a1))
+    torch.cuda.synchronize()
+    dec_launch_ms = float(np.mean([a.elapsed_time(b) for a, b in dec_ms]))
+    dec_bytes_now = decode_bytes(lens_before.cpu().numpy().tolist(), hq, hkv, G)
+    achieved = dec_bytes_now / (dec_launch_ms * 1e-3) / 1e9
+
+    # ---------------------------------------------------------------- BF16
+    bf16 = None
+    if bf16_layers:
+        lens_after.copy_(lens_before)   # decode the same lengths
+        g2 = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            bf16_step()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g2, stream=stream):
+            bf16_step()
+        torch.cuda.synchronize()
+        for _ in range(max(2, warm)):
+            g2.replay()
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record()
+        for _ in range(steps):
+            g2.replay()
+        b1.record()
+        torch.cuda.synchronize()
+        bf16_ms = b0.elapsed_time(b1) / steps
+        # INT2 decode-only graph over the same lengths, for the like-for-like ratio
+        g3 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g3, stream=stream):
+            for ly in layers:
+                oscar.decode_attn(ly.cache, ly.rk, ly.rv, ly.q, lens_after, max_len, 1 / math.sqrt(HEAD_DIM),
+                                  out=ly.out, workspace=ly.ws)
+        torch.cuda.synchronize()
+        for _ in range(max(2, warm)):
+            g3.replay()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(steps):
+            g3.replay()
+        c1.record()
+        torch.cuda.synchronize()
+        int2_dec_ms = c0.elapsed_time(c1) / steps
+        lens_now = lens_before.cpu().numpy().tolist()
+        bf16 = {"bf16_ms_per_step": round(bf16_ms, 4), "int2_decode_ms_per_step": round(int2_dec_ms, 4),
+                "int2_speedup_vs_bf16": round(bf16_ms / int2_dec_ms, 3),
+                "bf16_GBps": round(nl * bf16_bytes(lens_now, hq, hkv) / (bf16_ms * 1e-3) / 1e9, 1)}
+
+    # ---------------------------------------------------------------- CPU oracle
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args, W, final_lens, step_bytes)
+
+    line = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": W["name"], "layers": nl, "batch": B, "q_heads": hq, "kv_heads": hkv, "group": G,
+                   "context": int(max_len) if B == 1 else [int(W["len_lo"]), int(W["len_hi"])],
+                   "step": "per layer: write-on-append of one token + INT2 paged decode"},
+        "tokens_per_s": round(tokens_per_s, 1),
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "oscar_decode_attn call (q rotation + split-K decode + merge)",
+                     "avg_launch_us": round(dec_launch_ms * 1e3, 2), "bytes_per_launch": int(dec_bytes_now)},
+        "cpu_baseline": cpu,
+        "setup_s": round(setup_s, 1),
+    }
+    if bf16:
+        line.update(bf16)
+    print(json.dumps(line))
+
+
+def cpu_baseline(args, W, final_lens, step_bytes):
+    """The fp64 oracle timed on the host on a bounded sample: one layer of the
+    workload (first request only), prefilled untimed, then repeated
+    (append one token + decode) rounds timed; scaled to a whole step."""
+    import numpy as np
+
+    import synth
+    from oracle import oscar_ref as o
+    try:
+        import threadpoolctl
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    hq, hkv, G = W["hq"], W["hkv"], W["G"]
+    L = int(final_lens[0])
+    ld = synth.LayerData(args.seed + 1000, 0, hq, hkv)
+    k, v = ld.cache_kv(L + 16)
+    rng = np.random.default_rng(args.seed)
+    R = np.linalg.qr(rng.standard_normal((128, 128)))[0]
+    pt, npool = synth.shuffled_page_tables(args.seed, 0, [L + 16])
+    ref = o.LayerCacheRef(hkv, G, npool, 9, pt, synth.bf16_page_tables(1))
+    ref.write(R, R, 6.0, 6.0, k[:L - 8], v[:L - 8], [0, L - 8], [0])
+    q = ld.decode_q(1)
+    t0 = time.time()
+    rounds = 0
+    cur = L - 8
+    while rounds < 8 and (rounds < 2 or time.time() - t0 < 20.0):
+        ref.write(R, R, 6.0, 6.0, k[cur:cur + 1], v[cur:cur + 1], [0, 1], [cur])
+        cur += 1
+        o.decode_attn(ref, R, R, q, [cur], 1 / math.sqrt(128))
+        rounds += 1
+    per_layer_req_s = (time.time() - t0) / rounds
+    # a step = every layer x every request
+    step_s = per_layer_req_s * W["layers"] * len(final_lens)
+    return {"value": round(step_bytes / step_s / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rounds} rounds of (append 1 token + decode) on one layer of one {L}-token request "
+                      f"(Hq {hq}, Hkv {hkv}, G {G}), {per_layer_req_s:.2f} s each, scaled x{W['layers']} layers "
+                      f"x{len(final_lens)} requests",
+            "s_per_step_extrapolated": round(step_s, 2)}
+
+
+if __name__ == "__main__":
+    main()

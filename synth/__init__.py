@@ -135,3 +135,34 @@ def bf16_page_tables(batch: int, first_page: int = 0, shuffle_seed: int | None =
 def request_lengths(base_seed: int, batch: int, lo: int, hi: int) -> np.ndarray:
     """Integer lengths uniform in [lo, hi] (inclusive)."""
     return rng(base_seed, 0, S_LENS).integers(lo, hi + 1, size=batch).astype(np.int32)
+
+
+# ---------------------------------------------------------------- on device
+# Bulk generators for benchmark-sized workloads: the same distributions as
+# above, drawn with torch's seeded device generator instead of numpy.
+
+def device_generator(base_seed: int, layer: int, stream: int, device="cuda"):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(np.random.SeedSequence([base_seed, layer, stream]).generate_state(1)[0]))
+    return g
+
+
+def kv_device(gen, n: int, outliers: np.ndarray, device="cuda"):
+    """bf16 [n][Hkv][128] ~ N(0, 1) with the outlier channels scaled x20."""
+    import torch
+    hkv = outliers.shape[0]
+    scale = torch.ones((hkv, HEAD_DIM), dtype=torch.float32)
+    for h in range(hkv):
+        scale[h, torch.as_tensor(outliers[h])] = 20.0
+    x = torch.randn((n, hkv, HEAD_DIM), generator=gen, device=device, dtype=torch.float32)
+    x.mul_(scale.to(device))
+    return x.to(torch.bfloat16)
+
+
+def q_device(gen, n: int, n_q_heads: int, lam: np.ndarray, device="cuda"):
+    """bf16 [n][Hq][128] ~ N(0, diag(lam))."""
+    import torch
+    z = torch.randn((n, n_q_heads, HEAD_DIM), generator=gen, device=device, dtype=torch.float32)
+    z.mul_(torch.as_tensor(np.sqrt(lam), dtype=torch.float32, device=device))
+    return z.to(torch.bfloat16)
