@@ -126,7 +126,9 @@ size_t oscar_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_
 static int check_heads(int32_t hq, int32_t hkv) {
   if (hq < 1 || hkv < 1) return fail(OSCAR_EINVAL, "head counts must be >= 1");
   if (hq % hkv) return fail(OSCAR_EUNSUPPORTED, "n_q_heads %d not a multiple of n_kv_heads %d", hq, hkv);
-  if (hq / hkv > 16) return fail(OSCAR_EUNSUPPORTED, "GQA group %d > 16", hq / hkv);
+  const int g = hq / hkv;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(OSCAR_EUNSUPPORTED, "GQA group %d not in {1, 2, 4, 8}", g);
   return OSCAR_OK;
 }
 

@@ -1,0 +1,211 @@
+// Device helpers shared by the decode kernels: matrix-core operand types,
+// DPP / cross-lane reductions, the 2-bit code expansion, and one wave's pass
+// over a BF16 page.
+#pragma once
+
+#include "kernels.h"
+
+namespace oscar {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int WAVES = 4;            // waves per workgroup
+constexpr float LOG2E = 1.4426950408889634f;
+// The running max of a softmax is raised only when a score exceeds it by more
+// than this (log2 units), so probabilities stay <= 2^LAZY_TH; most pages then
+// skip the rescale of the accumulators.
+constexpr float LAZY_TH = 3.0f;
+constexpr int PART_STRIDE = D + 2;  // partial: o[128], m, l
+
+// lane l receives the value of lane l - N (mod 16) of its row of 16
+template <int N>
+__device__ inline float row_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, false));
+}
+
+__device__ inline float quad_sum(float v) {  // sum over lanes l, l^16, l^32, l^48
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+__device__ inline float quad_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ------------------------------------------------------------ code expansion
+// A code dword expands into fp16 pairs 1 + c/4 (mask 0x0300, slot pairs at
+// bits 8-9 / 24-25) and 1 + c/16 (mask 0x00C0, bits 6-7 / 22-23) after one of
+// four shifts (none, >>4, <<4, rotate right 8).  The constant 1 and the 1/4,
+// 1/16 weights are undone by the operand on the other side of the product.
+__device__ inline uint32_t ex4(uint32_t x) { return (x & 0x03000300u) | 0x3C003C00u; }
+__device__ inline uint32_t ex16(uint32_t x) { return (x & 0x00C000C0u) | 0x3C003C00u; }
+__device__ inline uint32_t rotr8(uint32_t x) { return __builtin_amdgcn_alignbit(x, x, 8); }
+
+__device__ inline f16x8 as_f16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  u32x4 u = {a, b, c, d};
+  return __builtin_bit_cast(f16x8, u);
+}
+__device__ inline f16x4 as_f16x4(uint32_t a, uint32_t b) {
+  u32x2 u = {a, b};
+  return __builtin_bit_cast(f16x4, u);
+}
+
+// K code block k (channels 32k..32k+31) as the A operand of a 16x16x32 MFMA
+__device__ inline f16x8 expand_k(uint32_t w0, uint32_t w1, int k) {
+  const uint32_t w = (k < 2) ? w0 : w1;
+  const uint32_t x0 = (k & 1) ? (w << 4) : w;
+  const uint32_t x1 = (k & 1) ? rotr8(w) : (w >> 4);
+  return as_f16x8(ex4(x0), ex16(x0), ex4(x1), ex16(x1));
+}
+
+// V code row-block r (channels 16r..16r+15) as the A operand of a 16x16x16 MFMA
+__device__ inline f16x4 expand_v(uint32_t w0, uint32_t w1, int r) {
+  const uint32_t w = (r < 4) ? w0 : w1;
+  const int s = r & 3;
+  const uint32_t x = s == 0 ? w : s == 1 ? (w >> 4) : s == 2 ? (w << 4) : rotr8(w);
+  return as_f16x4(ex4(x), ex16(x));
+}
+
+__device__ inline f32x4 mfma_k(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ inline f32x4 mfma_v(f16x4 a, f16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline float lo_f16(uint32_t w) {
+  return float(__builtin_bit_cast(_Float16, uint16_t(w & 0xFFFFu)));
+}
+__device__ inline float hi_f16(uint32_t w) {
+  return float(__builtin_bit_cast(_Float16, uint16_t(w >> 16)));
+}
+__device__ inline float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ------------------------------------------------------------ BF16 pages
+// One wave's online-softmax state over BF16 pages.  Scores use the 16x16x32
+// bf16 matrix core (lane (t = l%16, quad q = l/16) supplies K row t, channels
+// 32k+8q..+7; B holds the query heads in columns, bf16 exactly as given).
+// Probabilities go to the PV lanes by shuffles; PV runs on the vector ALUs
+// with lane (c = l%16, r = l/16) owning channels 8c..8c+7 and, per page, rows
+// 4r..4r+3 (partial sums reduced over r once at the end).
+template <int GQA>
+struct Bf16Wave {
+  bf16x8 bq[4];
+  float m_run, l_run;  // of head (l%16) in lanes with l%16 < GQA
+  float acc[GQA][8];
+  float scale;         // sm_scale * log2(e)
+
+  __device__ void init(const uint16_t *q_heads /* [GQA][128] bf16 */, float sm_scale, int lane) {
+    const int n = lane & 15, qd = lane >> 4;
+    for (int k = 0; k < 4; ++k) {
+      u32x4 u = {0, 0, 0, 0};
+      if (n < GQA) u = *reinterpret_cast<const u32x4 *>(q_heads + n * D + 32 * k + 8 * qd);
+      bq[k] = __builtin_bit_cast(bf16x8, u);
+    }
+    m_run = -INFINITY;
+    l_run = 0.f;
+    for (int h = 0; h < GQA; ++h)
+      for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
+    scale = sm_scale * LOG2E;
+  }
+
+  // kp, vp: the K and V rows of one page (16 x 128 bf16 each); rows whose bit
+  // in `valid` is clear are ignored.
+  __device__ void page(const uint16_t *kp, const uint16_t *vp, uint32_t valid, int lane) {
+    const int n = lane & 15, qd = lane >> 4;
+    u32x4 kf[4], vf[4];
+    for (int k = 0; k < 4; ++k) kf[k] = *reinterpret_cast<const u32x4 *>(kp + n * D + 32 * k + 8 * qd);
+    for (int i = 0; i < 4; ++i) vf[i] = *reinterpret_cast<const u32x4 *>(vp + (4 * qd + i) * D + 8 * n);
+    f32x4 d = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < 4; ++k)
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[k]), bq[k], d, 0, 0, 0);
+    float sc[4];
+    float mx = -INFINITY;
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = (valid >> (4 * qd + i)) & 1u;
+      sc[i] = ok ? d[i] * scale : -INFINITY;
+      mx = fmaxf(mx, sc[i]);
+    }
+    if (__any(mx > m_run + LAZY_TH)) {
+      const float mm = quad_max(fmaxf(mx, m_run));
+      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - mm);
+      l_run *= alpha;
+      m_run = mm;
+      for (int h = 0; h < GQA; ++h) {
+        const float ah = __shfl(alpha, (lane & 48) | h);
+        for (int j = 0; j < 8; ++j) acc[h][j] *= ah;
+      }
+    }
+    float p[4];
+    for (int i = 0; i < 4; ++i) {
+      p[i] = (sc[i] == -INFINITY) ? 0.f : fast_exp2(sc[i] - m_run);
+      l_run += p[i];
+    }
+    for (int i = 0; i < 4; ++i) {
+      // rows outside `valid` may hold any bits (even NaN): zero them
+      const bool ok = (valid >> (4 * qd + i)) & 1u;
+      float v[8];
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j] = ok ? bf16lo(vf[i][j]) : 0.f;
+        v[2 * j + 1] = ok ? bf16hi(vf[i][j]) : 0.f;
+      }
+      for (int h = 0; h < GQA; ++h) {
+        const float ph = __shfl(p[i], (lane & 48) | h);
+        for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(ph, v[j], acc[h][j]);
+      }
+    }
+  }
+
+  // Writes o[h][c] (unnormalised), m[h], l[h] of this wave into LDS.
+  __device__ void finish(float *o, float *m, float *l, int lane) {
+    const int n = lane & 15, qd = lane >> 4;
+    const float lt = quad_sum(l_run);
+    for (int h = 0; h < GQA; ++h)
+      for (int j = 0; j < 8; ++j) {
+        const float s = quad_sum(acc[h][j]);
+        if (qd == 0) o[h * D + 8 * n + j] = s;
+      }
+    if (qd == 0 && n < GQA) {
+      m[n] = m_run;
+      l[n] = lt;
+    }
+  }
+};
+
+// Combines the WAVES per-wave states in LDS and writes one partial
+// (o[128], m, l) per query head of the group.
+template <int GQA>
+__device__ inline void combine_waves(const float *o_lds, const float *m_lds, const float *l_lds,
+                                     float *part0, int64_t head_stride, int tid) {
+  for (int idx = tid; idx < GQA * D; idx += WAVES * 64) {
+    const int h = idx / D, c = idx % D;
+    float mst = -INFINITY;
+    for (int w = 0; w < WAVES; ++w) mst = fmaxf(mst, m_lds[w * GQA + h]);
+    float o = 0.f, l = 0.f;
+    for (int w = 0; w < WAVES; ++w) {
+      const float mw = m_lds[w * GQA + h];
+      const float e = (mw == -INFINITY) ? 0.f : fast_exp2(mw - mst);
+      o = fmaf(e, o_lds[(w * GQA + h) * D + c], o);
+      l = fmaf(e, l_lds[w * GQA + h], l);
+    }
+    float *part = part0 + h * head_stride;
+    part[c] = o;
+    if (c == 0) {
+      part[D] = mst;
+      part[D + 1] = l;
+    }
+  }
+}
+
+}  // namespace oscar

@@ -58,7 +58,7 @@ typedef struct ihipStream_t *oscar_stream_t;
 enum {
   OSCAR_OK = 0,
   OSCAR_EINVAL = -1,       /* null pointer, negative or inconsistent size    */
-  OSCAR_EUNSUPPORTED = -2, /* group not in {32,64,128}, Hq % Hkv != 0, ...   */
+  OSCAR_EUNSUPPORTED = -2, /* G not in {32,64,128}, Hq/Hkv not in {1,2,4,8} */
   OSCAR_EWORKSPACE = -3,   /* workspace smaller than the *_workspace_bytes() */
   OSCAR_EHIP = -4,         /* HIP runtime or launch error (text appended)    */
   OSCAR_ENODEV = -5        /* no usable gfx950 device                        */

@@ -133,7 +133,8 @@ def _decode(c=None, hq=8, batch=1, max_len=150, ws=0xA000, ws_bytes=1 << 30, sca
 def test_decode_validation_codes():
     E = _lib
     assert _decode(hq=7) == E.OSCAR_EUNSUPPORTED and "multiple" in _err()
-    assert _decode(hq=64) == E.OSCAR_EUNSUPPORTED            # GQA 32 > 16
+    assert _decode(hq=64) == E.OSCAR_EUNSUPPORTED            # GQA 32
+    assert _decode(hq=6) == E.OSCAR_EUNSUPPORTED             # GQA 3
     assert _decode(max_len=0) == E.OSCAR_EINVAL
     assert _decode(max_len=10_000) == E.OSCAR_EINVAL and "hist_pt_stride" in _err()
     assert _decode(q=0) == E.OSCAR_EINVAL
