@@ -189,7 +189,7 @@ def main():
                 off += Ls
             bl.kv, bl.pt = kv, ptd
             bl.out = torch.empty((B, hq, HEAD_DIM), dtype=torch.float32, device=dev)
-            bl.ws = torch.empty(oscar.bf16_decode_workspace_bytes(B, hq, hkv, max_len), dtype=torch.uint8,
+            bl.ws = torch.zeros(oscar.bf16_decode_workspace_bytes(B, hq, hkv, max_len), dtype=torch.uint8,
                                 device=dev)
             bf16_layers.append(bl)
         del k, v, qc, kc, vc
@@ -201,13 +201,11 @@ def main():
     # ---------------------------------------------------------------- the step
     lens_before = torch.from_numpy(start_lens.astype(np.int32)).to(dev)   # before this step's append
     lens_after = lens_before + 1
-    cu1 = torch.arange(B + 1, dtype=torch.int32, device=dev)
 
     def step():
         for ly in layers:
-            oscar.write_kv(ly.cache, ly.rk, ly.rv, ly.k_new, ly.v_new, cu1, lens_before, 1)
-            oscar.decode_attn(ly.cache, ly.rk, ly.rv, ly.q, lens_after, max_len, 1 / math.sqrt(HEAD_DIM),
-                              out=ly.out, workspace=ly.ws)
+            oscar.decode_step(ly.cache, ly.rk, ly.rv, ly.k_new, ly.v_new, lens_before, ly.q, max_len,
+                              1 / math.sqrt(HEAD_DIM), out=ly.out, workspace=ly.ws)
         lens_before.add_(1)
         lens_after.add_(1)
 
@@ -324,12 +322,12 @@ def main():
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": W["name"], "layers": nl, "batch": B, "q_heads": hq, "kv_heads": hkv, "group": G,
                    "context": int(max_len) if B == 1 else [int(W["len_lo"]), int(W["len_hi"])],
-                   "step": "per layer: write-on-append of one token + INT2 paged decode"},
+                   "step": "per layer: oscar_decode_step (write-on-append of one token + INT2 paged decode)"},
         "tokens_per_s": round(tokens_per_s, 1),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "oscar_decode_attn call (q rotation + split-K decode + merge)",
+                     "kernel": "oscar_decode_attn call (prologue: q rotation; attend: split-K decode + merge)",
                      "avg_launch_us": round(dec_launch_ms * 1e3, 2), "bytes_per_launch": int(dec_bytes_now)},
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),

@@ -61,6 +61,10 @@ SIGNATURES = [
      [ctypes.POINTER(LayerCacheC), ctypes.POINTER(RotationC), ctypes.POINTER(RotationC),
       c_p, ctypes.c_int32, c_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, c_p,
       c_p, ctypes.c_size_t, c_p]),
+    ("oscar_decode_step", ctypes.c_int,
+     [ctypes.POINTER(LayerCacheC), ctypes.POINTER(RotationC), ctypes.POINTER(RotationC),
+      c_p, c_p, c_p, c_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, c_p,
+      c_p, ctypes.c_size_t, c_p]),
     ("oscar_bf16_decode_workspace_bytes", ctypes.c_size_t,
      [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
     ("oscar_bf16_paged_decode", ctypes.c_int,
@@ -77,7 +81,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     if _lib is not None:
         return _lib
     if not os.path.exists(path):
-        raise ImportError(f"liboscar.so not built at {path}; run `python -m bit_rotated_kv_oscar_amd.build`")
+        raise ImportError(f"liboscar.so not built at {path}; run `python bit_rotated_kv_oscar_amd/build.py`")
     lib = ctypes.CDLL(path)
     for name, res, args in SIGNATURES:
         fn = getattr(lib, name)

@@ -144,6 +144,33 @@ def decode_attn(cache: LayerCache, rot_k: Rotation, rot_v: Rotation, q: torch.Te
     return out
 
 
+def decode_step(cache: LayerCache, rot_k: Rotation, rot_v: Rotation, k_new: torch.Tensor,
+                v_new: torch.Tensor, len_before: torch.Tensor, q: torch.Tensor, max_seq_len: int,
+                sm_scale: float | None = None, out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """oscar_decode_step: append k_new / v_new (bf16 [B, Hkv, 128]) at positions
+    len_before, then decode q (bf16 [B, Hq, 128]) over len_before + 1 tokens."""
+    dev = cache.device
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (q, "q")):
+        _need(t, n, (torch.bfloat16,), dev)
+    _need(len_before, "len_before", (torch.int32,), dev)
+    batch, hq = q.shape[0], q.shape[1]
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if out is None:
+        out = torch.empty((batch, hq, HEAD_DIM), dtype=torch.float32, device=dev)
+    _need(out, "out", (torch.float32,), dev)
+    need = decode_workspace_bytes(batch, hq, cache.n_kv_heads, max_seq_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    c = cache.c()
+    rk, rv = rot_k.c(), rot_v.c()
+    check(load().oscar_decode_step(ctypes.byref(c), ctypes.byref(rk), ctypes.byref(rv), _ptr(k_new), _ptr(v_new),
+                                   _ptr(len_before), _ptr(q), hq, batch, int(max_seq_len), float(sm_scale),
+                                   _ptr(out), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out
+
+
 def bf16_decode_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, max_seq_len: int) -> int:
     return int(load().oscar_bf16_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, max_seq_len))
 
@@ -165,8 +192,8 @@ def bf16_paged_decode(q: torch.Tensor, kv_pages: torch.Tensor, pt: torch.Tensor,
     if out is None:
         out = torch.empty((batch, hq, HEAD_DIM), dtype=torch.float32, device=dev)
     need = bf16_decode_workspace_bytes(batch, hq, hkv, max_seq_len)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace is None:  # zero-filled: it holds the merge counters
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
     check(load().oscar_bf16_paged_decode(_ptr(q), _ptr(kv_pages), kv_pages.shape[0], _ptr(pt), pt.shape[1],
                                          _ptr(seq_lens), batch, int(max_seq_len), hq, hkv, float(sm_scale),
                                          _ptr(out), _ptr(status), _ptr(workspace), workspace.numel(),

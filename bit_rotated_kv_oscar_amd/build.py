@@ -1,6 +1,7 @@
 """Compile liboscar.so (HIP for gfx950) in-tree.
 
-Usage: python -m bit_rotated_kv_oscar_amd.build  (or build() from Python).
+Usage: python bit_rotated_kv_oscar_amd/build.py (by path: importing the
+package would open the library that is about to be rebuilt).
 Every source is compiled on every call; objects go to _build/, the library
 to bit_rotated_kv_oscar_amd/liboscar.so.
 """

@@ -158,6 +158,34 @@ int oscar_decode_attn(const oscar_layer_cache *cache, const oscar_rotation *rot_
   return OSCAR_OK;
 }
 
+int oscar_decode_step(const oscar_layer_cache *cache, const oscar_rotation *rot_k, const oscar_rotation *rot_v,
+                      const uint16_t *k_new, const uint16_t *v_new, const int32_t *len_before,
+                      const uint16_t *q, int32_t n_q_heads, int32_t batch, int32_t max_seq_len,
+                      float sm_scale, float *out, void *workspace, size_t workspace_bytes,
+                      oscar_stream_t stream) {
+  if (int rc = check_cache(cache)) return rc;
+  if (int rc = check_rot(rot_k, "rot_k")) return rc;
+  if (int rc = check_rot(rot_v, "rot_v")) return rc;
+  if (int rc = check_heads(n_q_heads, cache->n_kv_heads)) return rc;
+  if (batch < 1 || batch > 65535) return fail(OSCAR_EINVAL, "batch %d outside [1, 65535]", batch);
+  if (max_seq_len < 1) return fail(OSCAR_EINVAL, "max_seq_len %d < 1", max_seq_len);
+  if (oscar::n_hist_pages(max_seq_len) > cache->hist_pt_stride)
+    return fail(OSCAR_EINVAL, "max_seq_len %d needs %d history pages, hist_pt_stride is %d", max_seq_len,
+                oscar::n_hist_pages(max_seq_len), cache->hist_pt_stride);
+  if (!k_new || !v_new || !len_before || !q || !out)
+    return fail(OSCAR_EINVAL, "k_new, v_new, len_before, q or out is NULL");
+  if (!std::isfinite(sm_scale) || sm_scale <= 0.f) return fail(OSCAR_EINVAL, "sm_scale must be finite and > 0");
+  const size_t need = oscar::decode_int2_ws_bytes(batch, n_q_heads, cache->n_kv_heads, max_seq_len);
+  if (!workspace || workspace_bytes < need)
+    return fail(OSCAR_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+  if (int rc = check_device()) return rc;
+  hipError_t e = oscar::launch_decode_step(*cache, rot_arg(rot_k), rot_arg(rot_v), k_new, v_new, len_before, q,
+                                           n_q_heads, nullptr, batch, max_seq_len, sm_scale, out, workspace,
+                                           reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode_step");
+  return OSCAR_OK;
+}
+
 size_t oscar_bf16_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                                          int32_t max_seq_len) {
   if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || max_seq_len < 1) return 0;

@@ -120,16 +120,24 @@ struct Bf16Wave {
     scale = sm_scale * LOG2E;
   }
 
-  // kp, vp: the K and V rows of one page (16 x 128 bf16 each); rows whose bit
-  // in `valid` is clear are ignored.
-  __device__ void page(const uint16_t *kp, const uint16_t *vp, uint32_t valid, int lane) {
-    const int n = lane & 15, qd = lane >> 4;
+  struct Loads {
     u32x4 kf[4], vf[4];
-    for (int k = 0; k < 4; ++k) kf[k] = *reinterpret_cast<const u32x4 *>(kp + n * D + 32 * k + 8 * qd);
-    for (int i = 0; i < 4; ++i) vf[i] = *reinterpret_cast<const u32x4 *>(vp + (4 * qd + i) * D + 8 * n);
+  };
+
+  // Issues the loads of one page: kp, vp = its K and V rows (16 x 128 bf16).
+  __device__ static void issue(const uint16_t *kp, const uint16_t *vp, Loads &ld, int lane) {
+    const int n = lane & 15, qd = lane >> 4;
+    for (int k = 0; k < 4; ++k) ld.kf[k] = *reinterpret_cast<const u32x4 *>(kp + n * D + 32 * k + 8 * qd);
+    for (int i = 0; i < 4; ++i) ld.vf[i] = *reinterpret_cast<const u32x4 *>(vp + (4 * qd + i) * D + 8 * n);
+  }
+
+  // Attends over one loaded page; rows whose bit in `valid` is clear are
+  // ignored (their bits may be anything, even NaN).
+  __device__ void compute(const Loads &ld, uint32_t valid, int lane) {
+    const int qd = lane >> 4;
     f32x4 d = {0.f, 0.f, 0.f, 0.f};
     for (int k = 0; k < 4; ++k)
-      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[k]), bq[k], d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ld.kf[k]), bq[k], d, 0, 0, 0);
     float sc[4];
     float mx = -INFINITY;
     for (int i = 0; i < 4; ++i) {
@@ -153,12 +161,11 @@ struct Bf16Wave {
       l_run += p[i];
     }
     for (int i = 0; i < 4; ++i) {
-      // rows outside `valid` may hold any bits (even NaN): zero them
       const bool ok = (valid >> (4 * qd + i)) & 1u;
       float v[8];
       for (int j = 0; j < 4; ++j) {
-        v[2 * j] = ok ? bf16lo(vf[i][j]) : 0.f;
-        v[2 * j + 1] = ok ? bf16hi(vf[i][j]) : 0.f;
+        v[2 * j] = ok ? bf16lo(ld.vf[i][j]) : 0.f;
+        v[2 * j + 1] = ok ? bf16hi(ld.vf[i][j]) : 0.f;
       }
       for (int h = 0; h < GQA; ++h) {
         const float ph = __shfl(p[i], (lane & 48) | h);
@@ -183,17 +190,17 @@ struct Bf16Wave {
   }
 };
 
-// Combines the WAVES per-wave states in LDS and writes one partial
-// (o[128], m, l) per query head of the group.
-template <int GQA>
+// Combines the NW per-wave states in LDS (o [NW][GQA][128], m, l [NW][GQA])
+// and writes one unnormalised partial (o[128], m, l) per query head.
+template <int GQA, int NW>
 __device__ inline void combine_waves(const float *o_lds, const float *m_lds, const float *l_lds,
                                      float *part0, int64_t head_stride, int tid) {
-  for (int idx = tid; idx < GQA * D; idx += WAVES * 64) {
+  for (int idx = tid; idx < GQA * D; idx += NW * 64) {
     const int h = idx / D, c = idx % D;
     float mst = -INFINITY;
-    for (int w = 0; w < WAVES; ++w) mst = fmaxf(mst, m_lds[w * GQA + h]);
+    for (int w = 0; w < NW; ++w) mst = fmaxf(mst, m_lds[w * GQA + h]);
     float o = 0.f, l = 0.f;
-    for (int w = 0; w < WAVES; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float mw = m_lds[w * GQA + h];
       const float e = (mw == -INFINITY) ? 0.f : fast_exp2(mw - mst);
       o = fmaf(e, o_lds[(w * GQA + h) * D + c], o);
@@ -206,6 +213,22 @@ __device__ inline void combine_waves(const float *o_lds, const float *m_lds, con
       part[D + 1] = l;
     }
   }
+}
+
+// After a workgroup has written its partial: publish it and count the
+// workgroup in (device scope).  True in exactly one workgroup, the last of
+// `expected`; that one then sees every partial.
+__device__ inline bool elect_last(uint32_t *count, uint32_t expected, int *flag_lds, int tid) {
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t done = __hip_atomic_fetch_add(count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    *flag_lds = done == expected - 1;
+  }
+  __syncthreads();
+  const bool last = *flag_lds;
+  if (last) __threadfence();
+  return last;
 }
 
 }  // namespace oscar

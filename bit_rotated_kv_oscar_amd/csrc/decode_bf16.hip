@@ -1,28 +1,39 @@
 // Plain BF16 paged decode attention: the all-BF16 baseline that OSCAR's
 // batch-1 decode speed-up is measured against (arXiv:2605.17757 v2 abstract).
-// Split-K over pages: one workgroup (4 waves, every 4th page each) per
-// (request, KV head, split) writes an unnormalised partial per query head; a
-// merge kernel LSE-combines them.  Scores on the bf16 matrix cores, PV on the
-// vector ALUs, fp32 accumulation throughout.
+// One kernel: a workgroup of 8 waves per (request, KV head, split); wave w
+// takes every 8th page of the split (page ids preloaded, the next page's
+// loads issued before the current page computes).  Scores on the bf16 matrix
+// cores, PV on the vector ALUs, fp32 accumulation.  Each workgroup writes an
+// unnormalised partial per query head; the last workgroup of a (request, KV
+// head) LSE-merges them and normalises.  The merge counters live in the
+// workspace and are left at zero by every call.
 #include "attn_common.h"
 
 namespace oscar {
 
+constexpr int BW = 8;  // waves per workgroup
+
 SplitPlan plan_bf16_splits(int batch, int n_kv_heads, int max_seq_len) {
   const int pages = (max_seq_len + PAGE - 1) / PAGE;
   const int64_t total = int64_t(pages) * batch * n_kv_heads;
-  int64_t pw = (total + int64_t(WAVES) * 1024 - 1) / (int64_t(WAVES) * 1024);
+  int64_t pw = (total + int64_t(BW) * 512 - 1) / (int64_t(BW) * 512);
   if (pw < 2) pw = 2;
-  if (pw > 32) pw = 32;
+  if (pw > 64) pw = 64;
+  const int64_t min_pw = (pages + int64_t(BW) * 255 - 1) / (int64_t(BW) * 255);
+  if (pw < min_pw) pw = min_pw;
   SplitPlan p;
-  p.pages_per_split = int(pw) * WAVES;
+  p.pages_per_split = int(pw) * BW;
   p.n_splits = (pages + p.pages_per_split - 1) / p.pages_per_split;
   return p;
 }
 
+static size_t count_off(int batch, int n_q_heads, int n_splits) {
+  return (size_t(batch) * n_q_heads * n_splits * PART_STRIDE * sizeof(float) + 255) & ~size_t(255);
+}
+
 size_t decode_bf16_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int max_seq_len) {
   const SplitPlan p = plan_bf16_splits(batch, n_kv_heads, max_seq_len);
-  return (size_t(batch) * n_q_heads * p.n_splits * PART_STRIDE * sizeof(float) + 255) & ~size_t(255);
+  return count_off(batch, n_q_heads, p.n_splits) + ((size_t(batch) * n_kv_heads * 4 + 255) & ~size_t(255));
 }
 
 struct Bf16Args {
@@ -35,95 +46,104 @@ struct Bf16Args {
   float sm_scale;
   float *out;
   uint32_t *status;
-  float *parts;
+  float *parts;     // [B][Hq][n_splits][PART_STRIDE]
+  uint32_t *count;  // [B][Hkv]
 };
 
 template <int GQA>
-__global__ void __launch_bounds__(WAVES * 64) bf16_split_kernel(Bf16Args a) {
+__device__ void bf16_merge(const Bf16Args &a, int b, int hk, int used, float *lds, int tid) {
+  const int wave = tid >> 6, lane = tid & 63;
+  const int64_t head_stride = int64_t(a.n_splits) * PART_STRIDE;
+  const float *parts0 = a.parts + (int64_t(b) * a.n_q_heads + hk * GQA) * head_stride;
+  float *w_lds = lds;              // [GQA][used]
+  float *lsum = w_lds + GQA * used;
+  if (wave < GQA) {
+    const float *ph = parts0 + wave * head_stride;
+    float m = -INFINITY;
+    for (int s = lane; s < used; s += 64) m = fmaxf(m, ph[s * PART_STRIDE + D]);
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    float l = 0.f;
+    for (int s = lane; s < used; s += 64) {
+      const float ms = ph[s * PART_STRIDE + D];
+      const float w = (ms == -INFINITY) ? 0.f : fast_exp2(ms - m);
+      w_lds[wave * used + s] = w;
+      l = fmaf(w, ph[s * PART_STRIDE + D + 1], l);
+    }
+    for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
+    if (lane == 0) lsum[wave] = l;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < GQA * D; idx += BW * 64) {
+    const int h = idx / D, ch = idx % D;
+    const float *ph = parts0 + h * head_stride;
+    float o = 0.f;
+    for (int s = 0; s < used; ++s) o = fmaf(w_lds[h * used + s], ph[s * PART_STRIDE + ch], o);
+    a.out[(int64_t(b) * a.n_q_heads + hk * GQA + h) * D + ch] = o / lsum[h];
+  }
+}
+
+template <int GQA>
+__global__ void __launch_bounds__(BW * 64) bf16_decode_kernel(Bf16Args a) {
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int L = a.seq_lens[b];
-  __shared__ float o_lds[WAVES * GQA * D];
-  __shared__ float m_lds[WAVES * GQA], l_lds[WAVES * GQA];
+  constexpr int LDS_COMBINE = BW * GQA * D + 2 * BW * GQA;
+  constexpr int LDS_MERGE = GQA * 256 + 8;
+  __shared__ float lds[LDS_COMBINE > LDS_MERGE ? LDS_COMBINE : LDS_MERGE];
+  __shared__ int last_s;
   if (L < 1 || L > a.max_seq_len) {
-    if (tid == 0 && split == 0 && hk == 0) flag_status(a.status, OSCAR_STATUS_BAD_LEN);
-    return;
-  }
-  Bf16Wave<GQA> st;
-  st.init(a.q + (int64_t(b) * a.n_q_heads + hk * GQA) * D, a.sm_scale, lane);
-  const int pages = (L + PAGE - 1) / PAGE;
-  const int j0 = split * a.pages_per_split;
-  const int j1 = min(pages, j0 + a.pages_per_split);
-  for (int j = j0 + wave; j < j1; j += WAVES) {
-    const int pid = __builtin_amdgcn_readfirstlane(a.pt[int64_t(b) * a.pt_stride + j]);
-    if (pid < 0 || pid >= a.n_pages) {
-      if (lane == 0) flag_status(a.status, OSCAR_STATUS_BAD_PAGE);
-      continue;
+    if (split == 0) {
+      if (tid == 0 && hk == 0) flag_status(a.status, OSCAR_STATUS_BAD_LEN);
+      for (int e = tid; e < GQA * D; e += BW * 64) a.out[(int64_t(b) * a.n_q_heads + hk * GQA) * D + e] = 0.f;
     }
-    const int rows = min(PAGE, L - PAGE * j);
-    const uint32_t valid = rows >= PAGE ? 0xFFFFu : ((1u << rows) - 1u);
-    const uint16_t *base = a.kv + (int64_t(pid) * a.n_kv_heads + hk) * 2 * PAGE * D;
-    st.page(base, base + PAGE * D, valid, lane);
-  }
-  st.finish(o_lds + wave * GQA * D, m_lds + wave * GQA, l_lds + wave * GQA, lane);
-  __syncthreads();
-  float *part0 = a.parts + ((int64_t(b) * a.n_q_heads + hk * GQA) * a.n_splits + split) * PART_STRIDE;
-  combine_waves<GQA>(o_lds, m_lds, l_lds, part0, int64_t(a.n_splits) * PART_STRIDE, tid);
-}
-
-__global__ void __launch_bounds__(256) bf16_merge_kernel(Bf16Args a) {
-  const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int L = a.seq_lens[b];
-  float *o = a.out + (int64_t(b) * a.n_q_heads + hq) * D;
-  if (L < 1 || L > a.max_seq_len) {
-    if (tid < D) o[tid] = 0.f;
     return;
   }
   const int pages = (L + PAGE - 1) / PAGE;
   const int used = (pages + a.pages_per_split - 1) / a.pages_per_split;
-  const float *parts = a.parts + (int64_t(b) * a.n_q_heads + hq) * a.n_splits * PART_STRIDE;
-  __shared__ float red[256];
-  __shared__ float acc2[2][D];
-  float m = -INFINITY;
-  for (int s = tid; s < used; s += 256) m = fmaxf(m, parts[s * PART_STRIDE + D]);
-  red[tid] = m;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
-    __syncthreads();
+  if (split >= used) return;
+  float *o_lds = lds, *m_lds = lds + BW * GQA * D, *l_lds = m_lds + BW * GQA;
+  Bf16Wave<GQA> st;
+  st.init(a.q + (int64_t(b) * a.n_q_heads + hk * GQA) * D, a.sm_scale, lane);
+  const int j0 = split * a.pages_per_split + wave;
+  const int j1 = min(pages, split * a.pages_per_split + a.pages_per_split);
+  const int npw = j1 > j0 ? (j1 - j0 + BW - 1) / BW : 0;
+  int my_pid = -1;
+  if (lane < npw) my_pid = a.pt[int64_t(b) * a.pt_stride + j0 + BW * lane];
+  typename Bf16Wave<GQA>::Loads cur, nxt;
+  auto issue = [&](int i, typename Bf16Wave<GQA>::Loads &ld) -> bool {
+    const int pid = __builtin_amdgcn_readlane(my_pid, i);
+    if (pid < 0 || pid >= a.n_pages) return false;
+    const uint16_t *base = a.kv + (int64_t(pid) * a.n_kv_heads + hk) * 2 * PAGE * D;
+    Bf16Wave<GQA>::issue(base, base + PAGE * D, ld, lane);
+    return true;
+  };
+  bool cur_ok = npw > 0 ? issue(0, cur) : false;
+  for (int i = 0; i < npw; ++i) {
+    bool nxt_ok = false;
+    if (i + 1 < npw) nxt_ok = issue(i + 1, nxt);
+    if (!cur_ok) {
+      if (lane == 0) flag_status(a.status, OSCAR_STATUS_BAD_PAGE);
+    } else {
+      const int rows = min(PAGE, L - PAGE * (j0 + BW * i));
+      st.compute(cur, rows >= PAGE ? 0xFFFFu : ((1u << rows) - 1u), lane);
+    }
+    cur = nxt;
+    cur_ok = nxt_ok;
   }
-  const float mst = red[0];
+  st.finish(o_lds + wave * GQA * D, m_lds + wave * GQA, l_lds + wave * GQA, lane);
   __syncthreads();
-  float l = 0.f;
-  for (int s = tid; s < used; s += 256) {
-    const float ms = parts[s * PART_STRIDE + D];
-    l = fmaf((ms == -INFINITY) ? 0.f : fast_exp2(ms - mst), parts[s * PART_STRIDE + D + 1], l);
-  }
-  red[tid] = l;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (tid < off) red[tid] += red[tid + off];
-    __syncthreads();
-  }
-  const float lsum = red[0];
-  const int ch = tid & (D - 1), half = tid >> 7;
-  float acc = 0.f;
-  for (int s = half; s < used; s += 2) {
-    const float ms = parts[s * PART_STRIDE + D];
-    const float w = (ms == -INFINITY) ? 0.f : fast_exp2(ms - mst);
-    acc = fmaf(w, parts[s * PART_STRIDE + ch], acc);
-  }
-  acc2[half][ch] = acc;
-  __syncthreads();
-  if (tid < D) o[tid] = (acc2[0][tid] + acc2[1][tid]) / lsum;
+  const int64_t head_stride = int64_t(a.n_splits) * PART_STRIDE;
+  float *part0 = a.parts + (int64_t(b) * a.n_q_heads + hk * GQA) * head_stride + split * PART_STRIDE;
+  combine_waves<GQA, BW>(o_lds, m_lds, l_lds, part0, head_stride, tid);
+  uint32_t *cnt = a.count + b * a.n_kv_heads + hk;
+  if (!elect_last(cnt, uint32_t(used), &last_s, tid)) return;
+  bf16_merge<GQA>(a, b, hk, used, lds, tid);
+  if (tid == 0) *cnt = 0u;  // ready for the next call
 }
 
 template <int GQA>
 static hipError_t launch_t(const Bf16Args &a, int batch, hipStream_t s) {
-  hipLaunchKernelGGL((bf16_split_kernel<GQA>), dim3(a.n_splits, a.n_kv_heads, batch), dim3(WAVES * 64), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bf16_merge_kernel, dim3(a.n_q_heads, batch), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((bf16_decode_kernel<GQA>), dim3(a.n_splits, a.n_kv_heads, batch), dim3(BW * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -148,6 +168,7 @@ hipError_t launch_decode_bf16(const uint16_t *q, const uint16_t *kv, int64_t n_p
   a.out = out;
   a.status = status;
   a.parts = static_cast<float *>(ws);
+  a.count = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(ws) + count_off(batch, n_q_heads, p.n_splits));
   switch (n_q_heads / n_kv_heads) {
     case 1: return launch_t<1>(a, batch, s);
     case 2: return launch_t<2>(a, batch, s);

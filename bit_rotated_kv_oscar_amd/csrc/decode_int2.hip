@@ -1,35 +1,45 @@
-// Mixed-precision paged decode attention over the OSCAR cache.
+// Mixed-precision paged decode attention over the OSCAR cache, and the
+// write-on-append of one token per request.
 //
 // OSCAR online phase (gist.science nl/fr technical summaries, section 2.2.B:
 // one fused kernel unpacks, dequantises, undoes the rotation and attends over
 // the INT2 history on paged storage with prefix caching; arXiv:2605.17757 v2
-// abstract: batch-1 decode gains come from cutting KV memory traffic).
+// abstract: fused write and decode kernels, batch-1 decode gains from cutting
+// KV memory traffic).
 //
 // The rotation is never undone per token: history keys stay in the rotated
 // basis and are scored against q R_K (R orthogonal keeps q.k), and the
 // history part of the output is rotated back by R_V^T once per (request,
-// query head) in the merge.  Per-group scale s and zero z are factored out of
-// both contractions, so the matrix cores see the 2-bit codes as exact fp16
-// values:
+// query head).  Per-group scale s and zero z are factored out of both
+// contractions so the matrix cores see the 2-bit codes as exact fp16 values:
 //   score_t = sum_g s_tg (q_g . c_tg) + z_tg sum_{i in g} q_i
 //   o       = sum_g [ sum_t (p_t s_tg) c_tg ] + sum_t p_t z_tg
 //
-// Kernels, in stream order:
-//   qprep:  per (request, KV head): q_rot = q R_K * sm_scale * log2(e) for the
-//           query heads of the group, laid out as the B operand of the score
-//           MFMAs (fp16 high + low parts), with the column sums that cancel
-//           the code expansion's constant and the per-group sums of q_rot.
-//   split:  one workgroup (4 waves) per (request, KV head, split).  Split 0
-//           attends over the raw BF16 sink + recent pages; split s >= 1 over
-//           history pages, each wave taking every 4th page.  Writes an
-//           unnormalised partial (o[128], m, l) per query head.
-//   merge:  LSE-combines the splits, rotates the history part back with
-//           R_V^T, adds the raw part and normalises (fp32 out).
+// Two kernels per call, in stream order:
+//   prologue (one block per (request, KV head)):
+//     - optional append: the token leaving the recent window (position
+//       L-128 when L >= 144) is read from its ring slot, rotated, clipped,
+//       quantised and stored in history; the new token takes the slot;
+//     - q_rot = q R_K * sm_scale * log2(e) for the query heads of the group,
+//       laid out as the B operand of the score MFMAs (fp16 high + low parts)
+//       with the column sums that cancel the code expansion's constant and
+//       the per-group sums of q_rot; resets the merge counter.
+//   attend (one workgroup of 8 waves per (request, KV head, split)):
+//     split 0 attends over the raw BF16 sink + recent pages, split s >= 1
+//     over history pages (wave w takes every 8th page of the split, page ids
+//     preloaded, next page's loads issued before the current page computes).
+//     Each workgroup writes an unnormalised partial (o[128], m, l) per query
+//     head; the last workgroup of a (request, KV head) LSE-merges them,
+//     rotates the history part back with R_V^T, adds the raw part and
+//     normalises (fp32 out).
 #include "attn_common.h"
 
 namespace oscar {
 
-constexpr int FRAG_DW = 32;  // dwords per lane of the q fragment block
+constexpr int AW = 8;                // waves per attend workgroup
+constexpr int FRAG_DW = 32;          // dwords per lane of the q fragment block
+constexpr int PRO_THREADS = 512;     // prologue block: K half + V half
+constexpr int MAX_SPLITS = 255;      // history splits per (request, KV head)
 
 // Column layout of the score and PV accumulators for a GQA group of GQA heads
 // and NG scale groups: column n = h + GQA * (part + 2 * cg); part 0/1 = fp16
@@ -41,134 +51,282 @@ struct Cols {
   static constexpr int CG = CG0 < NG ? CG0 : NG;
   static constexpr int NA = (NG + CG - 1) / CG;
   static constexpr int G = D / NG;
-  __device__ static int grp_of_kblock(int k) { return (32 * k) / G; }   // 32-channel block
-  __device__ static int grp_of_rblock(int r) { return (16 * r) / G; }   // 16-channel block
+  __device__ static constexpr int grp_of_kblock(int k) { return (32 * k) / G; }  // 32-channel block
+  __device__ static constexpr int grp_of_rblock(int r) { return (16 * r) / G; }  // 16-channel block
 };
 
 SplitPlan plan_int2_splits(int batch, int n_kv_heads, int max_seq_len) {
   const int pages = n_hist_pages(max_seq_len);
   SplitPlan p;
   if (pages == 0) {
-    p.pages_per_split = WAVES;
+    p.pages_per_split = AW;
     p.n_splits = 0;
     return p;
   }
-  // about 1024 workgroups per launch for the longest request (4 per CU)
+  // about 512 workgroups (two per CU) for the longest request
   const int64_t total = int64_t(pages) * batch * n_kv_heads;
-  int64_t pw = (total + int64_t(WAVES) * 1024 - 1) / (int64_t(WAVES) * 1024);
+  int64_t pw = (total + int64_t(AW) * 512 - 1) / (int64_t(AW) * 512);
   if (pw < 2) pw = 2;
-  if (pw > 32) pw = 32;
-  p.pages_per_split = int(pw) * WAVES;
+  if (pw > 64) pw = 64;
+  // at most MAX_SPLITS splits (bounds the merge's LDS)
+  const int64_t min_pw = (pages + int64_t(AW) * MAX_SPLITS - 1) / (int64_t(AW) * MAX_SPLITS);
+  if (pw < min_pw) pw = min_pw;
+  p.pages_per_split = int(pw) * AW;
   p.n_splits = (pages + p.pages_per_split - 1) / p.pages_per_split;
   return p;
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-
 static size_t frag_bytes(int batch, int hkv) { return align256(size_t(batch) * hkv * FRAG_DW * 64 * 4); }
+static size_t count_bytes(int batch, int hkv) { return align256(size_t(batch) * hkv * 4); }
 
 size_t decode_int2_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int max_seq_len) {
   const SplitPlan p = plan_int2_splits(batch, n_kv_heads, max_seq_len);
-  return frag_bytes(batch, n_kv_heads) +
+  return frag_bytes(batch, n_kv_heads) + count_bytes(batch, n_kv_heads) +
          align256(size_t(batch) * n_q_heads * (1 + p.n_splits) * PART_STRIDE * sizeof(float));
 }
 
-struct DecodeArgs {
+struct StepArgs {
   oscar_layer_cache c;
   const uint8_t *fk, *fv;
+  float clip_k, clip_v;
+  // append (may be null: no append)
+  const uint16_t *k_new, *v_new;  // [B][Hkv][128]
+  const int32_t *len_before;      // [B]: the new token goes to position len_before[b]
+  // decode (q may be null: append only)
   const uint16_t *q;
-  const int32_t *seq_lens;
+  const int32_t *seq_lens;        // [B] after the append
   int n_q_heads, max_seq_len, pages_per_split, n_splits;
   float sm_scale;
-  float pv_scale, pv_unscale;  // 2^k and 2^-k applied to the PV operand
-  uint32_t *frag;              // [B][Hkv][FRAG_DW][64]
-  float *parts;                // [B][Hq][1 + n_splits][PART_STRIDE]
-  float *out;
+  float pv_scale, pv_unscale;     // 2^k and 2^-k applied to the PV operand
+  uint32_t *frag;                 // [B][Hkv][FRAG_DW][64]
+  uint32_t *count;                // [B][Hkv] workgroups done (merge election)
+  float *parts;                   // [B][Hq][1 + n_splits][PART_STRIDE]
+  float *out;                     // [B][Hq][128]
 };
 
 __device__ inline bool valid_len(int L, int max_len) { return L >= 1 && L <= max_len; }
 
-// ------------------------------------------------------------------ qprep
+// ------------------------------------------------------------------ prologue
 
-template <int GQA, int NG>
-__global__ void __launch_bounds__(256) qprep_kernel(DecodeArgs a) {
-  using C = Cols<GQA, NG>;
-  const int hk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  __shared__ float qs[GQA][D];   // bf16 query, fp32
-  __shared__ float qr[GQA][D];   // q R_K * sm_scale * log2(e)
-  __shared__ float qz[GQA][NG];  // per-group sums of qr
-  __shared__ float red[256];
-  for (int e = tid; e < GQA * D; e += 256)
-    qs[e / D][e % D] = bf16_to_f32(a.q[(int64_t(b) * a.n_q_heads + hk * GQA) * D + e]);
-  __syncthreads();
-  const float *R = reinterpret_cast<const float *>(a.fk + FORM_R);
-  const float sc = a.sm_scale * LOG2E;
-  float amax = 0.f;
-  for (int e = tid; e < GQA * D; e += 256) {
-    const int h = e / D, j = e % D;
-    float s = 0.f;
-    for (int i = 0; i < D; ++i) s = fmaf(qs[h][i], R[i * D + j], s);
-    qr[h][j] = s * sc;
-    amax = fmaxf(amax, fabsf(s * sc));
-  }
-  red[tid] = amax;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
-    __syncthreads();
-  }
-  // the B operand holds qr * 16 at most: scale down by a power of two if that
-  // would leave the fp16 range (never for ordinary queries)
-  float kq = 1.f;
-  while (red[0] * 16.f * kq > 16384.f) kq *= 0.5f;
-  if (tid < GQA * NG) {
-    const int h = tid / NG, g = tid % NG;
-    float s = 0.f;
-    for (int i = 0; i < C::G; ++i) s += qr[h][g * C::G + i];
-    qz[h][g] = s;
-  }
-  __syncthreads();
-  if (tid < 64) {
-    const int lane = tid, n = lane & 15, qd = lane >> 4;
-    const int h = n % GQA, part = (n / GQA) & 1, cg = n / (2 * GQA);
-    const bool ncol = cg < C::CG;
-    uint32_t *fr = a.frag + (int64_t(b) * a.c.n_kv_heads + hk) * FRAG_DW * 64;
-    // value of the B operand at (channel c, column n)
-    auto bval = [&](int c) -> _Float16 {
-      const int g = (32 * (c / 32)) / C::G;
-      if (!ncol || (g % C::CG) != cg) return _Float16(0.f);
-      const float mult = ((c & 3) < 2) ? 4.f : 16.f;
-      const float x = qr[h][c] * mult * kq;
-      const _Float16 hi = _Float16(x);
-      return part ? _Float16(x - float(hi)) : hi;
-    };
-    for (int k = 0; k < 4; ++k)
-      for (int v = 0; v < 4; ++v) {
-        const int c0 = 32 * k + 8 * qd + 2 * v;
-        const uint16_t lo16 = __builtin_bit_cast(uint16_t, bval(c0));
-        const uint16_t hi16 = __builtin_bit_cast(uint16_t, bval(c0 + 1));
-        fr[(4 * k + v) * 64 + lane] = uint32_t(lo16) | (uint32_t(hi16) << 16);
-      }
-    for (int ai = 0; ai < C::NA; ++ai) {
-      // minus the column sum of B over the channel blocks of accumulator ai
-      float cs = 0.f;
-      for (int c = 0; c < D; ++c)
-        if (C::grp_of_kblock(c / 32) / C::CG == ai) cs += float(bval(c));
-      fr[(16 + ai) * 64 + lane] = __float_as_uint(-cs);
-      const int g = ai * C::CG + cg;
-      const float zq = (ncol && part == 0 && g < NG) ? qz[h][g] : 0.f;
-      fr[(16 + C::NA + ai) * 64 + lane] = __float_as_uint(zq);
+// Quantise one rotated vector (128 values in LDS, already in y) into history
+// row `row` of the block at `blk` (K or V area), G channels per group.
+// Threads t < 128 of the half take part; `codes` is LDS scratch.
+__device__ inline void store_int2_row(const float *y, float clip, int G, bool is_v, uint8_t *blk, int row,
+                                      uint8_t *codes, float *sz_lds, int t) {
+  const int ng = D / G;
+  if (t < ng) {
+    float lo = fminf(fmaxf(y[t * G], -clip), clip), hi = lo;
+    for (int i = 1; i < G; ++i) {
+      const float v = fminf(fmaxf(y[t * G + i], -clip), clip);
+      lo = fminf(lo, v);
+      hi = fmaxf(hi, v);
     }
-    fr[(16 + 2 * C::NA) * 64 + lane] = __float_as_uint(1.f / kq);
+    sz_lds[2 * t] = __half2float(__float2half_rn((hi - lo) / 3.0f));
+    sz_lds[2 * t + 1] = __half2float(__float2half_rn(lo));
+  }
+  __syncthreads();
+  if (t < D) {
+    const float v = fminf(fmaxf(y[t], -clip), clip);
+    const float s = sz_lds[2 * (t / G)], z = sz_lds[2 * (t / G) + 1];
+    codes[t] = s > 0.f ? uint8_t(min(3, max(0, int(rintf((v - z) / s))))) : uint8_t(0);
+  }
+  __syncthreads();
+  uint32_t *area = reinterpret_cast<uint32_t *>(blk + (is_v ? v_codes_off(G) : k_codes_off(G)));
+  if (!is_v) {
+    // the 8 dwords of token `row`: lanes 16q + row, halves d
+    if (t < 8) {
+      const int q = t >> 1, d = t & 1;
+      uint32_t w = 0;
+      for (int u = 0; u < 8; ++u) {
+        const int c0 = 32 * (2 * d + u / 4) + 8 * q + 2 * (u % 4);
+        w |= uint32_t(codes[c0]) << slot_lo(u);
+        w |= uint32_t(codes[c0 + 1]) << slot_hi(u);
+      }
+      area[2 * (16 * q + row) + d] = w;
+    }
+  } else {
+    // token `row` owns 4 codes in each of 32 dwords (lanes 16 (row/4) + m, halves d)
+    if (t < 32) {
+      const int m = t & 15, d = t >> 4, q = row >> 2, jj = (row & 3) >> 1;
+      const int bit_sel = row & 1;
+      uint32_t w = 0, mask = 0;
+      for (int rr = 0; rr < 4; ++rr) {
+        const int u = 2 * rr + jj;
+        const int c = 16 * (4 * d + rr) + m;
+        const int bit = bit_sel ? slot_hi(u) : slot_lo(u);
+        w |= uint32_t(codes[c]) << bit;
+        mask |= 3u << bit;
+      }
+      uint32_t *p = area + 2 * (16 * q + m) + d;
+      *p = (*p & ~mask) | w;
+    }
+  }
+  if (t < ng) {
+    __half2 *meta = reinterpret_cast<__half2 *>(blk + (is_v ? v_meta_off(G) : k_meta_off(G)));
+    meta[PAGE * t + row] = __halves2half2(__float2half_rn(sz_lds[2 * t]), __float2half_rn(sz_lds[2 * t + 1]));
   }
 }
 
-// ------------------------------------------------------------------ split
-
-// One wave over history pages j = j0 + wave, j0 + wave + WAVES, ... < j1.
 template <int GQA, int NG>
-__device__ void history_wave(const DecodeArgs &a, int b, int hk, int L, int j0, int j1, int wave,
-                             int lane, float *o_lds, float *m_lds, float *l_lds) {
+__global__ void __launch_bounds__(PRO_THREADS) prologue_kernel(StepArgs a) {
+  using C = Cols<GQA, NG>;
+  constexpr int G = C::G;
+  const int hk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int half = tid >> 8, t = tid & 255;  // half 0: K (and the query), 1: V
+  const oscar_layer_cache &c = a.c;
+  const int hkv = c.n_kv_heads;
+  __shared__ float xin[2][GQA + 1][D];       // [half][vector][channel]
+  __shared__ float yout[2][GQA + 1][D];
+  __shared__ float part_lds[2][2 * (GQA + 1) * D];
+  __shared__ uint8_t codes[2][D];
+  __shared__ float sz_lds[2][8];
+  __shared__ float red[256];
+  __shared__ int evict_s;
+
+  // ---------------- append (optional)
+  int evict_pos = -1;  // position leaving the ring, or -1
+  uint8_t *evict_blk = nullptr;
+  if (a.k_new) {
+    const int L0 = a.len_before[b];
+    if (L0 < 0 || L0 >= (1 << 30)) {
+      if (tid == 0 && hk == 0) flag_status(c.status, OSCAR_STATUS_BAD_LEN);
+    } else {
+      const uint16_t *src = (half ? a.v_new : a.k_new) + (int64_t(b) * hkv + hk) * D;
+      int page, row;
+      if (L0 < N_SINK) {
+        page = c.bf16_pt[b * BF16_PT];
+        row = L0;
+      } else {
+        const int slot = L0 % N_RECENT;
+        page = c.bf16_pt[b * BF16_PT + 1 + slot / PAGE];
+        row = slot % PAGE;
+        if (L0 >= N_RAW) evict_pos = L0 - N_RECENT;
+      }
+      const bool page_ok = page >= 0 && page < c.n_bf16_pages;
+      uint16_t *ring = page_ok ? c.bf16 + ((int64_t(page) * hkv + hk) * 2 + half) * (PAGE * D) + row * D : nullptr;
+      if (evict_pos >= 0) {
+        const int hj = (evict_pos - N_SINK) / PAGE;
+        const int pid = hj < c.hist_pt_stride ? c.hist_pt[int64_t(b) * c.hist_pt_stride + hj] : -1;
+        if (pid >= 0 && pid < c.n_hist_pages && page_ok)
+          evict_blk = c.hist + (int64_t(pid) * hkv + hk) * hist_block_bytes(G);
+        else if (t == 0 && half == 0)
+          flag_status(c.status, OSCAR_STATUS_BAD_PAGE);
+        if (t < D) xin[half][GQA][t] = (evict_blk && ring) ? bf16_to_f32(ring[t]) : 0.f;
+      } else if (!page_ok && t == 0 && half == 0) {
+        flag_status(c.status, OSCAR_STATUS_BAD_PAGE);
+      }
+      __syncthreads();  // the evicted row is read before the slot is overwritten
+      if (ring && t < D) ring[t] = src[t];
+    }
+  }
+  // ---------------- query (K half)
+  const bool want_q = a.q != nullptr;
+  if (want_q && half == 0) {
+    for (int e = t; e < GQA * D; e += 256)
+      xin[0][e / D][e % D] = bf16_to_f32(a.q[(int64_t(b) * a.n_q_heads + hk * GQA) * D + e]);
+  }
+  if (want_q) {
+    if (tid == 0) a.count[b * hkv + hk] = 0u;
+    const int L = a.k_new ? a.len_before[b] + 1 : a.seq_lens[b];
+    if (!valid_len(L, a.max_seq_len)) {  // attend skips this request: zero its output here
+      if (tid == 0 && hk == 0) flag_status(c.status, OSCAR_STATUS_BAD_LEN);
+      for (int e = tid; e < GQA * D; e += PRO_THREADS)
+        a.out[(int64_t(b) * a.n_q_heads + hk * GQA) * D + e] = 0.f;
+    }
+  }
+  if (tid == 0) evict_s = evict_blk ? 1 : 0;
+  __syncthreads();
+  // ---------------- rotations: K half rotates q heads + evicted k, V half the evicted v
+  const float *R = reinterpret_cast<const float *>((half ? a.fv : a.fk) + FORM_R);
+  {
+    // both halves run the same code path (uniform barriers); unused vectors are zero
+    const int jx = t & (D - 1), hf = t >> 7;
+    float acc[GQA + 1];
+#pragma unroll
+    for (int v = 0; v <= GQA; ++v) acc[v] = 0.f;
+    const bool need = (half == 0 && want_q) || evict_s;
+    if (need) {
+#pragma unroll 16
+      for (int i = 64 * hf; i < 64 * hf + 64; ++i) {
+        const float r = R[i * D + jx];
+#pragma unroll
+        for (int v = 0; v <= GQA; ++v) acc[v] = fmaf(xin[half][v][i], r, acc[v]);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v <= GQA; ++v) part_lds[half][(hf * (GQA + 1) + v) * D + jx] = acc[v];
+    __syncthreads();
+    if (t < D)
+#pragma unroll
+      for (int v = 0; v <= GQA; ++v)
+        yout[half][v][t] = part_lds[half][v * D + t] + part_lds[half][(GQA + 1 + v) * D + t];
+    __syncthreads();
+  }
+  // ---------------- quantise the evicted token into history
+  if (evict_s) {
+    const int hrow = (evict_pos - N_SINK) % PAGE;
+    store_int2_row(yout[half][GQA], half ? a.clip_v : a.clip_k, G, half == 1, evict_blk, hrow, codes[half],
+                   sz_lds[half], t);
+  }
+  // ---------------- q fragments (K half builds them; both halves share the barrier)
+  const float sc = a.sm_scale * LOG2E;
+  float amax = 0.f;
+  if (want_q && half == 0)
+    for (int e = t; e < GQA * D; e += 256) amax = fmaxf(amax, fabsf(yout[0][e / D][e % D] * sc));
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if ((t & 63) == 0 && half == 0) red[t >> 6] = amax;
+  __syncthreads();
+  if (!want_q || half == 1) return;  // no block barrier below this point
+  const float gmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float kq = 1.f;
+  while (gmax * 16.f * kq > 16384.f) kq *= 0.5f;
+  if (t >= 64) return;
+  const int lane = t, n = lane & 15, qd = lane >> 4;
+  const int h = n % GQA, part = (n / GQA) & 1, cg = n / (2 * GQA);
+  const bool ncol = cg < C::CG;
+  uint32_t *fr = a.frag + (int64_t(b) * hkv + hk) * FRAG_DW * 64;
+  auto bval = [&](int ch) -> _Float16 {
+    const int g = ch / G;
+    if (!ncol || (g % C::CG) != cg) return _Float16(0.f);
+    const float mult = ((ch & 3) < 2) ? 4.f : 16.f;
+    const float x = yout[0][h][ch] * sc * mult * kq;
+    const _Float16 hi = _Float16(x);
+    return part ? _Float16(x - float(hi)) : hi;
+  };
+  for (int k = 0; k < 4; ++k)
+    for (int v = 0; v < 4; ++v) {
+      const int c0 = 32 * k + 8 * qd + 2 * v;
+      const uint16_t lo16 = __builtin_bit_cast(uint16_t, bval(c0));
+      const uint16_t hi16 = __builtin_bit_cast(uint16_t, bval(c0 + 1));
+      fr[(4 * k + v) * 64 + lane] = uint32_t(lo16) | (uint32_t(hi16) << 16);
+    }
+  for (int ai = 0; ai < C::NA; ++ai) {
+    float cs = 0.f;  // column sum of B over the channel blocks of accumulator ai
+    for (int ch = 0; ch < D; ++ch)
+      if ((ch / G) / C::CG == ai) cs += float(bval(ch));
+    fr[(16 + ai) * 64 + lane] = __float_as_uint(-cs);
+    const int g = ai * C::CG + cg;
+    float zq = 0.f;
+    if (ncol && part == 0 && g < NG)
+      for (int i = 0; i < G; ++i) zq += yout[0][h][g * G + i] * sc;
+    fr[(16 + C::NA + ai) * 64 + lane] = __float_as_uint(zq);
+  }
+  fr[(16 + 2 * C::NA) * 64 + lane] = __float_as_uint(1.f / kq);
+}
+
+// ------------------------------------------------------------------ attend
+
+template <int NA>
+struct PageLoads {
+  u32x2 kc, vc;
+  u32x4 km[NA], vm[NA];
+};
+
+// One wave over its history pages j = j0 + wave + AW*i, i < npw.
+template <int GQA, int NG>
+__device__ void history_wave(const StepArgs &a, int b, int hk, int L, int j0, int j1, int wave, int lane,
+                             const uint32_t *frag_lds, float *o_lds, float *m_lds, float *l_lds) {
   using C = Cols<GQA, NG>;
   constexpr int NA = C::NA;
   const oscar_layer_cache &c = a.c;
@@ -178,121 +336,150 @@ __device__ void history_wave(const DecodeArgs &a, int b, int hk, int L, int j0, 
   const int blk_bytes = hist_block_bytes(C::G);
   const int kmeta = k_meta_off(C::G), vcode = v_codes_off(C::G), vmeta = v_meta_off(C::G);
   const int nh = n_hist_tokens(L);
+  const int npw = j1 > j0 + wave ? (j1 - j0 - wave + AW - 1) / AW : 0;
 
-  const uint32_t *fr = a.frag + (int64_t(b) * c.n_kv_heads + hk) * FRAG_DW * 64;
-  f16x8 bq[4];
-  for (int k = 0; k < 4; ++k)
-    bq[k] = as_f16x8(fr[(4 * k) * 64 + lane], fr[(4 * k + 1) * 64 + lane], fr[(4 * k + 2) * 64 + lane],
-                     fr[(4 * k + 3) * 64 + lane]);
   float cinit[NA], zq[NA];
   int goff[NA];
   bool gval[NA];
+#pragma unroll
   for (int ai = 0; ai < NA; ++ai) {
-    cinit[ai] = __uint_as_float(fr[(16 + ai) * 64 + lane]);
-    zq[ai] = __uint_as_float(fr[(16 + NA + ai) * 64 + lane]);
+    cinit[ai] = __uint_as_float(frag_lds[(16 + ai) * 64 + lane]);
+    zq[ai] = __uint_as_float(frag_lds[(16 + NA + ai) * 64 + lane]);
     const int g = ai * C::CG + cg;
     gval[ai] = ncol && g < NG;
     goff[ai] = 64 * (g < NG ? g : NG - 1) + 16 * qd;
   }
-  const float inv_kq = __uint_as_float(fr[(16 + 2 * NA) * 64 + lane]);
+  const float inv_kq = __uint_as_float(frag_lds[(16 + 2 * NA) * 64 + lane]);
+
+  // page ids of this wave, one per lane
+  int my_pid = -1;
+  if (lane < npw) my_pid = c.hist_pt[int64_t(b) * c.hist_pt_stride + j0 + wave + AW * lane];
 
   float m_run = -INFINITY, l_run = 0.f;
   float corr[NA], zacc[NA];
   f32x4 acc[8];
+#pragma unroll
   for (int r = 0; r < 8; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
   for (int ai = 0; ai < NA; ++ai) corr[ai] = zacc[ai] = 0.f;
 
-  for (int j = j0 + wave; j < j1; j += WAVES) {
-    const int pid = __builtin_amdgcn_readfirstlane(c.hist_pt[int64_t(b) * c.hist_pt_stride + j]);
-    if (pid < 0 || pid >= c.n_hist_pages) {
-      if (lane == 0) flag_status(c.status, OSCAR_STATUS_BAD_PAGE);
-      continue;
-    }
+  auto issue = [&](int i, PageLoads<NA> &ld) -> bool {
+    const int pid = __builtin_amdgcn_readlane(my_pid, i);
+    if (pid < 0 || pid >= c.n_hist_pages) return false;
     const uint8_t *blk = c.hist + (int64_t(pid) * c.n_kv_heads + hk) * blk_bytes;
-    const u32x2 kc = *reinterpret_cast<const u32x2 *>(blk + 8 * lane);
-    const u32x2 vc = *reinterpret_cast<const u32x2 *>(blk + vcode + 8 * lane);
-    u32x4 km[NA], vm[NA];
+    ld.kc = *reinterpret_cast<const u32x2 *>(blk + 8 * lane);
+    ld.vc = *reinterpret_cast<const u32x2 *>(blk + vcode + 8 * lane);
+#pragma unroll
     for (int ai = 0; ai < NA; ++ai) {
-      km[ai] = *reinterpret_cast<const u32x4 *>(blk + kmeta + goff[ai]);
-      vm[ai] = *reinterpret_cast<const u32x4 *>(blk + vmeta + goff[ai]);
+      ld.km[ai] = *reinterpret_cast<const u32x4 *>(blk + kmeta + goff[ai]);
+      ld.vm[ai] = *reinterpret_cast<const u32x4 *>(blk + vmeta + goff[ai]);
     }
-    const int nvalid = min(PAGE, nh - PAGE * j);
+    return true;
+  };
 
-    // ---- scores: D[t][n] = sum_c code_tc q'_cn, per accumulator
-    f32x4 dacc[NA];
-    for (int ai = 0; ai < NA; ++ai) dacc[ai] = f32x4{cinit[ai], cinit[ai], cinit[ai], cinit[ai]};
-    for (int k = 0; k < 4; ++k) {
-      const int ai = C::grp_of_kblock(k) / C::CG;
-      dacc[ai] = mfma_k(expand_k(kc[0], kc[1], k), bq[k], dacc[ai]);
-    }
-    float sc[4];
-    float mx = -INFINITY;
-    for (int i = 0; i < 4; ++i) {
-      float v = 0.f;
+  PageLoads<NA> cur, nxt;
+  bool cur_ok = npw > 0 ? issue(0, cur) : false;
+  for (int i = 0; i < npw; ++i) {
+    bool nxt_ok = false;
+    if (i + 1 < npw) nxt_ok = issue(i + 1, nxt);
+    if (!cur_ok) {
+      if (lane == 0) flag_status(c.status, OSCAR_STATUS_BAD_PAGE);
+    } else {
+      const int j = j0 + wave + AW * i;
+      const int nvalid = min(PAGE, nh - PAGE * j);
+      // ---- scores: D[t][n] = sum_c code_tc q'_cn, per accumulator
+      f32x4 dacc[NA];
+#pragma unroll
+      for (int ai = 0; ai < NA; ++ai) dacc[ai] = f32x4{cinit[ai], cinit[ai], cinit[ai], cinit[ai]};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int ai = C::grp_of_kblock(k) / C::CG;
+        const f16x8 bq = as_f16x8(frag_lds[(4 * k) * 64 + lane], frag_lds[(4 * k + 1) * 64 + lane],
+                                  frag_lds[(4 * k + 2) * 64 + lane], frag_lds[(4 * k + 3) * 64 + lane]);
+        dacc[ai] = mfma_k(expand_k(cur.kc[0], cur.kc[1], k), bq, dacc[ai]);
+      }
+      float sc[4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        float v = 0.f;
+#pragma unroll
+        for (int ai = 0; ai < NA; ++ai) {
+          const uint32_t sz = cur.km[ai][ii];
+          v = fmaf(lo_f16(sz) * inv_kq, dacc[ai][ii], fmaf(hi_f16(sz), zq[ai], v));
+        }
+        if constexpr (GQA < 16) v += row_ror<GQA>(v);
+        if constexpr (2 * GQA < 16) v += row_ror<2 * GQA>(v);
+        if constexpr (4 * GQA < 16) v += row_ror<4 * GQA>(v);
+        if constexpr (8 * GQA < 16) v += row_ror<8 * GQA>(v);
+        sc[ii] = (4 * qd + ii < nvalid) ? v : -INFINITY;
+        mx = fmaxf(mx, sc[ii]);
+      }
+      // ---- online softmax, max raised lazily
+      if (__any(mx > m_run + LAZY_TH)) {
+        const float mm = quad_max(fmaxf(mx, m_run));
+        const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - mm);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) acc[r] *= alpha;
+#pragma unroll
+        for (int ai = 0; ai < NA; ++ai) {
+          corr[ai] *= alpha;
+          zacc[ai] *= alpha;
+        }
+        l_run *= alpha;
+        m_run = mm;
+      }
+      float p[4];
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        p[ii] = (sc[ii] == -INFINITY) ? 0.f : fast_exp2(sc[ii] - m_run);
+        l_run += p[ii];
+      }
+      // ---- PV operand: p * s * (1/w) * 2^k as fp16 high / low parts
+      f16x4 bp[NA];
+#pragma unroll
       for (int ai = 0; ai < NA; ++ai) {
-        const uint32_t sz = km[ai][i];
-        v = fmaf(lo_f16(sz) * inv_kq, dacc[ai][i], fmaf(hi_f16(sz), zq[ai], v));
+        _Float16 e[4];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const uint32_t sz = cur.vm[ai][ii];
+          const bool ok = gval[ai] && (4 * qd + ii < nvalid);
+          const float mult = (ii < 2) ? 4.f : 16.f;
+          const float x = ok ? p[ii] * lo_f16(sz) * (mult * a.pv_scale) : 0.f;
+          const _Float16 hi = _Float16(x);
+          e[ii] = part ? _Float16(x - float(hi)) : hi;
+          corr[ai] += float(e[ii]);
+          zacc[ai] = ok ? fmaf(p[ii], hi_f16(sz), zacc[ai]) : zacc[ai];
+        }
+        bp[ai] = f16x4{e[0], e[1], e[2], e[3]};
       }
-      if constexpr (GQA < 16) v += row_ror<GQA>(v);
-      if constexpr (2 * GQA < 16) v += row_ror<2 * GQA>(v);
-      if constexpr (4 * GQA < 16) v += row_ror<4 * GQA>(v);
-      if constexpr (8 * GQA < 16) v += row_ror<8 * GQA>(v);
-      sc[i] = (4 * qd + i < nvalid) ? v : -INFINITY;
-      mx = fmaxf(mx, sc[i]);
-    }
-    // ---- online softmax, max raised lazily
-    if (__any(mx > m_run + LAZY_TH)) {
-      const float mm = quad_max(fmaxf(mx, m_run));
-      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - mm);
-      for (int r = 0; r < 8; ++r) acc[r] *= alpha;
-      for (int ai = 0; ai < NA; ++ai) {
-        corr[ai] *= alpha;
-        zacc[ai] *= alpha;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int ai = C::grp_of_rblock(r) / C::CG;
+        acc[r] = mfma_v(expand_v(cur.vc[0], cur.vc[1], r), bp[ai], acc[r]);
       }
-      l_run *= alpha;
-      m_run = mm;
     }
-    float p[4];
-    for (int i = 0; i < 4; ++i) {
-      p[i] = (sc[i] == -INFINITY) ? 0.f : fast_exp2(sc[i] - m_run);
-      l_run += p[i];
-    }
-    // ---- PV operand: p * s * (1/w) * 2^k as fp16 high / low parts
-    f16x4 bp[NA];
-    for (int ai = 0; ai < NA; ++ai) {
-      _Float16 e[4];
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t sz = vm[ai][i];
-        const bool ok = gval[ai] && (4 * qd + i < nvalid);
-        const float mult = (i < 2) ? 4.f : 16.f;
-        const float x = ok ? p[i] * lo_f16(sz) * (mult * a.pv_scale) : 0.f;
-        const _Float16 hi = _Float16(x);
-        e[i] = part ? _Float16(x - float(hi)) : hi;
-        corr[ai] += float(e[i]);
-        zacc[ai] = ok ? fmaf(p[i], hi_f16(sz), zacc[ai]) : zacc[ai];
-      }
-      bp[ai] = f16x4{e[0], e[1], e[2], e[3]};
-    }
-    for (int r = 0; r < 8; ++r) {
-      const int ai = C::grp_of_rblock(r) / C::CG;
-      acc[r] = mfma_v(expand_v(vc[0], vc[1], r), bp[ai], acc[r]);
-    }
+    cur = nxt;
+    cur_ok = nxt_ok;
   }
 
   // ---- this wave's o[h][c], m[h], l[h] into LDS
   const float lt = quad_sum(l_run);
+#pragma unroll
   for (int ai = 0; ai < NA; ++ai) {
     corr[ai] = quad_sum(corr[ai]);
     zacc[ai] = quad_sum(zacc[ai]);
   }
+#pragma unroll
   for (int r = 0; r < 8; ++r) {
     const int g = C::grp_of_rblock(r);
     const int ai = g / C::CG;
-    for (int i = 0; i < 4; ++i) {
-      float v = acc[r][i] - corr[ai];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      float v = acc[r][ii] - corr[ai];
       v += row_ror<16 - GQA>(v);  // add the low-part column n + GQA
       if (part == 0 && ncol && cg == g % C::CG)
-        o_lds[h * D + 16 * r + 4 * qd + i] = fmaf(v, a.pv_unscale, zacc[ai]);
+        o_lds[h * D + 16 * r + 4 * qd + ii] = fmaf(v, a.pv_unscale, zacc[ai]);
     }
   }
   if (qd == 0 && n < GQA) {
@@ -319,23 +506,94 @@ __device__ inline uint32_t raw_valid_rows(int L, int page) {
   return m;
 }
 
+// The last workgroup of (b, hk): merge `used` splits per query head, rotate
+// the history part back with R_V^T, add the raw part, normalise.
+template <int GQA>
+__device__ void merge_group(const StepArgs &a, int b, int hk, int used, float *lds, int tid) {
+  const int wave = tid >> 6, lane = tid & 63;
+  const int64_t head_stride = int64_t(1 + a.n_splits) * PART_STRIDE;
+  const float *parts0 = a.parts + (int64_t(b) * a.n_q_heads + hk * GQA) * head_stride;
+  float *w_lds = lds;                    // [GQA][used]
+  float *rot = w_lds + GQA * used;       // [GQA][128] history part (unnormalised)
+  float *plain = rot + GQA * D;          // [GQA][128]
+  float *lsum = plain + GQA * D;         // [GQA]
+  float *acc4 = lsum + 8;                // [4][GQA][128]
+  // weights per head: wave w handles head w
+  if (wave < GQA) {
+    const float *ph = parts0 + wave * head_stride;
+    float m = -INFINITY;
+    for (int s = lane; s < used; s += 64) m = fmaxf(m, ph[s * PART_STRIDE + D]);
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    float l = 0.f;
+    for (int s = lane; s < used; s += 64) {
+      const float ms = ph[s * PART_STRIDE + D];
+      const float w = (ms == -INFINITY) ? 0.f : fast_exp2(ms - m);
+      w_lds[wave * used + s] = w;
+      l = fmaf(w, ph[s * PART_STRIDE + D + 1], l);
+    }
+    for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
+    if (lane == 0) lsum[wave] = l;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < GQA * D; idx += AW * 64) {
+    const int h = idx / D, ch = idx % D;
+    const float *ph = parts0 + h * head_stride;
+    float o = 0.f;
+    for (int s = 1; s < used; ++s) o = fmaf(w_lds[h * used + s], ph[s * PART_STRIDE + ch], o);
+    rot[idx] = o;
+    plain[idx] = w_lds[h * used] * ph[ch];
+  }
+  __syncthreads();
+  // (rot R_V^T)[h][c] = sum_i rot[h][i] R_V[c][i]; thread: c = tid % 128, i-quarter tid / 128
+  {
+    const int ch = tid & (D - 1), qt = tid >> 7;
+    const float *R = reinterpret_cast<const float *>(a.fv + FORM_R) + ch * D + 32 * qt;
+    float acc[GQA];
+#pragma unroll
+    for (int h = 0; h < GQA; ++h) acc[h] = 0.f;
+#pragma unroll
+    for (int i4 = 0; i4 < 8; ++i4) {
+      const f32x4 r = *reinterpret_cast<const f32x4 *>(R + 4 * i4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int h = 0; h < GQA; ++h) acc[h] = fmaf(rot[h * D + 32 * qt + 4 * i4 + e], r[e], acc[h]);
+    }
+#pragma unroll
+    for (int h = 0; h < GQA; ++h) acc4[(qt * GQA + h) * D + ch] = acc[h];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < GQA * D; idx += AW * 64) {
+    const int h = idx / D, ch = idx % D;
+    const float back = acc4[(0 * GQA + h) * D + ch] + acc4[(1 * GQA + h) * D + ch] +
+                       acc4[(2 * GQA + h) * D + ch] + acc4[(3 * GQA + h) * D + ch];
+    a.out[(int64_t(b) * a.n_q_heads + hk * GQA + h) * D + ch] = (back + plain[idx]) / lsum[h];
+  }
+}
+
 template <int GQA, int NG>
-__global__ void __launch_bounds__(WAVES * 64) split_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(AW * 64) attend_kernel(StepArgs a) {
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const oscar_layer_cache &c = a.c;
-  const int L = a.seq_lens[b];
-  __shared__ float o_lds[WAVES * GQA * D];
-  __shared__ float m_lds[WAVES * GQA], l_lds[WAVES * GQA];
-  if (!valid_len(L, a.max_seq_len)) {
-    if (tid == 0 && split == 0 && hk == 0) flag_status(c.status, OSCAR_STATUS_BAD_LEN);
-    return;
-  }
+  const int L = a.k_new ? a.len_before[b] + 1 : a.seq_lens[b];
+  constexpr int LDS_COMBINE = AW * GQA * D + 2 * AW * GQA;
+  constexpr int LDS_MERGE = 6 * GQA * D + 8 + GQA * (MAX_SPLITS + 1);
+  __shared__ float lds[LDS_COMBINE > LDS_MERGE ? LDS_COMBINE : LDS_MERGE];
+  __shared__ uint32_t frag_lds[FRAG_DW * 64];
+  __shared__ int last_s;
+  if (!valid_len(L, a.max_seq_len)) return;  // flagged (and out zeroed) by the prologue
+  const int pages = n_hist_pages(L);
+  const int used = 1 + (pages + a.pages_per_split - 1) / a.pages_per_split;
+  if (split >= used) return;
+  float *o_lds = lds;
+  float *m_lds = lds + AW * GQA * D;
+  float *l_lds = m_lds + AW * GQA;
   float *o_w = o_lds + wave * GQA * D;
   if (split == 0) {
     Bf16Wave<GQA> st;
     st.init(a.q + (int64_t(b) * a.n_q_heads + hk * GQA) * D, a.sm_scale, lane);
-    for (int pg = wave; pg < BF16_PT; pg += WAVES) {
+    for (int pg = wave; pg < BF16_PT; pg += AW) {
       const uint32_t valid = raw_valid_rows(L, pg);
       if (!valid) continue;
       const int page = c.bf16_pt[b * BF16_PT + pg];
@@ -344,136 +602,109 @@ __global__ void __launch_bounds__(WAVES * 64) split_kernel(DecodeArgs a) {
         continue;
       }
       const uint16_t *base = c.bf16 + (int64_t(page) * c.n_kv_heads + hk) * 2 * PAGE * D;
-      st.page(base, base + PAGE * D, valid, lane);
+      typename Bf16Wave<GQA>::Loads ld;
+      Bf16Wave<GQA>::issue(base, base + PAGE * D, ld, lane);
+      st.compute(ld, valid, lane);
     }
     st.finish(o_w, m_lds + wave * GQA, l_lds + wave * GQA, lane);
   } else {
-    const int pages = n_hist_pages(L);
+    const uint32_t *fr = a.frag + (int64_t(b) * c.n_kv_heads + hk) * FRAG_DW * 64;
+    for (int e = tid; e < FRAG_DW * 64; e += AW * 64) frag_lds[e] = fr[e];
+    __syncthreads();
     const int j0 = (split - 1) * a.pages_per_split;
     const int j1 = min(pages, j0 + a.pages_per_split);
-    history_wave<GQA, NG>(a, b, hk, L, j0, j1, wave, lane, o_w, m_lds + wave * GQA, l_lds + wave * GQA);
+    history_wave<GQA, NG>(a, b, hk, L, j0, j1, wave, lane, frag_lds, o_w, m_lds + wave * GQA,
+                          l_lds + wave * GQA);
   }
   __syncthreads();
-  float *part0 = a.parts + ((int64_t(b) * a.n_q_heads + hk * GQA) * (1 + a.n_splits) + split) * PART_STRIDE;
-  combine_waves<GQA>(o_lds, m_lds, l_lds, part0, int64_t(1 + a.n_splits) * PART_STRIDE, tid);
-}
-
-// ------------------------------------------------------------------ merge
-
-__global__ void __launch_bounds__(256) merge_kernel(DecodeArgs a) {
-  const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int L = a.seq_lens[b];
-  float *o = a.out + (int64_t(b) * a.n_q_heads + hq) * D;
-  if (!valid_len(L, a.max_seq_len)) {
-    if (tid < D) o[tid] = 0.f;
-    return;
-  }
-  const int used = 1 + (n_hist_pages(L) + a.pages_per_split - 1) / a.pages_per_split;
-  const float *parts = a.parts + (int64_t(b) * a.n_q_heads + hq) * (1 + a.n_splits) * PART_STRIDE;
-  __shared__ float w_s[1024];
-  __shared__ float red[256];
-  __shared__ float rot[2][D];
-  // max over splits
-  float m = -INFINITY;
-  for (int s = tid; s < used; s += 256) m = fmaxf(m, parts[s * PART_STRIDE + D]);
-  red[tid] = m;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
-    __syncthreads();
-  }
-  const float mst = red[0];
-  __syncthreads();
-  float l = 0.f;
-  for (int s = tid; s < used; s += 256) {
-    const float ms = parts[s * PART_STRIDE + D];
-    const float w = (ms == -INFINITY) ? 0.f : fast_exp2(ms - mst);
-    if (s < 1024) w_s[s] = w;
-    l = fmaf(w, parts[s * PART_STRIDE + D + 1], l);
-  }
-  red[tid] = l;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (tid < off) red[tid] += red[tid + off];
-    __syncthreads();
-  }
-  const float lsum = red[0];
-  // history splits 1..used-1 in two halves, channel = tid % 128
-  const int ch = tid & (D - 1), half = tid >> 7;
-  float acc = 0.f;
-  for (int s = 1 + half; s < used; s += 2) {
-    const float ms = parts[s * PART_STRIDE + D];
-    const float w = s < 1024 ? w_s[s] : ((ms == -INFINITY) ? 0.f : fast_exp2(ms - mst));
-    acc = fmaf(w, parts[s * PART_STRIDE + ch], acc);
-  }
-  rot[half][ch] = acc;
-  __syncthreads();
-  if (tid < D) {
-    const float *RT = reinterpret_cast<const float *>(a.fv + FORM_RT);
-    float back = 0.f;  // (rot R_V^T)[tid] = sum_i rot[i] R_V[tid][i]
-    for (int i = 0; i < D; ++i) back = fmaf(rot[0][i] + rot[1][i], RT[i * D + tid], back);
-    const float plain = w_s[0] * parts[tid];
-    o[tid] = (back + plain) / lsum;
-  }
+  const int64_t head_stride = int64_t(1 + a.n_splits) * PART_STRIDE;
+  float *part0 = a.parts + (int64_t(b) * a.n_q_heads + hk * GQA) * head_stride + split * PART_STRIDE;
+  combine_waves<GQA, AW>(o_lds, m_lds, l_lds, part0, head_stride, tid);
+  // ---- the last workgroup of (b, hk) merges
+  if (!elect_last(a.count + b * c.n_kv_heads + hk, uint32_t(used), &last_s, tid)) return;
+  merge_group<GQA>(a, b, hk, used, lds, tid);
 }
 
 // ------------------------------------------------------------------ launch
 
 template <int GQA, int NG>
-static hipError_t launch_t(const DecodeArgs &a, int batch, int hkv, hipStream_t s) {
-  hipLaunchKernelGGL((qprep_kernel<GQA, NG>), dim3(hkv, batch), dim3(256), 0, s, a);
+static hipError_t launch_t(const StepArgs &a, int batch, int hkv, bool attend, hipStream_t s) {
+  hipLaunchKernelGGL((prologue_kernel<GQA, NG>), dim3(hkv, batch), dim3(PRO_THREADS), 0, s, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((split_kernel<GQA, NG>), dim3(1 + a.n_splits, hkv, batch), dim3(WAVES * 64), 0, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_kernel, dim3(a.n_q_heads, batch), dim3(256), 0, s, a);
+  if (e != hipSuccess || !attend) return e;
+  hipLaunchKernelGGL((attend_kernel<GQA, NG>), dim3(1 + a.n_splits, hkv, batch), dim3(AW * 64), 0, s, a);
   return hipGetLastError();
 }
 
 template <int GQA>
-static hipError_t launch_g(const DecodeArgs &a, int G, int batch, int hkv, hipStream_t s) {
+static hipError_t launch_g(const StepArgs &a, int G, int batch, int hkv, bool attend, hipStream_t s) {
   switch (G) {
-    case 32: return launch_t<GQA, 4>(a, batch, hkv, s);
-    case 64: return launch_t<GQA, 2>(a, batch, hkv, s);
-    default: return launch_t<GQA, 1>(a, batch, hkv, s);
+    case 32: return launch_t<GQA, 4>(a, batch, hkv, attend, s);
+    case 64: return launch_t<GQA, 2>(a, batch, hkv, attend, s);
+    default: return launch_t<GQA, 1>(a, batch, hkv, attend, s);
+  }
+}
+
+static float pv_scale_for(float clip_v) {
+  // PV operand: p <= 2^LAZY_TH, s <= 2 clip / 3, 1/w <= 16; keep it under 2^15
+  float k = 1.f;
+  const float vmax = 8.f * 16.f * (2.f * clip_v / 3.f);
+  while (vmax * k > 32768.f) k *= 0.5f;
+  while (vmax * k * 2.f <= 32768.f && k < 65536.f) k *= 2.f;
+  return k;
+}
+
+hipError_t launch_decode_step(const oscar_layer_cache &c, RotArg rk, RotArg rv, const uint16_t *k_new,
+                              const uint16_t *v_new, const int32_t *len_before, const uint16_t *q,
+                              int n_q_heads, const int32_t *seq_lens, int batch, int max_seq_len,
+                              float sm_scale, float *out, void *ws, hipStream_t s) {
+  StepArgs a;
+  a.c = c;
+  a.fk = rk.forms;
+  a.fv = rv.forms;
+  a.clip_k = rk.clip;
+  a.clip_v = rv.clip;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.len_before = len_before;
+  a.q = q;
+  a.seq_lens = seq_lens;
+  a.n_q_heads = n_q_heads;
+  a.max_seq_len = max_seq_len;
+  a.sm_scale = sm_scale;
+  a.out = out;
+  a.frag = nullptr;
+  a.count = nullptr;
+  a.parts = nullptr;
+  a.pages_per_split = AW;
+  a.n_splits = 0;
+  a.pv_scale = pv_scale_for(rv.clip);
+  a.pv_unscale = 1.f / a.pv_scale;
+  const bool attend = q != nullptr;
+  if (attend) {
+    const SplitPlan p = plan_int2_splits(batch, c.n_kv_heads, max_seq_len);
+    a.pages_per_split = p.pages_per_split;
+    a.n_splits = p.n_splits;
+    uint8_t *w = static_cast<uint8_t *>(ws);
+    a.frag = reinterpret_cast<uint32_t *>(w);
+    a.count = reinterpret_cast<uint32_t *>(w + frag_bytes(batch, c.n_kv_heads));
+    a.parts = reinterpret_cast<float *>(w + frag_bytes(batch, c.n_kv_heads) + count_bytes(batch, c.n_kv_heads));
+  }
+  const int gqa = attend ? n_q_heads / c.n_kv_heads : 1;
+  switch (gqa) {
+    case 1: return launch_g<1>(a, c.group, batch, c.n_kv_heads, attend, s);
+    case 2: return launch_g<2>(a, c.group, batch, c.n_kv_heads, attend, s);
+    case 4: return launch_g<4>(a, c.group, batch, c.n_kv_heads, attend, s);
+    case 8: return launch_g<8>(a, c.group, batch, c.n_kv_heads, attend, s);
+    default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_decode_int2(const oscar_layer_cache &c, RotArg rk, RotArg rv, const uint16_t *q,
                               int n_q_heads, const int32_t *seq_lens, int batch, int max_seq_len,
                               float sm_scale, float *out, void *ws, hipStream_t s) {
-  const SplitPlan p = plan_int2_splits(batch, c.n_kv_heads, max_seq_len);
-  DecodeArgs a;
-  a.c = c;
-  a.fk = rk.forms;
-  a.fv = rv.forms;
-  a.q = q;
-  a.seq_lens = seq_lens;
-  a.n_q_heads = n_q_heads;
-  a.max_seq_len = max_seq_len;
-  a.pages_per_split = p.pages_per_split;
-  a.n_splits = p.n_splits;
-  a.sm_scale = sm_scale;
-  // PV operand scale: p <= 2^LAZY_TH, s <= 2 clip / 3, 1/w <= 16; keep the
-  // largest value under 2^15
-  float k = 1.f;
-  const float vmax = 8.f * 16.f * (2.f * rv.clip / 3.f);
-  while (vmax * k > 32768.f) k *= 0.5f;
-  while (vmax * k * 2.f <= 32768.f && k < 65536.f) k *= 2.f;
-  a.pv_scale = k;
-  a.pv_unscale = 1.f / k;
-  a.frag = static_cast<uint32_t *>(ws);
-  a.parts = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + frag_bytes(batch, c.n_kv_heads));
-  a.out = out;
-  const int gqa = n_q_heads / c.n_kv_heads;
-  switch (gqa) {
-    case 1: return launch_g<1>(a, c.group, batch, c.n_kv_heads, s);
-    case 2: return launch_g<2>(a, c.group, batch, c.n_kv_heads, s);
-    case 4: return launch_g<4>(a, c.group, batch, c.n_kv_heads, s);
-    case 8: return launch_g<8>(a, c.group, batch, c.n_kv_heads, s);
-    default: return hipErrorInvalidValue;
-  }
+  return launch_decode_step(c, rk, rv, nullptr, nullptr, nullptr, q, n_q_heads, seq_lens, batch, max_seq_len,
+                            sm_scale, out, ws, s);
 }
 
 }  // namespace oscar

@@ -25,6 +25,13 @@ hipError_t launch_decode_int2(const oscar_layer_cache &c, RotArg rk, RotArg rv,
 
 size_t decode_int2_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int max_seq_len);
 
+// Append one token per request (k_new / v_new [B][Hkv][128] at positions
+// len_before[b]) and, when q is non-null, decode with lengths len_before + 1.
+hipError_t launch_decode_step(const oscar_layer_cache &c, RotArg rk, RotArg rv, const uint16_t *k_new,
+                              const uint16_t *v_new, const int32_t *len_before, const uint16_t *q,
+                              int n_q_heads, const int32_t *seq_lens, int batch, int max_seq_len,
+                              float sm_scale, float *out, void *ws, hipStream_t s);
+
 hipError_t launch_decode_bf16(const uint16_t *q, const uint16_t *kv, int64_t n_pages,
                               const int32_t *pt, int pt_stride, const int32_t *seq_lens,
                               int batch, int max_seq_len, int n_q_heads, int n_kv_heads,

@@ -215,6 +215,28 @@ OSCAR_API int oscar_decode_attn(const oscar_layer_cache *cache,
                       void *workspace, size_t workspace_bytes,
                       oscar_stream_t stream);
 
+/* One generation step of a layer: write-on-append of one token per request
+ * followed by the decode over the grown cache ([abs] "fused Triton write and
+ * decode kernels"; [nl]/[fr] §2.2.B).  Request b's new token k_new[b],
+ * v_new[b] (device bf16 [batch][Hkv][128]) goes to position len_before[b]
+ * (device int32 [batch]); a token leaving the recent window moves to history
+ * exactly as in oscar_write_kv.  Then q (device bf16 [batch][Hq][128])
+ * attends over all len_before[b] + 1 tokens as in oscar_decode_attn, which
+ * must be <= max_seq_len.  Same result as oscar_write_kv with one token per
+ * request followed by oscar_decode_attn, in two kernel launches.  The
+ * workspace is the one of oscar_decode_attn (oscar_decode_workspace_bytes);
+ * it may hold anything on entry.  Calls that share a workspace must not run
+ * concurrently. */
+OSCAR_API int oscar_decode_step(const oscar_layer_cache *cache,
+                                const oscar_rotation *rot_k,
+                                const oscar_rotation *rot_v,
+                                const uint16_t *k_new, const uint16_t *v_new,
+                                const int32_t *len_before, const uint16_t *q,
+                                int32_t n_q_heads, int32_t batch,
+                                int32_t max_seq_len, float sm_scale,
+                                float *out, void *workspace,
+                                size_t workspace_bytes, oscar_stream_t stream);
+
 /* Workspace for oscar_bf16_paged_decode. */
 OSCAR_API size_t oscar_bf16_decode_workspace_bytes(int32_t batch, int32_t n_q_heads,
                                          int32_t n_kv_heads,
@@ -225,7 +247,10 @@ OSCAR_API size_t oscar_bf16_decode_workspace_bytes(int32_t batch, int32_t n_q_he
  * kv_pages: device bf16 [n_pages][Hkv][2][16][128] (same page format as
  * the BF16 pool); pt: device int32 [batch][pt_stride] — token p of request
  * b is row p%16 of page pt[b][p/16]; other arguments as oscar_decode_attn.
- * status: device uint32 or NULL (OSCAR_STATUS_* bits). */
+ * status: device uint32 or NULL (OSCAR_STATUS_* bits).
+ * The workspace (oscar_bf16_decode_workspace_bytes) holds merge counters:
+ * it must be zero-filled before its first use, and every call leaves them
+ * at zero again.  Calls that share a workspace must not run concurrently. */
 OSCAR_API int oscar_bf16_paged_decode(const uint16_t *q, const uint16_t *kv_pages,
                             int64_t n_pages, const int32_t *pt,
                             int32_t pt_stride, const int32_t *seq_lens,

@@ -254,3 +254,92 @@ def test_calibration_matches_oracle(oscar):
     assert np.abs(R_V - cal["R_V"]).max() < 1e-8
     assert abs(ck - cal["clip_K"]) <= 1e-6 * cal["clip_K"]
     assert abs(cv - cal["clip_V"]) <= 1e-6 * cal["clip_V"]
+
+
+# ------------------------------------------------------------------ decode step
+
+
+def _prefix_cache(sc: Scenario, drop: int):
+    """Oracle cache holding all but the last `drop` tokens of every request."""
+    ref = o.LayerCacheRef(sc.hkv, sc.G, sc.n_hist_pages, sc.n_bf16_pages, sc.hist_pt, sc.bf16_pt)
+    keep = [max(0, L - drop) for L in sc.lens]
+    kp = np.concatenate([t[:n] for t, n in zip(sc.tok_k, keep)])
+    vp = np.concatenate([t[:n] for t, n in zip(sc.tok_v, keep)])
+    cu = np.concatenate([[0], np.cumsum(keep)]).astype(np.int32)
+    ref.write(sc.R_K, sc.R_V, sc.clip_k, sc.clip_v, kp, vp, cu, np.zeros(len(keep), np.int32))
+    return ref
+
+
+@pytest.mark.parametrize("G", [32, 64, 128])
+def test_decode_step_appends_then_decodes(oscar, G):
+    # lengths after the step; the appended token pushes position L-129 out of
+    # the window whenever L - 1 >= 144
+    lens = [1, 16, 17, 143, 144, 145, 146, 160, 161, 500, 1201]
+    sc = Scenario(1100 + G, 8, 2, G, lens)
+    pre = _prefix_cache(sc, 1)
+    full = sc.oracle_cache()
+    cache = gpu_cache(oscar, sc, hist=pre.hist, bf16=pre.bf16)
+    rk, rv = gpu_rotations(oscar, sc)
+    k_last = np.stack([t[-1] for t in sc.tok_k])
+    v_last = np.stack([t[-1] for t in sc.tok_v])
+    before = torch.tensor([L - 1 for L in lens], dtype=torch.int32, device="cuda")
+    out = oscar.decode_step(cache, rk, rv, to_dev_bf16(k_last), to_dev_bf16(v_last), before, to_dev_bf16(sc.q),
+                            max(lens), SCALE)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) == 0
+    stats = compare_history(cache.hist.cpu().numpy(), sc.hist_pt, sc.tok_k, sc.tok_v, sc.lens,
+                            sc.R_K, sc.R_V, sc.clip_k, sc.clip_v, G)
+    assert_history_ok(stats)
+    check_raw_rows(sc, bf16_pool_bits(cache.bf16), full)
+    assert_decode_close(out.cpu().numpy(), sc.oracle_decode(full), f"decode_step G={G}")
+
+
+def test_decode_step_many_steps(oscar):
+    # 40 consecutive steps: ring slots are reused and evicted tokens fill two
+    # history pages row by row
+    lens = [330, 200, 150]
+    steps = 40
+    sc = Scenario(1200, 8, 2, 64, lens)
+    pre = _prefix_cache(sc, steps)
+    full = sc.oracle_cache()
+    cache = gpu_cache(oscar, sc, hist=pre.hist, bf16=pre.bf16)
+    rk, rv = gpu_rotations(oscar, sc)
+    ws = torch.empty(oscar.decode_workspace_bytes(len(lens), 8, 2, max(lens)), dtype=torch.uint8, device="cuda")
+    q = to_dev_bf16(sc.q)
+    for s in range(steps, 0, -1):
+        k_s = np.stack([t[L - s] for t, L in zip(sc.tok_k, lens)])
+        v_s = np.stack([t[L - s] for t, L in zip(sc.tok_v, lens)])
+        before = torch.tensor([L - s for L in lens], dtype=torch.int32, device="cuda")
+        out = oscar.decode_step(cache, rk, rv, to_dev_bf16(k_s), to_dev_bf16(v_s), before, q, max(lens), SCALE,
+                                workspace=ws)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) == 0
+    stats = compare_history(cache.hist.cpu().numpy(), sc.hist_pt, sc.tok_k, sc.tok_v, sc.lens,
+                            sc.R_K, sc.R_V, sc.clip_k, sc.clip_v, 64)
+    assert_history_ok(stats)
+    check_raw_rows(sc, bf16_pool_bits(cache.bf16), full)
+    assert_decode_close(out.cpu().numpy(), sc.oracle_decode(full), "decode_step x40")
+
+
+def test_bf16_decode_reuses_workspace(oscar):
+    # the merge counters in the workspace must be back at zero after a call
+    lens = [700, 33]
+    ld = synth.LayerData(1300, 0, 8, 2)
+    k, v = ld.cache_kv(sum(lens))
+    pt, npages = synth.shuffled_page_tables(1300, 0, lens, n_pages_fn=lambda L: (L + 15) // 16)
+    pages = np.zeros((npages, 2, 2, 16, 128), dtype=np.uint16)
+    off = 0
+    for b, L in enumerate(lens):
+        p = np.arange(L)
+        pages[pt[b, p // 16], :, 0, p % 16] = k[off:off + L]
+        pages[pt[b, p // 16], :, 1, p % 16] = v[off:off + L]
+        off += L
+    q = ld.decode_q(len(lens))
+    ref = o.bf16_paged_decode(q, pages, pt, lens, SCALE)
+    ws = torch.zeros(oscar.bf16_decode_workspace_bytes(2, 8, 2, max(lens)), dtype=torch.uint8, device="cuda")
+    args = (to_dev_bf16(q), to_dev_bf16(pages), torch.from_numpy(pt).cuda(),
+            torch.tensor(lens, dtype=torch.int32, device="cuda"), max(lens), SCALE)
+    for _ in range(3):
+        out = oscar.bf16_paged_decode(*args, workspace=ws)
+        torch.cuda.synchronize()
+        assert_decode_close(out.cpu().numpy(), ref, "bf16 repeated")
