@@ -215,20 +215,4 @@ __device__ inline void combine_waves(const float *o_lds, const float *m_lds, con
   }
 }
 
-// After a workgroup has written its partial: publish it and count the
-// workgroup in (device scope).  True in exactly one workgroup, the last of
-// `expected`; that one then sees every partial.
-__device__ inline bool elect_last(uint32_t *count, uint32_t expected, int *flag_lds, int tid) {
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t done = __hip_atomic_fetch_add(count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    *flag_lds = done == expected - 1;
-  }
-  __syncthreads();
-  const bool last = *flag_lds;
-  if (last) __threadfence();
-  return last;
-}
-
 }  // namespace oscar

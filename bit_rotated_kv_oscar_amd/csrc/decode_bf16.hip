@@ -4,9 +4,8 @@
 // takes every 8th page of the split (page ids preloaded, the next page's
 // loads issued before the current page computes).  Scores on the bf16 matrix
 // cores, PV on the vector ALUs, fp32 accumulation.  Each workgroup writes an
-// unnormalised partial per query head; the last workgroup of a (request, KV
-// head) LSE-merges them and normalises.  The merge counters live in the
-// workspace and are left at zero by every call.
+// unnormalised partial per query head; a merge kernel (one block per
+// (request, KV head)) LSE-combines them and normalises.
 #include "attn_common.h"
 
 namespace oscar {
@@ -14,16 +13,17 @@ namespace oscar {
 constexpr int BW = 8;  // waves per workgroup
 
 SplitPlan plan_bf16_splits(int batch, int n_kv_heads, int max_seq_len) {
+  // as for the INT2 decode: fill one round of resident workgroups (two per
+  // CU) when the batch is small, else splits of 8 pages per wave
   const int pages = (max_seq_len + PAGE - 1) / PAGE;
-  const int64_t total = int64_t(pages) * batch * n_kv_heads;
-  int64_t pw = (total + int64_t(BW) * 512 - 1) / (int64_t(BW) * 512);
-  if (pw < 2) pw = 2;
-  if (pw > 64) pw = 64;
-  const int64_t min_pw = (pages + int64_t(BW) * 255 - 1) / (int64_t(BW) * 255);
-  if (pw < min_pw) pw = min_pw;
+  const int64_t units = int64_t(batch) * n_kv_heads;
+  int64_t pps = units <= 512 ? (pages + 512 / units - 1) / (512 / units) : 8 * BW;
+  if (pps < BW) pps = BW;
+  const int64_t min_pps = (pages + 255 - 1) / 255;
+  if (pps < min_pps) pps = min_pps;
   SplitPlan p;
-  p.pages_per_split = int(pw) * BW;
-  p.n_splits = (pages + p.pages_per_split - 1) / p.pages_per_split;
+  p.pages_per_split = int(pps);
+  p.n_splits = int((pages + pps - 1) / pps);
   return p;
 }
 
@@ -33,7 +33,7 @@ static size_t count_off(int batch, int n_q_heads, int n_splits) {
 
 size_t decode_bf16_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int max_seq_len) {
   const SplitPlan p = plan_bf16_splits(batch, n_kv_heads, max_seq_len);
-  return count_off(batch, n_q_heads, p.n_splits) + ((size_t(batch) * n_kv_heads * 4 + 255) & ~size_t(255));
+  return count_off(batch, n_q_heads, p.n_splits);
 }
 
 struct Bf16Args {
@@ -47,16 +47,21 @@ struct Bf16Args {
   float *out;
   uint32_t *status;
   float *parts;     // [B][Hq][n_splits][PART_STRIDE]
-  uint32_t *count;  // [B][Hkv]
 };
 
 template <int GQA>
-__device__ void bf16_merge(const Bf16Args &a, int b, int hk, int used, float *lds, int tid) {
+__global__ void __launch_bounds__(1024) bf16_merge_kernel(Bf16Args a) {
+  const int hk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
+  const int L = a.seq_lens[b];
+  if (L < 1 || L > a.max_seq_len) return;  // output zeroed by the split kernel
+  const int pages = (L + PAGE - 1) / PAGE;
+  const int used = (pages + a.pages_per_split - 1) / a.pages_per_split;
   const int64_t head_stride = int64_t(a.n_splits) * PART_STRIDE;
   const float *parts0 = a.parts + (int64_t(b) * a.n_q_heads + hk * GQA) * head_stride;
-  float *w_lds = lds;              // [GQA][used]
-  float *lsum = w_lds + GQA * used;
+  __shared__ float w_lds[GQA][256];
+  __shared__ float lsum[GQA];
+  __shared__ float half_o[2][GQA][D];
   if (wave < GQA) {
     const float *ph = parts0 + wave * head_stride;
     float m = -INFINITY;
@@ -66,19 +71,32 @@ __device__ void bf16_merge(const Bf16Args &a, int b, int hk, int used, float *ld
     for (int s = lane; s < used; s += 64) {
       const float ms = ph[s * PART_STRIDE + D];
       const float w = (ms == -INFINITY) ? 0.f : fast_exp2(ms - m);
-      w_lds[wave * used + s] = w;
+      w_lds[wave][s] = w;
       l = fmaf(w, ph[s * PART_STRIDE + D + 1], l);
     }
     for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
     if (lane == 0) lsum[wave] = l;
   }
   __syncthreads();
-  for (int idx = tid; idx < GQA * D; idx += BW * 64) {
+  for (int idx = tid; idx < 2 * GQA * D; idx += 1024) {
+    const int hf = idx / (GQA * D), h = (idx / D) % GQA, ch = idx % D;
+    const float *ph = parts0 + h * head_stride + ch;
+    const int s0 = hf ? used / 2 : 0, s1 = hf ? used : used / 2;
+    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    int s = s0;
+    for (; s + 3 < s1; s += 4) {
+      o0 = fmaf(w_lds[h][s], ph[s * PART_STRIDE], o0);
+      o1 = fmaf(w_lds[h][s + 1], ph[(s + 1) * PART_STRIDE], o1);
+      o2 = fmaf(w_lds[h][s + 2], ph[(s + 2) * PART_STRIDE], o2);
+      o3 = fmaf(w_lds[h][s + 3], ph[(s + 3) * PART_STRIDE], o3);
+    }
+    for (; s < s1; ++s) o0 = fmaf(w_lds[h][s], ph[s * PART_STRIDE], o0);
+    half_o[hf][h][ch] = (o0 + o1) + (o2 + o3);
+  }
+  __syncthreads();
+  for (int idx = tid; idx < GQA * D; idx += 1024) {
     const int h = idx / D, ch = idx % D;
-    const float *ph = parts0 + h * head_stride;
-    float o = 0.f;
-    for (int s = 0; s < used; ++s) o = fmaf(w_lds[h * used + s], ph[s * PART_STRIDE + ch], o);
-    a.out[(int64_t(b) * a.n_q_heads + hk * GQA + h) * D + ch] = o / lsum[h];
+    a.out[(int64_t(b) * a.n_q_heads + hk * GQA + h) * D + ch] = (half_o[0][h][ch] + half_o[1][h][ch]) / lsum[h];
   }
 }
 
@@ -87,10 +105,7 @@ __global__ void __launch_bounds__(BW * 64) bf16_decode_kernel(Bf16Args a) {
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int L = a.seq_lens[b];
-  constexpr int LDS_COMBINE = BW * GQA * D + 2 * BW * GQA;
-  constexpr int LDS_MERGE = GQA * 256 + 8;
-  __shared__ float lds[LDS_COMBINE > LDS_MERGE ? LDS_COMBINE : LDS_MERGE];
-  __shared__ int last_s;
+  __shared__ float lds[BW * GQA * D + 2 * BW * GQA];
   if (L < 1 || L > a.max_seq_len) {
     if (split == 0) {
       if (tid == 0 && hk == 0) flag_status(a.status, OSCAR_STATUS_BAD_LEN);
@@ -135,15 +150,14 @@ __global__ void __launch_bounds__(BW * 64) bf16_decode_kernel(Bf16Args a) {
   const int64_t head_stride = int64_t(a.n_splits) * PART_STRIDE;
   float *part0 = a.parts + (int64_t(b) * a.n_q_heads + hk * GQA) * head_stride + split * PART_STRIDE;
   combine_waves<GQA, BW>(o_lds, m_lds, l_lds, part0, head_stride, tid);
-  uint32_t *cnt = a.count + b * a.n_kv_heads + hk;
-  if (!elect_last(cnt, uint32_t(used), &last_s, tid)) return;
-  bf16_merge<GQA>(a, b, hk, used, lds, tid);
-  if (tid == 0) *cnt = 0u;  // ready for the next call
 }
 
 template <int GQA>
 static hipError_t launch_t(const Bf16Args &a, int batch, hipStream_t s) {
   hipLaunchKernelGGL((bf16_decode_kernel<GQA>), dim3(a.n_splits, a.n_kv_heads, batch), dim3(BW * 64), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bf16_merge_kernel<GQA>), dim3(a.n_kv_heads, batch), dim3(1024), 0, s, a);
   return hipGetLastError();
 }
 
@@ -168,7 +182,6 @@ hipError_t launch_decode_bf16(const uint16_t *q, const uint16_t *kv, int64_t n_p
   a.out = out;
   a.status = status;
   a.parts = static_cast<float *>(ws);
-  a.count = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(ws) + count_off(batch, n_q_heads, p.n_splits));
   switch (n_q_heads / n_kv_heads) {
     case 1: return launch_t<1>(a, batch, s);
     case 2: return launch_t<2>(a, batch, s);

@@ -15,7 +15,7 @@
 //   score_t = sum_g s_tg (q_g . c_tg) + z_tg sum_{i in g} q_i
 //   o       = sum_g [ sum_t (p_t s_tg) c_tg ] + sum_t p_t z_tg
 //
-// Two kernels per call, in stream order:
+// Three kernels per call, in stream order:
 //   prologue (one block per (request, KV head)):
 //     - optional append: the token leaving the recent window (position
 //       L-128 when L >= 144) is read from its ring slot, rotated, clipped,
@@ -23,15 +23,22 @@
 //     - q_rot = q R_K * sm_scale * log2(e) for the query heads of the group,
 //       laid out as the B operand of the score MFMAs (fp16 high + low parts)
 //       with the column sums that cancel the code expansion's constant and
-//       the per-group sums of q_rot; resets the merge counter.
+//       the per-group sums of q_rot.
 //   attend (one workgroup of 8 waves per (request, KV head, split)):
 //     split 0 attends over the raw BF16 sink + recent pages, split s >= 1
 //     over history pages (wave w takes every 8th page of the split, page ids
 //     preloaded, next page's loads issued before the current page computes).
 //     Each workgroup writes an unnormalised partial (o[128], m, l) per query
-//     head; the last workgroup of a (request, KV head) LSE-merges them,
+//     head.
+//   merge (one block per (request, KV head)): LSE-combines the partials,
 //     rotates the history part back with R_V^T, adds the raw part and
-//     normalises (fp32 out).
+//     normalises (fp32 out).  A kernel boundary, not an in-kernel fence, makes
+//     the partials visible: the L2 caches of the eight XCDs are not coherent
+//     with each other, and a device-scope fence writes back and invalidates
+//     the whole L2.
+#include <cmath>
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace oscar {
@@ -63,26 +70,33 @@ SplitPlan plan_int2_splits(int batch, int n_kv_heads, int max_seq_len) {
     p.n_splits = 0;
     return p;
   }
-  // about 512 workgroups (two per CU) for the longest request
-  const int64_t total = int64_t(pages) * batch * n_kv_heads;
-  int64_t pw = (total + int64_t(AW) * 512 - 1) / (int64_t(AW) * 512);
-  if (pw < 2) pw = 2;
-  if (pw > 64) pw = 64;
-  // at most MAX_SPLITS splits (bounds the merge's LDS)
-  const int64_t min_pw = (pages + int64_t(AW) * MAX_SPLITS - 1) / (int64_t(AW) * MAX_SPLITS);
-  if (pw < min_pw) pw = min_pw;
-  p.pages_per_split = int(pw) * AW;
-  p.n_splits = (pages + p.pages_per_split - 1) / p.pages_per_split;
+  // Resident attend workgroups: two per CU on 256 CUs.  When every unit
+  // (request, KV head) fits in one round with at least one history split,
+  // spread each unit's pages over as many splits as that round holds (its
+  // raw workgroup included); otherwise use splits of 8 pages per wave.
+  const int64_t units = int64_t(batch) * n_kv_heads;
+  const int64_t slots = 2 * 256;
+  int64_t pps;
+  if (slots - units >= units) {
+    const int64_t per_unit = (slots - units) / units;
+    pps = (pages + per_unit - 1) / per_unit;
+  } else {
+    pps = 8 * AW;
+  }
+  if (pps < AW) pps = AW;
+  const int64_t min_pps = (pages + MAX_SPLITS - 1) / MAX_SPLITS;  // bounds the merge's LDS
+  if (pps < min_pps) pps = min_pps;
+  p.pages_per_split = int(pps);
+  p.n_splits = int((pages + pps - 1) / pps);
   return p;
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 static size_t frag_bytes(int batch, int hkv) { return align256(size_t(batch) * hkv * FRAG_DW * 64 * 4); }
-static size_t count_bytes(int batch, int hkv) { return align256(size_t(batch) * hkv * 4); }
 
 size_t decode_int2_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int max_seq_len) {
   const SplitPlan p = plan_int2_splits(batch, n_kv_heads, max_seq_len);
-  return frag_bytes(batch, n_kv_heads) + count_bytes(batch, n_kv_heads) +
+  return frag_bytes(batch, n_kv_heads) +
          align256(size_t(batch) * n_q_heads * (1 + p.n_splits) * PART_STRIDE * sizeof(float));
 }
 
@@ -99,8 +113,9 @@ struct StepArgs {
   int n_q_heads, max_seq_len, pages_per_split, n_splits;
   float sm_scale;
   float pv_scale, pv_unscale;     // 2^k and 2^-k applied to the PV operand
+  float pk01, pk23;               // log2(4 * 2^k), log2(16 * 2^k): PV factors of tokens 4q+{0,1}, 4q+{2,3}
+  uint32_t ex_m4, ex_m16, ex_e;   // code expansion constants 0x03000300, 0x00C000C0, 0x3C003C00
   uint32_t *frag;                 // [B][Hkv][FRAG_DW][64]
-  uint32_t *count;                // [B][Hkv] workgroups done (merge election)
   float *parts;                   // [B][Hq][1 + n_splits][PART_STRIDE]
   float *out;                     // [B][Hq][128]
 };
@@ -184,6 +199,17 @@ __global__ void __launch_bounds__(PRO_THREADS) prologue_kernel(StepArgs a) {
   __shared__ float red[256];
   __shared__ int evict_s;
 
+  // R^T rows for this thread (output channel jx, inputs 64 hf .. 64 hf + 63),
+  // loaded first so they overlap the dependent loads below
+  const bool want_q = a.q != nullptr;
+  const int jx = t & (D - 1), hf = t >> 7;
+  f32x4 rr[16];
+  if ((half == 0 && want_q) || a.k_new) {
+    const float *RT = reinterpret_cast<const float *>((half ? a.fv : a.fk) + FORM_RT) + jx * D + 64 * hf;
+#pragma unroll
+    for (int i4 = 0; i4 < 16; ++i4) rr[i4] = *reinterpret_cast<const f32x4 *>(RT + 4 * i4);
+  }
+
   // ---------------- append (optional)
   int evict_pos = -1;  // position leaving the ring, or -1
   uint8_t *evict_blk = nullptr;
@@ -221,13 +247,11 @@ __global__ void __launch_bounds__(PRO_THREADS) prologue_kernel(StepArgs a) {
     }
   }
   // ---------------- query (K half)
-  const bool want_q = a.q != nullptr;
   if (want_q && half == 0) {
     for (int e = t; e < GQA * D; e += 256)
       xin[0][e / D][e % D] = bf16_to_f32(a.q[(int64_t(b) * a.n_q_heads + hk * GQA) * D + e]);
   }
   if (want_q) {
-    if (tid == 0) a.count[b * hkv + hk] = 0u;
     const int L = a.k_new ? a.len_before[b] + 1 : a.seq_lens[b];
     if (!valid_len(L, a.max_seq_len)) {  // attend skips this request: zero its output here
       if (tid == 0 && hk == 0) flag_status(c.status, OSCAR_STATUS_BAD_LEN);
@@ -238,21 +262,21 @@ __global__ void __launch_bounds__(PRO_THREADS) prologue_kernel(StepArgs a) {
   if (tid == 0) evict_s = evict_blk ? 1 : 0;
   __syncthreads();
   // ---------------- rotations: K half rotates q heads + evicted k, V half the evicted v
-  const float *R = reinterpret_cast<const float *>((half ? a.fv : a.fk) + FORM_R);
   {
     // both halves run the same code path (uniform barriers); unused vectors are zero
-    const int jx = t & (D - 1), hf = t >> 7;
     float acc[GQA + 1];
 #pragma unroll
     for (int v = 0; v <= GQA; ++v) acc[v] = 0.f;
     const bool need = (half == 0 && want_q) || evict_s;
     if (need) {
-#pragma unroll 16
-      for (int i = 64 * hf; i < 64 * hf + 64; ++i) {
-        const float r = R[i * D + jx];
 #pragma unroll
-        for (int v = 0; v <= GQA; ++v) acc[v] = fmaf(xin[half][v][i], r, acc[v]);
-      }
+      for (int i4 = 0; i4 < 16; ++i4)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 64 * hf + 4 * i4 + e;
+#pragma unroll
+          for (int v = 0; v <= GQA; ++v) acc[v] = fmaf(xin[half][v][i], rr[i4][e], acc[v]);
+        }
     }
 #pragma unroll
     for (int v = 0; v <= GQA; ++v) part_lds[half][(hf * (GQA + 1) + v) * D + jx] = acc[v];
@@ -307,10 +331,10 @@ __global__ void __launch_bounds__(PRO_THREADS) prologue_kernel(StepArgs a) {
       if ((ch / G) / C::CG == ai) cs += float(bval(ch));
     fr[(16 + ai) * 64 + lane] = __float_as_uint(-cs);
     const int g = ai * C::CG + cg;
-    float zq = 0.f;
+    float zq = 0.f;  // per-group sum of q_rot, in the kq units of the B operand
     if (ncol && part == 0 && g < NG)
       for (int i = 0; i < G; ++i) zq += yout[0][h][g * G + i] * sc;
-    fr[(16 + C::NA + ai) * 64 + lane] = __float_as_uint(zq);
+    fr[(16 + C::NA + ai) * 64 + lane] = __float_as_uint(zq * kq);
   }
   fr[(16 + 2 * C::NA) * 64 + lane] = __float_as_uint(1.f / kq);
 }
@@ -323,7 +347,40 @@ struct PageLoads {
   u32x4 km[NA], vm[NA];
 };
 
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+__device__ inline h2v as_h2(uint32_t w) { return __builtin_bit_cast(h2v, w); }
+
+// (x & m) | e.  m and e arrive as kernel arguments, so the compiler cannot
+// fold them into literals and forms one v_and_or_b32 (a VOP3 instruction,
+// which takes no literal on gfx950) instead of an AND and an OR; plain C++
+// keeps the compiler's hazard tracking between these writes and the matrix
+// instructions that read them.
+__device__ inline uint32_t and_or(uint32_t x, uint32_t m, uint32_t e) { return (x & m) | e; }
+
+struct Expander {
+  uint32_t m4, m16, e;  // 0x03000300, 0x00C000C0, 0x3C003C00
+  __device__ f16x8 k(uint32_t w0, uint32_t w1, int kb) const {
+    const uint32_t w = (kb < 2) ? w0 : w1;
+    const uint32_t x0 = (kb & 1) ? (w << 4) : w;
+    const uint32_t x1 = (kb & 1) ? rotr8(w) : (w >> 4);
+    return as_f16x8(and_or(x0, m4, e), and_or(x0, m16, e), and_or(x1, m4, e), and_or(x1, m16, e));
+  }
+  __device__ f16x4 v(uint32_t w0, uint32_t w1, int r) const {
+    const uint32_t w = (r < 4) ? w0 : w1;
+    const int s = r & 3;
+    const uint32_t x = s == 0 ? w : s == 1 ? (w >> 4) : s == 2 ? (w << 4) : rotr8(w);
+    return as_f16x4(and_or(x, m4, e), and_or(x, m16, e));
+  }
+};
+
 // One wave over its history pages j = j0 + wave + AW*i, i < npw.
+//
+// Lane (n = l%16, quad qd = l/16) holds column n = (h, part, cg) of the score
+// and PV accumulators and tokens 4qd..4qd+3 of each page.  Probabilities are
+// kept pre-multiplied by 2^k01 (tokens 4qd, 4qd+1) or 2^k23 (tokens 4qd+2,
+// 4qd+3), the 1/w weights of the V code expansion times the PV operand
+// scale, folded into the exponent; l and the z sums keep the two classes
+// apart and undo the factors once at the end.
 template <int GQA, int NG>
 __device__ void history_wave(const StepArgs &a, int b, int hk, int L, int j0, int j1, int wave, int lane,
                              const uint32_t *frag_lds, float *o_lds, float *m_lds, float *l_lds) {
@@ -338,30 +395,42 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int L, int j0, in
   const int nh = n_hist_tokens(L);
   const int npw = j1 > j0 + wave ? (j1 - j0 - wave + AW - 1) / AW : 0;
 
+  f16x8 bq[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    bq[k] = as_f16x8(frag_lds[(4 * k) * 64 + lane], frag_lds[(4 * k + 1) * 64 + lane],
+                     frag_lds[(4 * k + 2) * 64 + lane], frag_lds[(4 * k + 3) * 64 + lane]);
   float cinit[NA], zq[NA];
   int goff[NA];
-  bool gval[NA];
 #pragma unroll
   for (int ai = 0; ai < NA; ++ai) {
     cinit[ai] = __uint_as_float(frag_lds[(16 + ai) * 64 + lane]);
     zq[ai] = __uint_as_float(frag_lds[(16 + NA + ai) * 64 + lane]);
     const int g = ai * C::CG + cg;
-    gval[ai] = ncol && g < NG;
     goff[ai] = 64 * (g < NG ? g : NG - 1) + 16 * qd;
   }
   const float inv_kq = __uint_as_float(frag_lds[(16 + 2 * NA) * 64 + lane]);
+  const float k01 = a.pk01, k23 = a.pk23;  // log2 of the two PV factors
+  Expander ex;
+  ex.m4 = a.ex_m4;
+  ex.m16 = a.ex_m16;
+  ex.e = a.ex_e;
+  // keep the exponent pattern in a VGPR (the mask stays in an SGPR): then one
+  // v_and_or_b32 per expanded register.  The empty asm emits no instruction.
+  asm volatile("" : "+v"(ex.e));
+  // lanes holding the low fp16 part of the operands
+  const bool lo_lane = part == 1;
 
-  // page ids of this wave, one per lane
   int my_pid = -1;
   if (lane < npw) my_pid = c.hist_pt[int64_t(b) * c.hist_pt_stride + j0 + wave + AW * lane];
 
-  float m_run = -INFINITY, l_run = 0.f;
-  float corr[NA], zacc[NA];
+  float m_run = -INFINITY, l01 = 0.f, l23 = 0.f;
+  float corr[NA], z01[NA], z23[NA];
   f32x4 acc[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ai = 0; ai < NA; ++ai) corr[ai] = zacc[ai] = 0.f;
+  for (int ai = 0; ai < NA; ++ai) corr[ai] = z01[ai] = z23[ai] = 0.f;
 
   auto issue = [&](int i, PageLoads<NA> &ld) -> bool {
     const int pid = __builtin_amdgcn_readlane(my_pid, i);
@@ -377,6 +446,92 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int L, int j0, in
     return true;
   };
 
+  // one page; PARTIAL: rows >= nvalid are absent (their bits may be anything)
+  auto page = [&](const PageLoads<NA> &ld, int nvalid, auto partial_tag) {
+    constexpr bool PARTIAL = decltype(partial_tag)::value;
+    // ---- scores (kq units): D[t][n] = sum_c code_tc q'_cn
+    f32x4 dacc[NA];
+#pragma unroll
+    for (int ai = 0; ai < NA; ++ai) dacc[ai] = f32x4{cinit[ai], cinit[ai], cinit[ai], cinit[ai]};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int ai = C::grp_of_kblock(k) / C::CG;
+      dacc[ai] = mfma_k(ex.k(ld.kc[0], ld.kc[1], k), bq[k], dacc[ai]);
+    }
+    float sc[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = 0.f;
+#pragma unroll
+      for (int ai = 0; ai < NA; ++ai) {
+        const h2v sz = as_h2(ld.km[ai][i]);
+        v = fmaf(float(sz.x), dacc[ai][i], fmaf(float(sz.y), zq[ai], v));
+      }
+      if constexpr (GQA < 16) v += row_ror<GQA>(v);
+      if constexpr (2 * GQA < 16) v += row_ror<2 * GQA>(v);
+      if constexpr (4 * GQA < 16) v += row_ror<4 * GQA>(v);
+      if constexpr (8 * GQA < 16) v += row_ror<8 * GQA>(v);
+      if constexpr (PARTIAL) v = (4 * qd + i < nvalid) ? v : -INFINITY;
+      sc[i] = v;
+      mx = fmaxf(mx, v);
+    }
+    // ---- online softmax, max raised lazily (true log2 units)
+    mx *= inv_kq;
+    if (__any(mx > m_run + LAZY_TH)) {
+      const float mm = quad_max(fmaxf(mx, m_run));
+      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - mm);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) acc[r] *= alpha;
+#pragma unroll
+      for (int ai = 0; ai < NA; ++ai) {
+        corr[ai] *= alpha;
+        z01[ai] *= alpha;
+        z23[ai] *= alpha;
+      }
+      l01 *= alpha;
+      l23 *= alpha;
+      m_run = mm;
+    }
+    const float c01 = k01 - m_run, c23 = k23 - m_run;
+    float pe[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pe[i] = fast_exp2(fmaf(sc[i], inv_kq, i < 2 ? c01 : c23));
+    l01 += pe[0] + pe[1];
+    l23 += pe[2] + pe[3];
+    // ---- PV operand: pe * s as fp16 high / low parts
+    f16x4 bp[NA];
+#pragma unroll
+    for (int ai = 0; ai < NA; ++ai) {
+      _Float16 e[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const h2v sz = as_h2(ld.vm[ai][i]);
+        float sv = float(sz.x), zv = float(sz.y);
+        if constexpr (PARTIAL) {
+          const bool ok = 4 * qd + i < nvalid;
+          sv = ok ? sv : 0.f;
+          zv = ok ? zv : 0.f;
+        }
+        const float x = pe[i] * sv;
+        if (i < 2)
+          z01[ai] = fmaf(pe[i], zv, z01[ai]);
+        else
+          z23[ai] = fmaf(pe[i], zv, z23[ai]);
+        const _Float16 hi = _Float16(x);
+        const _Float16 lo = _Float16(x - float(hi));
+        e[i] = lo_lane ? lo : hi;
+        corr[ai] += float(e[i]);
+      }
+      bp[ai] = f16x4{e[0], e[1], e[2], e[3]};
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int ai = C::grp_of_rblock(r) / C::CG;
+      acc[r] = mfma_v(ex.v(ld.vc[0], ld.vc[1], r), bp[ai], acc[r]);
+    }
+  };
+
   PageLoads<NA> cur, nxt;
   bool cur_ok = npw > 0 ? issue(0, cur) : false;
   for (int i = 0; i < npw; ++i) {
@@ -385,90 +540,24 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int L, int j0, in
     if (!cur_ok) {
       if (lane == 0) flag_status(c.status, OSCAR_STATUS_BAD_PAGE);
     } else {
-      const int j = j0 + wave + AW * i;
-      const int nvalid = min(PAGE, nh - PAGE * j);
-      // ---- scores: D[t][n] = sum_c code_tc q'_cn, per accumulator
-      f32x4 dacc[NA];
-#pragma unroll
-      for (int ai = 0; ai < NA; ++ai) dacc[ai] = f32x4{cinit[ai], cinit[ai], cinit[ai], cinit[ai]};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int ai = C::grp_of_kblock(k) / C::CG;
-        const f16x8 bq = as_f16x8(frag_lds[(4 * k) * 64 + lane], frag_lds[(4 * k + 1) * 64 + lane],
-                                  frag_lds[(4 * k + 2) * 64 + lane], frag_lds[(4 * k + 3) * 64 + lane]);
-        dacc[ai] = mfma_k(expand_k(cur.kc[0], cur.kc[1], k), bq, dacc[ai]);
-      }
-      float sc[4];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        float v = 0.f;
-#pragma unroll
-        for (int ai = 0; ai < NA; ++ai) {
-          const uint32_t sz = cur.km[ai][ii];
-          v = fmaf(lo_f16(sz) * inv_kq, dacc[ai][ii], fmaf(hi_f16(sz), zq[ai], v));
-        }
-        if constexpr (GQA < 16) v += row_ror<GQA>(v);
-        if constexpr (2 * GQA < 16) v += row_ror<2 * GQA>(v);
-        if constexpr (4 * GQA < 16) v += row_ror<4 * GQA>(v);
-        if constexpr (8 * GQA < 16) v += row_ror<8 * GQA>(v);
-        sc[ii] = (4 * qd + ii < nvalid) ? v : -INFINITY;
-        mx = fmaxf(mx, sc[ii]);
-      }
-      // ---- online softmax, max raised lazily
-      if (__any(mx > m_run + LAZY_TH)) {
-        const float mm = quad_max(fmaxf(mx, m_run));
-        const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - mm);
-#pragma unroll
-        for (int r = 0; r < 8; ++r) acc[r] *= alpha;
-#pragma unroll
-        for (int ai = 0; ai < NA; ++ai) {
-          corr[ai] *= alpha;
-          zacc[ai] *= alpha;
-        }
-        l_run *= alpha;
-        m_run = mm;
-      }
-      float p[4];
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        p[ii] = (sc[ii] == -INFINITY) ? 0.f : fast_exp2(sc[ii] - m_run);
-        l_run += p[ii];
-      }
-      // ---- PV operand: p * s * (1/w) * 2^k as fp16 high / low parts
-      f16x4 bp[NA];
-#pragma unroll
-      for (int ai = 0; ai < NA; ++ai) {
-        _Float16 e[4];
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const uint32_t sz = cur.vm[ai][ii];
-          const bool ok = gval[ai] && (4 * qd + ii < nvalid);
-          const float mult = (ii < 2) ? 4.f : 16.f;
-          const float x = ok ? p[ii] * lo_f16(sz) * (mult * a.pv_scale) : 0.f;
-          const _Float16 hi = _Float16(x);
-          e[ii] = part ? _Float16(x - float(hi)) : hi;
-          corr[ai] += float(e[ii]);
-          zacc[ai] = ok ? fmaf(p[ii], hi_f16(sz), zacc[ai]) : zacc[ai];
-        }
-        bp[ai] = f16x4{e[0], e[1], e[2], e[3]};
-      }
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int ai = C::grp_of_rblock(r) / C::CG;
-        acc[r] = mfma_v(expand_v(cur.vc[0], cur.vc[1], r), bp[ai], acc[r]);
-      }
+      const int nvalid = min(PAGE, nh - PAGE * (j0 + wave + AW * i));
+      if (nvalid == PAGE)
+        page(cur, nvalid, std::false_type{});
+      else
+        page(cur, nvalid, std::true_type{});
     }
     cur = nxt;
     cur_ok = nxt_ok;
   }
 
   // ---- this wave's o[h][c], m[h], l[h] into LDS
-  const float lt = quad_sum(l_run);
+  const float inv01 = fast_exp2(-k01), inv23 = fast_exp2(-k23);
+  const float lt = quad_sum(fmaf(l01, inv01, l23 * inv23));
+  float zacc[NA];
 #pragma unroll
   for (int ai = 0; ai < NA; ++ai) {
     corr[ai] = quad_sum(corr[ai]);
-    zacc[ai] = quad_sum(zacc[ai]);
+    zacc[ai] = quad_sum(fmaf(z01[ai], inv01, z23[ai] * inv23));
   }
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
@@ -506,19 +595,27 @@ __device__ inline uint32_t raw_valid_rows(int L, int page) {
   return m;
 }
 
-// The last workgroup of (b, hk): merge `used` splits per query head, rotate
-// the history part back with R_V^T, add the raw part, normalise.
+// Merge of one (request, KV head): LSE-combines the `used` partials of each
+// query head of the group, rotates the history part back with R_V^T, adds
+// the raw part (split 0) and normalises.  1024 threads: wave h computes head
+// h's weights; then (head, channel, half of the splits) per thread.
+constexpr int MERGE_THREADS = 1024;
+
 template <int GQA>
-__device__ void merge_group(const StepArgs &a, int b, int hk, int used, float *lds, int tid) {
+__global__ void __launch_bounds__(MERGE_THREADS) merge_kernel(StepArgs a) {
+  const int hk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
+  const oscar_layer_cache &c = a.c;
+  const int L = a.k_new ? a.len_before[b] + 1 : a.seq_lens[b];
+  if (!valid_len(L, a.max_seq_len)) return;  // output zeroed by the prologue
+  const int used = 1 + (n_hist_pages(L) + a.pages_per_split - 1) / a.pages_per_split;
   const int64_t head_stride = int64_t(1 + a.n_splits) * PART_STRIDE;
   const float *parts0 = a.parts + (int64_t(b) * a.n_q_heads + hk * GQA) * head_stride;
-  float *w_lds = lds;                    // [GQA][used]
-  float *rot = w_lds + GQA * used;       // [GQA][128] history part (unnormalised)
-  float *plain = rot + GQA * D;          // [GQA][128]
-  float *lsum = plain + GQA * D;         // [GQA]
-  float *acc4 = lsum + 8;                // [4][GQA][128]
-  // weights per head: wave w handles head w
+  __shared__ float w_lds[GQA][MAX_SPLITS + 1];
+  __shared__ float lsum[GQA];
+  __shared__ float rot[2][GQA][D];    // history part, two halves of the splits
+  __shared__ float plain[GQA][D];
+  __shared__ float back[8][GQA][D];   // R_V^T partial sums, 8 row groups
   if (wave < GQA) {
     const float *ph = parts0 + wave * head_stride;
     float m = -INFINITY;
@@ -528,46 +625,59 @@ __device__ void merge_group(const StepArgs &a, int b, int hk, int used, float *l
     for (int s = lane; s < used; s += 64) {
       const float ms = ph[s * PART_STRIDE + D];
       const float w = (ms == -INFINITY) ? 0.f : fast_exp2(ms - m);
-      w_lds[wave * used + s] = w;
+      w_lds[wave][s] = w;
       l = fmaf(w, ph[s * PART_STRIDE + D + 1], l);
     }
     for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
     if (lane == 0) lsum[wave] = l;
   }
   __syncthreads();
-  for (int idx = tid; idx < GQA * D; idx += AW * 64) {
-    const int h = idx / D, ch = idx % D;
-    const float *ph = parts0 + h * head_stride;
-    float o = 0.f;
-    for (int s = 1; s < used; ++s) o = fmaf(w_lds[h * used + s], ph[s * PART_STRIDE + ch], o);
-    rot[idx] = o;
-    plain[idx] = w_lds[h * used] * ph[ch];
+  for (int idx = tid; idx < 2 * GQA * D; idx += MERGE_THREADS) {
+    const int hf = idx / (GQA * D), h = (idx / D) % GQA, ch = idx % D;
+    const float *ph = parts0 + h * head_stride + ch;
+    const int s0 = 1 + hf * ((used - 1 + 1) / 2), s1 = hf ? used : 1 + (used - 1 + 1) / 2;
+    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    int s = s0;
+    for (; s + 3 < s1; s += 4) {
+      o0 = fmaf(w_lds[h][s], ph[s * PART_STRIDE], o0);
+      o1 = fmaf(w_lds[h][s + 1], ph[(s + 1) * PART_STRIDE], o1);
+      o2 = fmaf(w_lds[h][s + 2], ph[(s + 2) * PART_STRIDE], o2);
+      o3 = fmaf(w_lds[h][s + 3], ph[(s + 3) * PART_STRIDE], o3);
+    }
+    for (; s < s1; ++s) o0 = fmaf(w_lds[h][s], ph[s * PART_STRIDE], o0);
+    rot[hf][h][ch] = (o0 + o1) + (o2 + o3);
+    if (hf == 0) plain[h][ch] = w_lds[h][0] * ph[0];
   }
   __syncthreads();
-  // (rot R_V^T)[h][c] = sum_i rot[h][i] R_V[c][i]; thread: c = tid % 128, i-quarter tid / 128
+  // (rot R_V^T)[h][c] = sum_i rot[h][i] R_V[c][i]; thread: c = tid % 128,
+  // rows i in [16 g, 16 g + 16) with g = tid / 128
   {
-    const int ch = tid & (D - 1), qt = tid >> 7;
-    const float *R = reinterpret_cast<const float *>(a.fv + FORM_R) + ch * D + 32 * qt;
+    const int ch = tid & (D - 1), g = tid >> 7;
+    const float *R = reinterpret_cast<const float *>(a.fv + FORM_R) + ch * D + 16 * g;
+    f32x4 r[4];
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) r[i4] = *reinterpret_cast<const f32x4 *>(R + 4 * i4);
     float acc[GQA];
 #pragma unroll
     for (int h = 0; h < GQA; ++h) acc[h] = 0.f;
 #pragma unroll
-    for (int i4 = 0; i4 < 8; ++i4) {
-      const f32x4 r = *reinterpret_cast<const f32x4 *>(R + 4 * i4);
+    for (int i4 = 0; i4 < 4; ++i4)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * g + 4 * i4 + e;
 #pragma unroll
-        for (int h = 0; h < GQA; ++h) acc[h] = fmaf(rot[h * D + 32 * qt + 4 * i4 + e], r[e], acc[h]);
-    }
+        for (int h = 0; h < GQA; ++h) acc[h] = fmaf(rot[0][h][i] + rot[1][h][i], r[i4][e], acc[h]);
+      }
 #pragma unroll
-    for (int h = 0; h < GQA; ++h) acc4[(qt * GQA + h) * D + ch] = acc[h];
+    for (int h = 0; h < GQA; ++h) back[g][h][ch] = acc[h];
   }
   __syncthreads();
-  for (int idx = tid; idx < GQA * D; idx += AW * 64) {
+  for (int idx = tid; idx < GQA * D; idx += MERGE_THREADS) {
     const int h = idx / D, ch = idx % D;
-    const float back = acc4[(0 * GQA + h) * D + ch] + acc4[(1 * GQA + h) * D + ch] +
-                       acc4[(2 * GQA + h) * D + ch] + acc4[(3 * GQA + h) * D + ch];
-    a.out[(int64_t(b) * a.n_q_heads + hk * GQA + h) * D + ch] = (back + plain[idx]) / lsum[h];
+    float v = plain[h][ch];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) v += back[g][h][ch];
+    a.out[(int64_t(b) * a.n_q_heads + hk * GQA + h) * D + ch] = v / lsum[h];
   }
 }
 
@@ -577,11 +687,8 @@ __global__ void __launch_bounds__(AW * 64) attend_kernel(StepArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const oscar_layer_cache &c = a.c;
   const int L = a.k_new ? a.len_before[b] + 1 : a.seq_lens[b];
-  constexpr int LDS_COMBINE = AW * GQA * D + 2 * AW * GQA;
-  constexpr int LDS_MERGE = 6 * GQA * D + 8 + GQA * (MAX_SPLITS + 1);
-  __shared__ float lds[LDS_COMBINE > LDS_MERGE ? LDS_COMBINE : LDS_MERGE];
+  __shared__ float lds[AW * GQA * D + 2 * AW * GQA];
   __shared__ uint32_t frag_lds[FRAG_DW * 64];
-  __shared__ int last_s;
   if (!valid_len(L, a.max_seq_len)) return;  // flagged (and out zeroed) by the prologue
   const int pages = n_hist_pages(L);
   const int used = 1 + (pages + a.pages_per_split - 1) / a.pages_per_split;
@@ -620,9 +727,6 @@ __global__ void __launch_bounds__(AW * 64) attend_kernel(StepArgs a) {
   const int64_t head_stride = int64_t(1 + a.n_splits) * PART_STRIDE;
   float *part0 = a.parts + (int64_t(b) * a.n_q_heads + hk * GQA) * head_stride + split * PART_STRIDE;
   combine_waves<GQA, AW>(o_lds, m_lds, l_lds, part0, head_stride, tid);
-  // ---- the last workgroup of (b, hk) merges
-  if (!elect_last(a.count + b * c.n_kv_heads + hk, uint32_t(used), &last_s, tid)) return;
-  merge_group<GQA>(a, b, hk, used, lds, tid);
 }
 
 // ------------------------------------------------------------------ launch
@@ -633,6 +737,9 @@ static hipError_t launch_t(const StepArgs &a, int batch, int hkv, bool attend, h
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !attend) return e;
   hipLaunchKernelGGL((attend_kernel<GQA, NG>), dim3(1 + a.n_splits, hkv, batch), dim3(AW * 64), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((merge_kernel<GQA>), dim3(hkv, batch), dim3(MERGE_THREADS), 0, s, a);
   return hipGetLastError();
 }
 
@@ -674,12 +781,16 @@ hipError_t launch_decode_step(const oscar_layer_cache &c, RotArg rk, RotArg rv, 
   a.sm_scale = sm_scale;
   a.out = out;
   a.frag = nullptr;
-  a.count = nullptr;
   a.parts = nullptr;
   a.pages_per_split = AW;
   a.n_splits = 0;
   a.pv_scale = pv_scale_for(rv.clip);
   a.pv_unscale = 1.f / a.pv_scale;
+  a.ex_m4 = 0x03000300u;
+  a.ex_m16 = 0x00C000C0u;
+  a.ex_e = 0x3C003C00u;
+  a.pk01 = std::log2(4.f * a.pv_scale);
+  a.pk23 = std::log2(16.f * a.pv_scale);
   const bool attend = q != nullptr;
   if (attend) {
     const SplitPlan p = plan_int2_splits(batch, c.n_kv_heads, max_seq_len);
@@ -687,8 +798,7 @@ hipError_t launch_decode_step(const oscar_layer_cache &c, RotArg rk, RotArg rv, 
     a.n_splits = p.n_splits;
     uint8_t *w = static_cast<uint8_t *>(ws);
     a.frag = reinterpret_cast<uint32_t *>(w);
-    a.count = reinterpret_cast<uint32_t *>(w + frag_bytes(batch, c.n_kv_heads));
-    a.parts = reinterpret_cast<float *>(w + frag_bytes(batch, c.n_kv_heads) + count_bytes(batch, c.n_kv_heads));
+    a.parts = reinterpret_cast<float *>(w + frag_bytes(batch, c.n_kv_heads));
   }
   const int gqa = attend ? n_q_heads / c.n_kv_heads : 1;
   switch (gqa) {

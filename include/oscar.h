@@ -223,7 +223,7 @@ OSCAR_API int oscar_decode_attn(const oscar_layer_cache *cache,
  * exactly as in oscar_write_kv.  Then q (device bf16 [batch][Hq][128])
  * attends over all len_before[b] + 1 tokens as in oscar_decode_attn, which
  * must be <= max_seq_len.  Same result as oscar_write_kv with one token per
- * request followed by oscar_decode_attn, in two kernel launches.  The
+ * request followed by oscar_decode_attn, in three kernel launches.  The
  * workspace is the one of oscar_decode_attn (oscar_decode_workspace_bytes);
  * it may hold anything on entry.  Calls that share a workspace must not run
  * concurrently. */
@@ -248,9 +248,8 @@ OSCAR_API size_t oscar_bf16_decode_workspace_bytes(int32_t batch, int32_t n_q_he
  * the BF16 pool); pt: device int32 [batch][pt_stride] — token p of request
  * b is row p%16 of page pt[b][p/16]; other arguments as oscar_decode_attn.
  * status: device uint32 or NULL (OSCAR_STATUS_* bits).
- * The workspace (oscar_bf16_decode_workspace_bytes) holds merge counters:
- * it must be zero-filled before its first use, and every call leaves them
- * at zero again.  Calls that share a workspace must not run concurrently. */
+ * The workspace (oscar_bf16_decode_workspace_bytes) may hold anything on
+ * entry; calls that share a workspace must not run concurrently. */
 OSCAR_API int oscar_bf16_paged_decode(const uint16_t *q, const uint16_t *kv_pages,
                             int64_t n_pages, const int32_t *pt,
                             int32_t pt_stride, const int32_t *seq_lens,
