@@ -14,12 +14,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int WAVES = 4;            // waves per workgroup
 constexpr float LOG2E = 1.4426950408889634f;
 // The running max of a softmax is raised only when a score exceeds it by more
-// than this (log2 units), so probabilities stay <= 2^LAZY_TH; most pages then
-// skip the rescale of the accumulators.
-constexpr float LAZY_TH = 3.0f;
+// than this (log2 units), so probabilities stay <= 2^LAZY_TH; nearly every
+// page then skips the rescale of the accumulators.
+constexpr float LAZY_TH = 8.0f;
 constexpr int PART_STRIDE = D + 2;  // partial: o[128], m, l
 
 // lane l receives the value of lane l - N (mod 16) of its row of 16
@@ -39,6 +38,11 @@ __device__ inline float quad_max(float v) {
   v = fmaxf(v, __shfl_xor(v, 32));
   return v;
 }
+
+// Wave index within the workgroup as a scalar: the compiler cannot tell that
+// threadIdx.x / 64 is the same in every lane, and a per-lane value would turn
+// loop counters and page bookkeeping into vector registers and exec masks.
+__device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -194,7 +198,7 @@ struct Bf16Wave {
 // and writes one unnormalised partial (o[128], m, l) per query head.
 template <int GQA, int NW>
 __device__ inline void combine_waves(const float *o_lds, const float *m_lds, const float *l_lds,
-                                     float *part0, int64_t head_stride, int tid) {
+                                     float *part0, int64_t head_stride, int tid, int o_wave_stride = GQA * D) {
   for (int idx = tid; idx < GQA * D; idx += NW * 64) {
     const int h = idx / D, c = idx % D;
     float mst = -INFINITY;
@@ -203,7 +207,7 @@ __device__ inline void combine_waves(const float *o_lds, const float *m_lds, con
     for (int w = 0; w < NW; ++w) {
       const float mw = m_lds[w * GQA + h];
       const float e = (mw == -INFINITY) ? 0.f : fast_exp2(mw - mst);
-      o = fmaf(e, o_lds[(w * GQA + h) * D + c], o);
+      o = fmaf(e, o_lds[w * o_wave_stride + h * D + c], o);
       l = fmaf(e, l_lds[w * GQA + h], l);
     }
     float *part = part0 + h * head_stride;

@@ -25,13 +25,13 @@ constexpr size_t FORM_RT_HI = FORM_RT + D * D * 4;  // fp16 hi(R[i][j]) at [j][i
 constexpr size_t FORM_RT_LO = FORM_RT_HI + D * D * 2;  // fp16 2^11 * (R - hi)
 constexpr size_t FORM_BYTES = FORM_RT_LO + D * D * 2;
 
-__host__ __device__ inline int n_groups(int G) { return D / G; }
-__host__ __device__ inline int meta_bytes(int G) { return 64 * (D / G); }
-__host__ __device__ inline int hist_block_bytes(int G) { return 1024 + 128 * (D / G); }
-__host__ __device__ inline int k_codes_off(int) { return 0; }
-__host__ __device__ inline int k_meta_off(int) { return CODE_BYTES; }
-__host__ __device__ inline int v_codes_off(int G) { return CODE_BYTES + meta_bytes(G); }
-__host__ __device__ inline int v_meta_off(int G) { return 2 * CODE_BYTES + meta_bytes(G); }
+__host__ __device__ constexpr int n_groups(int G) { return D / G; }
+__host__ __device__ constexpr int meta_bytes(int G) { return 64 * (D / G); }
+__host__ __device__ constexpr int hist_block_bytes(int G) { return 1024 + 128 * (D / G); }
+__host__ __device__ constexpr int k_codes_off(int) { return 0; }
+__host__ __device__ constexpr int k_meta_off(int) { return CODE_BYTES; }
+__host__ __device__ constexpr int v_codes_off(int G) { return CODE_BYTES + meta_bytes(G); }
+__host__ __device__ constexpr int v_meta_off(int G) { return 2 * CODE_BYTES + meta_bytes(G); }
 
 // Slot bit tables of a code dword (first code at LO[u], second at HI[u]).
 __host__ __device__ inline int slot_lo(int u) {

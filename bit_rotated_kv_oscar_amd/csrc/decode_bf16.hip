@@ -1,8 +1,9 @@
 // Plain BF16 paged decode attention: the all-BF16 baseline that OSCAR's
 // batch-1 decode speed-up is measured against (arXiv:2605.17757 v2 abstract).
 // One kernel: a workgroup of 8 waves per (request, KV head, split); wave w
-// takes every 8th page of the split (page ids preloaded, the next page's
-// loads issued before the current page computes).  Scores on the bf16 matrix
+// takes every 8th page of the split (page ids preloaded 64 at a time, the
+// next page's loads issued into a second register set before the current
+// page computes).  Scores on the bf16 matrix
 // cores, PV on the vector ALUs, fp32 accumulation.  Each workgroup writes an
 // unnormalised partial per query head; a merge kernel (one block per
 // (request, KV head)) LSE-combines them and normalises.
@@ -52,7 +53,7 @@ struct Bf16Args {
 template <int GQA>
 __global__ void __launch_bounds__(1024) bf16_merge_kernel(Bf16Args a) {
   const int hk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = wave_id(), lane = tid & 63;
   const int L = a.seq_lens[b];
   if (L < 1 || L > a.max_seq_len) return;  // output zeroed by the split kernel
   const int pages = (L + PAGE - 1) / PAGE;
@@ -103,7 +104,7 @@ __global__ void __launch_bounds__(1024) bf16_merge_kernel(Bf16Args a) {
 template <int GQA>
 __global__ void __launch_bounds__(BW * 64) bf16_decode_kernel(Bf16Args a) {
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int L = a.seq_lens[b];
   __shared__ float lds[BW * GQA * D + 2 * BW * GQA];
   if (L < 1 || L > a.max_seq_len) {
@@ -122,28 +123,40 @@ __global__ void __launch_bounds__(BW * 64) bf16_decode_kernel(Bf16Args a) {
   const int j0 = split * a.pages_per_split + wave;
   const int j1 = min(pages, split * a.pages_per_split + a.pages_per_split);
   const int npw = j1 > j0 ? (j1 - j0 + BW - 1) / BW : 0;
+  // page ids of pages 64k + lane, loaded per chunk of 64
+  const int32_t *pt = a.pt + int64_t(b) * a.pt_stride + j0;
   int my_pid = -1;
-  if (lane < npw) my_pid = a.pt[int64_t(b) * a.pt_stride + j0 + BW * lane];
-  typename Bf16Wave<GQA>::Loads cur, nxt;
-  auto issue = [&](int i, typename Bf16Wave<GQA>::Loads &ld) -> bool {
-    const int pid = __builtin_amdgcn_readlane(my_pid, i);
+  using Loads = typename Bf16Wave<GQA>::Loads;
+  auto issue = [&](int i, Loads &ld) -> bool {
+    if ((i & 63) == 0) {
+      my_pid = (i + lane < npw) ? pt[int64_t(BW) * (i + lane)] : -1;
+      // take the wait for this load here, once per 64 pages (see the INT2
+      // page loop): later readlanes then wait for nothing
+      asm volatile("" : "+v"(my_pid));
+    }
+    const int pid = __builtin_amdgcn_readlane(my_pid, i & 63);
     if (pid < 0 || pid >= a.n_pages) return false;
     const uint16_t *base = a.kv + (int64_t(pid) * a.n_kv_heads + hk) * 2 * PAGE * D;
     Bf16Wave<GQA>::issue(base, base + PAGE * D, ld, lane);
     return true;
   };
-  bool cur_ok = npw > 0 ? issue(0, cur) : false;
-  for (int i = 0; i < npw; ++i) {
-    bool nxt_ok = false;
-    if (i + 1 < npw) nxt_ok = issue(i + 1, nxt);
-    if (!cur_ok) {
+  auto run = [&](const Loads &ld, bool ok, int i) {
+    if (!ok) {
       if (lane == 0) flag_status(a.status, OSCAR_STATUS_BAD_PAGE);
-    } else {
-      const int rows = min(PAGE, L - PAGE * (j0 + BW * i));
-      st.compute(cur, rows >= PAGE ? 0xFFFFu : ((1u << rows) - 1u), lane);
+      return;
     }
-    cur = nxt;
-    cur_ok = nxt_ok;
+    const int rows = min(PAGE, L - PAGE * (j0 + BW * i));
+    st.compute(ld, rows >= PAGE ? 0xFFFFu : ((1u << rows) - 1u), lane);
+  };
+  // two load buffers used in turn (no copy of in-flight registers)
+  Loads ba, bb;
+  bool ok_a = npw > 0 ? issue(0, ba) : false, ok_b = false;
+  for (int i = 0; i < npw; i += 2) {
+    if (i + 1 < npw) ok_b = issue(i + 1, bb);
+    run(ba, ok_a, i);
+    if (i + 1 >= npw) break;
+    if (i + 2 < npw) ok_a = issue(i + 2, ba);
+    run(bb, ok_b, i + 1);
   }
   st.finish(o_lds + wave * GQA * D, m_lds + wave * GQA, l_lds + wave * GQA, lane);
   __syncthreads();

@@ -26,8 +26,9 @@
 //       the per-group sums of q_rot.
 //   attend (one workgroup of 8 waves per (request, KV head, split)):
 //     split 0 attends over the raw BF16 sink + recent pages, split s >= 1
-//     over history pages (wave w takes every 8th page of the split, page ids
-//     preloaded, next page's loads issued before the current page computes).
+//     over history pages (wave w takes every 8th page of the split; page ids
+//     preloaded 64 at a time; pages copied straight into a per-wave LDS ring
+//     DEPTH pages ahead of the one being computed).
 //     Each workgroup writes an unnormalised partial (o[128], m, l) per query
 //     head.
 //   merge (one block per (request, KV head)): LSE-combines the partials,
@@ -44,22 +45,43 @@
 namespace oscar {
 
 constexpr int AW = 8;                // waves per attend workgroup
-constexpr int FRAG_DW = 32;          // dwords per lane of the q fragment block
+constexpr int FRAG_DW = 96;          // dwords per lane of the q fragment block (at most)
 constexpr int PRO_THREADS = 512;     // prologue block: K half + V half
 constexpr int MAX_SPLITS = 255;      // history splits per (request, KV head)
 
-// Column layout of the score and PV accumulators for a GQA group of GQA heads
-// and NG scale groups: column n = h + GQA * (part + 2 * cg); part 0/1 = fp16
-// high/low part of the fp32 operand, cg = which of the CG groups sharing an
-// accumulator.  NA accumulators cover the NG groups.
+// Row layout of the score product for a GQA group of GQA query heads and NG
+// scale groups.  The A operand (16 rows) holds q' = q R_K: row r of chain ch
+// is J hl + 2 g + part (J = 2 NG rows per head): head HC ch + hl, scale group
+// g, part 0/1 = fp16 high part / low part x 2^11 (zero outside group g).
+// Lane (t = l%16, qd = l/16) of the result holds rows 4qd..4qd+3 for token t:
+// the two parts of row pairs 2qd and 2qd+1, pair P being (head P / NG,
+// group P % NG), so it forms its head's score for token t by itself (for
+// NG = 4 a head spans lanes l and l^16).
 template <int GQA, int NG>
-struct Cols {
-  static constexpr int CG0 = 16 / (2 * GQA);
-  static constexpr int CG = CG0 < NG ? CG0 : NG;
-  static constexpr int NA = (NG + CG - 1) / CG;
+struct Rows {
   static constexpr int G = D / NG;
-  __device__ static constexpr int grp_of_kblock(int k) { return (32 * k) / G; }  // 32-channel block
-  __device__ static constexpr int grp_of_rblock(int r) { return (16 * r) / G; }  // 16-channel block
+  static constexpr int J = 2 * NG;
+  static constexpr int HC = 16 / J;                // heads per chain
+  static constexpr int NCH = (GQA + HC - 1) / HC;  // chains
+  static constexpr int SPL = NG == 1 ? 2 : 1;      // scores per lane and chain
+  // per-lane dwords of the fragment block
+  static constexpr int FR_A = 0;                   // 16 per chain: A operand
+  static constexpr int FR_INIT = 16 * NCH;         // 4 per chain: accumulator start (rows 4qd + i)
+  static constexpr int FR_Q = FR_INIT + 4 * NCH;   // 2 per chain: kq * group sum of q' of pairs 2qd, 2qd+1
+  static constexpr int FR_INVKQ = FR_Q + 2 * NCH;  // 1: 1 / kq
+  static constexpr int FR_DW = FR_INVKQ + 1;
+  // head of score slot s of lane group qd (chain-local)
+  __device__ static constexpr int slot_head(int qd, int s) { return NG == 1 ? 2 * qd + s : (2 * qd) / NG; }
+  // chain-local head and group of pair k of lane group qd
+  __device__ static constexpr int pair_head(int qd, int k) { return (2 * qd + k) / NG; }
+  __device__ static constexpr int pair_group(int qd, int k) { return (2 * qd + k) % NG; }
+  // score slot holding pair k
+  __device__ static constexpr int pair_slot(int k) { return NG == 1 ? k : 0; }
+  // where head h's scores live: chain, lane group (for NG = 4 the first of
+  // the two), slot
+  __device__ static constexpr int head_chain(int h) { return h / HC; }
+  __device__ static constexpr int head_qd(int h) { return NG == 1 ? (h % HC) / 2 : NG == 2 ? h % HC : 2 * (h % HC); }
+  __device__ static constexpr int head_slot(int h) { return NG == 1 ? (h % HC) % 2 : 0; }
 };
 
 SplitPlan plan_int2_splits(int batch, int n_kv_heads, int max_seq_len) {
@@ -81,7 +103,7 @@ SplitPlan plan_int2_splits(int batch, int n_kv_heads, int max_seq_len) {
     const int64_t per_unit = (slots - units) / units;
     pps = (pages + per_unit - 1) / per_unit;
   } else {
-    pps = 8 * AW;
+    pps = 32 * AW;
   }
   if (pps < AW) pps = AW;
   const int64_t min_pps = (pages + MAX_SPLITS - 1) / MAX_SPLITS;  // bounds the merge's LDS
@@ -185,8 +207,8 @@ __device__ inline void store_int2_row(const float *y, float clip, int G, bool is
 
 template <int GQA, int NG>
 __global__ void __launch_bounds__(PRO_THREADS) prologue_kernel(StepArgs a) {
-  using C = Cols<GQA, NG>;
-  constexpr int G = C::G;
+  using R = Rows<GQA, NG>;
+  constexpr int G = R::G;
   const int hk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int half = tid >> 8, t = tid & 255;  // half 0: K (and the query), 1: V
   const oscar_layer_cache &c = a.c;
@@ -293,7 +315,7 @@ __global__ void __launch_bounds__(PRO_THREADS) prologue_kernel(StepArgs a) {
     store_int2_row(yout[half][GQA], half ? a.clip_v : a.clip_k, G, half == 1, evict_blk, hrow, codes[half],
                    sz_lds[half], t);
   }
-  // ---------------- q fragments (K half builds them; both halves share the barrier)
+  // ---------------- q fragments (K half builds them; both halves share the barriers)
   const float sc = a.sm_scale * LOG2E;
   float amax = 0.f;
   if (want_q && half == 0)
@@ -301,50 +323,169 @@ __global__ void __launch_bounds__(PRO_THREADS) prologue_kernel(StepArgs a) {
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
   if ((t & 63) == 0 && half == 0) red[t >> 6] = amax;
   __syncthreads();
-  if (!want_q || half == 1) return;  // no block barrier below this point
+  if (!want_q) return;  // uniform over the block
   const float gmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  float kq = 1.f;
+  float kq = 1.f;  // keeps |q' * 16 * kq| <= 2^14 (fp16 operands)
   while (gmax * 16.f * kq > 16384.f) kq *= 0.5f;
-  if (t >= 64) return;
-  const int lane = t, n = lane & 15, qd = lane >> 4;
-  const int h = n % GQA, part = (n / GQA) & 1, cg = n / (2 * GQA);
-  const bool ncol = cg < C::CG;
-  uint32_t *fr = a.frag + (int64_t(b) * hkv + hk) * FRAG_DW * 64;
-  auto bval = [&](int ch) -> _Float16 {
-    const int g = ch / G;
-    if (!ncol || (g % C::CG) != cg) return _Float16(0.f);
-    const float mult = ((ch & 3) < 2) ? 4.f : 16.f;
-    const float x = yout[0][h][ch] * sc * mult * kq;
-    const _Float16 hi = _Float16(x);
-    return part ? _Float16(x - float(hi)) : hi;
-  };
-  for (int k = 0; k < 4; ++k)
-    for (int v = 0; v < 4; ++v) {
-      const int c0 = 32 * k + 8 * qd + 2 * v;
-      const uint16_t lo16 = __builtin_bit_cast(uint16_t, bval(c0));
-      const uint16_t hi16 = __builtin_bit_cast(uint16_t, bval(c0 + 1));
-      fr[(4 * k + v) * 64 + lane] = uint32_t(lo16) | (uint32_t(hi16) << 16);
+  // A operand values q' * w_c * kq as fp16 high part and low part x 2^11;
+  // w_c = 4 or 16, the weight that the K code expansion puts on channel c
+  __shared__ _Float16 qa[2][GQA][D];
+  __shared__ float rsum[2][GQA][NG];  // row sums of the two parts per group
+  __shared__ float gsum[GQA][NG];     // kq * sum of q' over each group
+  if (half == 0)
+    for (int e = t; e < GQA * D; e += 256) {
+      const int h = e / D, ch = e % D;
+      const float x = yout[0][h][ch] * sc * (((ch & 3) < 2) ? 4.f : 16.f) * kq;
+      const _Float16 hi = _Float16(x);
+      qa[0][h][ch] = hi;
+      qa[1][h][ch] = _Float16((x - float(hi)) * 2048.f);
     }
-  for (int ai = 0; ai < C::NA; ++ai) {
-    float cs = 0.f;  // column sum of B over the channel blocks of accumulator ai
-    for (int ch = 0; ch < D; ++ch)
-      if ((ch / G) / C::CG == ai) cs += float(bval(ch));
-    fr[(16 + ai) * 64 + lane] = __float_as_uint(-cs);
-    const int g = ai * C::CG + cg;
-    float zq = 0.f;  // per-group sum of q_rot, in the kq units of the B operand
-    if (ncol && part == 0 && g < NG)
-      for (int i = 0; i < G; ++i) zq += yout[0][h][g * G + i] * sc;
-    fr[(16 + C::NA + ai) * 64 + lane] = __float_as_uint(zq * kq);
+  __syncthreads();
+  if (half == 0 && t < 3 * GQA * NG) {
+    const int which = t / (GQA * NG), h = (t % (GQA * NG)) / NG, g = t % NG;
+    float sum = 0.f;
+    if (which < 2) {
+      for (int i = 0; i < G; ++i) sum += float(qa[which][h][g * G + i]);
+      rsum[which][h][g] = sum;
+    } else {
+      for (int i = 0; i < G; ++i) sum += yout[0][h][g * G + i] * sc;
+      gsum[h][g] = sum * kq;
+    }
   }
-  fr[(16 + 2 * C::NA) * 64 + lane] = __float_as_uint(1.f / kq);
+  __syncthreads();
+  if (half == 1 || t >= 64) return;
+  const int lane = t, r = lane & 15, qd = lane >> 4;
+  uint32_t *fr = a.frag + (int64_t(b) * hkv + hk) * FRAG_DW * 64;
+  for (int ch = 0; ch < R::NCH; ++ch) {
+    {
+      const int h = R::HC * ch + r / R::J, g = (r % R::J) / 2, part = r & 1;
+      auto bits = [&](int cc) -> uint32_t {
+        return (h < GQA && cc / G == g) ? uint32_t(__builtin_bit_cast(uint16_t, qa[part][h][cc])) : 0u;
+      };
+      for (int kb = 0; kb < 4; ++kb)
+        for (int v = 0; v < 4; ++v) {
+          const int c0 = 32 * kb + 8 * qd + 2 * v;
+          fr[(R::FR_A + 16 * ch + 4 * kb + v) * 64 + lane] = bits(c0) | (bits(c0 + 1) << 16);
+        }
+    }
+    // the expanded codes are 1 + c / w_c: start each row at minus its sum
+    for (int i = 0; i < 4; ++i) {
+      const int rr = 4 * qd + i;
+      const int h = R::HC * ch + rr / R::J, g = (rr % R::J) / 2, part = rr & 1;
+      fr[(R::FR_INIT + 4 * ch + i) * 64 + lane] = __float_as_uint(h < GQA ? -rsum[part][h][g] : 0.f);
+    }
+    for (int k = 0; k < 2; ++k) {
+      const int h = R::HC * ch + R::pair_head(qd, k), g = R::pair_group(qd, k);
+      fr[(R::FR_Q + 2 * ch + k) * 64 + lane] = __float_as_uint(h < GQA ? gsum[h][g] : 0.f);
+    }
+  }
+  fr[R::FR_INVKQ * 64 + lane] = __float_as_uint(1.f / kq);
 }
 
 // ------------------------------------------------------------------ attend
 
-template <int NA>
-struct PageLoads {
+// History pages reach LDS by direct global->LDS copies (global_load_lds):
+// DEPTH pages per wave in flight without holding registers.  One page block
+// is 1024 + 128 NG bytes: one 16-byte-per-lane copy of the first 1 KB, one
+// of the rest on the first 8 NG lanes.  The compiler does not order LDS
+// reads after these copies, so the page loop waits for them itself (vmcnt
+// counts per instruction; loads complete in issue order).
+constexpr int DEPTH = 4;
+
+__device__ inline void lds_copy16(const void *src, void *lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+}
+
+template <int N>
+__device__ inline void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// wait until at most `pages` page copies (2 instructions each) are pending
+template <int P = DEPTH - 1>
+__device__ inline void wait_pages(int pages) {
+  static_assert(2 * P <= 63, "vmcnt range");
+  if constexpr (P == 0) {
+    wait_vmem<0>();
+  } else {
+    if (pages >= P)
+      wait_vmem<2 * P>();
+    else
+      wait_pages<P - 1>(pages);
+  }
+}
+
+// Orders this wave's LDS accesses around an exchange between its lanes: the
+// LDS unit runs one wave's instructions in order, so keeping the compiler
+// from moving loads and stores across this point is enough.
+__device__ inline void lds_order() { asm volatile("" ::: "memory"); }
+
+// LDS byte address of a pointer into __shared__ memory
+__device__ inline uint32_t lds_addr(const void *p) {
+  return uint32_t(uintptr_t((const __attribute__((address_space(3))) void *)p));
+}
+
+// One page's operands out of its ring slot.  Plain ds_read instructions in
+// one asm block that also waits for them: loads the compiler sees would each
+// get a wait for every LDS copy in flight, the prefetched pages included.
+// kc/vc: K/V code dwords of the lane; km/vm: K/V meta of (token, pair 0/1);
+// sv: V meta of tokens 4 qd .. 4 qd + 3 for each group (NG <= 4).
+template <int VCODE, int KMETA, int VMETA, int POFF>
+struct RingRead {
   u32x2 kc, vc;
-  u32x4 km[NA], vm[NA];
+  uint32_t km0, km1, vm0, vm1;
+  u32x4 sv0, sv1, sv2, sv3;
+  template <int NG>
+  __device__ void load(uint32_t a_code, uint32_t a_meta, uint32_t a_tok) {
+    if constexpr (NG == 1) {
+      asm volatile(
+          "ds_read_b64 %0, %6\n\t"
+          "ds_read_b64 %1, %6 offset:%9\n\t"
+          "ds_read_b32 %2, %7 offset:%10\n\t"
+          "ds_read_b32 %3, %7 offset:%11\n\t"
+          "ds_read_b128 %4, %8 offset:%11\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(kc), "=&v"(vc), "=&v"(km0), "=&v"(vm0), "=&v"(sv0), "=&v"(sv1)
+          : "v"(a_code), "v"(a_meta), "v"(a_tok), "n"(VCODE), "n"(KMETA), "n"(VMETA)
+          : "memory");
+      km1 = km0;
+      vm1 = vm0;
+    } else if constexpr (NG == 2) {
+      asm volatile(
+          "ds_read_b64 %0, %8\n\t"
+          "ds_read_b64 %1, %8 offset:%11\n\t"
+          "ds_read_b32 %2, %9 offset:%12\n\t"
+          "ds_read_b32 %3, %9 offset:%13\n\t"
+          "ds_read_b32 %4, %9 offset:%14\n\t"
+          "ds_read_b32 %5, %9 offset:%15\n\t"
+          "ds_read_b128 %6, %10 offset:%14\n\t"
+          "ds_read_b128 %7, %10 offset:%16\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(kc), "=&v"(vc), "=&v"(km0), "=&v"(km1), "=&v"(vm0), "=&v"(vm1), "=&v"(sv0), "=&v"(sv1)
+          : "v"(a_code), "v"(a_meta), "v"(a_tok), "n"(VCODE), "n"(KMETA), "n"(KMETA + POFF), "n"(VMETA),
+            "n"(VMETA + POFF), "n"(VMETA + 64)
+          : "memory");
+    } else {
+      asm volatile(
+          "ds_read_b64 %0, %10\n\t"
+          "ds_read_b64 %1, %10 offset:%13\n\t"
+          "ds_read_b32 %2, %11 offset:%14\n\t"
+          "ds_read_b32 %3, %11 offset:%15\n\t"
+          "ds_read_b32 %4, %11 offset:%16\n\t"
+          "ds_read_b32 %5, %11 offset:%17\n\t"
+          "ds_read_b128 %6, %12 offset:%16\n\t"
+          "ds_read_b128 %7, %12 offset:%18\n\t"
+          "ds_read_b128 %8, %12 offset:%19\n\t"
+          "ds_read_b128 %9, %12 offset:%20\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(kc), "=&v"(vc), "=&v"(km0), "=&v"(km1), "=&v"(vm0), "=&v"(vm1), "=&v"(sv0), "=&v"(sv1),
+            "=&v"(sv2), "=&v"(sv3)
+          : "v"(a_code), "v"(a_meta), "v"(a_tok), "n"(VCODE), "n"(KMETA), "n"(KMETA + POFF), "n"(VMETA),
+            "n"(VMETA + POFF), "n"(VMETA + 64), "n"(VMETA + 128), "n"(VMETA + 192)
+          : "memory");
+    }
+  }
+  __device__ u32x4 sv(int g) const { return g == 0 ? sv0 : g == 1 ? sv1 : g == 2 ? sv2 : sv3; }
 };
 
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
@@ -373,44 +514,80 @@ struct Expander {
   }
 };
 
+// x[ch][sl] of lane src (a byte address, 4 * lane) where (ch, sl) is this
+// lane's (chain, slot) pair; ds_bpermute moves registers between lanes
+// without touching memory.
+template <int NCH, int SPL>
+__device__ inline float gather(const float (&x)[NCH][SPL], int src, int my_ch, int my_sl) {
+  float v = 0.f;
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+    for (int sl = 0; sl < SPL; ++sl) {
+      const float y = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(x[ch][sl])));
+      if constexpr (NCH * SPL == 1)
+        v = y;
+      else
+        v = (ch == my_ch && sl == my_sl) ? y : v;
+    }
+  return v;
+}
+
 // One wave over its history pages j = j0 + wave + AW*i, i < npw.
 //
-// Lane (n = l%16, quad qd = l/16) holds column n = (h, part, cg) of the score
-// and PV accumulators and tokens 4qd..4qd+3 of each page.  Probabilities are
-// kept pre-multiplied by 2^k01 (tokens 4qd, 4qd+1) or 2^k23 (tokens 4qd+2,
-// 4qd+3), the 1/w weights of the V code expansion times the PV operand
-// scale, folded into the exponent; l and the z sums keep the two classes
-// apart and undo the factors once at the end.
+// Scores: D[r][t] = init_r + sum_c A[r][c] (1 + code_tc / w_c) over the four
+// 32-channel blocks (A: the q fragment, rows as in Rows; B: the exactly
+// expanded K codes, token t = column).  Lane (t, qd) turns its four rows into
+// score(h, t) = sum_g s_tg (D_hi + 2^-11 D_lo) + z_tg kq sum_{c in g} q'_c,
+// in kq units, and keeps m, l and the z sums of its head(s) for token t.
+// Probabilities leave the lane as pw = p w_t 2^kpv (w_t = 4 for tokens
+// 4q, 4q+1 and 16 for 4q+2, 4q+3, the weights of the V code expansion;
+// 2^kpv keeps the fp16 operand in range), folded into the exponent.
+// PV: lane (n, tq) takes pw of head n for tokens 4tq..4tq+3 from LDS and
+// forms B_g = fp16(pw s_tg) for each scale group g; acc[r] += Vexp_r B_g(r)
+// with Vexp = 1 + code/w_t, and cacc[g] += 1 B_g, whose rows all equal the
+// column sums of B_g: acc - cacc is then exactly sum_t B code / w_t.
 template <int GQA, int NG>
 __device__ void history_wave(const StepArgs &a, int b, int hk, int L, int j0, int j1, int wave, int lane,
-                             const uint32_t *frag_lds, float *o_lds, float *m_lds, float *l_lds) {
-  using C = Cols<GQA, NG>;
-  constexpr int NA = C::NA;
+                             const uint32_t *frag_lds, uint8_t *ring, float *zs, float *o_lds, float *m_lds,
+                             float *l_lds) {
+  using R = Rows<GQA, NG>;
+  constexpr int NCH = R::NCH, SPL = R::SPL, G = R::G, HC = R::HC;
+  constexpr int SB = hist_block_bytes(G);
+  constexpr int kmeta = k_meta_off(G), vcode = v_codes_off(G), vmeta = v_meta_off(G);
   const oscar_layer_cache &c = a.c;
-  const int n = lane & 15, qd = lane >> 4;
-  const int h = n % GQA, part = (n / GQA) & 1, cg = n / (2 * GQA);
-  const bool ncol = cg < C::CG;
-  const int blk_bytes = hist_block_bytes(C::G);
-  const int kmeta = k_meta_off(C::G), vcode = v_codes_off(C::G), vmeta = v_meta_off(C::G);
+  const int t = lane & 15, qd = lane >> 4;  // score side: token, lane group
+  const int hp = t % GQA;                   // PV side: head of column n = l%16 (tq = qd)
+  // PV side: lanes and registers holding head hp's scores for tokens 4qd + i
+  const int src_ch = R::head_chain(hp), src_sl = R::head_slot(hp);
+  const int src0 = 4 * (16 * R::head_qd(hp) + 4 * qd);
   const int nh = n_hist_tokens(L);
   const int npw = j1 > j0 + wave ? (j1 - j0 - wave + AW - 1) / AW : 0;
 
-  f16x8 bq[4];
+  f16x8 aq[NCH][4];
+  f32x4 dinit[NCH];
+  float qz[NCH][2];
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
-    bq[k] = as_f16x8(frag_lds[(4 * k) * 64 + lane], frag_lds[(4 * k + 1) * 64 + lane],
-                     frag_lds[(4 * k + 2) * 64 + lane], frag_lds[(4 * k + 3) * 64 + lane]);
-  float cinit[NA], zq[NA];
-  int goff[NA];
+  for (int ch = 0; ch < NCH; ++ch) {
 #pragma unroll
-  for (int ai = 0; ai < NA; ++ai) {
-    cinit[ai] = __uint_as_float(frag_lds[(16 + ai) * 64 + lane]);
-    zq[ai] = __uint_as_float(frag_lds[(16 + NA + ai) * 64 + lane]);
-    const int g = ai * C::CG + cg;
-    goff[ai] = 64 * (g < NG ? g : NG - 1) + 16 * qd;
+    for (int kb = 0; kb < 4; ++kb) {
+      const uint32_t *f = frag_lds + (R::FR_A + 16 * ch + 4 * kb) * 64 + lane;
+      aq[ch][kb] = as_f16x8(f[0], f[64], f[128], f[192]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dinit[ch][i] = __uint_as_float(frag_lds[(R::FR_INIT + 4 * ch + i) * 64 + lane]);
+    qz[ch][0] = __uint_as_float(frag_lds[(R::FR_Q + 2 * ch) * 64 + lane]);
+    qz[ch][1] = __uint_as_float(frag_lds[(R::FR_Q + 2 * ch + 1) * 64 + lane]);
   }
-  const float inv_kq = __uint_as_float(frag_lds[(16 + 2 * NA) * 64 + lane]);
-  const float k01 = a.pk01, k23 = a.pk23;  // log2 of the two PV factors
+  const float inv_kq = __uint_as_float(frag_lds[R::FR_INVKQ * 64 + lane]);
+  const float kq = 1.f / inv_kq;
+  const bool w16 = (t & 3) >= 2;
+  const float lw_t = w16 ? a.pk23 : a.pk01;  // log2(w_t 2^kpv)
+  const float inv_w = w16 ? 0.0625f : 0.25f;
+  // K/V meta dword of (token t, group of pair 0); pair 1 sits 16 dwords on
+  // (next group), or on the same dword when NG = 1
+  const int moff = 4 * (16 * R::pair_group(qd, 0) + t);
+  constexpr int POFF = NG == 1 ? 0 : 64;
   Expander ex;
   ex.m4 = a.ex_m4;
   ex.m16 = a.ex_m16;
@@ -418,162 +595,237 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int L, int j0, in
   // keep the exponent pattern in a VGPR (the mask stays in an SGPR): then one
   // v_and_or_b32 per expanded register.  The empty asm emits no instruction.
   asm volatile("" : "+v"(ex.e));
-  // lanes holding the low fp16 part of the operands
-  const bool lo_lane = part == 1;
+  const f16x4 ones = as_f16x4(0x3C003C00u, 0x3C003C00u);
 
-  int my_pid = -1;
-  if (lane < npw) my_pid = c.hist_pt[int64_t(b) * c.hist_pt_stride + j0 + wave + AW * lane];
-
-  float m_run = -INFINITY, l01 = 0.f, l23 = 0.f;
-  float corr[NA], z01[NA], z23[NA];
-  f32x4 acc[8];
+  bool started = false;  // wave-uniform: a max has been set
+  float m_run[NCH][SPL], thr[NCH][SPL], cl[NCH][SPL], lw[NCH][SPL], zw[NCH][2];
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+#pragma unroll
+    for (int sl = 0; sl < SPL; ++sl) {
+      m_run[ch][sl] = -INFINITY;
+      thr[ch][sl] = -INFINITY;
+      cl[ch][sl] = 0.f;
+      lw[ch][sl] = 0.f;
+    }
+    zw[ch][0] = zw[ch][1] = 0.f;
+  }
+  f32x4 acc[8], cacc[NG];
 #pragma unroll
   for (int r = 0; r < 8; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ai = 0; ai < NA; ++ai) corr[ai] = z01[ai] = z23[ai] = 0.f;
+  for (int g = 0; g < NG; ++g) cacc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto issue = [&](int i, PageLoads<NA> &ld) -> bool {
-    const int pid = __builtin_amdgcn_readlane(my_pid, i);
-    if (pid < 0 || pid >= c.n_hist_pages) return false;
-    const uint8_t *blk = c.hist + (int64_t(pid) * c.n_kv_heads + hk) * blk_bytes;
-    ld.kc = *reinterpret_cast<const u32x2 *>(blk + 8 * lane);
-    ld.vc = *reinterpret_cast<const u32x2 *>(blk + vcode + 8 * lane);
-#pragma unroll
-    for (int ai = 0; ai < NA; ++ai) {
-      ld.km[ai] = *reinterpret_cast<const u32x4 *>(blk + kmeta + goff[ai]);
-      ld.vm[ai] = *reinterpret_cast<const u32x4 *>(blk + vmeta + goff[ai]);
+  // page ids of pages 64k + lane, loaded per chunk of 64
+  const int32_t *pt = c.hist_pt + int64_t(b) * c.hist_pt_stride + j0 + wave;
+  int my_pid = -1;
+
+  // copy page i into ring slot sl; a bad page id copies page 0 instead (the
+  // page is skipped), so every page costs the same two copy instructions
+  uint32_t ok_slots = 0;
+  const uint32_t lane16 = 16u * uint32_t(lane);
+  auto issue = [&](int i, int sl) {
+    if ((i & 63) == 0) {
+      my_pid = (i + lane < npw) ? pt[int64_t(AW) * (i + lane)] : -1;
+      // take the wait for this load here, once per 64 pages: otherwise the
+      // compiler cannot tell on later pages that it has landed and waits for
+      // every copy in flight before each readlane
+      asm volatile("" : "+v"(my_pid));
     }
-    return true;
+    int pid = __builtin_amdgcn_readlane(my_pid, i & 63);
+    const bool ok = pid >= 0 && pid < c.n_hist_pages;
+    pid = ok ? pid : 0;
+    const uint8_t *blk = c.hist + (int64_t(pid) * c.n_kv_heads + hk) * SB;
+    uint8_t *dst = ring + sl * SB;
+    lds_copy16(blk + lane16, dst);
+    if (lane < (SB - 1024) / 16) lds_copy16(blk + 1024u + lane16, dst + 1024);
+    ok_slots = ok ? (ok_slots | (1u << sl)) : (ok_slots & ~(1u << sl));
   };
 
-  // one page; PARTIAL: rows >= nvalid are absent (their bits may be anything)
-  auto page = [&](const PageLoads<NA> &ld, int nvalid, auto partial_tag) {
+  // one page from the ring; PARTIAL: rows >= nvalid are absent (any bits)
+  auto page = [&](const uint8_t *src, int nvalid, auto partial_tag) {
     constexpr bool PARTIAL = decltype(partial_tag)::value;
-    // ---- scores (kq units): D[t][n] = sum_c code_tc q'_cn
-    f32x4 dacc[NA];
+    const uint32_t base = lds_addr(src);
+    RingRead<vcode, kmeta, vmeta, POFF> rd;
+    rd.template load<NG>(base + 8 * lane, base + moff, base + 16 * qd);
+    const u32x2 kc = rd.kc, vc = rd.vc;
+    const h2v km0 = as_h2(rd.km0), km1 = as_h2(rd.km1);
+    const h2v vm0 = as_h2(rd.vm0), vm1 = as_h2(rd.vm1);
+    const bool tok_ok = !PARTIAL || t < nvalid;
+    // ---- scores (kq units)
+    f16x8 kx[4];
 #pragma unroll
-    for (int ai = 0; ai < NA; ++ai) dacc[ai] = f32x4{cinit[ai], cinit[ai], cinit[ai], cinit[ai]};
+    for (int kb = 0; kb < 4; ++kb) kx[kb] = ex.k(kc[0], kc[1], kb);
+    float S[NCH][SPL];
+    bool up = false;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int ai = C::grp_of_kblock(k) / C::CG;
-      dacc[ai] = mfma_k(ex.k(ld.kc[0], ld.kc[1], k), bq[k], dacc[ai]);
-    }
-    float sc[4];
-    float mx = -INFINITY;
+    for (int ch = 0; ch < NCH; ++ch) {
+      f32x4 d = dinit[ch];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = 0.f;
-#pragma unroll
-      for (int ai = 0; ai < NA; ++ai) {
-        const h2v sz = as_h2(ld.km[ai][i]);
-        v = fmaf(float(sz.x), dacc[ai][i], fmaf(float(sz.y), zq[ai], v));
+      for (int kb = 0; kb < 4; ++kb) d = mfma_k(aq[ch][kb], kx[kb], d);
+      const float v0 = fmaf(float(km0.x), fmaf(d[1], 0x1p-11f, d[0]), float(km0.y) * qz[ch][0]);
+      const float v1 = fmaf(float(km1.x), fmaf(d[3], 0x1p-11f, d[2]), float(km1.y) * qz[ch][1]);
+      if constexpr (NG == 1) {
+        S[ch][0] = v0;
+        S[ch][1] = v1;
+      } else {
+        float sv = v0 + v1;
+        if constexpr (NG == 4) sv += __shfl_xor(sv, 16);
+        S[ch][0] = sv;
       }
-      if constexpr (GQA < 16) v += row_ror<GQA>(v);
-      if constexpr (2 * GQA < 16) v += row_ror<2 * GQA>(v);
-      if constexpr (4 * GQA < 16) v += row_ror<4 * GQA>(v);
-      if constexpr (8 * GQA < 16) v += row_ror<8 * GQA>(v);
-      if constexpr (PARTIAL) v = (4 * qd + i < nvalid) ? v : -INFINITY;
-      sc[i] = v;
-      mx = fmaxf(mx, v);
-    }
-    // ---- online softmax, max raised lazily (true log2 units)
-    mx *= inv_kq;
-    if (__any(mx > m_run + LAZY_TH)) {
-      const float mm = quad_max(fmaxf(mx, m_run));
-      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - mm);
 #pragma unroll
-      for (int r = 0; r < 8; ++r) acc[r] *= alpha;
-#pragma unroll
-      for (int ai = 0; ai < NA; ++ai) {
-        corr[ai] *= alpha;
-        z01[ai] *= alpha;
-        z23[ai] *= alpha;
+      for (int sl = 0; sl < SPL; ++sl) {
+        if constexpr (PARTIAL) S[ch][sl] = tok_ok ? S[ch][sl] : -INFINITY;
+        up |= S[ch][sl] > thr[ch][sl];
       }
-      l01 *= alpha;
-      l23 *= alpha;
-      m_run = mm;
     }
-    const float c01 = k01 - m_run, c23 = k23 - m_run;
-    float pe[4];
+    // ---- online softmax: the running max moves only when a score passes it
+    // by more than LAZY_TH (log2 units); then every lane of the head's row
+    // takes the row max
+    if (__any(up)) {
+      // the first rescale only sets the max: nothing has been accumulated
+      const bool scale = started;
+      started = true;
+      float alpha[NCH][SPL];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pe[i] = fast_exp2(fmaf(sc[i], inv_kq, i < 2 ? c01 : c23));
-    l01 += pe[0] + pe[1];
-    l23 += pe[2] + pe[3];
-    // ---- PV operand: pe * s as fp16 high / low parts
-    f16x4 bp[NA];
+      for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
-    for (int ai = 0; ai < NA; ++ai) {
-      _Float16 e[4];
+        for (int sl = 0; sl < SPL; ++sl) {
+          float mx = fmaxf(S[ch][sl] * inv_kq, m_run[ch][sl]);
+          mx = fmaxf(mx, row_ror<8>(mx));
+          mx = fmaxf(mx, row_ror<4>(mx));
+          mx = fmaxf(mx, row_ror<2>(mx));
+          mx = fmaxf(mx, row_ror<1>(mx));
+          const float al = m_run[ch][sl] == -INFINITY ? 0.f : fast_exp2(m_run[ch][sl] - mx);
+          alpha[ch][sl] = al;
+          m_run[ch][sl] = mx;
+          thr[ch][sl] = (mx + LAZY_TH) * kq;
+          cl[ch][sl] = lw_t - mx;
+          if (scale) {
+            lw[ch][sl] *= al;
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+              if (R::pair_slot(k) == sl) zw[ch][k] *= al;
+          }
+        }
+      if (scale) {
+        const float al = gather(alpha, src0, src_ch, src_sl);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) acc[r] *= al;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) cacc[g] *= al;
+      }
+    }
+    float pw[NCH][SPL];
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+#pragma unroll
+      for (int sl = 0; sl < SPL; ++sl) {
+        pw[ch][sl] = fast_exp2(fmaf(S[ch][sl], inv_kq, cl[ch][sl]));
+        lw[ch][sl] += pw[ch][sl];
+      }
+      float z0 = float(vm0.y), z1 = float(vm1.y);
+      if constexpr (PARTIAL) {
+        z0 = tok_ok ? z0 : 0.f;
+        z1 = tok_ok ? z1 : 0.f;
+      }
+      zw[ch][0] = fmaf(pw[ch][R::pair_slot(0)], z0, zw[ch][0]);
+      zw[ch][1] = fmaf(pw[ch][R::pair_slot(1)], z1, zw[ch][1]);
+    }
+    // ---- PV operands: lane (n, tq) = head hp, tokens 4tq..4tq+3
+    float p4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p4[i] = gather(pw, src0 + 4 * i, src_ch, src_sl);
+    f16x4 bp[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const u32x4 sv = rd.sv(g);  // V meta of tokens 4 qd .. 4 qd + 3, group g
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const h2v sz = as_h2(ld.vm[ai][i]);
-        float sv = float(sz.x), zv = float(sz.y);
-        if constexpr (PARTIAL) {
-          const bool ok = 4 * qd + i < nvalid;
-          sv = ok ? sv : 0.f;
-          zv = ok ? zv : 0.f;
-        }
-        const float x = pe[i] * sv;
-        if (i < 2)
-          z01[ai] = fmaf(pe[i], zv, z01[ai]);
-        else
-          z23[ai] = fmaf(pe[i], zv, z23[ai]);
-        const _Float16 hi = _Float16(x);
-        const _Float16 lo = _Float16(x - float(hi));
-        e[i] = lo_lane ? lo : hi;
-        corr[ai] += float(e[i]);
+        float x = p4[i] * float(as_h2(sv[i]).x);
+        if constexpr (PARTIAL) x = (4 * qd + i < nvalid) ? x : 0.f;
+        bp[g][i] = _Float16(x);
       }
-      bp[ai] = f16x4{e[0], e[1], e[2], e[3]};
     }
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int ai = C::grp_of_rblock(r) / C::CG;
-      acc[r] = mfma_v(ex.v(ld.vc[0], ld.vc[1], r), bp[ai], acc[r]);
+    for (int g = 0; g < NG; ++g) cacc[g] = mfma_v(ones, bp[g], cacc[g]);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc[r] = mfma_v(ex.v(vc[0], vc[1], r), bp[(16 * r) / G], acc[r]);
+  };
+
+  auto step = [&](int i, auto partial_tag) {
+    if (i + DEPTH - 1 < npw) issue(i + DEPTH - 1, (i + DEPTH - 1) % DEPTH);
+    wait_pages(min(DEPTH - 1, npw - 1 - i));
+    const int sl = i % DEPTH;
+    // tested as a per-lane value (the same in every lane): as a scalar branch
+    // the compiler copies the accumulators at its merge point every page
+    uint32_t okv = ok_slots;
+    asm volatile("" : "+v"(okv));
+    if (!((okv >> sl) & 1u)) {
+      if (lane == 0) flag_status(c.status, OSCAR_STATUS_BAD_PAGE);
+    } else {
+      page(ring + sl * SB, nh - PAGE * (j0 + wave + AW * i), partial_tag);
     }
   };
 
-  PageLoads<NA> cur, nxt;
-  bool cur_ok = npw > 0 ? issue(0, cur) : false;
-  for (int i = 0; i < npw; ++i) {
-    bool nxt_ok = false;
-    if (i + 1 < npw) nxt_ok = issue(i + 1, nxt);
-    if (!cur_ok) {
-      if (lane == 0) flag_status(c.status, OSCAR_STATUS_BAD_PAGE);
-    } else {
-      const int nvalid = min(PAGE, nh - PAGE * (j0 + wave + AW * i));
-      if (nvalid == PAGE)
-        page(cur, nvalid, std::false_type{});
-      else
-        page(cur, nvalid, std::true_type{});
-    }
-    cur = nxt;
-    cur_ok = nxt_ok;
+  if (npw > 0 && c.n_hist_pages < 1) {
+    if (lane == 0) flag_status(c.status, OSCAR_STATUS_BAD_PAGE);
+  } else if (npw > 0) {
+    // only the last history page of the request can be partial; it is the
+    // last page of whichever wave holds it
+    const bool last_partial = (nh % PAGE) != 0 && j0 + wave + AW * (npw - 1) == (nh - 1) / PAGE;
+    const int nfull = npw - (last_partial ? 1 : 0);
+    for (int i = 0; i < DEPTH - 1 && i < npw; ++i) issue(i, i);
+    for (int i = 0; i < nfull; ++i) step(i, std::false_type{});
+    if (last_partial) step(npw - 1, std::true_type{});
   }
 
   // ---- this wave's o[h][c], m[h], l[h] into LDS
-  const float inv01 = fast_exp2(-k01), inv23 = fast_exp2(-k23);
-  const float lt = quad_sum(fmaf(l01, inv01, l23 * inv23));
-  float zacc[NA];
+  float zsum[NCH][2];
 #pragma unroll
-  for (int ai = 0; ai < NA; ++ai) {
-    corr[ai] = quad_sum(corr[ai]);
-    zacc[ai] = quad_sum(fmaf(z01[ai], inv01, z23[ai] * inv23));
-  }
+  for (int ch = 0; ch < NCH; ++ch) {
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int g = C::grp_of_rblock(r);
-    const int ai = g / C::CG;
+    for (int sl = 0; sl < SPL; ++sl) {
+      float l = lw[ch][sl] * inv_w;
+      l += row_ror<8>(l);
+      l += row_ror<4>(l);
+      l += row_ror<2>(l);
+      l += row_ror<1>(l);
+      const int h = HC * ch + R::slot_head(qd, sl);
+      if (t == 0 && h < GQA && ((NG != 4) || (qd & 1) == 0)) {
+        m_lds[h] = m_run[ch][sl];
+        l_lds[h] = l * a.pv_unscale;
+      }
+    }
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      float v = acc[r][ii] - corr[ai];
-      v += row_ror<16 - GQA>(v);  // add the low-part column n + GQA
-      if (part == 0 && ncol && cg == g % C::CG)
-        o_lds[h * D + 16 * r + 4 * qd + ii] = fmaf(v, a.pv_unscale, zacc[ai]);
+    for (int k = 0; k < 2; ++k) {
+      float z = zw[ch][k] * inv_w;
+      z += row_ror<8>(z);
+      z += row_ror<4>(z);
+      z += row_ror<2>(z);
+      z += row_ror<1>(z);
+      zsum[ch][k] = z;
     }
   }
-  if (qd == 0 && n < GQA) {
-    m_lds[n] = m_run;
-    l_lds[n] = lt;
+  lds_order();
+  // z sums per (head, group) through LDS
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int h = HC * ch + R::pair_head(qd, k), g = R::pair_group(qd, k);
+      if (t == 0 && h < GQA) zs[h * NG + g] = zsum[ch][k];
+    }
+  lds_order();
+  if (t < GQA) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int g = (16 * r) / G;
+      const float zg = zs[t * NG + g];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o_lds[t * D + 16 * r + 4 * qd + i] = (acc[r][i] - cacc[g][i] + zg) * a.pv_unscale;
+    }
   }
 }
 
@@ -604,7 +856,7 @@ constexpr int MERGE_THREADS = 1024;
 template <int GQA>
 __global__ void __launch_bounds__(MERGE_THREADS) merge_kernel(StepArgs a) {
   const int hk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = wave_id(), lane = tid & 63;
   const oscar_layer_cache &c = a.c;
   const int L = a.k_new ? a.len_before[b] + 1 : a.seq_lens[b];
   if (!valid_len(L, a.max_seq_len)) return;  // output zeroed by the prologue
@@ -684,19 +936,24 @@ __global__ void __launch_bounds__(MERGE_THREADS) merge_kernel(StepArgs a) {
 template <int GQA, int NG>
 __global__ void __launch_bounds__(AW * 64) attend_kernel(StepArgs a) {
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const oscar_layer_cache &c = a.c;
   const int L = a.k_new ? a.len_before[b] + 1 : a.seq_lens[b];
-  __shared__ float lds[AW * GQA * D + 2 * AW * GQA];
-  __shared__ uint32_t frag_lds[FRAG_DW * 64];
+  // per wave: its page ring, reused for its o[GQA][128] once the pages are done
+  constexpr int SB = hist_block_bytes(D / NG);
+  constexpr int WREG = DEPTH * SB > GQA * D * 4 ? DEPTH * SB : GQA * D * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t wave_lds[AW * WREG];
+  __shared__ float ml_lds[2 * AW * GQA];
+  __shared__ float zs_lds[AW * GQA * NG];  // per wave: z sums per (head, group)
+  __shared__ uint32_t frag_lds[Rows<GQA, NG>::FR_DW * 64];
   if (!valid_len(L, a.max_seq_len)) return;  // flagged (and out zeroed) by the prologue
   const int pages = n_hist_pages(L);
   const int used = 1 + (pages + a.pages_per_split - 1) / a.pages_per_split;
   if (split >= used) return;
-  float *o_lds = lds;
-  float *m_lds = lds + AW * GQA * D;
+  float *o_lds = reinterpret_cast<float *>(wave_lds);
+  float *m_lds = ml_lds;
   float *l_lds = m_lds + AW * GQA;
-  float *o_w = o_lds + wave * GQA * D;
+  float *o_w = o_lds + wave * (WREG / 4);
   if (split == 0) {
     Bf16Wave<GQA> st;
     st.init(a.q + (int64_t(b) * a.n_q_heads + hk * GQA) * D, a.sm_scale, lane);
@@ -716,17 +973,17 @@ __global__ void __launch_bounds__(AW * 64) attend_kernel(StepArgs a) {
     st.finish(o_w, m_lds + wave * GQA, l_lds + wave * GQA, lane);
   } else {
     const uint32_t *fr = a.frag + (int64_t(b) * c.n_kv_heads + hk) * FRAG_DW * 64;
-    for (int e = tid; e < FRAG_DW * 64; e += AW * 64) frag_lds[e] = fr[e];
+    for (int e = tid; e < Rows<GQA, NG>::FR_DW * 64; e += AW * 64) frag_lds[e] = fr[e];
     __syncthreads();
     const int j0 = (split - 1) * a.pages_per_split;
     const int j1 = min(pages, j0 + a.pages_per_split);
-    history_wave<GQA, NG>(a, b, hk, L, j0, j1, wave, lane, frag_lds, o_w, m_lds + wave * GQA,
-                          l_lds + wave * GQA);
+    history_wave<GQA, NG>(a, b, hk, L, j0, j1, wave, lane, frag_lds, wave_lds + wave * WREG,
+                          zs_lds + wave * GQA * NG, o_w, m_lds + wave * GQA, l_lds + wave * GQA);
   }
   __syncthreads();
   const int64_t head_stride = int64_t(1 + a.n_splits) * PART_STRIDE;
   float *part0 = a.parts + (int64_t(b) * a.n_q_heads + hk * GQA) * head_stride + split * PART_STRIDE;
-  combine_waves<GQA, AW>(o_lds, m_lds, l_lds, part0, head_stride, tid);
+  combine_waves<GQA, AW>(o_lds, m_lds, l_lds, part0, head_stride, tid, WREG / 4);
 }
 
 // ------------------------------------------------------------------ launch
@@ -755,7 +1012,7 @@ static hipError_t launch_g(const StepArgs &a, int G, int batch, int hkv, bool at
 static float pv_scale_for(float clip_v) {
   // PV operand: p <= 2^LAZY_TH, s <= 2 clip / 3, 1/w <= 16; keep it under 2^15
   float k = 1.f;
-  const float vmax = 8.f * 16.f * (2.f * clip_v / 3.f);
+  const float vmax = exp2f(LAZY_TH) * 16.f * (2.f * clip_v / 3.f);
   while (vmax * k > 32768.f) k *= 0.5f;
   while (vmax * k * 2.f <= 32768.f && k < 65536.f) k *= 2.f;
   return k;

@@ -343,3 +343,64 @@ def test_bf16_decode_reuses_workspace(oscar):
         out = oscar.bf16_paged_decode(*args, workspace=ws)
         torch.cuda.synchronize()
         assert_decode_close(out.cpu().numpy(), ref, "bf16 repeated")
+
+
+# ------------------------------------------------------------------ long splits
+
+
+def _shared_page_batch(sc: Scenario, ref: o.LayerCacheRef, batch: int):
+    """`batch` requests of sc.lens[0] tokens that all read the pages of
+    request 0 (page tables repeated), with their own queries."""
+    hist_pt = np.repeat(sc.hist_pt[:1], batch, axis=0)
+    bf16_pt = np.repeat(sc.bf16_pt[:1], batch, axis=0)
+    q = sc.ld.decode_q(batch)
+    return hist_pt, bf16_pt, q
+
+
+def test_decode_more_than_64_pages_per_wave(oscar):
+    # 32 requests x 8 KV heads = 256 (request, head) units: one history split
+    # per unit, so each of the 8 waves walks 554 / 8 > 64 pages
+    L, B = 9000, 32
+    sc = Scenario(1300, 32, 8, 64, [L])
+    ref = sc.oracle_cache()
+    hist_pt, bf16_pt, q = _shared_page_batch(sc, ref, B)
+    dev = torch.device("cuda:0")
+    cache = oscar.LayerCache(sc.hkv, sc.G, sc.n_hist_pages, sc.n_bf16_pages, torch.from_numpy(hist_pt),
+                             torch.from_numpy(bf16_pt), device=dev)
+    cache.hist.copy_(torch.from_numpy(ref.hist))
+    cache.bf16.view(torch.int16).copy_(torch.from_numpy(ref.bf16.view(np.int16)))
+    rk, rv = gpu_rotations(oscar, sc)
+    out = oscar.decode_attn(cache, rk, rv, to_dev_bf16(q), torch.full((B,), L, dtype=torch.int32, device=dev),
+                            L, SCALE)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) == 0
+    got = out.cpu().numpy()
+    pick = [0, 13, 31]
+    ref.hist_pt = hist_pt[:len(pick)]
+    ref.bf16_pt = bf16_pt[:len(pick)]
+    expect = o.decode_attn(ref, sc.R_K, sc.R_V, q[pick], [L] * len(pick), SCALE)
+    assert_decode_close(got[pick], expect, "int2 long split")
+
+
+def test_bf16_decode_more_than_64_pages_per_wave(oscar):
+    # 40 requests x 8 KV heads = 320 units: one split per unit, 563 / 8 > 64
+    # pages per wave; all requests read the same pages
+    L, B, hq, hkv = 9000, 40, 32, 8
+    ld = synth.LayerData(1400, 0, hq, hkv)
+    k, v = ld.cache_kv(L)
+    pt1, npages = synth.shuffled_page_tables(1400, 0, [L], n_pages_fn=lambda n: (n + 15) // 16)
+    pages = np.zeros((npages, hkv, 2, 16, 128), dtype=np.uint16)
+    p = np.arange(L)
+    pages[pt1[0, p // 16], :, 0, p % 16] = k
+    pages[pt1[0, p // 16], :, 1, p % 16] = v
+    pt = np.repeat(pt1, B, axis=0)
+    q = ld.decode_q(B)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = oscar.bf16_paged_decode(to_dev_bf16(q), to_dev_bf16(pages), torch.from_numpy(pt).cuda(),
+                                  torch.full((B,), L, dtype=torch.int32, device="cuda"), L, SCALE,
+                                  status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    pick = [0, 21, 39]
+    expect = o.bf16_paged_decode(q[pick], pages, pt[:len(pick)], [L] * len(pick), SCALE)
+    assert_decode_close(out.cpu().numpy()[pick], expect, "bf16 long split")
