@@ -79,6 +79,18 @@ def decode_bytes(lens, hq, hkv, G):
     return b
 
 
+def attend_bytes(lens, hkv, G):
+    """Algorithmic bytes of the split-K attention kernel of one decode call:
+    INT2 codes + fp16 meta of every history token, raw bf16 sink/recent
+    tokens and the page-table entries it follows."""
+    per_tok_int2 = 2 * (32 + 4 * (128 // G))
+    b = 0
+    for L in lens:
+        nh = n_hist_tokens(L)
+        b += nh * hkv * per_tok_int2 + min(L, 144) * hkv * 2 * 256 + ((nh + 15) // 16) * 4 + 9 * 4
+    return b
+
+
 def append_bytes(batch, hkv, G):
     """Algorithmic bytes of one append call: the evicted ring token is read
     and written to history, the new token is read and stored raw, R_K and
@@ -193,6 +205,10 @@ def main():
                                 device=dev)
             bf16_layers.append(bl)
         del k, v, qc, kc, vc
+        if (l + 1) % 6 == 0 or l + 1 == nl:
+            torch.cuda.synchronize()
+            print(f"setup: {l + 1}/{nl} layers calibrated and prefilled ({time.time() - t_setup:.0f} s)",
+                  file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     for ly in layers:
         assert int(ly.cache.status.item()) == 0, "prefill flagged bad data"
@@ -255,22 +271,25 @@ def main():
     tokens_per_s = B / (ms_per_step * 1e-3)
 
     # ------------------------------------------------ dominant-kernel timing
-    # HIP events on the stream the decode is launched on, around each decode
-    # call of every layer (eager launches, lengths fixed at the final value)
-    dec_ms = []
+    # The split-K attention kernel dominates the step.  The library records a
+    # pair of HIP events on the decode stream right around that one kernel
+    # (oscar_profile_events); eager decode calls of every layer, three rounds.
+    pairs = []
     with torch.cuda.stream(stream):
         for rep in range(3):
             for ly in layers:
                 a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a0.record(stream)
+                a0.record(stream)   # creates the events; the library records them again
+                a1.record(stream)
+                oscar.profile_events(a0, a1)
                 oscar.decode_attn(ly.cache, ly.rk, ly.rv, ly.q, lens_before, max_len, 1 / math.sqrt(HEAD_DIM),
                                   out=ly.out, workspace=ly.ws)
-                a1.record(stream)
-                dec_ms.append((a0, a1))
+                pairs.append((a0, a1))
     torch.cuda.synchronize()
-    dec_launch_ms = float(np.mean([a.elapsed_time(b) for a, b in dec_ms]))
-    dec_bytes_now = decode_bytes(lens_before.cpu().numpy().tolist(), hq, hkv, G)
-    achieved = dec_bytes_now / (dec_launch_ms * 1e-3) / 1e9
+    attend_us = float(np.mean([a.elapsed_time(b) for a, b in pairs])) * 1e3
+    lens_now0 = lens_before.cpu().numpy().tolist()
+    attend_b = attend_bytes(lens_now0, hkv, G)
+    achieved = attend_b / (attend_us * 1e-6) / 1e9
 
     # ---------------------------------------------------------------- BF16
     bf16 = None
@@ -327,8 +346,8 @@ def main():
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "oscar_decode_attn call (prologue: q rotation; attend: split-K decode + merge)",
-                     "avg_launch_us": round(dec_launch_ms * 1e3, 2), "bytes_per_launch": int(dec_bytes_now)},
+                     "kernel": f"oscar::attend_kernel<{hq // hkv}, {128 // G}> (split-K INT2 + BF16 decode)",
+                     "avg_launch_us": round(attend_us, 2), "bytes_per_launch": int(attend_b)},
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
     }

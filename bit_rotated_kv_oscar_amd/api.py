@@ -201,6 +201,15 @@ def bf16_paged_decode(q: torch.Tensor, kv_pages: torch.Tensor, pt: torch.Tensor,
     return out
 
 
+def profile_events(before: "torch.cuda.Event | None", after: "torch.cuda.Event | None") -> None:
+    """The next decode call on this thread records `before` / `after` around
+    its split-K attention kernel (oscar_profile_events).  Events must have
+    been recorded once (torch creates them lazily)."""
+    h0 = ctypes.c_void_p(before.cuda_event) if before is not None else ctypes.c_void_p(None)
+    h1 = ctypes.c_void_p(after.cuda_event) if after is not None else ctypes.c_void_p(None)
+    check(load().oscar_profile_events(h0, h1))
+
+
 def calibrate_rotation(q_cal: torch.Tensor, k_cal: torch.Tensor, v_cal: torch.Tensor,
                        clip_quantile: float = 0.999):
     """oscar_calibrate_rotation: bf16 [N, Hq, 128], [N, Hkv, 128] x2 on the device ->

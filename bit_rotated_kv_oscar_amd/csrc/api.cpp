@@ -13,6 +13,7 @@
 namespace {
 
 thread_local std::string g_err;
+thread_local oscar::KernelEvents g_events;
 
 int fail(int code, const char *fmt, ...) {
   char buf[512];
@@ -75,7 +76,19 @@ oscar::RotArg rot_arg(const oscar_rotation *r) {
 
 }  // namespace
 
+namespace oscar {
+KernelEvents &profile_events() { return g_events; }
+}  // namespace oscar
+
 extern "C" {
+
+int oscar_profile_events(void *before, void *after) {
+  if ((before == nullptr) != (after == nullptr))
+    return fail(OSCAR_EINVAL, "profile events: give both events or neither");
+  g_events.before = static_cast<hipEvent_t>(before);
+  g_events.after = static_cast<hipEvent_t>(after);
+  return OSCAR_OK;
+}
 
 const char *oscar_last_error(void) { return g_err.c_str(); }
 

@@ -167,7 +167,9 @@ __global__ void __launch_bounds__(BW * 64) bf16_decode_kernel(Bf16Args a) {
 
 template <int GQA>
 static hipError_t launch_t(const Bf16Args &a, int batch, hipStream_t s) {
-  hipLaunchKernelGGL((bf16_decode_kernel<GQA>), dim3(a.n_splits, a.n_kv_heads, batch), dim3(BW * 64), 0, s, a);
+  const KernelEvents ev = take_profile_events();
+  hipExtLaunchKernelGGL((bf16_decode_kernel<GQA>), dim3(a.n_splits, a.n_kv_heads, batch), dim3(BW * 64), 0, s,
+                        ev.before, ev.after, 0, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bf16_merge_kernel<GQA>), dim3(a.n_kv_heads, batch), dim3(1024), 0, s, a);

@@ -993,7 +993,9 @@ static hipError_t launch_t(const StepArgs &a, int batch, int hkv, bool attend, h
   hipLaunchKernelGGL((prologue_kernel<GQA, NG>), dim3(hkv, batch), dim3(PRO_THREADS), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !attend) return e;
-  hipLaunchKernelGGL((attend_kernel<GQA, NG>), dim3(1 + a.n_splits, hkv, batch), dim3(AW * 64), 0, s, a);
+  const KernelEvents ev = take_profile_events();
+  hipExtLaunchKernelGGL((attend_kernel<GQA, NG>), dim3(1 + a.n_splits, hkv, batch), dim3(AW * 64), 0, s,
+                        ev.before, ev.after, 0, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((merge_kernel<GQA>), dim3(hkv, batch), dim3(MERGE_THREADS), 0, s, a);

@@ -2,6 +2,8 @@
 // They assume validated arguments; api.cpp validates.
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include "common.h"
 
 namespace oscar {
@@ -10,6 +12,23 @@ struct RotArg {
   const uint8_t *forms;  // device forms of one rotation (FORM_* offsets)
   float clip;
 };
+
+// Events that the next decode launch records around its split-K attention
+// kernel (set by oscar_profile_events; per host thread, cleared once used).
+struct KernelEvents {
+  hipEvent_t before = nullptr, after = nullptr;
+};
+KernelEvents &profile_events();
+
+// Takes (and clears) the pending profile events.  Launchers pass them to
+// hipExtLaunchKernelGGL, which records them when the kernel itself starts
+// and ends.
+inline KernelEvents take_profile_events() {
+  KernelEvents &ev = profile_events();
+  const KernelEvents use = ev;
+  ev = KernelEvents{};
+  return use;
+}
 
 hipError_t launch_prepare_rotation(const double *R, void *forms, hipStream_t s);
 

@@ -110,8 +110,8 @@ enum {
  *     (second).
  * This order lets the decode expand a dword into eight fp16 pairs with one
  * AND-OR each (after at most one shift), in exactly the register order the
- * gfx950 matrix-core instructions read: K in 16x16x32 (tokens x channels)
- * tiles, V in 16x16x16 (channels x tokens) tiles.
+ * gfx950 matrix-core instructions read: K as 16x16x32 operands (16 tokens,
+ * 32 channels per block), V as 16x16x16 operands (16 channels x 16 tokens).
  * ------------------------------------------------------------------------- */
 
 typedef struct oscar_layer_cache {
@@ -258,6 +258,15 @@ OSCAR_API int oscar_bf16_paged_decode(const uint16_t *q, const uint16_t *kv_page
                             float sm_scale, float *out, uint32_t *status,
                             void *workspace, size_t workspace_bytes,
                             oscar_stream_t stream);
+
+/* Instrumentation for benchmarks: the next decode call on this host thread
+ * (oscar_decode_attn, oscar_decode_step or oscar_bf16_paged_decode) launches
+ * its split-K attention kernel with hipExtLaunchKernelGGL so that event
+ * `before` is recorded when that kernel starts and `after` when it ends,
+ * then forgets both.  before, after: hipEvent_t handles created by the
+ * caller, or both NULL to cancel.  Returns OSCAR_EINVAL if exactly one of
+ * them is NULL. */
+OSCAR_API int oscar_profile_events(void *before, void *after);
 
 #ifdef __cplusplus
 }

@@ -182,3 +182,10 @@ def test_errors_raise_in_binding():
     with pytest.raises(_lib.OscarError) as ei:
         _lib.check(_write(c=_cache(group=16)))
     assert ei.value.code == _lib.OSCAR_EUNSUPPORTED
+
+
+def test_profile_events_needs_both_or_neither():
+    lib = _lib.load()
+    assert lib.oscar_profile_events(ctypes.c_void_p(0x1000), None) == _lib.OSCAR_EINVAL and "both" in _err()
+    assert lib.oscar_profile_events(None, ctypes.c_void_p(0x1000)) == _lib.OSCAR_EINVAL
+    assert lib.oscar_profile_events(None, None) == _lib.OSCAR_OK
