@@ -135,6 +135,18 @@ struct Bf16Wave {
     for (int i = 0; i < 4; ++i) ld.vf[i] = *reinterpret_cast<const u32x4 *>(vp + (4 * qd + i) * D + 8 * n);
   }
 
+  // As above, with row `row` of the page taken from krow / vrow (128 bf16 each).
+  __device__ static void issue(const uint16_t *kp, const uint16_t *vp, Loads &ld, int lane, int row,
+                               const uint16_t *krow, const uint16_t *vrow) {
+    const int n = lane & 15, qd = lane >> 4;
+    const uint16_t *kr = n == row ? krow : kp + n * D;
+    for (int k = 0; k < 4; ++k) ld.kf[k] = *reinterpret_cast<const u32x4 *>(kr + 32 * k + 8 * qd);
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t *vr = (4 * qd + i) == row ? vrow : vp + (4 * qd + i) * D;
+      ld.vf[i] = *reinterpret_cast<const u32x4 *>(vr + 8 * n);
+    }
+  }
+
   // Attends over one loaded page; rows whose bit in `valid` is clear are
   // ignored (their bits may be anything, even NaN).
   __device__ void compute(const Loads &ld, uint32_t valid, int lane) {

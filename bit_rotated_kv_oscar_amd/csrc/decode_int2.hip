@@ -15,22 +15,21 @@
 //   score_t = sum_g s_tg (q_g . c_tg) + z_tg sum_{i in g} q_i
 //   o       = sum_g [ sum_t (p_t s_tg) c_tg ] + sum_t p_t z_tg
 //
-// Three kernels per call, in stream order:
-//   prologue (one block per (request, KV head)):
-//     - optional append: the token leaving the recent window (position
-//       L-128 when L >= 144) is read from its ring slot, rotated, clipped,
-//       quantised and stored in history; the new token takes the slot;
-//     - q_rot = q R_K * sm_scale * log2(e) for the query heads of the group,
-//       laid out as the B operand of the score MFMAs (fp16 high + low parts)
-//       with the column sums that cancel the code expansion's constant and
-//       the per-group sums of q_rot.
+// Two kernels per call, in stream order:
 //   attend (one workgroup of 8 waves per (request, KV head, split)):
-//     split 0 attends over the raw BF16 sink + recent pages, split s >= 1
-//     over history pages (wave w takes every 8th page of the split; page ids
-//     preloaded 64 at a time; pages copied straight into a per-wave LDS ring
-//     DEPTH pages ahead of the one being computed).
-//     Each workgroup writes an unnormalised partial (o[128], m, l) per query
-//     head.
+//     split 0 attends over the raw BF16 sink + recent pages (a token being
+//     appended is read from k_new / v_new); splits s >= 1 over history pages
+//     (wave w takes every 8th page of the split; page ids preloaded 64 at a
+//     time; pages copied straight into a per-wave LDS ring DEPTH pages ahead
+//     of the one being computed).  While the first copies fly, each history
+//     workgroup computes q_rot = q R_K * sm_scale * log2(e) for the query
+//     heads of its group and lays it out as the A operand of the score
+//     MFMAs (fp16 high + low parts, scale groups in separate rows).  On an
+//     append, the workgroup holding the last history page rotates, clips and
+//     quantises the token leaving the recent window (position L-128 when
+//     L >= 144) into history (and patches its own LDS copy of the page),
+//     then stores the new token in that ring slot.  Each workgroup writes an
+//     unnormalised partial (o[128], m, l) per query head.
 //   merge (one block per (request, KV head)): LSE-combines the partials,
 //     rotates the history part back with R_V^T, adds the raw part and
 //     normalises (fp32 out).  A kernel boundary, not an in-kernel fence, makes
@@ -45,8 +44,6 @@
 namespace oscar {
 
 constexpr int AW = 8;                // waves per attend workgroup
-constexpr int FRAG_DW = 96;          // dwords per lane of the q fragment block (at most)
-constexpr int PRO_THREADS = 512;     // prologue block: K half + V half
 constexpr int MAX_SPLITS = 255;      // history splits per (request, KV head)
 
 // Row layout of the score product for a GQA group of GQA query heads and NG
@@ -92,12 +89,15 @@ SplitPlan plan_int2_splits(int batch, int n_kv_heads, int max_seq_len) {
     p.n_splits = 0;
     return p;
   }
-  // Resident attend workgroups: two per CU on 256 CUs.  When every unit
-  // (request, KV head) fits in one round with at least one history split,
-  // spread each unit's pages over as many splits as that round holds (its
-  // raw workgroup included); otherwise use splits of 8 pages per wave.
+  // One round of attend workgroups, one per CU on 256 CUs (measured faster
+  // at batch 1 than two per CU: each workgroup's fixed work, the q fragment
+  // and the epilogue, is paid half as often and the merge reads half the
+  // partials).  When every unit (request, KV head) fits in that round with
+  // at least one history split, spread each unit's pages over as many splits
+  // as it holds (its raw workgroup included); otherwise use splits of 32
+  // pages per wave.
   const int64_t units = int64_t(batch) * n_kv_heads;
-  const int64_t slots = 2 * 256;
+  const int64_t slots = 256;
   int64_t pps;
   if (slots - units >= units) {
     const int64_t per_unit = (slots - units) / units;
@@ -114,12 +114,10 @@ SplitPlan plan_int2_splits(int batch, int n_kv_heads, int max_seq_len) {
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-static size_t frag_bytes(int batch, int hkv) { return align256(size_t(batch) * hkv * FRAG_DW * 64 * 4); }
 
 size_t decode_int2_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int max_seq_len) {
   const SplitPlan p = plan_int2_splits(batch, n_kv_heads, max_seq_len);
-  return frag_bytes(batch, n_kv_heads) +
-         align256(size_t(batch) * n_q_heads * (1 + p.n_splits) * PART_STRIDE * sizeof(float));
+  return align256(size_t(batch) * n_q_heads * (1 + p.n_splits) * PART_STRIDE * sizeof(float));
 }
 
 struct StepArgs {
@@ -137,20 +135,23 @@ struct StepArgs {
   float pv_scale, pv_unscale;     // 2^k and 2^-k applied to the PV operand
   float pk01, pk23;               // log2(4 * 2^k), log2(16 * 2^k): PV factors of tokens 4q+{0,1}, 4q+{2,3}
   uint32_t ex_m4, ex_m16, ex_e;   // code expansion constants 0x03000300, 0x00C000C0, 0x3C003C00
-  uint32_t *frag;                 // [B][Hkv][FRAG_DW][64]
   float *parts;                   // [B][Hq][1 + n_splits][PART_STRIDE]
   float *out;                     // [B][Hq][128]
 };
 
 __device__ inline bool valid_len(int L, int max_len) { return L >= 1 && L <= max_len; }
 
-// ------------------------------------------------------------------ prologue
+// ------------------------------------------------------------------ q and append
 
-// Quantise one rotated vector (128 values in LDS, already in y) into history
-// row `row` of the block at `blk` (K or V area), G channels per group.
-// Threads t < 128 of the half take part; `codes` is LDS scratch.
+// Quantise one rotated vector y (128 values in LDS) into row `row` of the K
+// or V area of the history block `blk` (global; may be null), G channels
+// per group, and record the same bytes as a patch for a copy of the block
+// in LDS: entries (byte offset in the block, value, mask), K: 8 code dwords
+// then NG meta dwords; V: 32 code dwords then NG meta dwords.  Threads
+// t < 128 of the caller's half work; the barriers are workgroup-wide, so
+// every thread of the workgroup calls this.
 __device__ inline void store_int2_row(const float *y, float clip, int G, bool is_v, uint8_t *blk, int row,
-                                      uint8_t *codes, float *sz_lds, int t) {
+                                      uint8_t *codes, float *sz_lds, uint32_t *patch, int t) {
   const int ng = D / G;
   if (t < ng) {
     float lo = fminf(fmaxf(y[t * G], -clip), clip), hi = lo;
@@ -169,7 +170,14 @@ __device__ inline void store_int2_row(const float *y, float clip, int G, bool is
     codes[t] = s > 0.f ? uint8_t(min(3, max(0, int(rintf((v - z) / s))))) : uint8_t(0);
   }
   __syncthreads();
-  uint32_t *area = reinterpret_cast<uint32_t *>(blk + (is_v ? v_codes_off(G) : k_codes_off(G)));
+  const int area_off = is_v ? v_codes_off(G) : k_codes_off(G);
+  uint32_t *area = blk ? reinterpret_cast<uint32_t *>(blk + area_off) : nullptr;
+  auto put = [&](int e, int dw, uint32_t w, uint32_t mask) {
+    patch[3 * e] = uint32_t(area_off + 4 * dw);
+    patch[3 * e + 1] = w;
+    patch[3 * e + 2] = mask;
+    if (blk) area[dw] = (mask == 0xFFFFFFFFu) ? w : ((area[dw] & ~mask) | w);
+  };
   if (!is_v) {
     // the 8 dwords of token `row`: lanes 16q + row, halves d
     if (t < 8) {
@@ -180,7 +188,7 @@ __device__ inline void store_int2_row(const float *y, float clip, int G, bool is
         w |= uint32_t(codes[c0]) << slot_lo(u);
         w |= uint32_t(codes[c0 + 1]) << slot_hi(u);
       }
-      area[2 * (16 * q + row) + d] = w;
+      put(t, 2 * (16 * q + row) + d, w, 0xFFFFFFFFu);
     }
   } else {
     // token `row` owns 4 codes in each of 32 dwords (lanes 16 (row/4) + m, halves d)
@@ -195,191 +203,242 @@ __device__ inline void store_int2_row(const float *y, float clip, int G, bool is
         w |= uint32_t(codes[c]) << bit;
         mask |= 3u << bit;
       }
-      uint32_t *p = area + 2 * (16 * q + m) + d;
-      *p = (*p & ~mask) | w;
+      put(t, 2 * (16 * q + m) + d, w, mask);
     }
   }
   if (t < ng) {
-    __half2 *meta = reinterpret_cast<__half2 *>(blk + (is_v ? v_meta_off(G) : k_meta_off(G)));
-    meta[PAGE * t + row] = __halves2half2(__float2half_rn(sz_lds[2 * t]), __float2half_rn(sz_lds[2 * t + 1]));
+    const int meta_off = is_v ? v_meta_off(G) : k_meta_off(G);
+    const uint32_t w = uint32_t(__half_as_ushort(__float2half_rn(sz_lds[2 * t]))) |
+                       (uint32_t(__half_as_ushort(__float2half_rn(sz_lds[2 * t + 1]))) << 16);
+    const int e = (is_v ? 32 : 8) + t;
+    patch[3 * e] = uint32_t(meta_off + 4 * (PAGE * t + row));
+    patch[3 * e + 1] = w;
+    patch[3 * e + 2] = 0xFFFFFFFFu;
+    if (blk) *reinterpret_cast<uint32_t *>(blk + meta_off + 4 * (PAGE * t + row)) = w;
   }
 }
 
+// LDS work area of the q fragment build and of the token that leaves the
+// recent window.
 template <int GQA, int NG>
-__global__ void __launch_bounds__(PRO_THREADS) prologue_kernel(StepArgs a) {
+struct QWork {
+  static constexpr int SEG = (D / NG) < 64 ? (D / NG) : 64;  // channels per wave-level partial sum
+  float x[GQA + 1][D];  // q heads in, then the evicted k
+  float y[GQA + 1][D];  // rotated
+  float xv[D], yv[D];   // evicted v, rotated
+  _Float16 qa[2][GQA][D];
+  float gpart[3][GQA][D / SEG];
+  float red[AW];
+  uint8_t codes[2][D];
+  float sz[2][8];
+  uint32_t patch_k[3 * 12];
+  uint32_t patch_v[3 * 36];
+};
+
+// Where the new token of an append goes and which token leaves the window.
+struct AppendPlan {
+  int L0;          // position of the new token
+  int raw_page;    // BF16 page id of its row (-1 if bad)
+  int raw_row;     // row in that page
+  int raw_pg;      // index of that page in the request's BF16 table (0 sink, 1..8 ring)
+  bool evict;      // position L0 - 128 moves into history (L0 >= 144)
+  int evict_j;     // its history page index (= last history page)
+  int evict_row;   // its row
+};
+
+__device__ inline AppendPlan plan_append(const StepArgs &a, int b) {
+  AppendPlan p;
+  const oscar_layer_cache &c = a.c;
+  p.L0 = a.len_before[b];
+  if (p.L0 < N_SINK) {
+    p.raw_pg = 0;
+    p.raw_row = p.L0;
+  } else {
+    const int slot = p.L0 % N_RECENT;
+    p.raw_pg = 1 + slot / PAGE;
+    p.raw_row = slot % PAGE;
+  }
+  const int page = c.bf16_pt[b * BF16_PT + p.raw_pg];
+  p.raw_page = (page >= 0 && page < c.n_bf16_pages) ? page : -1;
+  p.evict = p.L0 >= N_RAW;
+  const int h = p.L0 - N_RAW;  // history index of position L0 - 128
+  p.evict_j = p.evict ? h / PAGE : -1;
+  p.evict_row = p.evict ? h % PAGE : 0;
+  return p;
+}
+
+// Workgroup-wide: q' = q R_K (and, when `evict`, the rotation and INT2 row of
+// the token leaving the recent window, written to history and recorded as
+// patches; then the new token takes its ring slot), and the A-operand
+// fragment block of the score product in frag_lds (layout of Rows).
+template <int GQA, int NG>
+__device__ void build_q(const StepArgs &a, int b, int hk, int tid, QWork<GQA, NG> &w, uint32_t *frag_lds,
+                        bool evict, const AppendPlan &ap, uint8_t *evict_blk) {
   using R = Rows<GQA, NG>;
-  constexpr int G = R::G;
-  const int hk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int half = tid >> 8, t = tid & 255;  // half 0: K (and the query), 1: V
+  constexpr int G = R::G, SEG = QWork<GQA, NG>::SEG, NT = AW * 64;
   const oscar_layer_cache &c = a.c;
   const int hkv = c.n_kv_heads;
-  __shared__ float xin[2][GQA + 1][D];       // [half][vector][channel]
-  __shared__ float yout[2][GQA + 1][D];
-  __shared__ float part_lds[2][2 * (GQA + 1) * D];
-  __shared__ uint8_t codes[2][D];
-  __shared__ float sz_lds[2][8];
-  __shared__ float red[256];
-  __shared__ int evict_s;
-
-  // R^T rows for this thread (output channel jx, inputs 64 hf .. 64 hf + 63),
-  // loaded first so they overlap the dependent loads below
-  const bool want_q = a.q != nullptr;
-  const int jx = t & (D - 1), hf = t >> 7;
-  f32x4 rr[16];
-  if ((half == 0 && want_q) || a.k_new) {
-    const float *RT = reinterpret_cast<const float *>((half ? a.fv : a.fk) + FORM_RT) + jx * D + 64 * hf;
-#pragma unroll
-    for (int i4 = 0; i4 < 16; ++i4) rr[i4] = *reinterpret_cast<const f32x4 *>(RT + 4 * i4);
-  }
-
-  // ---------------- append (optional)
-  int evict_pos = -1;  // position leaving the ring, or -1
-  uint8_t *evict_blk = nullptr;
-  if (a.k_new) {
-    const int L0 = a.len_before[b];
-    if (L0 < 0 || L0 >= (1 << 30)) {
-      if (tid == 0 && hk == 0) flag_status(c.status, OSCAR_STATUS_BAD_LEN);
-    } else {
-      const uint16_t *src = (half ? a.v_new : a.k_new) + (int64_t(b) * hkv + hk) * D;
-      int page, row;
-      if (L0 < N_SINK) {
-        page = c.bf16_pt[b * BF16_PT];
-        row = L0;
-      } else {
-        const int slot = L0 % N_RECENT;
-        page = c.bf16_pt[b * BF16_PT + 1 + slot / PAGE];
-        row = slot % PAGE;
-        if (L0 >= N_RAW) evict_pos = L0 - N_RECENT;
-      }
-      const bool page_ok = page >= 0 && page < c.n_bf16_pages;
-      uint16_t *ring = page_ok ? c.bf16 + ((int64_t(page) * hkv + hk) * 2 + half) * (PAGE * D) + row * D : nullptr;
-      if (evict_pos >= 0) {
-        const int hj = (evict_pos - N_SINK) / PAGE;
-        const int pid = hj < c.hist_pt_stride ? c.hist_pt[int64_t(b) * c.hist_pt_stride + hj] : -1;
-        if (pid >= 0 && pid < c.n_hist_pages && page_ok)
-          evict_blk = c.hist + (int64_t(pid) * hkv + hk) * hist_block_bytes(G);
-        else if (t == 0 && half == 0)
-          flag_status(c.status, OSCAR_STATUS_BAD_PAGE);
-        if (t < D) xin[half][GQA][t] = (evict_blk && ring) ? bf16_to_f32(ring[t]) : 0.f;
-      } else if (!page_ok && t == 0 && half == 0) {
-        flag_status(c.status, OSCAR_STATUS_BAD_PAGE);
-      }
-      __syncthreads();  // the evicted row is read before the slot is overwritten
-      if (ring && t < D) ring[t] = src[t];
-    }
-  }
-  // ---------------- query (K half)
-  if (want_q && half == 0) {
-    for (int e = t; e < GQA * D; e += 256)
-      xin[0][e / D][e % D] = bf16_to_f32(a.q[(int64_t(b) * a.n_q_heads + hk * GQA) * D + e]);
-  }
-  if (want_q) {
-    const int L = a.k_new ? a.len_before[b] + 1 : a.seq_lens[b];
-    if (!valid_len(L, a.max_seq_len)) {  // attend skips this request: zero its output here
-      if (tid == 0 && hk == 0) flag_status(c.status, OSCAR_STATUS_BAD_LEN);
-      for (int e = tid; e < GQA * D; e += PRO_THREADS)
-        a.out[(int64_t(b) * a.n_q_heads + hk * GQA) * D + e] = 0.f;
-    }
-  }
-  if (tid == 0) evict_s = evict_blk ? 1 : 0;
-  __syncthreads();
-  // ---------------- rotations: K half rotates q heads + evicted k, V half the evicted v
+  // R^T rows jr and jr + 64 (output channels), inputs 32k + 4qq .. + 3 for
+  // k = 0..3: eight consecutive lanes read one 128-byte line of a row
+  const int jr = tid >> 3, qq = tid & 7;
+  f32x4 rk[8], rv[8];
   {
-    // both halves run the same code path (uniform barriers); unused vectors are zero
-    float acc[GQA + 1];
+    const float *RT = reinterpret_cast<const float *>(a.fk + FORM_RT) + jr * D + 4 * qq;
 #pragma unroll
-    for (int v = 0; v <= GQA; ++v) acc[v] = 0.f;
-    const bool need = (half == 0 && want_q) || evict_s;
-    if (need) {
+    for (int k = 0; k < 8; ++k) rk[k] = *reinterpret_cast<const f32x4 *>(RT + (k >> 2) * 64 * D + 32 * (k & 3));
+  }
+  if (evict) {
+    const float *RT = reinterpret_cast<const float *>(a.fv + FORM_RT) + jr * D + 4 * qq;
 #pragma unroll
-      for (int i4 = 0; i4 < 16; ++i4)
+    for (int k = 0; k < 8; ++k) rv[k] = *reinterpret_cast<const f32x4 *>(RT + (k >> 2) * 64 * D + 32 * (k & 3));
+  }
+  for (int e = tid; e < GQA * D; e += NT)
+    w.x[e / D][e % D] = bf16_to_f32(a.q[(int64_t(b) * a.n_q_heads + hk * GQA) * D + e]);
+  uint16_t *ring_k = nullptr, *ring_v = nullptr;
+  if (evict) {
+    // the ring slot of the new token holds the token that leaves the window
+    if (ap.raw_page >= 0) {
+      ring_k = c.bf16 + ((int64_t(ap.raw_page) * hkv + hk) * 2 + 0) * (PAGE * D) + ap.raw_row * D;
+      ring_v = ring_k + PAGE * D;
+    }
+    if (tid < D) w.x[GQA][tid] = ring_k ? bf16_to_f32(ring_k[tid]) : 0.f;
+    else if (tid < 2 * D) w.xv[tid - D] = ring_k ? bf16_to_f32(ring_v[tid - D]) : 0.f;
+  }
+  __syncthreads();
+  if (evict && ring_k) {  // the old row is in LDS: the new token takes the slot
+    const uint16_t *kn = a.k_new + (int64_t(b) * hkv + hk) * D, *vn = a.v_new + (int64_t(b) * hkv + hk) * D;
+    if (tid < D) ring_k[tid] = kn[tid];
+    else if (tid < 2 * D) ring_v[tid - D] = vn[tid - D];
+  }
+  // rotations: thread (jr, qq) sums 16 inputs of rows jr and jr + 64, eight
+  // lanes combine; the largest |q'| is tracked on the way
+  float amax = 0.f;
+  {
+    const int nv = evict ? GQA + 1 : GQA;
+    for (int v = 0; v <= GQA; ++v) {
+      if (v >= nv) break;
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int i = 64 * hf + 4 * i4 + e;
-#pragma unroll
-          for (int v = 0; v <= GQA; ++v) acc[v] = fmaf(xin[half][v][i], rr[i4][e], acc[v]);
+          const float xi = w.x[v][32 * k + 4 * qq + e];
+          a0 = fmaf(xi, rk[k][e], a0);
+          a1 = fmaf(xi, rk[4 + k][e], a1);
         }
+#pragma unroll
+      for (int off = 1; off < 8; off <<= 1) {
+        a0 += __shfl_xor(a0, off);
+        a1 += __shfl_xor(a1, off);
+      }
+      if (qq == 0) {
+        w.y[v][jr] = a0;
+        w.y[v][jr + 64] = a1;
+      }
+      if (v < GQA) amax = fmaxf(amax, fmaxf(fabsf(a0), fabsf(a1)));
     }
+    if (evict) {
+      float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-    for (int v = 0; v <= GQA; ++v) part_lds[half][(hf * (GQA + 1) + v) * D + jx] = acc[v];
-    __syncthreads();
-    if (t < D)
+      for (int k = 0; k < 4; ++k)
 #pragma unroll
-      for (int v = 0; v <= GQA; ++v)
-        yout[half][v][t] = part_lds[half][v * D + t] + part_lds[half][(GQA + 1 + v) * D + t];
-    __syncthreads();
+        for (int e = 0; e < 4; ++e) {
+          const float xi = w.xv[32 * k + 4 * qq + e];
+          a0 = fmaf(xi, rv[k][e], a0);
+          a1 = fmaf(xi, rv[4 + k][e], a1);
+        }
+#pragma unroll
+      for (int off = 1; off < 8; off <<= 1) {
+        a0 += __shfl_xor(a0, off);
+        a1 += __shfl_xor(a1, off);
+      }
+      if (qq == 0) {
+        w.yv[jr] = a0;
+        w.yv[jr + 64] = a1;
+      }
+    }
   }
-  // ---------------- quantise the evicted token into history
-  if (evict_s) {
-    const int hrow = (evict_pos - N_SINK) % PAGE;
-    store_int2_row(yout[half][GQA], half ? a.clip_v : a.clip_k, G, half == 1, evict_blk, hrow, codes[half],
-                   sz_lds[half], t);
-  }
-  // ---------------- q fragments (K half builds them; both halves share the barriers)
-  const float sc = a.sm_scale * LOG2E;
-  float amax = 0.f;
-  if (want_q && half == 0)
-    for (int e = t; e < GQA * D; e += 256) amax = fmaxf(amax, fabsf(yout[0][e / D][e % D] * sc));
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  if ((t & 63) == 0 && half == 0) red[t >> 6] = amax;
+  if ((tid & 63) == 0) w.red[tid >> 6] = amax;
   __syncthreads();
-  if (!want_q) return;  // uniform over the block
-  const float gmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  if (evict) {  // uniform over the workgroup (barriers inside)
+    const int half = tid >> 8, t = tid & 255;
+    store_int2_row(half ? w.yv : w.y[GQA], half ? a.clip_v : a.clip_k, G, half == 1, evict_blk, ap.evict_row,
+                   w.codes[half], w.sz[half], half ? w.patch_v : w.patch_k, t);
+  }
+  // ---------------- the fragment block
+  const float sc = a.sm_scale * LOG2E;
+  float gmax = 0.f;
+#pragma unroll
+  for (int i = 0; i < AW; ++i) gmax = fmaxf(gmax, w.red[i]);
+  gmax *= sc;
   float kq = 1.f;  // keeps |q' * 16 * kq| <= 2^14 (fp16 operands)
   while (gmax * 16.f * kq > 16384.f) kq *= 0.5f;
-  // A operand values q' * w_c * kq as fp16 high part and low part x 2^11;
-  // w_c = 4 or 16, the weight that the K code expansion puts on channel c
-  __shared__ _Float16 qa[2][GQA][D];
-  __shared__ float rsum[2][GQA][NG];  // row sums of the two parts per group
-  __shared__ float gsum[GQA][NG];     // kq * sum of q' over each group
-  if (half == 0)
-    for (int e = t; e < GQA * D; e += 256) {
-      const int h = e / D, ch = e % D;
-      const float x = yout[0][h][ch] * sc * (((ch & 3) < 2) ? 4.f : 16.f) * kq;
-      const _Float16 hi = _Float16(x);
-      qa[0][h][ch] = hi;
-      qa[1][h][ch] = _Float16((x - float(hi)) * 2048.f);
+  // A operand values q' * w_c * kq as fp16 high part and low part x 2^11
+  // (w_c = 4 or 16, the weight that the K code expansion puts on channel c),
+  // and their sums over each scale group by wave reductions: a wave covers
+  // 64 consecutive channels of one head (uniform loop bounds)
+  for (int e0 = 0; e0 < GQA * D; e0 += NT) {
+    const int e = e0 + tid;
+    const bool in = e < GQA * D;
+    const int h = in ? e / D : 0, ch = e % D;
+    float vh = 0.f, vl = 0.f, vq = 0.f;
+    if (in) {
+      const float y = w.y[h][ch] * sc;
+      const float x = y * (((ch & 3) < 2) ? 4.f : 16.f) * kq;
+      const _Float16 hi = _Float16(x), lo = _Float16((x - float(hi)) * 2048.f);
+      w.qa[0][h][ch] = hi;
+      w.qa[1][h][ch] = lo;
+      vh = float(hi);
+      vl = float(lo);
+      vq = y * kq;
     }
-  __syncthreads();
-  if (half == 0 && t < 3 * GQA * NG) {
-    const int which = t / (GQA * NG), h = (t % (GQA * NG)) / NG, g = t % NG;
-    float sum = 0.f;
-    if (which < 2) {
-      for (int i = 0; i < G; ++i) sum += float(qa[which][h][g * G + i]);
-      rsum[which][h][g] = sum;
-    } else {
-      for (int i = 0; i < G; ++i) sum += yout[0][h][g * G + i] * sc;
-      gsum[h][g] = sum * kq;
+#pragma unroll
+    for (int off = 1; off < SEG; off <<= 1) {
+      vh += __shfl_xor(vh, off);
+      vl += __shfl_xor(vl, off);
+      vq += __shfl_xor(vq, off);
+    }
+    if (in && ch % SEG == 0) {
+      w.gpart[0][h][ch / SEG] = vh;
+      w.gpart[1][h][ch / SEG] = vl;
+      w.gpart[2][h][ch / SEG] = vq;
     }
   }
   __syncthreads();
-  if (half == 1 || t >= 64) return;
-  const int lane = t, r = lane & 15, qd = lane >> 4;
-  uint32_t *fr = a.frag + (int64_t(b) * hkv + hk) * FRAG_DW * 64;
-  for (int ch = 0; ch < R::NCH; ++ch) {
-    {
+  auto gsum = [&](int which, int h, int g) {
+    float sum = 0.f;
+    for (int k = 0; k < G / SEG; ++k) sum += w.gpart[which][h][g * (G / SEG) + k];
+    return sum;
+  };
+  for (int idx = tid; idx < R::FR_DW * 64; idx += NT) {
+    const int d = idx / 64, lane = idx % 64, r = lane & 15, qd = lane >> 4;
+    uint32_t fw;
+    if (d < R::FR_INIT) {
+      // A operand: row r of chain ch, k-block kb, dword v (channels c0, c0+1)
+      const int ch = d / 16, kb = (d % 16) / 4, v = d % 4;
       const int h = R::HC * ch + r / R::J, g = (r % R::J) / 2, part = r & 1;
+      const int c0 = 32 * kb + 8 * qd + 2 * v;
       auto bits = [&](int cc) -> uint32_t {
-        return (h < GQA && cc / G == g) ? uint32_t(__builtin_bit_cast(uint16_t, qa[part][h][cc])) : 0u;
+        return (h < GQA && cc / G == g) ? uint32_t(__builtin_bit_cast(uint16_t, w.qa[part][h][cc])) : 0u;
       };
-      for (int kb = 0; kb < 4; ++kb)
-        for (int v = 0; v < 4; ++v) {
-          const int c0 = 32 * kb + 8 * qd + 2 * v;
-          fr[(R::FR_A + 16 * ch + 4 * kb + v) * 64 + lane] = bits(c0) | (bits(c0 + 1) << 16);
-        }
-    }
-    // the expanded codes are 1 + c / w_c: start each row at minus its sum
-    for (int i = 0; i < 4; ++i) {
+      fw = bits(c0) | (bits(c0 + 1) << 16);
+    } else if (d < R::FR_Q) {
+      // the expanded codes are 1 + c / w_c: each row starts at minus its sum
+      const int ch = (d - R::FR_INIT) / 4, i = (d - R::FR_INIT) % 4;
       const int rr = 4 * qd + i;
       const int h = R::HC * ch + rr / R::J, g = (rr % R::J) / 2, part = rr & 1;
-      fr[(R::FR_INIT + 4 * ch + i) * 64 + lane] = __float_as_uint(h < GQA ? -rsum[part][h][g] : 0.f);
-    }
-    for (int k = 0; k < 2; ++k) {
+      fw = __float_as_uint(h < GQA ? -gsum(part, h, g) : 0.f);
+    } else if (d < R::FR_INVKQ) {
+      const int ch = (d - R::FR_Q) / 2, k = (d - R::FR_Q) % 2;
       const int h = R::HC * ch + R::pair_head(qd, k), g = R::pair_group(qd, k);
-      fr[(R::FR_Q + 2 * ch + k) * 64 + lane] = __float_as_uint(h < GQA ? gsum[h][g] : 0.f);
+      fw = __float_as_uint(h < GQA ? gsum(2, h, g) : 0.f);
+    } else {
+      fw = __float_as_uint(1.f / kq);
     }
+    frag_lds[idx] = fw;
   }
-  fr[R::FR_INVKQ * 64 + lane] = __float_as_uint(1.f / kq);
+  __syncthreads();
 }
 
 // ------------------------------------------------------------------ attend
@@ -547,10 +606,11 @@ __device__ inline float gather(const float (&x)[NCH][SPL], int src, int my_ch, i
 // forms B_g = fp16(pw s_tg) for each scale group g; acc[r] += Vexp_r B_g(r)
 // with Vexp = 1 + code/w_t, and cacc[g] += 1 B_g, whose rows all equal the
 // column sums of B_g: acc - cacc is then exactly sum_t B code / w_t.
-template <int GQA, int NG>
+template <int GQA, int NG, class Prep>
 __device__ void history_wave(const StepArgs &a, int b, int hk, int L, int j0, int j1, int wave, int lane,
-                             const uint32_t *frag_lds, uint8_t *ring, float *zs, float *o_lds, float *m_lds,
-                             float *l_lds) {
+                             Prep &&prep, const uint32_t *frag_lds, uint8_t *ring, float *zs, float *o_lds,
+                             float *m_lds, float *l_lds, int patch_i, const uint32_t *patch_k,
+                             const uint32_t *patch_v) {
   using R = Rows<GQA, NG>;
   constexpr int NCH = R::NCH, SPL = R::SPL, G = R::G, HC = R::HC;
   constexpr int SB = hist_block_bytes(G);
@@ -564,23 +624,11 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int L, int j0, in
   const int nh = n_hist_tokens(L);
   const int npw = j1 > j0 + wave ? (j1 - j0 - wave + AW - 1) / AW : 0;
 
+  // the q fragment (filled from LDS once the first page copies are issued)
   f16x8 aq[NCH][4];
   f32x4 dinit[NCH];
   float qz[NCH][2];
-#pragma unroll
-  for (int ch = 0; ch < NCH; ++ch) {
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const uint32_t *f = frag_lds + (R::FR_A + 16 * ch + 4 * kb) * 64 + lane;
-      aq[ch][kb] = as_f16x8(f[0], f[64], f[128], f[192]);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dinit[ch][i] = __uint_as_float(frag_lds[(R::FR_INIT + 4 * ch + i) * 64 + lane]);
-    qz[ch][0] = __uint_as_float(frag_lds[(R::FR_Q + 2 * ch) * 64 + lane]);
-    qz[ch][1] = __uint_as_float(frag_lds[(R::FR_Q + 2 * ch + 1) * 64 + lane]);
-  }
-  const float inv_kq = __uint_as_float(frag_lds[R::FR_INVKQ * 64 + lane]);
-  const float kq = 1.f / inv_kq;
+  float inv_kq = 1.f, kq = 1.f;
   const bool w16 = (t & 3) >= 2;
   const float lw_t = w16 ? a.pk23 : a.pk01;  // log2(w_t 2^kpv)
   const float inv_w = w16 ? 0.0625f : 0.25f;
@@ -757,6 +805,16 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int L, int j0, in
     if (i + DEPTH - 1 < npw) issue(i + DEPTH - 1, (i + DEPTH - 1) % DEPTH);
     wait_pages(min(DEPTH - 1, npw - 1 - i));
     const int sl = i % DEPTH;
+    if (i == patch_i) {
+      // the row of the token that has just left the recent window: this
+      // workgroup quantised it (and wrote it to history) before the loop
+      constexpr int NK = 8 + NG, NV = 32 + NG;
+      if (lane < NK + NV) {
+        const uint32_t *pe = lane < NK ? patch_k + 3 * lane : patch_v + 3 * (lane - NK);
+        uint32_t *d = reinterpret_cast<uint32_t *>(ring + sl * SB + pe[0]);
+        *d = (*d & ~pe[2]) | pe[1];
+      }
+    }
     // tested as a per-lane value (the same in every lane): as a scalar branch
     // the compiler copies the accumulators at its merge point every page
     uint32_t okv = ok_slots;
@@ -768,14 +826,34 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int L, int j0, in
     }
   };
 
-  if (npw > 0 && c.n_hist_pages < 1) {
+  // first page copies, then the q fragment (global -> LDS, whole workgroup)
+  // while they fly
+  const bool any_pages = npw > 0 && c.n_hist_pages >= 1;
+  if (any_pages)
+    for (int i = 0; i < DEPTH - 1 && i < npw; ++i) issue(i, i);
+  prep();  // workgroup-wide: the q fragment into frag_lds (and the append)
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const uint32_t *f = frag_lds + (R::FR_A + 16 * ch + 4 * kb) * 64 + lane;
+      aq[ch][kb] = as_f16x8(f[0], f[64], f[128], f[192]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dinit[ch][i] = __uint_as_float(frag_lds[(R::FR_INIT + 4 * ch + i) * 64 + lane]);
+    qz[ch][0] = __uint_as_float(frag_lds[(R::FR_Q + 2 * ch) * 64 + lane]);
+    qz[ch][1] = __uint_as_float(frag_lds[(R::FR_Q + 2 * ch + 1) * 64 + lane]);
+  }
+  inv_kq = __uint_as_float(frag_lds[R::FR_INVKQ * 64 + lane]);
+  kq = 1.f / inv_kq;
+
+  if (npw > 0 && !any_pages) {
     if (lane == 0) flag_status(c.status, OSCAR_STATUS_BAD_PAGE);
   } else if (npw > 0) {
     // only the last history page of the request can be partial; it is the
     // last page of whichever wave holds it
     const bool last_partial = (nh % PAGE) != 0 && j0 + wave + AW * (npw - 1) == (nh - 1) / PAGE;
     const int nfull = npw - (last_partial ? 1 : 0);
-    for (int i = 0; i < DEPTH - 1 && i < npw; ++i) issue(i, i);
     for (int i = 0; i < nfull; ++i) step(i, std::false_type{});
     if (last_partial) step(npw - 1, std::true_type{});
   }
@@ -849,88 +927,124 @@ __device__ inline uint32_t raw_valid_rows(int L, int page) {
 
 // Merge of one (request, KV head): LSE-combines the `used` partials of each
 // query head of the group, rotates the history part back with R_V^T, adds
-// the raw part (split 0) and normalises.  1024 threads: wave h computes head
-// h's weights; then (head, channel, half of the splits) per thread.
-constexpr int MERGE_THREADS = 1024;
+// the raw part (split 0) and normalises.  Built for latency: thread (h, c)
+// issues the loads of all its partial values, the (m, l) pairs and its slice
+// of R_V at once, so the kernel waits on memory about once.
+constexpr int MERGE_CH = 32;  // partials per thread held in registers at a time
 
 template <int GQA>
-__global__ void __launch_bounds__(MERGE_THREADS) merge_kernel(StepArgs a) {
+constexpr int merge_threads() { return D * (GQA < 2 ? 2 : GQA); }
+
+template <int GQA>
+__global__ void __launch_bounds__(merge_threads<GQA>()) merge_kernel(StepArgs a) {
+  constexpr int NT = merge_threads<GQA>();
   const int hk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int wave = wave_id(), lane = tid & 63;
-  const oscar_layer_cache &c = a.c;
+  const int h = tid / D, c = tid % D;  // (query head of the group, channel); h may be >= GQA
   const int L = a.k_new ? a.len_before[b] + 1 : a.seq_lens[b];
-  if (!valid_len(L, a.max_seq_len)) return;  // output zeroed by the prologue
+  if (!valid_len(L, a.max_seq_len)) return;  // output zeroed by the attend kernel
   const int used = 1 + (n_hist_pages(L) + a.pages_per_split - 1) / a.pages_per_split;
   const int64_t head_stride = int64_t(1 + a.n_splits) * PART_STRIDE;
   const float *parts0 = a.parts + (int64_t(b) * a.n_q_heads + hk * GQA) * head_stride;
-  __shared__ float w_lds[GQA][MAX_SPLITS + 1];
+  __shared__ float w_lds[GQA][MAX_SPLITS + 1];  // m, then the weight of each split
+  __shared__ float l_lds[GQA][MAX_SPLITS + 1];
   __shared__ float lsum[GQA];
-  __shared__ float rot[2][GQA][D];    // history part, two halves of the splits
-  __shared__ float plain[GQA][D];
-  __shared__ float back[8][GQA][D];   // R_V^T partial sums, 8 row groups
-  if (wave < GQA) {
-    const float *ph = parts0 + wave * head_stride;
-    float m = -INFINITY;
-    for (int s = lane; s < used; s += 64) m = fmaxf(m, ph[s * PART_STRIDE + D]);
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    float l = 0.f;
-    for (int s = lane; s < used; s += 64) {
-      const float ms = ph[s * PART_STRIDE + D];
-      const float w = (ms == -INFINITY) ? 0.f : fast_exp2(ms - m);
-      w_lds[wave][s] = w;
-      l = fmaf(w, ph[s * PART_STRIDE + D + 1], l);
-    }
-    for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
-    if (lane == 0) lsum[wave] = l;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < 2 * GQA * D; idx += MERGE_THREADS) {
-    const int hf = idx / (GQA * D), h = (idx / D) % GQA, ch = idx % D;
-    const float *ph = parts0 + h * head_stride + ch;
-    const int s0 = 1 + hf * ((used - 1 + 1) / 2), s1 = hf ? used : 1 + (used - 1 + 1) / 2;
-    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-    int s = s0;
-    for (; s + 3 < s1; s += 4) {
-      o0 = fmaf(w_lds[h][s], ph[s * PART_STRIDE], o0);
-      o1 = fmaf(w_lds[h][s + 1], ph[(s + 1) * PART_STRIDE], o1);
-      o2 = fmaf(w_lds[h][s + 2], ph[(s + 2) * PART_STRIDE], o2);
-      o3 = fmaf(w_lds[h][s + 3], ph[(s + 3) * PART_STRIDE], o3);
-    }
-    for (; s < s1; ++s) o0 = fmaf(w_lds[h][s], ph[s * PART_STRIDE], o0);
-    rot[hf][h][ch] = (o0 + o1) + (o2 + o3);
-    if (hf == 0) plain[h][ch] = w_lds[h][0] * ph[0];
-  }
-  __syncthreads();
-  // (rot R_V^T)[h][c] = sum_i rot[h][i] R_V[c][i]; thread: c = tid % 128,
-  // rows i in [16 g, 16 g + 16) with g = tid / 128
-  {
-    const int ch = tid & (D - 1), g = tid >> 7;
-    const float *R = reinterpret_cast<const float *>(a.fv + FORM_R) + ch * D + 16 * g;
-    f32x4 r[4];
+  __shared__ float rot[GQA][D];
+  __shared__ float back[GQA][D];
+
+  // ---- loads, all issued before any use
+  // R_V rows cr + 64 m (m < NR), inputs 16 k + 2 qq .. ; eight lanes per row
+  // read 128 contiguous bytes
+  constexpr int NR = 1024 / NT;  // rows per thread: 128 rows x 8 lanes over NT threads
+  const int cr = tid >> 3, qq = tid & 7;
+  const float *Rc = reinterpret_cast<const float *>(a.fv + FORM_R) + cr * D + 4 * qq;
+  f32x4 rv[4 * NR];
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) r[i4] = *reinterpret_cast<const f32x4 *>(R + 4 * i4);
+  for (int m = 0; m < NR; ++m)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      rv[4 * m + k] = *reinterpret_cast<const f32x4 *>(Rc + m * (NT / 8) * D + 32 * k);
+  const bool own = h < GQA;
+  const float *ph = parts0 + (own ? h : 0) * head_stride + c;
+  float ov[MERGE_CH];
+#pragma unroll
+  for (int j = 0; j < MERGE_CH; ++j) ov[j] = (own && 1 + j < used) ? ph[(1 + j) * PART_STRIDE] : 0.f;
+  const float o_raw = own ? ph[0] : 0.f;
+  for (int e = tid; e < GQA * used; e += NT) {
+    const int hh = e / used, sp = e % used;
+    const float *pm = parts0 + hh * head_stride + sp * PART_STRIDE + D;
+    w_lds[hh][sp] = pm[0];
+    l_lds[hh][sp] = pm[1];
+  }
+  __syncthreads();
+  // ---- per head: max over splits, split weights, total l (wave hh)
+  {
+    const int wave = wave_id(), lane = tid & 63;
+    for (int hh = wave; hh < GQA; hh += NT / 64) {
+      float m = -INFINITY;
+      for (int sp = lane; sp < used; sp += 64) m = fmaxf(m, w_lds[hh][sp]);
+      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      float l = 0.f;
+      for (int sp = lane; sp < used; sp += 64) {
+        const float ms = w_lds[hh][sp];
+        const float w = (ms == -INFINITY) ? 0.f : fast_exp2(ms - m);
+        w_lds[hh][sp] = w;
+        l = fmaf(w, l_lds[hh][sp], l);
+      }
+      for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
+      if (lane == 0) lsum[hh] = l;
+    }
+  }
+  __syncthreads();
+  // ---- history part of head h, channel c (rotated basis)
+  float raw = 0.f;
+  if (own) {
+    float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < MERGE_CH; ++j) {
+      const float w = (1 + j < used) ? w_lds[h][1 + j] : 0.f;
+      if (j & 1)
+        acc1 = fmaf(w, ov[j], acc1);
+      else
+        acc0 = fmaf(w, ov[j], acc0);
+    }
+    for (int s0 = 1 + MERGE_CH; s0 < used; s0 += MERGE_CH) {
+      float o2[MERGE_CH];
+#pragma unroll
+      for (int j = 0; j < MERGE_CH; ++j) o2[j] = (s0 + j < used) ? ph[(s0 + j) * PART_STRIDE] : 0.f;
+#pragma unroll
+      for (int j = 0; j < MERGE_CH; ++j) {
+        const float w = (s0 + j < used) ? w_lds[h][s0 + j] : 0.f;
+        acc0 = fmaf(w, o2[j], acc0);
+      }
+    }
+    rot[h][c] = acc0 + acc1;
+    raw = w_lds[h][0] * o_raw;
+  }
+  __syncthreads();
+  // ---- (rot R_V^T)[hh][c] = sum_i rot[hh][i] R_V[c][i]
+#pragma unroll
+  for (int m = 0; m < NR; ++m) {
+    const int cc = cr + m * (NT / 8);
     float acc[GQA];
 #pragma unroll
-    for (int h = 0; h < GQA; ++h) acc[h] = 0.f;
+    for (int hh = 0; hh < GQA; ++hh) acc[hh] = 0.f;
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4)
+    for (int k = 0; k < 4; ++k)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 16 * g + 4 * i4 + e;
+        const int i = 32 * k + 4 * qq + e;
 #pragma unroll
-        for (int h = 0; h < GQA; ++h) acc[h] = fmaf(rot[0][h][i] + rot[1][h][i], r[i4][e], acc[h]);
+        for (int hh = 0; hh < GQA; ++hh) acc[hh] = fmaf(rot[hh][i], rv[4 * m + k][e], acc[hh]);
       }
 #pragma unroll
-    for (int h = 0; h < GQA; ++h) back[g][h][ch] = acc[h];
+    for (int hh = 0; hh < GQA; ++hh) {
+#pragma unroll
+      for (int off = 1; off < 8; off <<= 1) acc[hh] += __shfl_xor(acc[hh], off);
+      if (qq == 0) back[hh][cc] = acc[hh];
+    }
   }
   __syncthreads();
-  for (int idx = tid; idx < GQA * D; idx += MERGE_THREADS) {
-    const int h = idx / D, ch = idx % D;
-    float v = plain[h][ch];
-#pragma unroll
-    for (int g = 0; g < 8; ++g) v += back[g][h][ch];
-    a.out[(int64_t(b) * a.n_q_heads + hk * GQA + h) * D + ch] = v / lsum[h];
-  }
+  if (own) a.out[(int64_t(b) * a.n_q_heads + hk * GQA + h) * D + c] = (raw + back[h][c]) / lsum[h];
 }
 
 template <int GQA, int NG>
@@ -938,7 +1052,8 @@ __global__ void __launch_bounds__(AW * 64) attend_kernel(StepArgs a) {
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const oscar_layer_cache &c = a.c;
-  const int L = a.k_new ? a.len_before[b] + 1 : a.seq_lens[b];
+  const bool append = a.k_new != nullptr;
+  const int L = append ? a.len_before[b] + 1 : a.seq_lens[b];
   // per wave: its page ring, reused for its o[GQA][128] once the pages are done
   constexpr int SB = hist_block_bytes(D / NG);
   constexpr int WREG = DEPTH * SB > GQA * D * 4 ? DEPTH * SB : GQA * D * 4;
@@ -946,15 +1061,36 @@ __global__ void __launch_bounds__(AW * 64) attend_kernel(StepArgs a) {
   __shared__ float ml_lds[2 * AW * GQA];
   __shared__ float zs_lds[AW * GQA * NG];  // per wave: z sums per (head, group)
   __shared__ uint32_t frag_lds[Rows<GQA, NG>::FR_DW * 64];
-  if (!valid_len(L, a.max_seq_len)) return;  // flagged (and out zeroed) by the prologue
+  __shared__ QWork<GQA, NG> qw;
+  if (!valid_len(L, a.max_seq_len)) {
+    // the request is skipped: flag it once, zero its output
+    if (split == 0) {
+      if (tid == 0 && hk == 0) flag_status(c.status, OSCAR_STATUS_BAD_LEN);
+      for (int e = tid; e < GQA * D; e += AW * 64) a.out[(int64_t(b) * a.n_q_heads + hk * GQA) * D + e] = 0.f;
+    }
+    return;
+  }
   const int pages = n_hist_pages(L);
   const int used = 1 + (pages + a.pages_per_split - 1) / a.pages_per_split;
   if (split >= used) return;
+  AppendPlan ap{};
+  if (append) ap = plan_append(a, b);
   float *o_lds = reinterpret_cast<float *>(wave_lds);
   float *m_lds = ml_lds;
   float *l_lds = m_lds + AW * GQA;
   float *o_w = o_lds + wave * (WREG / 4);
   if (split == 0) {
+    // raw BF16 sink + recent pages; an appended token is read from k_new /
+    // v_new (its slot may still hold the token that leaves the window)
+    const uint16_t *kn = append ? a.k_new + (int64_t(b) * c.n_kv_heads + hk) * D : nullptr;
+    const uint16_t *vn = append ? a.v_new + (int64_t(b) * c.n_kv_heads + hk) * D : nullptr;
+    if (append && ap.raw_page < 0 && tid == 0) flag_status(c.status, OSCAR_STATUS_BAD_PAGE);
+    if (append && !ap.evict && ap.raw_page >= 0) {
+      // nothing leaves the window: store the new token in its row now
+      uint16_t *rk_ = c.bf16 + ((int64_t(ap.raw_page) * c.n_kv_heads + hk) * 2) * (PAGE * D) + ap.raw_row * D;
+      if (tid < D) rk_[tid] = kn[tid];
+      else if (tid < 2 * D) rk_[PAGE * D + tid - D] = vn[tid - D];
+    }
     Bf16Wave<GQA> st;
     st.init(a.q + (int64_t(b) * a.n_q_heads + hk * GQA) * D, a.sm_scale, lane);
     for (int pg = wave; pg < BF16_PT; pg += AW) {
@@ -967,18 +1103,34 @@ __global__ void __launch_bounds__(AW * 64) attend_kernel(StepArgs a) {
       }
       const uint16_t *base = c.bf16 + (int64_t(page) * c.n_kv_heads + hk) * 2 * PAGE * D;
       typename Bf16Wave<GQA>::Loads ld;
-      Bf16Wave<GQA>::issue(base, base + PAGE * D, ld, lane);
+      if (append && pg == ap.raw_pg)
+        Bf16Wave<GQA>::issue(base, base + PAGE * D, ld, lane, ap.raw_row, kn, vn);
+      else
+        Bf16Wave<GQA>::issue(base, base + PAGE * D, ld, lane);
       st.compute(ld, valid, lane);
     }
     st.finish(o_w, m_lds + wave * GQA, l_lds + wave * GQA, lane);
   } else {
-    const uint32_t *fr = a.frag + (int64_t(b) * c.n_kv_heads + hk) * FRAG_DW * 64;
-    for (int e = tid; e < Rows<GQA, NG>::FR_DW * 64; e += AW * 64) frag_lds[e] = fr[e];
-    __syncthreads();
     const int j0 = (split - 1) * a.pages_per_split;
     const int j1 = min(pages, j0 + a.pages_per_split);
-    history_wave<GQA, NG>(a, b, hk, L, j0, j1, wave, lane, frag_lds, wave_lds + wave * WREG,
-                          zs_lds + wave * GQA * NG, o_w, m_lds + wave * GQA, l_lds + wave * GQA);
+    // the workgroup holding the last history page also moves the token that
+    // leaves the recent window into history (and its new token into the slot)
+    const bool evict_here = append && ap.evict && ap.evict_j >= j0 && ap.evict_j < j1;
+    uint8_t *evict_blk = nullptr;
+    int patch_i = -1;
+    if (evict_here) {
+      const int pid = c.hist_pt[int64_t(b) * c.hist_pt_stride + ap.evict_j];
+      if (pid >= 0 && pid < c.n_hist_pages && ap.raw_page >= 0)
+        evict_blk = c.hist + (int64_t(pid) * c.n_kv_heads + hk) * SB;
+      else if (tid == 0)
+        flag_status(c.status, OSCAR_STATUS_BAD_PAGE);
+      if (wave == (ap.evict_j - j0) % AW) patch_i = (ap.evict_j - j0) / AW;
+    }
+    auto prep = [&] { build_q<GQA, NG>(a, b, hk, tid, qw, frag_lds, evict_here, ap, evict_blk); };
+    // every wave of the workgroup calls this (it holds workgroup barriers)
+    history_wave<GQA, NG>(a, b, hk, L, j0, j1, wave, lane, prep, frag_lds, wave_lds + wave * WREG,
+                          zs_lds + wave * GQA * NG, o_w, m_lds + wave * GQA, l_lds + wave * GQA,
+                          evict_blk ? patch_i : -1, qw.patch_k, qw.patch_v);
   }
   __syncthreads();
   const int64_t head_stride = int64_t(1 + a.n_splits) * PART_STRIDE;
@@ -989,25 +1141,22 @@ __global__ void __launch_bounds__(AW * 64) attend_kernel(StepArgs a) {
 // ------------------------------------------------------------------ launch
 
 template <int GQA, int NG>
-static hipError_t launch_t(const StepArgs &a, int batch, int hkv, bool attend, hipStream_t s) {
-  hipLaunchKernelGGL((prologue_kernel<GQA, NG>), dim3(hkv, batch), dim3(PRO_THREADS), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !attend) return e;
+static hipError_t launch_t(const StepArgs &a, int batch, int hkv, hipStream_t s) {
   const KernelEvents ev = take_profile_events();
   hipExtLaunchKernelGGL((attend_kernel<GQA, NG>), dim3(1 + a.n_splits, hkv, batch), dim3(AW * 64), 0, s,
                         ev.before, ev.after, 0, a);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((merge_kernel<GQA>), dim3(hkv, batch), dim3(MERGE_THREADS), 0, s, a);
+  hipLaunchKernelGGL((merge_kernel<GQA>), dim3(hkv, batch), dim3(merge_threads<GQA>()), 0, s, a);
   return hipGetLastError();
 }
 
 template <int GQA>
-static hipError_t launch_g(const StepArgs &a, int G, int batch, int hkv, bool attend, hipStream_t s) {
+static hipError_t launch_g(const StepArgs &a, int G, int batch, int hkv, hipStream_t s) {
   switch (G) {
-    case 32: return launch_t<GQA, 4>(a, batch, hkv, attend, s);
-    case 64: return launch_t<GQA, 2>(a, batch, hkv, attend, s);
-    default: return launch_t<GQA, 1>(a, batch, hkv, attend, s);
+    case 32: return launch_t<GQA, 4>(a, batch, hkv, s);
+    case 64: return launch_t<GQA, 2>(a, batch, hkv, s);
+    default: return launch_t<GQA, 1>(a, batch, hkv, s);
   }
 }
 
@@ -1039,10 +1188,6 @@ hipError_t launch_decode_step(const oscar_layer_cache &c, RotArg rk, RotArg rv, 
   a.max_seq_len = max_seq_len;
   a.sm_scale = sm_scale;
   a.out = out;
-  a.frag = nullptr;
-  a.parts = nullptr;
-  a.pages_per_split = AW;
-  a.n_splits = 0;
   a.pv_scale = pv_scale_for(rv.clip);
   a.pv_unscale = 1.f / a.pv_scale;
   a.ex_m4 = 0x03000300u;
@@ -1050,21 +1195,15 @@ hipError_t launch_decode_step(const oscar_layer_cache &c, RotArg rk, RotArg rv, 
   a.ex_e = 0x3C003C00u;
   a.pk01 = std::log2(4.f * a.pv_scale);
   a.pk23 = std::log2(16.f * a.pv_scale);
-  const bool attend = q != nullptr;
-  if (attend) {
-    const SplitPlan p = plan_int2_splits(batch, c.n_kv_heads, max_seq_len);
-    a.pages_per_split = p.pages_per_split;
-    a.n_splits = p.n_splits;
-    uint8_t *w = static_cast<uint8_t *>(ws);
-    a.frag = reinterpret_cast<uint32_t *>(w);
-    a.parts = reinterpret_cast<float *>(w + frag_bytes(batch, c.n_kv_heads));
-  }
-  const int gqa = attend ? n_q_heads / c.n_kv_heads : 1;
-  switch (gqa) {
-    case 1: return launch_g<1>(a, c.group, batch, c.n_kv_heads, attend, s);
-    case 2: return launch_g<2>(a, c.group, batch, c.n_kv_heads, attend, s);
-    case 4: return launch_g<4>(a, c.group, batch, c.n_kv_heads, attend, s);
-    case 8: return launch_g<8>(a, c.group, batch, c.n_kv_heads, attend, s);
+  const SplitPlan p = plan_int2_splits(batch, c.n_kv_heads, max_seq_len);
+  a.pages_per_split = p.pages_per_split;
+  a.n_splits = p.n_splits;
+  a.parts = static_cast<float *>(ws);
+  switch (n_q_heads / c.n_kv_heads) {
+    case 1: return launch_g<1>(a, c.group, batch, c.n_kv_heads, s);
+    case 2: return launch_g<2>(a, c.group, batch, c.n_kv_heads, s);
+    case 4: return launch_g<4>(a, c.group, batch, c.n_kv_heads, s);
+    case 8: return launch_g<8>(a, c.group, batch, c.n_kv_heads, s);
     default: return hipErrorInvalidValue;
   }
 }
