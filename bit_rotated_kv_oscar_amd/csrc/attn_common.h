@@ -39,11 +39,6 @@ __device__ inline float quad_max(float v) {
   return v;
 }
 
-// Wave index within the workgroup as a scalar: the compiler cannot tell that
-// threadIdx.x / 64 is the same in every lane, and a per-lane value would turn
-// loop counters and page bookkeeping into vector registers and exec masks.
-__device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
-
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ------------------------------------------------------------ code expansion

@@ -23,7 +23,8 @@ constexpr size_t FORM_R = 0;                        // fp32 R[i][j]
 constexpr size_t FORM_RT = FORM_R + D * D * 4;      // fp32 RT[j][i] = R[i][j]
 constexpr size_t FORM_RT_HI = FORM_RT + D * D * 4;  // fp16 hi(R[i][j]) at [j][i]
 constexpr size_t FORM_RT_LO = FORM_RT_HI + D * D * 2;  // fp16 2^11 * (R - hi)
-constexpr size_t FORM_BYTES = FORM_RT_LO + D * D * 2;
+constexpr size_t FORM_RT_B = FORM_RT_LO + D * D * 2;   // 3 x bf16 [j][i]: R = b1 + b2 + b3
+constexpr size_t FORM_BYTES = FORM_RT_B + 3 * D * D * 2;
 
 __host__ __device__ constexpr int n_groups(int G) { return D / G; }
 __host__ __device__ constexpr int meta_bytes(int G) { return 64 * (D / G); }
@@ -79,5 +80,10 @@ struct SplitPlan {
 
 SplitPlan plan_int2_splits(int batch, int n_kv_heads, int max_seq_len);
 SplitPlan plan_bf16_splits(int batch, int n_kv_heads, int max_seq_len);
+
+// Wave index within the workgroup as a scalar: the compiler cannot tell that
+// threadIdx.x / 64 is the same in every lane, and a per-lane value would turn
+// loop counters and page bookkeeping into vector registers and exec masks.
+__device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 }  // namespace oscar
