@@ -27,6 +27,87 @@ __device__ inline float row_ror(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, false));
 }
 
+// DPP quad_perm: lane l receives lane (l & ~3) | sel[l & 3] (XOR1: 1,0,3,2;
+// XOR2: 2,3,0,1)
+template <int CTRL>
+__device__ inline float quad_perm(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int QP_XOR1 = 0xB1, QP_XOR2 = 0x4E;
+
+// Sum over the aligned group of 8 lanes; the total is in lanes with
+// (l & 7) >= 4 (others hold a mix of two groups).
+__device__ inline float oct_sum(float v) {
+  v += quad_perm<QP_XOR1>(v);
+  v += quad_perm<QP_XOR2>(v);
+  return v + row_ror<4>(v);
+}
+
+// Every lane of a row of 16 receives the row's sum / max.
+__device__ inline float row_sum(float v) {
+  v += row_ror<8>(v);
+  v += row_ror<4>(v);
+  v += row_ror<2>(v);
+  return v + row_ror<1>(v);
+}
+__device__ inline float row_max(float v) {
+  v = fmaxf(v, row_ror<8>(v));
+  v = fmaxf(v, row_ror<4>(v));
+  v = fmaxf(v, row_ror<2>(v));
+  return fmaxf(v, row_ror<1>(v));
+}
+__device__ inline float lane_value(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+// Whole-wave sum / max, the same in every lane (row reductions by DPP, then
+// four lane reads: no LDS round trips)
+__device__ inline float wave_sum(float v) {
+  v = row_sum(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+__device__ inline float wave_max(float v) {
+  v = row_max(v);
+  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
+}
+__device__ inline float wave_min(float v) {
+  v = fminf(v, row_ror<8>(v));
+  v = fminf(v, row_ror<4>(v));
+  v = fminf(v, row_ror<2>(v));
+  v = fminf(v, row_ror<1>(v));
+  return fminf(fminf(lane_value(v, 0), lane_value(v, 16)), fminf(lane_value(v, 32), lane_value(v, 48)));
+}
+// Min / max over aligned segments of SEG = 32 or 64 lanes, the same in every
+// lane of the segment.
+template <int SEG>
+__device__ inline float seg_min(float v, int lane) {
+  static_assert(SEG == 32 || SEG == 64, "segment of 32 or 64 lanes");
+  v = fminf(v, row_ror<8>(v));
+  v = fminf(v, row_ror<4>(v));
+  v = fminf(v, row_ror<2>(v));
+  v = fminf(v, row_ror<1>(v));
+  const float r01 = fminf(lane_value(v, 0), lane_value(v, 16)), r23 = fminf(lane_value(v, 32), lane_value(v, 48));
+  if constexpr (SEG == 64) return fminf(r01, r23);
+  return lane < 32 ? r01 : r23;
+}
+template <int SEG>
+__device__ inline float seg_max(float v, int lane) {
+  static_assert(SEG == 32 || SEG == 64, "segment of 32 or 64 lanes");
+  v = row_max(v);
+  const float r01 = fmaxf(lane_value(v, 0), lane_value(v, 16)), r23 = fmaxf(lane_value(v, 32), lane_value(v, 48));
+  if constexpr (SEG == 64) return fmaxf(r01, r23);
+  return lane < 32 ? r01 : r23;
+}
+// Sum over aligned segments of SEG = 32 or 64 lanes, the same in every lane
+// of the segment.
+template <int SEG>
+__device__ inline float seg_sum(float v, int lane) {
+  static_assert(SEG == 32 || SEG == 64, "segment of 32 or 64 lanes");
+  v = row_sum(v);
+  const float r01 = lane_value(v, 0) + lane_value(v, 16), r23 = lane_value(v, 32) + lane_value(v, 48);
+  if constexpr (SEG == 64) return r01 + r23;
+  return lane < 32 ? r01 : r23;
+}
+
 __device__ inline float quad_sum(float v) {  // sum over lanes l, l^16, l^32, l^48
   v += __shfl_xor(v, 16);
   v += __shfl_xor(v, 32);
@@ -202,15 +283,23 @@ struct Bf16Wave {
 };
 
 // Combines the NW per-wave states in LDS (o [NW][GQA][128], m, l [NW][GQA])
-// and writes one unnormalised partial (o[128], m, l) per query head.
+// and writes one unnormalised partial (o[128], m, l) per query head.  With
+// xm, one more token joins: value xo[128] (every head), score xm[h] (log2
+// units, finite).
 template <int GQA, int NW>
 __device__ inline void combine_waves(const float *o_lds, const float *m_lds, const float *l_lds,
-                                     float *part0, int64_t head_stride, int tid, int o_wave_stride = GQA * D) {
+                                     float *part0, int64_t head_stride, int tid, int o_wave_stride = GQA * D,
+                                     const float *xo = nullptr, const float *xm = nullptr) {
   for (int idx = tid; idx < GQA * D; idx += NW * 64) {
     const int h = idx / D, c = idx % D;
-    float mst = -INFINITY;
+    float mst = xm ? xm[h] : -INFINITY;
     for (int w = 0; w < NW; ++w) mst = fmaxf(mst, m_lds[w * GQA + h]);
     float o = 0.f, l = 0.f;
+    if (xm) {
+      const float e = fast_exp2(xm[h] - mst);
+      o = e * xo[c];
+      l = e;
+    }
     for (int w = 0; w < NW; ++w) {
       const float mw = m_lds[w * GQA + h];
       const float e = (mw == -INFINITY) ? 0.f : fast_exp2(mw - mst);

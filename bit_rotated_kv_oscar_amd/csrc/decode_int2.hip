@@ -19,17 +19,19 @@
 //   attend (one workgroup of 8 waves per (request, KV head, split)):
 //     split 0 attends over the raw BF16 sink + recent pages (a token being
 //     appended is read from k_new / v_new); splits s >= 1 over history pages
-//     (wave w takes every 8th page of the split; page ids preloaded 64 at a
-//     time; pages copied straight into a per-wave LDS ring DEPTH pages ahead
-//     of the one being computed).  While the first copies fly, each history
+//     (wave w takes every 8th page of the split; its first 64 page ids are
+//     loaded at entry with the other loads that need no request length;
+//     pages are copied straight into a per-wave LDS ring DEPTH pages ahead of
+//     the one being computed).  While the first pages fly, each history
 //     workgroup computes q_rot = q R_K * sm_scale * log2(e) for the query
 //     heads of its group and lays it out as the A operand of the score
 //     MFMAs (fp16 high + low parts, scale groups in separate rows).  On an
-//     append, the workgroup holding the last history page rotates, clips and
-//     quantises the token leaving the recent window (position L-128 when
-//     L >= 144) into history (and patches its own LDS copy of the page),
-//     then stores the new token in that ring slot.  Each workgroup writes an
-//     unnormalised partial (o[128], m, l) per query head.
+//     append whose token at position L-128 leaves the recent window (L >=
+//     144), the raw workgroup rotates, clips and quantises that token into
+//     history, stores the new token in its ring row, and attends the token
+//     itself (dequantised, rotated back); the history workgroups leave its
+//     row out.  Each workgroup writes an unnormalised partial (o[128], m, l)
+//     per query head.
 //   merge (one block per (request, KV head)): LSE-combines the partials,
 //     rotates the history part back with R_V^T, adds the raw part and
 //     normalises (fp32 out).  A kernel boundary, not an in-kernel fence, makes
@@ -143,96 +145,15 @@ __device__ inline bool valid_len(int L, int max_len) { return L >= 1 && L <= max
 
 // ------------------------------------------------------------------ q and append
 
-// Quantise one rotated vector y (128 values in LDS) into row `row` of the K
-// or V area of the history block `blk` (global; may be null), G channels
-// per group, and record the same bytes as a patch for a copy of the block
-// in LDS: entries (byte offset in the block, value, mask), K: 8 code dwords
-// then NG meta dwords; V: 32 code dwords then NG meta dwords.  Threads
-// t < 128 of the caller's half work; the barriers are workgroup-wide, so
-// every thread of the workgroup calls this.
-__device__ inline void store_int2_row(const float *y, float clip, int G, bool is_v, uint8_t *blk, int row,
-                                      uint8_t *codes, float *sz_lds, uint32_t *patch, int t) {
-  const int ng = D / G;
-  if (t < ng) {
-    float lo = fminf(fmaxf(y[t * G], -clip), clip), hi = lo;
-    for (int i = 1; i < G; ++i) {
-      const float v = fminf(fmaxf(y[t * G + i], -clip), clip);
-      lo = fminf(lo, v);
-      hi = fmaxf(hi, v);
-    }
-    sz_lds[2 * t] = __half2float(__float2half_rn((hi - lo) / 3.0f));
-    sz_lds[2 * t + 1] = __half2float(__float2half_rn(lo));
-  }
-  __syncthreads();
-  if (t < D) {
-    const float v = fminf(fmaxf(y[t], -clip), clip);
-    const float s = sz_lds[2 * (t / G)], z = sz_lds[2 * (t / G) + 1];
-    codes[t] = s > 0.f ? uint8_t(min(3, max(0, int(rintf((v - z) / s))))) : uint8_t(0);
-  }
-  __syncthreads();
-  const int area_off = is_v ? v_codes_off(G) : k_codes_off(G);
-  uint32_t *area = blk ? reinterpret_cast<uint32_t *>(blk + area_off) : nullptr;
-  auto put = [&](int e, int dw, uint32_t w, uint32_t mask) {
-    patch[3 * e] = uint32_t(area_off + 4 * dw);
-    patch[3 * e + 1] = w;
-    patch[3 * e + 2] = mask;
-    if (blk) area[dw] = (mask == 0xFFFFFFFFu) ? w : ((area[dw] & ~mask) | w);
-  };
-  if (!is_v) {
-    // the 8 dwords of token `row`: lanes 16q + row, halves d
-    if (t < 8) {
-      const int q = t >> 1, d = t & 1;
-      uint32_t w = 0;
-      for (int u = 0; u < 8; ++u) {
-        const int c0 = 32 * (2 * d + u / 4) + 8 * q + 2 * (u % 4);
-        w |= uint32_t(codes[c0]) << slot_lo(u);
-        w |= uint32_t(codes[c0 + 1]) << slot_hi(u);
-      }
-      put(t, 2 * (16 * q + row) + d, w, 0xFFFFFFFFu);
-    }
-  } else {
-    // token `row` owns 4 codes in each of 32 dwords (lanes 16 (row/4) + m, halves d)
-    if (t < 32) {
-      const int m = t & 15, d = t >> 4, q = row >> 2, jj = (row & 3) >> 1;
-      const int bit_sel = row & 1;
-      uint32_t w = 0, mask = 0;
-      for (int rr = 0; rr < 4; ++rr) {
-        const int u = 2 * rr + jj;
-        const int c = 16 * (4 * d + rr) + m;
-        const int bit = bit_sel ? slot_hi(u) : slot_lo(u);
-        w |= uint32_t(codes[c]) << bit;
-        mask |= 3u << bit;
-      }
-      put(t, 2 * (16 * q + m) + d, w, mask);
-    }
-  }
-  if (t < ng) {
-    const int meta_off = is_v ? v_meta_off(G) : k_meta_off(G);
-    const uint32_t w = uint32_t(__half_as_ushort(__float2half_rn(sz_lds[2 * t]))) |
-                       (uint32_t(__half_as_ushort(__float2half_rn(sz_lds[2 * t + 1]))) << 16);
-    const int e = (is_v ? 32 : 8) + t;
-    patch[3 * e] = uint32_t(meta_off + 4 * (PAGE * t + row));
-    patch[3 * e + 1] = w;
-    patch[3 * e + 2] = 0xFFFFFFFFu;
-    if (blk) *reinterpret_cast<uint32_t *>(blk + meta_off + 4 * (PAGE * t + row)) = w;
-  }
-}
-
-// LDS work area of the q fragment build and of the token that leaves the
-// recent window.
+// LDS work area of the q fragment build.
 template <int GQA, int NG>
 struct QWork {
   static constexpr int SEG = (D / NG) < 64 ? (D / NG) : 64;  // channels per wave-level partial sum
-  float x[GQA + 1][D];  // q heads in, then the evicted k
-  float y[GQA + 1][D];  // rotated
-  float xv[D], yv[D];   // evicted v, rotated
+  float x[GQA][D];  // q heads
+  float y[GQA][D];  // rotated
   _Float16 qa[2][GQA][D];
   float gpart[3][GQA][D / SEG];
   float red[AW];
-  uint8_t codes[2][D];
-  float sz[2][8];
-  uint32_t patch_k[3 * 12];
-  uint32_t patch_v[3 * 36];
 };
 
 // Where the new token of an append goes and which token leaves the window.
@@ -246,10 +167,12 @@ struct AppendPlan {
   int evict_row;   // its row
 };
 
-__device__ inline AppendPlan plan_append(const StepArgs &a, int b) {
+// bpt_lane: entry min(lane, 8) of the request's BF16 page table (loaded by
+// the caller before the length is known)
+__device__ inline AppendPlan plan_append(const StepArgs &a, int len_before, int bpt_lane) {
   AppendPlan p;
   const oscar_layer_cache &c = a.c;
-  p.L0 = a.len_before[b];
+  p.L0 = len_before;
   if (p.L0 < N_SINK) {
     p.raw_pg = 0;
     p.raw_row = p.L0;
@@ -258,7 +181,7 @@ __device__ inline AppendPlan plan_append(const StepArgs &a, int b) {
     p.raw_pg = 1 + slot / PAGE;
     p.raw_row = slot % PAGE;
   }
-  const int page = c.bf16_pt[b * BF16_PT + p.raw_pg];
+  const int page = __builtin_amdgcn_readlane(bpt_lane, p.raw_pg);
   p.raw_page = (page >= 0 && page < c.n_bf16_pages) ? page : -1;
   p.evict = p.L0 >= N_RAW;
   const int h = p.L0 - N_RAW;  // history index of position L0 - 128
@@ -267,105 +190,271 @@ __device__ inline AppendPlan plan_append(const StepArgs &a, int b) {
   return p;
 }
 
-// Workgroup-wide: q' = q R_K (and, when `evict`, the rotation and INT2 row of
-// the token leaving the recent window, written to history and recorded as
-// patches; then the new token takes its ring slot), and the A-operand
+// LDS work area of the token that leaves the recent window.
+struct EvictWork {
+  float x[2][D];      // its K and V (plain basis)
+  float y[2][D];      // rotated
+  float d[2][D];      // dequantised (rotated basis)
+  float u[2][D];      // dequantised, rotated back to the plain basis
+  float mm[2][2][2];  // groups of 128 channels: per vector and wave, min and max
+  float sz[2][8];     // per vector and group: s, z
+  uint8_t codes[2][D];
+  float sc[8];        // its score per query head (log2 units)
+};
+
+// Append, raw workgroup: the token at position L0 - 128 leaves the recent
+// window (OSCAR write path, gist.science technical summaries section 2.2:
+// rotate, clip, quantise per group into the paged INT2 history).  Its K and
+// V are read from their ring row and rotated by R_K / R_V, clipped and
+// quantised (G channels per group), and its row of history block `blk` (null:
+// bad page id) is written: the K codes and the meta are dwords of its own; the
+// V codes share dwords with three other tokens (read-modify-write).  The new
+// token then takes the ring row.  The attention takes this token from here,
+// dequantised and rotated back (e.u; q.k is the same in either basis) with its
+// score per query head (e.sc): the history workgroups leave its row out,
+// since their copy of the page may predate this write.  Workgroup-wide.
+template <int GQA, int G>
+__device__ void evict_token(const StepArgs &a, int b, int hk, int tid, int wave, const AppendPlan &ap, uint8_t *blk,
+                            EvictWork &e) {
+  const oscar_layer_cache &c = a.c;
+  const int hkv = c.n_kv_heads, lane = tid & 63;
+  const int jr = tid >> 3, qq = tid & 7;  // rows jr, jr + 64; inputs 32k + 4qq .. + 3
+  // ---- loads: ring row and new token (threads < 256: K channel tid, V
+  // channel tid - 128), R^T rows of R_K and R_V, the query heads
+  const int v = (tid >> 7) & 1, ch = tid & (D - 1);
+  uint16_t *ring = c.bf16 + ((int64_t(ap.raw_page) * hkv + hk) * 2 + v) * (PAGE * D) + ap.raw_row * D + ch;
+  const uint16_t *nw = (v ? a.v_new : a.k_new) + (int64_t(b) * hkv + hk) * D + ch;
+  uint16_t old_kv = 0, new_kv = 0;
+  if (tid < 2 * D) {
+    old_kv = *ring;
+    new_kv = *nw;
+  }
+  f32x4 rf[2][8];
+#pragma unroll
+  for (int vec = 0; vec < 2; ++vec) {
+    const float *RT = reinterpret_cast<const float *>((vec ? a.fv : a.fk) + FORM_RT) + jr * D + 4 * qq;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) rf[vec][k] = *reinterpret_cast<const f32x4 *>(RT + (k >> 2) * 64 * D + 32 * (k & 3));
+  }
+  float q0 = 0.f, q1 = 0.f;
+  if (wave < GQA) {
+    const uint16_t *qh = a.q + (int64_t(b) * a.n_q_heads + hk * GQA + wave) * D;
+    q0 = bf16_to_f32(qh[lane]);
+    q1 = bf16_to_f32(qh[lane + 64]);
+  }
+  if (tid < 2 * D) {
+    e.x[v][ch] = bf16_to_f32(old_kv);
+    *ring = new_kv;  // the old value is read: the new token takes the row
+  }
+  __syncthreads();
+  // ---- rotate: y[j] = sum_i x[i] R[i][j]; the eight lanes of a row combine
+  // by DPP, the sum lands in lanes qq >= 4
+  {
+    float y0[2] = {0.f, 0.f}, y1[2] = {0.f, 0.f};
+#pragma unroll
+    for (int vec = 0; vec < 2; ++vec)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const f32x4 xi = *reinterpret_cast<const f32x4 *>(&e.x[vec][32 * k + 4 * qq]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          y0[vec] = fmaf(xi[i], rf[vec][k][i], y0[vec]);
+          y1[vec] = fmaf(xi[i], rf[vec][4 + k][i], y1[vec]);
+        }
+      }
+#pragma unroll
+    for (int vec = 0; vec < 2; ++vec) {
+      y0[vec] = oct_sum(y0[vec]);
+      y1[vec] = oct_sum(y1[vec]);
+      if (qq == 4) {
+        e.y[vec][jr] = y0[vec];
+        e.y[vec][jr + 64] = y1[vec];
+      }
+    }
+  }
+  // rows of R_K and R_V for the way back, in flight during the quantisation
+  f32x4 rb[2][8];
+#pragma unroll
+  for (int vec = 0; vec < 2; ++vec) {
+    const float *Rr = reinterpret_cast<const float *>((vec ? a.fv : a.fk) + FORM_R) + jr * D + 4 * qq;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) rb[vec][k] = *reinterpret_cast<const f32x4 *>(Rr + (k >> 2) * 64 * D + 32 * (k & 3));
+  }
+  __syncthreads();
+  // ---- clip and quantise: group min / max over G consecutive channels (all
+  // threads take part; threads >= 256 repeat the work of threads < 256)
+  const float clip = v ? a.clip_v : a.clip_k;
+  const float xc = fminf(fmaxf(e.y[v][ch], -clip), clip);
+  float lo, hi;
+  if constexpr (G == 128) {
+    lo = wave_min(xc);
+    hi = wave_max(xc);
+    if (lane == 0 && tid < 2 * D) {
+      e.mm[v][wave & 1][0] = lo;
+      e.mm[v][wave & 1][1] = hi;
+    }
+    __syncthreads();
+    lo = fminf(e.mm[v][0][0], e.mm[v][1][0]);
+    hi = fmaxf(e.mm[v][0][1], e.mm[v][1][1]);
+  } else {
+    lo = seg_min<G>(xc, lane);
+    hi = seg_max<G>(xc, lane);
+  }
+  const float sq = __half2float(__float2half_rn((hi - lo) / 3.0f));
+  const float zq = __half2float(__float2half_rn(lo));
+  const int code = sq > 0.f ? min(3, max(0, int(rintf((xc - zq) / sq)))) : 0;
+  if (tid < 2 * D) {
+    e.codes[v][ch] = uint8_t(code);
+    e.d[v][ch] = fmaf(sq, float(code), zq);
+    if (ch % G == 0) {
+      e.sz[v][2 * (ch / G)] = sq;
+      e.sz[v][2 * (ch / G) + 1] = zq;
+    }
+  }
+  __syncthreads();
+  // ---- the row in history (layouts of the code dwords: include/oscar.h)
+  if (blk) {
+    const int row = ap.evict_row;
+    if (tid < 8) {
+      // K: the 8 dwords of token `row` (lanes 16q + row, halves d)
+      const int q = tid >> 1, d = tid & 1;
+      uint32_t w = 0;
+      for (int u = 0; u < 8; ++u) {
+        const int c0 = 32 * (2 * d + u / 4) + 8 * q + 2 * (u % 4);
+        w |= uint32_t(e.codes[0][c0]) << slot_lo(u);
+        w |= uint32_t(e.codes[0][c0 + 1]) << slot_hi(u);
+      }
+      *reinterpret_cast<uint32_t *>(blk + k_codes_off(G) + 4 * (2 * (16 * q + row) + d)) = w;
+    } else if (tid >= 64 && tid < 96) {
+      // V: 4 codes of token `row` in each of 32 dwords (lanes 16 (row/4) + m, halves d)
+      const int t = tid - 64, m = t & 15, d = t >> 4, q = row >> 2, jj = (row & 3) >> 1;
+      uint32_t w = 0, mask = 0;
+      for (int rr = 0; rr < 4; ++rr) {
+        const int u = 2 * rr + jj;
+        const int bit = (row & 1) ? slot_hi(u) : slot_lo(u);
+        w |= uint32_t(e.codes[1][16 * (4 * d + rr) + m]) << bit;
+        mask |= 3u << bit;
+      }
+      uint32_t *p = reinterpret_cast<uint32_t *>(blk + v_codes_off(G) + 4 * (2 * (16 * q + m) + d));
+      *p = (*p & ~mask) | w;
+    } else if (tid >= 128 && tid < 128 + 2 * (D / G)) {
+      // meta: (s, z) as fp16 per vector and group
+      const int vec = (tid - 128) / (D / G), g = (tid - 128) % (D / G);
+      const uint32_t w = uint32_t(__half_as_ushort(__float2half_rn(e.sz[vec][2 * g]))) |
+                         (uint32_t(__half_as_ushort(__float2half_rn(e.sz[vec][2 * g + 1]))) << 16);
+      *reinterpret_cast<uint32_t *>(blk + (vec ? v_meta_off(G) : k_meta_off(G)) + 4 * (PAGE * g + row)) = w;
+    }
+  }
+  // ---- back to the plain basis: u[i] = sum_j d[j] R[i][j]
+  {
+    float u0[2] = {0.f, 0.f}, u1[2] = {0.f, 0.f};
+#pragma unroll
+    for (int vec = 0; vec < 2; ++vec)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const f32x4 di = *reinterpret_cast<const f32x4 *>(&e.d[vec][32 * k + 4 * qq]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          u0[vec] = fmaf(di[i], rb[vec][k][i], u0[vec]);
+          u1[vec] = fmaf(di[i], rb[vec][4 + k][i], u1[vec]);
+        }
+      }
+#pragma unroll
+    for (int vec = 0; vec < 2; ++vec) {
+      u0[vec] = oct_sum(u0[vec]);
+      u1[vec] = oct_sum(u1[vec]);
+      if (qq == 4) {
+        e.u[vec][jr] = u0[vec];
+        e.u[vec][jr + 64] = u1[vec];
+      }
+    }
+  }
+  __syncthreads();
+  // ---- its score per query head (wave h < GQA)
+  if (wave < GQA) {
+    const float sc = wave_sum(fmaf(q0, e.u[0][lane], q1 * e.u[0][lane + 64])) * (a.sm_scale * LOG2E);
+    if (lane == 0) e.sc[wave] = sc;
+  }
+  __syncthreads();
+}
+
+// Global loads of the q fragment build, held in registers.  They are
+// issued with the other loads that need no request length, ahead of the
+// first page loads: the compiler waits for a load by counting the memory
+// instructions issued after it, so the build then starts without waiting
+// for any page.
+template <int GQA>
+struct QLoads {
+  static constexpr int NQ = (GQA * D + AW * 64 - 1) / (AW * 64);
+  f32x4 rk[8];     // R^T rows jr and jr + 64 of R_K, inputs 32k + 4qq .. + 3
+  uint16_t q[NQ];  // query elements tid + 512 i of the group
+};
+
+// Every load is issued on every path (`hist` false: every lane re-reads one
+// line of R_K), so the compiler can count exactly how many loads its waits
+// may leave in flight.
+template <int GQA>
+__device__ inline void build_q_issue(const StepArgs &a, int b, int hk, int tid, bool hist, QLoads<GQA> &ql) {
+  constexpr int NT = AW * 64;
+  // eight consecutive lanes read one 128-byte line of a row
+  const int jr = tid >> 3, qq = tid & 7;
+  const float *RT = reinterpret_cast<const float *>(a.fk + FORM_RT) + (hist ? jr * D : 0) + 4 * qq;
+  const int s_hi = hist ? 64 * D : 0, s_k = hist ? 32 : 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) ql.rk[k] = *reinterpret_cast<const f32x4 *>(RT + (k >> 2) * s_hi + s_k * (k & 3));
+  const uint16_t *qg = a.q + (int64_t(b) * a.n_q_heads + hk * GQA) * D;
+#pragma unroll
+  for (int i = 0; i < QLoads<GQA>::NQ; ++i) ql.q[i] = qg[min(tid + NT * i, GQA * D - 1)];
+}
+
+// Workgroup-wide, from the loads above: q' = q R_K and the A-operand
 // fragment block of the score product in frag_lds (layout of Rows).
 template <int GQA, int NG>
-__device__ void build_q(const StepArgs &a, int b, int hk, int tid, QWork<GQA, NG> &w, uint32_t *frag_lds,
-                        bool evict, const AppendPlan &ap, uint8_t *evict_blk) {
+__device__ void build_q(const StepArgs &a, int tid, QWork<GQA, NG> &w, uint32_t *frag_lds, const QLoads<GQA> &ql) {
   using R = Rows<GQA, NG>;
   constexpr int G = R::G, SEG = QWork<GQA, NG>::SEG, NT = AW * 64;
-  const oscar_layer_cache &c = a.c;
-  const int hkv = c.n_kv_heads;
-  // R^T rows jr and jr + 64 (output channels), inputs 32k + 4qq .. + 3 for
-  // k = 0..3: eight consecutive lanes read one 128-byte line of a row
   const int jr = tid >> 3, qq = tid & 7;
-  f32x4 rk[8], rv[8];
-  {
-    const float *RT = reinterpret_cast<const float *>(a.fk + FORM_RT) + jr * D + 4 * qq;
+  const f32x4(&rk)[8] = ql.rk;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) rk[k] = *reinterpret_cast<const f32x4 *>(RT + (k >> 2) * 64 * D + 32 * (k & 3));
-  }
-  if (evict) {
-    const float *RT = reinterpret_cast<const float *>(a.fv + FORM_RT) + jr * D + 4 * qq;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) rv[k] = *reinterpret_cast<const f32x4 *>(RT + (k >> 2) * 64 * D + 32 * (k & 3));
-  }
-  for (int e = tid; e < GQA * D; e += NT)
-    w.x[e / D][e % D] = bf16_to_f32(a.q[(int64_t(b) * a.n_q_heads + hk * GQA) * D + e]);
-  uint16_t *ring_k = nullptr, *ring_v = nullptr;
-  if (evict) {
-    // the ring slot of the new token holds the token that leaves the window
-    if (ap.raw_page >= 0) {
-      ring_k = c.bf16 + ((int64_t(ap.raw_page) * hkv + hk) * 2 + 0) * (PAGE * D) + ap.raw_row * D;
-      ring_v = ring_k + PAGE * D;
-    }
-    if (tid < D) w.x[GQA][tid] = ring_k ? bf16_to_f32(ring_k[tid]) : 0.f;
-    else if (tid < 2 * D) w.xv[tid - D] = ring_k ? bf16_to_f32(ring_v[tid - D]) : 0.f;
+  for (int i = 0; i < QLoads<GQA>::NQ; ++i) {
+    const int e = tid + NT * i;
+    if (e < GQA * D) w.x[e / D][e % D] = bf16_to_f32(ql.q[i]);
   }
   __syncthreads();
-  if (evict && ring_k) {  // the old row is in LDS: the new token takes the slot
-    const uint16_t *kn = a.k_new + (int64_t(b) * hkv + hk) * D, *vn = a.v_new + (int64_t(b) * hkv + hk) * D;
-    if (tid < D) ring_k[tid] = kn[tid];
-    else if (tid < 2 * D) ring_v[tid - D] = vn[tid - D];
-  }
-  // rotations: thread (jr, qq) sums 16 inputs of rows jr and jr + 64, eight
-  // lanes combine; the largest |q'| is tracked on the way
+  // rotations: thread (jr, qq) sums 16 inputs of rows jr and jr + 64, the
+  // eight lanes of a row combine by DPP (the sum lands in lanes qq >= 4);
+  // the largest |q'| is tracked on the way
+  const bool wr = qq == 4;
   float amax = 0.f;
   {
-    const int nv = evict ? GQA + 1 : GQA;
-    for (int v = 0; v <= GQA; ++v) {
-      if (v >= nv) break;
-      float a0 = 0.f, a1 = 0.f;
+    float a0[GQA], a1[GQA];
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
+    for (int v = 0; v < GQA; ++v) {
+      a0[v] = a1[v] = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const f32x4 xi = *reinterpret_cast<const f32x4 *>(&w.x[v][32 * k + 4 * qq]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float xi = w.x[v][32 * k + 4 * qq + e];
-          a0 = fmaf(xi, rk[k][e], a0);
-          a1 = fmaf(xi, rk[4 + k][e], a1);
+          a0[v] = fmaf(xi[e], rk[k][e], a0[v]);
+          a1[v] = fmaf(xi[e], rk[4 + k][e], a1[v]);
         }
-#pragma unroll
-      for (int off = 1; off < 8; off <<= 1) {
-        a0 += __shfl_xor(a0, off);
-        a1 += __shfl_xor(a1, off);
       }
-      if (qq == 0) {
-        w.y[v][jr] = a0;
-        w.y[v][jr + 64] = a1;
-      }
-      if (v < GQA) amax = fmaxf(amax, fmaxf(fabsf(a0), fabsf(a1)));
     }
-    if (evict) {
-      float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float xi = w.xv[32 * k + 4 * qq + e];
-          a0 = fmaf(xi, rv[k][e], a0);
-          a1 = fmaf(xi, rv[4 + k][e], a1);
-        }
-#pragma unroll
-      for (int off = 1; off < 8; off <<= 1) {
-        a0 += __shfl_xor(a0, off);
-        a1 += __shfl_xor(a1, off);
-      }
-      if (qq == 0) {
-        w.yv[jr] = a0;
-        w.yv[jr + 64] = a1;
+    for (int v = 0; v < GQA; ++v) {
+      a0[v] = oct_sum(a0[v]);
+      a1[v] = oct_sum(a1[v]);
+      if (wr) {
+        w.y[v][jr] = a0[v];
+        w.y[v][jr + 64] = a1[v];
+        amax = fmaxf(amax, fmaxf(fabsf(a0[v]), fabsf(a1[v])));
       }
     }
   }
-  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  amax = wave_max(amax);
   if ((tid & 63) == 0) w.red[tid >> 6] = amax;
   __syncthreads();
-  if (evict) {  // uniform over the workgroup (barriers inside)
-    const int half = tid >> 8, t = tid & 255;
-    store_int2_row(half ? w.yv : w.y[GQA], half ? a.clip_v : a.clip_k, G, half == 1, evict_blk, ap.evict_row,
-                   w.codes[half], w.sz[half], half ? w.patch_v : w.patch_k, t);
-  }
   // ---------------- the fragment block
   const float sc = a.sm_scale * LOG2E;
   float gmax = 0.f;
@@ -393,12 +482,9 @@ __device__ void build_q(const StepArgs &a, int b, int hk, int tid, QWork<GQA, NG
       vl = float(lo);
       vq = y * kq;
     }
-#pragma unroll
-    for (int off = 1; off < SEG; off <<= 1) {
-      vh += __shfl_xor(vh, off);
-      vl += __shfl_xor(vl, off);
-      vq += __shfl_xor(vq, off);
-    }
+    vh = seg_sum<SEG>(vh, tid & 63);
+    vl = seg_sum<SEG>(vl, tid & 63);
+    vq = seg_sum<SEG>(vq, tid & 63);
     if (in && ch % SEG == 0) {
       w.gpart[0][h][ch / SEG] = vh;
       w.gpart[1][h][ch / SEG] = vl;
@@ -607,10 +693,9 @@ __device__ inline float gather(const float (&x)[NCH][SPL], int src, int my_ch, i
 // with Vexp = 1 + code/w_t, and cacc[g] += 1 B_g, whose rows all equal the
 // column sums of B_g: acc - cacc is then exactly sum_t B code / w_t.
 template <int GQA, int NG, class Prep>
-__device__ void history_wave(const StepArgs &a, int b, int hk, int L, int j0, int j1, int wave, int lane,
-                             Prep &&prep, const uint32_t *frag_lds, uint8_t *ring, float *zs, float *o_lds,
-                             float *m_lds, float *l_lds, int patch_i, const uint32_t *patch_k,
-                             const uint32_t *patch_v) {
+__device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, int j1, int wave, int lane,
+                             int pid_pre, Prep &&prep, const uint32_t *frag_lds, uint8_t *ring, float *zs,
+                             float *o_lds, float *m_lds, float *l_lds) {
   using R = Rows<GQA, NG>;
   constexpr int NCH = R::NCH, SPL = R::SPL, G = R::G, HC = R::HC;
   constexpr int SB = hist_block_bytes(G);
@@ -621,7 +706,6 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int L, int j0, in
   // PV side: lanes and registers holding head hp's scores for tokens 4qd + i
   const int src_ch = R::head_chain(hp), src_sl = R::head_slot(hp);
   const int src0 = 4 * (16 * R::head_qd(hp) + 4 * qd);
-  const int nh = n_hist_tokens(L);
   const int npw = j1 > j0 + wave ? (j1 - j0 - wave + AW - 1) / AW : 0;
 
   // the q fragment (filled from LDS once the first page copies are issued)
@@ -664,7 +748,8 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int L, int j0, in
 #pragma unroll
   for (int g = 0; g < NG; ++g) cacc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // page ids of pages 64k + lane, loaded per chunk of 64
+  // page ids of pages 64k + lane, loaded per chunk of 64 (the first chunk by
+  // the caller; lanes past the wave's pages hold ids that are never used)
   const int32_t *pt = c.hist_pt + int64_t(b) * c.hist_pt_stride + j0 + wave;
   int my_pid = -1;
 
@@ -672,8 +757,10 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int L, int j0, in
   // page is skipped), so every page costs the same two copy instructions
   uint32_t ok_slots = 0;
   const uint32_t lane16 = 16u * uint32_t(lane);
-  auto issue = [&](int i, int sl) {
-    if ((i & 63) == 0) {
+  constexpr int N2 = (SB - 1024) / 16;  // lanes of the second copy
+  static_assert((N2 & (N2 - 1)) == 0 && N2 <= 64, "second copy part: a power of two of lanes");
+  auto page_block = [&](int i, int sl) {
+    if ((i & 63) == 0 && i > 0) {
       my_pid = (i + lane < npw) ? pt[int64_t(AW) * (i + lane)] : -1;
       // take the wait for this load here, once per 64 pages: otherwise the
       // compiler cannot tell on later pages that it has landed and waits for
@@ -683,11 +770,27 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int L, int j0, in
     int pid = __builtin_amdgcn_readlane(my_pid, i & 63);
     const bool ok = pid >= 0 && pid < c.n_hist_pages;
     pid = ok ? pid : 0;
-    const uint8_t *blk = c.hist + (int64_t(pid) * c.n_kv_heads + hk) * SB;
+    ok_slots = ok ? (ok_slots | (1u << sl)) : (ok_slots & ~(1u << sl));
+    return c.hist + (int64_t(pid) * c.n_kv_heads + hk) * SB;
+  };
+  auto issue = [&](int i, int sl) {
+    const uint8_t *blk = page_block(i, sl);
     uint8_t *dst = ring + sl * SB;
     lds_copy16(blk + lane16, dst);
-    if (lane < (SB - 1024) / 16) lds_copy16(blk + 1024u + lane16, dst + 1024);
-    ok_slots = ok ? (ok_slots | (1u << sl)) : (ok_slots & ~(1u << sl));
+    if (lane < N2) lds_copy16(blk + 1024u + lane16, dst + 1024);
+  };
+  // the first DEPTH - 1 pages go through registers: no copy into LDS is in
+  // flight while the workgroup builds the q fragment (the compiler would
+  // wait for every such copy before the build's first LDS access).  Both
+  // loads are issued in every lane and on every path (lanes past the second
+  // part re-read it; with no pages the rotation forms stand in), so the
+  // compiler's waits count them exactly.
+  typedef const __attribute__((address_space(1))) u32x4 *gp4;
+  u32x4 preg[DEPTH - 1][2];
+  auto issue_reg = [&](int i, bool on) {
+    const uint8_t *blk = on ? page_block(i, i) : a.fk;
+    preg[i][0] = *(gp4)(blk + lane16);
+    preg[i][1] = *(gp4)(blk + 1024u + 16u * uint32_t(lane & (N2 - 1)));
   };
 
   // one page from the ring; PARTIAL: rows >= nvalid are absent (any bits)
@@ -805,16 +908,6 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int L, int j0, in
     if (i + DEPTH - 1 < npw) issue(i + DEPTH - 1, (i + DEPTH - 1) % DEPTH);
     wait_pages(min(DEPTH - 1, npw - 1 - i));
     const int sl = i % DEPTH;
-    if (i == patch_i) {
-      // the row of the token that has just left the recent window: this
-      // workgroup quantised it (and wrote it to history) before the loop
-      constexpr int NK = 8 + NG, NV = 32 + NG;
-      if (lane < NK + NV) {
-        const uint32_t *pe = lane < NK ? patch_k + 3 * lane : patch_v + 3 * (lane - NK);
-        uint32_t *d = reinterpret_cast<uint32_t *>(ring + sl * SB + pe[0]);
-        *d = (*d & ~pe[2]) | pe[1];
-      }
-    }
     // tested as a per-lane value (the same in every lane): as a scalar branch
     // the compiler copies the accumulators at its merge point every page
     uint32_t okv = ok_slots;
@@ -826,12 +919,23 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int L, int j0, in
     }
   };
 
-  // first page copies, then the q fragment (global -> LDS, whole workgroup)
-  // while they fly
+  // the page ids (loaded by the caller, with the loads of the q fragment
+  // build), then the first pages; the build (workgroup-wide: the q fragment
+  // into frag_lds, and the append) runs while the pages fly
   const bool any_pages = npw > 0 && c.n_hist_pages >= 1;
-  if (any_pages)
-    for (int i = 0; i < DEPTH - 1 && i < npw; ++i) issue(i, i);
-  prep();  // workgroup-wide: the q fragment into frag_lds (and the append)
+  my_pid = pid_pre;
+  asm volatile("" : "+v"(my_pid));
+#pragma unroll
+  for (int i = 0; i < DEPTH - 1; ++i) issue_reg(i, any_pages);
+  prep();
+  if (any_pages) {
+#pragma unroll
+    for (int i = 0; i < DEPTH - 1; ++i)
+      if (i < npw) {
+        *reinterpret_cast<u32x4 *>(ring + i * SB + lane16) = preg[i][0];
+        if (lane < N2) *reinterpret_cast<u32x4 *>(ring + i * SB + 1024u + lane16) = preg[i][1];
+      }
+  }
 #pragma unroll
   for (int ch = 0; ch < NCH; ++ch) {
 #pragma unroll
@@ -1053,7 +1157,24 @@ __global__ void __launch_bounds__(AW * 64) attend_kernel(StepArgs a) {
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const oscar_layer_cache &c = a.c;
   const bool append = a.k_new != nullptr;
-  const int L = append ? a.len_before[b] + 1 : a.seq_lens[b];
+  // loads that need no request length, issued together: the length, the
+  // request's BF16 page table, the first 64 page ids of each wave (history
+  // splits) and the loads of the q fragment build
+  const int L0 = append ? a.len_before[b] : a.seq_lens[b];
+  const int bpt_lane = c.bf16_pt[b * BF16_PT + min(lane, BF16_PT - 1)];
+  const int j0 = (split - 1) * a.pages_per_split;
+  int pid_pre;
+  {
+    const int jend = min(c.hist_pt_stride, j0 + a.pages_per_split);
+    const int j = max(0, min(j0 + wave + AW * lane, jend - 1));
+    pid_pre = c.hist_pt[int64_t(b) * c.hist_pt_stride + j];
+  }
+  QLoads<GQA> ql;
+  build_q_issue<GQA>(a, b, hk, tid, split > 0, ql);
+  // keeps these loads ahead of the length checks below (otherwise the
+  // compiler sinks them past the early exits, behind the wait for L0)
+  asm volatile("" ::: "memory");
+  const int L = append ? L0 + 1 : L0;
   // per wave: its page ring, reused for its o[GQA][128] once the pages are done
   constexpr int SB = hist_block_bytes(D / NG);
   constexpr int WREG = DEPTH * SB > GQA * D * 4 ? DEPTH * SB : GQA * D * 4;
@@ -1061,25 +1182,33 @@ __global__ void __launch_bounds__(AW * 64) attend_kernel(StepArgs a) {
   __shared__ float ml_lds[2 * AW * GQA];
   __shared__ float zs_lds[AW * GQA * NG];  // per wave: z sums per (head, group)
   __shared__ uint32_t frag_lds[Rows<GQA, NG>::FR_DW * 64];
-  __shared__ QWork<GQA, NG> qw;
+  __shared__ __attribute__((aligned(16))) union {
+    QWork<GQA, NG> q;  // history workgroups
+    EvictWork e;       // the raw workgroup of an append
+  } work;
   if (!valid_len(L, a.max_seq_len)) {
     // the request is skipped: flag it once, zero its output
     if (split == 0) {
       if (tid == 0 && hk == 0) flag_status(c.status, OSCAR_STATUS_BAD_LEN);
       for (int e = tid; e < GQA * D; e += AW * 64) a.out[(int64_t(b) * a.n_q_heads + hk * GQA) * D + e] = 0.f;
     }
+    __builtin_amdgcn_s_waitcnt(0);  // the loads above land before the wave ends
     return;
   }
   const int pages = n_hist_pages(L);
   const int used = 1 + (pages + a.pages_per_split - 1) / a.pages_per_split;
-  if (split >= used) return;
-  AppendPlan ap{};
-  if (append) ap = plan_append(a, b);
+  if (split >= used) {
+    __builtin_amdgcn_s_waitcnt(0);
+    return;
+  }
   float *o_lds = reinterpret_cast<float *>(wave_lds);
   float *m_lds = ml_lds;
   float *l_lds = m_lds + AW * GQA;
   float *o_w = o_lds + wave * (WREG / 4);
+  bool extra = false;  // the raw workgroup attends the token leaving the window
   if (split == 0) {
+    AppendPlan ap{};
+    if (append) ap = plan_append(a, L0, bpt_lane);
     // raw BF16 sink + recent pages; an appended token is read from k_new /
     // v_new (its slot may still hold the token that leaves the window)
     const uint16_t *kn = append ? a.k_new + (int64_t(b) * c.n_kv_heads + hk) * D : nullptr;
@@ -1110,32 +1239,33 @@ __global__ void __launch_bounds__(AW * 64) attend_kernel(StepArgs a) {
       st.compute(ld, valid, lane);
     }
     st.finish(o_w, m_lds + wave * GQA, l_lds + wave * GQA, lane);
-  } else {
-    const int j0 = (split - 1) * a.pages_per_split;
-    const int j1 = min(pages, j0 + a.pages_per_split);
-    // the workgroup holding the last history page also moves the token that
-    // leaves the recent window into history (and its new token into the slot)
-    const bool evict_here = append && ap.evict && ap.evict_j >= j0 && ap.evict_j < j1;
-    uint8_t *evict_blk = nullptr;
-    int patch_i = -1;
-    if (evict_here) {
+    if (append && ap.evict && ap.raw_page >= 0) {
       const int pid = c.hist_pt[int64_t(b) * c.hist_pt_stride + ap.evict_j];
-      if (pid >= 0 && pid < c.n_hist_pages && ap.raw_page >= 0)
-        evict_blk = c.hist + (int64_t(pid) * c.n_kv_heads + hk) * SB;
+      uint8_t *blk = nullptr;
+      if (pid >= 0 && pid < c.n_hist_pages)
+        blk = c.hist + (int64_t(pid) * c.n_kv_heads + hk) * hist_block_bytes(D / NG);
       else if (tid == 0)
         flag_status(c.status, OSCAR_STATUS_BAD_PAGE);
-      if (wave == (ap.evict_j - j0) % AW) patch_i = (ap.evict_j - j0) / AW;
+      evict_token<GQA, D / NG>(a, b, hk, tid, wave, ap, blk, work.e);
+      extra = true;
     }
-    auto prep = [&] { build_q<GQA, NG>(a, b, hk, tid, qw, frag_lds, evict_here, ap, evict_blk); };
+  } else {
+    // the newest history token has just left the recent window in an
+    // append: the raw workgroup attends it
+    const int nh = n_hist_tokens(L) - (append && L0 >= N_RAW ? 1 : 0);
+    const int j1 = min((nh + PAGE - 1) / PAGE, j0 + a.pages_per_split);
+    auto prep = [&] { build_q<GQA, NG>(a, tid, work.q, frag_lds, ql); };
     // every wave of the workgroup calls this (it holds workgroup barriers)
-    history_wave<GQA, NG>(a, b, hk, L, j0, j1, wave, lane, prep, frag_lds, wave_lds + wave * WREG,
-                          zs_lds + wave * GQA * NG, o_w, m_lds + wave * GQA, l_lds + wave * GQA,
-                          evict_blk ? patch_i : -1, qw.patch_k, qw.patch_v);
+    history_wave<GQA, NG>(a, b, hk, nh, j0, j1, wave, lane, pid_pre, prep, frag_lds, wave_lds + wave * WREG,
+                          zs_lds + wave * GQA * NG, o_w, m_lds + wave * GQA, l_lds + wave * GQA);
   }
   __syncthreads();
   const int64_t head_stride = int64_t(1 + a.n_splits) * PART_STRIDE;
   float *part0 = a.parts + (int64_t(b) * a.n_q_heads + hk * GQA) * head_stride + split * PART_STRIDE;
-  combine_waves<GQA, AW>(o_lds, m_lds, l_lds, part0, head_stride, tid, WREG / 4);
+  if (extra)
+    combine_waves<GQA, AW>(o_lds, m_lds, l_lds, part0, head_stride, tid, WREG / 4, work.e.u[1], work.e.sc);
+  else
+    combine_waves<GQA, AW>(o_lds, m_lds, l_lds, part0, head_stride, tid, WREG / 4);
 }
 
 // ------------------------------------------------------------------ launch
