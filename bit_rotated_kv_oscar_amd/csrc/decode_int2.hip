@@ -1034,14 +1034,17 @@ __device__ inline uint32_t raw_valid_rows(int L, int page) {
 // the raw part (split 0) and normalises.  Built for latency: thread (h, c)
 // issues the loads of all its partial values, the (m, l) pairs and its slice
 // of R_V at once, so the kernel waits on memory about once.
-constexpr int MERGE_CH = 32;  // partials per thread held in registers at a time
+// partials per thread held in registers at a time (1024-thread blocks for
+// GQA 8 have half the registers per thread)
+template <int GQA>
+constexpr int merge_ch() { return GQA >= 8 ? 16 : 32; }
 
 template <int GQA>
 constexpr int merge_threads() { return D * (GQA < 2 ? 2 : GQA); }
 
 template <int GQA>
 __global__ void __launch_bounds__(merge_threads<GQA>()) merge_kernel(StepArgs a) {
-  constexpr int NT = merge_threads<GQA>();
+  constexpr int NT = merge_threads<GQA>(), MCH = merge_ch<GQA>();
   const int hk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int h = tid / D, c = tid % D;  // (query head of the group, channel); h may be >= GQA
   const int L = a.k_new ? a.len_before[b] + 1 : a.seq_lens[b];
@@ -1052,7 +1055,7 @@ __global__ void __launch_bounds__(merge_threads<GQA>()) merge_kernel(StepArgs a)
   __shared__ float w_lds[GQA][MAX_SPLITS + 1];  // m, then the weight of each split
   __shared__ float l_lds[GQA][MAX_SPLITS + 1];
   __shared__ float lsum[GQA];
-  __shared__ float rot[GQA][D];
+  __shared__ __attribute__((aligned(16))) float rot[GQA][D];
   __shared__ float back[GQA][D];
 
   // ---- loads, all issued before any use
@@ -1069,9 +1072,9 @@ __global__ void __launch_bounds__(merge_threads<GQA>()) merge_kernel(StepArgs a)
       rv[4 * m + k] = *reinterpret_cast<const f32x4 *>(Rc + m * (NT / 8) * D + 32 * k);
   const bool own = h < GQA;
   const float *ph = parts0 + (own ? h : 0) * head_stride + c;
-  float ov[MERGE_CH];
+  float ov[MCH];
 #pragma unroll
-  for (int j = 0; j < MERGE_CH; ++j) ov[j] = (own && 1 + j < used) ? ph[(1 + j) * PART_STRIDE] : 0.f;
+  for (int j = 0; j < MCH; ++j) ov[j] = (own && 1 + j < used) ? ph[(1 + j) * PART_STRIDE] : 0.f;
   const float o_raw = own ? ph[0] : 0.f;
   for (int e = tid; e < GQA * used; e += NT) {
     const int hh = e / used, sp = e % used;
@@ -1080,13 +1083,14 @@ __global__ void __launch_bounds__(merge_threads<GQA>()) merge_kernel(StepArgs a)
     l_lds[hh][sp] = pm[1];
   }
   __syncthreads();
-  // ---- per head: max over splits, split weights, total l (wave hh)
+  // ---- per head: max over splits, split weights, total l (wave hh; DPP
+  // reductions)
   {
     const int wave = wave_id(), lane = tid & 63;
     for (int hh = wave; hh < GQA; hh += NT / 64) {
       float m = -INFINITY;
       for (int sp = lane; sp < used; sp += 64) m = fmaxf(m, w_lds[hh][sp]);
-      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      m = wave_max(m);
       float l = 0.f;
       for (int sp = lane; sp < used; sp += 64) {
         const float ms = w_lds[hh][sp];
@@ -1094,7 +1098,7 @@ __global__ void __launch_bounds__(merge_threads<GQA>()) merge_kernel(StepArgs a)
         w_lds[hh][sp] = w;
         l = fmaf(w, l_lds[hh][sp], l);
       }
-      for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
+      l = wave_sum(l);
       if (lane == 0) lsum[hh] = l;
     }
   }
@@ -1104,19 +1108,19 @@ __global__ void __launch_bounds__(merge_threads<GQA>()) merge_kernel(StepArgs a)
   if (own) {
     float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-    for (int j = 0; j < MERGE_CH; ++j) {
+    for (int j = 0; j < MCH; ++j) {
       const float w = (1 + j < used) ? w_lds[h][1 + j] : 0.f;
       if (j & 1)
         acc1 = fmaf(w, ov[j], acc1);
       else
         acc0 = fmaf(w, ov[j], acc0);
     }
-    for (int s0 = 1 + MERGE_CH; s0 < used; s0 += MERGE_CH) {
-      float o2[MERGE_CH];
+    for (int s0 = 1 + MCH; s0 < used; s0 += MCH) {
+      float o2[MCH];
 #pragma unroll
-      for (int j = 0; j < MERGE_CH; ++j) o2[j] = (s0 + j < used) ? ph[(s0 + j) * PART_STRIDE] : 0.f;
+      for (int j = 0; j < MCH; ++j) o2[j] = (s0 + j < used) ? ph[(s0 + j) * PART_STRIDE] : 0.f;
 #pragma unroll
-      for (int j = 0; j < MERGE_CH; ++j) {
+      for (int j = 0; j < MCH; ++j) {
         const float w = (s0 + j < used) ? w_lds[h][s0 + j] : 0.f;
         acc0 = fmaf(w, o2[j], acc0);
       }
@@ -1125,26 +1129,26 @@ __global__ void __launch_bounds__(merge_threads<GQA>()) merge_kernel(StepArgs a)
     raw = w_lds[h][0] * o_raw;
   }
   __syncthreads();
-  // ---- (rot R_V^T)[hh][c] = sum_i rot[hh][i] R_V[c][i]
+  // ---- (rot R_V^T)[hh][c] = sum_i rot[hh][i] R_V[c][i]: the eight lanes of
+  // a row combine by DPP (the sum lands in lanes qq >= 4)
 #pragma unroll
   for (int m = 0; m < NR; ++m) {
     const int cc = cr + m * (NT / 8);
     float acc[GQA];
 #pragma unroll
-    for (int hh = 0; hh < GQA; ++hh) acc[hh] = 0.f;
+    for (int hh = 0; hh < GQA; ++hh) {
+      acc[hh] = 0.f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+      for (int k = 0; k < 4; ++k) {
+        const f32x4 r = *reinterpret_cast<const f32x4 *>(&rot[hh][32 * k + 4 * qq]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 32 * k + 4 * qq + e;
-#pragma unroll
-        for (int hh = 0; hh < GQA; ++hh) acc[hh] = fmaf(rot[hh][i], rv[4 * m + k][e], acc[hh]);
+        for (int e = 0; e < 4; ++e) acc[hh] = fmaf(r[e], rv[4 * m + k][e], acc[hh]);
       }
+    }
 #pragma unroll
     for (int hh = 0; hh < GQA; ++hh) {
-#pragma unroll
-      for (int off = 1; off < 8; off <<= 1) acc[hh] += __shfl_xor(acc[hh], off);
-      if (qq == 0) back[hh][cc] = acc[hh];
+      acc[hh] = oct_sum(acc[hh]);
+      if (qq == 4) back[hh][cc] = acc[hh];
     }
   }
   __syncthreads();
