@@ -1155,8 +1155,14 @@ __global__ void __launch_bounds__(merge_threads<GQA>()) merge_kernel(StepArgs a)
   if (own) a.out[(int64_t(b) * a.n_q_heads + hk * GQA + h) * D + c] = (raw + back[h][c]) / lsum[h];
 }
 
+// Waves per SIMD the register budget is set for: 4 (two workgroups per CU,
+// at most 128 registers) where the page loop fits, else whatever it needs.
 template <int GQA, int NG>
-__global__ void __launch_bounds__(AW * 64) attend_kernel(StepArgs a) {
+constexpr int attend_waves() { return (GQA <= 4 && NG <= 2) ? 4 : 1; }
+
+template <int GQA, int NG>
+__global__ void __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(attend_waves<GQA, NG>())))
+attend_kernel(StepArgs a) {
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const oscar_layer_cache &c = a.c;
