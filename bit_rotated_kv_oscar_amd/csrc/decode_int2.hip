@@ -742,11 +742,7 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
     }
     zw[ch][0] = zw[ch][1] = 0.f;
   }
-  f32x4 acc[8], cacc[NG];
-#pragma unroll
-  for (int r = 0; r < 8; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int g = 0; g < NG; ++g) cacc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[8], cacc[NG];  // zeroed once the prologue is done (register pressure)
 
   // page ids of pages 64k + lane, loaded per chunk of 64 (the first chunk by
   // the caller; lanes past the wave's pages hold ids that are never used)
@@ -781,16 +777,22 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
   };
   // the first DEPTH - 1 pages go through registers: no copy into LDS is in
   // flight while the workgroup builds the q fragment (the compiler would
-  // wait for every such copy before the build's first LDS access).  Both
-  // loads are issued in every lane and on every path (lanes past the second
-  // part re-read it; with no pages the rotation forms stand in), so the
-  // compiler's waits count them exactly.
+  // wait for every such copy before the build's first LDS access).  A page
+  // is 16 bytes per lane, then its last SB - 1024 bytes as one or two dwords
+  // per lane.  Both loads are issued in every lane and on every path (lanes
+  // past the tail re-read it; with no pages the rotation forms stand in), so
+  // the compiler's waits count them exactly.
+  typedef typename std::conditional<(SB - 1024 > 256), u32x2, uint32_t>::type Tail;
+  constexpr int TB = sizeof(Tail), NT2 = (SB - 1024) / TB;  // tail lanes
+  static_assert((NT2 & (NT2 - 1)) == 0 && NT2 <= 64, "tail: a power of two of lanes");
   typedef const __attribute__((address_space(1))) u32x4 *gp4;
-  u32x4 preg[DEPTH - 1][2];
+  typedef const __attribute__((address_space(1))) Tail *gpt;
+  u32x4 preg[DEPTH - 1];
+  Tail ptail[DEPTH - 1];
   auto issue_reg = [&](int i, bool on) {
     const uint8_t *blk = on ? page_block(i, i) : a.fk;
-    preg[i][0] = *(gp4)(blk + lane16);
-    preg[i][1] = *(gp4)(blk + 1024u + 16u * uint32_t(lane & (N2 - 1)));
+    preg[i] = *(gp4)(blk + lane16);
+    ptail[i] = *(gpt)(blk + 1024u + TB * uint32_t(lane & (NT2 - 1)));
   };
 
   // one page from the ring; PARTIAL: rows >= nvalid are absent (any bits)
@@ -932,10 +934,14 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
 #pragma unroll
     for (int i = 0; i < DEPTH - 1; ++i)
       if (i < npw) {
-        *reinterpret_cast<u32x4 *>(ring + i * SB + lane16) = preg[i][0];
-        if (lane < N2) *reinterpret_cast<u32x4 *>(ring + i * SB + 1024u + lane16) = preg[i][1];
+        *reinterpret_cast<u32x4 *>(ring + i * SB + lane16) = preg[i];
+        if (lane < NT2) *reinterpret_cast<Tail *>(ring + i * SB + 1024u + TB * lane) = ptail[i];
       }
   }
+#pragma unroll
+  for (int r = 0; r < 8; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int g = 0; g < NG; ++g) cacc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ch = 0; ch < NCH; ++ch) {
 #pragma unroll
