@@ -573,64 +573,40 @@ __device__ inline uint32_t lds_addr(const void *p) {
 // One page's operands out of its ring slot.  Plain ds_read instructions in
 // one asm block that also waits for them: loads the compiler sees would each
 // get a wait for every LDS copy in flight, the prefetched pages included.
-// kc/vc: K/V code dwords of the lane; km/vm: K/V meta of (token, pair 0/1);
-// sv: V meta of tokens 4 qd .. 4 qd + 3 for each group (NG <= 4).
+// kc/vc: K/V code dwords of the lane; km/vm: K/V meta of (token, pair 0/1).
 template <int VCODE, int KMETA, int VMETA, int POFF>
 struct RingRead {
   u32x2 kc, vc;
   uint32_t km0, km1, vm0, vm1;
-  u32x4 sv0, sv1, sv2, sv3;
   template <int NG>
-  __device__ void load(uint32_t a_code, uint32_t a_meta, uint32_t a_tok) {
+  __device__ void load(uint32_t a_code, uint32_t a_meta) {
     if constexpr (NG == 1) {
       asm volatile(
-          "ds_read_b64 %0, %6\n\t"
-          "ds_read_b64 %1, %6 offset:%9\n\t"
-          "ds_read_b32 %2, %7 offset:%10\n\t"
-          "ds_read_b32 %3, %7 offset:%11\n\t"
-          "ds_read_b128 %4, %8 offset:%11\n\t"
+          "ds_read_b64 %0, %4\n\t"
+          "ds_read_b64 %1, %4 offset:%6\n\t"
+          "ds_read_b32 %2, %5 offset:%7\n\t"
+          "ds_read_b32 %3, %5 offset:%8\n\t"
           "s_waitcnt lgkmcnt(0)"
-          : "=&v"(kc), "=&v"(vc), "=&v"(km0), "=&v"(vm0), "=&v"(sv0), "=&v"(sv1)
-          : "v"(a_code), "v"(a_meta), "v"(a_tok), "n"(VCODE), "n"(KMETA), "n"(VMETA)
+          : "=&v"(kc), "=&v"(vc), "=&v"(km0), "=&v"(vm0)
+          : "v"(a_code), "v"(a_meta), "n"(VCODE), "n"(KMETA), "n"(VMETA)
           : "memory");
       km1 = km0;
       vm1 = vm0;
-    } else if constexpr (NG == 2) {
-      asm volatile(
-          "ds_read_b64 %0, %8\n\t"
-          "ds_read_b64 %1, %8 offset:%11\n\t"
-          "ds_read_b32 %2, %9 offset:%12\n\t"
-          "ds_read_b32 %3, %9 offset:%13\n\t"
-          "ds_read_b32 %4, %9 offset:%14\n\t"
-          "ds_read_b32 %5, %9 offset:%15\n\t"
-          "ds_read_b128 %6, %10 offset:%14\n\t"
-          "ds_read_b128 %7, %10 offset:%16\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(kc), "=&v"(vc), "=&v"(km0), "=&v"(km1), "=&v"(vm0), "=&v"(vm1), "=&v"(sv0), "=&v"(sv1)
-          : "v"(a_code), "v"(a_meta), "v"(a_tok), "n"(VCODE), "n"(KMETA), "n"(KMETA + POFF), "n"(VMETA),
-            "n"(VMETA + POFF), "n"(VMETA + 64)
-          : "memory");
     } else {
       asm volatile(
-          "ds_read_b64 %0, %10\n\t"
-          "ds_read_b64 %1, %10 offset:%13\n\t"
-          "ds_read_b32 %2, %11 offset:%14\n\t"
-          "ds_read_b32 %3, %11 offset:%15\n\t"
-          "ds_read_b32 %4, %11 offset:%16\n\t"
-          "ds_read_b32 %5, %11 offset:%17\n\t"
-          "ds_read_b128 %6, %12 offset:%16\n\t"
-          "ds_read_b128 %7, %12 offset:%18\n\t"
-          "ds_read_b128 %8, %12 offset:%19\n\t"
-          "ds_read_b128 %9, %12 offset:%20\n\t"
+          "ds_read_b64 %0, %6\n\t"
+          "ds_read_b64 %1, %6 offset:%8\n\t"
+          "ds_read_b32 %2, %7 offset:%9\n\t"
+          "ds_read_b32 %3, %7 offset:%10\n\t"
+          "ds_read_b32 %4, %7 offset:%11\n\t"
+          "ds_read_b32 %5, %7 offset:%12\n\t"
           "s_waitcnt lgkmcnt(0)"
-          : "=&v"(kc), "=&v"(vc), "=&v"(km0), "=&v"(km1), "=&v"(vm0), "=&v"(vm1), "=&v"(sv0), "=&v"(sv1),
-            "=&v"(sv2), "=&v"(sv3)
-          : "v"(a_code), "v"(a_meta), "v"(a_tok), "n"(VCODE), "n"(KMETA), "n"(KMETA + POFF), "n"(VMETA),
-            "n"(VMETA + POFF), "n"(VMETA + 64), "n"(VMETA + 128), "n"(VMETA + 192)
+          : "=&v"(kc), "=&v"(vc), "=&v"(km0), "=&v"(km1), "=&v"(vm0), "=&v"(vm1)
+          : "v"(a_code), "v"(a_meta), "n"(VCODE), "n"(KMETA), "n"(KMETA + POFF), "n"(VMETA),
+            "n"(VMETA + POFF)
           : "memory");
     }
   }
-  __device__ u32x4 sv(int g) const { return g == 0 ? sv0 : g == 1 ? sv1 : g == 2 ? sv2 : sv3; }
 };
 
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
@@ -677,6 +653,22 @@ __device__ inline float gather(const float (&x)[NCH][SPL], int src, int my_ch, i
     }
   return v;
 }
+
+// x[ch] of lane src (a byte address, 4 * lane), ch being this lane's chain.
+template <int NCH>
+__device__ inline uint32_t gather_u32(const uint32_t (&x)[NCH], int src, int my_ch) {
+  uint32_t v = 0;
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+    const uint32_t y = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(x[ch])));
+    v = (NCH == 1 || ch == my_ch) ? y : v;
+  }
+  return v;
+}
+
+// Halves of two dwords: (lo(a), lo(b)) or (hi(a), hi(b)) as one dword
+constexpr uint32_t PERM_LO = 0x05040100u, PERM_HI = 0x07060302u;
+__device__ inline uint32_t halves(uint32_t a, uint32_t b, uint32_t sel) { return __builtin_amdgcn_perm(b, a, sel); }
 
 // One wave over its history pages j = j0 + wave + AW*i, i < npw.
 //
@@ -800,7 +792,7 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
     constexpr bool PARTIAL = decltype(partial_tag)::value;
     const uint32_t base = lds_addr(src);
     RingRead<vcode, kmeta, vmeta, POFF> rd;
-    rd.template load<NG>(base + 8 * lane, base + moff, base + 16 * qd);
+    rd.template load<NG>(base + 8 * lane, base + moff);
     const u32x2 kc = rd.kc, vc = rd.vc;
     const h2v km0 = as_h2(rd.km0), km1 = as_h2(rd.km1);
     const h2v vm0 = as_h2(rd.vm0), vm1 = as_h2(rd.vm1);
@@ -885,19 +877,47 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
       zw[ch][0] = fmaf(pw[ch][R::pair_slot(0)], z0, zw[ch][0]);
       zw[ch][1] = fmaf(pw[ch][R::pair_slot(1)], z1, zw[ch][1]);
     }
-    // ---- PV operands: lane (n, tq) = head hp, tokens 4tq..4tq+3
-    float p4[4];
+    // ---- PV operands, formed where the probabilities are: fp16(pw s_tg) of
+    // the lane's two scale groups (NG >= 2: pair 0, pair 1) or of its two
+    // heads (NG = 1) in one dword
+    uint32_t ps[NCH];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p4[i] = gather(pw, src0 + 4 * i, src_ch, src_sl);
+    for (int ch = 0; ch < NCH; ++ch) {
+      float x0, x1;
+      if constexpr (NG == 1) {
+        const float sv = float(vm0.x);
+        x0 = pw[ch][0] * sv;
+        x1 = pw[ch][1] * sv;
+      } else {
+        x0 = pw[ch][0] * float(vm0.x);
+        x1 = pw[ch][0] * float(vm1.x);
+      }
+      if constexpr (PARTIAL) {  // absent rows: their meta may be anything
+        x0 = tok_ok ? x0 : 0.f;
+        x1 = tok_ok ? x1 : 0.f;
+      }
+      const h2v hv = {_Float16(x0), _Float16(x1)};
+      ps[ch] = __builtin_bit_cast(uint32_t, hv);
+    }
+    // lane (n, tq) = head hp, tokens 4tq..4tq+3: B_g from the dwords of its
+    // head's lanes (NG = 4: groups 0, 1 in the first lane group, 2, 3 in the
+    // next)
     f16x4 bp[NG];
+    {
+      constexpr int ND = NG == 4 ? 8 : 4;
+      uint32_t dw[ND];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const u32x4 sv = rd.sv(g);  // V meta of tokens 4 qd .. 4 qd + 3, group g
+      for (int i = 0; i < ND; ++i) dw[i] = gather_u32<NCH>(ps, src0 + 4 * (i & 3) + 64 * (i >> 2), src_ch);
+      if constexpr (NG == 1) {
+        const uint32_t sel = src_sl ? PERM_HI : PERM_LO;
+        bp[0] = __builtin_bit_cast(f16x4, u32x2{halves(dw[0], dw[1], sel), halves(dw[2], dw[3], sel)});
+      } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x = p4[i] * float(as_h2(sv[i]).x);
-        if constexpr (PARTIAL) x = (4 * qd + i < nvalid) ? x : 0.f;
-        bp[g][i] = _Float16(x);
+        for (int gp = 0; gp < NG / 2; ++gp) {
+          const uint32_t *d = dw + 4 * gp;
+          bp[2 * gp] = __builtin_bit_cast(f16x4, u32x2{halves(d[0], d[1], PERM_LO), halves(d[2], d[3], PERM_LO)});
+          bp[2 * gp + 1] = __builtin_bit_cast(f16x4, u32x2{halves(d[0], d[1], PERM_HI), halves(d[2], d[3], PERM_HI)});
+        }
       }
     }
 #pragma unroll
@@ -930,13 +950,13 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
 #pragma unroll
   for (int i = 0; i < DEPTH - 1; ++i) issue_reg(i, any_pages);
   prep();
-  if (any_pages) {
+  // stored on every path, used or not: a load still in flight into a
+  // register at the loop entry would make the compiler wait for every load
+  // in flight (the prefetched pages) wherever the loop reuses that register
 #pragma unroll
-    for (int i = 0; i < DEPTH - 1; ++i)
-      if (i < npw) {
-        *reinterpret_cast<u32x4 *>(ring + i * SB + lane16) = preg[i];
-        if (lane < NT2) *reinterpret_cast<Tail *>(ring + i * SB + 1024u + TB * lane) = ptail[i];
-      }
+  for (int i = 0; i < DEPTH - 1; ++i) {
+    *reinterpret_cast<u32x4 *>(ring + i * SB + lane16) = preg[i];
+    if (lane < NT2) *reinterpret_cast<Tail *>(ring + i * SB + 1024u + TB * lane) = ptail[i];
   }
 #pragma unroll
   for (int r = 0; r < 8; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
