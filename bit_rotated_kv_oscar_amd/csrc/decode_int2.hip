@@ -941,6 +941,21 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
     }
   };
 
+  // the common case: every page id of the wave in its first chunk and in
+  // range (checked once), so no per-page checks or bookkeeping
+  auto issue_fast = [&](int i, int sl) {
+    const int pid = __builtin_amdgcn_readlane(my_pid, i);
+    const uint8_t *blk = c.hist + (int64_t(pid) * c.n_kv_heads + hk) * SB;
+    uint8_t *dst = ring + sl * SB;
+    lds_copy16(blk + lane16, dst);
+    if (lane < N2) lds_copy16(blk + 1024u + lane16, dst + 1024);
+  };
+  auto step_fast = [&](int i, auto partial_tag) {
+    if (i + DEPTH - 1 < npw) issue_fast(i + DEPTH - 1, (i + DEPTH - 1) % DEPTH);
+    wait_pages(min(DEPTH - 1, npw - 1 - i));
+    page(ring + (i % DEPTH) * SB, nh - PAGE * (j0 + wave + AW * i), partial_tag);
+  };
+
   // the page ids (loaded by the caller, with the loads of the q fragment
   // build), then the first pages; the build (workgroup-wide: the q fragment
   // into frag_lds, and the append) runs while the pages fly
@@ -984,8 +999,14 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
     // last page of whichever wave holds it
     const bool last_partial = (nh % PAGE) != 0 && j0 + wave + AW * (npw - 1) == (nh - 1) / PAGE;
     const int nfull = npw - (last_partial ? 1 : 0);
-    for (int i = 0; i < nfull; ++i) step(i, std::false_type{});
-    if (last_partial) step(npw - 1, std::true_type{});
+    const bool fast = npw <= 64 && __ballot(lane < npw && !(my_pid >= 0 && my_pid < c.n_hist_pages)) == 0;
+    if (fast) {
+      for (int i = 0; i < nfull; ++i) step_fast(i, std::false_type{});
+      if (last_partial) step_fast(npw - 1, std::true_type{});
+    } else {
+      for (int i = 0; i < nfull; ++i) step(i, std::false_type{});
+      if (last_partial) step(npw - 1, std::true_type{});
+    }
   }
 
   // ---- this wave's o[h][c], m[h], l[h] into LDS
