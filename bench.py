@@ -14,6 +14,12 @@ and replayed; sequence lengths advance on the device each replay.
 `--workload bs64` runs the batch-64 configuration (per-request lengths
 uniform in [8192, 32768], pages of all requests interleaved in one pool).
 
+`--workload write` runs the fused write path at prefill (Qwen3-4B-shaped,
+36 layers, 32 q / 8 KV heads, G = 32): one step writes 8 prompts x 32768 new
+tokens into every layer's cache (rotate, clip, INT2-pack, page-store; sink and
+recent kept bf16); then 64 decode steps with write-on-append of each new
+token are timed as well.  Its line names its own metric (write GB/s).
+
 Printed: one JSON line (metric, value in GB/s of algorithmic bytes per step,
 tokens/s, the in-run BF16 paged-decode comparison, the roofline of the
 dominant kernel and the CPU oracle baseline).
@@ -41,7 +47,7 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", choices=["bs1", "bs64"], default="bs1")
+    p.add_argument("--workload", choices=["bs1", "bs64", "write"], default="bs1")
     p.add_argument("--layers", type=int, default=None, help="override the layer count (testing only)")
     p.add_argument("--seed", type=int, default=1)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -56,7 +62,10 @@ WORKLOADS = {
                 layers=36, hq=32, hkv=8, G=64, batch=1, len_lo=32768, len_hi=32768),
     "bs64": dict(name="qwen3-8b-shaped attention decode, 36 layers, batch 64, contexts U[8192, 32768], G 64",
                  layers=36, hq=32, hkv=8, G=64, batch=64, len_lo=8192, len_hi=32768),
+    "write": dict(name="qwen3-4b-shaped fused KV write at prefill, 36 layers, 8 prompts x 32768 tokens, G 32",
+                  layers=36, hq=32, hkv=8, G=32, batch=8, len_lo=32768, len_hi=32768),
 }
+WRITE_METRIC = "INT2 fused KV write GB/s (% HBM peak) + tokens/s, prefill 8 x 32K, 36 layers"
 
 
 def n_hist_tokens(L):
@@ -99,6 +108,19 @@ def append_bytes(batch, hkv, G):
     return batch * hkv * 2 * (256 + per_tok_int2 + 256 + 256) + 2 * 128 * 128 * 4
 
 
+def write_bytes(lens, hkv, G):
+    """Algorithmic bytes of one prefill write call: every new token's K and V
+    read once (bf16), history tokens written as INT2 codes + fp16 meta, sink /
+    recent tokens written raw; and of its history kernel alone."""
+    per_tok_int2 = 32 + 4 * (128 // G)
+    hist = raw = 0
+    for L in lens:
+        nh = n_hist_tokens(L)
+        hist += nh * hkv * 2 * (256 + per_tok_int2)
+        raw += min(L, 144) * hkv * 2 * (256 + 256)
+    return hist + raw, hist
+
+
 def bf16_bytes(lens, hq, hkv):
     b = 0
     for L in lens:
@@ -136,6 +158,9 @@ def main():
     W = dict(WORKLOADS[args.workload])
     if args.layers:
         W["layers"] = args.layers
+    if args.workload == "write":
+        write_main(args, W, dev)
+        return
     nl, hq, hkv, G, B = W["layers"], W["hq"], W["hkv"], W["G"], W["batch"]
     steps, warm = args.steps, args.warmup
     headroom = steps + warm + 1
@@ -354,6 +379,178 @@ def main():
     if bf16:
         line.update(bf16)
     print(json.dumps(line))
+
+
+def write_main(args, W, dev):
+    """The write workload: 36 layers' prefill of 8 x 32768 tokens per step,
+    then 64 append + decode steps (one HIP graph per step)."""
+    import numpy as np
+    import torch
+
+    import bit_rotated_kv_oscar_amd as oscar
+    import synth
+
+    nl, hq, hkv, G, B = W["layers"], W["hq"], W["hkv"], W["G"], W["batch"]
+    L = int(W["len_hi"])
+    steps, warm = args.steps, args.warmup
+    n_dec = 64
+    lens = np.full(B, L, dtype=np.int32)
+    t_setup = time.time()
+    # the prompts (shared by every layer: inputs resident in HBM)
+    ld0 = synth.LayerData(args.seed, 0, hq, hkv)
+    k = synth.kv_device(synth.device_generator(args.seed, 0, synth.S_CACHE_K), B * L, ld0.outliers, dev)
+    v = synth.kv_device(synth.device_generator(args.seed, 0, synth.S_CACHE_V), B * L, ld0.outliers, dev)
+    cu = torch.from_numpy(np.arange(B + 1, dtype=np.int32) * L).to(dev)
+    zeros = torch.zeros(B, dtype=torch.int32, device=dev)
+
+    class Layer:
+        pass
+
+    layers = []
+    final = lens + n_dec + 1
+    for l in range(nl):
+        ly = Layer()
+        ld = synth.LayerData(args.seed, l, hq, hkv)
+        qc = synth.q_device(synth.device_generator(args.seed, l, synth.S_CAL_Q), 2048, hq, ld.lam, dev)
+        kc = synth.kv_device(synth.device_generator(args.seed, l, synth.S_CAL_K), 2048, ld.outliers, dev)
+        vc = synth.kv_device(synth.device_generator(args.seed, l, synth.S_CAL_V), 2048, ld.outliers, dev)
+        R_K, R_V, ck, cv = oscar.calibrate_rotation(qc, kc, vc, 0.999)
+        ly.rk, ly.rv = oscar.Rotation(R_K, ck, dev), oscar.Rotation(R_V, cv, dev)
+        pages = [synth.hist_pages_needed(int(x)) for x in final]
+        hist_pt, n_pool = synth.shuffled_page_tables(args.seed, l, final, n_pool_pages=sum(pages) + 1)
+        ly.cache = oscar.LayerCache(hkv, G, n_pool, 9 * B, torch.from_numpy(hist_pt),
+                                    torch.from_numpy(synth.bf16_page_tables(B, shuffle_seed=args.seed + l)),
+                                    device=dev)
+        ly.k_new = synth.kv_device(synth.device_generator(args.seed, l, synth.S_NEW_K), B, ld.outliers, dev)
+        ly.v_new = synth.kv_device(synth.device_generator(args.seed, l, synth.S_NEW_V), B, ld.outliers, dev)
+        ly.q = synth.q_device(synth.device_generator(args.seed, l, synth.S_DEC_Q), B, hq, ld.lam, dev)
+        ly.out = torch.empty((B, hq, HEAD_DIM), dtype=torch.float32, device=dev)
+        ly.ws = torch.empty(oscar.decode_workspace_bytes(B, hq, hkv, int(final.max())), dtype=torch.uint8,
+                            device=dev)
+        layers.append(ly)
+        del qc, kc, vc
+        if (l + 1) % 6 == 0 or l + 1 == nl:
+            torch.cuda.synchronize()
+            print(f"setup: {l + 1}/{nl} layers calibrated ({time.time() - t_setup:.0f} s)", file=sys.stderr,
+                  flush=True)
+    setup_s = time.time() - t_setup
+
+    def prefill():
+        for ly in layers:
+            oscar.write_kv(ly.cache, ly.rk, ly.rv, k, v, cu, zeros, L)
+
+    stream = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(stream):
+        for _ in range(warm):
+            prefill()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            prefill()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_per_step = e0.elapsed_time(e1) / steps
+        # dominant kernel: the history write kernel of each layer's call
+        pairs = []
+        for ly in layers:
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            a1.record(stream)
+            oscar.profile_events(a0, a1)
+            oscar.write_kv(ly.cache, ly.rk, ly.rv, k, v, cu, zeros, L)
+            pairs.append((a0, a1))
+        torch.cuda.synchronize()
+    for ly in layers:
+        assert int(ly.cache.status.item()) == 0, "write flagged bad data"
+    hist_us = float(np.mean([a.elapsed_time(b) for a, b in pairs])) * 1e3
+    all_b, hist_b = write_bytes(lens.tolist(), hkv, G)
+    gbs = nl * all_b / (ms_per_step * 1e-3) / 1e9
+    achieved = hist_b / (hist_us * 1e-6) / 1e9
+
+    # 64 decode steps, each the write-on-append of one token + INT2 decode
+    lens_before = torch.from_numpy(lens.copy()).to(dev)
+    scale = 1 / math.sqrt(HEAD_DIM)
+    max_len = int(final.max())
+
+    def dstep():
+        for ly in layers:
+            oscar.decode_step(ly.cache, ly.rk, ly.rv, ly.k_new, ly.v_new, lens_before, ly.q, max_len, scale,
+                              out=ly.out, workspace=ly.ws)
+        lens_before.add_(1)
+
+    with torch.cuda.stream(stream):
+        dstep()
+        lens_before.sub_(1)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        dstep()
+    torch.cuda.synchronize()
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record()
+    for _ in range(n_dec):
+        graph.replay()
+    d1.record()
+    torch.cuda.synchronize()
+    dec_ms = d0.elapsed_time(d1) / n_dec
+    for ly in layers:
+        assert int(ly.cache.status.item()) == 0, "decode flagged bad data"
+        assert torch.isfinite(ly.out).all(), "non-finite decode output"
+
+    cpu = None if args.no_cpu_baseline else write_cpu_baseline(args, W, all_b / (B * L))
+    line = {
+        "metric": WRITE_METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": W["name"], "layers": nl, "batch": B, "q_heads": hq, "kv_heads": hkv, "group": G,
+                   "new_tokens_per_prompt": L,
+                   "step": "per layer: oscar_write_kv of every prompt (history rotated on the matrix cores, "
+                           "clipped, INT2-packed; sink and recent raw)"},
+        "tokens_per_s": round(B * L / (ms_per_step * 1e-3), 1),
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": f"oscar::write_hist_kernel<{G}> (rotate, clip, INT2-pack, page-store)",
+                     "avg_launch_us": round(hist_us, 2), "bytes_per_launch": int(hist_b)},
+        "append_decode": {"steps": n_dec, "ms_per_step": round(dec_ms, 4),
+                          "tokens_per_s": round(B / (dec_ms * 1e-3), 1)},
+        "cpu_baseline": cpu,
+        "setup_s": round(setup_s, 1),
+    }
+    print(json.dumps(line))
+
+
+def write_cpu_baseline(args, W, bytes_per_token):
+    """The fp64 oracle's write timed on the host on a bounded sample: one
+    prompt of one layer written in chunks of 1024 tokens for about 15 s;
+    scaled by the algorithmic bytes per token of the whole step."""
+    import numpy as np
+
+    import synth
+    from oracle import oscar_ref as o
+    try:
+        import threadpoolctl
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    hq, hkv, G = W["hq"], W["hkv"], W["G"]
+    L = int(W["len_hi"])
+    ld = synth.LayerData(args.seed + 1000, 0, hq, hkv)
+    k, v = ld.cache_kv(L)
+    R = np.linalg.qr(np.random.default_rng(args.seed).standard_normal((128, 128)))[0]
+    pt, npool = synth.shuffled_page_tables(args.seed, 0, [L])
+    ref = o.LayerCacheRef(hkv, G, npool, 9, pt, synth.bf16_page_tables(1))
+    chunk, done = 1024, 0
+    t0 = time.time()
+    while done + chunk <= L and (done < 2 * chunk or time.time() - t0 < 15.0):
+        ref.write(R, R, 6.0, 6.0, k[done:done + chunk], v[done:done + chunk], [0, chunk], [done])
+        done += chunk
+    tok_s = done / (time.time() - t0)
+    return {"value": round(tok_s * bytes_per_token / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {done} tokens of one {L}-token prompt into one layer (Hkv {hkv}, G {G}), written in "
+                      f"chunks of {chunk}: {tok_s:.0f} tokens/s x the bytes per token of one layer's write"}
 
 
 def cpu_baseline(args, W, final_lens, step_bytes):

@@ -203,7 +203,8 @@ def bf16_paged_decode(q: torch.Tensor, kv_pages: torch.Tensor, pt: torch.Tensor,
 
 def profile_events(before: "torch.cuda.Event | None", after: "torch.cuda.Event | None") -> None:
     """The next decode call on this thread records `before` / `after` around
-    its split-K attention kernel (oscar_profile_events).  Events must have
+    its split-K attention kernel, the next write call around its history
+    write kernel (oscar_profile_events).  Events must have
     been recorded once (torch creates them lazily)."""
     h0 = ctypes.c_void_p(before.cuda_event) if before is not None else ctypes.c_void_p(None)
     h1 = ctypes.c_void_p(after.cuda_event) if after is not None else ctypes.c_void_p(None)

@@ -377,10 +377,11 @@ hipError_t launch_write_kv(const oscar_layer_cache &c, RotArg rk, RotArg rv,
   // history positions entering in one call span at most max_new + 16 rows
   const int tiles = (max_new + PAGE - 1) / PAGE + 2;
   const dim3 grid((tiles + WPP - 1) / WPP, 2 * ((c.n_kv_heads + WHC - 1) / WHC), batch);
+  const KernelEvents ev = take_profile_events();
   switch (c.group) {
-    case 32: hipLaunchKernelGGL(write_hist_kernel<32>, grid, dim3(256), 0, s, a); break;
-    case 64: hipLaunchKernelGGL(write_hist_kernel<64>, grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL(write_hist_kernel<128>, grid, dim3(256), 0, s, a); break;
+    case 32: hipExtLaunchKernelGGL(write_hist_kernel<32>, grid, dim3(256), 0, s, ev.before, ev.after, 0, a); break;
+    case 64: hipExtLaunchKernelGGL(write_hist_kernel<64>, grid, dim3(256), 0, s, ev.before, ev.after, 0, a); break;
+    default: hipExtLaunchKernelGGL(write_hist_kernel<128>, grid, dim3(256), 0, s, ev.before, ev.after, 0, a); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

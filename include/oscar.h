@@ -259,11 +259,11 @@ OSCAR_API int oscar_bf16_paged_decode(const uint16_t *q, const uint16_t *kv_page
                             void *workspace, size_t workspace_bytes,
                             oscar_stream_t stream);
 
-/* Instrumentation for benchmarks: the next decode call on this host thread
- * (oscar_decode_attn, oscar_decode_step or oscar_bf16_paged_decode) launches
- * its split-K attention kernel with hipExtLaunchKernelGGL so that event
- * `before` is recorded when that kernel starts and `after` when it ends,
- * then forgets both.  before, after: hipEvent_t handles created by the
+/* Instrumentation for benchmarks: the next decode or write call on this host
+ * thread (oscar_decode_attn, oscar_decode_step, oscar_bf16_paged_decode:
+ * their split-K attention kernel; oscar_write_kv: its history write kernel)
+ * launches that kernel with hipExtLaunchKernelGGL so that event `before` is
+ * recorded when it starts and `after` when it ends, then forgets both.  before, after: hipEvent_t handles created by the
  * caller, or both NULL to cancel.  Returns OSCAR_EINVAL if exactly one of
  * them is NULL. */
 OSCAR_API int oscar_profile_events(void *before, void *after);
