@@ -28,9 +28,15 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-fvisibility=hidden", "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 
 
+# Per-source extra flags.  The write kernels reduce over clipped, finite
+# values: without the IEEE NaN mode the min / max row reductions fold their
+# DPP lane moves into v_min / v_max (no quieting of each operand).
+EXTRA = {"write.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, "-c", src, "-o", obj] + COMMON
+    cmd = [HIPCC, "-c", src, "-o", obj] + COMMON + EXTRA.get(os.path.basename(src), [])
     if src.endswith(".cpp"):
         cmd = [HIPCC, "-x", "hip", "-c", src, "-o", obj] + COMMON
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -40,51 +40,97 @@ __device__ inline bool request_ok(const WriteArgs &a, int b, int &L0, int &n) {
          int64_t(L0) + n < (int64_t(1) << 30);
 }
 
-constexpr int WHC = 8;  // KV heads per write workgroup
+constexpr int WHC = 4;   // KV heads per write workgroup
+constexpr int WPP = 16;  // history pages per write workgroup (the R pieces stay in registers)
+constexpr int XSTR = WHC * D * 2 + 16;  // LDS bytes per staged token row (all WHC heads; padded)
 
 typedef __bf16 bf16x8w __attribute__((ext_vector_type(8)));
 typedef float f32x4w __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4w __attribute__((ext_vector_type(4)));
-
-// One workgroup (4 waves) per (request, touched history page, K|V, chunk of
-// up to 8 KV heads).  The page's 16 rows that enter history in this call --
-// new tokens, or ring tokens pushed out of the recent window -- are rotated
-// on the matrix cores: Y = X R with X the bf16 rows (exact) and R split into
-// three bf16 pieces (b1 + b2 + b3 = R to 2^-24), each piece accumulated in
-// its own fp32 accumulator and added at the end (small pieces last), so the
-// error stays within the fp32 dot-product bound.  Wave w computes output
-// channels 32w .. 32w+31 (two 16-column tiles) for every head of the chunk;
-// then clip, per-(token, group) fp16 zero = min and scale = (max - min)/3
-// (group min / max by row reductions across the 16 lanes of a tile row,
-// then across the waves of a group), codes, and the packed store in the
-// documented layout (read-modify-write for rows already present).
-constexpr int WPP = 8;  // history pages per write workgroup (the R pieces stay in registers)
+typedef uint32_t u32x2w __attribute__((ext_vector_type(2)));
 
 // value of lane (l - N) mod 16 within each row of 16 lanes (DPP row_ror)
 template <int N>
 __device__ inline float row_rot(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, false));
 }
+__device__ inline float row16_min(float v) {
+  v = fminf(v, row_rot<8>(v));
+  v = fminf(v, row_rot<4>(v));
+  v = fminf(v, row_rot<2>(v));
+  return fminf(v, row_rot<1>(v));
+}
+__device__ inline float row16_max(float v) {
+  v = fmaxf(v, row_rot<8>(v));
+  v = fmaxf(v, row_rot<4>(v));
+  v = fmaxf(v, row_rot<2>(v));
+  return fmaxf(v, row_rot<1>(v));
+}
+
+// One code dword of the documented layout from 16 code bytes (code k in the
+// low two bits of byte k % 4 of w[k / 4]; code k goes to slot k / 2, low
+// half for even k, high half for odd k).  The slot bit offsets fall into
+// four classes by their offset within a byte (0, 2, 4, 6); each class is one
+// byte permutation, shifted into place.
+__device__ inline uint32_t pack16(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+  const uint32_t p0 = __builtin_amdgcn_perm(w0, w3, 0x05000401u);
+  const uint32_t p2 = __builtin_amdgcn_perm(w1, w2, 0x07030602u);
+  const uint32_t p4 = __builtin_amdgcn_perm(w1, w2, 0x05010400u);
+  const uint32_t p6 = __builtin_amdgcn_perm(w0, w3, 0x03070206u);
+  return p0 | (p2 << 2) | (p4 << 4) | (p6 << 6);
+}
 
 template <int G>
 struct WriteShared {
-  const uint16_t *tok_ptr[PAGE];  // row of head h0 (or null: inactive)
-  int tok_stride[PAGE];           // elements between heads
-  int active_s[PAGE];
-  int bad;
-  const uint16_t *any_row;  // a valid row for loads whose result is discarded
-  float pmin[WHC][PAGE][4], pmax[WHC][PAGE][4];
+  uint8_t xs[PAGE * XSTR];               // the page's rows, all heads of the chunk (bf16)
+  uint8_t codes[WHC][PAGE * D];          // K: [token][channel]; V: [channel][token]
+  float pmin[WHC][PAGE][4], pmax[WHC][PAGE][4];  // per wave (groups wider than a wave)
   float sz[WHC][PAGE][D / G][2];
-  uint8_t codes[WHC][PAGE][D];
 };
 
-template <int G>
-__device__ void write_page(const WriteArgs &a, int b, int tensor, int h0, int nh, int L0, int hlo, int hhi,
-                           int pos0, int pid, float clip, const bf16x8w (&rb)[2][4][3], WriteShared<G> &sh,
-                           int tid, int wave, int lane);
+// Where the token at position p (uniform) comes from: the ring (it leaves
+// the recent window now) or the new rows (src: rows of head h0, starting at
+// the request's first new row).  Sets row/stride (elements between heads) or
+// leaves row null (inactive); bad: its ring page id is out of range.
+__device__ inline void token_source(const WriteArgs &a, int b, int tensor, int h0, int L0, int hlo, int hhi, int p,
+                                    const uint16_t *src, const uint16_t *&row, int &stride, bool &bad) {
+  const oscar_layer_cache &c = a.c;
+  const int hkv = c.n_kv_heads;
+  row = nullptr;
+  stride = 0;
+  bad = false;
+  if (p < hlo || p >= hhi) return;
+  if (p >= L0) {
+    row = src + int64_t(p - L0) * hkv * D;
+    stride = D;
+  } else {
+    const int slot = p % N_RECENT;
+    const int bp = c.bf16_pt[b * BF16_PT + 1 + slot / PAGE];
+    if (bp >= 0 && bp < c.n_bf16_pages) {
+      row = c.bf16 + ((int64_t(bp) * hkv + h0) * 2 + tensor) * (PAGE * D) + (slot % PAGE) * D;
+      stride = 2 * PAGE * D;
+    } else {
+      bad = true;
+    }
+  }
+}
 
+// One workgroup (4 waves) per (request, WPP consecutive history pages, K|V,
+// up to WHC KV heads).  Per page: the rows that enter history in this call
+// -- new tokens, or ring tokens pushed out of the recent window -- are staged
+// in LDS for all heads of the chunk (the next page's rows are loaded into
+// registers meanwhile), rotated on the matrix cores: Y = X R with X the bf16
+// rows (exact) and R split into three bf16 pieces (b1 + b2 + b3 = R to
+// 2^-24), each piece accumulated in its own fp32 accumulator and added at
+// the end (small pieces last), so the error stays within the fp32
+// dot-product bound.  Wave w computes output channels 32w .. 32w+31 of every
+// head; then clip, per-(token, group) fp16 zero = min and scale =
+// (max - min)/3 (row reductions across the 16 lanes of a tile row, then
+// across the waves of a group wider than 32), codes, and the packed store in
+// the documented layout.
 template <int G>
 __global__ void __launch_bounds__(256) write_hist_kernel(WriteArgs a) {
+  constexpr int NG = D / G, WPG = G / 32;
   const int b = blockIdx.z;
   const int tensor = blockIdx.y & 1, hc = blockIdx.y >> 1;
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
@@ -99,224 +145,241 @@ __global__ void __launch_bounds__(256) write_hist_kernel(WriteArgs a) {
     if (tid == 0 && blockIdx.x == 0 && blockIdx.y == 0) flag_status(c.status, OSCAR_STATUS_BAD_LEN);
     return;
   }
+  // uniform values loaded through vector loads: scalar from here on, so that
+  // the page loop and its branches are scalar
+  L0 = __builtin_amdgcn_readfirstlane(L0);
+  n = __builtin_amdgcn_readfirstlane(n);
   const int L = L0 + n;
   const int hlo = max(N_SINK, L0 - N_RECENT);  // first position entering history
   const int hhi = L - N_RECENT;                 // one past the last
   if (hhi <= hlo) return;
   const int jfirst = (hlo - N_SINK) / PAGE + blockIdx.x * WPP;
   if (N_SINK + PAGE * jfirst >= hhi) return;
-  __shared__ WriteShared<G> sh;
+  const int jend = min((hhi - N_SINK + PAGE - 1) / PAGE, jfirst + WPP);
+  __shared__ __attribute__((aligned(16))) WriteShared<G> sh;
+  __shared__ int bad_w[4];
+  const float clip = a.clip[tensor];
+  const int r_a = lane & 15, qd = lane >> 4;  // MFMA: token row (A) / column (B, D); k sub-block / row group
+
+  // ---- the next page's rows, into registers: thread piece k covers token
+  // wave + 4k, head (lane / 16), bytes 16 (lane % 16) .. of its row
+  u32x4w xr[4];
+  bool bad_next = false;
+  // the request's new rows of head h0 (a uniform base: scalar address math)
+  const uint16_t *src0 = a.src[tensor] + (int64_t(__builtin_amdgcn_readfirstlane(a.cu_new[b])) * hkv + h0) * D;
+  auto load_page = [&](int j) {
+    const int pos0 = N_SINK + PAGE * j;
+    bool bad = false;
+    const int hh = lane >> 4, c16 = lane & 15;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int p = __builtin_amdgcn_readfirstlane(pos0 + wave + 4 * k);
+      const uint16_t *row;
+      int stride;
+      bool bd;
+      token_source(a, b, tensor, h0, L0, hlo, hhi, p, src0, row, stride, bd);
+      bad |= bd;
+      const bool on = row != nullptr && hh < nh;
+      const uint16_t *src = on ? row + hh * stride + 8 * c16 : src0;
+      const u32x4w v = *reinterpret_cast<const u32x4w *>(src);
+      xr[k] = on ? v : u32x4w{0u, 0u, 0u, 0u};
+    }
+    bad_next = bad;
+  };
+  load_page(jfirst);
+
   // B operands: R pieces for this wave's two column tiles; lane l holds
   // R[i][j] for j = 32 wave + 16 ct + l%16, i = 32 kk + 8 (l/16) .. + 7
   bf16x8w rb[2][4][3];
   {
     const uint16_t *RB = reinterpret_cast<const uint16_t *>(a.forms[tensor] + FORM_RT_B);
-    const int qd = lane >> 4, nn = lane & 15;
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
         for (int pc = 0; pc < 3; ++pc) {
-          const int jj = 32 * wave + 16 * ct + nn, ii = 32 * kk + 8 * qd;
+          const int jj = 32 * wave + 16 * ct + r_a, ii = 32 * kk + 8 * qd;
           const u32x4w u = *reinterpret_cast<const u32x4w *>(RB + pc * D * D + jj * D + ii);
           rb[ct][kk][pc] = __builtin_bit_cast(bf16x8w, u);
         }
   }
-  const float clip = a.clip[tensor];
-  for (int jj = 0; jj < WPP; ++jj) {
-    const int j = jfirst + jj;
+
+  for (int jv = jfirst; jv < jend; ++jv) {
+    const int j = __builtin_amdgcn_readfirstlane(jv);  // uniform (kept scalar)
     const int pos0 = N_SINK + PAGE * j;
-    if (pos0 >= hhi) break;  // uniform
-    if (j >= c.hist_pt_stride) {
-      if (tid == 0) flag_status(c.status, OSCAR_STATUS_BAD_PAGE);
-      break;
+    // ---- stage this page's rows (the previous page is done with the LDS)
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int t = wave + 4 * k, hh = lane >> 4, c16 = lane & 15;
+      *reinterpret_cast<u32x4w *>(sh.xs + t * XSTR + hh * (D * 2) + 16 * c16) = xr[k];
     }
-    const int pid = c.hist_pt[int64_t(b) * c.hist_pt_stride + j];
-    if (pid < 0 || pid >= c.n_hist_pages) {
+    if (lane == 0) bad_w[wave] = __ballot(bad_next) != 0;
+    __syncthreads();
+    const bool page_bad = __builtin_amdgcn_readfirstlane(bad_w[0] | bad_w[1] | bad_w[2] | bad_w[3]) != 0;
+    if (j + 1 < jend) load_page(j + 1);  // in flight during this page
+    bool skip = page_bad;
+    int pid = -1;
+    if (j >= c.hist_pt_stride) {
+      skip = true;
+    } else {
+      pid = __builtin_amdgcn_readfirstlane(c.hist_pt[int64_t(b) * c.hist_pt_stride + j]);
+      if (pid < 0 || pid >= c.n_hist_pages) skip = true;
+    }
+    if (skip) {  // uniform: nothing of this page is written
       if (tid == 0) flag_status(c.status, OSCAR_STATUS_BAD_PAGE);
       continue;
     }
-    write_page<G>(a, b, tensor, h0, nh, L0, hlo, hhi, pos0, pid, clip, rb, sh, tid, wave, lane);
-  }
-}
 
-// One history page of the chunk's heads (all threads of the workgroup).
-template <int G>
-__device__ void write_page(const WriteArgs &a, int b, int tensor, int h0, int nh, int L0, int hlo, int hhi,
-                           int pos0, int pid, float clip, const bf16x8w (&rb)[2][4][3], WriteShared<G> &sh,
-                           int tid, int wave, int lane) {
-  constexpr int NG = D / G, WPG = G / 32;
-  const oscar_layer_cache &c = a.c;
-  const int hkv = c.n_kv_heads;
-  auto &tok_ptr = sh.tok_ptr;
-  auto &tok_stride = sh.tok_stride;
-  auto &active_s = sh.active_s;
-  auto &pmin = sh.pmin;
-  auto &pmax = sh.pmax;
-  auto &sz = sh.sz;
-  auto &codes = sh.codes;
-  __syncthreads();  // the previous page is done with the shared arrays
-  if (tid < PAGE) {
-    const int p = pos0 + tid;
-    const bool act = p >= hlo && p < hhi;
-    const uint16_t *row = nullptr;
-    int stride = 0;
-    int is_bad = 0;
-    if (act) {
-      if (p < L0) {  // leaves the ring now
-        const int slot = p % N_RECENT;
-        const int bp = c.bf16_pt[b * BF16_PT + 1 + slot / PAGE];
-        if (bp >= 0 && bp < c.n_bf16_pages) {
-          row = c.bf16 + ((int64_t(bp) * hkv + h0) * 2 + tensor) * (PAGE * D) + (slot % PAGE) * D;
-          stride = 2 * PAGE * D;
-        } else {
-          is_bad = 1;
-        }
-      } else {
-        const int64_t src_row = a.cu_new[b] + (p - L0);
-        row = a.src[tensor] + (src_row * hkv + h0) * D;
-        stride = D;
-      }
-    }
-    tok_ptr[tid] = row;
-    tok_stride[tid] = stride;
-    active_s[tid] = act;
-    // any bad row makes the whole page bad (flagged, nothing written)
-    const uint64_t any_bad = __ballot(is_bad);
-    const uint64_t on = __ballot(row != nullptr);
-    if (tid == 0) sh.bad = any_bad != 0;
-    if (on && tid == __builtin_ctzll(on)) sh.any_row = row;
-  }
-  __syncthreads();
-  if (sh.bad) {
-    if (tid == 0) flag_status(c.status, OSCAR_STATUS_BAD_PAGE);
-    return;
-  }
-  const int r_a = lane & 15, qd = lane >> 4;  // A operand: row (token), k sub-block
-  const uint16_t *my_row = tok_ptr[r_a];
-  const int my_stride = tok_stride[r_a];
-  const int g = (32 * wave) / G;  // scale group of this wave's channels
-  // rows of head hh (A operand), loaded one head ahead; an inactive row (or
-  // a head past the chunk) reads row 0 of the page's first active token and
-  // is zeroed after the load, so the loads carry no branch.  The pointers
-  // come back from LDS, so they are cast to the global address space: flat
-  // loads would also count against the LDS wait counter.
-  typedef const __attribute__((address_space(1))) u32x4w *gptr;
-  const bool row_on = my_row != nullptr;
-  const uint16_t *safe_row = row_on ? my_row : sh.any_row;
-  auto load_x = [&](int hh, u32x4w (&u)[4]) {
-    const bool on = row_on && hh < nh;
-    const uint16_t *rp = safe_row + (on ? int64_t(hh) * my_stride : 0);
+    // ---- rotate, clip, per-(token, wave) min / max; then scale, zero and
+    // codes (at once when a group is the wave's 32 channels, else after the
+    // waves of each group have combined their partials through LDS)
+    const int g = (32 * wave) / G;
+    auto rotate = [&](int hh, f32x4w (&yc)[2], float (&lo)[4], float (&hi)[4]) {
+      bf16x8w xa[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const u32x4w v = *(gptr)(rp + 32 * kk + 8 * qd);
-      u[kk] = on ? v : u32x4w{0u, 0u, 0u, 0u};
-    }
-  };
-  u32x4w xn[4];
-  load_x(0, xn);
-  for (int hh = 0; hh < nh; ++hh) {
-    bf16x8w xa[4];
+      for (int kk = 0; kk < 4; ++kk)
+        xa[kk] = __builtin_bit_cast(
+            bf16x8w, *reinterpret_cast<const u32x4w *>(sh.xs + r_a * XSTR + hh * (D * 2) + 2 * (32 * kk + 8 * qd)));
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) xa[kk] = __builtin_bit_cast(bf16x8w, xn[kk]);
-    load_x(hh + 1, xn);
-    f32x4w yc[2];  // clipped rotated values: rows 4 qd + i, column 32 wave + 16 ct + l%16
+      for (int ct = 0; ct < 2; ++ct) {
+        // smallest pieces first, one accumulator: twelve fp32 accumulation
+        // steps stay well inside the fp32 dot-product error bound
+        f32x4w acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      f32x4w acc[3];
+        for (int pc = 2; pc >= 0; --pc)
 #pragma unroll
-      for (int pc = 0; pc < 3; ++pc) {
-        acc[pc] = f32x4w{0.f, 0.f, 0.f, 0.f};
+          for (int kk = 0; kk < 4; ++kk)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[kk], rb[ct][kk][pc], acc, 0, 0, 0);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          acc[pc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[kk], rb[ct][kk][pc], acc[pc], 0, 0, 0);
+        for (int i = 0; i < 4; ++i) yc[ct][i] = fminf(fmaxf(acc[i], -clip), clip);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float y = acc[0][i] + (acc[1][i] + acc[2][i]);
-        yc[ct][i] = fminf(fmaxf(y, -clip), clip);
+        lo[i] = row16_min(fminf(yc[0][i], yc[1][i]));
+        hi[i] = row16_max(fmaxf(yc[0][i], yc[1][i]));
+      }
+    };
+    auto quantise = [&](int hh, const f32x4w (&yc)[2], const float (&lo)[4], const float (&hi)[4]) {
+      uint32_t vcode[2] = {0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 4 * qd + i;
+        // (max - min) / 3 by a product with fp32(1/3) and the code step by a
+        // hardware reciprocal: each within two fp32 ulps, far inside the
+        // error bound of the rotated values they come from
+        const float sq = __half2float(__float2half_rn((hi[i] - lo[i]) * (1.0f / 3.0f)));
+        const float zq = __half2float(__float2half_rn(lo[i]));
+        if (r_a == 0 && wave % WPG == 0) {
+          sh.sz[hh][t][g][0] = sq;
+          sh.sz[hh][t][g][1] = zq;
+        }
+        const float inv = sq > 0.f ? __builtin_amdgcn_rcpf(sq) : 0.f;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const uint32_t cd = uint32_t(min(3, max(0, int(rintf((yc[ct][i] - zq) * inv)))));
+          if (tensor == 0)
+            sh.codes[hh][t * D + 32 * wave + 16 * ct + r_a] = uint8_t(cd);
+          else
+            vcode[ct] |= cd << (8 * i);
+        }
+      }
+      if (tensor != 0) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+          *reinterpret_cast<uint32_t *>(&sh.codes[hh][(32 * wave + 16 * ct + r_a) * PAGE + 4 * qd]) = vcode[ct];
+      }
+    };
+    if constexpr (WPG == 1) {
+#pragma unroll
+      for (int hh = 0; hh < WHC; ++hh) {
+        f32x4w yc[2];
+        float lo[4], hi[4];
+        rotate(hh, yc, lo, hi);
+        quantise(hh, yc, lo, hi);
+      }
+    } else {
+      f32x4w yc[WHC][2];
+      float lo[WHC][4], hi[WHC][4];
+#pragma unroll
+      for (int hh = 0; hh < WHC; ++hh) {
+        rotate(hh, yc[hh], lo[hh], hi[hh]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (r_a == 0) {
+            sh.pmin[hh][4 * qd + i][wave] = lo[hh][i];
+            sh.pmax[hh][4 * qd + i][wave] = hi[hh][i];
+          }
+      }
+      __syncthreads();
+      const int w0 = (wave / WPG) * WPG;
+#pragma unroll
+      for (int hh = 0; hh < WHC; ++hh) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float l2 = sh.pmin[hh][4 * qd + i][w0], h2 = sh.pmax[hh][4 * qd + i][w0];
+#pragma unroll
+          for (int w = 1; w < WPG; ++w) {
+            l2 = fminf(l2, sh.pmin[hh][4 * qd + i][w0 + w]);
+            h2 = fmaxf(h2, sh.pmax[hh][4 * qd + i][w0 + w]);
+          }
+          lo[hh][i] = l2;
+          hi[hh][i] = h2;
+        }
+        quantise(hh, yc[hh], lo[hh], hi[hh]);
       }
     }
-    // min / max of each token over this wave's 32 channels (16 lanes of a row)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float lo = fminf(yc[0][i], yc[1][i]), hi = fmaxf(yc[0][i], yc[1][i]);
-      lo = fminf(lo, row_rot<8>(lo));
-      hi = fmaxf(hi, row_rot<8>(hi));
-      lo = fminf(lo, row_rot<4>(lo));
-      hi = fmaxf(hi, row_rot<4>(hi));
-      lo = fminf(lo, row_rot<2>(lo));
-      hi = fmaxf(hi, row_rot<2>(hi));
-      lo = fminf(lo, row_rot<1>(lo));
-      hi = fmaxf(hi, row_rot<1>(hi));
-      if (r_a == 0) {
-        pmin[hh][4 * qd + i][wave] = lo;
-        pmax[hh][4 * qd + i][wave] = hi;
-      }
-    }
-    __syncthreads();  // partials of every wave of the group are in
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 4 * qd + i;
-      float lo = pmin[hh][t][WPG * g], hi = pmax[hh][t][WPG * g];
-      for (int w = 1; w < WPG; ++w) {
-        lo = fminf(lo, pmin[hh][t][WPG * g + w]);
-        hi = fmaxf(hi, pmax[hh][t][WPG * g + w]);
-      }
-      const float s = __half2float(__float2half_rn((hi - lo) / 3.0f));
-      const float z = __half2float(__float2half_rn(lo));
-      if (r_a == 0 && wave == WPG * g) {
-        sz[hh][t][g][0] = s;
-        sz[hh][t][g][1] = z;
-      }
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        int cd = 0;
-        if (s > 0.f) cd = min(3, max(0, int(rintf((yc[ct][i] - z) / s))));
-        codes[hh][t][32 * wave + 16 * ct + r_a] = uint8_t(cd);
-      }
-    }
-  }
-  __syncthreads();
-  // packed store: 128 code dwords per head, then the meta entries
-  for (int e = tid; e < nh * 128; e += 256) {
-    const int hh = e >> 7, w = e & 127;
-    const int ln = w >> 1, d = w & 1, lq = ln >> 4, la = ln & 15;
-    uint32_t word = 0, mask = 0;
-    for (int u = 0; u < 8; ++u) {
-      int t0, t1, c0, c1;
+    __syncthreads();
+
+    // ---- packed store: 128 code dwords per head, then the meta entries.
+    // K dword (token t, q, d): channels 64d + 8q .. +7 and 64d + 32 + 8q ..
+    // +7 of token t; V dword (q, m, d): tokens 4q .. 4q+3 of channels
+    // 16 (4d + r) + m, r < 4.  Rows below hlo are already in history and are
+    // kept (read-modify-write); rows at or past hhi are not yet and may be
+    // overwritten.
+    const int hbb = hist_block_bytes(G);
+    for (int e = tid; e < nh * 128; e += 256) {
+      const int hh = e >> 7, w = e & 127;
+      const int ln = w >> 1, d = w & 1, lq = ln >> 4, la = ln & 15;
+      uint8_t *blk = c.hist + (int64_t(pid) * hkv + h0 + hh) * hbb;
       if (tensor == 0) {
-        t0 = t1 = la;
-        c0 = 32 * (2 * d + u / 4) + 8 * lq + 2 * (u % 4);
-        c1 = c0 + 1;
+        const int t = la, p = pos0 + t;
+        if (p < hlo || p >= hhi) continue;
+        const uint8_t *src = &sh.codes[hh][t * D + 64 * d + 8 * lq];
+        const u32x2w x0 = *reinterpret_cast<const u32x2w *>(src);
+        const u32x2w x1 = *reinterpret_cast<const u32x2w *>(src + 32);
+        reinterpret_cast<uint32_t *>(blk + k_codes_off(G))[w] = pack16(x0[0], x0[1], x1[0], x1[1]);
       } else {
-        c0 = c1 = 16 * (4 * d + u / 2) + la;
-        t0 = 4 * lq + 2 * (u % 2);
-        t1 = t0 + 1;
-      }
-      if (active_s[t0]) {
-        word |= uint32_t(codes[hh][t0][c0]) << slot_lo(u);
-        mask |= 3u << slot_lo(u);
-      }
-      if (active_s[t1]) {
-        word |= uint32_t(codes[hh][t1][c1]) << slot_hi(u);
-        mask |= 3u << slot_hi(u);
+        uint32_t keep = 0, on = 0;  // bytes of kept / written tokens 4lq + byte
+#pragma unroll
+        for (int by = 0; by < 4; ++by) {
+          const int p = pos0 + 4 * lq + by;
+          if (p < hlo) keep |= 0x03u << (8 * by);
+          else if (p < hhi) on |= 0x03u << (8 * by);
+        }
+        if (!on) continue;
+        uint32_t x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          x[r] = *reinterpret_cast<const uint32_t *>(&sh.codes[hh][(16 * (4 * d + r) + la) * PAGE + 4 * lq]) & on;
+        const uint32_t word = pack16(x[0], x[1], x[2], x[3]);
+        uint32_t *dst = reinterpret_cast<uint32_t *>(blk + v_codes_off(G)) + w;
+        if (keep) {
+          const uint32_t km = pack16(keep, keep, keep, keep);
+          *dst = (*dst & km) | word;
+        } else {
+          *dst = word;
+        }
       }
     }
-    uint8_t *blk = c.hist + (int64_t(pid) * hkv + h0 + hh) * hist_block_bytes(G);
-    uint32_t *area = reinterpret_cast<uint32_t *>(blk + (tensor ? v_codes_off(G) : k_codes_off(G)));
-    if (mask == 0xFFFFFFFFu)
-      area[w] = word;
-    else if (mask)
-      area[w] = (area[w] & ~mask) | word;
-  }
-  for (int e = tid; e < nh * PAGE * NG; e += 256) {
-    const int hh = e / (PAGE * NG), t = (e / NG) % PAGE, g = e % NG;
-    if (active_s[t]) {
-      uint8_t *blk = c.hist + (int64_t(pid) * hkv + h0 + hh) * hist_block_bytes(G);
+    for (int e = tid; e < nh * PAGE * NG; e += 256) {
+      const int hh = e / (PAGE * NG), t = (e / NG) % PAGE, gg = e % NG;
+      const int p = pos0 + t;
+      if (p < hlo || p >= hhi) continue;
+      uint8_t *blk = c.hist + (int64_t(pid) * hkv + h0 + hh) * hbb;
       __half2 *meta = reinterpret_cast<__half2 *>(blk + (tensor ? v_meta_off(G) : k_meta_off(G)));
-      meta[PAGE * g + t] = __halves2half2(__float2half_rn(sz[hh][t][g][0]), __float2half_rn(sz[hh][t][g][1]));
+      meta[PAGE * gg + t] = __halves2half2(__float2half_rn(sh.sz[hh][t][gg][0]), __float2half_rn(sh.sz[hh][t][gg][1]));
     }
   }
 }
