@@ -234,14 +234,20 @@ __global__ void __launch_bounds__(256) write_hist_kernel(WriteArgs a) {
 
     // ---- rotate, clip, per-(token, wave) min / max; then scale, zero and
     // codes (at once when a group is the wave's 32 channels, else after the
-    // waves of each group have combined their partials through LDS)
+    // waves of each group have combined their partials through LDS).  The
+    // product is taken transposed, Y^T = R^T X^T (A: rows of R^T, B: the
+    // staged rows), so that lane (n = l%16, qd = l/16) holds token n,
+    // channels 32 wave + 16 ct + 4 qd + i: the per-token work runs once per
+    // lane, and a token's 32 channels of the wave are in the four lanes
+    // n + 16 qd.
     const int g = (32 * wave) / G;
-    auto rotate = [&](int hh, f32x4w (&yc)[2], float (&lo)[4], float (&hi)[4]) {
-      bf16x8w xa[4];
+    const int tok = r_a;
+    auto rotate = [&](int hh, f32x4w (&yc)[2], float &lo, float &hi) {
+      bf16x8w xb[4];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        xa[kk] = __builtin_bit_cast(
-            bf16x8w, *reinterpret_cast<const u32x4w *>(sh.xs + r_a * XSTR + hh * (D * 2) + 2 * (32 * kk + 8 * qd)));
+        xb[kk] = __builtin_bit_cast(
+            bf16x8w, *reinterpret_cast<const u32x4w *>(sh.xs + tok * XSTR + hh * (D * 2) + 2 * (32 * kk + 8 * qd)));
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         // smallest pieces first, one accumulator: twelve fp32 accumulation
@@ -251,83 +257,76 @@ __global__ void __launch_bounds__(256) write_hist_kernel(WriteArgs a) {
         for (int pc = 2; pc >= 0; --pc)
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[kk], rb[ct][kk][pc], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rb[ct][kk][pc], xb[kk], acc, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) yc[ct][i] = fminf(fmaxf(acc[i], -clip), clip);
+        for (int i = 0; i < 4; ++i) yc[ct][i] = __builtin_amdgcn_fmed3f(acc[i], -clip, clip);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lo[i] = row16_min(fminf(yc[0][i], yc[1][i]));
-        hi[i] = row16_max(fmaxf(yc[0][i], yc[1][i]));
-      }
+      lo = fminf(fminf(fminf(yc[0][0], yc[0][1]), fminf(yc[0][2], yc[0][3])),
+                 fminf(fminf(yc[1][0], yc[1][1]), fminf(yc[1][2], yc[1][3])));
+      hi = fmaxf(fmaxf(fmaxf(yc[0][0], yc[0][1]), fmaxf(yc[0][2], yc[0][3])),
+                 fmaxf(fmaxf(yc[1][0], yc[1][1]), fmaxf(yc[1][2], yc[1][3])));
+      lo = fminf(lo, __shfl_xor(lo, 16));
+      hi = fmaxf(hi, __shfl_xor(hi, 16));
+      lo = fminf(lo, __shfl_xor(lo, 32));
+      hi = fmaxf(hi, __shfl_xor(hi, 32));
     };
-    auto quantise = [&](int hh, const f32x4w (&yc)[2], const float (&lo)[4], const float (&hi)[4]) {
-      uint32_t vcode[2] = {0u, 0u};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 4 * qd + i;
-        // (max - min) / 3 by a product with fp32(1/3) and the code step by a
-        // hardware reciprocal: each within two fp32 ulps, far inside the
-        // error bound of the rotated values they come from
-        const float sq = __half2float(__float2half_rn((hi[i] - lo[i]) * (1.0f / 3.0f)));
-        const float zq = __half2float(__float2half_rn(lo[i]));
-        if (r_a == 0 && wave % WPG == 0) {
-          sh.sz[hh][t][g][0] = sq;
-          sh.sz[hh][t][g][1] = zq;
-        }
-        const float inv = sq > 0.f ? __builtin_amdgcn_rcpf(sq) : 0.f;
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          const uint32_t cd = uint32_t(min(3, max(0, int(rintf((yc[ct][i] - zq) * inv)))));
-          if (tensor == 0)
-            sh.codes[hh][t * D + 32 * wave + 16 * ct + r_a] = uint8_t(cd);
-          else
-            vcode[ct] |= cd << (8 * i);
-        }
+    auto quantise = [&](int hh, const f32x4w (&yc)[2], float lo, float hi) {
+      // (max - min) / 3 by a product with fp32(1/3) and the code step by a
+      // hardware reciprocal: each within two fp32 ulps, far inside the error
+      // bound of the rotated values they come from
+      const float sq = __half2float(__float2half_rn((hi - lo) * (1.0f / 3.0f)));
+      const float zq = __half2float(__float2half_rn(lo));
+      if (qd == 0 && wave % WPG == 0) {
+        sh.sz[hh][tok][g][0] = sq;
+        sh.sz[hh][tok][g][1] = zq;
       }
-      if (tensor != 0) {
+      const float inv = sq > 0.f ? __builtin_amdgcn_rcpf(sq) : 0.f;
+      const float zi = zq * inv;
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-          *reinterpret_cast<uint32_t *>(&sh.codes[hh][(32 * wave + 16 * ct + r_a) * PAGE + 4 * qd]) = vcode[ct];
+      for (int ct = 0; ct < 2; ++ct) {
+        uint32_t cd[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          cd[i] = uint32_t(rintf(__builtin_amdgcn_fmed3f(fmaf(yc[ct][i], inv, -zi), 0.f, 3.f)));
+        const int ch = 32 * wave + 16 * ct + 4 * qd;
+        if (tensor == 0) {
+          *reinterpret_cast<uint32_t *>(&sh.codes[hh][tok * D + ch]) = cd[0] | (cd[1] << 8) | (cd[2] << 16) | (cd[3] << 24);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sh.codes[hh][(ch + i) * PAGE + tok] = uint8_t(cd[i]);
+        }
       }
     };
     if constexpr (WPG == 1) {
 #pragma unroll
       for (int hh = 0; hh < WHC; ++hh) {
         f32x4w yc[2];
-        float lo[4], hi[4];
+        float lo, hi;
         rotate(hh, yc, lo, hi);
         quantise(hh, yc, lo, hi);
       }
     } else {
       f32x4w yc[WHC][2];
-      float lo[WHC][4], hi[WHC][4];
+      float lo[WHC], hi[WHC];
 #pragma unroll
       for (int hh = 0; hh < WHC; ++hh) {
         rotate(hh, yc[hh], lo[hh], hi[hh]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (r_a == 0) {
-            sh.pmin[hh][4 * qd + i][wave] = lo[hh][i];
-            sh.pmax[hh][4 * qd + i][wave] = hi[hh][i];
-          }
+        if (qd == 0) {
+          sh.pmin[hh][tok][wave] = lo[hh];
+          sh.pmax[hh][tok][wave] = hi[hh];
+        }
       }
       __syncthreads();
       const int w0 = (wave / WPG) * WPG;
 #pragma unroll
       for (int hh = 0; hh < WHC; ++hh) {
+        float l2 = sh.pmin[hh][tok][w0], h2 = sh.pmax[hh][tok][w0];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float l2 = sh.pmin[hh][4 * qd + i][w0], h2 = sh.pmax[hh][4 * qd + i][w0];
-#pragma unroll
-          for (int w = 1; w < WPG; ++w) {
-            l2 = fminf(l2, sh.pmin[hh][4 * qd + i][w0 + w]);
-            h2 = fmaxf(h2, sh.pmax[hh][4 * qd + i][w0 + w]);
-          }
-          lo[hh][i] = l2;
-          hi[hh][i] = h2;
+        for (int w = 1; w < WPG; ++w) {
+          l2 = fminf(l2, sh.pmin[hh][tok][w0 + w]);
+          h2 = fmaxf(h2, sh.pmax[hh][tok][w0 + w]);
         }
-        quantise(hh, yc[hh], lo[hh], hi[hh]);
+        quantise(hh, yc[hh], l2, h2);
       }
     }
     __syncthreads();
