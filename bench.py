@@ -54,7 +54,81 @@ def parse_args():
     p.add_argument("--no-bf16", action="store_true")
     p.add_argument("--copy-probe-mb", type=int, default=0,
                    help="only run a plain device copy of this many MiB (counter scale reference)")
+    p.add_argument("--traffic-from", nargs=5, metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                       "COPY_WRITE_CSV"),
+                   help="only turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter files of a run of WORKLOAD and "
+                        "of --copy-probe-mb into per-launch HBM bytes of its dominant kernel, stored in "
+                        "profiles/hbm_traffic.json")
     return p.parse_args()
+
+
+# ------------------------------------------------------------ HBM traffic
+# Measured HBM bytes per launch of each workload's dominant kernel, from two
+# rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled
+# by what the same counter reports for a plain device copy of known size.  An
+# entry is used only while the kernel's sources are the ones it was measured
+# on (their SHA-256 is stored with it).
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+DOMINANT = {"bs1": ("attend_kernel", ["decode_int2.hip", "attn_common.h", "common.h", "kernels.h"]),
+            "bs64": ("attend_kernel", ["decode_int2.hip", "attn_common.h", "common.h", "kernels.h"]),
+            "write": ("write_hist_kernel", ["write.hip", "common.h", "kernels.h"])}
+
+
+def kernel_sources_sha(workload):
+    import hashlib
+    h = hashlib.sha256()
+    for f in DOMINANT[workload][1]:
+        with open(os.path.join(ROOT, "bit_rotated_kv_oscar_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the workload's dominant kernel, or None when
+    not measured on the current sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            e = json.load(fh).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not e or e.get("sources_sha256") != kernel_sources_sha(workload):
+        return None
+    return int(e["hbm_bytes_per_launch"])
+
+
+def traffic_from(args):
+    import csv
+
+    workload, f_csv, w_csv, cf_csv, cw_csv = args.traffic_from
+    kname = DOMINANT[workload][0]
+
+    def mean_kib(path, pattern):
+        vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path)) if pattern in r["Kernel_Name"]]
+        return sum(vals) / len(vals), len(vals)
+
+    copy_bytes = 1024 * (1 << 20)
+    fc, _ = mean_kib(cf_csv, "copyBuffer")
+    wc, _ = mean_kib(cw_csv, "copyBuffer")
+    fetch_scale, write_scale = copy_bytes / (fc * 1024), copy_bytes / (wc * 1024)
+    fk, nf = mean_kib(f_csv, kname)
+    wk, nw = mean_kib(w_csv, kname)
+    fetch_b, write_b = fk * 1024 * fetch_scale, wk * 1024 * write_scale
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        data = {}
+    data[workload] = {"kernel": kname, "sources_sha256": kernel_sources_sha(workload),
+                      "hbm_bytes_per_launch": int(round(fetch_b + write_b)),
+                      "fetch_bytes_per_launch": int(round(fetch_b)), "write_bytes_per_launch": int(round(write_b)),
+                      "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
+                      "dispatches": [nf, nw],
+                      "copy_probe": {"bytes": copy_bytes, "fetch_kib": round(fc, 1), "write_kib": round(wc, 1),
+                                     "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4)}}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps(data[workload]))
 
 
 WORKLOADS = {
@@ -130,6 +204,9 @@ def bf16_bytes(lens, hq, hkv):
 
 def main():
     args = parse_args()
+    if args.traffic_from:
+        traffic_from(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the path is single-GPU; "
               f"see the sharding notes in DESIGN.md)", file=sys.stderr)
@@ -370,7 +447,7 @@ def main():
         "tokens_per_s": round(tokens_per_s, 1),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload),
                      "kernel": f"oscar::attend_kernel<{hq // hkv}, {128 // G}> (split-K INT2 + BF16 decode)",
                      "avg_launch_us": round(attend_us, 2), "bytes_per_launch": int(attend_b)},
         "cpu_baseline": cpu,
@@ -510,7 +587,7 @@ def write_main(args, W, dev):
         "tokens_per_s": round(B * L / (ms_per_step * 1e-3), 1),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("write"),
                      "kernel": f"oscar::write_hist_kernel<{G}> (rotate, clip, INT2-pack, page-store)",
                      "avg_launch_us": round(hist_us, 2), "bytes_per_launch": int(hist_b)},
         "append_decode": {"steps": n_dec, "ms_per_step": round(dec_ms, 4),
