@@ -536,6 +536,8 @@ __device__ void build_q(const StepArgs &a, int tid, QWork<GQA, NG> &w, uint32_t 
 // reads after these copies, so the page loop waits for them itself (vmcnt
 // counts per instruction; loads complete in issue order).
 constexpr int DEPTH = 4;
+constexpr int RP = 3;  // pages loaded through registers before the q build (at most DEPTH - 1)
+static_assert(RP <= DEPTH - 1, "register pages fit the ring");
 
 __device__ inline void lds_copy16(const void *src, void *lds_base) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
@@ -779,8 +781,8 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
   static_assert((NT2 & (NT2 - 1)) == 0 && NT2 <= 64, "tail: a power of two of lanes");
   typedef const __attribute__((address_space(1))) u32x4 *gp4;
   typedef const __attribute__((address_space(1))) Tail *gpt;
-  u32x4 preg[DEPTH - 1];
-  Tail ptail[DEPTH - 1];
+  u32x4 preg[RP];
+  Tail ptail[RP];
   auto issue_reg = [&](int i, bool on) {
     const uint8_t *blk = on ? page_block(i, i) : a.fk;
     preg[i] = *(gp4)(blk + lane16);
@@ -963,16 +965,19 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
   my_pid = pid_pre;
   asm volatile("" : "+v"(my_pid));
 #pragma unroll
-  for (int i = 0; i < DEPTH - 1; ++i) issue_reg(i, any_pages);
+  for (int i = 0; i < RP; ++i) issue_reg(i, any_pages);
   prep();
   // stored on every path, used or not: a load still in flight into a
   // register at the loop entry would make the compiler wait for every load
   // in flight (the prefetched pages) wherever the loop reuses that register
 #pragma unroll
-  for (int i = 0; i < DEPTH - 1; ++i) {
+  for (int i = 0; i < RP; ++i) {
     *reinterpret_cast<u32x4 *>(ring + i * SB + lane16) = preg[i];
     if (lane < NT2) *reinterpret_cast<Tail *>(ring + i * SB + 1024u + TB * lane) = ptail[i];
   }
+  // the rest of the ring fills by direct copies from here
+  if (any_pages)
+    for (int i = RP; i < DEPTH - 1 && i < npw; ++i) issue(i, i);
 #pragma unroll
   for (int r = 0; r < 8; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
