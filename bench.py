@@ -283,7 +283,7 @@ def main():
         ly.v_new = synth.kv_device(synth.device_generator(args.seed, l, synth.S_NEW_V), B, ld.outliers, dev)
         ly.q = synth.q_device(synth.device_generator(args.seed, l, synth.S_DEC_Q), B, hq, ld.lam, dev)
         ly.out = torch.empty((B, hq, HEAD_DIM), dtype=torch.float32, device=dev)
-        ly.ws = torch.empty(oscar.decode_workspace_bytes(B, hq, hkv, max_len), dtype=torch.uint8, device=dev)
+        ly.ws = torch.zeros(oscar.decode_workspace_bytes(B, hq, hkv, max_len), dtype=torch.uint8, device=dev)
         layers.append(ly)
         if not args.no_bf16:
             # the same tokens, all raw bf16, for the in-run BF16 baseline
@@ -502,7 +502,7 @@ def write_main(args, W, dev):
         ly.v_new = synth.kv_device(synth.device_generator(args.seed, l, synth.S_NEW_V), B, ld.outliers, dev)
         ly.q = synth.q_device(synth.device_generator(args.seed, l, synth.S_DEC_Q), B, hq, ld.lam, dev)
         ly.out = torch.empty((B, hq, HEAD_DIM), dtype=torch.float32, device=dev)
-        ly.ws = torch.empty(oscar.decode_workspace_bytes(B, hq, hkv, int(final.max())), dtype=torch.uint8,
+        ly.ws = torch.zeros(oscar.decode_workspace_bytes(B, hq, hkv, int(final.max())), dtype=torch.uint8,
                             device=dev)
         layers.append(ly)
         del qc, kc, vc

@@ -134,8 +134,8 @@ def decode_attn(cache: LayerCache, rot_k: Rotation, rot_v: Rotation, q: torch.Te
         out = torch.empty((batch, hq, HEAD_DIM), dtype=torch.float32, device=dev)
     _need(out, "out", (torch.float32,), dev)
     need = decode_workspace_bytes(batch, hq, cache.n_kv_heads, max_seq_len)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace is None:  # zero-filled: it holds the merge counters
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
     c = cache.c()
     rk, rv = rot_k.c(), rot_v.c()
     check(load().oscar_decode_attn(ctypes.byref(c), ctypes.byref(rk), ctypes.byref(rv), _ptr(q), hq,
@@ -161,8 +161,8 @@ def decode_step(cache: LayerCache, rot_k: Rotation, rot_v: Rotation, k_new: torc
         out = torch.empty((batch, hq, HEAD_DIM), dtype=torch.float32, device=dev)
     _need(out, "out", (torch.float32,), dev)
     need = decode_workspace_bytes(batch, hq, cache.n_kv_heads, max_seq_len)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace is None:  # zero-filled: it holds the merge counters
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
     c = cache.c()
     rk, rv = rot_k.c(), rot_v.c()
     check(load().oscar_decode_step(ctypes.byref(c), ctypes.byref(rk), ctypes.byref(rv), _ptr(k_new), _ptr(v_new),
@@ -192,8 +192,8 @@ def bf16_paged_decode(q: torch.Tensor, kv_pages: torch.Tensor, pt: torch.Tensor,
     if out is None:
         out = torch.empty((batch, hq, HEAD_DIM), dtype=torch.float32, device=dev)
     need = bf16_decode_workspace_bytes(batch, hq, hkv, max_seq_len)
-    if workspace is None:  # zero-filled: it holds the merge counters
-        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     check(load().oscar_bf16_paged_decode(_ptr(q), _ptr(kv_pages), kv_pages.shape[0], _ptr(pt), pt.shape[1],
                                          _ptr(seq_lens), batch, int(max_seq_len), hq, hkv, float(sm_scale),
                                          _ptr(out), _ptr(status), _ptr(workspace), workspace.numel(),

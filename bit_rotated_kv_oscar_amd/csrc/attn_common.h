@@ -282,11 +282,21 @@ struct Bf16Wave {
   }
 };
 
+// Stores of values that another workgroup, possibly on another XCD, reads
+// in the same kernel: agent-scope atomic stores, which go through the XCD's
+// L2 to memory (the L2 caches of the XCDs are not coherent with each other).
+__device__ inline void store_agent(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float load_agent(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Combines the NW per-wave states in LDS (o [NW][GQA][128], m, l [NW][GQA])
-// and writes one unnormalised partial (o[128], m, l) per query head.  With
-// xm, one more token joins: value xo[128] (every head), score xm[h] (log2
-// units, finite).
-template <int GQA, int NW>
+// and writes one unnormalised partial (o[128], m, l) per query head
+// (AGENT: with agent-scope stores).  With xm, one more token joins: value
+// xo[128] (every head), score xm[h] (log2 units, finite).
+template <int GQA, int NW, bool AGENT = false>
 __device__ inline void combine_waves(const float *o_lds, const float *m_lds, const float *l_lds,
                                      float *part0, int64_t head_stride, int tid, int o_wave_stride = GQA * D,
                                      const float *xo = nullptr, const float *xm = nullptr) {
@@ -307,10 +317,18 @@ __device__ inline void combine_waves(const float *o_lds, const float *m_lds, con
       l = fmaf(e, l_lds[w * GQA + h], l);
     }
     float *part = part0 + h * head_stride;
-    part[c] = o;
-    if (c == 0) {
-      part[D] = mst;
-      part[D + 1] = l;
+    if constexpr (AGENT) {
+      store_agent(part + c, o);
+      if (c == 0) {
+        store_agent(part + D, mst);
+        store_agent(part + D + 1, l);
+      }
+    } else {
+      part[c] = o;
+      if (c == 0) {
+        part[D] = mst;
+        part[D + 1] = l;
+      }
     }
   }
 }

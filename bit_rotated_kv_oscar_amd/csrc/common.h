@@ -76,6 +76,7 @@ __host__ __device__ inline int n_hist_pages(int L) { return (n_hist_tokens(L) + 
 struct SplitPlan {
   int pages_per_split;  // history pages per split
   int n_splits;         // history splits (the BF16 part is one more)
+  bool fused = false;   // INT2: the attend kernel merges (last workgroup of each unit)
 };
 
 SplitPlan plan_int2_splits(int batch, int n_kv_heads, int max_seq_len);

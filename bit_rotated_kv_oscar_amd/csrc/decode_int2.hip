@@ -9,14 +9,16 @@
 //
 // The rotation is never undone per token: history keys stay in the rotated
 // basis and are scored against q R_K (R orthogonal keeps q.k), and the
-// history part of the output is rotated back by R_V^T once per (request,
-// query head).  Per-group scale s and zero z are factored out of both
+// history part of the output is rotated back by R_V^T once per partial sum
+// over a split of pages (or once per (request, query head) when a separate
+// merge kernel combines the splits).  Per-group scale s and zero z are
+// factored out of both
 // contractions so the matrix cores see the 2-bit codes as exact fp16 values:
 //   score_t = sum_g s_tg (q_g . c_tg) + z_tg sum_{i in g} q_i
 //   o       = sum_g [ sum_t (p_t s_tg) c_tg ] + sum_t p_t z_tg
 //
-// Two kernels per call, in stream order:
-//   attend (one workgroup of 8 waves per (request, KV head, split)):
+// The attend kernel runs one workgroup of 8 waves per (request, KV head,
+// split):
 //     split 0 attends over the raw BF16 sink + recent pages (a token being
 //     appended is read from k_new / v_new); splits s >= 1 over history pages
 //     (wave w takes every 8th page of the split; its first 64 page ids are
@@ -32,12 +34,18 @@
 //     itself (dequantised, rotated back); the history workgroups leave its
 //     row out.  Each workgroup writes an unnormalised partial (o[128], m, l)
 //     per query head.
-//   merge (one block per (request, KV head)): LSE-combines the partials,
-//     rotates the history part back with R_V^T, adds the raw part and
-//     normalises (fp32 out).  A kernel boundary, not an in-kernel fence, makes
-//     the partials visible: the L2 caches of the eight XCDs are not coherent
-//     with each other, and a device-scope fence writes back and invalidates
-//     the whole L2.
+//   Merging the partials (LSE-combine, normalise, fp32 out) takes one of two
+//   forms.  When all workgroups run in one round (small batches), the
+//   attend kernel merges: history workgroups rotate their partial back with
+//   R_V^T before storing it, and the last workgroup of a (request, KV head)
+//   to finish, counted by an atomic counter in the workspace, combines them.
+//   The L2 caches of the eight XCDs are not coherent with each other, and a
+//   device-scope release fence writes back the whole L2, so the partials
+//   travel by agent-scope stores and loads instead (they bypass the
+//   non-coherent L2 state): a workgroup's stores complete before its count,
+//   and the last workgroup's loads start after it.  Otherwise a merge kernel
+//   (one block per (request, KV head)) combines the partials after the
+//   attend kernel, rotating the history part back once.
 #include <cmath>
 #include <type_traits>
 
@@ -86,9 +94,10 @@ struct Rows {
 SplitPlan plan_int2_splits(int batch, int n_kv_heads, int max_seq_len) {
   const int pages = n_hist_pages(max_seq_len);
   SplitPlan p;
-  if (pages == 0) {
+  if (pages == 0) {  // the raw workgroup alone: it merges its own partial
     p.pages_per_split = AW;
     p.n_splits = 0;
+    p.fused = true;
     return p;
   }
   // One round of attend workgroups, one per CU on 256 CUs (measured faster
@@ -98,12 +107,17 @@ SplitPlan plan_int2_splits(int batch, int n_kv_heads, int max_seq_len) {
   // at least one history split, spread each unit's pages over as many splits
   // as it holds (its raw workgroup included); otherwise use splits of 32
   // pages per wave.
+  // In the one-round case the last workgroup of each unit merges inside the
+  // attend kernel (measured: ~2.5 us less per call at batch 1); with several
+  // rounds, the election and the merge hold workgroup slots that other units
+  // need, and a separate merge kernel is faster (~6 % at batch 64).
   const int64_t units = int64_t(batch) * n_kv_heads;
   const int64_t slots = 256;
   int64_t pps;
   if (slots - units >= units) {
     const int64_t per_unit = (slots - units) / units;
     pps = (pages + per_unit - 1) / per_unit;
+    p.fused = true;
   } else {
     pps = 32 * AW;
   }
@@ -117,9 +131,21 @@ SplitPlan plan_int2_splits(int batch, int n_kv_heads, int max_seq_len) {
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Partial slots per query head: one per split (raw + history), and at least
+// the merge's first register window, which it loads without bounds checks.
+constexpr int MERGE_WINDOW = 32;
+static int part_slots(const SplitPlan &p) { return 1 + (p.n_splits > MERGE_WINDOW ? p.n_splits : MERGE_WINDOW); }
+
+// Workspace: the partials, then one merge counter per (request, KV head),
+// each on a 256-byte line of its own (atomics on one line serialise)
+constexpr int COUNTER_STRIDE = 64;  // uint32 words
+static size_t parts_bytes(int batch, int n_q_heads, const SplitPlan &p) {
+  return align256(size_t(batch) * n_q_heads * part_slots(p) * PART_STRIDE * sizeof(float));
+}
+
 size_t decode_int2_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int max_seq_len) {
   const SplitPlan p = plan_int2_splits(batch, n_kv_heads, max_seq_len);
-  return align256(size_t(batch) * n_q_heads * (1 + p.n_splits) * PART_STRIDE * sizeof(float));
+  return parts_bytes(batch, n_q_heads, p) + size_t(batch) * n_kv_heads * COUNTER_STRIDE * sizeof(uint32_t);
 }
 
 struct StepArgs {
@@ -137,7 +163,9 @@ struct StepArgs {
   float pv_scale, pv_unscale;     // 2^k and 2^-k applied to the PV operand
   float pk01, pk23;               // log2(4 * 2^k), log2(16 * 2^k): PV factors of tokens 4q+{0,1}, 4q+{2,3}
   uint32_t ex_m4, ex_m16, ex_e;   // code expansion constants 0x03000300, 0x00C000C0, 0x3C003C00
-  float *parts;                   // [B][Hq][1 + n_splits][PART_STRIDE]
+  float *parts;                   // [B][Hq][part_slots][PART_STRIDE]
+  int part_slots;                 // partials per query head: 1 + max(n_splits, merge window)
+  uint32_t *counters;             // [B][Hkv][COUNTER_STRIDE]: word 0 = workgroups done (zero between calls)
   float *out;                     // [B][Hq][128]
 };
 
@@ -1081,16 +1109,176 @@ __device__ inline uint32_t raw_valid_rows(int L, int page) {
   return m;
 }
 
-// Merge of one (request, KV head): LSE-combines the `used` partials of each
+// R_V rows of a workgroup thread for the way back to the plain basis: rows
+// cr + 64 m (m < 2), inputs 32 k + 4 qq .. + 3 (cr = tid / 8, qq = tid % 8);
+// eight lanes per row read 128 contiguous bytes.
+struct RvRows {
+  f32x4 r[8];
+  __device__ void load(const uint8_t *fv, int tid) {
+    const float *Rc = reinterpret_cast<const float *>(fv + FORM_R) + (tid >> 3) * D + 4 * (tid & 7);
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) r[4 * m + k] = *reinterpret_cast<const f32x4 *>(Rc + m * 64 * D + 32 * k);
+  }
+};
+static_assert(AW * 64 == 512, "R_V rows: 128 rows x 8 lanes over the workgroup");
+
+// History workgroups: combines the per-wave states like combine_waves and
+// brings the partial back to the plain basis before it is stored,
+// o_plain[h][c] = sum_i o_rot[h][i] R_V[c][i] (linear, so the merge's
+// weighted sum may follow), through rot[GQA][D] in LDS.  Agent-scope stores.
+template <int GQA>
+__device__ void combine_rotate(const float *o_lds, const float *m_lds, const float *l_lds, float *part0,
+                               int64_t head_stride, int tid, int o_wave_stride, const RvRows &rv,
+                               float (*rot)[D]) {
+  for (int idx = tid; idx < GQA * D; idx += AW * 64) {
+    const int h = idx / D, c = idx % D;
+    float mst = -INFINITY;
+    for (int w = 0; w < AW; ++w) mst = fmaxf(mst, m_lds[w * GQA + h]);
+    float o = 0.f, l = 0.f;
+    for (int w = 0; w < AW; ++w) {
+      const float mw = m_lds[w * GQA + h];
+      const float e = (mw == -INFINITY) ? 0.f : fast_exp2(mw - mst);
+      o = fmaf(e, o_lds[w * o_wave_stride + h * D + c], o);
+      l = fmaf(e, l_lds[w * GQA + h], l);
+    }
+    rot[h][c] = o;
+    if (c == 0) {
+      store_agent(part0 + h * head_stride + D, mst);
+      store_agent(part0 + h * head_stride + D + 1, l);
+    }
+  }
+  __syncthreads();
+  // the eight lanes of a row combine by DPP (the sum lands in lanes qq >= 4)
+  const int cr = tid >> 3, qq = tid & 7;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int cc = cr + 64 * m;
+#pragma unroll
+    for (int hh = 0; hh < GQA; ++hh) {
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const f32x4 r = *reinterpret_cast<const f32x4 *>(&rot[hh][32 * k + 4 * qq]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = fmaf(r[e], rv.r[4 * m + k][e], acc);
+      }
+      acc = oct_sum(acc);
+      if (qq == 4) store_agent(part0 + hh * head_stride + cc, acc);
+    }
+  }
+}
+
+// Merge of one (request, KV head), run inside the attend kernel by the
+// workgroup that finishes last: LSE-combines the `used` partials of each
+// query head of the group (all in the plain basis: the history workgroups
+// rotated theirs back) and normalises.  Built for latency: thread (h, c)
+// issues the loads of all its partial values and the (m, l) pairs at once,
+// so the workgroup waits on memory about once.  The partials of other
+// workgroups are read with agent-scope loads (they may sit in the L2 of
+// another XCD until written through).
+template <int GQA>
+struct MergeWork {
+  float w[GQA][MAX_SPLITS + 1];  // m, then the weight of each split (0 past `used`)
+  float l[GQA][MAX_SPLITS + 1];
+  float lsum[GQA];
+};
+
+// partials per (head, channel) a merging thread holds in registers at a time
+template <int GQA>
+constexpr int merge_ch() { return GQA >= 8 ? 16 : 32; }
+
+template <int GQA>
+__device__ void merge_unit(const StepArgs &a, int b, int hk, int used, int tid, MergeWork<GQA> &mw) {
+  constexpr int NT = AW * 64;
+  constexpr int KH = (GQA * D + NT - 1) / NT;  // (head, channel) pairs per thread
+  constexpr int MCH = merge_ch<GQA>();
+  static_assert(MCH <= MERGE_WINDOW && MCH <= MAX_SPLITS + 1, "the first register window fits");
+  const int64_t head_stride = int64_t(a.part_slots) * PART_STRIDE;
+  const float *parts0 = a.parts + (int64_t(b) * a.n_q_heads + hk * GQA) * head_stride;
+
+  // ---- loads, all issued before any use: partial values of splits
+  // 0..MCH-1 (every head has at least MCH slots, so these loads need no
+  // bounds; slots >= used are never summed), then the (m, l) pairs
+  float ov[KH][MCH];
+#pragma unroll
+  for (int k = 0; k < KH; ++k) {
+    const int idx = tid + NT * k, h = idx / D, c = idx % D;
+    const float *ph = parts0 + (h < GQA ? h : 0) * head_stride + c;
+#pragma unroll
+    for (int j = 0; j < MCH; ++j) ov[k][j] = load_agent(ph + j * PART_STRIDE);
+  }
+  for (int e = tid; e < GQA * used; e += NT) {
+    const int hh = e / used, sp = e % used;
+    const float *pm = parts0 + hh * head_stride + sp * PART_STRIDE + D;
+    mw.w[hh][sp] = load_agent(pm);
+    mw.l[hh][sp] = load_agent(pm + 1);
+  }
+  __syncthreads();
+  // ---- per head: max over splits, split weights, total l (wave hh; DPP
+  // reductions)
+  {
+    const int wave = wave_id(), lane = tid & 63;
+    const int nw = used > MCH ? used : MCH;
+    for (int hh = wave; hh < GQA; hh += NT / 64) {
+      float m = -INFINITY;
+      for (int sp = lane; sp < used; sp += 64) m = fmaxf(m, mw.w[hh][sp]);
+      m = wave_max(m);
+      float l = 0.f;
+      for (int sp = lane; sp < nw; sp += 64) {
+        float w = 0.f;
+        if (sp < used) {
+          const float ms = mw.w[hh][sp];
+          w = (ms == -INFINITY) ? 0.f : fast_exp2(ms - m);
+          l = fmaf(w, mw.l[hh][sp], l);
+        }
+        mw.w[hh][sp] = w;
+      }
+      l = wave_sum(l);
+      if (lane == 0) mw.lsum[hh] = l;
+    }
+  }
+  __syncthreads();
+  // ---- output channel c of head h
+#pragma unroll
+  for (int k = 0; k < KH; ++k) {
+    const int idx = tid + NT * k, h = idx / D, c = idx % D;
+    if (h < GQA) {
+      float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+      for (int j = 0; j < MCH; ++j) {
+        const float t = fmaf(mw.w[h][j], ov[k][j], j & 1 ? acc1 : acc0);
+        if (j & 1)
+          acc1 = (j < used) ? t : acc1;
+        else
+          acc0 = (j < used) ? t : acc0;
+      }
+      // the first window is summed here, before the later windows' loads
+      asm volatile("" : "+v"(acc0), "+v"(acc1));
+      const float *ph = parts0 + h * head_stride + c;
+      for (int s0 = MCH; s0 < used; s0 += MCH) {
+        float o2[MCH];
+#pragma unroll
+        for (int j = 0; j < MCH; ++j) o2[j] = (s0 + j < used) ? load_agent(ph + (s0 + j) * PART_STRIDE) : 0.f;
+#pragma unroll
+        for (int j = 0; j < MCH; ++j) {
+          const float w = (s0 + j < used) ? mw.w[h][s0 + j] : 0.f;
+          acc0 = fmaf(w, o2[j], acc0);
+        }
+      }
+      a.out[(int64_t(b) * a.n_q_heads + hk * GQA + h) * D + c] = (acc0 + acc1) / mw.lsum[h];
+    }
+  }
+}
+
+// Separate merge kernel (large batches, where the attend workgroups run in
+// several rounds and the in-kernel election costs more than a launch): one
+// block per (request, KV head) LSE-combines the `used` partials of each
 // query head of the group, rotates the history part back with R_V^T, adds
 // the raw part (split 0) and normalises.  Built for latency: thread (h, c)
 // issues the loads of all its partial values, the (m, l) pairs and its slice
 // of R_V at once, so the kernel waits on memory about once.
-// partials per thread held in registers at a time (1024-thread blocks for
-// GQA 8 have half the registers per thread)
-template <int GQA>
-constexpr int merge_ch() { return GQA >= 8 ? 16 : 32; }
-
 template <int GQA>
 constexpr int merge_threads() { return D * (GQA < 2 ? 2 : GQA); }
 
@@ -1102,7 +1290,7 @@ __global__ void __launch_bounds__(merge_threads<GQA>()) merge_kernel(StepArgs a)
   const int L = a.k_new ? a.len_before[b] + 1 : a.seq_lens[b];
   if (!valid_len(L, a.max_seq_len)) return;  // output zeroed by the attend kernel
   const int used = 1 + (n_hist_pages(L) + a.pages_per_split - 1) / a.pages_per_split;
-  const int64_t head_stride = int64_t(1 + a.n_splits) * PART_STRIDE;
+  const int64_t head_stride = int64_t(a.part_slots) * PART_STRIDE;
   const float *parts0 = a.parts + (int64_t(b) * a.n_q_heads + hk * GQA) * head_stride;
   __shared__ float w_lds[GQA][MAX_SPLITS + 1];  // m, then the weight of each split
   __shared__ float l_lds[GQA][MAX_SPLITS + 1];
@@ -1212,7 +1400,7 @@ __global__ void __launch_bounds__(merge_threads<GQA>()) merge_kernel(StepArgs a)
 template <int GQA, int NG>
 constexpr int attend_waves() { return (GQA <= 4 && NG <= 2) ? 4 : 1; }
 
-template <int GQA, int NG>
+template <int GQA, int NG, bool FUSED>
 __global__ void __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(attend_waves<GQA, NG>())))
 attend_kernel(StepArgs a) {
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
@@ -1321,22 +1509,67 @@ attend_kernel(StepArgs a) {
     history_wave<GQA, NG>(a, b, hk, nh, j0, j1, wave, lane, pid_pre, prep, frag_lds, wave_lds + wave * WREG,
                           zs_lds + wave * GQA * NG, o_w, m_lds + wave * GQA, l_lds + wave * GQA);
   }
-  __syncthreads();
-  const int64_t head_stride = int64_t(1 + a.n_splits) * PART_STRIDE;
+  const int64_t head_stride = int64_t(a.part_slots) * PART_STRIDE;
   float *part0 = a.parts + (int64_t(b) * a.n_q_heads + hk * GQA) * head_stride + split * PART_STRIDE;
-  if (extra)
-    combine_waves<GQA, AW>(o_lds, m_lds, l_lds, part0, head_stride, tid, WREG / 4, work.e.u[1], work.e.sc);
-  else
-    combine_waves<GQA, AW>(o_lds, m_lds, l_lds, part0, head_stride, tid, WREG / 4);
+  if constexpr (!FUSED) {
+    // partials for the merge kernel
+    __syncthreads();
+    if (extra)
+      combine_waves<GQA, AW>(o_lds, m_lds, l_lds, part0, head_stride, tid, WREG / 4, work.e.u[1], work.e.sc);
+    else
+      combine_waves<GQA, AW>(o_lds, m_lds, l_lds, part0, head_stride, tid, WREG / 4);
+  } else {
+    // R_V rows for the history partial's way back, in flight during the
+    // barrier (the page loop's registers are free)
+    RvRows rv;
+    {
+      // computed here, not hoisted above the page loop (register pressure)
+      int t = tid;
+      asm volatile("" : "+v"(t));
+      if (split > 0) rv.load(a.fv, t);
+    }
+    __syncthreads();
+    if (split > 0)
+      combine_rotate<GQA>(o_lds, m_lds, l_lds, part0, head_stride, tid, WREG / 4, rv, work.q.y);
+    else if (extra)
+      combine_waves<GQA, AW, true>(o_lds, m_lds, l_lds, part0, head_stride, tid, WREG / 4, work.e.u[1],
+                                   work.e.sc);
+    else
+      combine_waves<GQA, AW, true>(o_lds, m_lds, l_lds, part0, head_stride, tid, WREG / 4);
+    // ---- the last workgroup of (b, hk) to finish merges.  Its partial
+    // stores have completed (agent scope: in memory, past this XCD's L2)
+    // before the counter counts the workgroup in; the last one reads every
+    // partial with agent-scope loads and leaves the counter at zero for the
+    // next call.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (used > 1) {
+      __shared__ int last;
+      if (tid == 0) {
+        uint32_t *cnt = a.counters + COUNTER_STRIDE * (b * c.n_kv_heads + hk);
+        const uint32_t done = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = done == uint32_t(used - 1);
+        if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
+      if (!last) return;
+    }
+    static_assert(sizeof(MergeWork<GQA>) <= sizeof(wave_lds), "merge work area fits the page rings");
+    merge_unit<GQA>(a, b, hk, used, tid, *reinterpret_cast<MergeWork<GQA> *>(wave_lds));
+  }
 }
 
 // ------------------------------------------------------------------ launch
 
 template <int GQA, int NG>
-static hipError_t launch_t(const StepArgs &a, int batch, int hkv, hipStream_t s) {
+static hipError_t launch_t(const StepArgs &a, bool fused, int batch, int hkv, hipStream_t s) {
   const KernelEvents ev = take_profile_events();
-  hipExtLaunchKernelGGL((attend_kernel<GQA, NG>), dim3(1 + a.n_splits, hkv, batch), dim3(AW * 64), 0, s,
-                        ev.before, ev.after, 0, a);
+  const dim3 grid(1 + a.n_splits, hkv, batch);
+  if (fused) {
+    hipExtLaunchKernelGGL((attend_kernel<GQA, NG, true>), grid, dim3(AW * 64), 0, s, ev.before, ev.after, 0, a);
+    return hipGetLastError();
+  }
+  hipExtLaunchKernelGGL((attend_kernel<GQA, NG, false>), grid, dim3(AW * 64), 0, s, ev.before, ev.after, 0, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((merge_kernel<GQA>), dim3(hkv, batch), dim3(merge_threads<GQA>()), 0, s, a);
@@ -1344,11 +1577,11 @@ static hipError_t launch_t(const StepArgs &a, int batch, int hkv, hipStream_t s)
 }
 
 template <int GQA>
-static hipError_t launch_g(const StepArgs &a, int G, int batch, int hkv, hipStream_t s) {
+static hipError_t launch_g(const StepArgs &a, bool fused, int G, int batch, int hkv, hipStream_t s) {
   switch (G) {
-    case 32: return launch_t<GQA, 4>(a, batch, hkv, s);
-    case 64: return launch_t<GQA, 2>(a, batch, hkv, s);
-    default: return launch_t<GQA, 1>(a, batch, hkv, s);
+    case 32: return launch_t<GQA, 4>(a, fused, batch, hkv, s);
+    case 64: return launch_t<GQA, 2>(a, fused, batch, hkv, s);
+    default: return launch_t<GQA, 1>(a, fused, batch, hkv, s);
   }
 }
 
@@ -1391,11 +1624,13 @@ hipError_t launch_decode_step(const oscar_layer_cache &c, RotArg rk, RotArg rv, 
   a.pages_per_split = p.pages_per_split;
   a.n_splits = p.n_splits;
   a.parts = static_cast<float *>(ws);
+  a.part_slots = part_slots(p);
+  a.counters = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + parts_bytes(batch, n_q_heads, p));
   switch (n_q_heads / c.n_kv_heads) {
-    case 1: return launch_g<1>(a, c.group, batch, c.n_kv_heads, s);
-    case 2: return launch_g<2>(a, c.group, batch, c.n_kv_heads, s);
-    case 4: return launch_g<4>(a, c.group, batch, c.n_kv_heads, s);
-    case 8: return launch_g<8>(a, c.group, batch, c.n_kv_heads, s);
+    case 1: return launch_g<1>(a, p.fused, c.group, batch, c.n_kv_heads, s);
+    case 2: return launch_g<2>(a, p.fused, c.group, batch, c.n_kv_heads, s);
+    case 4: return launch_g<4>(a, p.fused, c.group, batch, c.n_kv_heads, s);
+    case 8: return launch_g<8>(a, p.fused, c.group, batch, c.n_kv_heads, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -194,7 +194,13 @@ OSCAR_API int oscar_write_kv(const oscar_layer_cache *cache, const oscar_rotatio
                    int64_t total_tokens, int32_t max_new,
                    oscar_stream_t stream);
 
-/* Workspace for oscar_decode_attn (device, any alignment >= 256 B). */
+/* Workspace for oscar_decode_attn and oscar_decode_step (device, any
+ * alignment >= 256 B): the partial results of the splits, then one counter
+ * per (request, KV head) that elects the workgroup which merges them.  Fill
+ * it with zeros before its first call; every call that runs to completion
+ * leaves the counters at zero again, so a workspace is reused without
+ * clearing (after a call that faulted on the device, clear it again).  Calls
+ * that share a workspace must not run concurrently. */
 OSCAR_API size_t oscar_decode_workspace_bytes(int32_t batch, int32_t n_q_heads,
                                     int32_t n_kv_heads, int32_t max_seq_len);
 
@@ -203,10 +209,12 @@ OSCAR_API size_t oscar_decode_workspace_bytes(int32_t batch, int32_t n_q_heads,
  * cached tokens: BF16 sink/recent tokens directly, INT2 history through
  * dequantisation.  History keys stay in the rotated basis and are scored
  * against q*R_K; the history part of the output is brought back with R_V^T
- * once per (request, query head).  softmax scale sm_scale; query head h uses
+ * once per partial sum over a split of pages (never per token).  softmax
+ * scale sm_scale; query head h uses
  * KV head h / (Hq/Hkv).
  * q: device bf16 [batch][Hq][128]; seq_lens: device int32 [batch], each in
- * [1, max_seq_len]; out: device fp32 [batch][Hq][128]. */
+ * [1, max_seq_len]; out: device fp32 [batch][Hq][128]; workspace: see
+ * oscar_decode_workspace_bytes (zero-filled before its first use). */
 OSCAR_API int oscar_decode_attn(const oscar_layer_cache *cache,
                       const oscar_rotation *rot_k, const oscar_rotation *rot_v,
                       const uint16_t *q, int32_t n_q_heads,
@@ -223,10 +231,9 @@ OSCAR_API int oscar_decode_attn(const oscar_layer_cache *cache,
  * exactly as in oscar_write_kv.  Then q (device bf16 [batch][Hq][128])
  * attends over all len_before[b] + 1 tokens as in oscar_decode_attn, which
  * must be <= max_seq_len.  Same result as oscar_write_kv with one token per
- * request followed by oscar_decode_attn, in three kernel launches.  The
- * workspace is the one of oscar_decode_attn (oscar_decode_workspace_bytes);
- * it may hold anything on entry.  Calls that share a workspace must not run
- * concurrently. */
+ * request followed by oscar_decode_attn, in one kernel launch.  The
+ * workspace is the one of oscar_decode_attn (oscar_decode_workspace_bytes,
+ * zero-filled before its first use). */
 OSCAR_API int oscar_decode_step(const oscar_layer_cache *cache,
                                 const oscar_rotation *rot_k,
                                 const oscar_rotation *rot_v,

@@ -203,6 +203,29 @@ def test_decode_shared_prefix_pages(oscar):
     assert_decode_close(gpu_decode(oscar, sc, cache, rk, rv), sc.oracle_decode(ref))
 
 
+def test_decode_many_splits_reuses_workspace(oscar):
+    # one request over 2 KV heads at 20K: 125 history splits per head, so the
+    # merging workgroup sums its partials in several register windows; the
+    # workspace is filled with zeros once, and every call leaves its merge
+    # counters (the last bytes) at zero again
+    L = 20000
+    sc = Scenario(1500, 8, 2, 64, [L])
+    ref = sc.oracle_cache()
+    cache = gpu_cache(oscar, sc, hist=ref.hist, bf16=ref.bf16)
+    rk, rv = gpu_rotations(oscar, sc)
+    need = oscar.decode_workspace_bytes(1, 8, 2, L)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    expect = sc.oracle_decode(ref)
+    lens = torch.tensor([L], dtype=torch.int32, device="cuda")
+    q = to_dev_bf16(sc.q)
+    for rep in range(3):
+        out = oscar.decode_attn(cache, rk, rv, q, lens, L, SCALE, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(cache.status.item()) == 0
+        assert_decode_close(out.cpu().numpy(), expect, f"many splits, call {rep}")
+        assert int(ws[-256:].count_nonzero().item()) == 0
+
+
 def test_bad_page_ids_are_flagged_not_followed(oscar):
     sc = Scenario(800, 8, 2, 64, [600])
     ref = sc.oracle_cache()
@@ -312,7 +335,7 @@ def test_decode_step_many_steps(oscar):
     full = sc.oracle_cache()
     cache = gpu_cache(oscar, sc, hist=pre.hist, bf16=pre.bf16)
     rk, rv = gpu_rotations(oscar, sc)
-    ws = torch.empty(oscar.decode_workspace_bytes(len(lens), 8, 2, max(lens)), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(oscar.decode_workspace_bytes(len(lens), 8, 2, max(lens)), dtype=torch.uint8, device="cuda")
     q = to_dev_bf16(sc.q)
     for s in range(steps, 0, -1):
         k_s = np.stack([t[L - s] for t, L in zip(sc.tok_k, lens)])
@@ -330,7 +353,7 @@ def test_decode_step_many_steps(oscar):
 
 
 def test_bf16_decode_reuses_workspace(oscar):
-    # the merge counters in the workspace must be back at zero after a call
+    # one workspace, filled once, serves repeated calls
     lens = [700, 33]
     ld = synth.LayerData(1300, 0, 8, 2)
     k, v = ld.cache_kv(sum(lens))
