@@ -44,27 +44,40 @@ constexpr int WHC = 4;   // KV heads per write workgroup
 constexpr int WPP = 16;  // history pages per write workgroup (the R pieces stay in registers)
 constexpr int XSTR = WHC * D * 2 + 16;  // LDS bytes per staged token row (all WHC heads; padded)
 
-typedef __bf16 bf16x8w __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8w __attribute__((ext_vector_type(8)));
 typedef float f32x4w __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4w __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2w __attribute__((ext_vector_type(2)));
 
-// value of lane (l - N) mod 16 within each row of 16 lanes (DPP row_ror)
-template <int N>
-__device__ inline float row_rot(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, false));
+// Minimum / maximum over the four lanes l, l^16, l^32, l^48 (one token of
+// the transposed product), in every one of them: row swaps between lanes of
+// registers, no LDS round trip.
+__device__ inline float lanes4_min(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float m = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fminf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
-__device__ inline float row16_min(float v) {
-  v = fminf(v, row_rot<8>(v));
-  v = fminf(v, row_rot<4>(v));
-  v = fminf(v, row_rot<2>(v));
-  return fminf(v, row_rot<1>(v));
+__device__ inline float lanes4_max(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
-__device__ inline float row16_max(float v) {
-  v = fmaxf(v, row_rot<8>(v));
-  v = fmaxf(v, row_rot<4>(v));
-  v = fmaxf(v, row_rot<2>(v));
-  return fmaxf(v, row_rot<1>(v));
+
+// Eight bf16 values (four dwords) as eight fp16 values: exact for
+// 2^-14 <= |x| <= 65504; below, within 2^-24; beyond, saturated to 65504
+// (round toward zero).
+__device__ inline u32x4w bf16x8_to_f16x8(u32x4w u) {
+  u32x4w r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(u[i] << 16), __uint_as_float(u[i] & 0xFFFF0000u));
+    r[i] = __builtin_bit_cast(uint32_t, h);
+  }
+  return r;
 }
 
 // One code dword of the documented layout from 16 code bytes (code k in the
@@ -82,18 +95,20 @@ __device__ inline uint32_t pack16(uint32_t w0, uint32_t w1, uint32_t w2, uint32_
 
 template <int G>
 struct WriteShared {
-  uint8_t xs[PAGE * XSTR];               // the page's rows, all heads of the chunk (bf16)
-  uint8_t codes[WHC][PAGE * D];          // K: [token][channel]; V: [channel][token]
+  uint8_t xs[PAGE * XSTR];                  // the page's rows, all heads of the chunk (bf16)
+  uint8_t codes[2][WHC][PAGE * D];          // per buffer -- K: [token][channel]; V: [channel][token]
   float pmin[WHC][PAGE][4], pmax[WHC][PAGE][4];  // per wave (groups wider than a wave)
-  float sz[WHC][PAGE][D / G][2];
+  float sz[2][WHC][PAGE][D / G][2];         // per buffer: (scale, zero) after fp16 rounding
+  int bad[2][4];                            // per page parity: a wave met a bad ring page id
 };
 
 // Where the token at position p (uniform) comes from: the ring (it leaves
 // the recent window now) or the new rows (src: rows of head h0, starting at
 // the request's first new row).  Sets row/stride (elements between heads) or
-// leaves row null (inactive); bad: its ring page id is out of range.
-__device__ inline void token_source(const WriteArgs &a, int b, int tensor, int h0, int L0, int hlo, int hhi, int p,
-                                    const uint16_t *src, const uint16_t *&row, int &stride, bool &bad) {
+// leaves row null (inactive); bad: its ring page id is out of range.  ids:
+// lane 16 + i holds bf16_pt[b][i] (the request's BF16 page ids, loaded once).
+__device__ inline void token_source(const WriteArgs &a, int ids, int tensor, int h0, int L0, int hlo, int hhi,
+                                    int p, const uint16_t *src, const uint16_t *&row, int &stride, bool &bad) {
   const oscar_layer_cache &c = a.c;
   const int hkv = c.n_kv_heads;
   row = nullptr;
@@ -105,7 +120,7 @@ __device__ inline void token_source(const WriteArgs &a, int b, int tensor, int h
     stride = D;
   } else {
     const int slot = p % N_RECENT;
-    const int bp = c.bf16_pt[b * BF16_PT + 1 + slot / PAGE];
+    const int bp = __builtin_amdgcn_readlane(ids, 16 + 1 + slot / PAGE);
     if (bp >= 0 && bp < c.n_bf16_pages) {
       row = c.bf16 + ((int64_t(bp) * hkv + h0) * 2 + tensor) * (PAGE * D) + (slot % PAGE) * D;
       stride = 2 * PAGE * D;
@@ -118,18 +133,22 @@ __device__ inline void token_source(const WriteArgs &a, int b, int tensor, int h
 // One workgroup (4 waves) per (request, WPP consecutive history pages, K|V,
 // up to WHC KV heads).  Per page: the rows that enter history in this call
 // -- new tokens, or ring tokens pushed out of the recent window -- are staged
-// in LDS for all heads of the chunk (the next page's rows are loaded into
-// registers meanwhile), rotated on the matrix cores: Y = X R with X the bf16
-// rows (exact) and R split into three bf16 pieces (b1 + b2 + b3 = R to
-// 2^-24), each piece accumulated in its own fp32 accumulator and added at
-// the end (small pieces last), so the error stays within the fp32
-// dot-product bound.  Wave w computes output channels 32w .. 32w+31 of every
-// head; then clip, per-(token, group) fp16 zero = min and scale =
-// (max - min)/3 (row reductions across the 16 lanes of a tile row, then
-// across the waves of a group wider than 32), codes, and the packed store in
-// the documented layout.
+// in LDS for all heads of the chunk as fp16 (exact in fp16's normal range),
+// rotated on the matrix cores: Y = X R_hi + 2^-11 X R_lo with R_hi = fp16(R)
+// and R_lo = fp16(2^11 (R - R_hi)), each product accumulated in fp32, so the
+// error stays within the fp32 dot-product bound.  Wave w computes output channels 32w ..
+// 32w+31 of every head; then clip, per-(token, group) fp16 zero = min and
+// scale = (max - min)/3 (reductions across the lanes of a token, then across
+// the waves of a group wider than 32), codes, and the packed store in the
+// documented layout.
+//
+// Pipeline: page j's rows are staged from registers loaded during page j-1;
+// page j+1's loads are issued right after staging, then page j-1's codes and
+// meta (kept in the other LDS buffer) are stored, then page j is computed.
+// The next wait for loads comes at page j+1's staging, a whole page later.
+// All page ids of the workgroup are loaded once, into lanes of one register.
 template <int G>
-__global__ void __launch_bounds__(256) write_hist_kernel(WriteArgs a) {
+__device__ __forceinline__ void write_hist_body(const WriteArgs &a) {
   constexpr int NG = D / G, WPG = G / 32;
   const int b = blockIdx.z;
   const int tensor = blockIdx.y & 1, hc = blockIdx.y >> 1;
@@ -157,19 +176,32 @@ __global__ void __launch_bounds__(256) write_hist_kernel(WriteArgs a) {
   if (N_SINK + PAGE * jfirst >= hhi) return;
   const int jend = min((hhi - N_SINK + PAGE - 1) / PAGE, jfirst + WPP);
   __shared__ __attribute__((aligned(16))) WriteShared<G> sh;
-  __shared__ int bad_w[4];
   const float clip = a.clip[tensor];
   const int r_a = lane & 15, qd = lane >> 4;  // MFMA: token row (A) / column (B, D); k sub-block / row group
 
+  // page ids: lane i < WPP holds hist_pt[b][jfirst + i] (-1 past the table),
+  // lane 16 + i holds bf16_pt[b][i]
+  int ids = -1;
+  if (lane < WPP) {
+    const int j = jfirst + lane;
+    if (j < jend && j < c.hist_pt_stride) ids = c.hist_pt[int64_t(b) * c.hist_pt_stride + j];
+  } else if (lane >= 16 && lane < 16 + BF16_PT) {
+    ids = c.bf16_pt[b * BF16_PT + lane - 16];
+  }
+
   // ---- the next page's rows, into registers: thread piece k covers token
-  // wave + 4k, head (lane / 16), bytes 16 (lane % 16) .. of its row
+  // wave + 4k, head (lane / 16), bytes 16 (lane % 16) .. of its row.  Pieces
+  // without a row load a valid address and are zeroed when staged (bit k of
+  // xon), so no wait follows the loads.
   u32x4w xr[4];
+  uint32_t xon = 0;
   bool bad_next = false;
   // the request's new rows of head h0 (a uniform base: scalar address math)
   const uint16_t *src0 = a.src[tensor] + (int64_t(__builtin_amdgcn_readfirstlane(a.cu_new[b])) * hkv + h0) * D;
   auto load_page = [&](int j) {
     const int pos0 = N_SINK + PAGE * j;
     bool bad = false;
+    uint32_t on_bits = 0;
     const int hh = lane >> 4, c16 = lane & 15;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -177,167 +209,43 @@ __global__ void __launch_bounds__(256) write_hist_kernel(WriteArgs a) {
       const uint16_t *row;
       int stride;
       bool bd;
-      token_source(a, b, tensor, h0, L0, hlo, hhi, p, src0, row, stride, bd);
+      token_source(a, ids, tensor, h0, L0, hlo, hhi, p, src0, row, stride, bd);
       bad |= bd;
       const bool on = row != nullptr && hh < nh;
       const uint16_t *src = on ? row + hh * stride + 8 * c16 : src0;
-      const u32x4w v = *reinterpret_cast<const u32x4w *>(src);
-      xr[k] = on ? v : u32x4w{0u, 0u, 0u, 0u};
+      xr[k] = *reinterpret_cast<const u32x4w *>(src);
+      on_bits |= uint32_t(on) << k;
     }
+    xon = on_bits;
     bad_next = bad;
   };
   load_page(jfirst);
 
-  // B operands: R pieces for this wave's two column tiles; lane l holds
-  // R[i][j] for j = 32 wave + 16 ct + l%16, i = 32 kk + 8 (l/16) .. + 7
-  bf16x8w rb[2][4][3];
+  // A operands: the fp16 high part and the 2^11-scaled fp16 low part of R
+  // for this wave's two tiles of output channels; lane l holds R[i][j] for
+  // j = 32 wave + 16 ct + l%16, i = 32 kk + 8 (l/16) .. + 7
+  f16x8w rh[2][4], rl[2][4];
   {
-    const uint16_t *RB = reinterpret_cast<const uint16_t *>(a.forms[tensor] + FORM_RT_B);
+    const uint16_t *RH = reinterpret_cast<const uint16_t *>(a.forms[tensor] + FORM_RT_HI);
+    const uint16_t *RL = reinterpret_cast<const uint16_t *>(a.forms[tensor] + FORM_RT_LO);
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int pc = 0; pc < 3; ++pc) {
-          const int jj = 32 * wave + 16 * ct + r_a, ii = 32 * kk + 8 * qd;
-          const u32x4w u = *reinterpret_cast<const u32x4w *>(RB + pc * D * D + jj * D + ii);
-          rb[ct][kk][pc] = __builtin_bit_cast(bf16x8w, u);
-        }
+      for (int kk = 0; kk < 4; ++kk) {
+        const int jj = 32 * wave + 16 * ct + r_a, ii = 32 * kk + 8 * qd;
+        rh[ct][kk] = __builtin_bit_cast(f16x8w, *reinterpret_cast<const u32x4w *>(RH + jj * D + ii));
+        rl[ct][kk] = __builtin_bit_cast(f16x8w, *reinterpret_cast<const u32x4w *>(RL + jj * D + ii));
+      }
   }
 
-  for (int jv = jfirst; jv < jend; ++jv) {
-    const int j = __builtin_amdgcn_readfirstlane(jv);  // uniform (kept scalar)
-    const int pos0 = N_SINK + PAGE * j;
-    // ---- stage this page's rows (the previous page is done with the LDS)
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int t = wave + 4 * k, hh = lane >> 4, c16 = lane & 15;
-      *reinterpret_cast<u32x4w *>(sh.xs + t * XSTR + hh * (D * 2) + 16 * c16) = xr[k];
-    }
-    if (lane == 0) bad_w[wave] = __ballot(bad_next) != 0;
-    __syncthreads();
-    const bool page_bad = __builtin_amdgcn_readfirstlane(bad_w[0] | bad_w[1] | bad_w[2] | bad_w[3]) != 0;
-    if (j + 1 < jend) load_page(j + 1);  // in flight during this page
-    bool skip = page_bad;
-    int pid = -1;
-    if (j >= c.hist_pt_stride) {
-      skip = true;
-    } else {
-      pid = __builtin_amdgcn_readfirstlane(c.hist_pt[int64_t(b) * c.hist_pt_stride + j]);
-      if (pid < 0 || pid >= c.n_hist_pages) skip = true;
-    }
-    if (skip) {  // uniform: nothing of this page is written
-      if (tid == 0) flag_status(c.status, OSCAR_STATUS_BAD_PAGE);
-      continue;
-    }
-
-    // ---- rotate, clip, per-(token, wave) min / max; then scale, zero and
-    // codes (at once when a group is the wave's 32 channels, else after the
-    // waves of each group have combined their partials through LDS).  The
-    // product is taken transposed, Y^T = R^T X^T (A: rows of R^T, B: the
-    // staged rows), so that lane (n = l%16, qd = l/16) holds token n,
-    // channels 32 wave + 16 ct + 4 qd + i: the per-token work runs once per
-    // lane, and a token's 32 channels of the wave are in the four lanes
-    // n + 16 qd.
-    const int g = (32 * wave) / G;
-    const int tok = r_a;
-    auto rotate = [&](int hh, f32x4w (&yc)[2], float &lo, float &hi) {
-      bf16x8w xb[4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        xb[kk] = __builtin_bit_cast(
-            bf16x8w, *reinterpret_cast<const u32x4w *>(sh.xs + tok * XSTR + hh * (D * 2) + 2 * (32 * kk + 8 * qd)));
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        // smallest pieces first, one accumulator: twelve fp32 accumulation
-        // steps stay well inside the fp32 dot-product error bound
-        f32x4w acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int pc = 2; pc >= 0; --pc)
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rb[ct][kk][pc], xb[kk], acc, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) yc[ct][i] = __builtin_amdgcn_fmed3f(acc[i], -clip, clip);
-      }
-      lo = fminf(fminf(fminf(yc[0][0], yc[0][1]), fminf(yc[0][2], yc[0][3])),
-                 fminf(fminf(yc[1][0], yc[1][1]), fminf(yc[1][2], yc[1][3])));
-      hi = fmaxf(fmaxf(fmaxf(yc[0][0], yc[0][1]), fmaxf(yc[0][2], yc[0][3])),
-                 fmaxf(fmaxf(yc[1][0], yc[1][1]), fmaxf(yc[1][2], yc[1][3])));
-      lo = fminf(lo, __shfl_xor(lo, 16));
-      hi = fmaxf(hi, __shfl_xor(hi, 16));
-      lo = fminf(lo, __shfl_xor(lo, 32));
-      hi = fmaxf(hi, __shfl_xor(hi, 32));
-    };
-    auto quantise = [&](int hh, const f32x4w (&yc)[2], float lo, float hi) {
-      // (max - min) / 3 by a product with fp32(1/3) and the code step by a
-      // hardware reciprocal: each within two fp32 ulps, far inside the error
-      // bound of the rotated values they come from
-      const float sq = __half2float(__float2half_rn((hi - lo) * (1.0f / 3.0f)));
-      const float zq = __half2float(__float2half_rn(lo));
-      if (qd == 0 && wave % WPG == 0) {
-        sh.sz[hh][tok][g][0] = sq;
-        sh.sz[hh][tok][g][1] = zq;
-      }
-      const float inv = sq > 0.f ? __builtin_amdgcn_rcpf(sq) : 0.f;
-      const float zi = zq * inv;
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        uint32_t cd[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          cd[i] = uint32_t(rintf(__builtin_amdgcn_fmed3f(fmaf(yc[ct][i], inv, -zi), 0.f, 3.f)));
-        const int ch = 32 * wave + 16 * ct + 4 * qd;
-        if (tensor == 0) {
-          *reinterpret_cast<uint32_t *>(&sh.codes[hh][tok * D + ch]) = cd[0] | (cd[1] << 8) | (cd[2] << 16) | (cd[3] << 24);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sh.codes[hh][(ch + i) * PAGE + tok] = uint8_t(cd[i]);
-        }
-      }
-    };
-    if constexpr (WPG == 1) {
-#pragma unroll
-      for (int hh = 0; hh < WHC; ++hh) {
-        f32x4w yc[2];
-        float lo, hi;
-        rotate(hh, yc, lo, hi);
-        quantise(hh, yc, lo, hi);
-      }
-    } else {
-      f32x4w yc[WHC][2];
-      float lo[WHC], hi[WHC];
-#pragma unroll
-      for (int hh = 0; hh < WHC; ++hh) {
-        rotate(hh, yc[hh], lo[hh], hi[hh]);
-        if (qd == 0) {
-          sh.pmin[hh][tok][wave] = lo[hh];
-          sh.pmax[hh][tok][wave] = hi[hh];
-        }
-      }
-      __syncthreads();
-      const int w0 = (wave / WPG) * WPG;
-#pragma unroll
-      for (int hh = 0; hh < WHC; ++hh) {
-        float l2 = sh.pmin[hh][tok][w0], h2 = sh.pmax[hh][tok][w0];
-#pragma unroll
-        for (int w = 1; w < WPG; ++w) {
-          l2 = fminf(l2, sh.pmin[hh][tok][w0 + w]);
-          h2 = fmaxf(h2, sh.pmax[hh][tok][w0 + w]);
-        }
-        quantise(hh, yc[hh], l2, h2);
-      }
-    }
-    __syncthreads();
-
-    // ---- packed store: 128 code dwords per head, then the meta entries.
-    // K dword (token t, q, d): channels 64d + 8q .. +7 and 64d + 32 + 8q ..
-    // +7 of token t; V dword (q, m, d): tokens 4q .. 4q+3 of channels
-    // 16 (4d + r) + m, r < 4.  Rows below hlo are already in history and are
-    // kept (read-modify-write); rows at or past hhi are not yet and may be
-    // overwritten.
-    const int hbb = hist_block_bytes(G);
+  // ---- packed store of a computed page (codes and meta in LDS buffer buf):
+  // 128 code dwords per head, then the meta entries.  K dword (token t, q,
+  // d): channels 64d + 8q .. +7 and 64d + 32 + 8q .. +7 of token t; V dword
+  // (q, m, d): tokens 4q .. 4q+3 of channels 16 (4d + r) + m, r < 4.  Rows
+  // below hlo are already in history and are kept (read-modify-write); rows
+  // at or past hhi are not yet and may be overwritten.
+  const int hbb = hist_block_bytes(G);
+  auto store_page = [&](int pid, int pos0, int buf) {
     for (int e = tid; e < nh * 128; e += 256) {
       const int hh = e >> 7, w = e & 127;
       const int ln = w >> 1, d = w & 1, lq = ln >> 4, la = ln & 15;
@@ -345,7 +253,7 @@ __global__ void __launch_bounds__(256) write_hist_kernel(WriteArgs a) {
       if (tensor == 0) {
         const int t = la, p = pos0 + t;
         if (p < hlo || p >= hhi) continue;
-        const uint8_t *src = &sh.codes[hh][t * D + 64 * d + 8 * lq];
+        const uint8_t *src = &sh.codes[buf][hh][t * D + 64 * d + 8 * lq];
         const u32x2w x0 = *reinterpret_cast<const u32x2w *>(src);
         const u32x2w x1 = *reinterpret_cast<const u32x2w *>(src + 32);
         reinterpret_cast<uint32_t *>(blk + k_codes_off(G))[w] = pack16(x0[0], x0[1], x1[0], x1[1]);
@@ -361,7 +269,7 @@ __global__ void __launch_bounds__(256) write_hist_kernel(WriteArgs a) {
         uint32_t x[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          x[r] = *reinterpret_cast<const uint32_t *>(&sh.codes[hh][(16 * (4 * d + r) + la) * PAGE + 4 * lq]) & on;
+          x[r] = *reinterpret_cast<const uint32_t *>(&sh.codes[buf][hh][(16 * (4 * d + r) + la) * PAGE + 4 * lq]) & on;
         const uint32_t word = pack16(x[0], x[1], x[2], x[3]);
         uint32_t *dst = reinterpret_cast<uint32_t *>(blk + v_codes_off(G)) + w;
         if (keep) {
@@ -378,9 +286,153 @@ __global__ void __launch_bounds__(256) write_hist_kernel(WriteArgs a) {
       if (p < hlo || p >= hhi) continue;
       uint8_t *blk = c.hist + (int64_t(pid) * hkv + h0 + hh) * hbb;
       __half2 *meta = reinterpret_cast<__half2 *>(blk + (tensor ? v_meta_off(G) : k_meta_off(G)));
-      meta[PAGE * gg + t] = __halves2half2(__float2half_rn(sh.sz[hh][t][gg][0]), __float2half_rn(sh.sz[hh][t][gg][1]));
+      meta[PAGE * gg + t] =
+          __halves2half2(__float2half_rn(sh.sz[buf][hh][t][gg][0]), __float2half_rn(sh.sz[buf][hh][t][gg][1]));
     }
+  };
+
+  int prev_pid = -1, prev_pos0 = 0, buf = 0;
+  for (int jv = jfirst; jv < jend; ++jv) {
+    const int j = __builtin_amdgcn_readfirstlane(jv);  // uniform (kept scalar)
+    const int pos0 = N_SINK + PAGE * j;
+    // ---- stage this page's rows (the previous page's barrier freed xs)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int t = wave + 4 * k, hh = lane >> 4, c16 = lane & 15;
+      const u32x4w v = ((xon >> k) & 1u) ? bf16x8_to_f16x8(xr[k]) : u32x4w{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4w *>(sh.xs + t * XSTR + hh * (D * 2) + 16 * c16) = v;
+    }
+    if (lane == 0) sh.bad[j & 1][wave] = __ballot(bad_next) != 0;
+    __syncthreads();
+    const bool page_bad =
+        __builtin_amdgcn_readfirstlane(sh.bad[j & 1][0] | sh.bad[j & 1][1] | sh.bad[j & 1][2] | sh.bad[j & 1][3]) != 0;
+    if (j + 1 < jend) load_page(j + 1);  // in flight during this page
+    if (prev_pid >= 0) store_page(prev_pid, prev_pos0, buf ^ 1);
+    const int pid = __builtin_amdgcn_readlane(ids, j - jfirst);
+    const bool skip = page_bad || pid < 0 || pid >= c.n_hist_pages;  // uniform
+    if (skip) {
+      if (tid == 0) flag_status(c.status, OSCAR_STATUS_BAD_PAGE);
+    } else {
+      // ---- rotate, clip, per-(token, wave) min / max; then scale, zero and
+      // codes (at once when a group is the wave's 32 channels, else after
+      // the waves of each group have combined their partials through LDS).
+      // The product is taken transposed, Y^T = R^T X^T (A: rows of R^T, B:
+      // the staged rows), so that lane (n = l%16, qd = l/16) holds token n,
+      // channels 32 wave + 16 ct + 4 qd + i: the per-token work runs once
+      // per lane, and a token's 32 channels of the wave are in the four
+      // lanes n + 16 qd.
+      const int g = (32 * wave) / G;
+      const int tok = r_a;
+      auto rotate = [&](int hh, f32x4w (&yc)[2], float &lo, float &hi) {
+        f16x8w xb[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          xb[kk] = __builtin_bit_cast(
+              f16x8w, *reinterpret_cast<const u32x4w *>(sh.xs + tok * XSTR + hh * (D * 2) + 2 * (32 * kk + 8 * qd)));
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          // fp16 x fp16 products are exact in the fp32 accumulators; the low
+          // part carries R to ~2^-23 relative, so y stays within the fp32
+          // dot-product error bound
+          f32x4w ah = {0.f, 0.f, 0.f, 0.f}, al = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            ah = __builtin_amdgcn_mfma_f32_16x16x32_f16(rh[ct][kk], xb[kk], ah, 0, 0, 0);
+            al = __builtin_amdgcn_mfma_f32_16x16x32_f16(rl[ct][kk], xb[kk], al, 0, 0, 0);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            yc[ct][i] = __builtin_amdgcn_fmed3f(fmaf(al[i], 1.0f / 2048.0f, ah[i]), -clip, clip);
+        }
+        lo = fminf(fminf(fminf(yc[0][0], yc[0][1]), fminf(yc[0][2], yc[0][3])),
+                   fminf(fminf(yc[1][0], yc[1][1]), fminf(yc[1][2], yc[1][3])));
+        hi = fmaxf(fmaxf(fmaxf(yc[0][0], yc[0][1]), fmaxf(yc[0][2], yc[0][3])),
+                   fmaxf(fmaxf(yc[1][0], yc[1][1]), fmaxf(yc[1][2], yc[1][3])));
+        lo = lanes4_min(lo);
+        hi = lanes4_max(hi);
+      };
+      auto quantise = [&](int hh, const f32x4w (&yc)[2], float lo, float hi) {
+        // (max - min) / 3 by a product with fp32(1/3) and the code step by a
+        // hardware reciprocal: each within two fp32 ulps, far inside the
+        // error bound of the rotated values they come from
+        const float sq = __half2float(__float2half_rn((hi - lo) * (1.0f / 3.0f)));
+        const float zq = __half2float(__float2half_rn(lo));
+        if (qd == 0 && wave % WPG == 0) {
+          sh.sz[buf][hh][tok][g][0] = sq;
+          sh.sz[buf][hh][tok][g][1] = zq;
+        }
+        const float inv = sq > 0.f ? __builtin_amdgcn_rcpf(sq) : 0.f;
+        const float zi = zq * inv;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          // code = round-half-even of the clamped step: adding 1.5 * 2^23
+          // rounds to an integer (ulp 1) and leaves it in the low byte
+          uint32_t cd[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            cd[i] = __float_as_uint(__builtin_amdgcn_fmed3f(fmaf(yc[ct][i], inv, -zi), 0.f, 3.f) + 12582912.0f);
+          const int ch = 32 * wave + 16 * ct + 4 * qd;
+          if (tensor == 0) {
+            *reinterpret_cast<uint32_t *>(&sh.codes[buf][hh][tok * D + ch]) =
+                __builtin_amdgcn_perm(__builtin_amdgcn_perm(cd[3], cd[2], 0x0c0c0400u),
+                                      __builtin_amdgcn_perm(cd[1], cd[0], 0x0c0c0400u), 0x05040100u);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sh.codes[buf][hh][(ch + i) * PAGE + tok] = uint8_t(cd[i]);
+          }
+        }
+      };
+      if constexpr (WPG == 1) {
+#pragma unroll
+        for (int hh = 0; hh < WHC; ++hh) {
+          f32x4w yc[2];
+          float lo, hi;
+          rotate(hh, yc, lo, hi);
+          quantise(hh, yc, lo, hi);
+        }
+      } else {
+        f32x4w yc[WHC][2];
+        float lo[WHC], hi[WHC];
+#pragma unroll
+        for (int hh = 0; hh < WHC; ++hh) {
+          rotate(hh, yc[hh], lo[hh], hi[hh]);
+          if (qd == 0) {
+            sh.pmin[hh][tok][wave] = lo[hh];
+            sh.pmax[hh][tok][wave] = hi[hh];
+          }
+        }
+        __syncthreads();
+        const int w0 = (wave / WPG) * WPG;
+#pragma unroll
+        for (int hh = 0; hh < WHC; ++hh) {
+          float l2 = sh.pmin[hh][tok][w0], h2 = sh.pmax[hh][tok][w0];
+#pragma unroll
+          for (int w = 1; w < WPG; ++w) {
+            l2 = fminf(l2, sh.pmin[hh][tok][w0 + w]);
+            h2 = fmaxf(h2, sh.pmax[hh][tok][w0 + w]);
+          }
+          quantise(hh, yc[hh], l2, h2);
+        }
+      }
+    }
+    // this page's codes are complete and nobody reads xs any more
+    __syncthreads();
+    prev_pid = skip ? -1 : pid;
+    prev_pos0 = pos0;
+    if (!skip) buf ^= 1;
   }
+  if (prev_pid >= 0) store_page(prev_pid, prev_pos0, buf ^ 1);
+}
+
+// G = 32 fits three waves per SIMD without spills (one group per wave: no
+// min / max partials held across a barrier); wider groups keep two.
+template <int G>
+__global__ void __launch_bounds__(256) write_hist_kernel(WriteArgs a) {
+  write_hist_body<G>(a);
+}
+template <>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) write_hist_kernel<32>(WriteArgs a) {
+  write_hist_body<32>(a);
 }
 
 // New tokens that land in the sink or the recent ring: raw bf16 copies.
