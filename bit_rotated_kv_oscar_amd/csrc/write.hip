@@ -32,9 +32,12 @@ struct WriteArgs {
 // Request b's rows cu_new[b]..cu_new[b+1]-1 must lie in [0, total_tokens) and
 // number at most max_new (the grid covers no more); otherwise the request is
 // skipped and flagged.
+// The values are read into scalars, so the checks and everything that
+// follows from them stay uniform branches.
 __device__ inline bool request_ok(const WriteArgs &a, int b, int &L0, int &n) {
-  const int c0 = a.cu_new[b], c1 = a.cu_new[b + 1];
-  L0 = a.len_before[b];
+  const int c0 = __builtin_amdgcn_readfirstlane(a.cu_new[b]);
+  const int c1 = __builtin_amdgcn_readfirstlane(a.cu_new[b + 1]);
+  L0 = __builtin_amdgcn_readfirstlane(a.len_before[b]);
   n = c1 - c0;
   return c0 >= 0 && c1 >= c0 && int64_t(c1) <= a.total_tokens && n <= a.max_new && L0 >= 0 &&
          int64_t(L0) + n < (int64_t(1) << 30);
@@ -150,9 +153,13 @@ __device__ inline void token_source(const WriteArgs &a, int ids, int tensor, int
 template <int G>
 __device__ __forceinline__ void write_hist_body(const WriteArgs &a) {
   constexpr int NG = D / G, WPG = G / 32;
-  const int b = blockIdx.z;
-  const int tensor = blockIdx.y & 1, hc = blockIdx.y >> 1;
-  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
+  // workgroup and work-item ids through the builtins: in an inlined body,
+  // blockIdx / threadIdx may become calls that return vector registers
+  const int bx = __builtin_amdgcn_workgroup_id_x(), by = __builtin_amdgcn_workgroup_id_y();
+  const int b = __builtin_amdgcn_workgroup_id_z();
+  const int tensor = by & 1, hc = by >> 1;
+  const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const oscar_layer_cache &c = a.c;
   const int hkv = c.n_kv_heads;
   const int h0 = hc * WHC;
@@ -161,18 +168,14 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a) {
 
   int L0, n;
   if (!request_ok(a, b, L0, n)) {
-    if (tid == 0 && blockIdx.x == 0 && blockIdx.y == 0) flag_status(c.status, OSCAR_STATUS_BAD_LEN);
+    if (tid == 0 && bx == 0 && by == 0) flag_status(c.status, OSCAR_STATUS_BAD_LEN);
     return;
   }
-  // uniform values loaded through vector loads: scalar from here on, so that
-  // the page loop and its branches are scalar
-  L0 = __builtin_amdgcn_readfirstlane(L0);
-  n = __builtin_amdgcn_readfirstlane(n);
   const int L = L0 + n;
   const int hlo = max(N_SINK, L0 - N_RECENT);  // first position entering history
   const int hhi = L - N_RECENT;                 // one past the last
   if (hhi <= hlo) return;
-  const int jfirst = (hlo - N_SINK) / PAGE + blockIdx.x * WPP;
+  const int jfirst = (hlo - N_SINK) / PAGE + bx * WPP;
   if (N_SINK + PAGE * jfirst >= hhi) return;
   const int jend = min((hhi - N_SINK + PAGE - 1) / PAGE, jfirst + WPP);
   __shared__ __attribute__((aligned(16))) WriteShared<G> sh;
