@@ -96,12 +96,16 @@ __device__ inline uint32_t pack16(uint32_t w0, uint32_t w1, uint32_t w2, uint32_
   return p0 | (p2 << 2) | (p4 << 4) | (p6 << 6);
 }
 
+// K code rows in LDS: 136 bytes apart (34 dwords), so the 16 tokens of a
+// row-group write and read distinct banks
+constexpr int KROW = D + 8;
+
 template <int G>
 struct WriteShared {
   uint8_t xs[PAGE * XSTR];                  // the page's rows, all heads of the chunk (bf16)
-  uint8_t codes[2][WHC][PAGE * D];          // per buffer -- K: [token][channel]; V: [channel][token]
+  uint8_t codes[2][WHC][PAGE * KROW];       // per buffer -- K: [token][channel] (rows KROW bytes apart); V: [channel][token]
   float pmin[WHC][PAGE][4], pmax[WHC][PAGE][4];  // per wave (groups wider than a wave)
-  float sz[2][WHC][PAGE][D / G][2];         // per buffer: (scale, zero) after fp16 rounding
+  float sz[2][WHC][D / G][PAGE][2];         // per buffer: (scale, zero) after fp16 rounding
   int bad[2][4];                            // per page parity: a wave met a bad ring page id
 };
 
@@ -150,14 +154,15 @@ __device__ inline void token_source(const WriteArgs &a, int ids, int tensor, int
 // meta (kept in the other LDS buffer) are stored, then page j is computed.
 // The next wait for loads comes at page j+1's staging, a whole page later.
 // All page ids of the workgroup are loaded once, into lanes of one register.
-template <int G>
-__device__ __forceinline__ void write_hist_body(const WriteArgs &a) {
+template <int G, int TENSOR>
+__device__ __forceinline__ void write_hist_body(const WriteArgs &a, WriteShared<G> &sh) {
   constexpr int NG = D / G, WPG = G / 32;
   // workgroup and work-item ids through the builtins: in an inlined body,
   // blockIdx / threadIdx may become calls that return vector registers
   const int bx = __builtin_amdgcn_workgroup_id_x(), by = __builtin_amdgcn_workgroup_id_y();
   const int b = __builtin_amdgcn_workgroup_id_z();
-  const int tensor = by & 1, hc = by >> 1;
+  constexpr int tensor = TENSOR;  // 0: K, 1: V (the low bit of blockIdx.y)
+  const int hc = by >> 1;
   const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const oscar_layer_cache &c = a.c;
@@ -178,8 +183,7 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a) {
   const int jfirst = (hlo - N_SINK) / PAGE + bx * WPP;
   if (N_SINK + PAGE * jfirst >= hhi) return;
   const int jend = min((hhi - N_SINK + PAGE - 1) / PAGE, jfirst + WPP);
-  __shared__ __attribute__((aligned(16))) WriteShared<G> sh;
-  const float clip = a.clip[tensor];
+  const float clip_s = a.clip[tensor] * 2048.0f;  // the clip in the accumulators' 2^11 scale
   const int r_a = lane & 15, qd = lane >> 4;  // MFMA: token row (A) / column (B, D); k sub-block / row group
 
   // page ids: lane i < WPP holds hist_pt[b][jfirst + i] (-1 past the table),
@@ -193,19 +197,21 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a) {
   }
 
   // ---- the next page's rows, into registers: thread piece k covers token
-  // wave + 4k, head (lane / 16), bytes 16 (lane % 16) .. of its row.  Pieces
-  // without a row load a valid address and are zeroed when staged (bit k of
-  // xon), so no wait follows the loads.
+  // wave + 4k, head (lane / 16), bytes 16 (lane % 16) .. of its row.  Each
+  // row is read through a buffer resource whose size covers exactly the
+  // chunk's heads of that row (none when the position has no row): lanes
+  // past it read zeros, with no select and no wait after the loads.
   u32x4w xr[4];
-  uint32_t xon = 0;
   bool bad_next = false;
   // the request's new rows of head h0 (a uniform base: scalar address math)
   const uint16_t *src0 = a.src[tensor] + (int64_t(__builtin_amdgcn_readfirstlane(a.cu_new[b])) * hkv + h0) * D;
+  // lane byte offsets in a new row (heads D elements apart) and in a ring
+  // row (heads 2 PAGE D elements apart)
+  const uint32_t off_new = uint32_t((lane >> 4) * (D * 2) + 16 * (lane & 15));
+  const uint32_t off_ring = uint32_t((lane >> 4) * (2 * PAGE * D * 2) + 16 * (lane & 15));
   auto load_page = [&](int j) {
     const int pos0 = N_SINK + PAGE * j;
     bool bad = false;
-    uint32_t on_bits = 0;
-    const int hh = lane >> 4, c16 = lane & 15;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int p = __builtin_amdgcn_readfirstlane(pos0 + wave + 4 * k);
@@ -214,19 +220,21 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a) {
       bool bd;
       token_source(a, ids, tensor, h0, L0, hlo, hhi, p, src0, row, stride, bd);
       bad |= bd;
-      const bool on = row != nullptr && hh < nh;
-      const uint16_t *src = on ? row + hh * stride + 8 * c16 : src0;
-      xr[k] = *reinterpret_cast<const u32x4w *>(src);
-      on_bits |= uint32_t(on) << k;
+      const bool ring = stride != D;
+      const int nrec = row == nullptr ? 0 : (nh - 1) * stride * 2 + D * 2;
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(row ? row : src0), 0, nrec, 0x00020000);
+      xr[k] = __builtin_bit_cast(u32x4w, __builtin_amdgcn_raw_buffer_load_b128(rs, ring ? off_ring : off_new, 0, 0));
     }
-    xon = on_bits;
     bad_next = bad;
   };
   load_page(jfirst);
 
-  // A operands: the fp16 high part and the 2^11-scaled fp16 low part of R
-  // for this wave's two tiles of output channels; lane l holds R[i][j] for
-  // j = 32 wave + 16 ct + l%16, i = 32 kk + 8 (l/16) .. + 7
+  // A operands: 2^11 times the fp16 high part and the 2^11-scaled fp16 low
+  // part of R (both exact scalings) for this wave's two tiles of output
+  // channels; lane l holds R[i][j] for j = 32 wave + 16 ct + l%16,
+  // i = 32 kk + 8 (l/16) .. + 7.  The products then land in one accumulator
+  // as 2^11 y.
   f16x8w rh[2][4], rl[2][4];
   {
     const uint16_t *RH = reinterpret_cast<const uint16_t *>(a.forms[tensor] + FORM_RT_HI);
@@ -236,7 +244,8 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int jj = 32 * wave + 16 * ct + r_a, ii = 32 * kk + 8 * qd;
-        rh[ct][kk] = __builtin_bit_cast(f16x8w, *reinterpret_cast<const u32x4w *>(RH + jj * D + ii));
+        rh[ct][kk] = __builtin_bit_cast(f16x8w, *reinterpret_cast<const u32x4w *>(RH + jj * D + ii)) *
+                     (_Float16)2048.0f;
         rl[ct][kk] = __builtin_bit_cast(f16x8w, *reinterpret_cast<const u32x4w *>(RL + jj * D + ii));
       }
   }
@@ -248,15 +257,19 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a) {
   // below hlo are already in history and are kept (read-modify-write); rows
   // at or past hhi are not yet and may be overwritten.
   const int hbb = hist_block_bytes(G);
+  // Heads are wave-uniform (waves 2i, 2i+1 take head 2k + i of the codes,
+  // wave w head w of the meta), so block addresses stay scalar.
   auto store_page = [&](int pid, int pos0, int buf) {
-    for (int e = tid; e < nh * 128; e += 256) {
-      const int hh = e >> 7, w = e & 127;
+    for (int hb = 0; hb < nh; hb += 2) {
+      const int hh = hb + (wave >> 1);
+      if (hh >= nh) break;
+      const int w = tid & 127;
       const int ln = w >> 1, d = w & 1, lq = ln >> 4, la = ln & 15;
       uint8_t *blk = c.hist + (int64_t(pid) * hkv + h0 + hh) * hbb;
-      if (tensor == 0) {
+      if constexpr (tensor == 0) {
         const int t = la, p = pos0 + t;
         if (p < hlo || p >= hhi) continue;
-        const uint8_t *src = &sh.codes[buf][hh][t * D + 64 * d + 8 * lq];
+        const uint8_t *src = &sh.codes[buf][hh][t * KROW + 64 * d + 8 * lq];
         const u32x2w x0 = *reinterpret_cast<const u32x2w *>(src);
         const u32x2w x1 = *reinterpret_cast<const u32x2w *>(src + 32);
         reinterpret_cast<uint32_t *>(blk + k_codes_off(G))[w] = pack16(x0[0], x0[1], x1[0], x1[1]);
@@ -283,14 +296,15 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a) {
         }
       }
     }
-    for (int e = tid; e < nh * PAGE * NG; e += 256) {
-      const int hh = e / (PAGE * NG), t = (e / NG) % PAGE, gg = e % NG;
+    if (wave < nh && lane < PAGE * NG) {
+      const int hh = wave, t = lane / NG, gg = lane % NG;
       const int p = pos0 + t;
-      if (p < hlo || p >= hhi) continue;
-      uint8_t *blk = c.hist + (int64_t(pid) * hkv + h0 + hh) * hbb;
-      __half2 *meta = reinterpret_cast<__half2 *>(blk + (tensor ? v_meta_off(G) : k_meta_off(G)));
-      meta[PAGE * gg + t] =
-          __halves2half2(__float2half_rn(sh.sz[buf][hh][t][gg][0]), __float2half_rn(sh.sz[buf][hh][t][gg][1]));
+      if (p >= hlo && p < hhi) {
+        uint8_t *blk = c.hist + (int64_t(pid) * hkv + h0 + hh) * hbb;
+        __half2 *meta = reinterpret_cast<__half2 *>(blk + (tensor ? v_meta_off(G) : k_meta_off(G)));
+        meta[PAGE * gg + t] =
+            __halves2half2(__float2half_rn(sh.sz[buf][hh][gg][t][0]), __float2half_rn(sh.sz[buf][hh][gg][t][1]));
+      }
     }
   };
 
@@ -302,7 +316,7 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int t = wave + 4 * k, hh = lane >> 4, c16 = lane & 15;
-      const u32x4w v = ((xon >> k) & 1u) ? bf16x8_to_f16x8(xr[k]) : u32x4w{0u, 0u, 0u, 0u};
+      const u32x4w v = bf16x8_to_f16x8(xr[k]);
       *reinterpret_cast<u32x4w *>(sh.xs + t * XSTR + hh * (D * 2) + 16 * c16) = v;
     }
     if (lane == 0) sh.bad[j & 1][wave] = __ballot(bad_next) != 0;
@@ -326,7 +340,13 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a) {
       // lanes n + 16 qd.
       const int g = (32 * wave) / G;
       const int tok = r_a;
-      auto rotate = [&](int hh, f32x4w (&yc)[2], float &lo, float &hi) {
+      // byte selectors of the quad transpose: first swap 2-byte halves with
+      // lane ^ 2, then single bytes with lane ^ 1 (perm: bytes 0-3 own, 4-7
+      // the partner's)
+      const uint32_t selA = (tok & 2) ? 0x03020706u : 0x05040100u;
+      const uint32_t selB = (tok & 1) ? 0x03070105u : 0x06020400u;
+      float szv[WHC][2];  // (scale, zero) of each head's group; stored after the heads
+      auto products = [&](int hh, f32x4w (&acc2)[2]) {
         f16x8w xb[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
@@ -334,25 +354,29 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a) {
               f16x8w, *reinterpret_cast<const u32x4w *>(sh.xs + tok * XSTR + hh * (D * 2) + 2 * (32 * kk + 8 * qd)));
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          // fp16 x fp16 products are exact in the fp32 accumulators; the low
-          // part carries R to ~2^-23 relative, so y stays within the fp32
-          // dot-product error bound
-          f32x4w ah = {0.f, 0.f, 0.f, 0.f}, al = {0.f, 0.f, 0.f, 0.f};
+          // fp16 x fp16 products are exact in fp32; the small low-part
+          // products are summed first, so the accumulator's rounding stays
+          // within the fp32 dot-product bound of the high part's sum, and R
+          // is carried to 2^-22 relative
+          f32x4w acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            ah = __builtin_amdgcn_mfma_f32_16x16x32_f16(rh[ct][kk], xb[kk], ah, 0, 0, 0);
-            al = __builtin_amdgcn_mfma_f32_16x16x32_f16(rl[ct][kk], xb[kk], al, 0, 0, 0);
-          }
+          for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(rl[ct][kk], xb[kk], acc, 0, 0, 0);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            yc[ct][i] = __builtin_amdgcn_fmed3f(fmaf(al[i], 1.0f / 2048.0f, ah[i]), -clip, clip);
+          for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(rh[ct][kk], xb[kk], acc, 0, 0, 0);
+          acc2[ct] = acc;
         }
+      };
+      auto finish = [&](const f32x4w (&acc2)[2], f32x4w (&yc)[2], float &lo, float &hi) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) yc[ct][i] = __builtin_amdgcn_fmed3f(acc2[ct][i], -clip_s, clip_s);
         lo = fminf(fminf(fminf(yc[0][0], yc[0][1]), fminf(yc[0][2], yc[0][3])),
                    fminf(fminf(yc[1][0], yc[1][1]), fminf(yc[1][2], yc[1][3])));
         hi = fmaxf(fmaxf(fmaxf(yc[0][0], yc[0][1]), fmaxf(yc[0][2], yc[0][3])),
                    fmaxf(fmaxf(yc[1][0], yc[1][1]), fmaxf(yc[1][2], yc[1][3])));
-        lo = lanes4_min(lo);
-        hi = lanes4_max(hi);
+        lo = lanes4_min(lo) * (1.0f / 2048.0f);
+        hi = lanes4_max(hi) * (1.0f / 2048.0f);
       };
       auto quantise = [&](int hh, const f32x4w (&yc)[2], float lo, float hi) {
         // (max - min) / 3 by a product with fp32(1/3) and the code step by a
@@ -360,12 +384,11 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a) {
         // error bound of the rotated values they come from
         const float sq = __half2float(__float2half_rn((hi - lo) * (1.0f / 3.0f)));
         const float zq = __half2float(__float2half_rn(lo));
-        if (qd == 0 && wave % WPG == 0) {
-          sh.sz[buf][hh][tok][g][0] = sq;
-          sh.sz[buf][hh][tok][g][1] = zq;
-        }
+        szv[hh][0] = sq;
+        szv[hh][1] = zq;
         const float inv = sq > 0.f ? __builtin_amdgcn_rcpf(sq) : 0.f;
         const float zi = zq * inv;
+        const float inv_s = inv * (1.0f / 2048.0f);  // for the 2^11-scaled values
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
           // code = round-half-even of the clamped step: adding 1.5 * 2^23
@@ -373,32 +396,57 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a) {
           uint32_t cd[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            cd[i] = __float_as_uint(__builtin_amdgcn_fmed3f(fmaf(yc[ct][i], inv, -zi), 0.f, 3.f) + 12582912.0f);
+            cd[i] = __float_as_uint(__builtin_amdgcn_fmed3f(fmaf(yc[ct][i], inv_s, -zi), 0.f, 3.f) + 12582912.0f);
           const int ch = 32 * wave + 16 * ct + 4 * qd;
-          if (tensor == 0) {
-            *reinterpret_cast<uint32_t *>(&sh.codes[buf][hh][tok * D + ch]) =
-                __builtin_amdgcn_perm(__builtin_amdgcn_perm(cd[3], cd[2], 0x0c0c0400u),
-                                      __builtin_amdgcn_perm(cd[1], cd[0], 0x0c0c0400u), 0x05040100u);
+          // the four codes (channels ch .. ch+3 of the lane's token) as bytes
+          const uint32_t pk = __builtin_amdgcn_perm(__builtin_amdgcn_perm(cd[3], cd[2], 0x0c0c0400u),
+                                                    __builtin_amdgcn_perm(cd[1], cd[0], 0x0c0c0400u), 0x05040100u);
+          if constexpr (tensor == 0) {
+            *reinterpret_cast<uint32_t *>(&sh.codes[buf][hh][tok * KROW + ch]) = pk;
           } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sh.codes[buf][hh][(ch + i) * PAGE + tok] = uint8_t(cd[i]);
+            // 4 x 4 byte transpose within each quad of lanes (tokens 4q ..
+            // 4q+3): afterwards lane 4q + r holds channel ch + r of the
+            // quad's four tokens, one dword of the [channel][token] layout
+            const uint32_t xa = uint32_t(__builtin_amdgcn_mov_dpp(int(pk), 0x4E, 0xF, 0xF, false));  // lane ^ 2
+            const uint32_t pa = __builtin_amdgcn_perm(xa, pk, selA);
+            const uint32_t xb = uint32_t(__builtin_amdgcn_mov_dpp(int(pa), 0xB1, 0xF, 0xF, false));  // lane ^ 1
+            const uint32_t pb = __builtin_amdgcn_perm(xb, pa, selB);
+            *reinterpret_cast<uint32_t *>(&sh.codes[buf][hh][(ch + (tok & 3)) * PAGE + (tok & ~3)]) = pb;
           }
         }
       };
       if constexpr (WPG == 1) {
+        // the next head's products are issued before this head's vector
+        // work, so the matrix cores run while the lanes quantise
+        f32x4w acc_cur[2], acc_next[2];
+        products(0, acc_cur);
 #pragma unroll
         for (int hh = 0; hh < WHC; ++hh) {
+          if (hh + 1 < WHC) products(hh + 1, acc_next);
           f32x4w yc[2];
           float lo, hi;
-          rotate(hh, yc, lo, hi);
+          finish(acc_cur, yc, lo, hi);
           quantise(hh, yc, lo, hi);
+          if (hh + 1 < WHC) {
+            acc_cur[0] = acc_next[0];
+            acc_cur[1] = acc_next[1];
+            // spread the next head's sixteen products over this head's
+            // vector instructions
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            }
+          }
         }
       } else {
         f32x4w yc[WHC][2];
         float lo[WHC], hi[WHC];
 #pragma unroll
         for (int hh = 0; hh < WHC; ++hh) {
-          rotate(hh, yc[hh], lo[hh], hi[hh]);
+          f32x4w acc2[2];
+          products(hh, acc2);
+          finish(acc2, yc[hh], lo[hh], hi[hh]);
           if (qd == 0) {
             sh.pmin[hh][tok][wave] = lo[hh];
             sh.pmax[hh][tok][wave] = hi[hh];
@@ -417,6 +465,13 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a) {
           quantise(hh, yc[hh], l2, h2);
         }
       }
+      if (qd == 0 && wave % WPG == 0) {
+#pragma unroll
+        for (int hh = 0; hh < WHC; ++hh) {
+          sh.sz[buf][hh][g][tok][0] = szv[hh][0];
+          sh.sz[buf][hh][g][tok][1] = szv[hh][1];
+        }
+      }
     }
     // this page's codes are complete and nobody reads xs any more
     __syncthreads();
@@ -429,13 +484,23 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a) {
 
 // G = 32 fits three waves per SIMD without spills (one group per wave: no
 // min / max partials held across a barrier); wider groups keep two.
+// K and V workgroups (the low bit of blockIdx.y) run separate instances of
+// the body, so the tensor's branches are resolved at compile time.
 template <int G>
 __global__ void __launch_bounds__(256) write_hist_kernel(WriteArgs a) {
-  write_hist_body<G>(a);
+  __shared__ __attribute__((aligned(16))) WriteShared<G> sh;
+  if (__builtin_amdgcn_workgroup_id_y() & 1)
+    write_hist_body<G, 1>(a, sh);
+  else
+    write_hist_body<G, 0>(a, sh);
 }
 template <>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) write_hist_kernel<32>(WriteArgs a) {
-  write_hist_body<32>(a);
+  __shared__ __attribute__((aligned(16))) WriteShared<32> sh;
+  if (__builtin_amdgcn_workgroup_id_y() & 1)
+    write_hist_body<32, 1>(a, sh);
+  else
+    write_hist_body<32, 0>(a, sh);
 }
 
 // New tokens that land in the sink or the recent ring: raw bf16 copies.
