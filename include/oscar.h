@@ -183,7 +183,10 @@ OSCAR_API int oscar_calibrate_rotation(const uint16_t *q_cal, const uint16_t *k_
  * ring tokens pushed out by this call, are rotated by R (x*R), clamped to
  * [-clip, clip], split into groups of G consecutive rotated channels, and
  * stored as codes c = clamp(rint((x - z)/s), 0, 3) with z = fp16(min),
- * s = fp16((max - min)/3) (all codes 0 when s == 0).
+ * s = fp16((max - min)/3) (all codes 0 when s == 0).  The rotation keeps
+ * fp32 dot-product accuracy with fp16 operands on the matrix cores: entries
+ * of k_new / v_new beyond the fp16 range (|x| > 65504) are saturated to
+ * +-65504 before rotating.
  * cu_new: device int32 [batch+1]; len_before: device int32 [batch].
  * max_new: host upper bound of n_b (sizes the grid).  History pages a call
  * writes must not be shared with another live request (caller's duty). */
