@@ -47,7 +47,7 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", choices=["bs1", "bs64", "write"], default="bs1")
+    p.add_argument("--workload", choices=["bs1", "bs64", "write", "28x100k"], default="bs1")
     p.add_argument("--layers", type=int, default=None, help="override the layer count (testing only)")
     p.add_argument("--seed", type=int, default=1)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -71,7 +71,8 @@ def parse_args():
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 DOMINANT = {"bs1": ("attend_kernel", ["decode_int2.hip", "attn_common.h", "common.h", "kernels.h"]),
             "bs64": ("attend_kernel", ["decode_int2.hip", "attn_common.h", "common.h", "kernels.h"]),
-            "write": ("write_hist_kernel", ["write.hip", "common.h", "kernels.h"])}
+            "write": ("write_hist_kernel", ["write.hip", "common.h", "kernels.h"]),
+            "28x100k": ("attend_kernel", ["decode_int2.hip", "attn_common.h", "common.h", "kernels.h"])}
 
 
 def kernel_sources_sha(workload):
@@ -138,6 +139,11 @@ WORKLOADS = {
                  layers=36, hq=32, hkv=8, G=64, batch=64, len_lo=8192, len_hi=32768),
     "write": dict(name="qwen3-4b-shaped fused KV write at prefill, 36 layers, 8 prompts x 32768 tokens, G 32",
                   layers=36, hq=32, hkv=8, G=32, batch=8, len_lo=32768, len_hi=32768),
+    # ~104 GB of INT2 cache (64 layers x 1.63 GB) on one GPU; its all-BF16
+    # copy (734 GB) does not fit, so this workload has no in-run BF16 ratio
+    "28x100k": dict(name="qwen3-32b-shaped attention decode, 64 layers, 28 requests x 100000-token context, G 128",
+                    layers=64, hq=64, hkv=8, G=128, batch=28, len_lo=100000, len_hi=100000,
+                    bf16_bytes_note="all-BF16 cache of the same tokens: 734 GB, beyond one GPU's 288 GB"),
 }
 WRITE_METRIC = "INT2 fused KV write GB/s (% HBM peak) + tokens/s, prefill 8 x 32K, 36 layers"
 
@@ -278,6 +284,8 @@ def main():
         cu = torch.from_numpy(np.concatenate([[0], np.cumsum(start_lens)]).astype(np.int32)).to(dev)
         oscar.write_kv(ly.cache, ly.rk, ly.rv, k, v, cu, torch.zeros(B, dtype=torch.int32, device=dev),
                        int(start_lens.max()))
+        if "bf16_bytes_note" in W:
+            torch.cuda.synchronize()   # free the bulk tokens before the next layer draws its own
         # per-step inputs (the same new token and query every step)
         ly.k_new = synth.kv_device(synth.device_generator(args.seed, l, synth.S_NEW_K), B, ld.outliers, dev)
         ly.v_new = synth.kv_device(synth.device_generator(args.seed, l, synth.S_NEW_V), B, ld.outliers, dev)
@@ -285,7 +293,7 @@ def main():
         ly.out = torch.empty((B, hq, HEAD_DIM), dtype=torch.float32, device=dev)
         ly.ws = torch.zeros(oscar.decode_workspace_bytes(B, hq, hkv, max_len), dtype=torch.uint8, device=dev)
         layers.append(ly)
-        if not args.no_bf16:
+        if not args.no_bf16 and "bf16_bytes_note" not in W:
             # the same tokens, all raw bf16, for the in-run BF16 baseline
             bl = Layer()
             n_pages = [(int(L) + 15) // 16 for L in final_lens]
@@ -455,6 +463,8 @@ def main():
     }
     if bf16:
         line.update(bf16)
+    elif "bf16_bytes_note" in W:
+        line["bf16_baseline"] = "not run: " + W["bf16_bytes_note"]
     print(json.dumps(line))
 
 

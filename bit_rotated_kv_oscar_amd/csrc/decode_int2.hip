@@ -439,7 +439,7 @@ __device__ inline void build_q_issue(const StepArgs &a, int b, int hk, int tid, 
 // Workgroup-wide, from the loads above: q' = q R_K and the A-operand
 // fragment block of the score product in frag_lds (layout of Rows).
 template <int GQA, int NG>
-__device__ void build_q(const StepArgs &a, int tid, QWork<GQA, NG> &w, uint32_t *frag_lds, const QLoads<GQA> &ql) {
+__device__ __forceinline__ void build_q(const StepArgs &a, int tid, QWork<GQA, NG> &w, uint32_t *frag_lds, const QLoads<GQA> &ql) {
   using R = Rows<GQA, NG>;
   constexpr int G = R::G, SEG = QWork<GQA, NG>::SEG, NT = AW * 64;
   const int jr = tid >> 3, qq = tid & 7;
