@@ -52,6 +52,8 @@ SIGNATURES = [
     ("oscar_calibrate_rotation", ctypes.c_int,
      [c_p, c_p, c_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
       c_p, c_p, c_p, c_p, c_p]),
+    ("oscar_clip_threshold", ctypes.c_int,
+     [c_p, ctypes.c_int64, c_p, ctypes.c_double, c_p, c_p]),
     ("oscar_write_kv", ctypes.c_int,
      [ctypes.POINTER(LayerCacheC), ctypes.POINTER(RotationC), ctypes.POINTER(RotationC),
       c_p, c_p, c_p, c_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, c_p]),

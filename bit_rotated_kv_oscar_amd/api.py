@@ -211,6 +211,20 @@ def profile_events(before: "torch.cuda.Event | None", after: "torch.cuda.Event |
     check(load().oscar_profile_events(h0, h1))
 
 
+def clip_threshold(x_cal: torch.Tensor, R: torch.Tensor, clip_quantile: float = 0.999) -> float:
+    """oscar_clip_threshold: the clip of a caller-chosen rotation R (float64
+    CPU [128, 128]) from bf16 calibration vectors [..., 128] on the device."""
+    dev = x_cal.device
+    _need(x_cal, "x_cal", (torch.bfloat16,), dev)
+    R = R.detach().to(torch.float64).contiguous().cpu()
+    if R.shape != (HEAD_DIM, HEAD_DIM):
+        raise ValueError("R must be [128, 128]")
+    out = ctypes.c_float(0)
+    check(load().oscar_clip_threshold(_ptr(x_cal), x_cal.numel() // HEAD_DIM, _ptr(R), float(clip_quantile),
+                                      ctypes.byref(out), _stream(dev)))
+    return out.value
+
+
 def calibrate_rotation(q_cal: torch.Tensor, k_cal: torch.Tensor, v_cal: torch.Tensor,
                        clip_quantile: float = 0.999):
     """oscar_calibrate_rotation: bf16 [N, Hq, 128], [N, Hkv, 128] x2 on the device ->

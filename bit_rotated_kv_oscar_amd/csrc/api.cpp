@@ -298,4 +298,27 @@ int oscar_calibrate_rotation(const uint16_t *q_cal, const uint16_t *k_cal, const
   return OSCAR_OK;
 }
 
+int oscar_clip_threshold(const uint16_t *x_cal, int64_t n_vec, const double *R, double clip_quantile,
+                         float *clip, oscar_stream_t stream) {
+  if (!x_cal || !R || !clip) return fail(OSCAR_EINVAL, "clip_threshold: NULL argument");
+  if (n_vec < 1 || n_vec > (int64_t(1) << 24)) return fail(OSCAR_EINVAL, "n_vec %lld outside [1, 2^24]", (long long)n_vec);
+  if (!(clip_quantile > 0.0 && clip_quantile <= 1.0)) return fail(OSCAR_EINVAL, "clip_quantile must be in (0, 1]");
+  if (int rc = check_device()) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int D = oscar::D;
+  double *Rd = nullptr, *y = nullptr;
+  std::vector<double> absv(size_t(n_vec) * D);
+  hipError_t e = hipMalloc(&Rd, D * D * sizeof(double));
+  if (e == hipSuccess) e = hipMalloc(&y, absv.size() * sizeof(double));
+  if (e == hipSuccess) e = hipMemcpyAsync(Rd, R, D * D * sizeof(double), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = oscar::launch_calib_rotate_abs(x_cal, n_vec, Rd, y, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(absv.data(), y, absv.size() * sizeof(double), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (Rd) (void)hipFree(Rd);
+  if (y) (void)hipFree(y);
+  if (e != hipSuccess) return hip_fail(e, "clip_threshold");
+  *clip = float(oscar::quantile_linear(absv, clip_quantile));
+  return OSCAR_OK;
+}
+
 }  // extern "C"

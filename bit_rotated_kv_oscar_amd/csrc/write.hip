@@ -386,17 +386,26 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a, WriteShared<
         const float zq = __half2float(__float2half_rn(lo));
         szv[hh][0] = sq;
         szv[hh][1] = zq;
-        const float inv = sq > 0.f ? __builtin_amdgcn_rcpf(sq) : 0.f;
-        const float zi = zq * inv;
-        const float inv_s = inv * (1.0f / 2048.0f);  // for the 2^11-scaled values
+        // scale and zero in the accumulators' 2^11 scale (exact)
+        const float ss = sq * 2048.0f, zs = zq * 2048.0f;
+        const float inv = sq > 0.f ? __builtin_amdgcn_rcpf(ss) : 0.f;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          // code = round-half-even of the clamped step: adding 1.5 * 2^23
-          // rounds to an integer (ulp 1) and leaves it in the low byte
+          // step t = (x - z) / s: x - z is exact for exactly representable
+          // inputs, and one residual correction of the reciprocal product
+          // makes t exact whenever the true quotient is a float, so a value
+          // exactly halfway between two levels rounds like the fp64 rule
+          // (x - z = 1.5 s happens with unrotated bf16 inputs).  Then code =
+          // round-half-even of the clamped step: adding 1.5 * 2^23 rounds to
+          // an integer (ulp 1) and leaves it in the low byte.
           uint32_t cd[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            cd[i] = __float_as_uint(__builtin_amdgcn_fmed3f(fmaf(yc[ct][i], inv_s, -zi), 0.f, 3.f) + 12582912.0f);
+          for (int i = 0; i < 4; ++i) {
+            const float d = yc[ct][i] - zs;
+            const float t0 = d * inv;
+            const float t = fmaf(fmaf(-t0, ss, d), inv, t0);
+            cd[i] = __float_as_uint(__builtin_amdgcn_fmed3f(t, 0.f, 3.f) + 12582912.0f);
+          }
           const int ch = 32 * wave + 16 * ct + 4 * qd;
           // the four codes (channels ch .. ch+3 of the lane's token) as bytes
           const uint32_t pk = __builtin_amdgcn_perm(__builtin_amdgcn_perm(cd[3], cd[2], 0x0c0c0400u),

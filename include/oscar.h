@@ -12,9 +12,10 @@
  * Every pointer argument is a plain pointer; "device" means memory the HIP
  * runtime can address on the current device, "host" means CPU memory.
  * The caller owns every buffer.  The library allocates device memory only in
- * oscar_calibrate_rotation (freed before it returns) and keeps no state
- * besides a thread-local error string.  All calls except
- * oscar_calibrate_rotation are asynchronous on the given stream.
+ * oscar_calibrate_rotation and oscar_clip_threshold (freed before they
+ * return) and keeps no state besides a thread-local error string.  All
+ * calls except oscar_calibrate_rotation and oscar_clip_threshold are
+ * asynchronous on the given stream.
  *
  * Return value: OSCAR_OK (0) or a negative code; oscar_last_error() then
  * holds a message.  Arguments are validated on the host before any launch;
@@ -150,6 +151,21 @@ OSCAR_API size_t oscar_rotation_bytes(void);
  * part plus a 2^11-scaled fp16 low part for the matrix cores).
  * forms: device buffer of oscar_rotation_bytes(). */
 OSCAR_API int oscar_prepare_rotation(const double *R, void *forms, oscar_stream_t stream);
+
+/* Clip threshold of one fixed rotation ([nl]/[fr] §2.2.A "clipping
+ * thresholds"): the clip_quantile quantile (linear interpolation between
+ * order statistics) of |x R| over every vector and channel of x_cal, the
+ * same rule oscar_calibrate_rotation applies to its own R_K and R_V.  It
+ * serves rotations chosen by the caller, such as the Hadamard-only
+ * (QuaRot-style) R = H P_br and the identity of plain INT2 that the pages
+ * compare OSCAR with ([abs]; [nl]/[fr] §2.1).
+ * x_cal: device bf16 [n_vec][128]; R: host fp64 [128][128] (row-vector
+ * convention, x R); clip: host float out.  Allocates and frees temporary
+ * device memory and synchronises the stream.  Errors: OSCAR_EINVAL for
+ * NULL pointers, n_vec outside [1, 2^24] or clip_quantile outside (0, 1];
+ * OSCAR_EHIP for runtime failures. */
+OSCAR_API int oscar_clip_threshold(const uint16_t *x_cal, int64_t n_vec, const double *R,
+                         double clip_quantile, float *clip, oscar_stream_t stream);
 
 /* Offline calibration ([nl] §2.2.A, [fr] §2.2.A, [abs]):
  *   C_Q = mean over tokens and query heads of the outer product q q^T;

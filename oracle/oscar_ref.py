@@ -188,6 +188,41 @@ def calibrate(q, k, v, clip_quantile: float = 0.999) -> dict:
 
 
 # --------------------------------------------------------------------------
+# rotation variants and distortion diagnostics ([abs]: OSCAR against
+# Hadamard-only, QuaRot-style INT2; [nl]/[fr] §2.1: data-oblivious Hadamard
+# rotations and naive INT2, whose outliers dominate the quantisation scale)
+# --------------------------------------------------------------------------
+
+def hadamard_only_rotation(n: int = D) -> np.ndarray:
+    """The data-oblivious rotation R = H P_br: OSCAR's composition without a
+    covariance eigenbasis (U = I)."""
+    return hadamard(n) @ bitrev_permutation(n)
+
+
+def identity_rotation(n: int = D) -> np.ndarray:
+    """No rotation: plain per-token INT2 of the raw channels."""
+    return np.eye(n)
+
+
+def logit_distortion(q: np.ndarray, K: np.ndarray, K_hat: np.ndarray) -> float:
+    """Query-weighted logit distortion: the mean over query heads h and tokens
+    t of (q_h . (K[t, g(h)] - K_hat[t, g(h)]))^2 with g(h) = h // (Hq/Hkv),
+    the error the attention logits see.  q: [Hq][128]; K, K_hat: [L][Hkv][128]."""
+    hq, hkv = q.shape[0], K.shape[1]
+    dK = K - K_hat
+    total = 0.0
+    for h in range(hq):
+        g = h // (hq // hkv)
+        total += float(((dK[:, g, :] @ q[h]) ** 2).sum())
+    return total / (hq * K.shape[0])
+
+
+def relative_l2(x: np.ndarray, ref: np.ndarray) -> float:
+    """||x - ref||_2 / ||ref||_2 over all entries."""
+    return float(np.linalg.norm(np.asarray(x, np.float64) - ref) / np.linalg.norm(ref))
+
+
+# --------------------------------------------------------------------------
 # the INT2 quantiser  ([nl]/[fr] §1 four levels, §2.2.B rotate + clip + INT2)
 # --------------------------------------------------------------------------
 

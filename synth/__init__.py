@@ -9,7 +9,9 @@ recipe follows the workload descriptions used throughout this repository:
   drawn without replacement; the same channels serve calibration and cache
   tokens.
 * Q ~ N(0, diag(lam)) with lam_i = 10**u_i, u_i ~ U(-2, 1) (log-uniform in
-  [0.01, 10]); one lam per layer, shared by its query heads.
+  [0.01, 10]); one lam per layer, shared by its query heads.  The optional
+  dense variant draws Q ~ N(0, B diag(lam) B^T) with B a seeded random
+  orthogonal basis (correlated query channels).
 * Every float is rounded to bf16 (round to nearest even from fp32) and handed
   over as uint16 bit patterns.
 * Every stream has its own seed: numpy PCG64 seeded by
@@ -27,6 +29,7 @@ N_RECENT = 128
 # stream ids of SeedSequence([base, layer, stream])
 S_SIGMA, S_OUTLIER, S_CAL_Q, S_CAL_K, S_CAL_V = 0, 1, 2, 3, 4
 S_CACHE_K, S_CACHE_V, S_DEC_Q, S_PAGES, S_LENS, S_NEW_K, S_NEW_V = 5, 6, 7, 8, 9, 10, 11
+S_BASIS, S_EVAL_Q = 12, 13
 
 
 def rng(base_seed: int, layer: int, stream: int) -> np.random.Generator:
@@ -64,23 +67,35 @@ def kv_f32(g: np.random.Generator, n: int, outliers: np.ndarray) -> np.ndarray:
     return x
 
 
-def q_f32(g: np.random.Generator, n: int, n_q_heads: int, lam: np.ndarray) -> np.ndarray:
+def q_f32(g: np.random.Generator, n: int, n_q_heads: int, lam: np.ndarray, basis=None) -> np.ndarray:
     z = g.standard_normal((n, n_q_heads, HEAD_DIM), dtype=np.float32)
-    return z * np.sqrt(lam).astype(np.float32)
+    y = z * np.sqrt(lam).astype(np.float32)
+    if basis is not None:
+        y = (y.astype(np.float64) @ basis.T).astype(np.float32)
+    return y
+
+
+def random_basis(base_seed: int, layer: int) -> np.ndarray:
+    """A seeded random orthogonal 128 x 128 matrix (the Q factor of a Gaussian
+    matrix, columns signed by the diagonal of R)."""
+    a = rng(base_seed, layer, S_BASIS).standard_normal((HEAD_DIM, HEAD_DIM))
+    qm, r = np.linalg.qr(a)
+    return qm * np.sign(np.diag(r))
 
 
 class LayerData:
     """All seeded host inputs of one layer of one workload."""
 
-    def __init__(self, base_seed: int, layer: int, n_q_heads: int, n_kv_heads: int):
+    def __init__(self, base_seed: int, layer: int, n_q_heads: int, n_kv_heads: int, dense_q: bool = False):
         self.base_seed, self.layer = base_seed, layer
         self.hq, self.hkv = n_q_heads, n_kv_heads
         self.lam = layer_lambda(base_seed, layer)
         self.outliers = outlier_channels(base_seed, layer, n_kv_heads)
+        self.basis = random_basis(base_seed, layer) if dense_q else None
 
     def calibration(self, n_tokens: int):
         """(q, k, v) bf16 bits: [N][Hq][128], [N][Hkv][128], [N][Hkv][128]."""
-        q = bf16_bits(q_f32(rng(self.base_seed, self.layer, S_CAL_Q), n_tokens, self.hq, self.lam))
+        q = bf16_bits(q_f32(rng(self.base_seed, self.layer, S_CAL_Q), n_tokens, self.hq, self.lam, self.basis))
         k = bf16_bits(kv_f32(rng(self.base_seed, self.layer, S_CAL_K), n_tokens, self.outliers))
         v = bf16_bits(kv_f32(rng(self.base_seed, self.layer, S_CAL_V), n_tokens, self.outliers))
         return q, k, v
@@ -92,7 +107,7 @@ class LayerData:
         return k, v
 
     def decode_q(self, batch: int, stream: int = S_DEC_Q):
-        return bf16_bits(q_f32(rng(self.base_seed, self.layer, stream), batch, self.hq, self.lam))
+        return bf16_bits(q_f32(rng(self.base_seed, self.layer, stream), batch, self.hq, self.lam, self.basis))
 
 
 def hist_pages_needed(seq_len: int) -> int:

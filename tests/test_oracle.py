@@ -640,3 +640,90 @@ def test_decode_brute_force_with_history():
     for h in range(2):
         ref = _brute_attention(qf[h].tolist(), Ks, Vs, 0.1)
         np.testing.assert_allclose(out[0, h], ref, rtol=1e-11, atol=1e-11)
+
+
+# ------------------------------------------------------- rotation variants
+
+
+def test_sorted_diagonal_query_covariance_gives_hadamard_only():
+    # q_n = sqrt(N lambda_n) e_n makes C_Q exactly diag(lambda); with distinct
+    # descending lambda the eigenbasis is the identity (largest entry
+    # positive), so OSCAR's R_K is the data-oblivious H P_br
+    lam = np.sort(10.0 ** RNG.uniform(-2, 1, 128))[::-1]
+    q = np.zeros((128, 1, 128))
+    q[np.arange(128), 0, np.arange(128)] = np.sqrt(128 * lam)
+    C = o.query_covariance(q)
+    assert np.abs(C - np.diag(lam)).max() < 1e-12
+    R = o.compose_rotation(o.eigenbasis(C))
+    assert np.abs(R - o.hadamard_only_rotation()).max() < 1e-12
+    assert np.abs(o.hadamard_only_rotation().T @ o.hadamard_only_rotation() - np.eye(128)).max() < 1e-14
+    assert np.array_equal(o.identity_rotation(), np.eye(128))
+
+
+def test_hadamard_only_equalises_only_diagonal_importance():
+    # for a diagonal C_Q every Hadamard column sees tr(C_Q)/128; a dense C_Q
+    # breaks that for H P_br but not for OSCAR's U_Q H P_br
+    lam = 10.0 ** RNG.uniform(-2, 1, 128)
+    Hp = o.hadamard_only_rotation()
+    d = np.diag(Hp.T @ np.diag(lam) @ Hp)
+    assert np.abs(d - lam.sum() / 128).max() < 1e-12
+    B = np.linalg.qr(RNG.standard_normal((128, 128)))[0]
+    C = B @ np.diag(lam) @ B.T
+    d_h = np.diag(Hp.T @ C @ Hp)
+    R = o.compose_rotation(o.eigenbasis(C))
+    d_o = np.diag(R.T @ C @ R)
+    assert np.abs(d_o - np.trace(C) / 128).max() < 1e-11
+    assert d_h.max() / d_h.min() > 1.5
+
+
+def test_logit_distortion_hand_values():
+    q = np.zeros((2, 128))
+    q[0, :2] = [1.0, 2.0]
+    q[1, 1] = 1.0
+    K = RNG.standard_normal((2, 1, 128))
+    dK = np.zeros((2, 1, 128))
+    dK[0, 0, :2] = [3.0, -1.0]     # head 0: (3 - 2)^2 = 1, head 1: 1
+    dK[1, 0, 1] = 2.0              # head 0: 4^2 = 16, head 1: 2^2 = 4
+    assert o.logit_distortion(q, K, K) == 0.0
+    assert abs(o.logit_distortion(q, K, K - dK) - (1 + 1 + 16 + 4) / 4) < 1e-12
+    # GQA: query heads 0, 1 read KV head 0, heads 2, 3 KV head 1
+    q4 = np.zeros((4, 128))
+    q4[:, 0] = [1.0, 2.0, 3.0, 4.0]
+    K2 = np.zeros((1, 2, 128))
+    Kh = K2.copy()
+    Kh[0, 0, 0] = -1.0
+    Kh[0, 1, 0] = -2.0
+    assert abs(o.logit_distortion(q4, K2, Kh) - (1 + 4 + 36 + 64) / 4) < 1e-12
+
+
+def test_logit_distortion_rotation_invariant():
+    # (q R) . (dk R) = q . dk for orthogonal R: the diagnostic reads the same
+    # in either basis, and a transposed operand breaks the identity
+    R = np.linalg.qr(RNG.standard_normal((128, 128)))[0]
+    q = RNG.standard_normal((8, 128))
+    K = RNG.standard_normal((40, 2, 128))
+    Kh = K + 0.1 * RNG.standard_normal(K.shape)
+    a = o.logit_distortion(q, K, Kh)
+    b = o.logit_distortion(q @ R, K @ R, Kh @ R)
+    assert abs(a - b) < 1e-12 * a
+    assert abs(o.logit_distortion(q @ R.T, K @ R, Kh @ R) - a) > 1e-3 * a
+
+
+def test_relative_l2_hand_value():
+    assert abs(o.relative_l2(np.array([3.0, 4.0]), np.array([0.0, 5.0])) - math.sqrt(10) / 5) < 1e-15
+
+
+def test_identity_rotation_outliers_dominate_int2_error():
+    # [nl]/[fr] §2.1: a x20 outlier channel sets the range of its group under
+    # plain INT2; spreading it over the channels (any orthogonal mixing such
+    # as H P_br) shrinks the per-group range and the reconstruction error
+    g = np.random.default_rng(77)
+    x = g.standard_normal((256, 128))
+    x[:, 5] *= 20.0
+    err = {}
+    for name, R in (("identity", o.identity_rotation()), ("hadamard", o.hadamard_only_rotation())):
+        clip = o.clip_threshold(x, R, 0.999)
+        qq = o.quantize(x, R, clip, 32)
+        xh = o.dequantize(qq["codes"], qq["scale"], qq["zero"], 32) @ R.T
+        err[name] = o.relative_l2(xh, x)
+    assert err["hadamard"] < 0.8 * err["identity"], err
