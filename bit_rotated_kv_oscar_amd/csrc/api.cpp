@@ -243,7 +243,7 @@ int oscar_calibrate_rotation(const uint16_t *q_cal, const uint16_t *k_cal, const
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int D = oscar::D;
   const int64_t nq = n_tokens * n_q_heads, nkv = n_tokens * n_kv_heads;
-  double *cov = nullptr, *o = nullptr, *Rd = nullptr, *y = nullptr;
+  double *cov = nullptr, *o = nullptr, *Rd = nullptr, *y = nullptr, *part = nullptr;
   int rc = OSCAR_OK;
   std::vector<double> cq(D * D), cs(D * D);
   hipError_t e;
@@ -252,6 +252,7 @@ int oscar_calibrate_rotation(const uint16_t *q_cal, const uint16_t *k_cal, const
     if (o) (void)hipFree(o);
     if (Rd) (void)hipFree(Rd);
     if (y) (void)hipFree(y);
+    if (part) (void)hipFree(part);
   };
 #define CHECK_HIP(expr, where)       \
   do {                               \
@@ -266,9 +267,10 @@ int oscar_calibrate_rotation(const uint16_t *q_cal, const uint16_t *k_cal, const
   CHECK_HIP(hipMalloc(&o, size_t(nq) * D * sizeof(double)), "hipMalloc");
   CHECK_HIP(hipMalloc(&Rd, D * D * sizeof(double)), "hipMalloc");
   CHECK_HIP(hipMalloc(&y, size_t(nkv) * D * sizeof(double)), "hipMalloc");
-  CHECK_HIP(oscar::launch_calib_outer(q_cal, nullptr, nq, cov, s), "calib C_Q");
+  CHECK_HIP(hipMalloc(&part, oscar::calib_outer_part_bytes()), "hipMalloc");
+  CHECK_HIP(oscar::launch_calib_outer(q_cal, nullptr, nq, cov, part, s), "calib C_Q");
   CHECK_HIP(oscar::launch_calib_attention(q_cal, k_cal, v_cal, n_tokens, n_q_heads, n_kv_heads, o, s), "calib attention");
-  CHECK_HIP(oscar::launch_calib_outer(nullptr, o, nq, cov + D * D, s), "calib C_S");
+  CHECK_HIP(oscar::launch_calib_outer(nullptr, o, nq, cov + D * D, part, s), "calib C_S");
   CHECK_HIP(hipMemcpyAsync(cq.data(), cov, D * D * sizeof(double), hipMemcpyDeviceToHost, s), "copy C_Q");
   CHECK_HIP(hipMemcpyAsync(cs.data(), cov + D * D, D * D * sizeof(double), hipMemcpyDeviceToHost, s), "copy C_S");
   CHECK_HIP(hipStreamSynchronize(s), "sync");

@@ -46,30 +46,73 @@ hipError_t launch_prepare_rotation(const double *R, void *forms, hipStream_t s) 
 
 // ---------------------------------------------------------------- moments
 
-// cov[i][j] = sum_n x[n][i] x[n][j]; one thread per (i, j), fixed summation
-// order (deterministic).  Exactly one of xb (bf16) / xd (fp64) is non-null.
-__global__ void __launch_bounds__(256) outer_sum_kernel(const uint16_t *__restrict__ xb,
-                                                        const double *__restrict__ xd,
-                                                        int64_t n_vec, double *__restrict__ cov) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  const int i = e / D, j = e % D;
-  double acc = 0.0;
-  if (xb) {
-    for (int64_t n = 0; n < n_vec; ++n) {
-      const double a = bf16_to_f32(xb[n * D + i]);
-      const double b = bf16_to_f32(xb[n * D + j]);
-      acc = fma(a, b, acc);
-    }
-  } else {
-    for (int64_t n = 0; n < n_vec; ++n) acc = fma(xd[n * D + i], xd[n * D + j], acc);
-  }
-  cov[e] = acc;
+// Second moments cov[i][j] = sum_n x[n][i] x[n][j] on the matrix cores, in
+// two deterministic steps.  outer_partial_kernel: workgroup w sums rows
+// [w rows, (w+1) rows) of x into part[w] with v_mfma_f64_16x16x4_f64 (fp64
+// products and sums, four rows per step in a fixed order); wave I owns the
+// 16-row block I of cov and all eight column blocks.  outer_reduce_kernel
+// adds the partials in workgroup order.  Exactly one of xb (bf16) / xd
+// (fp64) is non-null.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+constexpr int OUTER_WAVES = D / 16;  // one wave per 16-row block
+constexpr int OUTER_MAX_PARTS = 256;
+
+__device__ inline double outer_load(const uint16_t *xb, const double *xd, int64_t n, int64_t n_end, int col) {
+  if (n >= n_end) return 0.0;
+  return xb ? double(bf16_to_f32(xb[n * D + col])) : xd[n * D + col];
 }
 
+__global__ void __launch_bounds__(OUTER_WAVES * 64) outer_partial_kernel(const uint16_t *__restrict__ xb,
+                                                                       const double *__restrict__ xd,
+                                                                       int64_t n_vec, int64_t rows,
+                                                                       double *__restrict__ part) {
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int c = lane & 15, kq = lane >> 4;  // column in a block; row in a step of four
+  const int64_t r0 = int64_t(blockIdx.x) * rows;
+  const int64_t r1 = min(n_vec, r0 + rows);
+  f64x4 acc[D / 16];
+#pragma unroll
+  for (int jb = 0; jb < D / 16; ++jb) acc[jb] = f64x4{0.0, 0.0, 0.0, 0.0};
+  for (int64_t n0 = r0; n0 < r1; n0 += 4) {
+    const int64_t n = n0 + kq;
+    // A: x[n0 + k][16 wave + i] at (i = c, k = kq); B: x[n0 + k][16 jb + j]
+    const double a = outer_load(xb, xd, n, r1, 16 * wave + c);
+    double b[D / 16];
+#pragma unroll
+    for (int jb = 0; jb < D / 16; ++jb) b[jb] = outer_load(xb, xd, n, r1, 16 * jb + c);
+#pragma unroll
+    for (int jb = 0; jb < D / 16; ++jb) acc[jb] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b[jb], acc[jb], 0, 0, 0);
+  }
+  // the fp64 16x16 result: lane (c, kq), register r holds row kq + 4 r of
+  // column c of each tile
+  double *P = part + int64_t(blockIdx.x) * D * D;
+#pragma unroll
+  for (int jb = 0; jb < D / 16; ++jb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) P[(16 * wave + kq + 4 * r) * D + 16 * jb + c] = acc[jb][r];
+}
+
+__global__ void __launch_bounds__(256) outer_reduce_kernel(const double *__restrict__ part, int n_parts,
+                                                           double *__restrict__ cov) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  double s = 0.0;
+  for (int w = 0; w < n_parts; ++w) s += part[int64_t(w) * D * D + e];
+  cov[e] = s;
+}
+
+size_t calib_outer_part_bytes() { return size_t(OUTER_MAX_PARTS) * D * D * sizeof(double); }
+
 hipError_t launch_calib_outer(const uint16_t *x_bf16, const double *x_f64, int64_t n_vec,
-                              double *cov, hipStream_t s) {
-  hipLaunchKernelGGL(outer_sum_kernel, dim3(D * D / 256), dim3(256), 0, s, x_bf16, x_f64, n_vec,
-                     cov);
+                              double *cov, double *part, hipStream_t s) {
+  // rows per workgroup: a multiple of four, at least 64, at most 256 workgroups
+  int64_t rows = (n_vec + OUTER_MAX_PARTS - 1) / OUTER_MAX_PARTS;
+  rows = rows < 64 ? 64 : (rows + 3) / 4 * 4;
+  const int n_parts = int((n_vec + rows - 1) / rows);
+  hipLaunchKernelGGL(outer_partial_kernel, dim3(n_parts), dim3(OUTER_WAVES * 64), 0, s, x_bf16, x_f64, n_vec,
+                     rows, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(outer_reduce_kernel, dim3(D * D / 256), dim3(256), 0, s, part, n_parts, cov);
   return hipGetLastError();
 }
 

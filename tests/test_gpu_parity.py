@@ -143,6 +143,28 @@ def test_write_chunks_and_appends(oscar):
     check_raw_rows(sc, bf16_pool_bits(cache.bf16), ref)
 
 
+def test_write_bad_page_id_is_flagged_and_skipped(oscar):
+    # one history page id of request 0 points outside the pool: the kernel
+    # flags it, writes nothing for that page, and writes every other page
+    sc = Scenario(310, 8, 2, 32, [1000, 600])
+    cache = gpu_cache(oscar, sc)
+    cache.hist.fill_(0xAB)
+    bad_j = 5
+    cache.hist_pt[0, bad_j] = sc.n_hist_pages + 1000
+    rk, rv = gpu_rotations(oscar, sc)
+    gpu_write(oscar, sc, cache, rk, rv)
+    assert int(cache.status.item()) & 1
+    gh = cache.hist.cpu().numpy()
+    # the page the oracle would have used holds no history of request 0
+    assert np.all(gh[sc.hist_pt[0, bad_j]] == 0xAB)
+    hist0 = np.arange(o.N_SINK, sc.lens[0] - o.N_RECENT)
+    keep0 = hist0[(hist0 - o.N_SINK) // o.PAGE != bad_j]
+    hist1 = np.arange(o.N_SINK, sc.lens[1] - o.N_RECENT)
+    stats = compare_history(gh, sc.hist_pt, sc.tok_k, sc.tok_v, sc.lens, sc.R_K, sc.R_V, sc.clip_k, sc.clip_v,
+                            sc.G, positions=[keep0, hist1])
+    assert_history_ok(stats)
+
+
 # ------------------------------------------------------------------ decode
 
 
