@@ -347,6 +347,31 @@ def test_decode_step_appends_then_decodes(oscar, G):
     assert_decode_close(out.cpu().numpy(), sc.oracle_decode(full), f"decode_step G={G}")
 
 
+@pytest.mark.parametrize("rot", ["hadamard", "identity"])
+def test_decode_step_rotation_variants(oscar, rot):
+    # write-on-append under the pages' comparison rotations (unrotated bf16
+    # values put many quantisation steps exactly halfway between levels)
+    lens = [145, 146, 161, 500, 1201]
+    sc = Scenario(1150, 8, 2, 32, lens, rot=rot)
+    pre = _prefix_cache(sc, 1)
+    full = sc.oracle_cache()
+    cache = gpu_cache(oscar, sc, hist=pre.hist, bf16=pre.bf16)
+    rk, rv = gpu_rotations(oscar, sc)
+    k_last = np.stack([t[-1] for t in sc.tok_k])
+    v_last = np.stack([t[-1] for t in sc.tok_v])
+    before = torch.tensor([L - 1 for L in lens], dtype=torch.int32, device="cuda")
+    out = oscar.decode_step(cache, rk, rv, to_dev_bf16(k_last), to_dev_bf16(v_last), before, to_dev_bf16(sc.q),
+                            max(lens), SCALE)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) == 0
+    stats = compare_history(cache.hist.cpu().numpy(), sc.hist_pt, sc.tok_k, sc.tok_v, sc.lens,
+                            sc.R_K, sc.R_V, sc.clip_k, sc.clip_v, 32)
+    assert_history_ok(stats)
+    assert stats.get("code_in_band", 0) == 0, stats
+    check_raw_rows(sc, bf16_pool_bits(cache.bf16), full)
+    assert_decode_close(out.cpu().numpy(), sc.oracle_decode(full), f"decode_step ({rot})")
+
+
 def test_decode_step_many_steps(oscar):
     # 40 consecutive steps: ring slots are reused and evicted tokens fill two
     # history pages row by row
