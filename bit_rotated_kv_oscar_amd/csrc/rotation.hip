@@ -116,79 +116,113 @@ hipError_t launch_calib_outer(const uint16_t *x_bf16, const double *x_f64, int64
   return hipGetLastError();
 }
 
-__device__ inline double block_reduce_max128(double v, double *red) {
-  red[threadIdx.x] = v;
-  __syncthreads();
-  for (int off = 64; off > 0; off >>= 1) {
-    if (threadIdx.x < off) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + off]);
-    __syncthreads();
-  }
-  const double r = red[0];
-  __syncthreads();
-  return r;
+// Causal attention of the calibration sequence in fp64 on the matrix cores
+// (v_mfma_f64_16x16x4_f64).  One wave per (block of 16 query positions,
+// query head); key blocks of 16 in order with a running max and sum.  The
+// products are taken transposed so that no lane exchange is needed between
+// them: S^T = K Q^T (rows keys, columns queries) and O^T += V^T P^T, whose B
+// operand for keys 4s .. 4s+3 is register s of P^T in the result layout
+// (lane 16 (r mod 4) + c, register r / 4 holds row r, column c).  Lane
+// (c, kq) thus holds query c throughout; a query's 16 keys of a block sit in
+// its four lanes c, c+16, c+32, c+48 and their four registers.
+// o[n][h][:] = sum_j p_j v_j, p = softmax over j <= n of q_n . k_j / sqrt(128).
+__device__ inline double lanes4_max_f64(double v) {
+  v = fmax(v, __shfl_xor(v, 16));
+  return fmax(v, __shfl_xor(v, 32));
+}
+__device__ inline double lanes4_sum_f64(double v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
 }
 
-__device__ inline double block_reduce_sum128(double v, double *red) {
-  red[threadIdx.x] = v;
-  __syncthreads();
-  for (int off = 64; off > 0; off >>= 1) {
-    if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
-    __syncthreads();
-  }
-  const double r = red[0];
-  __syncthreads();
-  return r;
-}
-
-// One block (128 threads) per (query position n, query head h): causal
-// softmax attention over keys 0..n in fp64, keys taken 128 at a time with a
-// running max / sum.  o[n][h][:] = sum_j p_j v_j.
-__global__ void __launch_bounds__(128) calib_attention_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-    const uint16_t *__restrict__ v, int n_q_heads, int n_kv_heads, double *__restrict__ o) {
-  const int64_t n = blockIdx.x;
+__global__ void __launch_bounds__(64) calib_attention_kernel(const uint16_t *__restrict__ q,
+                                                             const uint16_t *__restrict__ k,
+                                                             const uint16_t *__restrict__ v, int64_t n_tokens,
+                                                             int n_q_heads, int n_kv_heads, double *__restrict__ o) {
+  const int64_t n0 = int64_t(blockIdx.x) * 16;
   const int h = blockIdx.y;
   const int g = h / (n_q_heads / n_kv_heads);
-  const int tid = threadIdx.x;
-  __shared__ double qs[D];
-  __shared__ double ps[D];
-  __shared__ double red[D];
+  const int lane = threadIdx.x;
+  const int c = lane & 15, kq = lane >> 4;  // column (query) of the tiles; k row within a step of four
   const double scale = 1.0 / sqrt(double(D));
-  qs[tid] = bf16_to_f32(q[(n * n_q_heads + h) * D + tid]) * scale;
-  __syncthreads();
-  double m = -INFINITY, l = 0.0, acc = 0.0;
-  for (int64_t j0 = 0; j0 <= n; j0 += D) {
-    const int64_t j = j0 + tid;
-    double sc = -INFINITY;
-    if (j <= n) {
-      const uint16_t *kr = k + (j * n_kv_heads + g) * D;
-      double s = 0.0;
-      for (int i = 0; i < D; ++i) s = fma(qs[i], double(bf16_to_f32(kr[i])), s);
-      sc = s;
-    }
-    const double mc = block_reduce_max128(sc, red);
-    const double mn = fmax(m, mc);
-    const double p = (j <= n) ? exp(sc - mn) : 0.0;
-    const double alpha = (m == -INFINITY) ? 0.0 : exp(m - mn);
-    const double ls = block_reduce_sum128(p, red);
-    ps[tid] = p;
-    __syncthreads();
-    l = l * alpha + ls;
-    acc *= alpha;
-    const int64_t cnt = (n - j0 + 1 < D) ? (n - j0 + 1) : D;
-    for (int t = 0; t < cnt; ++t)
-      acc = fma(ps[t], double(bf16_to_f32(v[((j0 + t) * n_kv_heads + g) * D + tid])), acc);
-    m = mn;
-    __syncthreads();
+  // B operand of S^T = K Q^T for channel step t: q[n0 + c][h][4t + kq] / sqrt(128)
+  double qb[D / 4];
+  {
+    const int64_t n = n0 + c;
+#pragma unroll
+    for (int t = 0; t < D / 4; ++t)
+      qb[t] = n < n_tokens ? double(bf16_to_f32(q[(n * n_q_heads + h) * D + 4 * t + kq])) * scale : 0.0;
   }
-  o[(n * n_q_heads + h) * D + tid] = acc / l;
+  f64x4 acc[D / 16];  // O^T tiles: channels 16 ct .. 16 ct + 15 x the 16 queries
+#pragma unroll
+  for (int ct = 0; ct < D / 16; ++ct) acc[ct] = f64x4{0.0, 0.0, 0.0, 0.0};
+  double m = -INFINITY, l = 0.0;  // running max / sum of query c
+  const int64_t q_last = min(n_tokens, n0 + 16) - 1;
+  for (int64_t j0 = 0; j0 <= q_last; j0 += 16) {
+    // S^T: A = k[j0 + c] (key c of the block), channels 4t + kq
+    f64x4 st = {0.0, 0.0, 0.0, 0.0};
+    {
+      const int64_t j = j0 + c;
+      const uint16_t *kr = k + (j * n_kv_heads + g) * D;
+#pragma unroll
+      for (int t = 0; t < D / 4; ++t) {
+        const double ka = j < n_tokens ? double(bf16_to_f32(kr[4 * t + kq])) : 0.0;
+        st = __builtin_amdgcn_mfma_f64_16x16x4f64(ka, qb[t], st, 0, 0, 0);
+      }
+    }
+    // register r: key j0 + kq + 4r of query n0 + c; causal mask
+    double mb = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t key = j0 + kq + 4 * r;
+      if (key > n0 + c || key >= n_tokens) st[r] = -INFINITY;
+      mb = fmax(mb, st[r]);
+    }
+    mb = lanes4_max_f64(mb);
+    const double mn = fmax(m, mb);
+    const double alpha = m == -INFINITY ? 0.0 : exp(m - mn);
+    double ps = 0.0;
+    f64x4 p;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = st[r] == -INFINITY ? 0.0 : exp(st[r] - mn);
+      ps += p[r];
+    }
+    ps = lanes4_sum_f64(ps);
+    l = l * alpha + ps;
+    m = mn;
+    // every register of the lane belongs to query c: rescale, then
+    // O^T += V^T P^T with A = v[j0 + 4s + kq] at channel 16 ct + c, B = p[s]
+#pragma unroll
+    for (int ct = 0; ct < D / 16; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[ct][r] *= alpha;
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      const int64_t j = j0 + 4 * s2 + kq;
+      const uint16_t *vr = v + (j * n_kv_heads + g) * D;
+#pragma unroll
+      for (int ct = 0; ct < D / 16; ++ct) {
+        const double va = j < n_tokens ? double(bf16_to_f32(vr[16 * ct + c])) : 0.0;
+        acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(va, p[s2], acc[ct], 0, 0, 0);
+      }
+    }
+  }
+  // O^T tile ct, register r: channel 16 ct + kq + 4 r of query n0 + c
+  const int64_t n = n0 + c;
+  if (n < n_tokens) {
+#pragma unroll
+    for (int ct = 0; ct < D / 16; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[(n * n_q_heads + h) * D + 16 * ct + kq + 4 * r] = acc[ct][r] / l;
+  }
 }
 
 hipError_t launch_calib_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                   int64_t n_tokens, int n_q_heads, int n_kv_heads, double *o,
                                   hipStream_t s) {
-  hipLaunchKernelGGL(calib_attention_kernel, dim3(unsigned(n_tokens), n_q_heads), dim3(D), 0, s,
-                     q, k, v, n_q_heads, n_kv_heads, o);
+  hipLaunchKernelGGL(calib_attention_kernel, dim3(unsigned((n_tokens + 15) / 16), n_q_heads), dim3(64), 0, s,
+                     q, k, v, n_tokens, n_q_heads, n_kv_heads, o);
   return hipGetLastError();
 }
 
