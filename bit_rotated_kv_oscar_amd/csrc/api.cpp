@@ -303,7 +303,7 @@ int oscar_calibrate_rotation(const uint16_t *q_cal, const uint16_t *k_cal, const
 int oscar_clip_threshold(const uint16_t *x_cal, int64_t n_vec, const double *R, double clip_quantile,
                          float *clip, oscar_stream_t stream) {
   if (!x_cal || !R || !clip) return fail(OSCAR_EINVAL, "clip_threshold: NULL argument");
-  if (n_vec < 1 || n_vec > (int64_t(1) << 24)) return fail(OSCAR_EINVAL, "n_vec %lld outside [1, 2^24]", (long long)n_vec);
+  if (n_vec < 1 || n_vec > (int64_t(1) << 20)) return fail(OSCAR_EINVAL, "n_vec %lld outside [1, 2^20]", (long long)n_vec);
   if (!(clip_quantile > 0.0 && clip_quantile <= 1.0)) return fail(OSCAR_EINVAL, "clip_quantile must be in (0, 1]");
   if (int rc = check_device()) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

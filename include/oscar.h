@@ -162,7 +162,8 @@ OSCAR_API int oscar_prepare_rotation(const double *R, void *forms, oscar_stream_
  * x_cal: device bf16 [n_vec][128]; R: host fp64 [128][128] (row-vector
  * convention, x R); clip: host float out.  Allocates and frees temporary
  * device memory and synchronises the stream.  Errors: OSCAR_EINVAL for
- * NULL pointers, n_vec outside [1, 2^24] or clip_quantile outside (0, 1];
+ * NULL pointers, n_vec outside [1, 2^20] (2^20 vectors take 1 GiB of
+ * temporary device and host memory) or clip_quantile outside (0, 1];
  * OSCAR_EHIP for runtime failures. */
 OSCAR_API int oscar_clip_threshold(const uint16_t *x_cal, int64_t n_vec, const double *R,
                          double clip_quantile, float *clip, oscar_stream_t stream);
