@@ -214,8 +214,9 @@ def main():
         traffic_from(args)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the path is single-GPU; "
-              f"see the sharding notes in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the path runs on a single GPU; "
+              f"requests, KV heads or context ranges would shard across GPUs, with one exchange of the "
+              f"per-query-head partials to merge a context split)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
