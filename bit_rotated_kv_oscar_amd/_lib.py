@@ -52,6 +52,9 @@ SIGNATURES = [
     ("oscar_calibrate_rotation", ctypes.c_int,
      [c_p, c_p, c_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
       c_p, c_p, c_p, c_p, c_p]),
+    ("oscar_calib_accumulate", ctypes.c_int,
+     [c_p, c_p, c_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, c_p, c_p]),
+    ("oscar_calib_rotations", ctypes.c_int, [c_p, ctypes.c_double, c_p, c_p, c_p]),
     ("oscar_clip_threshold", ctypes.c_int,
      [c_p, ctypes.c_int64, c_p, ctypes.c_double, c_p, c_p]),
     ("oscar_write_kv", ctypes.c_int,

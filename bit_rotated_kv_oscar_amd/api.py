@@ -211,6 +211,32 @@ def profile_events(before: "torch.cuda.Event | None", after: "torch.cuda.Event |
     check(load().oscar_profile_events(h0, h1))
 
 
+def calib_accumulate(q_cal: torch.Tensor, k_cal: torch.Tensor, v_cal: torch.Tensor, sums: torch.Tensor) -> int:
+    """oscar_calib_accumulate: adds one calibration sequence's moment sums to
+    sums (float64 [2, 128, 128] on the device); returns n_tokens * Hq, the
+    caller's count increment."""
+    dev = q_cal.device
+    for t, n in ((q_cal, "q_cal"), (k_cal, "k_cal"), (v_cal, "v_cal")):
+        _need(t, n, (torch.bfloat16,), dev)
+    _need(sums, "sums", (torch.float64,), dev)
+    if tuple(sums.shape) != (2, HEAD_DIM, HEAD_DIM):
+        raise ValueError("sums must be [2, 128, 128]")
+    check(load().oscar_calib_accumulate(_ptr(q_cal), _ptr(k_cal), _ptr(v_cal), q_cal.shape[0], q_cal.shape[1],
+                                        k_cal.shape[1], _ptr(sums), _stream(dev)))
+    return int(q_cal.shape[0] * q_cal.shape[1])
+
+
+def calib_rotations(sums: torch.Tensor, count: float):
+    """oscar_calib_rotations: (R_K, R_V) float64 CPU tensors [128, 128] from
+    accumulated moment sums and their count."""
+    dev = sums.device
+    _need(sums, "sums", (torch.float64,), dev)
+    R_K = torch.empty((HEAD_DIM, HEAD_DIM), dtype=torch.float64)
+    R_V = torch.empty((HEAD_DIM, HEAD_DIM), dtype=torch.float64)
+    check(load().oscar_calib_rotations(_ptr(sums), float(count), _ptr(R_K), _ptr(R_V), _stream(dev)))
+    return R_K, R_V
+
+
 def clip_threshold(x_cal: torch.Tensor, R: torch.Tensor, clip_quantile: float = 0.999) -> float:
     """oscar_clip_threshold: the clip of a caller-chosen rotation R (float64
     CPU [128, 128]) from bf16 calibration vectors [..., 128] on the device."""

@@ -300,6 +300,53 @@ int oscar_calibrate_rotation(const uint16_t *q_cal, const uint16_t *k_cal, const
   return OSCAR_OK;
 }
 
+int oscar_calib_accumulate(const uint16_t *q_cal, const uint16_t *k_cal, const uint16_t *v_cal,
+                           int64_t n_tokens, int32_t n_q_heads, int32_t n_kv_heads, double *sums,
+                           oscar_stream_t stream) {
+  if (!q_cal || !k_cal || !v_cal || !sums) return fail(OSCAR_EINVAL, "calib_accumulate: NULL argument");
+  if (n_tokens < 1 || n_tokens > 65536) return fail(OSCAR_EINVAL, "n_tokens %lld outside [1, 65536]", (long long)n_tokens);
+  if (n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || n_q_heads > 256)
+    return fail(OSCAR_EUNSUPPORTED, "head counts %d/%d unsupported", n_q_heads, n_kv_heads);
+  if (int rc = check_device()) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int D = oscar::D;
+  const int64_t nq = n_tokens * n_q_heads;
+  double *o = nullptr, *part = nullptr;
+  hipError_t e = hipMalloc(&o, size_t(nq) * D * sizeof(double));
+  if (e == hipSuccess) e = hipMalloc(&part, oscar::calib_outer_part_bytes());
+  if (e == hipSuccess) e = oscar::launch_calib_outer(q_cal, nullptr, nq, sums, part, s, true);
+  if (e == hipSuccess) e = oscar::launch_calib_attention(q_cal, k_cal, v_cal, n_tokens, n_q_heads, n_kv_heads, o, s);
+  if (e == hipSuccess) e = oscar::launch_calib_outer(nullptr, o, nq, sums + D * D, part, s, true);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (o) (void)hipFree(o);
+  if (part) (void)hipFree(part);
+  if (e != hipSuccess) return hip_fail(e, "calib_accumulate");
+  return OSCAR_OK;
+}
+
+int oscar_calib_rotations(const double *sums, double count, double *R_K, double *R_V, oscar_stream_t stream) {
+  if (!sums || !R_K || !R_V) return fail(OSCAR_EINVAL, "calib_rotations: NULL argument");
+  if (!(count > 0.0) || !std::isfinite(count)) return fail(OSCAR_EINVAL, "count must be positive and finite");
+  if (int rc = check_device()) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int D = oscar::D;
+  std::vector<double> c(2 * D * D);
+  hipError_t e = hipMemcpyAsync(c.data(), sums, c.size() * sizeof(double), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "calib_rotations");
+  for (auto &x : c) x /= count;
+  for (double x : c)
+    if (!std::isfinite(x)) return fail(OSCAR_EINVAL, "calib_rotations: non-finite moments");
+  std::vector<double> cq(c.begin(), c.begin() + D * D), cs(c.begin() + D * D, c.end()), U, Rk, Rv;
+  oscar::eigenbasis(cq, D, U);
+  oscar::compose_rotation(U, Rk);
+  oscar::eigenbasis(cs, D, U);
+  oscar::compose_rotation(U, Rv);
+  std::memcpy(R_K, Rk.data(), D * D * sizeof(double));
+  std::memcpy(R_V, Rv.data(), D * D * sizeof(double));
+  return OSCAR_OK;
+}
+
 int oscar_clip_threshold(const uint16_t *x_cal, int64_t n_vec, const double *R, double clip_quantile,
                          float *clip, oscar_stream_t stream) {
   if (!x_cal || !R || !clip) return fail(OSCAR_EINVAL, "clip_threshold: NULL argument");

@@ -60,11 +60,11 @@ hipError_t launch_decode_bf16(const uint16_t *q, const uint16_t *kv, int64_t n_p
 size_t decode_bf16_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int max_seq_len);
 
 // Calibration moments (device fp64).
-// cov[128][128] = sum over the n_vec vectors of x x^T (not yet divided);
-// part: calib_outer_part_bytes() of device scratch for the partial sums
+// cov[128][128] = (accumulate ? cov : 0) + sum over the n_vec vectors of
+// x x^T (not divided); part: calib_outer_part_bytes() of device scratch
 size_t calib_outer_part_bytes();
 hipError_t launch_calib_outer(const uint16_t *x_bf16, const double *x_f64, int64_t n_vec,
-                              double *cov, double *part, hipStream_t s);
+                              double *cov, double *part, hipStream_t s, bool accumulate = false);
 // o[N][Hq][128] (fp64) = causal softmax(q k^T / sqrt(128)) v per query head
 hipError_t launch_calib_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                   int64_t n_tokens, int n_q_heads, int n_kv_heads,

@@ -93,17 +93,17 @@ __global__ void __launch_bounds__(OUTER_WAVES * 64) outer_partial_kernel(const u
 }
 
 __global__ void __launch_bounds__(256) outer_reduce_kernel(const double *__restrict__ part, int n_parts,
-                                                           double *__restrict__ cov) {
+                                                           double *__restrict__ cov, bool accumulate) {
   const int e = blockIdx.x * 256 + threadIdx.x;
   double s = 0.0;
   for (int w = 0; w < n_parts; ++w) s += part[int64_t(w) * D * D + e];
-  cov[e] = s;
+  cov[e] = accumulate ? cov[e] + s : s;
 }
 
 size_t calib_outer_part_bytes() { return size_t(OUTER_MAX_PARTS) * D * D * sizeof(double); }
 
 hipError_t launch_calib_outer(const uint16_t *x_bf16, const double *x_f64, int64_t n_vec,
-                              double *cov, double *part, hipStream_t s) {
+                              double *cov, double *part, hipStream_t s, bool accumulate) {
   // rows per workgroup: a multiple of four, at least 64, at most 256 workgroups
   int64_t rows = (n_vec + OUTER_MAX_PARTS - 1) / OUTER_MAX_PARTS;
   rows = rows < 64 ? 64 : (rows + 3) / 4 * 4;
@@ -112,7 +112,7 @@ hipError_t launch_calib_outer(const uint16_t *x_bf16, const double *x_f64, int64
                      rows, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(outer_reduce_kernel, dim3(D * D / 256), dim3(256), 0, s, part, n_parts, cov);
+  hipLaunchKernelGGL(outer_reduce_kernel, dim3(D * D / 256), dim3(256), 0, s, part, n_parts, cov, accumulate);
   return hipGetLastError();
 }
 

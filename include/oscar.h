@@ -12,10 +12,10 @@
  * Every pointer argument is a plain pointer; "device" means memory the HIP
  * runtime can address on the current device, "host" means CPU memory.
  * The caller owns every buffer.  The library allocates device memory only in
- * oscar_calibrate_rotation and oscar_clip_threshold (freed before they
- * return) and keeps no state besides a thread-local error string.  All
- * calls except oscar_calibrate_rotation and oscar_clip_threshold are
- * asynchronous on the given stream.
+ * the calibration calls (oscar_calibrate_rotation, oscar_calib_accumulate,
+ * oscar_calib_rotations, oscar_clip_threshold; freed before they return)
+ * and keeps no state besides a thread-local error string.  All calls except
+ * those calibration calls are asynchronous on the given stream.
  *
  * Return value: OSCAR_OK (0) or a negative code; oscar_last_error() then
  * holds a message.  Arguments are validated on the host before any launch;
@@ -151,6 +151,30 @@ OSCAR_API size_t oscar_rotation_bytes(void);
  * part plus a 2^11-scaled fp16 low part for the matrix cores).
  * forms: device buffer of oscar_rotation_bytes(). */
 OSCAR_API int oscar_prepare_rotation(const double *R, void *forms, oscar_stream_t stream);
+
+/* Calibration over many sequences ([nl]/[fr] §2.2.A; the moments are sums,
+ * so they accumulate over any number of calibration sequences):
+ * oscar_calib_accumulate adds one sequence's second-moment sums to sums,
+ *   sums[0] += sum over tokens and query heads of q q^T,
+ *   sums[1] += sum over tokens and query heads of o o^T, o the causal
+ *              softmax(q K^T / sqrt(128)) V output of this sequence (query
+ *              head h reads KV head h / (Hq/Hkv)),
+ * and the caller adds n_tokens * Hq to its count.  oscar_calib_rotations
+ * divides by count and returns R_K = U_Q H P_br and R_V = U_S H P_br as
+ * oscar_calibrate_rotation does; the clips then come from
+ * oscar_clip_threshold over the calibration K and V vectors.
+ * q_cal: device bf16 [n_tokens][Hq][128]; k_cal, v_cal: device bf16
+ * [n_tokens][Hkv][128]; sums: device fp64 [2][128][128], zeroed by the
+ * caller before the first sequence; R_K, R_V: host fp64 [128][128] out.
+ * Both calls allocate temporary device memory and synchronise the stream.
+ * Errors: OSCAR_EINVAL (NULL pointers, n_tokens outside [1, 65536], count
+ * not positive, non-finite moments), OSCAR_EUNSUPPORTED (head counts),
+ * OSCAR_EHIP. */
+OSCAR_API int oscar_calib_accumulate(const uint16_t *q_cal, const uint16_t *k_cal,
+                           const uint16_t *v_cal, int64_t n_tokens, int32_t n_q_heads,
+                           int32_t n_kv_heads, double *sums, oscar_stream_t stream);
+OSCAR_API int oscar_calib_rotations(const double *sums, double count, double *R_K, double *R_V,
+                          oscar_stream_t stream);
 
 /* Clip threshold of one fixed rotation ([nl]/[fr] §2.2.A "clipping
  * thresholds"): the clip_quantile quantile (linear interpolation between

@@ -187,6 +187,27 @@ def calibrate(q, k, v, clip_quantile: float = 0.999) -> dict:
             "clip_V": clip_threshold(v, R_V, clip_quantile)}
 
 
+def calibrate_sequences(seqs, clip_quantile: float = 0.999) -> dict:
+    """Calibration over several sequences (list of (q, k, v) float64 arrays,
+    q [N_s][Hq][128], k, v [N_s][Hkv][128]): C_Q and C_S are means over every
+    token and query head of all sequences, each sequence's attention causal
+    within itself; R and the clips as in calibrate, the clips over the
+    vectors of all sequences ([nl]/[fr] §2.2.A: moments of a calibration
+    set)."""
+    hq = seqs[0][0].shape[1]
+    weights = [q.shape[0] * hq for q, _, _ in seqs]
+    total = float(sum(weights))
+    C_Q = sum(w * query_covariance(q) for w, (q, _, _) in zip(weights, seqs)) / total
+    C_S = sum(w * score_covariance(q, k, v) for w, (q, k, v) in zip(weights, seqs)) / total
+    R_K = compose_rotation(eigenbasis(C_Q))
+    R_V = compose_rotation(eigenbasis(C_S))
+    k_all = np.concatenate([k for _, k, _ in seqs])
+    v_all = np.concatenate([v for _, _, v in seqs])
+    return {"R_K": R_K, "R_V": R_V, "C_Q": C_Q, "C_S": C_S,
+            "clip_K": clip_threshold(k_all, R_K, clip_quantile),
+            "clip_V": clip_threshold(v_all, R_V, clip_quantile)}
+
+
 # --------------------------------------------------------------------------
 # rotation variants and distortion diagnostics ([abs]: OSCAR against
 # Hadamard-only, QuaRot-style INT2; [nl]/[fr] §2.1: data-oblivious Hadamard

@@ -176,6 +176,12 @@ def test_calibrate_and_prepare_validation_codes():
     assert lib.oscar_calibrate_rotation(0x1, 0x1, 0x1, 16, 8, 2, 1.5, R, R, ctypes.byref(f), ctypes.byref(f),
                                         None) == E.OSCAR_EINVAL
     assert lib.oscar_prepare_rotation(0, 0x1, None) == E.OSCAR_EINVAL
+    assert lib.oscar_calib_accumulate(0, 0x1, 0x1, 16, 8, 2, 0x1, None) == E.OSCAR_EINVAL
+    assert lib.oscar_calib_accumulate(0x1, 0x1, 0x1, 0, 8, 2, 0x1, None) == E.OSCAR_EINVAL
+    assert lib.oscar_calib_accumulate(0x1, 0x1, 0x1, 16, 8, 3, 0x1, None) == E.OSCAR_EUNSUPPORTED
+    assert lib.oscar_calib_rotations(0x1, 0.0, R, R, None) == E.OSCAR_EINVAL
+    assert lib.oscar_calib_rotations(0x1, float("nan"), R, R, None) == E.OSCAR_EINVAL
+    assert lib.oscar_calib_rotations(0, 10.0, R, R, None) == E.OSCAR_EINVAL
     assert lib.oscar_clip_threshold(0, 16, R, 0.999, ctypes.byref(f), None) == E.OSCAR_EINVAL
     assert lib.oscar_clip_threshold(0x1, 0, R, 0.999, ctypes.byref(f), None) == E.OSCAR_EINVAL
     assert lib.oscar_clip_threshold(0x1, 16, R, 0.0, ctypes.byref(f), None) == E.OSCAR_EINVAL

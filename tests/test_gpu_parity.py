@@ -309,6 +309,36 @@ def test_calibration_matches_oracle(oscar):
     assert abs(cv - cal["clip_V"]) <= 1e-6 * cal["clip_V"]
 
 
+def test_calibration_over_sequences_matches_oracle(oscar):
+    # three calibration sequences of different lengths, moments accumulated
+    # on the device, rotations and clips against the oracle's pooled ones
+    seqs_bits = []
+    for i, n in enumerate((700, 1024, 300)):
+        ld = synth.LayerData(1300 + i, 0, 8, 2)
+        seqs_bits.append(ld.calibration(n))
+    sums = torch.zeros((2, 128, 128), dtype=torch.float64, device="cuda")
+    count = 0
+    for qc, kc, vc in seqs_bits:
+        count += oscar.calib_accumulate(to_dev_bf16(qc), to_dev_bf16(kc), to_dev_bf16(vc), sums)
+    R_K, R_V = oscar.calib_rotations(sums, count)
+    k_all = to_dev_bf16(np.concatenate([k for _, k, _ in seqs_bits]))
+    v_all = to_dev_bf16(np.concatenate([v for _, _, v in seqs_bits]))
+    ck = oscar.clip_threshold(k_all, R_K)
+    cv = oscar.clip_threshold(v_all, R_V)
+    cal = o.calibrate_sequences([tuple(o.bf16_to_f64(x) for x in sb) for sb in seqs_bits])
+    assert count == (700 + 1024 + 300) * 8
+    R_K, R_V = R_K.numpy(), R_V.numpy()
+    for R, C in ((R_K, cal["C_Q"]), (R_V, cal["C_S"])):
+        assert np.abs(R.T @ R - np.eye(128)).max() < 1e-12
+        lam = np.sort(np.linalg.eigvalsh(C))[::-1]
+        H, P = o.hadamard(), o.bitrev_permutation()
+        assert np.abs(R.T @ C @ R - P @ H @ np.diag(lam) @ H @ P).max() < 1e-10 * np.abs(C).max()
+    assert np.abs(R_K - cal["R_K"]).max() < 1e-8
+    assert np.abs(R_V - cal["R_V"]).max() < 1e-8
+    assert abs(ck - cal["clip_K"]) <= 1e-6 * cal["clip_K"]
+    assert abs(cv - cal["clip_V"]) <= 1e-6 * cal["clip_V"]
+
+
 # ------------------------------------------------------------------ decode step
 
 

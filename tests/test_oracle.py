@@ -727,3 +727,36 @@ def test_identity_rotation_outliers_dominate_int2_error():
         xh = o.dequantize(qq["codes"], qq["scale"], qq["zero"], 32) @ R.T
         err[name] = o.relative_l2(xh, x)
     assert err["hadamard"] < 0.8 * err["identity"], err
+
+
+# ------------------------------------------------ calibration over sequences
+
+
+def test_calibration_over_sequences_pools_query_moments():
+    # C_Q has no attention in it: pooling sequences equals one concatenation
+    g = np.random.default_rng(41)
+    seqs = [(g.standard_normal((n, 4, 128)), g.standard_normal((n, 2, 128)), g.standard_normal((n, 2, 128)))
+            for n in (5, 9, 3)]
+    cal = o.calibrate_sequences(seqs)
+    q_all = np.concatenate([q for q, _, _ in seqs])
+    assert np.abs(cal["C_Q"] - o.query_covariance(q_all)).max() < 1e-13
+
+
+def test_calibration_over_single_token_sequences_closed_form():
+    # a one-token sequence attends to itself only: o = v of its KV head, so
+    # C_S is the mean of v v^T over sequences and query heads
+    g = np.random.default_rng(42)
+    hq, hkv = 4, 2
+    seqs = [(g.standard_normal((1, hq, 128)), g.standard_normal((1, hkv, 128)), g.standard_normal((1, hkv, 128)))
+            for _ in range(7)]
+    cal = o.calibrate_sequences(seqs)
+    C = np.zeros((128, 128))
+    for _, _, v in seqs:
+        for h in range(hq):
+            x = v[0, h // (hq // hkv)]
+            C += np.outer(x, x)
+    assert np.abs(cal["C_S"] - C / (7 * hq)).max() < 1e-13
+    # the clips cover the vectors of every sequence
+    k_all = np.concatenate([k for _, k, _ in seqs]).reshape(-1, 128)
+    ref = float(np.quantile(np.abs(k_all @ cal["R_K"]), 0.999, method="linear"))
+    assert abs(cal["clip_K"] - ref) < 1e-12 * ref
