@@ -47,7 +47,9 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", choices=["bs1", "bs64", "write", "28x100k"], default="bs1")
+    p.add_argument("--workload", choices=["bs1", "bs64", "write", "28x100k"], default=None,
+                   help="default: bs1, with the bs64 figures added to its line")
+    p.add_argument("--no-companion", action="store_true", help="default run: leave out the bs64 figures")
     p.add_argument("--layers", type=int, default=None, help="override the layer count (testing only)")
     p.add_argument("--seed", type=int, default=1)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -241,12 +243,43 @@ def main():
         print(json.dumps({"copy_probe_bytes": n}))
         return
 
+    workload_default = args.workload is None
+    if workload_default:
+        args.workload = "bs1"
     W = dict(WORKLOADS[args.workload])
     if args.layers:
         W["layers"] = args.layers
     if args.workload == "write":
         write_main(args, W, dev)
         return
+    line = decode_main(args, W, dev, args.workload)
+    if workload_default and not args.no_companion:
+        # the metric names batch 1 and batch 64: the default run adds the
+        # batch-64 workload's figures to its line
+        import gc
+        gc.collect()
+        torch.cuda.empty_cache()
+        a64 = argparse.Namespace(**vars(args))
+        a64.workload, a64.no_cpu_baseline = "bs64", True
+        l64 = decode_main(a64, dict(WORKLOADS["bs64"]), dev, "bs64")
+        line["bs64"] = {k: l64[k] for k in ("value", "unit", "ms_per_step", "tokens_per_s", "pct_hbm_peak",
+                                          "roofline", "bf16_ms_per_step", "int2_decode_ms_per_step",
+                                          "int2_speedup_vs_bf16") if k in l64}
+        line["bs64"]["config"] = l64["config"]
+    print(json.dumps(line))
+
+
+def decode_main(args, W, dev, workload):
+    """A decode workload: per-layer caches prefilled, then graph-replayed
+    steps of write-on-append + decode; returns the bench line."""
+    import numpy as np
+    import torch
+
+    import bit_rotated_kv_oscar_amd as oscar
+    import synth
+
+    if args.layers:
+        W["layers"] = args.layers
     nl, hq, hkv, G, B = W["layers"], W["hq"], W["hkv"], W["G"], W["batch"]
     steps, warm = args.steps, args.warmup
     headroom = steps + warm + 1
@@ -458,7 +491,7 @@ def main():
         "tokens_per_s": round(tokens_per_s, 1),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(workload),
                      "kernel": f"oscar::attend_kernel<{hq // hkv}, {128 // G}> (split-K INT2 + BF16 decode)",
                      "avg_launch_us": round(attend_us, 2), "bytes_per_launch": int(attend_b)},
         "cpu_baseline": cpu,
@@ -468,8 +501,7 @@ def main():
         line.update(bf16)
     elif "bf16_bytes_note" in W:
         line["bf16_baseline"] = "not run: " + W["bf16_bytes_note"]
-    print(json.dumps(line))
-
+    return line
 
 def write_main(args, W, dev):
     """The write workload: 36 layers' prefill of 8 x 32768 tokens per step,
