@@ -23,8 +23,7 @@ constexpr size_t FORM_R = 0;                        // fp32 R[i][j]
 constexpr size_t FORM_RT = FORM_R + D * D * 4;      // fp32 RT[j][i] = R[i][j]
 constexpr size_t FORM_RT_HI = FORM_RT + D * D * 4;  // fp16 hi(R[i][j]) at [j][i]
 constexpr size_t FORM_RT_LO = FORM_RT_HI + D * D * 2;  // fp16 2^11 * (R - hi)
-constexpr size_t FORM_RT_B = FORM_RT_LO + D * D * 2;   // 3 x bf16 [j][i]: R = b1 + b2 + b3
-constexpr size_t FORM_BYTES = FORM_RT_B + 3 * D * D * 2;
+constexpr size_t FORM_BYTES = FORM_RT_LO + D * D * 2;
 
 __host__ __device__ constexpr int n_groups(int G) { return D / G; }
 __host__ __device__ constexpr int meta_bytes(int G) { return 64 * (D / G); }

@@ -26,16 +26,6 @@ __global__ void __launch_bounds__(256) prepare_rotation_kernel(const double *__r
   const __half h = __float2half_rn(float(r));
   hi[j * D + i] = h;
   lo[j * D + i] = __float2half_rn(float((r - double(__half2float(h))) * 2048.0));
-  // three bf16 pieces, each the rounding of what the previous ones leave
-  uint16_t *bp = reinterpret_cast<uint16_t *>(forms + FORM_RT_B);
-  double rest = r;
-  for (int k = 0; k < 3; ++k) {
-    uint32_t u = __float_as_uint(float(rest));
-    u += 0x7FFFu + ((u >> 16) & 1u);  // round to nearest even
-    const uint16_t piece = uint16_t(u >> 16);
-    bp[k * D * D + j * D + i] = piece;
-    rest -= double(__uint_as_float(uint32_t(piece) << 16));
-  }
 }
 
 hipError_t launch_prepare_rotation(const double *R, void *forms, hipStream_t s) {

@@ -75,7 +75,7 @@ def test_struct_layout_matches_c():
 def test_sizes():
     assert [oscar.hist_block_bytes(g) for g in (32, 64, 128)] == [1536, 1280, 1152]
     assert oscar.hist_block_bytes(48) == 0
-    assert oscar.rotation_bytes() == 196608 + 3 * 128 * 128 * 2
+    assert oscar.rotation_bytes() == 196608
     assert oscar.decode_workspace_bytes(1, 32, 8, 32768) > 0
     assert oscar.decode_workspace_bytes(0, 32, 8, 32768) == 0
     assert oscar.bf16_decode_workspace_bytes(64, 32, 8, 32768) > 0
