@@ -80,6 +80,30 @@ namespace oscar {
 KernelEvents &profile_events() { return g_events; }
 }  // namespace oscar
 
+namespace {
+
+// Eigenbasis (sorted, signed) of the symmetric 128 x 128 matrix at mat (device,
+// destroyed) by the device Jacobi iteration; work: device scratch of
+// 128 * 128 doubles + one int.
+hipError_t device_eigenbasis(double *mat, double *work, hipStream_t s, std::vector<double> &U) {
+  const int D = oscar::D;
+  int *sweeps = reinterpret_cast<int *>(work + D * D);
+  hipError_t e = oscar::launch_jacobi(mat, work, sweeps, s);
+  std::vector<double> VT(D * D), V(D * D), A(D * D), w(D);
+  if (e == hipSuccess) e = hipMemcpyAsync(VT.data(), work, VT.size() * sizeof(double), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(A.data(), mat, A.size() * sizeof(double), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return e;
+  for (int i = 0; i < D; ++i) {
+    w[i] = A[size_t(i) * D + i];
+    for (int j = 0; j < D; ++j) V[size_t(i) * D + j] = VT[size_t(j) * D + i];
+  }
+  oscar::sorted_basis(V, w, D, U);
+  return hipSuccess;
+}
+
+}  // namespace
+
 extern "C" {
 
 int oscar_profile_events(void *before, void *after) {
@@ -245,7 +269,6 @@ int oscar_calibrate_rotation(const uint16_t *q_cal, const uint16_t *k_cal, const
   const int64_t nq = n_tokens * n_q_heads, nkv = n_tokens * n_kv_heads;
   double *cov = nullptr, *o = nullptr, *Rd = nullptr, *y = nullptr, *part = nullptr;
   int rc = OSCAR_OK;
-  std::vector<double> cq(D * D), cs(D * D);
   hipError_t e;
   auto cleanup = [&]() {
     if (cov) (void)hipFree(cov);
@@ -271,15 +294,12 @@ int oscar_calibrate_rotation(const uint16_t *q_cal, const uint16_t *k_cal, const
   CHECK_HIP(oscar::launch_calib_outer(q_cal, nullptr, nq, cov, part, s), "calib C_Q");
   CHECK_HIP(oscar::launch_calib_attention(q_cal, k_cal, v_cal, n_tokens, n_q_heads, n_kv_heads, o, s), "calib attention");
   CHECK_HIP(oscar::launch_calib_outer(nullptr, o, nq, cov + D * D, part, s), "calib C_S");
-  CHECK_HIP(hipMemcpyAsync(cq.data(), cov, D * D * sizeof(double), hipMemcpyDeviceToHost, s), "copy C_Q");
-  CHECK_HIP(hipMemcpyAsync(cs.data(), cov + D * D, D * D * sizeof(double), hipMemcpyDeviceToHost, s), "copy C_S");
-  CHECK_HIP(hipStreamSynchronize(s), "sync");
-  for (auto &x : cq) x /= double(nq);
-  for (auto &x : cs) x /= double(nq);
+  // eigenbases of the sums (the 1/(N Hq) scale changes no eigenvector);
+  // the Jacobi work area reuses the first partials of the moment step
   std::vector<double> U, Rk, Rv, absv(size_t(nkv) * D);
-  oscar::eigenbasis(cq, D, U);
+  CHECK_HIP(device_eigenbasis(cov, part, s, U), "eigenbasis C_Q");
   oscar::compose_rotation(U, Rk);
-  oscar::eigenbasis(cs, D, U);
+  CHECK_HIP(device_eigenbasis(cov + D * D, part, s, U), "eigenbasis C_S");
   oscar::compose_rotation(U, Rv);
   double clips[2];
   const uint16_t *xs[2] = {k_cal, v_cal};
@@ -334,14 +354,22 @@ int oscar_calib_rotations(const double *sums, double count, double *R_K, double 
   hipError_t e = hipMemcpyAsync(c.data(), sums, c.size() * sizeof(double), hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "calib_rotations");
-  for (auto &x : c) x /= count;
   for (double x : c)
-    if (!std::isfinite(x)) return fail(OSCAR_EINVAL, "calib_rotations: non-finite moments");
-  std::vector<double> cq(c.begin(), c.begin() + D * D), cs(c.begin() + D * D, c.end()), U, Rk, Rv;
-  oscar::eigenbasis(cq, D, U);
-  oscar::compose_rotation(U, Rk);
-  oscar::eigenbasis(cs, D, U);
-  oscar::compose_rotation(U, Rv);
+    if (!std::isfinite(x / count)) return fail(OSCAR_EINVAL, "calib_rotations: non-finite moments");
+  // the caller's sums stay intact: the iteration runs on a copy (the 1/count
+  // scale changes no eigenvector)
+  double *mat = nullptr, *work = nullptr;
+  std::vector<double> U, Rk, Rv;
+  e = hipMalloc(&mat, 2 * D * D * sizeof(double));
+  if (e == hipSuccess) e = hipMalloc(&work, D * D * sizeof(double) + 256);
+  if (e == hipSuccess) e = hipMemcpyAsync(mat, sums, 2 * D * D * sizeof(double), hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = device_eigenbasis(mat, work, s, U);
+  if (e == hipSuccess) oscar::compose_rotation(U, Rk);
+  if (e == hipSuccess) e = device_eigenbasis(mat + D * D, work, s, U);
+  if (e == hipSuccess) oscar::compose_rotation(U, Rv);
+  if (mat) (void)hipFree(mat);
+  if (work) (void)hipFree(work);
+  if (e != hipSuccess) return hip_fail(e, "calib_rotations");
   std::memcpy(R_K, Rk.data(), D * D * sizeof(double));
   std::memcpy(R_V, Rv.data(), D * D * sizeof(double));
   return OSCAR_OK;

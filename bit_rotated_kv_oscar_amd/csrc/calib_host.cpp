@@ -1,6 +1,7 @@
 // Host fp64 parts of the offline calibration (OSCAR, gist.science nl/fr
-// technical summaries, section 2.2.A): eigendecomposition of the covariance
-// targets, the composite rotation R = U H P_br, and the clip quantile.
+// technical summaries, section 2.2.A): order and signs of the eigenbasis of
+// the covariance targets, the composite rotation R = U H P_br, and the clip
+// quantile.
 #include <algorithm>
 #include <cmath>
 #include <numeric>
@@ -10,59 +11,11 @@
 
 namespace oscar {
 
-// Cyclic Jacobi eigenvalue iteration for a symmetric n x n matrix
-// (Golub & Van Loan, "Matrix Computations", section 8.5): sweeps of plane
-// rotations that zero one off-diagonal pair at a time until the
-// off-diagonal mass is negligible.  A is overwritten; V (row-major, columns
-// are eigenvectors) and w receive the result.
-void jacobi_eigh(std::vector<double> &A, int n, std::vector<double> &V, std::vector<double> &w) {
-  V.assign(size_t(n) * n, 0.0);
-  for (int i = 0; i < n; ++i) V[size_t(i) * n + i] = 1.0;
-  auto a = [&](int i, int j) -> double & { return A[size_t(i) * n + j]; };
-  double fro = 0.0;
-  for (double x : A) fro += x * x;
-  fro = std::sqrt(fro);
-  for (int sweep = 0; sweep < 100; ++sweep) {
-    double off = 0.0;
-    for (int i = 0; i < n; ++i)
-      for (int j = i + 1; j < n; ++j) off += a(i, j) * a(i, j);
-    if (std::sqrt(off) <= 1e-16 * fro) break;
-    for (int p = 0; p < n - 1; ++p) {
-      for (int q = p + 1; q < n; ++q) {
-        const double apq = a(p, q);
-        if (apq == 0.0) continue;
-        const double theta = (a(q, q) - a(p, p)) / (2.0 * apq);
-        const double t = (theta >= 0 ? 1.0 : -1.0) / (std::fabs(theta) + std::sqrt(theta * theta + 1.0));
-        const double c = 1.0 / std::sqrt(t * t + 1.0);
-        const double s = t * c;
-        for (int k = 0; k < n; ++k) {  // columns p, q
-          const double akp = a(k, p), akq = a(k, q);
-          a(k, p) = c * akp - s * akq;
-          a(k, q) = s * akp + c * akq;
-        }
-        for (int k = 0; k < n; ++k) {  // rows p, q
-          const double apk = a(p, k), aqk = a(q, k);
-          a(p, k) = c * apk - s * aqk;
-          a(q, k) = s * apk + c * aqk;
-        }
-        for (int k = 0; k < n; ++k) {
-          double &vkp = V[size_t(k) * n + p], &vkq = V[size_t(k) * n + q];
-          const double x = vkp, y = vkq;
-          vkp = c * x - s * y;
-          vkq = s * x + c * y;
-        }
-      }
-    }
-  }
-  w.resize(n);
-  for (int i = 0; i < n; ++i) w[i] = a(i, i);
-}
-
-// Eigenbasis with eigenvalues descending and each column's largest-magnitude
-// entry positive (first index on ties).  U row-major, columns = vectors.
-void eigenbasis(const std::vector<double> &C, int n, std::vector<double> &U) {
-  std::vector<double> A = C, V, w;
-  jacobi_eigh(A, n, V, w);
+// Eigenbasis from an eigen-decomposition V, w (V row-major, columns are
+// eigenvectors; from the device Jacobi iteration): eigenvalues descending and
+// each column's largest-magnitude entry positive (first index on ties).  U
+// row-major, columns = vectors.
+void sorted_basis(const std::vector<double> &V, const std::vector<double> &w, int n, std::vector<double> &U) {
   std::vector<int> order(n);
   std::iota(order.begin(), order.end(), 0);
   std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return w[x] > w[y]; });

@@ -5,8 +5,8 @@
 
 namespace oscar {
 
-void jacobi_eigh(std::vector<double> &A, int n, std::vector<double> &V, std::vector<double> &w);
-void eigenbasis(const std::vector<double> &C, int n, std::vector<double> &U);
+// U: columns of V reordered by descending w, each with its largest-|entry| positive
+void sorted_basis(const std::vector<double> &V, const std::vector<double> &w, int n, std::vector<double> &U);
 void compose_rotation(const std::vector<double> &U, std::vector<double> &R);
 double quantile_linear(std::vector<double> &x, double p);
 

@@ -69,6 +69,10 @@ hipError_t launch_calib_outer(const uint16_t *x_bf16, const double *x_f64, int64
 hipError_t launch_calib_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                   int64_t n_tokens, int n_q_heads, int n_kv_heads,
                                   double *o, hipStream_t s);
+// Jacobi eigen-decomposition of the symmetric 128 x 128 matrix a (device,
+// overwritten: eigenvalues on its diagonal); vt: device [128][128] out, the
+// eigenvectors as rows, unsorted; sweeps: device int out
+hipError_t launch_jacobi(double *a, double *vt, int *sweeps, hipStream_t s);
 // y[n][128] = |x[n] R| (fp64), x bf16 [n][128]
 hipError_t launch_calib_rotate_abs(const uint16_t *x, int64_t n_vec, const double *R,
                                    double *y, hipStream_t s);

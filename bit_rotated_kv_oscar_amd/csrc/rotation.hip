@@ -237,3 +237,111 @@ hipError_t launch_calib_rotate_abs(const uint16_t *x, int64_t n_vec, const doubl
 }
 
 }  // namespace oscar
+
+namespace oscar {
+
+// ---------------------------------------------------------------- eigenbasis
+
+// Cyclic Jacobi eigenvalue iteration for the symmetric 128 x 128 moment
+// matrix (Golub & Van Loan, "Matrix Computations", section 8.5, the
+// parallel ordering of section 8.5.4): each round applies 64 plane
+// rotations on disjoint index pairs at once (a round-robin tournament: slot
+// 0 stays, the other 127 slots rotate), 127 rounds per sweep, sweeps until
+// the off-diagonal norm is below 1e-16 of the Frobenius norm.  One
+// workgroup; the matrix lives in LDS (128 KiB), the accumulated rotation in
+// global memory as vt = V^T (a rotation of columns p, q of V is then a
+// contiguous update of rows p, q).  On exit a holds the eigenvalues on its
+// diagonal and vt the eigenvectors as rows, unsorted.
+constexpr int JACOBI_THREADS = 1024;
+constexpr int JS = D + 1;  // LDS row stride of the matrix (doubles)
+
+__global__ void __launch_bounds__(JACOBI_THREADS) jacobi_kernel(double *__restrict__ a, double *__restrict__ vt,
+                                                               int *__restrict__ sweeps_out) {
+  __shared__ double A[D * JS];  // rows padded to JS doubles (no bank conflicts down a column)
+  __shared__ double cs[D / 2], sn[D / 2];
+  __shared__ int pp[D / 2], qq[D / 2];
+  __shared__ double red[JACOBI_THREADS / 64];
+  const int tid = threadIdx.x;
+  double fro = 0.0;
+  for (int e = tid; e < D * D; e += JACOBI_THREADS) {
+    A[(e / D) * JS + e % D] = a[e];
+    vt[e] = (e / D == e % D) ? 1.0 : 0.0;
+    fro += a[e] * a[e];
+  }
+  auto block_sum = [&](double x) {
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    if ((tid & 63) == 0) red[tid >> 6] = x;
+    __syncthreads();
+    double s = 0.0;
+    for (int i = 0; i < JACOBI_THREADS / 64; ++i) s += red[i];
+    __syncthreads();
+    return s;
+  };
+  fro = sqrt(block_sum(fro));
+  int sweep = 0;
+  for (; sweep < 60; ++sweep) {
+    double off = 0.0;
+    for (int e = tid; e < D * D; e += JACOBI_THREADS)
+      if (e % D > e / D) off += A[(e / D) * JS + e % D] * A[(e / D) * JS + e % D];
+    off = block_sum(off);
+    if (sqrt(off) <= 1e-16 * fro) break;
+    for (int r = 0; r < D - 1; ++r) {
+      if (tid < D / 2) {
+        auto slot = [&](int s) { return s == 0 ? 0 : (s - 1 + r) % (D - 1) + 1; };
+        int p = slot(tid), q = slot(D - 1 - tid);
+        if (p > q) {
+          const int t = p;
+          p = q;
+          q = t;
+        }
+        const double apq = A[p * JS + q];
+        double c = 1.0, s = 0.0;
+        if (apq != 0.0) {
+          const double theta = (A[q * JS + q] - A[p * JS + p]) / (2.0 * apq);
+          const double t = (theta >= 0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
+          c = 1.0 / sqrt(t * t + 1.0);
+          s = t * c;
+        }
+        cs[tid] = c;
+        sn[tid] = s;
+        pp[tid] = p;
+        qq[tid] = q;
+      }
+      __syncthreads();
+      // columns p, q of A; rows p, q of V^T
+#pragma unroll
+      for (int it = 0; it < (D / 2) * D / JACOBI_THREADS; ++it) {
+        const int e = tid + JACOBI_THREADS * it;
+        const int k = e / D, i = e % D;
+        const int p = pp[k], q = qq[k];
+        const double c = cs[k], s = sn[k];
+        const double x = A[i * JS + p], y = A[i * JS + q];
+        A[i * JS + p] = c * x - s * y;
+        A[i * JS + q] = s * x + c * y;
+        const double vx = vt[p * D + i], vy = vt[q * D + i];
+        vt[p * D + i] = c * vx - s * vy;
+        vt[q * D + i] = s * vx + c * vy;
+      }
+      __syncthreads();
+      // rows p, q of A
+      for (int e = tid; e < (D / 2) * D; e += JACOBI_THREADS) {
+        const int k = e / D, j = e % D;
+        const int p = pp[k], q = qq[k];
+        const double c = cs[k], s = sn[k];
+        const double x = A[p * JS + j], y = A[q * JS + j];
+        A[p * JS + j] = c * x - s * y;
+        A[q * JS + j] = s * x + c * y;
+      }
+      __syncthreads();
+    }
+  }
+  for (int e = tid; e < D * D; e += JACOBI_THREADS) a[e] = A[(e / D) * JS + e % D];
+  if (tid == 0) *sweeps_out = sweep;
+}
+
+hipError_t launch_jacobi(double *a, double *vt, int *sweeps, hipStream_t s) {
+  hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(JACOBI_THREADS), 0, s, a, vt, sweeps);
+  return hipGetLastError();
+}
+
+}  // namespace oscar
