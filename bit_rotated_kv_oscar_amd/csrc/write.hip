@@ -141,12 +141,13 @@ __device__ inline void token_source(const WriteArgs &a, int ids, int tensor, int
 // up to WHC KV heads).  Per page: the rows that enter history in this call
 // -- new tokens, or ring tokens pushed out of the recent window -- are staged
 // in LDS for all heads of the chunk as fp16 (exact in fp16's normal range),
-// rotated on the matrix cores: Y = X R_hi + 2^-11 X R_lo with R_hi = fp16(R)
-// and R_lo = fp16(2^11 (R - R_hi)), each product accumulated in fp32, so the
-// error stays within the fp32 dot-product bound.  Wave w computes output channels 32w ..
-// 32w+31 of every head; then clip, per-(token, group) fp16 zero = min and
-// scale = (max - min)/3 (reductions across the lanes of a token, then across
-// the waves of a group wider than 32), codes, and the packed store in the
+// rotated on the matrix cores as 2^11 Y = X (2^11 R_hi) + X R_lo with
+// R_hi = fp16(R) and R_lo = fp16(2^11 (R - R_hi)), both products summed in
+// one fp32 accumulator (the small ones first), so the error stays within the
+// fp32 dot-product bound.  Wave w computes output channels 32w .. 32w+31 of
+// every head; then clip, per-(token, group) fp16 zero = min and scale =
+// (max - min)/3 (reductions across the lanes of a token, then across the
+// waves of a group wider than 32), codes, and the packed store in the
 // documented layout.
 //
 // Pipeline: page j's rows are staged from registers loaded during page j-1;
@@ -188,6 +189,7 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a, WriteShared<
 
   // page ids: lane i < WPP holds hist_pt[b][jfirst + i] (-1 past the table),
   // lane 16 + i holds bf16_pt[b][i]
+  static_assert(WPP <= 16 && 16 + BF16_PT <= 64, "page ids fit the lanes of one register");
   int ids = -1;
   if (lane < WPP) {
     const int j = jfirst + lane;
