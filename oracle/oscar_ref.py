@@ -30,7 +30,9 @@ notes of this repository):
     fp16 scale is 0;
   * sink = first 16 tokens, recent = last 128 tokens (exact sliding window),
     both raw bf16 and unrotated; history in between;
-  * decode: one query per request over all cached tokens, no mask, fp64.
+  * decode: one query per request over all cached tokens, no mask, fp64;
+  * extend: new tokens see the cached prefix as it stands plus the chunk's
+    own earlier tokens at bf16 (the chunk is written afterwards), fp64.
 """
 from __future__ import annotations
 
@@ -528,6 +530,33 @@ def decode_attn(cache: LayerCacheRef, rot_k, rot_v, q_bits: np.ndarray, seq_lens
     for b in range(q.shape[0]):
         K, V = cache.gather(b, int(seq_lens[b]), rot_k, rot_v)
         out[b] = attention(q[b], K, V, sm_scale)
+    return out
+
+
+def extend_attn(cache: LayerCacheRef, rot_k, rot_v, q_bits: np.ndarray, k_new: np.ndarray,
+                v_new: np.ndarray, cu_new, len_before, sm_scale: float) -> np.ndarray:
+    """Chunked-prefill ("extend") attention of new tokens over a cached prefix
+    ([abs]: paged layouts with prefix caching; [nl]/[fr] section 2.2.B: the
+    fused kernel reads the INT2 history, dequantises and inverse-rotates it).
+
+    Request b's prefix is the cache as it stands, len_before[b] tokens: sink,
+    INT2 history and recent window, each read as the decode reads it.  Its
+    new tokens are rows cu_new[b] .. cu_new[b+1]-1 of q_bits / k_new / v_new
+    (bf16 bits, [T][Hq or Hkv][128]), at positions len_before[b] + i; new
+    token i attends to the whole prefix and to new tokens 0..i at full bf16
+    precision (causal).  The chunk is not written here.  Returns
+    [T][Hq][128] fp64."""
+    q = bf16_to_f64(q_bits)
+    out = np.empty(q.shape)
+    for b in range(len(len_before)):
+        L0 = int(len_before[b])
+        r0, r1 = int(cu_new[b]), int(cu_new[b + 1])
+        Kp, Vp = cache.gather(b, L0, rot_k, rot_v)
+        Kn, Vn = bf16_to_f64(k_new[r0:r1]), bf16_to_f64(v_new[r0:r1])
+        for i in range(r1 - r0):
+            K = np.concatenate([Kp, Kn[:i + 1]])
+            V = np.concatenate([Vp, Vn[:i + 1]])
+            out[r0 + i] = attention(q[r0 + i], K, V, sm_scale)
     return out
 
 

@@ -760,3 +760,82 @@ def test_calibration_over_single_token_sequences_closed_form():
     k_all = np.concatenate([k for _, k, _ in seqs]).reshape(-1, 128)
     ref = float(np.quantile(np.abs(k_all @ cal["R_K"]), 0.999, method="linear"))
     assert abs(cal["clip_K"] - ref) < 1e-12 * ref
+
+
+# ------------------------------------------------------------------ extend
+
+
+def _sdpa_rows(q, K, V, first_pos, sm_scale):
+    """Library attention (torch's scaled_dot_product_attention, fp64, CPU):
+    query row i sits at position first_pos + i and sees keys 0 .. first_pos + i.
+    q [T][Hq][128], K/V [L][Hkv][128] -> [T][Hq][128]."""
+    import torch
+    T, hq = q.shape[0], q.shape[1]
+    gqa = hq // K.shape[1]
+    qt = torch.from_numpy(q).permute(1, 0, 2)[None]
+    kt = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(gqa, 0)[None]
+    vt = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(gqa, 0)[None]
+    mask = torch.arange(K.shape[0])[None, :] <= (first_pos + torch.arange(T))[:, None]
+    o_ = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=sm_scale)
+    return o_[0].permute(1, 0, 2).numpy()
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (2, 2), (8, 1)])
+def test_extend_without_prefix_is_causal_attention(hq, hkv):
+    # empty prefix: the chunk attends causally to itself, textbook attention
+    T = 37
+    ld = synth.LayerData(31, 0, hq, hkv)
+    k, v = ld.cache_kv(T)
+    q = ld.decode_q(T)
+    c = _make_cache(T, hkv=hkv)
+    R = _rot()
+    out = o.extend_attn(c, R, R.T, q, k, v, [0, T], [0], 0.088)
+    ref = _sdpa_rows(o.bf16_to_f64(q), o.bf16_to_f64(k), o.bf16_to_f64(v), 0, 0.088)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_extend_lossless_prefix_equals_full_causal_attention():
+    # A prefix with sink, INT2 history and recent window, quantised losslessly
+    # (rotated values on the grid z + c s, see the decode pin above), so the
+    # extend over the cached prefix plus the raw chunk equals plain causal
+    # attention over all tokens, row by row.  Two requests with different
+    # prefix lengths share one call.
+    lens0, T = [180, 150], [23, 9]
+    # different shifts for K and V: swapping R_K and R_V breaks the equality
+    shift_k, shift_v = np.roll(np.eye(128), 5, axis=1), np.roll(np.eye(128), 9, axis=1)
+    rng = np.random.default_rng(41)
+    tot = [a + t for a, t in zip(lens0, T)]
+    kv = []
+    for shift in (shift_k, shift_v):
+        lv = rng.integers(0, 4, size=(sum(tot), 2, 128)).astype(np.float32)
+        lv[..., 0::32] = 0
+        lv[..., 1::32] = 3
+        kv.append(synth.bf16_bits((lv * 0.5 - 1.0) @ shift.T))
+    k, v = kv
+    q = synth.LayerData(6, 0, 8, 2).decode_q(sum(T))
+    c = _make_cache(max(lens0), batch=2)
+    starts = np.concatenate([[0], np.cumsum(tot)])
+    pre_k = np.concatenate([k[starts[b]:starts[b] + lens0[b]] for b in range(2)])
+    pre_v = np.concatenate([v[starts[b]:starts[b] + lens0[b]] for b in range(2)])
+    c.write(shift_k, shift_v, 100.0, 100.0, pre_k, pre_v, [0, lens0[0], sum(lens0)], [0, 0])
+    new_k = np.concatenate([k[starts[b] + lens0[b]:starts[b + 1]] for b in range(2)])
+    new_v = np.concatenate([v[starts[b] + lens0[b]:starts[b + 1]] for b in range(2)])
+    cu = [0, T[0], sum(T)]
+    out = o.extend_attn(c, shift_k, shift_v, q, new_k, new_v, cu, lens0, 0.088)
+    for b in range(2):
+        K = o.bf16_to_f64(k[starts[b]:starts[b + 1]])
+        V = o.bf16_to_f64(v[starts[b]:starts[b + 1]])
+        ref = _sdpa_rows(o.bf16_to_f64(q[cu[b]:cu[b + 1]]), K, V, lens0[b], 0.088)
+        np.testing.assert_allclose(out[cu[b]:cu[b + 1]], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_extend_single_token_short_prefix_equals_decode_after_append():
+    # no history involved (L0 + 1 <= 144): one new token equals the decode of
+    # the cache after that token is appended
+    for L0 in (0, 15, 16, 100, 143):
+        c, k, v, q, R, Rv = _filled(L0 + 1)
+        pre = _make_cache(L0 + 1)
+        pre.write(R, Rv, 4.0, 3.0, k[:L0], v[:L0], [0, L0], [0])
+        out = o.extend_attn(pre, R, Rv, q, k[L0:L0 + 1], v[L0:L0 + 1], [0, 1], [L0], 0.088)
+        ref = o.decode_attn(c, R, Rv, q, [L0 + 1], 0.088)
+        np.testing.assert_allclose(out, ref, rtol=1e-13, atol=1e-13)
