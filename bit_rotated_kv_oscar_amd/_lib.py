@@ -70,6 +70,10 @@ SIGNATURES = [
      [ctypes.POINTER(LayerCacheC), ctypes.POINTER(RotationC), ctypes.POINTER(RotationC),
       c_p, c_p, c_p, c_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, c_p,
       c_p, ctypes.c_size_t, c_p]),
+    ("oscar_extend_attn", ctypes.c_int,
+     [ctypes.POINTER(LayerCacheC), ctypes.POINTER(RotationC), ctypes.POINTER(RotationC),
+      c_p, ctypes.c_int32, c_p, c_p, c_p, c_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+      ctypes.c_float, c_p, c_p]),
     ("oscar_profile_events", ctypes.c_int, [c_p, c_p]),
     ("oscar_bf16_decode_workspace_bytes", ctypes.c_size_t,
      [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),

@@ -171,6 +171,34 @@ def decode_step(cache: LayerCache, rot_k: Rotation, rot_v: Rotation, k_new: torc
     return out
 
 
+def extend_attn(cache: LayerCache, rot_k: Rotation, rot_v: Rotation, q: torch.Tensor, k_new: torch.Tensor,
+                v_new: torch.Tensor, cu_new: torch.Tensor, len_before: torch.Tensor, max_new: int,
+                max_prefix: int, sm_scale: float | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """oscar_extend_attn: new tokens (rows cu_new[b]..cu_new[b+1]-1 of q bf16
+    [T, Hq, 128], k_new / v_new bf16 [T, Hkv, 128]) attend to request b's
+    cached prefix of len_before[b] tokens and causally to each other; the
+    chunk is not written.  Returns out fp32 [T, Hq, 128]."""
+    dev = cache.device
+    for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new")):
+        _need(t, n, (torch.bfloat16,), dev)
+    _need(cu_new, "cu_new", (torch.int32,), dev)
+    _need(len_before, "len_before", (torch.int32,), dev)
+    batch, hq = len_before.shape[0], q.shape[1]
+    if cu_new.shape[0] != batch + 1:
+        raise ValueError("cu_new must have batch + 1 entries")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if out is None:
+        out = torch.empty((q.shape[0], hq, HEAD_DIM), dtype=torch.float32, device=dev)
+    _need(out, "out", (torch.float32,), dev)
+    c = cache.c()
+    rk, rv = rot_k.c(), rot_v.c()
+    check(load().oscar_extend_attn(ctypes.byref(c), ctypes.byref(rk), ctypes.byref(rv), _ptr(q), hq, _ptr(k_new),
+                                   _ptr(v_new), _ptr(cu_new), _ptr(len_before), batch, q.shape[0], int(max_new),
+                                   int(max_prefix), float(sm_scale), _ptr(out), _stream(dev)))
+    return out
+
+
 def bf16_decode_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, max_seq_len: int) -> int:
     return int(load().oscar_bf16_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, max_seq_len))
 

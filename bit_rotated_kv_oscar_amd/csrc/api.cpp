@@ -223,6 +223,33 @@ int oscar_decode_step(const oscar_layer_cache *cache, const oscar_rotation *rot_
   return OSCAR_OK;
 }
 
+int oscar_extend_attn(const oscar_layer_cache *cache, const oscar_rotation *rot_k, const oscar_rotation *rot_v,
+                      const uint16_t *q, int32_t n_q_heads, const uint16_t *k_new, const uint16_t *v_new,
+                      const int32_t *cu_new, const int32_t *len_before, int32_t batch, int64_t total_tokens,
+                      int32_t max_new, int32_t max_prefix, float sm_scale, float *out, oscar_stream_t stream) {
+  if (int rc = check_cache(cache)) return rc;
+  if (int rc = check_rot(rot_k, "rot_k")) return rc;
+  if (int rc = check_rot(rot_v, "rot_v")) return rc;
+  if (int rc = check_heads(n_q_heads, cache->n_kv_heads)) return rc;
+  if (batch < 1 || batch > 65535) return fail(OSCAR_EINVAL, "batch %d outside [1, 65535]", batch);
+  if (total_tokens < 0 || max_new < 0 || max_prefix < 0) return fail(OSCAR_EINVAL, "negative token counts");
+  if (int64_t(max_new) > total_tokens) return fail(OSCAR_EINVAL, "max_new %d > total_tokens %lld", max_new, (long long)total_tokens);
+  if (max_new > (1 << 24)) return fail(OSCAR_EINVAL, "max_new %d too large", max_new);
+  if (oscar::n_hist_pages(max_prefix) > cache->hist_pt_stride)
+    return fail(OSCAR_EINVAL, "max_prefix %d needs %d history pages, hist_pt_stride is %d", max_prefix,
+                oscar::n_hist_pages(max_prefix), cache->hist_pt_stride);
+  if (!cu_new || !len_before) return fail(OSCAR_EINVAL, "cu_new or len_before is NULL");
+  if (total_tokens > 0 && (!q || !k_new || !v_new || !out)) return fail(OSCAR_EINVAL, "q, k_new, v_new or out is NULL");
+  if (!std::isfinite(sm_scale) || sm_scale <= 0.f) return fail(OSCAR_EINVAL, "sm_scale must be finite and > 0");
+  if (max_new == 0) return OSCAR_OK;
+  if (int rc = check_device()) return rc;
+  hipError_t e = oscar::launch_extend(*cache, rot_arg(rot_k), rot_arg(rot_v), q, n_q_heads, k_new, v_new, cu_new,
+                                      len_before, batch, max_new, max_prefix, sm_scale, out,
+                                      reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "extend_attn");
+  return OSCAR_OK;
+}
+
 size_t oscar_bf16_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                                          int32_t max_seq_len) {
   if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || max_seq_len < 1) return 0;

@@ -59,6 +59,14 @@ hipError_t launch_decode_bf16(const uint16_t *q, const uint16_t *kv, int64_t n_p
 
 size_t decode_bf16_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int max_seq_len);
 
+// Extend attention of the new tokens (rows cu_new[b] .. cu_new[b+1]-1 of q,
+// k_new, v_new) over the cached prefix of len_before[b] tokens plus the
+// chunk itself (causal); out fp32 [total][Hq][128].
+hipError_t launch_extend(const oscar_layer_cache &c, RotArg rk, RotArg rv, const uint16_t *q, int n_q_heads,
+                         const uint16_t *k_new, const uint16_t *v_new, const int32_t *cu_new,
+                         const int32_t *len_before, int batch, int max_new, int max_prefix, float sm_scale,
+                         float *out, hipStream_t s);
+
 // Calibration moments (device fp64).
 // cov[128][128] = (accumulate ? cov : 0) + sum over the n_vec vectors of
 // x x^T (not divided); part: calib_outer_part_bytes() of device scratch

@@ -288,6 +288,35 @@ OSCAR_API int oscar_decode_step(const oscar_layer_cache *cache,
                                 float *out, void *workspace,
                                 size_t workspace_bytes, oscar_stream_t stream);
 
+/* Extend (chunked-prefill) attention over the cache ([abs]: paged KV layouts
+ * with prefix caching; [nl]/[fr] §2.2.B: the fused kernel dequantises and
+ * inverse-rotates the INT2 history inside the attention).  Request b has a
+ * cached prefix of len_before[b] tokens (device int32 [batch], each in
+ * [0, max_prefix]) and new tokens at rows cu_new[b] .. cu_new[b+1]-1
+ * (device int32 [batch+1], non-decreasing, cu_new[0] = 0, at most max_new
+ * per request) of q (device bf16 [total_tokens][Hq][128]) and k_new, v_new
+ * (device bf16 [total_tokens][Hkv][128]), at positions len_before[b] + i.
+ * New token i attends to the whole prefix as oscar_decode_attn reads it
+ * (BF16 sink and recent window, INT2 history scored against q*R_K, its
+ * output part brought back with R_V^T once per query) and causally to new
+ * tokens 0..i of its request at bf16.  The chunk is not written: call
+ * oscar_write_kv with the same rows afterwards to append it.  Softmax scale
+ * sm_scale; query head h uses KV head h / (Hq/Hkv).  out: device fp32
+ * [total_tokens][Hq][128].  Needs no workspace.  A request whose length or
+ * chunk is out of range sets OSCAR_STATUS_BAD_LEN and leaves its rows
+ * unwritten; a page id out of range sets OSCAR_STATUS_BAD_PAGE and that
+ * page is left out. */
+OSCAR_API int oscar_extend_attn(const oscar_layer_cache *cache,
+                                const oscar_rotation *rot_k,
+                                const oscar_rotation *rot_v,
+                                const uint16_t *q, int32_t n_q_heads,
+                                const uint16_t *k_new, const uint16_t *v_new,
+                                const int32_t *cu_new, const int32_t *len_before,
+                                int32_t batch, int64_t total_tokens,
+                                int32_t max_new, int32_t max_prefix,
+                                float sm_scale, float *out,
+                                oscar_stream_t stream);
+
 /* Workspace for oscar_bf16_paged_decode. */
 OSCAR_API size_t oscar_bf16_decode_workspace_bytes(int32_t batch, int32_t n_q_heads,
                                          int32_t n_kv_heads,

@@ -199,3 +199,25 @@ def test_profile_events_needs_both_or_neither():
     assert lib.oscar_profile_events(ctypes.c_void_p(0x1000), None) == _lib.OSCAR_EINVAL and "both" in _err()
     assert lib.oscar_profile_events(None, ctypes.c_void_p(0x1000)) == _lib.OSCAR_EINVAL
     assert lib.oscar_profile_events(None, None) == _lib.OSCAR_OK
+
+
+def test_extend_validation_codes():
+    lib = _lib.load()
+    E = _lib
+
+    def call(c=None, hq=8, batch=1, total=16, max_new=16, max_prefix=100, scale=0.088, q=0xB000, cu=0x8000):
+        c = c if c is not None else _cache()
+        return lib.oscar_extend_attn(ctypes.byref(c), ctypes.byref(ROT), ctypes.byref(ROT), q, hq, 0x6000, 0x7000,
+                                     cu, 0x9000, batch, total, max_new, max_prefix, scale, 0xD000, None)
+    assert call(hq=6) == E.OSCAR_EUNSUPPORTED
+    assert call(c=_cache(group=48)) == E.OSCAR_EUNSUPPORTED
+    assert call(batch=0) == E.OSCAR_EINVAL
+    assert call(max_new=32, total=16) == E.OSCAR_EINVAL
+    assert call(max_prefix=-1) == E.OSCAR_EINVAL
+    assert call(max_prefix=10_000) == E.OSCAR_EINVAL and "hist_pt_stride" in _err()
+    assert call(scale=float("inf")) == E.OSCAR_EINVAL
+    assert call(q=0) == E.OSCAR_EINVAL
+    assert call(cu=0) == E.OSCAR_EINVAL
+    assert call(max_new=0, total=0, q=0) == E.OSCAR_OK
+    if NO_GPU:
+        assert call() == E.OSCAR_ENODEV

@@ -1,0 +1,127 @@
+"""GPU parity of the extend (chunked-prefill) attention against the oracle.
+
+Each case writes the prefix of every request with the oracle, uploads that
+cache, and runs oscar_extend_attn for the chunk that follows; both sides see
+identical cache bytes.  Outputs are compared under the decode tolerance
+(max |gpu - oracle| <= 2e-2, relative L2 <= 5e-3)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import oscar_ref as o
+from tests.parity_tools import Scenario, assert_decode_close, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+SCALE = 1.0 / math.sqrt(128)
+
+
+@pytest.fixture(scope="module")
+def oscar():
+    import bit_rotated_kv_oscar_amd as m
+    return m
+
+
+def _setup(oscar, seed, hq, hkv, G, prefix, chunk, rot="random", layer=0):
+    lens = [p + c for p, c in zip(prefix, chunk)]
+    sc = Scenario(seed, hq, hkv, G, lens, rot=rot, layer=layer)
+    ref = o.LayerCacheRef(hkv, G, sc.n_hist_pages, sc.n_bf16_pages, sc.hist_pt, sc.bf16_pt)
+    kp = np.concatenate([t[:n] for t, n in zip(sc.tok_k, prefix)])
+    vp = np.concatenate([t[:n] for t, n in zip(sc.tok_v, prefix)])
+    cu_p = np.concatenate([[0], np.cumsum(prefix)]).astype(np.int32)
+    ref.write(sc.R_K, sc.R_V, sc.clip_k, sc.clip_v, kp, vp, cu_p, np.zeros(len(prefix), np.int32))
+    kn = np.concatenate([t[p:] for t, p in zip(sc.tok_k, prefix)])
+    vn = np.concatenate([t[p:] for t, p in zip(sc.tok_v, prefix)])
+    cu = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    q = sc.ld.decode_q(int(cu[-1]), stream=synth.S_EVAL_Q)
+    dev = torch.device("cuda:0")
+    cache = oscar.LayerCache(hkv, G, sc.n_hist_pages, sc.n_bf16_pages, torch.from_numpy(sc.hist_pt),
+                             torch.from_numpy(sc.bf16_pt), device=dev)
+    cache.hist.copy_(torch.from_numpy(ref.hist))
+    cache.bf16.view(torch.int16).copy_(torch.from_numpy(ref.bf16.view(np.int16)))
+    rk, rv = oscar.Rotation(sc.R_K, sc.clip_k), oscar.Rotation(sc.R_V, sc.clip_v)
+    return sc, ref, cache, rk, rv, q, kn, vn, cu
+
+
+def _run(oscar, cache, rk, rv, q, kn, vn, cu, prefix, max_prefix=None):
+    chunk = np.diff(cu)
+    out = oscar.extend_attn(cache, rk, rv, to_dev_bf16(q), to_dev_bf16(kn), to_dev_bf16(vn),
+                            torch.from_numpy(cu).cuda(), torch.tensor(prefix, dtype=torch.int32, device="cuda"),
+                            int(chunk.max()), max(prefix) if max_prefix is None else max_prefix, SCALE)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("G", [32, 64, 128])
+def test_extend_ragged_prefixes_and_chunks(oscar, G):
+    # prefixes: none, inside the sink, sink only, ring only, exactly sink +
+    # window, one history token, several pages; chunks: ragged tiles, one
+    # token, whole tiles
+    prefix = [0, 5, 16, 100, 144, 145, 300, 700]
+    chunk = [37, 16, 1, 50, 17, 33, 64, 20]
+    sc, ref, cache, rk, rv, q, kn, vn, cu = _setup(oscar, 2000 + G, 8, 2, G, prefix, chunk)
+    out = _run(oscar, cache, rk, rv, q, kn, vn, cu, prefix)
+    assert int(cache.status.item()) == 0
+    exp = o.extend_attn(ref, sc.R_K, sc.R_V, q, kn, vn, cu, prefix, SCALE)
+    assert_decode_close(out, exp, f"extend G={G}")
+
+
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 2), (16, 2)])
+def test_extend_gqa_groups(oscar, hq, hkv):
+    prefix, chunk = [260, 31], [40, 70]
+    sc, ref, cache, rk, rv, q, kn, vn, cu = _setup(oscar, 2100 + hq, hq, hkv, 64, prefix, chunk)
+    out = _run(oscar, cache, rk, rv, q, kn, vn, cu, prefix)
+    exp = o.extend_attn(ref, sc.R_K, sc.R_V, q, kn, vn, cu, prefix, SCALE)
+    assert_decode_close(out, exp, f"extend hq={hq} hkv={hkv}")
+
+
+def test_extend_calibrated_long_prefix(oscar):
+    # calibrated rotations and clips, a prefix of many history pages
+    prefix, chunk = [2500], [48]
+    sc, ref, cache, rk, rv, q, kn, vn, cu = _setup(oscar, 2200, 8, 2, 64, prefix, chunk, rot="calibrated")
+    out = _run(oscar, cache, rk, rv, q, kn, vn, cu, prefix)
+    exp = o.extend_attn(ref, sc.R_K, sc.R_V, q, kn, vn, cu, prefix, SCALE)
+    assert_decode_close(out, exp, "extend calibrated")
+
+
+def test_extend_single_token_matches_decode_without_history(oscar):
+    # one new token over a prefix with no history equals the decode after
+    # appending it (both read the same bf16 values)
+    prefix, chunk = [0, 15, 100, 143], [1, 1, 1, 1]
+    sc, ref, cache, rk, rv, q, kn, vn, cu = _setup(oscar, 2300, 8, 2, 32, prefix, chunk)
+    out = _run(oscar, cache, rk, rv, q, kn, vn, cu, prefix)
+    oscar.write_kv(cache, rk, rv, to_dev_bf16(kn), to_dev_bf16(vn), torch.from_numpy(cu).cuda(),
+                   torch.tensor(prefix, dtype=torch.int32, device="cuda"), 1)
+    lens = torch.tensor([p + 1 for p in prefix], dtype=torch.int32, device="cuda")
+    dec = oscar.decode_attn(cache, rk, rv, to_dev_bf16(q), lens, 144, SCALE)
+    torch.cuda.synchronize()
+    assert_decode_close(out, dec.cpu().numpy(), "extend vs decode after append")
+    exp = o.extend_attn(ref, sc.R_K, sc.R_V, q, kn, vn, cu, prefix, SCALE)
+    assert_decode_close(out, exp, "extend single token")
+
+
+def test_extend_bad_page_and_length_are_flagged(oscar):
+    prefix, chunk = [400, 200], [20, 20]
+    sc, ref, cache, rk, rv, q, kn, vn, cu = _setup(oscar, 2400, 8, 2, 64, prefix, chunk)
+    # request 0: a history page id past the pool; request 1 is untouched
+    pt = sc.hist_pt.copy()
+    pt[0, 3] = sc.n_hist_pages + 5
+    cache.hist_pt.copy_(torch.from_numpy(pt))
+    out = _run(oscar, cache, rk, rv, q, kn, vn, cu, prefix)
+    assert int(cache.status.item()) & oscar._lib.STATUS_BAD_PAGE
+    exp = o.extend_attn(ref, sc.R_K, sc.R_V, q, kn, vn, cu, prefix, SCALE)
+    assert_decode_close(out[cu[1]:cu[2]], exp[cu[1]:cu[2]], "extend request beside a bad page")
+    # a prefix length above max_prefix: flagged, rows left as they were
+    cache.status.zero_()
+    cache.hist_pt.copy_(torch.from_numpy(sc.hist_pt))
+    sentinel = torch.full((int(cu[-1]), 8, 128), 7.0, device="cuda")
+    oscar.extend_attn(cache, rk, rv, to_dev_bf16(q), to_dev_bf16(kn), to_dev_bf16(vn), torch.from_numpy(cu).cuda(),
+                      torch.tensor(prefix, dtype=torch.int32, device="cuda"), 20, 300, SCALE, out=sentinel)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) & oscar._lib.STATUS_BAD_LEN
+    s = sentinel.cpu().numpy()
+    assert np.all(s[:cu[1]] == 7.0)
+    assert_decode_close(s[cu[1]:], exp[cu[1]:], "extend request beside a bad length")
