@@ -14,6 +14,11 @@ and replayed; sequence lengths advance on the device each replay.
 `--workload bs64` runs the batch-64 configuration (per-request lengths
 uniform in [8192, 32768], pages of all requests interleaved in one pool).
 
+`--workload extend` runs the extend (chunked-prefill) attention: per layer, a
+4096-token chunk attends to its 28672-token cached prefix and causally to
+itself (Qwen3-8B-shaped, 36 layers, G = 64); its line names its own metric
+(TFLOP/s against the matrix-core peak).
+
 `--workload write` runs the fused write path at prefill (Qwen3-4B-shaped,
 36 layers, 32 q / 8 KV heads, G = 32): one step writes 8 prompts x 32768 new
 tokens into every layer's cache (rotate, clip, INT2-pack, page-store; sink and
@@ -47,7 +52,7 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", choices=["bs1", "bs64", "write", "28x100k"], default=None,
+    p.add_argument("--workload", choices=["bs1", "bs64", "write", "28x100k", "extend"], default=None,
                    help="default: bs1, with the bs64 figures added to its line")
     p.add_argument("--no-companion", action="store_true", help="default run: leave out the bs64 figures")
     p.add_argument("--layers", type=int, default=None, help="override the layer count (testing only)")
@@ -76,6 +81,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 DOMINANT = {"bs1": ("attend_kernel", ["decode_int2.hip", "attn_common.h", "common.h"]),
             "bs64": ("attend_kernel", ["decode_int2.hip", "attn_common.h", "common.h"]),
             "write": ("write_hist_kernel", ["write.hip", "common.h"]),
+            "extend": ("extend_kernel", ["extend.hip", "attn_common.h", "common.h"]),
             "28x100k": ("attend_kernel", ["decode_int2.hip", "attn_common.h", "common.h"])}
 
 
@@ -150,6 +156,12 @@ WORKLOADS = {
                     bf16_bytes_note="all-BF16 cache of the same tokens: 734 GB, beyond one GPU's 288 GB"),
 }
 WRITE_METRIC = "INT2 fused KV write GB/s (% HBM peak) + tokens/s, prefill 8 x 32K, 36 layers"
+WORKLOADS["extend"] = dict(
+    name="qwen3-8b-shaped extend attention (chunked prefill) over a cached INT2 + BF16 prefix, 36 layers, "
+         "batch 1, prefix 28672 + chunk 4096, G 64",
+    layers=36, hq=32, hkv=8, G=64, batch=1, len_lo=28672, len_hi=28672, chunk=4096)
+EXTEND_METRIC = "INT2 extend-attn TFLOP/s (% MFMA peak) + tokens/s, prefix 28672 + chunk 4096, 36 layers"
+MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16 matrix-core peak
 
 
 def n_hist_tokens(L):
@@ -251,6 +263,9 @@ def main():
         W["layers"] = args.layers
     if args.workload == "write":
         write_main(args, W, dev)
+        return
+    if args.workload == "extend":
+        extend_main(args, W, dev)
         return
     line = decode_main(args, W, dev, args.workload)
     if workload_default and not args.no_companion:
@@ -641,6 +656,151 @@ def write_main(args, W, dev):
         "setup_s": round(setup_s, 1),
     }
     print(json.dumps(line))
+
+
+def extend_flops(prefix, chunk, hq):
+    """Algorithmic flops of one extend call: every new token i of a request
+    scores and weights prefix + i + 1 keys per query head (2 flops per
+    multiply-add, QK^T and PV)."""
+    return sum(hq * 4 * HEAD_DIM * (n * L0 + n * (n + 1) // 2) for L0, n in zip(prefix, chunk))
+
+
+def extend_main(args, W, dev):
+    """The extend workload: per layer, the new chunk of every request attends
+    to its cached prefix (sink + INT2 history + recent window) and causally to
+    itself.  The prefix caches are written once (untimed)."""
+    import numpy as np
+    import torch
+
+    import bit_rotated_kv_oscar_amd as oscar
+    import synth
+
+    nl, hq, hkv, G, B = W["layers"], W["hq"], W["hkv"], W["G"], W["batch"]
+    L0, n = int(W["len_hi"]), int(W["chunk"])
+    steps, warm = args.steps, args.warmup
+    t_setup = time.time()
+    prefix = np.full(B, L0, dtype=np.int32)
+    cu = torch.from_numpy(np.arange(B + 1, dtype=np.int32) * n).to(dev)
+    lb = torch.from_numpy(prefix).to(dev)
+    zeros = torch.zeros(B, dtype=torch.int32, device=dev)
+    cu_pre = torch.from_numpy(np.arange(B + 1, dtype=np.int32) * L0).to(dev)
+
+    class Layer:
+        pass
+
+    layers = []
+    for l in range(nl):
+        ly = Layer()
+        ld = synth.LayerData(args.seed, l, hq, hkv)
+        qc = synth.q_device(synth.device_generator(args.seed, l, synth.S_CAL_Q), 2048, hq, ld.lam, dev)
+        kc = synth.kv_device(synth.device_generator(args.seed, l, synth.S_CAL_K), 2048, ld.outliers, dev)
+        vc = synth.kv_device(synth.device_generator(args.seed, l, synth.S_CAL_V), 2048, ld.outliers, dev)
+        R_K, R_V, ck, cv = oscar.calibrate_rotation(qc, kc, vc, 0.999)
+        ly.rk, ly.rv = oscar.Rotation(R_K, ck, dev), oscar.Rotation(R_V, cv, dev)
+        full = prefix + n
+        pages = [synth.hist_pages_needed(int(x)) for x in full]
+        hist_pt, n_pool = synth.shuffled_page_tables(args.seed, l, full, n_pool_pages=sum(pages) + 1)
+        ly.cache = oscar.LayerCache(hkv, G, n_pool, 9 * B, torch.from_numpy(hist_pt),
+                                    torch.from_numpy(synth.bf16_page_tables(B, shuffle_seed=args.seed + l)),
+                                    device=dev)
+        kp = synth.kv_device(synth.device_generator(args.seed, l, synth.S_CACHE_K), B * L0, ld.outliers, dev)
+        vp = synth.kv_device(synth.device_generator(args.seed, l, synth.S_CACHE_V), B * L0, ld.outliers, dev)
+        oscar.write_kv(ly.cache, ly.rk, ly.rv, kp, vp, cu_pre, zeros, L0)
+        ly.k = synth.kv_device(synth.device_generator(args.seed, l, synth.S_NEW_K), B * n, ld.outliers, dev)
+        ly.v = synth.kv_device(synth.device_generator(args.seed, l, synth.S_NEW_V), B * n, ld.outliers, dev)
+        ly.q = synth.q_device(synth.device_generator(args.seed, l, synth.S_DEC_Q), B * n, hq, ld.lam, dev)
+        ly.out = torch.empty((B * n, hq, HEAD_DIM), dtype=torch.float32, device=dev)
+        layers.append(ly)
+        del qc, kc, vc, kp, vp
+        if (l + 1) % 6 == 0 or l + 1 == nl:
+            torch.cuda.synchronize()
+            print(f"setup: {l + 1}/{nl} layers calibrated and prefilled ({time.time() - t_setup:.0f} s)",
+                  file=sys.stderr, flush=True)
+    setup_s = time.time() - t_setup
+    scale = 1 / math.sqrt(HEAD_DIM)
+
+    def step():
+        for ly in layers:
+            oscar.extend_attn(ly.cache, ly.rk, ly.rv, ly.q, ly.k, ly.v, cu, lb, n, L0, scale, out=ly.out)
+
+    stream = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(stream):
+        for _ in range(warm):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_per_step = e0.elapsed_time(e1) / steps
+        pairs = []
+        for ly in layers:
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            a1.record(stream)
+            oscar.profile_events(a0, a1)
+            oscar.extend_attn(ly.cache, ly.rk, ly.rv, ly.q, ly.k, ly.v, cu, lb, n, L0, scale, out=ly.out)
+            pairs.append((a0, a1))
+        torch.cuda.synchronize()
+    for ly in layers:
+        assert int(ly.cache.status.item()) == 0, "extend flagged bad data"
+        assert torch.isfinite(ly.out).all(), "non-finite extend output"
+    kern_us = float(np.mean([a.elapsed_time(b) for a, b in pairs])) * 1e3
+    fl = extend_flops(prefix.tolist(), [n] * B, hq)
+    tflops = nl * fl / (ms_per_step * 1e-3) / 1e12
+    achieved = fl / (kern_us * 1e-6) / 1e12
+    cpu = None if args.no_cpu_baseline else extend_cpu_baseline(args, W)
+    line = {
+        "metric": EXTEND_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+        "warmup": warm, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": W["name"], "layers": nl, "batch": B, "q_heads": hq, "kv_heads": hkv, "group": G,
+                   "prefix": L0, "chunk": n,
+                   "step": "per layer: oscar_extend_attn of the chunk over the cached prefix (INT2 history "
+                           "scored on exact codes against q R_K, BF16 sink / window / chunk raw, causal chunk)"},
+        "tokens_per_s": round(B * n / (ms_per_step * 1e-3), 1),
+        "pct_mfma_peak": round(100 * tflops / MFMA_PEAK_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_PEAK_TFLOPS, 4), "traffic": measured_traffic("extend"),
+                     "kernel": f"oscar::extend_kernel<4, {G}> (INT2 + BF16 extend attention)",
+                     "avg_launch_us": round(kern_us, 2), "flops_per_launch": int(fl)},
+        "cpu_baseline": cpu,
+        "setup_s": round(setup_s, 1),
+    }
+    print(json.dumps(line))
+
+
+def extend_cpu_baseline(args, W):
+    """The fp64 oracle's extend timed on the host on a bounded sample: one
+    layer, one request, the first 8 tokens of the chunk over the full prefix
+    (the prefix written untimed); reported in algorithmic TFLOP/s."""
+    import numpy as np
+
+    import synth
+    from oracle import oscar_ref as o
+    try:
+        import threadpoolctl
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    hq, hkv, G = W["hq"], W["hkv"], W["G"]
+    L0, m = int(W["len_hi"]), 8
+    ld = synth.LayerData(args.seed + 1000, 0, hq, hkv)
+    k, v = ld.cache_kv(L0 + m)
+    R = np.linalg.qr(np.random.default_rng(args.seed).standard_normal((128, 128)))[0]
+    pt, npool = synth.shuffled_page_tables(args.seed, 0, [L0 + m])
+    ref = o.LayerCacheRef(hkv, G, npool, 9, pt, synth.bf16_page_tables(1))
+    ref.write(R, R, 6.0, 6.0, k[:L0], v[:L0], [0, L0], [0])
+    q = ld.decode_q(m)
+    t0 = time.time()
+    o.extend_attn(ref, R, R, q, k[L0:], v[L0:], [0, m], [L0], 1 / math.sqrt(HEAD_DIM))
+    dt = time.time() - t0
+    fl = extend_flops([L0], [m], hq)
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {m} chunk tokens of one request over its {L0}-token prefix, one layer (Hq {hq}, "
+                      f"Hkv {hkv}, G {G}): {dt:.1f} s, {m / dt:.2f} tokens/s"}
 
 
 def write_cpu_baseline(args, W, bytes_per_token):

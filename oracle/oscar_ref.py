@@ -534,7 +534,7 @@ def decode_attn(cache: LayerCacheRef, rot_k, rot_v, q_bits: np.ndarray, seq_lens
 
 
 def extend_attn(cache: LayerCacheRef, rot_k, rot_v, q_bits: np.ndarray, k_new: np.ndarray,
-                v_new: np.ndarray, cu_new, len_before, sm_scale: float) -> np.ndarray:
+                v_new: np.ndarray, cu_new, len_before, sm_scale: float, rows=None) -> np.ndarray:
     """Chunked-prefill ("extend") attention of new tokens over a cached prefix
     ([abs]: paged layouts with prefix caching; [nl]/[fr] section 2.2.B: the
     fused kernel reads the INT2 history, dequantises and inverse-rotates it).
@@ -545,19 +545,25 @@ def extend_attn(cache: LayerCacheRef, rot_k, rot_v, q_bits: np.ndarray, k_new: n
     (bf16 bits, [T][Hq or Hkv][128]), at positions len_before[b] + i; new
     token i attends to the whole prefix and to new tokens 0..i at full bf16
     precision (causal).  The chunk is not written here.  Returns
-    [T][Hq][128] fp64."""
+    [T][Hq][128] fp64; with rows (indices into the T rows) only those rows
+    are computed and returned, in that order."""
     q = bf16_to_f64(q_bits)
     out = np.empty(q.shape)
+    want = None if rows is None else set(int(r) for r in rows)
     for b in range(len(len_before)):
         L0 = int(len_before[b])
         r0, r1 = int(cu_new[b]), int(cu_new[b + 1])
+        if want is not None and not any(r0 <= r < r1 for r in want):
+            continue
         Kp, Vp = cache.gather(b, L0, rot_k, rot_v)
         Kn, Vn = bf16_to_f64(k_new[r0:r1]), bf16_to_f64(v_new[r0:r1])
         for i in range(r1 - r0):
+            if want is not None and r0 + i not in want:
+                continue
             K = np.concatenate([Kp, Kn[:i + 1]])
             V = np.concatenate([Vp, Vn[:i + 1]])
             out[r0 + i] = attention(q[r0 + i], K, V, sm_scale)
-    return out
+    return out if rows is None else out[np.asarray(rows, dtype=np.int64)]
 
 
 def bf16_paged_decode(q_bits, kv_pages, pt, seq_lens, sm_scale) -> np.ndarray:

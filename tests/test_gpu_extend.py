@@ -125,3 +125,20 @@ def test_extend_bad_page_and_length_are_flagged(oscar):
     s = sentinel.cpu().numpy()
     assert np.all(s[:cu[1]] == 7.0)
     assert_decode_close(s[cu[1]:], exp[cu[1]:], "extend request beside a bad length")
+
+
+def test_extend_bench_shape_sampled_rows(oscar):
+    # the timed shape of the extend workload (one layer): Hq 32 / Hkv 8, G 64,
+    # prefix 28672 + chunk 4096, in the launch the benchmark uses; rows at the
+    # chunk's start, tile edges and end are checked against the oracle
+    import time
+    t0 = time.time()
+    L0, n = 28672, 4096
+    sc, ref, cache, rk, rv, q, kn, vn, cu = _setup(oscar, 2500, 32, 8, 64, [L0], [n])
+    print(f"setup {time.time() - t0:.1f} s", flush=True)
+    out = _run(oscar, cache, rk, rv, q, kn, vn, cu, [L0])
+    assert int(cache.status.item()) == 0
+    rows = [0, 1, 15, 16, 2047, 2048, 4079, 4095]
+    exp = o.extend_attn(ref, sc.R_K, sc.R_V, q, kn, vn, cu, [L0], SCALE, rows=rows)
+    print(f"oracle done {time.time() - t0:.1f} s", flush=True)
+    assert_decode_close(out[rows], exp, "extend bench shape")

@@ -839,3 +839,15 @@ def test_extend_single_token_short_prefix_equals_decode_after_append():
         out = o.extend_attn(pre, R, Rv, q, k[L0:L0 + 1], v[L0:L0 + 1], [0, 1], [L0], 0.088)
         ref = o.decode_attn(c, R, Rv, q, [L0 + 1], 0.088)
         np.testing.assert_allclose(out, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_extend_selected_rows_equal_full_rows():
+    prefix, T = 170, 21
+    c, k, v, q, R, Rv = _filled(prefix + T)
+    pre = _make_cache(prefix + T)
+    pre.write(R, Rv, 6.0, 6.0, k[:prefix], v[:prefix], [0, prefix], [0])
+    qs = synth.LayerData(8, 0, 8, 2).decode_q(T)
+    full = o.extend_attn(pre, R, Rv, qs, k[prefix:], v[prefix:], [0, T], [prefix], 0.088)
+    rows = [20, 0, 7]
+    part = o.extend_attn(pre, R, Rv, qs, k[prefix:], v[prefix:], [0, T], [prefix], 0.088, rows=rows)
+    np.testing.assert_array_equal(part, full[rows])
