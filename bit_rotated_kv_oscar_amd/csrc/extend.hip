@@ -51,7 +51,22 @@ struct ExtendArgs {
 
 constexpr int EXT_TILE = 16;
 
-__device__ inline float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+// Max / sum over the four lanes l, l^16, l^32, l^48 that hold one query
+// (row swaps between lanes, no LDS round trip); every one of them receives it.
+__device__ inline float lanes4_max(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float lanes4_sum(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float m = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 // bf16 bits of x, round to nearest even (x finite)
 __device__ inline uint32_t bf16_rne(float x) {
@@ -85,45 +100,55 @@ __device__ inline f16x4 codes_v(uint32_t w0, uint32_t w1, int r) {
   return expand_v(w0, w1, r) * m - m;
 }
 
-template <int NG>
-struct ExtState {
-  f32x4 acc_r[8];  // history part, rotated basis: channel 16 b + 4 (l/16) + r
-  f32x4 acc_p[8];  // BF16 part: channel 32 (b/2) + 2 (4 (l/16) + r) + b%2
-  float zacc[NG];  // sum_t p_t z_t of the lane's keys, per group
-  float m, l;      // running max (log2 units) of the lane's query; lane-partial sum
+// Online-softmax state of one part of the keys: the BF16 keys (sink, window,
+// chunk; acc = O^T in the original basis) or the INT2 history (acc = O^T in
+// the rotated basis, plus the zero-point sums per group).  The two parts are
+// merged at the end, so only one part's accumulators are live at a time.
+template <int NZ>
+struct SoftState {
+  f32x4 acc[8];
+  float zacc[NZ > 0 ? NZ : 1];  // sum_t p_t z_t of the lane's keys, per group
+  float m, l;                   // running max (log2 units) of the lane's query; lane-partial sum
+  __device__ void init() {
+    for (int b = 0; b < 8; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < (NZ > 0 ? NZ : 1); ++g) zacc[g] = 0.f;
+    m = -INFINITY;
+    l = 0.f;
+  }
 };
 
 // Online softmax over one tile: s[r] = scaled score of key 4(l/16)+r for the
 // lane's query (-inf where masked); p[r] receives the probabilities relative
-// to the updated running max, and every accumulator is rescaled.
-template <int NG>
-__device__ inline void softmax_tile(ExtState<NG> &st, const float (&s)[4], float (&p)[4]) {
-  float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-  mx = fmaxf(mx, shfl_xor(mx, 16));
-  mx = fmaxf(mx, shfl_xor(mx, 32));
-  const float mn = fmaxf(st.m, mx);
-  const float ref = mn == -INFINITY ? 0.f : mn;
-  const float alpha = exp2f(st.m - ref);
+// to the running max.  The running max is raised only when a score exceeds it
+// by more than 2^LAZY_TH (so p <= 2^LAZY_TH); the accumulators are rescaled
+// only in the waves where some query's max was raised.
+template <int NZ>
+__device__ inline void softmax_tile(SoftState<NZ> &st, const float (&s)[4], float (&p)[4]) {
+  const float mx = lanes4_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+  const bool raise = mx > st.m + LAZY_TH;  // false while both are -inf
+  if (__builtin_amdgcn_ballot_w64(raise)) {
+    const float mn = raise ? mx : st.m;
+    const float alpha = raise ? __builtin_amdgcn_exp2f(st.m - mn) : 1.f;  // st.m = -inf: 0
+    st.l *= alpha;
+    for (int b = 0; b < 8; ++b) st.acc[b] *= alpha;
+    for (int g = 0; g < NZ; ++g) st.zacc[g] *= alpha;
+    st.m = mn;
+  }
+  const float ref = st.m == -INFINITY ? 0.f : st.m;
   float sum = 0.f;
   for (int r = 0; r < 4; ++r) {
-    p[r] = exp2f(s[r] - ref);
+    p[r] = __builtin_amdgcn_exp2f(s[r] - ref);
     sum += p[r];
   }
-  st.l = st.l * alpha + sum;
-  st.m = mn;
-  for (int b = 0; b < 8; ++b) {
-    st.acc_r[b] *= alpha;
-    st.acc_p[b] *= alpha;
-  }
-  for (int g = 0; g < NG; ++g) st.zacc[g] *= alpha;
+  st.l += sum;
 }
 
 // One tile of 16 raw bf16 keys: key t's K row at kp + t * stride (elements),
 // V row at vp + t * stride, for t < nrows; rows t >= nrows are not read (their
 // loads repeat row 0).  valid(t, i) says whether key t is visible to query i
 // of the tile, valid(t, -1) whether key t exists at all.
-template <int NG, class Valid>
-__device__ inline void bf16_tile(ExtState<NG> &st, const uint16_t *kp, const uint16_t *vp, int64_t stride,
+template <class Valid>
+__device__ inline void bf16_tile(SoftState<0> &st, const uint16_t *kp, const uint16_t *vp, int64_t stride,
                                  int nrows, const bf16x8 (&qb)[4], float scale_log2, int lane, Valid valid) {
   const int kq = lane >> 4, m = lane & 15;
   // scores S^T[t][i] = K[t] . q[i]
@@ -157,35 +182,47 @@ __device__ inline void bf16_tile(ExtState<NG> &st, const uint16_t *kp, const uin
     const uint32_t o1 = __builtin_amdgcn_perm(u[3], u[2], 0x07060302u);
     const s16x4 ae = __builtin_bit_cast(s16x4, u32x2{e0, e1});
     const s16x4 ao = __builtin_bit_cast(s16x4, u32x2{o0, o1});
-    st.acc_p[2 * c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ae, phi, st.acc_p[2 * c], 0, 0, 0);
-    st.acc_p[2 * c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ae, plo, st.acc_p[2 * c], 0, 0, 0);
-    st.acc_p[2 * c + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ao, phi, st.acc_p[2 * c + 1], 0, 0, 0);
-    st.acc_p[2 * c + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ao, plo, st.acc_p[2 * c + 1], 0, 0, 0);
+    st.acc[2 * c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ae, phi, st.acc[2 * c], 0, 0, 0);
+    st.acc[2 * c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ae, plo, st.acc[2 * c], 0, 0, 0);
+    st.acc[2 * c + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ao, phi, st.acc[2 * c + 1], 0, 0, 0);
+    st.acc[2 * c + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ao, plo, st.acc[2 * c + 1], 0, 0, 0);
   }
 }
 
-// One INT2 history page (block of one KV head), rows < n_valid.
+// One INT2 history page (block of one KV head): the lane's code dwords and
+// the scale / zero entries of its four keys per group.
+template <int NG>
+struct HistData {
+  u32x2 kc, vc;
+  u32x4 km[NG], vm[NG];
+};
+
 template <int G>
-__device__ inline void hist_tile(ExtState<D / G> &st, const uint8_t *blk, int n_valid, const f16x8 (&qh)[4],
+__device__ inline void hist_load(HistData<D / G> &hd, const uint8_t *blk, int lane) {
+  const int kq = lane >> 4;
+  hd.kc = *reinterpret_cast<const u32x2 *>(blk + k_codes_off(G) + 8 * lane);
+  hd.vc = *reinterpret_cast<const u32x2 *>(blk + v_codes_off(G) + 8 * lane);
+  for (int g = 0; g < D / G; ++g) {
+    hd.km[g] = *reinterpret_cast<const u32x4 *>(blk + k_meta_off(G) + 4 * (16 * g + 4 * kq));
+    hd.vm[g] = *reinterpret_cast<const u32x4 *>(blk + v_meta_off(G) + 4 * (16 * g + 4 * kq));
+  }
+}
+
+// Attention over one loaded history page, rows < n_valid.
+template <int G>
+__device__ inline void hist_tile(SoftState<D / G> &st, const HistData<D / G> &hd, int n_valid, const f16x8 (&qh)[4],
                                  const f16x8 (&ql)[4], const float (&qs)[D / G], float scale_log2, int lane) {
   constexpr int NG = D / G;
   const int kq = lane >> 4;
-  const u32x2 kc = *reinterpret_cast<const u32x2 *>(blk + k_codes_off(G) + 8 * lane);
-  const u32x2 vc = *reinterpret_cast<const u32x2 *>(blk + v_codes_off(G) + 8 * lane);
-  u32x4 km[NG], vm[NG];
-  for (int g = 0; g < NG; ++g) {
-    km[g] = *reinterpret_cast<const u32x4 *>(blk + k_meta_off(G) + 4 * (16 * g + 4 * kq));
-    vm[g] = *reinterpret_cast<const u32x4 *>(blk + v_meta_off(G) + 4 * (16 * g + 4 * kq));
-  }
   float s[4] = {0.f, 0.f, 0.f, 0.f};
   for (int g = 0; g < NG; ++g) {
     f32x4 d = {0.f, 0.f, 0.f, 0.f};
     for (int kb = g * G / 32; kb < (g + 1) * G / 32; ++kb) {
-      const f16x8 c = codes_k(kc[0], kc[1], kb);
+      const f16x8 c = codes_k(hd.kc[0], hd.kc[1], kb);
       d = mfma_k(c, ql[kb], d);
       d = mfma_k(c, qh[kb], d);
     }
-    for (int r = 0; r < 4; ++r) s[r] += lo_f16(km[g][r]) * d[r] + hi_f16(km[g][r]) * qs[g];
+    for (int r = 0; r < 4; ++r) s[r] += lo_f16(hd.km[g][r]) * d[r] + hi_f16(hd.km[g][r]) * qs[g];
   }
   bool ok[4];
   float p[4];
@@ -197,15 +234,15 @@ __device__ inline void hist_tile(ExtState<D / G> &st, const uint8_t *blk, int n_
   for (int g = 0; g < NG; ++g) {
     float ps[4];
     for (int r = 0; r < 4; ++r) {
-      ps[r] = ok[r] ? p[r] * lo_f16(vm[g][r]) : 0.f;
-      st.zacc[g] += ok[r] ? p[r] * hi_f16(vm[g][r]) : 0.f;
+      ps[r] = ok[r] ? p[r] * lo_f16(hd.vm[g][r]) : 0.f;
+      st.zacc[g] += ok[r] ? p[r] * hi_f16(hd.vm[g][r]) : 0.f;
     }
     f16x4 bh, bl;
     split_f16(ps, bh, bl);
     for (int b = g * G / 16; b < (g + 1) * G / 16; ++b) {
-      const f16x4 a = codes_v(vc[0], vc[1], b);
-      st.acc_r[b] = mfma_v(a, bl, st.acc_r[b]);
-      st.acc_r[b] = mfma_v(a, bh, st.acc_r[b]);
+      const f16x4 a = codes_v(hd.vc[0], hd.vc[1], b);
+      st.acc[b] = mfma_v(a, bl, st.acc[b]);
+      st.acc[b] = mfma_v(a, bh, st.acc[b]);
     }
   }
 }
@@ -214,9 +251,10 @@ template <int GQA, int G>
 __global__ void __launch_bounds__(64 * (GQA < 4 ? GQA : 4)) extend_kernel(ExtendArgs a) {
   constexpr int WAVES = GQA < 4 ? GQA : 4;
   constexpr int NG = D / G;
-  __shared__ float buf_all[WAVES][EXT_TILE * D];
+  __shared__ float buf_all[WAVES][2][EXT_TILE * D];
   const int lane = threadIdx.x & 63, w = wave_id();
-  float *buf = buf_all[w];
+  float *buf = buf_all[w][0];   // q staging, then the history part of the output
+  float *bufp = buf_all[w][1];  // the BF16 part of the output
   const int b = __builtin_amdgcn_workgroup_id_z();
   const int h = __builtin_amdgcn_workgroup_id_y() * WAVES + w;
   const int kh = h / GQA;
@@ -276,16 +314,7 @@ __global__ void __launch_bounds__(64 * (GQA < 4 ? GQA : 4)) extend_kernel(Extend
       qs[(32 * kb) / G] += x;
     }
   }
-  for (int g = 0; g < NG; ++g) {
-    qs[g] += shfl_xor(qs[g], 16);
-    qs[g] += shfl_xor(qs[g], 32);
-  }
-
-  ExtState<NG> st;
-  for (int i = 0; i < 8; ++i) st.acc_r[i] = st.acc_p[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int g = 0; g < NG; ++g) st.zacc[g] = 0.f;
-  st.m = -INFINITY;
-  st.l = 0.f;
+  for (int g = 0; g < NG; ++g) qs[g] = lanes4_sum(qs[g]);
 
   const int32_t *bpt = a.bf16_pt + int64_t(b) * BF16_PT;
   const int64_t page_elems = int64_t(2) * PAGE * D;  // K and V of one head
@@ -299,67 +328,94 @@ __global__ void __launch_bounds__(64 * (GQA < 4 ? GQA : 4)) extend_kernel(Extend
     return true;
   };
 
-  // ---- prefix: sink page
+  // ======== BF16 keys: sink, recent window, the chunk
+  SoftState<0> sp;
+  sp.init();
   if (L0 > 0) {
     const uint16_t *kp;
     if (bf16_page(0, kp)) {
       const int ns = L0 < N_SINK ? L0 : N_SINK;
-      bf16_tile(st, kp, kp + PAGE * D, D, PAGE, qb, a.scale_log2, lane, [&](int t, int) { return t < ns; });
+      bf16_tile(sp, kp, kp + PAGE * D, D, PAGE, qb, a.scale_log2, lane, [&](int t, int) { return t < ns; });
     }
   }
-  // ---- prefix: INT2 history pages
-  const int nht = n_hist_tokens(L0), nhp = n_hist_pages(L0);
-  const int32_t *hpt = a.hist_pt + int64_t(b) * a.hist_pt_stride;
-  const int blk_bytes = hist_block_bytes(G);
-#pragma unroll 1
-  for (int j = 0; j < nhp; ++j) {
-    const int pid = __builtin_amdgcn_readfirstlane(hpt[j]);
-    if (pid < 0 || pid >= a.n_hist_pages) {
-      if (lane == 0) flag_status(a.status, OSCAR_STATUS_BAD_PAGE);
-      continue;
-    }
-    const uint8_t *blk = a.hist + (int64_t(pid) * a.hkv + kh) * blk_bytes;
-    const int nv = nht - PAGE * j < PAGE ? nht - PAGE * j : PAGE;
-    hist_tile<G>(st, blk, nv, qh, ql, qs, a.scale_log2, lane);
-  }
-  // ---- prefix: recent window (ring slot s holds position L0 - 128 + ((s - L0) mod 128))
+  // ring slot s holds position L0 - 128 + ((s - L0) mod 128)
   if (L0 > N_SINK) {
 #pragma unroll 1
     for (int rp = 0; rp < N_RECENT / PAGE; ++rp) {
       const uint16_t *kp;
       if (!bf16_page(1 + rp, kp)) continue;
-      bf16_tile(st, kp, kp + PAGE * D, D, PAGE, qb, a.scale_log2, lane, [&](int t, int) {
+      bf16_tile(sp, kp, kp + PAGE * D, D, PAGE, qb, a.scale_log2, lane, [&](int t, int) {
         const int s = PAGE * rp + t;
         const int pos = L0 - N_RECENT + (((s - L0) % N_RECENT) + N_RECENT) % N_RECENT;
         return pos >= N_SINK;
       });
     }
   }
-  // ---- the chunk itself, causal: key j visible to query i iff j <= i
+  // the chunk itself, causal: key j visible to query i iff j <= i
   const int64_t nstride = int64_t(a.hkv) * D;
 #pragma unroll 1
   for (int j0 = 0; j0 <= t0; j0 += EXT_TILE) {
     const int nk = n - j0 < EXT_TILE ? n - j0 : EXT_TILE;  // keys of this tile that exist
     const uint16_t *kp = a.k_new + (int64_t(r0 + j0) * a.hkv + kh) * D;
     const uint16_t *vp = a.v_new + (int64_t(r0 + j0) * a.hkv + kh) * D;
-    bf16_tile(st, kp, vp, nstride, nk, qb, a.scale_log2, lane, [&](int t, int i) {
+    bf16_tile(sp, kp, vp, nstride, nk, qb, a.scale_log2, lane, [&](int t, int i) {
       return t < nk && (i < 0 || j0 + t <= t0 + i);
     });
   }
+  // park the BF16 accumulator in LDS (bufp[c][16], unnormalised)
+  for (int bb = 0; bb < 8; ++bb)
+    for (int r = 0; r < 4; ++r) {
+      const int c = 32 * (bb >> 1) + 2 * (4 * kq + r) + (bb & 1);
+      bufp[c * EXT_TILE + m] = sp.acc[bb][r];
+    }
+  const float m1 = sp.m, l1 = lanes4_sum(sp.l);
 
-  // ---- epilogue: totals over the four lanes of each query
-  st.l += shfl_xor(st.l, 16);
-  st.l += shfl_xor(st.l, 32);
-  for (int g = 0; g < NG; ++g) {
-    st.zacc[g] += shfl_xor(st.zacc[g], 16);
-    st.zacc[g] += shfl_xor(st.zacc[g], 32);
+  // ======== INT2 history pages
+  SoftState<NG> sh;
+  sh.init();
+  const int nht = n_hist_tokens(L0), nhp = n_hist_pages(L0);
+  const int32_t *hpt = a.hist_pt + int64_t(b) * a.hist_pt_stride;
+  const int blk_bytes = hist_block_bytes(G);
+  // page ids 64 at a time (lane i: page j0 + i, -1 past the end); the next
+  // page's data is loaded while the current one is computed
+  auto page_block = [&](int pid) -> const uint8_t * { return a.hist + (int64_t(pid) * a.hkv + kh) * blk_bytes; };
+  auto bad_page = [&](int pid) { return pid < 0 || pid >= a.n_hist_pages; };
+  if (nhp > 0) {
+    int ids = lane < nhp ? hpt[lane] : -1;
+    int pid = __builtin_amdgcn_readfirstlane(ids);
+    HistData<NG> cur, nxt;
+    if (!bad_page(pid)) hist_load<G>(cur, page_block(pid), lane);  // a bad page is never read
+#pragma unroll 1
+    for (int j = 0; j < nhp; ++j) {
+      const int jn = j + 1;
+      int pid_n = -1;
+      if (jn < nhp) {
+        if ((jn & 63) == 0) ids = jn + lane < nhp ? hpt[jn + lane] : -1;
+        pid_n = __builtin_amdgcn_readlane(ids, jn & 63);
+        if (!bad_page(pid_n)) hist_load<G>(nxt, page_block(pid_n), lane);
+      }
+      if (bad_page(pid)) {
+        if (lane == 0) flag_status(a.status, OSCAR_STATUS_BAD_PAGE);
+      } else {
+        const int nv = nht - PAGE * j < PAGE ? nht - PAGE * j : PAGE;
+        hist_tile<G>(sh, cur, nv, qh, ql, qs, a.scale_log2, lane);
+      }
+      cur = nxt;
+      pid = pid_n;
+    }
   }
-  // rotated part (+ zero-point sums) into buf[c][16], then times R_V^T
-  __syncthreads();
+
+  // ======== merge: o = (f2 (acc_r + z) R_V^T + f1 acc_p) / (f1 l1 + f2 l2)
+  const float l2 = lanes4_sum(sh.l);
+  for (int g = 0; g < NG; ++g) sh.zacc[g] = lanes4_sum(sh.zacc[g]);
+  const float mm = fmaxf(m1, sh.m);  // finite: every query sees at least itself
+  const float f1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+  const float f2 = sh.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sh.m - mm);
+  const float inv = 1.f / (f1 * l1 + f2 * l2);
   for (int bb = 0; bb < 8; ++bb)
     for (int r = 0; r < 4; ++r) {
       const int c = 16 * bb + 4 * kq + r;
-      buf[c * EXT_TILE + m] = st.acc_r[bb][r] + st.zacc[c / G];
+      buf[c * EXT_TILE + m] = (sh.acc[bb][r] + sh.zacc[c / G]) * f2;
     }
   __syncthreads();
   float o[EXT_TILE][2];
@@ -376,22 +432,12 @@ __global__ void __launch_bounds__(64 * (GQA < 4 ? GQA : 4)) extend_kernel(Extend
       }
     }
   }
-  __syncthreads();
-  // BF16 part into buf[c][16]
-  for (int bb = 0; bb < 8; ++bb)
-    for (int r = 0; r < 4; ++r) {
-      const int c = 32 * (bb >> 1) + 2 * (4 * kq + r) + (bb & 1);
-      buf[c * EXT_TILE + m] = st.acc_p[bb][r];
-    }
-  __syncthreads();
-  const float inv = 1.f / st.l;
-  for (int jj = 0; jj < 2; ++jj)
-    for (int i = 0; i < EXT_TILE; ++i) o[i][jj] += buf[(2 * lane + jj) * EXT_TILE + i];
   for (int i = 0; i < EXT_TILE; ++i) {
     if (t0 + i >= n) break;
-    const float s = lane_value(inv, i);
+    const float fi = lane_value(f1, i), si = lane_value(inv, i);
+    const float p0 = bufp[(2 * lane) * EXT_TILE + i], p1 = bufp[(2 * lane + 1) * EXT_TILE + i];
     *reinterpret_cast<float2 *>(a.out + (int64_t(r0 + t0 + i) * a.hq + h) * D + 2 * lane) =
-        make_float2(o[i][0] * s, o[i][1] * s);
+        make_float2(fmaf(fi, p0, o[i][0]) * si, fmaf(fi, p1, o[i][1]) * si);
   }
 }
 
