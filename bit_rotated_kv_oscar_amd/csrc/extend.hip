@@ -13,8 +13,9 @@
 // online softmax per query, and accumulates O^T = V^T P^T on the matrix cores
 // with P^T taken straight from the score registers:
 //   history (INT2) tiles: A = the stored 2-bit codes expanded to exact fp16
-//     integers, B = q R_K (scores) or p s_V (values) split into fp16 high and
-//     low parts, so each product is exact and the sums are fp32; scale and
+//     integers, B = q R_K split into fp16 high and low parts (scores: exact
+//     products, fp32 sums) or p s_V scaled by a power of two and rounded to
+//     fp16 once (values: one rounding per weight, fp32 sums); scale and
 //     zero of a group enter per key: score = sum_g s_g (q_g . c_g) + z_g
 //     sum(q_g), value = sum_t p_t s_t c_t + (sum_t p_t z_t);
 //   BF16 tiles (sink, ring, chunk): A = raw bf16 rows, B = q (bf16, exact)
@@ -46,6 +47,7 @@ struct ExtendArgs {
   const int32_t *cu_new, *len_before;
   int hq, hkv, max_new, max_prefix;
   float scale_log2;  // sm_scale * log2(e)
+  float pv_scale;    // power of two: p s_V pv_scale stays below 2^15 (fp16 operand)
   float *out;
 };
 
@@ -80,13 +82,6 @@ __device__ inline void split_bf16(const float (&x)[4], s16x4 &hi, s16x4 &lo) {
     const uint32_t h = bf16_rne(x[j]);
     hi[j] = short(h);
     lo[j] = short(bf16_rne(x[j] - __uint_as_float(h << 16)));
-  }
-}
-__device__ inline void split_f16(const float (&x)[4], f16x4 &hi, f16x4 &lo) {
-  for (int j = 0; j < 4; ++j) {
-    const _Float16 h = _Float16(x[j]);
-    hi[j] = h;
-    lo[j] = _Float16(x[j] - float(h));
   }
 }
 
@@ -211,7 +206,8 @@ __device__ inline void hist_load(HistData<D / G> &hd, const uint8_t *blk, int la
 // Attention over one loaded history page, rows < n_valid.
 template <int G>
 __device__ inline void hist_tile(SoftState<D / G> &st, const HistData<D / G> &hd, int n_valid, const f16x8 (&qh)[4],
-                                 const f16x8 (&ql)[4], const float (&qs)[D / G], float scale_log2, int lane) {
+                                 const f16x8 (&ql)[4], const float (&qs)[D / G], float scale_log2, float pv_scale,
+                                 int lane) {
   constexpr int NG = D / G;
   const int kq = lane >> 4;
   float s[4] = {0.f, 0.f, 0.f, 0.f};
@@ -232,18 +228,12 @@ __device__ inline void hist_tile(SoftState<D / G> &st, const HistData<D / G> &hd
   }
   softmax_tile(st, s, p);
   for (int g = 0; g < NG; ++g) {
-    float ps[4];
+    f16x4 bp;
     for (int r = 0; r < 4; ++r) {
-      ps[r] = ok[r] ? p[r] * lo_f16(hd.vm[g][r]) : 0.f;
+      bp[r] = _Float16(ok[r] ? p[r] * pv_scale * lo_f16(hd.vm[g][r]) : 0.f);
       st.zacc[g] += ok[r] ? p[r] * hi_f16(hd.vm[g][r]) : 0.f;
     }
-    f16x4 bh, bl;
-    split_f16(ps, bh, bl);
-    for (int b = g * G / 16; b < (g + 1) * G / 16; ++b) {
-      const f16x4 a = codes_v(hd.vc[0], hd.vc[1], b);
-      st.acc[b] = mfma_v(a, bl, st.acc[b]);
-      st.acc[b] = mfma_v(a, bh, st.acc[b]);
-    }
+    for (int b = g * G / 16; b < (g + 1) * G / 16; ++b) st.acc[b] = mfma_v(codes_v(hd.vc[0], hd.vc[1], b), bp, st.acc[b]);
   }
 }
 
@@ -382,26 +372,35 @@ __global__ void __launch_bounds__(64 * (GQA < 4 ? GQA : 4)) extend_kernel(Extend
   auto bad_page = [&](int pid) { return pid < 0 || pid >= a.n_hist_pages; };
   if (nhp > 0) {
     int ids = lane < nhp ? hpt[lane] : -1;
-    int pid = __builtin_amdgcn_readfirstlane(ids);
-    HistData<NG> cur, nxt;
-    if (!bad_page(pid)) hist_load<G>(cur, page_block(pid), lane);  // a bad page is never read
-#pragma unroll 1
-    for (int j = 0; j < nhp; ++j) {
-      const int jn = j + 1;
-      int pid_n = -1;
-      if (jn < nhp) {
-        if ((jn & 63) == 0) ids = jn + lane < nhp ? hpt[jn + lane] : -1;
-        pid_n = __builtin_amdgcn_readlane(ids, jn & 63);
-        if (!bad_page(pid_n)) hist_load<G>(nxt, page_block(pid_n), lane);
-      }
+    // page j's id and data; a bad page is never read
+    auto page_id = [&](int j) {
+      if (j > 0 && (j & 63) == 0) ids = j + lane < nhp ? hpt[j + lane] : -1;
+      return __builtin_amdgcn_readlane(ids, j & 63);
+    };
+    auto run = [&](int j, int pid, const HistData<NG> &hd) {
       if (bad_page(pid)) {
         if (lane == 0) flag_status(a.status, OSCAR_STATUS_BAD_PAGE);
-      } else {
-        const int nv = nht - PAGE * j < PAGE ? nht - PAGE * j : PAGE;
-        hist_tile<G>(sh, cur, nv, qh, ql, qs, a.scale_log2, lane);
+        return;
       }
-      cur = nxt;
-      pid = pid_n;
+      const int nv = nht - PAGE * j < PAGE ? nht - PAGE * j : PAGE;
+      hist_tile<G>(sh, hd, nv, qh, ql, qs, a.scale_log2, a.pv_scale, lane);
+    };
+    HistData<NG> d0, d1;
+    int p0 = page_id(0), p1 = -1;
+    if (!bad_page(p0)) hist_load<G>(d0, page_block(p0), lane);
+#pragma unroll 1
+    for (int j = 0; j < nhp; j += 2) {
+      if (j + 1 < nhp) {
+        p1 = page_id(j + 1);
+        if (!bad_page(p1)) hist_load<G>(d1, page_block(p1), lane);
+      }
+      run(j, p0, d0);
+      if (j + 1 >= nhp) break;
+      if (j + 2 < nhp) {
+        p0 = page_id(j + 2);
+        if (!bad_page(p0)) hist_load<G>(d0, page_block(p0), lane);
+      }
+      run(j + 1, p1, d1);
     }
   }
 
@@ -412,10 +411,11 @@ __global__ void __launch_bounds__(64 * (GQA < 4 ? GQA : 4)) extend_kernel(Extend
   const float f1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
   const float f2 = sh.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sh.m - mm);
   const float inv = 1.f / (f1 * l1 + f2 * l2);
+  const float pv_unscale = 1.f / a.pv_scale;
   for (int bb = 0; bb < 8; ++bb)
     for (int r = 0; r < 4; ++r) {
       const int c = 16 * bb + 4 * kq + r;
-      buf[c * EXT_TILE + m] = (sh.acc[bb][r] + sh.zacc[c / G]) * f2;
+      buf[c * EXT_TILE + m] = fmaf(sh.acc[bb][r], pv_unscale, sh.zacc[c / G]) * f2;
     }
   __syncthreads();
   float o[EXT_TILE][2];
@@ -482,6 +482,13 @@ hipError_t launch_extend(const oscar_layer_cache &c, RotArg rk, RotArg rv, const
   a.max_new = max_new;
   a.max_prefix = max_prefix;
   a.scale_log2 = sm_scale * LOG2E;
+  // p <= 2^LAZY_TH and s_V <= 2 clip_V / 3: the fp16 operand p s_V k stays in
+  // [2^14, 2^15) at its largest
+  float k = 1.f;
+  const float vmax = exp2f(LAZY_TH) * (2.f * rv.clip / 3.f);
+  while (vmax * k > 32768.f) k *= 0.5f;
+  while (vmax * k * 2.f <= 32768.f && k < 65536.f) k *= 2.f;
+  a.pv_scale = k;
   a.out = out;
   switch (n_q_heads / c.n_kv_heads) {
     case 1: return launch_gqa<1>(a, c.group, batch, max_new, s);
