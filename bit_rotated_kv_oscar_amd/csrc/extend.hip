@@ -12,10 +12,11 @@
 // matrix cores (lane l holds query l%16 and keys 4(l/16)..+3), keeps an
 // online softmax per query, and accumulates O^T = V^T P^T on the matrix cores
 // with P^T taken straight from the score registers:
-//   history (INT2) tiles: A = the stored 2-bit codes expanded to exact fp16
-//     integers, B = q R_K split into fp16 high and low parts (scores: exact
-//     products, fp32 sums) or p s_V scaled by a power of two and rounded to
-//     fp16 once (values: one rounding per weight, fp32 sums); scale and
+//   history (INT2) tiles: A = the stored 2-bit codes expanded to fp16 1 + c w
+//     (w = 1/4 or 1/16, the decode's expansion), B = q R_K / w split into
+//     fp16 high and low parts (scores: exact products, fp32 sums, the
+//     constant 1 taken off per group) or p s_V / w scaled by a power of two
+//     and rounded to fp16 once (values: one rounding per weight); scale and
 //     zero of a group enter per key: score = sum_g s_g (q_g . c_g) + z_g
 //     sum(q_g), value = sum_t p_t s_t c_t + (sum_t p_t z_t);
 //   BF16 tiles (sink, ring, chunk): A = raw bf16 rows, B = q (bf16, exact)
@@ -83,16 +84,6 @@ __device__ inline void split_bf16(const float (&x)[4], s16x4 &hi, s16x4 &lo) {
     hi[j] = short(h);
     lo[j] = short(bf16_rne(x[j] - __uint_as_float(h << 16)));
   }
-}
-
-// exact code values 0..3 from the expanded operands (1 + c/4, 1 + c/16)
-__device__ inline f16x8 codes_k(uint32_t w0, uint32_t w1, int kb) {
-  const f16x8 m = {4, 4, 16, 16, 4, 4, 16, 16};
-  return expand_k(w0, w1, kb) * m - m;
-}
-__device__ inline f16x4 codes_v(uint32_t w0, uint32_t w1, int r) {
-  const f16x4 m = {4, 4, 16, 16};
-  return expand_v(w0, w1, r) * m - m;
 }
 
 // Online-softmax state of one part of the keys: the BF16 keys (sink, window,
@@ -206,34 +197,39 @@ __device__ inline void hist_load(HistData<D / G> &hd, const uint8_t *blk, int la
 // Attention over one loaded history page, rows < n_valid.
 template <int G>
 __device__ inline void hist_tile(SoftState<D / G> &st, const HistData<D / G> &hd, int n_valid, const f16x8 (&qh)[4],
-                                 const f16x8 (&ql)[4], const float (&qs)[D / G], float scale_log2, float pv_scale,
-                                 int lane) {
+                                 const f16x8 (&ql)[4], const float (&qs)[D / G], const float (&qoff)[D / G],
+                                 float pv_scale, float pv_unscale, int lane) {
   constexpr int NG = D / G;
   const int kq = lane >> 4;
   float s[4] = {0.f, 0.f, 0.f, 0.f};
   for (int g = 0; g < NG; ++g) {
     f32x4 d = {0.f, 0.f, 0.f, 0.f};
     for (int kb = g * G / 32; kb < (g + 1) * G / 32; ++kb) {
-      const f16x8 c = codes_k(hd.kc[0], hd.kc[1], kb);
-      d = mfma_k(c, ql[kb], d);
-      d = mfma_k(c, qh[kb], d);
+      const f16x8 x = expand_k(hd.kc[0], hd.kc[1], kb);  // 1 + c w, w = 1/4 or 1/16
+      d = mfma_k(x, ql[kb], d);
+      d = mfma_k(x, qh[kb], d);
     }
-    for (int r = 0; r < 4; ++r) s[r] += lo_f16(hd.km[g][r]) * d[r] + hi_f16(hd.km[g][r]) * qs[g];
+    // d - qoff = sum_c c q_c (q carries 1/w and the softmax scale)
+    for (int r = 0; r < 4; ++r) s[r] += lo_f16(hd.km[g][r]) * (d[r] - qoff[g]) + hi_f16(hd.km[g][r]) * qs[g];
   }
   bool ok[4];
   float p[4];
   for (int r = 0; r < 4; ++r) {
     ok[r] = 4 * kq + r < n_valid;
-    s[r] = ok[r] ? s[r] * scale_log2 : -INFINITY;
+    s[r] = ok[r] ? s[r] : -INFINITY;
   }
   softmax_tile(st, s, p);
+  // A = 1 + c w (w = 1/4 for rows 0, 1 of the lane's four keys, 1/16 for
+  // rows 2, 3), B = fp16(p s k / w): the product is B + c p s k; the sum of
+  // the B as rounded leaves through the zero-point accumulator
   for (int g = 0; g < NG; ++g) {
     f16x4 bp;
     for (int r = 0; r < 4; ++r) {
-      bp[r] = _Float16(ok[r] ? p[r] * pv_scale * lo_f16(hd.vm[g][r]) : 0.f);
-      st.zacc[g] += ok[r] ? p[r] * hi_f16(hd.vm[g][r]) : 0.f;
+      const float wi = r < 2 ? 4.f : 16.f;
+      bp[r] = _Float16(ok[r] ? p[r] * (pv_scale * wi) * lo_f16(hd.vm[g][r]) : 0.f);
+      st.zacc[g] += ok[r] ? fmaf(p[r], hi_f16(hd.vm[g][r]), -float(bp[r]) * pv_unscale) : 0.f;
     }
-    for (int b = g * G / 16; b < (g + 1) * G / 16; ++b) st.acc[b] = mfma_v(codes_v(hd.vc[0], hd.vc[1], b), bp, st.acc[b]);
+    for (int b = g * G / 16; b < (g + 1) * G / 16; ++b) st.acc[b] = mfma_v(expand_v(hd.vc[0], hd.vc[1], b), bp, st.acc[b]);
   }
 }
 
@@ -292,19 +288,29 @@ __global__ void __launch_bounds__(64 * (GQA < 4 ? GQA : 4)) extend_kernel(Extend
   __syncthreads();
   for (int i = 0; i < EXT_TILE; ++i) *reinterpret_cast<float2 *>(buf + i * D + 2 * lane) = make_float2(qr[i][0], qr[i][1]);
   __syncthreads();
+  // history operands: y = q R_K sm_scale log2(e) / w (w = 1/4 or 1/16 per
+  // element, the weight of the code expansion) as fp16 high + low parts;
+  // qs = sum of the scaled q per group (zero points), qoff = sum of the
+  // operands as used (the expansion's constant 1)
   f16x8 qh[4], ql[4];
-  float qs[NG];
-  for (int g = 0; g < NG; ++g) qs[g] = 0.f;
+  float qs[NG], qoff[NG];
+  for (int g = 0; g < NG; ++g) qs[g] = qoff[g] = 0.f;
   for (int kb = 0; kb < 4; ++kb) {
     for (int e = 0; e < 8; ++e) {
-      const float x = buf[m * D + 32 * kb + 8 * kq + e];
-      const _Float16 hi = _Float16(x);
+      const float x = buf[m * D + 32 * kb + 8 * kq + e] * a.scale_log2;
+      const float y = x * ((e & 2) ? 16.f : 4.f);
+      const _Float16 hi = _Float16(y);
+      const _Float16 lo = _Float16(y - float(hi));
       qh[kb][e] = hi;
-      ql[kb][e] = _Float16(x - float(hi));
+      ql[kb][e] = lo;
       qs[(32 * kb) / G] += x;
+      qoff[(32 * kb) / G] += float(hi) + float(lo);
     }
   }
-  for (int g = 0; g < NG; ++g) qs[g] = lanes4_sum(qs[g]);
+  for (int g = 0; g < NG; ++g) {
+    qs[g] = lanes4_sum(qs[g]);
+    qoff[g] = lanes4_sum(qoff[g]);
+  }
 
   const int32_t *bpt = a.bf16_pt + int64_t(b) * BF16_PT;
   const int64_t page_elems = int64_t(2) * PAGE * D;  // K and V of one head
@@ -361,6 +367,7 @@ __global__ void __launch_bounds__(64 * (GQA < 4 ? GQA : 4)) extend_kernel(Extend
   const float m1 = sp.m, l1 = lanes4_sum(sp.l);
 
   // ======== INT2 history pages
+  const float pv_unscale = 1.f / a.pv_scale;
   SoftState<NG> sh;
   sh.init();
   const int nht = n_hist_tokens(L0), nhp = n_hist_pages(L0);
@@ -383,7 +390,7 @@ __global__ void __launch_bounds__(64 * (GQA < 4 ? GQA : 4)) extend_kernel(Extend
         return;
       }
       const int nv = nht - PAGE * j < PAGE ? nht - PAGE * j : PAGE;
-      hist_tile<G>(sh, hd, nv, qh, ql, qs, a.scale_log2, a.pv_scale, lane);
+      hist_tile<G>(sh, hd, nv, qh, ql, qs, qoff, a.pv_scale, pv_unscale, lane);
     };
     HistData<NG> d0, d1;
     int p0 = page_id(0), p1 = -1;
@@ -411,7 +418,6 @@ __global__ void __launch_bounds__(64 * (GQA < 4 ? GQA : 4)) extend_kernel(Extend
   const float f1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
   const float f2 = sh.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sh.m - mm);
   const float inv = 1.f / (f1 * l1 + f2 * l2);
-  const float pv_unscale = 1.f / a.pv_scale;
   for (int bb = 0; bb < 8; ++bb)
     for (int r = 0; r < 4; ++r) {
       const int c = 16 * bb + 4 * kq + r;
@@ -482,10 +488,10 @@ hipError_t launch_extend(const oscar_layer_cache &c, RotArg rk, RotArg rv, const
   a.max_new = max_new;
   a.max_prefix = max_prefix;
   a.scale_log2 = sm_scale * LOG2E;
-  // p <= 2^LAZY_TH and s_V <= 2 clip_V / 3: the fp16 operand p s_V k stays in
-  // [2^14, 2^15) at its largest
+  // p <= 2^LAZY_TH, s_V <= 2 clip_V / 3, 1/w <= 16: the fp16 operand
+  // p s_V k / w stays in [2^14, 2^15) at its largest
   float k = 1.f;
-  const float vmax = exp2f(LAZY_TH) * (2.f * rv.clip / 3.f);
+  const float vmax = exp2f(LAZY_TH) * 16.f * (2.f * rv.clip / 3.f);
   while (vmax * k > 32768.f) k *= 0.5f;
   while (vmax * k * 2.f <= 32768.f && k < 65536.f) k *= 2.f;
   a.pv_scale = k;
