@@ -186,11 +186,19 @@ def extend_attn(cache: LayerCache, rot_k: Rotation, rot_v: Rotation, q: torch.Te
     batch, hq = len_before.shape[0], q.shape[1]
     if cu_new.shape[0] != batch + 1:
         raise ValueError("cu_new must have batch + 1 entries")
+    T = q.shape[0]
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError(f"q must be [T, Hq, {HEAD_DIM}]")
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        if tuple(t.shape) != (T, cache.n_kv_heads, HEAD_DIM):
+            raise ValueError(f"{n} must be [{T}, {cache.n_kv_heads}, {HEAD_DIM}], got {tuple(t.shape)}")
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(HEAD_DIM)
     if out is None:
-        out = torch.empty((q.shape[0], hq, HEAD_DIM), dtype=torch.float32, device=dev)
+        out = torch.empty((T, hq, HEAD_DIM), dtype=torch.float32, device=dev)
     _need(out, "out", (torch.float32,), dev)
+    if tuple(out.shape) != (T, hq, HEAD_DIM):
+        raise ValueError(f"out must be [{T}, {hq}, {HEAD_DIM}], got {tuple(out.shape)}")
     c = cache.c()
     rk, rv = rot_k.c(), rot_v.c()
     check(load().oscar_extend_attn(ctypes.byref(c), ctypes.byref(rk), ctypes.byref(rv), _ptr(q), hq, _ptr(k_new),

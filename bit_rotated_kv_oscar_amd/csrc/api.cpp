@@ -244,7 +244,7 @@ int oscar_extend_attn(const oscar_layer_cache *cache, const oscar_rotation *rot_
   if (max_new == 0) return OSCAR_OK;
   if (int rc = check_device()) return rc;
   hipError_t e = oscar::launch_extend(*cache, rot_arg(rot_k), rot_arg(rot_v), q, n_q_heads, k_new, v_new, cu_new,
-                                      len_before, batch, max_new, max_prefix, sm_scale, out,
+                                      len_before, batch, total_tokens, max_new, max_prefix, sm_scale, out,
                                       reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "extend_attn");
   return OSCAR_OK;

@@ -120,6 +120,24 @@ __device__ inline float quad_max(float v) {
   return v;
 }
 
+// Raw (BF16) sink + recent pages of one request: page 0 = sink, pages 1..8 =
+// ring; slot s of the ring holds a live token iff its position is in the
+// recent window.
+__device__ inline uint32_t raw_valid_rows(int L, int page) {
+  uint32_t m = 0;
+  for (int r = 0; r < PAGE; ++r) {
+    bool ok;
+    if (page == 0) {
+      ok = r < L && r < N_SINK;
+    } else {
+      const int s = PAGE * (page - 1) + r;
+      ok = (L >= N_RAW) || (s >= N_SINK && s < L) || (s < N_SINK && s + N_RECENT < L);
+    }
+    m |= uint32_t(ok) << r;
+  }
+  return m;
+}
+
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ------------------------------------------------------------ code expansion

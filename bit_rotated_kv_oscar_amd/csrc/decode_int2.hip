@@ -1092,24 +1092,6 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
   }
 }
 
-// Raw (BF16) sink + recent pages of one request: page 0 = sink, pages 1..8 =
-// ring; slot s of the ring holds a live token iff its position is in the
-// recent window.
-__device__ inline uint32_t raw_valid_rows(int L, int page) {
-  uint32_t m = 0;
-  for (int r = 0; r < PAGE; ++r) {
-    bool ok;
-    if (page == 0) {
-      ok = r < L && r < N_SINK;
-    } else {
-      const int s = PAGE * (page - 1) + r;
-      ok = (L >= N_RAW) || (s >= N_SINK && s < L) || (s < N_SINK && s + N_RECENT < L);
-    }
-    m |= uint32_t(ok) << r;
-  }
-  return m;
-}
-
 // R_V rows of a workgroup thread for the way back to the plain basis: rows
 // cr + 64 m (m < 2), inputs 32 k + 4 qq .. + 3 (cr = tid / 8, qq = tid % 8);
 // eight lanes per row read 128 contiguous bytes.

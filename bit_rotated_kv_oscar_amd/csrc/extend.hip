@@ -47,6 +47,7 @@ struct ExtendArgs {
   const uint16_t *q, *k_new, *v_new;
   const int32_t *cu_new, *len_before;
   int hq, hkv, max_new, max_prefix;
+  int64_t total_tokens;  // rows of q / k_new / v_new / out
   float scale_log2;  // sm_scale * log2(e)
   float pv_scale;    // power of two: p s_V pv_scale stays below 2^15 (fp16 operand)
   float *out;
@@ -198,7 +199,7 @@ __device__ inline void hist_load(HistData<D / G> &hd, const uint8_t *blk, int la
 template <int G>
 __device__ inline void hist_tile(SoftState<D / G> &st, const HistData<D / G> &hd, int n_valid, const f16x8 (&qh)[4],
                                  const f16x8 (&ql)[4], const float (&qs)[D / G], const float (&qoff)[D / G],
-                                 float pv_scale, float pv_unscale, int lane) {
+                                 float inv_kqs, float pv_scale, float pv_unscale, int lane) {
   constexpr int NG = D / G;
   const int kq = lane >> 4;
   float s[4] = {0.f, 0.f, 0.f, 0.f};
@@ -216,7 +217,7 @@ __device__ inline void hist_tile(SoftState<D / G> &st, const HistData<D / G> &hd
   float p[4];
   for (int r = 0; r < 4; ++r) {
     ok[r] = 4 * kq + r < n_valid;
-    s[r] = ok[r] ? s[r] : -INFINITY;
+    s[r] = ok[r] ? s[r] * inv_kqs : -INFINITY;
   }
   softmax_tile(st, s, p);
   // A = 1 + c w (w = 1/4 for rows 0, 1 of the lane's four keys, 1/16 for
@@ -248,7 +249,10 @@ __global__ void __launch_bounds__(64 * (GQA < 4 ? GQA : 4)) extend_kernel(Extend
   const int r0 = __builtin_amdgcn_readfirstlane(a.cu_new[b]);
   const int n = __builtin_amdgcn_readfirstlane(a.cu_new[b + 1]) - r0;
   const int L0 = __builtin_amdgcn_readfirstlane(a.len_before[b]);
-  if (n < 0 || n > a.max_new || L0 < 0 || L0 > a.max_prefix) {
+  // the request's rows must lie inside the total_tokens rows of the inputs
+  // and the output (no access outside them), its counts inside the bounds
+  // the grid was sized for
+  if (r0 < 0 || n < 0 || n > a.max_new || int64_t(r0) + n > a.total_tokens || L0 < 0 || L0 > a.max_prefix) {
     if (t0 == 0 && threadIdx.x == 0 && __builtin_amdgcn_workgroup_id_y() == 0) flag_status(a.status, OSCAR_STATUS_BAD_LEN);
     return;
   }
@@ -288,16 +292,31 @@ __global__ void __launch_bounds__(64 * (GQA < 4 ? GQA : 4)) extend_kernel(Extend
   __syncthreads();
   for (int i = 0; i < EXT_TILE; ++i) *reinterpret_cast<float2 *>(buf + i * D + 2 * lane) = make_float2(qr[i][0], qr[i][1]);
   __syncthreads();
-  // history operands: y = q R_K sm_scale log2(e) / w (w = 1/4 or 1/16 per
-  // element, the weight of the code expansion) as fp16 high + low parts;
-  // qs = sum of the scaled q per group (zero points), qoff = sum of the
-  // operands as used (the expansion's constant 1)
+  // history operands: y = q R_K sm_scale log2(e) kqs / w (w = 1/4 or 1/16
+  // per element, the weight of the code expansion) as fp16 high + low
+  // parts; kqs is a power of two that brings the wave's largest |y| into
+  // (2^13, 2^14]: no fp16 overflow for large q or sm_scale, and the low
+  // parts stay normal numbers for the elements that matter; scores come out
+  // in kqs units and are multiplied by 1/kqs.  qs = sum of the scaled q per
+  // group (zero points), qoff = sum of the operands as used (the
+  // expansion's constant 1), both in kqs units.
+  float amax = 0.f;
+  for (int kb = 0; kb < 4; ++kb)
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(buf[m * D + 32 * kb + 8 * kq + e]));
+  amax = wave_max(amax) * a.scale_log2 * 16.f;
+  float kqs = 1.f;
+  if (amax > 0.f && amax < INFINITY) {
+    int ex;
+    (void)frexpf(amax, &ex);              // amax in [2^(ex-1), 2^ex)
+    kqs = ldexpf(1.f, 14 - ex);           // amax kqs in [2^13, 2^14)
+  }
+  const float inv_kqs = 1.f / kqs;
   f16x8 qh[4], ql[4];
   float qs[NG], qoff[NG];
   for (int g = 0; g < NG; ++g) qs[g] = qoff[g] = 0.f;
   for (int kb = 0; kb < 4; ++kb) {
     for (int e = 0; e < 8; ++e) {
-      const float x = buf[m * D + 32 * kb + 8 * kq + e] * a.scale_log2;
+      const float x = buf[m * D + 32 * kb + 8 * kq + e] * a.scale_log2 * kqs;
       const float y = x * ((e & 2) ? 16.f : 4.f);
       const _Float16 hi = _Float16(y);
       const _Float16 lo = _Float16(y - float(hi));
@@ -338,6 +357,9 @@ __global__ void __launch_bounds__(64 * (GQA < 4 ? GQA : 4)) extend_kernel(Extend
   if (L0 > N_SINK) {
 #pragma unroll 1
     for (int rp = 0; rp < N_RECENT / PAGE; ++rp) {
+      // a ring page without a visible token is never looked up (its table
+      // entry may be unset while the window is still filling)
+      if (!raw_valid_rows(L0, 1 + rp)) continue;
       const uint16_t *kp;
       if (!bf16_page(1 + rp, kp)) continue;
       bf16_tile(sp, kp, kp + PAGE * D, D, PAGE, qb, a.scale_log2, lane, [&](int t, int) {
@@ -390,7 +412,7 @@ __global__ void __launch_bounds__(64 * (GQA < 4 ? GQA : 4)) extend_kernel(Extend
         return;
       }
       const int nv = nht - PAGE * j < PAGE ? nht - PAGE * j : PAGE;
-      hist_tile<G>(sh, hd, nv, qh, ql, qs, qoff, a.pv_scale, pv_unscale, lane);
+      hist_tile<G>(sh, hd, nv, qh, ql, qs, qoff, inv_kqs, a.pv_scale, pv_unscale, lane);
     };
     HistData<NG> d0, d1;
     int p0 = page_id(0), p1 = -1;
@@ -465,8 +487,8 @@ hipError_t launch_gqa(const ExtendArgs &a, int G, int batch, int max_new, hipStr
 
 hipError_t launch_extend(const oscar_layer_cache &c, RotArg rk, RotArg rv, const uint16_t *q, int n_q_heads,
                          const uint16_t *k_new, const uint16_t *v_new, const int32_t *cu_new,
-                         const int32_t *len_before, int batch, int max_new, int max_prefix, float sm_scale,
-                         float *out, hipStream_t s) {
+                         const int32_t *len_before, int batch, int64_t total_tokens, int max_new,
+                         int max_prefix, float sm_scale, float *out, hipStream_t s) {
   ExtendArgs a;
   a.hist = c.hist;
   a.n_hist_pages = c.n_hist_pages;
@@ -487,6 +509,7 @@ hipError_t launch_extend(const oscar_layer_cache &c, RotArg rk, RotArg rv, const
   a.hkv = c.n_kv_heads;
   a.max_new = max_new;
   a.max_prefix = max_prefix;
+  a.total_tokens = total_tokens;
   a.scale_log2 = sm_scale * LOG2E;
   // p <= 2^LAZY_TH, s_V <= 2 clip_V / 3, 1/w <= 16: the fp16 operand
   // p s_V k / w stays in [2^14, 2^15) at its largest

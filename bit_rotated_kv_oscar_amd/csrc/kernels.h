@@ -64,8 +64,8 @@ size_t decode_bf16_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int max_se
 // chunk itself (causal); out fp32 [total][Hq][128].
 hipError_t launch_extend(const oscar_layer_cache &c, RotArg rk, RotArg rv, const uint16_t *q, int n_q_heads,
                          const uint16_t *k_new, const uint16_t *v_new, const int32_t *cu_new,
-                         const int32_t *len_before, int batch, int max_new, int max_prefix, float sm_scale,
-                         float *out, hipStream_t s);
+                         const int32_t *len_before, int batch, int64_t total_tokens, int max_new,
+                         int max_prefix, float sm_scale, float *out, hipStream_t s);
 
 // Calibration moments (device fp64).
 // cov[128][128] = (accumulate ? cov : 0) + sum over the n_vec vectors of

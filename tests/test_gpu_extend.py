@@ -142,3 +142,71 @@ def test_extend_bench_shape_sampled_rows(oscar):
     exp = o.extend_attn(ref, sc.R_K, sc.R_V, q, kn, vn, cu, [L0], SCALE, rows=rows)
     print(f"oracle done {time.time() - t0:.1f} s", flush=True)
     assert_decode_close(out[rows], exp, "extend bench shape")
+
+
+def test_extend_rows_past_total_tokens_are_flagged(oscar):
+    # cu_new runs past the rows of q / k_new / v_new / out for request 1:
+    # flagged OSCAR_STATUS_BAD_LEN, its rows never read or written; request
+    # 0 is computed as usual
+    prefix, chunk = [300, 250], [20, 20]
+    sc, ref, cache, rk, rv, q, kn, vn, cu = _setup(oscar, 2410, 8, 2, 64, prefix, chunk)
+    bad_cu = np.array([0, 20, 45], dtype=np.int32)          # 45 > T = 40
+    sentinel = torch.full((40, 8, 128), 7.0, device="cuda")
+    oscar.extend_attn(cache, rk, rv, to_dev_bf16(q), to_dev_bf16(kn), to_dev_bf16(vn),
+                      torch.from_numpy(bad_cu).cuda(), torch.tensor(prefix, dtype=torch.int32, device="cuda"),
+                      25, max(prefix), SCALE, out=sentinel)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) & oscar._lib.STATUS_BAD_LEN
+    s = sentinel.cpu().numpy()
+    assert np.all(s[20:] == 7.0)
+    exp = o.extend_attn(ref, sc.R_K, sc.R_V, q, kn, vn, cu, prefix, SCALE)
+    assert_decode_close(s[:20], exp[:20], "extend request beside rows past the end")
+    # a negative first offset is flagged the same way
+    cache.status.zero_()
+    neg_cu = np.array([-5, 15, 40], dtype=np.int32)
+    sentinel.fill_(7.0)
+    oscar.extend_attn(cache, rk, rv, to_dev_bf16(q), to_dev_bf16(kn), to_dev_bf16(vn),
+                      torch.from_numpy(neg_cu).cuda(), torch.tensor(prefix, dtype=torch.int32, device="cuda"),
+                      25, max(prefix), SCALE, out=sentinel)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) & oscar._lib.STATUS_BAD_LEN
+
+
+def test_extend_unused_ring_entries_are_not_looked_up(oscar):
+    # prefixes that fill the window only in part: ring pages without a
+    # visible token have table entry -1; nothing is flagged, results exact
+    prefix, chunk = [20, 100, 140], [9, 30, 12]
+    sc, ref, cache, rk, rv, q, kn, vn, cu = _setup(oscar, 2420, 8, 2, 32, prefix, chunk)
+    bpt = sc.bf16_pt.copy()
+    for b, L0 in enumerate(prefix):
+        for rp in range(8):
+            slots = [16 * rp + t for t in range(16)]
+            # slot s holds position L0 - 128 + ((s - L0) mod 128); visible iff >= 16
+            if not any(L0 - 128 + ((s - L0) % 128) >= 16 for s in slots):
+                bpt[b, 1 + rp] = -1
+    assert (bpt == -1).sum() >= 6
+    cache.bf16_pt.copy_(torch.from_numpy(bpt))
+    out = _run(oscar, cache, rk, rv, q, kn, vn, cu, prefix)
+    assert int(cache.status.item()) == 0
+    exp = o.extend_attn(ref, sc.R_K, sc.R_V, q, kn, vn, cu, prefix, SCALE)
+    assert_decode_close(out, exp, "extend with unset ring entries")
+
+
+@pytest.mark.parametrize("q_mult,sm_scale", [(400.0, 1.0), (1e-3, SCALE)])
+def test_extend_large_and_small_query_norms(oscar, q_mult, sm_scale):
+    # q R_K sm_scale log2(e) far above the fp16 range of the history operand
+    # (x400 at sm_scale 1), or so small that an unscaled low part would be
+    # subnormal: the power-of-two guard keeps both exact to the tolerance
+    prefix, chunk = [600, 350], [24, 17]
+    sc, ref, cache, rk, rv, q, kn, vn, cu = _setup(oscar, 2430, 8, 2, 64, prefix, chunk)
+    qf = synth.bf16_to_f64(q) * q_mult
+    qb = synth.bf16_bits(qf.astype(np.float32))
+    out = oscar.extend_attn(cache, rk, rv, to_dev_bf16(qb), to_dev_bf16(kn), to_dev_bf16(vn),
+                            torch.from_numpy(cu).cuda(), torch.tensor(prefix, dtype=torch.int32, device="cuda"),
+                            int(np.diff(cu).max()), max(prefix), sm_scale)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) == 0
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    exp = o.extend_attn(ref, sc.R_K, sc.R_V, qb, kn, vn, cu, prefix, sm_scale)
+    assert_decode_close(got, exp, f"extend q x{q_mult} sm_scale {sm_scale}")

@@ -7,9 +7,11 @@ redo a 32K or 100K context for every head, so it checks sampled
 (request, KV head) pairs one at a time: it writes that request's tokens of
 that head into a cache of its own and attends over it with the query heads
 of the group.  Requests share one seeded host token array as prefixes of
-different lengths (each request still has pages of its own, written by the
-GPU write kernel); the 28 x 100K case shares one written request's pages
-between all requests (a shared prefix), each with its own query.
+different lengths, each starting at its own row offset so that no two
+requests hold the same tokens (each request has pages of its own, written
+by the GPU write kernel); in the 28 x 100K case most requests share one
+written request's pages (a shared prefix), two have pages and tokens of
+their own, and every request has its own query.
 """
 import math
 
@@ -37,24 +39,41 @@ def oscar():
 class FullCase:
     """Shared host tokens, rotations and per-request page tables."""
 
-    def __init__(self, seed, hq, hkv, G, lens, shared_pages=False):
+    def __init__(self, seed, hq, hkv, G, lens, shared_pages=0, offset_step=37):
+        """shared_pages = n > 0: requests 0 .. B-n hold the pages of request 0
+        (a shared prefix); the last n - 1 requests and request 0 have pages
+        of their own.  Request b's tokens are rows off[b] .. off[b] + L_b of
+        one seeded host array (off[b] = offset_step * b, request 0 at 0)."""
         self.hq, self.hkv, self.G = hq, hkv, G
         self.lens = np.asarray(lens, dtype=np.int64)
-        self.ld = synth.LayerData(seed, 0, hq, hkv)
-        self.k, self.v = self.ld.cache_kv(int(self.lens.max()))   # bf16 bits [Lmax][Hkv][128]
-        self.R_K, self.R_V = random_rotation(seed), random_rotation(seed + 1)
-        self.q = self.ld.decode_q(len(self.lens))
-        self.shared = shared_pages
         B = len(self.lens)
-        if shared_pages:
-            pt1, self.n_hist_pages = synth.shuffled_page_tables(seed, 0, self.lens[:1])
-            self.hist_pt = np.repeat(pt1, B, axis=0)
-            self.bf16_pt = np.repeat(synth.bf16_page_tables(1, shuffle_seed=seed + 7), B, axis=0)
-            self.n_bf16_pages = 9
-        else:
-            self.hist_pt, self.n_hist_pages = synth.shuffled_page_tables(seed, 0, self.lens)
-            self.bf16_pt = synth.bf16_page_tables(B, shuffle_seed=seed + 7)
-            self.n_bf16_pages = 9 * B
+        self.shared = int(shared_pages)
+        own = self.own_requests()
+        self.off = np.zeros(B, dtype=np.int64)
+        self.off[own] = offset_step * np.arange(len(own))
+        self.ld = synth.LayerData(seed, 0, hq, hkv)
+        self.k, self.v = self.ld.cache_kv(int((self.lens + self.off).max()))  # bf16 bits [rows][Hkv][128]
+        self.R_K, self.R_V = random_rotation(seed), random_rotation(seed + 1)
+        self.q = self.ld.decode_q(B)
+        pt_own, self.n_hist_pages = synth.shuffled_page_tables(seed, 0, self.lens[own])
+        bpt_own = synth.bf16_page_tables(len(own), shuffle_seed=seed + 7)
+        self.n_bf16_pages = 9 * len(own)
+        slot = np.array([own.index(b) if b in own else 0 for b in range(B)])
+        self.hist_pt = pt_own[slot]
+        self.bf16_pt = bpt_own[slot]
+
+    def own_requests(self):
+        """Requests whose pages the GPU writes (the others share request 0's)."""
+        B = len(self.lens)
+        if not self.shared:
+            return list(range(B))
+        return [0] + list(range(B - self.shared + 1, B))
+
+    def tokens(self, b, h=None):
+        """Request b's token rows (bf16 bits [L_b][Hkv or 1][128])."""
+        L, a = int(self.lens[b]), int(self.off[b])
+        hs = slice(None) if h is None else slice(h, h + 1)
+        return self.k[a:a + L, hs], self.v[a:a + L, hs]
 
     def gpu(self, oscar):
         """Write every request's tokens through the GPU write kernel."""
@@ -63,10 +82,18 @@ class FullCase:
                                  torch.from_numpy(self.hist_pt), torch.from_numpy(self.bf16_pt), device=dev)
         rk, rv = oscar.Rotation(self.R_K, CLIP, dev), oscar.Rotation(self.R_V, CLIP, dev)
         kd, vd = to_dev_bf16(self.k), to_dev_bf16(self.v)
-        lens = self.lens[:1] if self.shared else self.lens
-        idx = torch.cat([torch.arange(int(L), device=dev) for L in lens])
+        own = self.own_requests()
+        lens = self.lens[own]
+        idx = torch.cat([torch.arange(int(self.off[b]), int(self.off[b] + self.lens[b]), device=dev) for b in own])
         cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(dev)
-        oscar.write_kv(cache, rk, rv, kd.index_select(0, idx).contiguous(), vd.index_select(0, idx).contiguous(),
+        wcache = cache
+        if self.shared:
+            # the write addresses the own requests' rows of the page tables
+            wcache = oscar.LayerCache(self.hkv, self.G, self.n_hist_pages, self.n_bf16_pages,
+                                      torch.from_numpy(self.hist_pt[own]), torch.from_numpy(self.bf16_pt[own]),
+                                      device=dev, hist=cache.hist, bf16=cache.bf16)
+            wcache.status = cache.status
+        oscar.write_kv(wcache, rk, rv, kd.index_select(0, idx).contiguous(), vd.index_select(0, idx).contiguous(),
                        cu, torch.zeros(len(lens), dtype=torch.int32, device=dev), int(lens.max()))
         torch.cuda.synchronize()
         assert int(cache.status.item()) == 0
@@ -79,8 +106,8 @@ class FullCase:
         nh = synth.hist_pages_needed(L)
         ref = o.LayerCacheRef(1, self.G, nh, 9, np.arange(nh, dtype=np.int32)[None],
                               np.arange(9, dtype=np.int32)[None])
-        ref.write(self.R_K, self.R_V, CLIP, CLIP, self.k[:L, h:h + 1], self.v[:L, h:h + 1],
-                  np.array([0, L], np.int32), np.zeros(1, np.int32))
+        kb, vb = self.tokens(b, h)
+        ref.write(self.R_K, self.R_V, CLIP, CLIP, kb, vb, np.array([0, L], np.int32), np.zeros(1, np.int32))
         qb = (self.q if q is None else q)[b:b + 1, h * gqa:(h + 1) * gqa]
         return o.decode_attn(ref, self.R_K, self.R_V, qb, [L], SCALE)[0]
 
@@ -126,12 +153,13 @@ def test_bs64_8k_to_32k_g64(oscar):
 
 def test_28_requests_100k_gqa8_g128(oscar):
     # 28 concurrent 100000-token requests, 64 q / 8 KV heads, group 128
-    # (pages shared between requests, queries their own)
-    fc = FullCase(2103, 64, 8, 128, [100000] * 28, shared_pages=True)
+    # (requests 0..25 share request 0's pages, 26 and 27 have pages and
+    # tokens of their own; every query is its own)
+    fc = FullCase(2103, 64, 8, 128, [100000] * 28, shared_pages=3, offset_step=1000)
     cache, rk, rv = fc.gpu(oscar)
     out = _decode(oscar, fc, cache, rk, rv)
     assert np.isfinite(out).all()
-    _check(fc, out, [(0, 2), (27, 2)], "28 x 100K")
+    _check(fc, out, [(0, 2), (13, 7), (26, 5), (27, 2)], "28 x 100K")
 
 
 def test_write_prefill_8x32k_g32(oscar):
@@ -142,7 +170,8 @@ def test_write_prefill_8x32k_g32(oscar):
     hist = cache.hist.cpu().numpy()
     for b, h in ((0, 0), (5, 3), (7, 7)):
         L = int(fc.lens[b])
-        stats = compare_history(hist[:, h:h + 1], fc.hist_pt[b:b + 1], [fc.k[:L, h:h + 1]], [fc.v[:L, h:h + 1]],
+        kb, vb = fc.tokens(b, h)
+        stats = compare_history(hist[:, h:h + 1], fc.hist_pt[b:b + 1], [kb], [vb],
                                 [L], fc.R_K, fc.R_V, CLIP, CLIP, fc.G)
         assert_history_ok(stats)
         print(f"write 8x32K b={b} h={h}: {stats}", flush=True)
@@ -162,9 +191,10 @@ def test_write_then_64_appends_decode_g32(oscar):
     kd, vd = to_dev_bf16(fc.k), to_dev_bf16(fc.v)
     q = to_dev_bf16(fc.q)
     ws = torch.zeros(oscar.decode_workspace_bytes(8, fc.hq, fc.hkv, P + S), dtype=torch.uint8, device=dev)
+    rows = torch.from_numpy(fc.off + P).to(dev)
     for s in range(S):
-        kn = kd[P + s].unsqueeze(0).expand(8, -1, -1).contiguous()
-        vn = vd[P + s].unsqueeze(0).expand(8, -1, -1).contiguous()
+        kn = kd.index_select(0, rows + s).contiguous()   # request b's token at position P + s
+        vn = vd.index_select(0, rows + s).contiguous()
         before = torch.full((8,), P + s, dtype=torch.int32, device=dev)
         out = oscar.decode_step(cache, rk, rv, kn, vn, before, q, P + S, SCALE, workspace=ws)
     torch.cuda.synchronize()

@@ -851,3 +851,94 @@ def test_extend_selected_rows_equal_full_rows():
     rows = [20, 0, 7]
     part = o.extend_attn(pre, R, Rv, qs, k[prefix:], v[prefix:], [0, T], [prefix], 0.088, rows=rows)
     np.testing.assert_array_equal(part, full[rows])
+
+
+# ------------------------------------------------- pins added for the gaps
+
+
+def test_bf16_to_f64_fixed_values():
+    # bf16 = the top 16 bits of an IEEE binary32: sign, 8 exponent bits
+    # (bias 127), 7 fraction bits; values by hand from that definition
+    cases = {
+        0x3F80: 1.0,                      # 0 01111111 0000000
+        0xC000: -2.0,                     # 1 10000000 0000000
+        0x4049: 2.0 * (1 + 73 / 128),     # 0 10000000 1001001 = 3.140625
+        0x0001: 2.0 ** -133,              # smallest subnormal: 2^-126 * 2^-7
+        0x0080: 2.0 ** -126,              # smallest normal
+        0x7F7F: (2 - 2.0 ** -7) * 2.0 ** 127,  # largest finite
+        0x3E00: 0.125,                    # 0 01111100 0000000
+        0xBF40: -0.75,                    # 1 01111110 1000000
+    }
+    got = o.bf16_to_f64(np.array(list(cases), dtype=np.uint16))
+    np.testing.assert_array_equal(got, np.array(list(cases.values())))
+    z = o.bf16_to_f64(np.array([0x8000, 0x7F80, 0xFF80], dtype=np.uint16))
+    assert z[0] == 0.0 and math.copysign(1.0, z[0]) < 0
+    assert z[1] == math.inf and z[2] == -math.inf
+
+
+def test_bf16_paged_decode_follows_page_table():
+    # the request's pages sit at permuted positions of a pool that also holds
+    # decoy pages; the last page is partial, so which physical page is last
+    # matters too.  The result must be attention over the tokens in logical
+    # order (gathered here by hand), and reading the pool in its own order or
+    # ignoring the partial page must differ from it.
+    rng = np.random.default_rng(77)
+    L, hq, hkv = 75, 4, 2
+    n_log = (L + 15) // 16                      # 5 logical pages, last holds 11 rows
+    pool = synth.bf16_bits(rng.standard_normal((12, hkv, 2, 16, 128)).astype(np.float32))
+    perm = np.array([9, 2, 11, 0, 6], dtype=np.int32)
+    pt = np.full((1, 8), -1, dtype=np.int32)
+    pt[0, :n_log] = perm
+    q = synth.bf16_bits(rng.standard_normal((1, hq, 128)).astype(np.float32))
+    got = o.bf16_paged_decode(q, pool, pt, [L], 0.088)
+    # by hand: token p is row p % 16 of page perm[p // 16]
+    K = np.empty((L, hkv, 128))
+    V = np.empty((L, hkv, 128))
+    for p in range(L):
+        for h in range(hkv):
+            K[p, h] = synth.bf16_to_f64(pool[perm[p // 16], h, 0, p % 16])
+            V[p, h] = synth.bf16_to_f64(pool[perm[p // 16], h, 1, p % 16])
+    qf = synth.bf16_to_f64(q[0])
+    for h in range(hq):
+        g = h // (hq // hkv)
+        logits = [float(np.dot(qf[h], K[p, g])) * 0.088 for p in range(L)]
+        m = max(logits)
+        w = [math.exp(x - m) for x in logits]
+        ref = sum(w[p] * V[p, g] for p in range(L)) / sum(w)
+        np.testing.assert_allclose(got[0, h], ref, rtol=1e-12, atol=1e-12)
+    # an identity table over the same pool gives a different answer
+    ident = o.bf16_paged_decode(q, pool, np.arange(8, dtype=np.int32)[None], [L], 0.088)
+    assert np.abs(ident - got).max() > 1e-3
+    # the permuted table equals the identity table over a pool permuted the same way
+    pool2 = pool.copy()
+    pool2[:n_log] = pool[perm]
+    same = o.bf16_paged_decode(q, pool2, np.arange(8, dtype=np.int32)[None], [L], 0.088)
+    np.testing.assert_allclose(same, got, rtol=1e-13, atol=1e-13)
+
+
+def test_calibrate_clip_wiring():
+    # clip_K is the 0.999 quantile (type 7) of |k R_K| and clip_V that of
+    # |v R_V| ([nl]/[fr] section 2.2.A: one clip per layer and tensor from
+    # the rotated calibration values).  V is drawn at three times the scale
+    # of K, so a swap of k and v, or of R_K and R_V, gives other numbers.
+    ld = synth.LayerData(31, 0, 4, 2)
+    qb, kb, vb = ld.calibration(300)
+    q, k = o.bf16_to_f64(qb), o.bf16_to_f64(kb)
+    v = 3.0 * o.bf16_to_f64(vb)
+    cal = o.calibrate(q, k, v)
+
+    def q999(x):
+        # type 7 by hand: sorted values, h = (n - 1) p, linear interpolation
+        s = np.sort(np.abs(x).ravel())
+        h = (s.size - 1) * 0.999
+        f = int(math.floor(h))
+        return s[f] + (h - f) * (s[min(f + 1, s.size - 1)] - s[f])
+
+    kr = k.reshape(-1, 128) @ cal["R_K"]
+    vr = v.reshape(-1, 128) @ cal["R_V"]
+    assert abs(cal["clip_K"] - q999(kr)) <= 1e-12 * q999(kr)
+    assert abs(cal["clip_V"] - q999(vr)) <= 1e-12 * q999(vr)
+    # the alternatives a wiring mistake would produce are far from these
+    assert abs(q999(k.reshape(-1, 128) @ cal["R_V"]) - cal["clip_K"]) > 1e-2 * cal["clip_K"]
+    assert abs(q999(v.reshape(-1, 128) @ cal["R_K"]) - cal["clip_V"]) > 1e-2 * cal["clip_V"]
+    assert cal["clip_V"] > 2.0 * cal["clip_K"]
