@@ -25,9 +25,22 @@ tokens into every layer's cache (rotate, clip, INT2-pack, page-store; sink and
 recent kept bf16); then 64 decode steps with write-on-append of each new
 token are timed as well.  Its line names its own metric (write GB/s).
 
+`--workload 28x100k` runs the capacity workload (Qwen3-32B-shaped, 64 layers,
+28 requests x 100000 tokens, GQA 8, G = 128, ~104 GB of INT2 cache; its
+all-BF16 copy does not fit one GPU) and `--workload config0` the single-layer
+4096-token correctness configuration (8 query / 2 KV heads, G = 32).
+
+The default run (no --workload) times bs1 -- its `value` -- and adds every
+other workload's line under its name ("bs64", "28x100k", "write", "extend",
+"config0"), each with its own roofline and CPU oracle baseline, plus the
+measured read ceilings of the device ("read_ceiling": streaming and
+page-gather reads by oscar_read_probe), against which each bandwidth-bound
+roofline also reports `frac_of_measured_ceiling`.
+
 Printed: one JSON line (metric, value in GB/s of algorithmic bytes per step,
-tokens/s, the in-run BF16 paged-decode comparison, the roofline of the
-dominant kernel and the CPU oracle baseline).
+tokens/s, per-replay median / p10 / p90, the in-run BF16 paged-decode
+comparison, the roofline of the dominant kernel and the CPU oracle baseline
+with the host's core count and CPU model).
 """
 from __future__ import annotations
 
@@ -52,9 +65,9 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", choices=["bs1", "bs64", "write", "28x100k", "extend"], default=None,
-                   help="default: bs1, with the bs64 figures added to its line")
-    p.add_argument("--no-companion", action="store_true", help="default run: leave out the bs64 figures")
+    p.add_argument("--workload", choices=["bs1", "bs64", "write", "28x100k", "extend", "config0"], default=None,
+                   help="default: bs1, with every other workload's figures added to its line")
+    p.add_argument("--no-companion", action="store_true", help="default run: bs1 alone")
     p.add_argument("--layers", type=int, default=None, help="override the layer count (testing only)")
     p.add_argument("--seed", type=int, default=1)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -82,7 +95,8 @@ DOMINANT = {"bs1": ("attend_kernel", ["decode_int2.hip", "attn_common.h", "commo
             "bs64": ("attend_kernel", ["decode_int2.hip", "attn_common.h", "common.h"]),
             "write": ("write_hist_kernel", ["write.hip", "common.h"]),
             "extend": ("extend_kernel", ["extend.hip", "attn_common.h", "common.h"]),
-            "28x100k": ("attend_kernel", ["decode_int2.hip", "attn_common.h", "common.h"])}
+            "28x100k": ("attend_kernel", ["decode_int2.hip", "attn_common.h", "common.h"]),
+            "config0": ("attend_kernel", ["decode_int2.hip", "attn_common.h", "common.h"])}
 
 
 def kernel_sources_sha(workload):
@@ -155,6 +169,11 @@ WORKLOADS = {
                     layers=64, hq=64, hkv=8, G=128, batch=28, len_lo=100000, len_hi=100000,
                     bf16_bytes_note="all-BF16 cache of the same tokens: 734 GB, beyond one GPU's 288 GB"),
 }
+# the single-layer correctness configuration (cache-resident: a latency
+# figure, not a bandwidth result); pages contiguous
+WORKLOADS["config0"] = dict(name="single layer, batch 1, 8 q / 2 KV heads, context 4096 (16 sink + 128 recent BF16 + "
+                                 "3952 INT2), G 32, one decode step", layers=1, hq=8, hkv=2, G=32, batch=1,
+                            len_lo=4096, len_hi=4096, contiguous_pages=True)
 WRITE_METRIC = "INT2 fused KV write GB/s (% HBM peak) + tokens/s, prefill 8 x 32K, 36 layers"
 WORKLOADS["extend"] = dict(
     name="qwen3-8b-shaped extend attention (chunked prefill) over a cached INT2 + BF16 prefix, 36 layers, "
@@ -262,26 +281,153 @@ def main():
     if args.layers:
         W["layers"] = args.layers
     if args.workload == "write":
-        write_main(args, W, dev)
+        print(json.dumps(write_main(args, W, dev)))
         return
     if args.workload == "extend":
-        extend_main(args, W, dev)
+        print(json.dumps(extend_main(args, W, dev)))
         return
     line = decode_main(args, W, dev, args.workload)
     if workload_default and not args.no_companion:
-        # the metric names batch 1 and batch 64: the default run adds the
-        # batch-64 workload's figures to its line
+        # every other workload, one after another (each frees its memory
+        # before the next starts), then the device's read ceilings
         import gc
+        for name in ("bs64", "28x100k", "write", "extend", "config0"):
+            gc.collect()
+            torch.cuda.empty_cache()
+            a2 = argparse.Namespace(**vars(args))
+            a2.workload = name
+            W2 = dict(WORKLOADS[name])
+            t0 = time.time()
+            if name == "write":
+                leg = write_main(a2, W2, dev)
+            elif name == "extend":
+                leg = extend_main(a2, W2, dev)
+            else:
+                leg = decode_main(a2, W2, dev, name)
+            leg["leg_wall_s"] = round(time.time() - t0, 1)
+            for k in ("n_gpus", "steps", "warmup", "higher_is_better", "scaling", "vs_baseline", "data"):
+                leg.pop(k, None)
+            line[name] = leg
+            print(f"leg {name}: {leg['value']} {leg['unit']} ({leg['leg_wall_s']} s)", file=sys.stderr, flush=True)
         gc.collect()
         torch.cuda.empty_cache()
-        a64 = argparse.Namespace(**vars(args))
-        a64.workload, a64.no_cpu_baseline = "bs64", True
-        l64 = decode_main(a64, dict(WORKLOADS["bs64"]), dev, "bs64")
-        line["bs64"] = {k: l64[k] for k in ("value", "unit", "ms_per_step", "tokens_per_s", "pct_hbm_peak",
-                                          "roofline", "bf16_ms_per_step", "int2_decode_ms_per_step",
-                                          "int2_speedup_vs_bf16") if k in l64}
-        line["bs64"]["config"] = l64["config"]
+        ceil = read_ceiling(dev)
+        line["read_ceiling"] = ceil
+        attach_ceiling(line, ceil)
+        for name in ("bs64", "28x100k", "write", "config0"):
+            attach_ceiling(line[name], ceil)
+    elif args.workload != "config0":
+        ceil = read_ceiling(dev)
+        line["read_ceiling"] = ceil
+        attach_ceiling(line, ceil)
     print(json.dumps(line))
+
+
+# gather block of each workload's history pages, and which ceiling bounds it
+CEILING_OF = {"bs1": "gather_1280", "bs64": "gather_1280", "28x100k": "gather_1152", "write": "stream"}
+
+
+def read_ceiling(dev, reps=5):
+    """Measured read ceilings (oscar_read_probe, median of `reps` timed
+    launches): streaming 4 KB blocks of a 4 GiB buffer, and gathers of
+    history-page-sized blocks (1152 / 1280 / 1536 B: G = 128 / 64 / 32) in a
+    seeded random order from a 4 GiB pool."""
+    import numpy as np
+    import torch
+
+    import bit_rotated_kv_oscar_amd as oscar
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = {"probe": "oscar_read_probe, 16-byte loads, median of %d launches" % reps}
+
+    def timed(n_blocks, bb, ids=None):
+        ts = []
+        for r in range(reps + 1):
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record()
+            a1.record()
+            oscar.profile_events(a0, a1)
+            oscar.read_probe(buf, n_blocks, bb, ids, sink)
+            torch.cuda.synchronize()
+            if r:
+                ts.append(a0.elapsed_time(a1) * 1e-3)
+        return n_blocks * bb / float(np.median(ts)) / 1e9
+
+    out["stream"] = round(timed(nbytes // 4096, 4096), 1)
+    for bb in (1152, 1280, 1536):
+        n_slots = nbytes // bb
+        ids = torch.from_numpy(np.random.default_rng(bb).permutation(n_slots)[: n_slots * 3 // 4].astype(np.int32))
+        out[f"gather_{bb}"] = round(timed(ids.numel(), bb, ids.to(dev)), 1)
+    out["unit"] = "GB/s"
+    del buf
+    return out
+
+
+def attach_ceiling(leg, ceil):
+    """Adds the measured ceiling that bounds a bandwidth-bound leg and its
+    dominant kernel's fraction of it."""
+    wl = None
+    for k, v in WORKLOADS.items():
+        if v["name"] == leg.get("config", {}).get("workload"):
+            wl = k
+    key = CEILING_OF.get(wl)
+    r = leg.get("roofline")
+    if key is None or not r or r.get("unit") != "GB/s":
+        return
+    r["measured_ceiling"] = {"kind": key, "GBps": ceil[key]}
+    r["frac_of_measured_ceiling"] = round(r["achieved"] / ceil[key], 4)
+
+
+def replay_stats(run_once, steps):
+    """Times `steps` calls of run_once (one replay each) with an event after
+    each: mean over the whole bracket, median, p10 and p90 of the single
+    replays (ms)."""
+    import numpy as np
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(steps):
+        run_once()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    return {"mean": ev[0].elapsed_time(ev[-1]) / steps, "median": float(np.median(per)),
+            "p10": float(np.percentile(per, 10)), "p90": float(np.percentile(per, 90))}
+
+
+def stats_fields(st):
+    return {"ms_per_step_median": round(st["median"], 4), "ms_per_step_p10": round(st["p10"], 4),
+            "ms_per_step_p90": round(st["p90"], 4)}
+
+
+def host_info(threads_used):
+    """Cores the CPU baseline used, the host's logical CPUs and CPU model."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count()
+    return {"cores": int(threads_used), "nproc": int(avail), "cpu_count": int(os.cpu_count() or 0),
+            "cpu_model": model}
+
+
+def blas_threads():
+    try:
+        import threadpoolctl
+        return max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    except Exception:
+        return os.cpu_count() or 1
 
 
 def decode_main(args, W, dev, workload):
@@ -324,8 +470,14 @@ def decode_main(args, W, dev, workload):
         R_K, R_V, ck, cv = oscar.calibrate_rotation(qc, kc, vc, 0.999)
         ly.rk, ly.rv = oscar.Rotation(R_K, ck, dev), oscar.Rotation(R_V, cv, dev)
         # page tables: every request's history pages from one shuffled pool
-        hist_pt, n_pool = synth.shuffled_page_tables(args.seed, l, final_lens, n_pool_pages=sum(pages_per_req) + 1)
-        bf16_pt = synth.bf16_page_tables(B, shuffle_seed=args.seed + l)
+        if W.get("contiguous_pages"):
+            hist_pt = np.arange(sum(pages_per_req), dtype=np.int32).reshape(B, -1)
+            n_pool = sum(pages_per_req)
+            bf16_pt = synth.bf16_page_tables(B)
+        else:
+            hist_pt, n_pool = synth.shuffled_page_tables(args.seed, l, final_lens,
+                                                         n_pool_pages=sum(pages_per_req) + 1)
+            bf16_pt = synth.bf16_page_tables(B, shuffle_seed=args.seed + l)
         ly.cache = oscar.LayerCache(hkv, G, n_pool, 9 * B, torch.from_numpy(hist_pt), torch.from_numpy(bf16_pt),
                                     device=dev)
         # prefill: every request's first start_len tokens in one write call
@@ -409,13 +561,8 @@ def decode_main(args, W, dev, workload):
         graph.replay()
     torch.cuda.synchronize()
     lens_at_timing = lens_before.cpu().numpy().copy()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms_per_step = e0.elapsed_time(e1) / steps
+    st = replay_stats(graph.replay, steps)
+    ms_per_step = st["mean"]
     for ly in layers:
         assert int(ly.cache.status.item()) == 0, "decode flagged bad data"
         assert torch.isfinite(ly.out).all(), "non-finite decode output"
@@ -494,7 +641,11 @@ def decode_main(args, W, dev, workload):
                 "bf16_GBps": round(nl * bf16_bytes(lens_now, hq, hkv) / (bf16_ms * 1e-3) / 1e9, 1)}
 
     # ---------------------------------------------------------------- CPU oracle
-    cpu = None if args.no_cpu_baseline else cpu_baseline(args, W, final_lens, step_bytes)
+    cpu = None
+    if not args.no_cpu_baseline:
+        # 28 x 100K: one KV head (with its query heads) of one request per
+        # layer sample; the others: every head
+        cpu = cpu_baseline(args, W, final_lens, step_bytes, kv_sample=1 if W["hkv"] * W["len_hi"] > 400000 else None)
 
     line = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warm,
@@ -512,6 +663,7 @@ def decode_main(args, W, dev, workload):
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
     }
+    line.update(stats_fields(st))
     if bf16:
         line.update(bf16)
     elif "bf16_bytes_note" in W:
@@ -581,13 +733,8 @@ def write_main(args, W, dev):
         for _ in range(warm):
             prefill()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            prefill()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms_per_step = e0.elapsed_time(e1) / steps
+        st = replay_stats(prefill, steps)
+        ms_per_step = st["mean"]
         # dominant kernel: the history write kernel of each layer's call
         pairs = []
         for ly in layers:
@@ -655,7 +802,8 @@ def write_main(args, W, dev):
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
     }
-    print(json.dumps(line))
+    line.update(stats_fields(st))
+    return line
 
 
 def extend_flops(prefix, chunk, hq):
@@ -728,13 +876,8 @@ def extend_main(args, W, dev):
         for _ in range(warm):
             step()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms_per_step = e0.elapsed_time(e1) / steps
+        st = replay_stats(step, steps)
+        ms_per_step = st["mean"]
         pairs = []
         for ly in layers:
             a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -769,7 +912,8 @@ def extend_main(args, W, dev):
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
     }
-    print(json.dumps(line))
+    line.update(stats_fields(st))
+    return line
 
 
 def extend_cpu_baseline(args, W):
@@ -780,11 +924,7 @@ def extend_cpu_baseline(args, W):
 
     import synth
     from oracle import oscar_ref as o
-    try:
-        import threadpoolctl
-        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count()
+    threads = blas_threads()
     hq, hkv, G = W["hq"], W["hkv"], W["G"]
     L0, m = int(W["len_hi"]), 8
     ld = synth.LayerData(args.seed + 1000, 0, hq, hkv)
@@ -798,9 +938,11 @@ def extend_cpu_baseline(args, W):
     o.extend_attn(ref, R, R, q, k[L0:], v[L0:], [0, m], [L0], 1 / math.sqrt(HEAD_DIM))
     dt = time.time() - t0
     fl = extend_flops([L0], [m], hq)
-    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {m} chunk tokens of one request over its {L0}-token prefix, one layer (Hq {hq}, "
-                      f"Hkv {hkv}, G {G}): {dt:.1f} s, {m / dt:.2f} tokens/s"}
+    out = {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "kind": "oracle",
+           "sample": f"first {m} chunk tokens of one request over its {L0}-token prefix, one layer (Hq {hq}, "
+                     f"Hkv {hkv}, G {G}): {dt:.1f} s, {m / dt:.2f} tokens/s"}
+    out.update(host_info(threads))
+    return out
 
 
 def write_cpu_baseline(args, W, bytes_per_token):
@@ -811,11 +953,7 @@ def write_cpu_baseline(args, W, bytes_per_token):
 
     import synth
     from oracle import oscar_ref as o
-    try:
-        import threadpoolctl
-        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count()
+    threads = blas_threads()
     hq, hkv, G = W["hq"], W["hkv"], W["G"]
     L = int(W["len_hi"])
     ld = synth.LayerData(args.seed + 1000, 0, hq, hkv)
@@ -829,51 +967,61 @@ def write_cpu_baseline(args, W, bytes_per_token):
         ref.write(R, R, 6.0, 6.0, k[done:done + chunk], v[done:done + chunk], [0, chunk], [done])
         done += chunk
     tok_s = done / (time.time() - t0)
-    return {"value": round(tok_s * bytes_per_token / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"first {done} tokens of one {L}-token prompt into one layer (Hkv {hkv}, G {G}), written in "
-                      f"chunks of {chunk}: {tok_s:.0f} tokens/s x the bytes per token of one layer's write"}
+    out = {"value": round(tok_s * bytes_per_token / 1e9, 4), "unit": "GB/s", "kind": "oracle",
+           "sample": f"first {done} tokens of one {L}-token prompt into one layer (Hkv {hkv}, G {G}), written in "
+                     f"chunks of {chunk}: {tok_s:.0f} tokens/s x the bytes per token of one layer's write"}
+    out.update(host_info(threads))
+    return out
 
 
-def cpu_baseline(args, W, final_lens, step_bytes):
-    """The fp64 oracle timed on the host on a bounded sample: one layer of the
-    workload (first request only), prefilled untimed, then repeated
-    (append one token + decode) rounds timed; scaled to a whole step."""
+def cpu_baseline(args, W, final_lens, step_bytes, kv_sample=None):
+    """The fp64 oracle timed on the host on a bounded sample of the step: one
+    layer of the first request (kv_sample: only that many KV heads, with their
+    query heads), prefilled untimed, then rounds of (append one token +
+    decode) timed for up to ~20 s.  value = the algorithmic bytes of the
+    sampled rounds / their time, the same unit as the GPU's value; the whole
+    step's time at that rate is reported as extrapolated."""
     import numpy as np
 
     import synth
     from oracle import oscar_ref as o
-    try:
-        import threadpoolctl
-        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count()
+    threads = blas_threads()
     hq, hkv, G = W["hq"], W["hkv"], W["G"]
+    gqa = hq // hkv
+    hkv_s = kv_sample or hkv
+    hq_s = gqa * hkv_s
     L = int(final_lens[0])
-    ld = synth.LayerData(args.seed + 1000, 0, hq, hkv)
+    ld = synth.LayerData(args.seed + 1000, 0, hq_s, hkv_s)
     k, v = ld.cache_kv(L + 16)
     rng = np.random.default_rng(args.seed)
     R = np.linalg.qr(rng.standard_normal((128, 128)))[0]
     pt, npool = synth.shuffled_page_tables(args.seed, 0, [L + 16])
-    ref = o.LayerCacheRef(hkv, G, npool, 9, pt, synth.bf16_page_tables(1))
+    ref = o.LayerCacheRef(hkv_s, G, npool, 9, pt, synth.bf16_page_tables(1))
+    t_pre = time.time()
     ref.write(R, R, 6.0, 6.0, k[:L - 8], v[:L - 8], [0, L - 8], [0])
+    prefill_s = time.time() - t_pre
     q = ld.decode_q(1)
     t0 = time.time()
-    rounds = 0
+    rounds, sample_bytes = 0, 0
     cur = L - 8
     while rounds < 8 and (rounds < 2 or time.time() - t0 < 20.0):
         ref.write(R, R, 6.0, 6.0, k[cur:cur + 1], v[cur:cur + 1], [0, 1], [cur])
         cur += 1
         o.decode_attn(ref, R, R, q, [cur], 1 / math.sqrt(128))
+        sample_bytes += decode_bytes([cur], hq_s, hkv_s, G) + append_bytes(1, hkv_s, G)
         rounds += 1
-    per_layer_req_s = (time.time() - t0) / rounds
-    # a step = every layer x every request
-    step_s = per_layer_req_s * W["layers"] * len(final_lens)
-    return {"value": round(step_bytes / step_s / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{rounds} rounds of (append 1 token + decode) on one layer of one {L}-token request "
-                      f"(Hq {hq}, Hkv {hkv}, G {G}), {per_layer_req_s:.2f} s each, scaled x{W['layers']} layers "
-                      f"x{len(final_lens)} requests",
-            "s_per_step_extrapolated": round(step_s, 2)}
+    dt = time.time() - t0
+    rate = sample_bytes / dt
+    heads = f"{hkv_s} of {hkv} KV heads" if hkv_s != hkv else f"all {hkv} KV heads"
+    exact = W["layers"] == 1 and len(final_lens) == 1 and hkv_s == hkv
+    out = {"value": round(rate / 1e9, 4), "unit": "GB/s", "kind": "oracle",
+           "sample": f"{rounds} rounds of (append 1 token + decode) on one layer of one {L}-token request "
+                     f"({heads}, {gqa} query heads each, G {G}): {dt / rounds:.2f} s per round; value = "
+                     f"algorithmic bytes of those rounds / their time",
+           "measured" if exact else "s_per_step_extrapolated": round(step_bytes / rate, 3),
+           "prefill_untimed_s": round(prefill_s, 1)}
+    out.update(host_info(threads))
+    return out
 
 
 if __name__ == "__main__":

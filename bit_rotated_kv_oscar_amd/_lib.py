@@ -75,6 +75,8 @@ SIGNATURES = [
       c_p, ctypes.c_int32, c_p, c_p, c_p, c_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
       ctypes.c_float, c_p, c_p]),
     ("oscar_profile_events", ctypes.c_int, [c_p, c_p]),
+    ("oscar_read_probe", ctypes.c_int,
+     [c_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, c_p, c_p, c_p]),
     ("oscar_bf16_decode_workspace_bytes", ctypes.c_size_t,
      [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
     ("oscar_bf16_paged_decode", ctypes.c_int,

@@ -247,6 +247,25 @@ def profile_events(before: "torch.cuda.Event | None", after: "torch.cuda.Event |
     check(load().oscar_profile_events(h0, h1))
 
 
+def read_probe(buf: torch.Tensor, n_blocks: int, block_bytes: int, ids: torch.Tensor | None = None,
+               sink: torch.Tensor | None = None) -> torch.Tensor:
+    """oscar_read_probe: reads n_blocks blocks of block_bytes bytes of buf
+    (slot ids[i], or slot i without ids) and adds their 32-bit words mod 2^32
+    into sink (int32 [1] on the device, returned)."""
+    dev = buf.device
+    _need(buf, "buf", (torch.uint8,), dev)
+    if ids is not None:
+        _need(ids, "ids", (torch.int32,), dev)
+        if ids.numel() < n_blocks:
+            raise ValueError("ids holds fewer than n_blocks entries")
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    _need(sink, "sink", (torch.int32,), dev)
+    check(load().oscar_read_probe(_ptr(buf), buf.numel(), int(n_blocks), int(block_bytes), _ptr(ids), _ptr(sink),
+                                  _stream(dev)))
+    return sink
+
+
 def calib_accumulate(q_cal: torch.Tensor, k_cal: torch.Tensor, v_cal: torch.Tensor, sums: torch.Tensor) -> int:
     """oscar_calib_accumulate: adds one calibration sequence's moment sums to
     sums (float64 [2, 128, 128] on the device); returns n_tokens * Hq, the

@@ -114,6 +114,22 @@ int oscar_profile_events(void *before, void *after) {
   return OSCAR_OK;
 }
 
+int oscar_read_probe(const void *buf, int64_t buf_bytes, int64_t n_blocks, int32_t block_bytes, const int32_t *ids,
+                     uint32_t *sink, oscar_stream_t stream) {
+  if (!buf || !sink) return fail(OSCAR_EINVAL, "read_probe: buf or sink is NULL");
+  if (block_bytes < 16 || block_bytes > 4096 || block_bytes % 16)
+    return fail(OSCAR_EINVAL, "read_probe: block_bytes %d not a multiple of 16 in [16, 4096]", block_bytes);
+  if (n_blocks < 1 || buf_bytes < block_bytes) return fail(OSCAR_EINVAL, "read_probe: no blocks to read");
+  if (!ids && n_blocks > buf_bytes / block_bytes)
+    return fail(OSCAR_EINVAL, "read_probe: %lld blocks of %d bytes exceed the %lld-byte buffer", (long long)n_blocks,
+                block_bytes, (long long)buf_bytes);
+  if (int rc = check_device()) return rc;
+  hipError_t e = oscar::launch_read_probe(buf, buf_bytes, n_blocks, block_bytes, ids, sink,
+                                          reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "read_probe");
+  return OSCAR_OK;
+}
+
 const char *oscar_last_error(void) { return g_err.c_str(); }
 
 const char *oscar_version(void) { return "oscar-gfx950 0.1"; }

@@ -85,4 +85,10 @@ hipError_t launch_jacobi(double *a, double *vt, int *sweeps, hipStream_t s);
 hipError_t launch_calib_rotate_abs(const uint16_t *x, int64_t n_vec, const double *R,
                                    double *y, hipStream_t s);
 
+// Read probe: sums (mod 2^32) the words of n_blocks blocks of block_bytes
+// bytes into *sink; block i is slot ids[i] of buf (ids null: slot i), slots
+// outside the buf_bytes / block_bytes of buf are skipped.
+hipError_t launch_read_probe(const void *buf, int64_t buf_bytes, int64_t n_blocks, int block_bytes,
+                             const int32_t *ids, uint32_t *sink, hipStream_t s);
+
 }  // namespace oscar

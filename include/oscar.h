@@ -348,6 +348,23 @@ OSCAR_API int oscar_bf16_paged_decode(const uint16_t *q, const uint16_t *kv_page
  * them is NULL. */
 OSCAR_API int oscar_profile_events(void *before, void *after);
 
+/* Instrumentation for benchmarks: the read ceiling of the device.  Reads
+ * n_blocks blocks of block_bytes bytes each with 16-byte vector loads --
+ * block i is slot ids[i] of buf (slot k = bytes k*block_bytes ..
+ * (k+1)*block_bytes-1), or slot i itself when ids is NULL -- and adds every
+ * 32-bit word read, modulo 2^32, to *sink, so that no read can be left out.
+ * Contiguous slots measure streaming reads; a permuted ids array measures
+ * gathers of page-sized blocks, the access pattern of the decode's history
+ * reads.  The decode kernels' bandwidth is reported against both ceilings.
+ * buf: device, buf_bytes long; ids: device int32 [n_blocks] or NULL; sink:
+ * device uint32.  Ids outside [0, buf_bytes / block_bytes) are skipped.
+ * The next launch is timed by oscar_profile_events like the decode kernels.
+ * Errors: OSCAR_EINVAL for NULL buf or sink, block_bytes not a multiple of
+ * 16 in [16, 4096], n_blocks < 1, or (ids NULL) n_blocks * block_bytes >
+ * buf_bytes; OSCAR_EHIP. */
+OSCAR_API int oscar_read_probe(const void *buf, int64_t buf_bytes, int64_t n_blocks, int32_t block_bytes,
+                               const int32_t *ids, uint32_t *sink, oscar_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -221,3 +221,14 @@ def test_extend_validation_codes():
     assert call(max_new=0, total=0, q=0) == E.OSCAR_OK
     if NO_GPU:
         assert call() == E.OSCAR_ENODEV
+
+
+def test_read_probe_validation_codes():
+    lib = _lib.load()
+    E = _lib
+    assert lib.oscar_read_probe(0, 4096, 1, 1024, None, 0x10, None) == E.OSCAR_EINVAL        # NULL buf
+    assert lib.oscar_read_probe(0x10, 4096, 1, 1024, None, 0, None) == E.OSCAR_EINVAL        # NULL sink
+    assert lib.oscar_read_probe(0x10, 4096, 1, 1000, None, 0x10, None) == E.OSCAR_EINVAL     # not x16
+    assert lib.oscar_read_probe(0x10, 1 << 20, 1, 8192, None, 0x10, None) == E.OSCAR_EINVAL  # > 4096
+    assert lib.oscar_read_probe(0x10, 4096, 0, 1024, None, 0x10, None) == E.OSCAR_EINVAL     # no blocks
+    assert lib.oscar_read_probe(0x10, 4096, 5, 1024, None, 0x10, None) == E.OSCAR_EINVAL     # past the end
