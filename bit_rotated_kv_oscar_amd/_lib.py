@@ -75,6 +75,10 @@ SIGNATURES = [
       c_p, ctypes.c_int32, c_p, c_p, c_p, c_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
       ctypes.c_float, c_p, c_p]),
     ("oscar_profile_events", ctypes.c_int, [c_p, c_p]),
+    ("oscar_decode_noalloc_max_bytes", ctypes.c_size_t, []),
+    ("oscar_decode_attn_noalloc", ctypes.c_int,
+     [ctypes.POINTER(LayerCacheC), ctypes.POINTER(RotationC), ctypes.POINTER(RotationC),
+      c_p, ctypes.c_int32, c_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, c_p, c_p]),
     ("oscar_read_probe", ctypes.c_int,
      [c_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, c_p, c_p, c_p]),
     ("oscar_bf16_decode_workspace_bytes", ctypes.c_size_t,

@@ -144,6 +144,28 @@ def decode_attn(cache: LayerCache, rot_k: Rotation, rot_v: Rotation, q: torch.Te
     return out
 
 
+def decode_attn_noalloc(cache: LayerCache, rot_k: Rotation, rot_v: Rotation, q: torch.Tensor,
+                        seq_lens: torch.Tensor, max_seq_len: int, sm_scale: float | None = None,
+                        out: torch.Tensor | None = None) -> torch.Tensor:
+    """oscar_decode_attn_noalloc: oscar_decode_attn on the library's own
+    per-GPU scratch (no workspace, no allocation in the call)."""
+    dev = cache.device
+    _need(q, "q", (torch.bfloat16,), dev)
+    _need(seq_lens, "seq_lens", (torch.int32,), dev)
+    batch, hq = q.shape[0], q.shape[1]
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if out is None:
+        out = torch.empty((batch, hq, HEAD_DIM), dtype=torch.float32, device=dev)
+    _need(out, "out", (torch.float32,), dev)
+    c = cache.c()
+    rk, rv = rot_k.c(), rot_v.c()
+    check(load().oscar_decode_attn_noalloc(ctypes.byref(c), ctypes.byref(rk), ctypes.byref(rv), _ptr(q), hq,
+                                           _ptr(seq_lens), batch, int(max_seq_len), float(sm_scale), _ptr(out),
+                                           _stream(dev)))
+    return out
+
+
 def decode_step(cache: LayerCache, rot_k: Rotation, rot_v: Rotation, k_new: torch.Tensor,
                 v_new: torch.Tensor, len_before: torch.Tensor, q: torch.Tensor, max_seq_len: int,
                 sm_scale: float | None = None, out: torch.Tensor | None = None,

@@ -211,6 +211,40 @@ int oscar_decode_attn(const oscar_layer_cache *cache, const oscar_rotation *rot_
   return OSCAR_OK;
 }
 
+size_t oscar_decode_noalloc_max_bytes(void) { return oscar::NOALLOC_SCRATCH_BYTES; }
+
+int oscar_decode_attn_noalloc(const oscar_layer_cache *cache, const oscar_rotation *rot_k,
+                              const oscar_rotation *rot_v, const uint16_t *q, int32_t n_q_heads,
+                              const int32_t *seq_lens, int32_t batch, int32_t max_seq_len, float sm_scale,
+                              float *out, oscar_stream_t stream) {
+  if (int rc = check_cache(cache)) return rc;
+  if (int rc = check_rot(rot_k, "rot_k")) return rc;
+  if (int rc = check_rot(rot_v, "rot_v")) return rc;
+  if (int rc = check_heads(n_q_heads, cache->n_kv_heads)) return rc;
+  if (batch < 1 || batch > 65535) return fail(OSCAR_EINVAL, "batch %d outside [1, 65535]", batch);
+  if (max_seq_len < 1) return fail(OSCAR_EINVAL, "max_seq_len %d < 1", max_seq_len);
+  if (oscar::n_hist_pages(max_seq_len) > cache->hist_pt_stride)
+    return fail(OSCAR_EINVAL, "max_seq_len %d needs %d history pages, hist_pt_stride is %d", max_seq_len,
+                oscar::n_hist_pages(max_seq_len), cache->hist_pt_stride);
+  if (!q || !seq_lens || !out) return fail(OSCAR_EINVAL, "q, seq_lens or out is NULL");
+  if (!std::isfinite(sm_scale) || sm_scale <= 0.f) return fail(OSCAR_EINVAL, "sm_scale must be finite and > 0");
+  const int64_t units = int64_t(batch) * cache->n_kv_heads;
+  const size_t parts = oscar::decode_int2_parts_bytes(batch, n_q_heads, cache->n_kv_heads, max_seq_len);
+  const size_t room = oscar::NOALLOC_SCRATCH_BYTES -
+                      size_t(oscar::NOALLOC_MAX_UNITS) * 64 * sizeof(uint32_t);
+  if (units > oscar::NOALLOC_MAX_UNITS || parts > room)
+    return fail(OSCAR_EWORKSPACE,
+                "decode_attn_noalloc: %lld (request, KV head) units and %zu bytes of partials exceed the library's "
+                "scratch (%d units, %zu bytes); use oscar_decode_attn with a workspace",
+                (long long)units, parts, oscar::NOALLOC_MAX_UNITS, room);
+  if (int rc = check_device()) return rc;
+  hipError_t e = oscar::launch_decode_int2_noalloc(*cache, rot_arg(rot_k), rot_arg(rot_v), q, n_q_heads, seq_lens,
+                                                   batch, max_seq_len, sm_scale, out,
+                                                   reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode_attn_noalloc");
+  return OSCAR_OK;
+}
+
 int oscar_decode_step(const oscar_layer_cache *cache, const oscar_rotation *rot_k, const oscar_rotation *rot_v,
                       const uint16_t *k_new, const uint16_t *v_new, const int32_t *len_before,
                       const uint16_t *q, int32_t n_q_heads, int32_t batch, int32_t max_seq_len,

@@ -47,6 +47,7 @@
 //   (one block per (request, KV head)) combines the partials after the
 //   attend kernel, rotating the history part back once.
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 #include "attn_common.h"
@@ -1580,7 +1581,7 @@ static float pv_scale_for(float clip_v) {
 hipError_t launch_decode_step(const oscar_layer_cache &c, RotArg rk, RotArg rv, const uint16_t *k_new,
                               const uint16_t *v_new, const int32_t *len_before, const uint16_t *q,
                               int n_q_heads, const int32_t *seq_lens, int batch, int max_seq_len,
-                              float sm_scale, float *out, void *ws, hipStream_t s) {
+                              float sm_scale, float *out, void *ws, hipStream_t s, uint32_t *counters) {
   StepArgs a;
   a.c = c;
   a.fk = rk.forms;
@@ -1608,7 +1609,8 @@ hipError_t launch_decode_step(const oscar_layer_cache &c, RotArg rk, RotArg rv, 
   a.n_splits = p.n_splits;
   a.parts = static_cast<float *>(ws);
   a.part_slots = part_slots(p);
-  a.counters = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + parts_bytes(batch, n_q_heads, p));
+  a.counters = counters ? counters
+                        : reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + parts_bytes(batch, n_q_heads, p));
   switch (n_q_heads / c.n_kv_heads) {
     case 1: return launch_g<1>(a, p.fused, c.group, batch, c.n_kv_heads, s);
     case 2: return launch_g<2>(a, p.fused, c.group, batch, c.n_kv_heads, s);
@@ -1616,6 +1618,66 @@ hipError_t launch_decode_step(const oscar_layer_cache &c, RotArg rk, RotArg rv, 
     case 8: return launch_g<8>(a, p.fused, c.group, batch, c.n_kv_heads, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+// ------------------------------------------------------------------ scratch
+// Decode without a caller workspace (oscar_decode_attn_noalloc): the partials
+// and the merge counters live in this file-scope device array, one copy per
+// GPU.  Host code never passes the array's name to a kernel (on the host it
+// is a stand-in, not a device address): the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current and
+// kept.  Layout: the counters first (a fixed region, cleared by a fill
+// kernel when the address is first taken; every completed call leaves them
+// at zero again, whatever its shape), then the partials.
+constexpr size_t SCRATCH_COUNTERS = size_t(NOALLOC_MAX_UNITS) * COUNTER_STRIDE * sizeof(uint32_t);
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+static_assert(SCRATCH_COUNTERS % 256 == 0 && SCRATCH_COUNTERS < NOALLOC_SCRATCH_BYTES, "scratch layout");
+
+__global__ void __launch_bounds__(256) fill_u32_kernel(uint32_t *p, int64_t n, uint32_t v) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) p[i] = v;
+}
+
+namespace {
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+uint8_t *g_scratch_ptr[SCRATCH_MAX_DEVICES] = {};
+}  // namespace
+
+// The device address of this GPU's scratch array (set up on first use on the
+// device, counters cleared on stream s).
+static hipError_t scratch_address(hipStream_t s, uint8_t **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    const int64_t n = int64_t(SCRATCH_COUNTERS / sizeof(uint32_t));
+    hipLaunchKernelGGL(fill_u32_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s,
+                       static_cast<uint32_t *>(ptr), n, 0u);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<uint8_t *>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+size_t decode_int2_parts_bytes(int batch, int n_q_heads, int n_kv_heads, int max_seq_len) {
+  return parts_bytes(batch, n_q_heads, plan_int2_splits(batch, n_kv_heads, max_seq_len));
+}
+
+hipError_t launch_decode_int2_noalloc(const oscar_layer_cache &c, RotArg rk, RotArg rv, const uint16_t *q,
+                                      int n_q_heads, const int32_t *seq_lens, int batch, int max_seq_len,
+                                      float sm_scale, float *out, hipStream_t s) {
+  uint8_t *base = nullptr;
+  hipError_t e = scratch_address(s, &base);
+  if (e != hipSuccess) return e;
+  return launch_decode_step(c, rk, rv, nullptr, nullptr, nullptr, q, n_q_heads, seq_lens, batch, max_seq_len,
+                            sm_scale, out, base + SCRATCH_COUNTERS, s, reinterpret_cast<uint32_t *>(base));
 }
 
 hipError_t launch_decode_int2(const oscar_layer_cache &c, RotArg rk, RotArg rv, const uint16_t *q,

@@ -46,10 +46,23 @@ size_t decode_int2_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int max_se
 
 // Append one token per request (k_new / v_new [B][Hkv][128] at positions
 // len_before[b]) and, when q is non-null, decode with lengths len_before + 1.
+// counters: the merge counters (null: inside ws, after the partials)
 hipError_t launch_decode_step(const oscar_layer_cache &c, RotArg rk, RotArg rv, const uint16_t *k_new,
                               const uint16_t *v_new, const int32_t *len_before, const uint16_t *q,
                               int n_q_heads, const int32_t *seq_lens, int batch, int max_seq_len,
-                              float sm_scale, float *out, void *ws, hipStream_t s);
+                              float sm_scale, float *out, void *ws, hipStream_t s,
+                              uint32_t *counters = nullptr);
+
+// Decode with the library's own per-GPU scratch array instead of a caller
+// workspace (no allocation): at most NOALLOC_MAX_UNITS (request, KV head)
+// units and NOALLOC_SCRATCH_BYTES of scratch (counters first, then the
+// partials, decode_int2_parts_bytes of them).
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(16) << 20;
+constexpr int NOALLOC_MAX_UNITS = 4096;
+size_t decode_int2_parts_bytes(int batch, int n_q_heads, int n_kv_heads, int max_seq_len);
+hipError_t launch_decode_int2_noalloc(const oscar_layer_cache &c, RotArg rk, RotArg rv, const uint16_t *q,
+                                      int n_q_heads, const int32_t *seq_lens, int batch, int max_seq_len,
+                                      float sm_scale, float *out, hipStream_t s);
 
 hipError_t launch_decode_bf16(const uint16_t *q, const uint16_t *kv, int64_t n_pages,
                               const int32_t *pt, int pt_stride, const int32_t *seq_lens,

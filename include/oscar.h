@@ -267,6 +267,27 @@ OSCAR_API int oscar_decode_attn(const oscar_layer_cache *cache,
                       void *workspace, size_t workspace_bytes,
                       oscar_stream_t stream);
 
+/* oscar_decode_attn without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation): the partials and merge counters live in a
+ * scratch array inside the library, one per GPU, held until the process
+ * ends.  Same arguments, layout and results as oscar_decode_attn (the same
+ * kernels and split plan), minus the workspace.  This call allocates
+ * nothing.  Limit: at most 4096 (request, KV head) units and
+ * oscar_decode_noalloc_max_bytes() bytes of scratch in all (16 MiB, of
+ * which 1 MiB holds the counters); beyond that it returns OSCAR_EWORKSPACE
+ * and launches nothing.  All calls on one GPU share its scratch array:
+ * calls that overlap on one GPU (several streams or host threads at once)
+ * race and must be serialised by the caller; a call that faulted on the
+ * device may leave the counters dirty for later calls in this process. */
+OSCAR_API size_t oscar_decode_noalloc_max_bytes(void);
+OSCAR_API int oscar_decode_attn_noalloc(const oscar_layer_cache *cache,
+                                        const oscar_rotation *rot_k, const oscar_rotation *rot_v,
+                                        const uint16_t *q, int32_t n_q_heads,
+                                        const int32_t *seq_lens, int32_t batch,
+                                        int32_t max_seq_len, float sm_scale, float *out,
+                                        oscar_stream_t stream);
+
 /* One generation step of a layer: write-on-append of one token per request
  * followed by the decode over the grown cache ([abs] "fused Triton write and
  * decode kernels"; [nl]/[fr] §2.2.B).  Request b's new token k_new[b],

@@ -232,3 +232,26 @@ def test_read_probe_validation_codes():
     assert lib.oscar_read_probe(0x10, 1 << 20, 1, 8192, None, 0x10, None) == E.OSCAR_EINVAL  # > 4096
     assert lib.oscar_read_probe(0x10, 4096, 0, 1024, None, 0x10, None) == E.OSCAR_EINVAL     # no blocks
     assert lib.oscar_read_probe(0x10, 4096, 5, 1024, None, 0x10, None) == E.OSCAR_EINVAL     # past the end
+
+
+def _decode_noalloc(c=None, hq=8, batch=1, max_len=150, scale=0.088, q=0xB000):
+    lib = _lib.load()
+    c = c if c is not None else _cache()
+    return lib.oscar_decode_attn_noalloc(ctypes.byref(c), ctypes.byref(ROT), ctypes.byref(ROT), q, hq, 0xC000, batch,
+                                         max_len, scale, 0xD000, None)
+
+
+def test_decode_noalloc_validation_codes():
+    E = _lib
+    assert _lib.load().oscar_decode_noalloc_max_bytes() == 16 << 20
+    assert _decode_noalloc(hq=7) == E.OSCAR_EUNSUPPORTED
+    assert _decode_noalloc(max_len=0) == E.OSCAR_EINVAL
+    assert _decode_noalloc(q=0) == E.OSCAR_EINVAL
+    assert _decode_noalloc(batch=0) == E.OSCAR_EINVAL
+    # beyond the library's scratch: more (request, KV head) units than it
+    # holds, or more partials than fit -- refused before any device call
+    assert _decode_noalloc(batch=4097) == E.OSCAR_EWORKSPACE and "scratch" in _err()
+    big = _cache(hist_pt_stride=4096)
+    assert _decode_noalloc(c=big, batch=300, max_len=60000) == E.OSCAR_EWORKSPACE
+    if NO_GPU:
+        assert _decode_noalloc() == E.OSCAR_ENODEV
