@@ -49,14 +49,18 @@ SIGNATURES = [
     ("oscar_hist_block_bytes", ctypes.c_size_t, [ctypes.c_int32]),
     ("oscar_rotation_bytes", ctypes.c_size_t, []),
     ("oscar_prepare_rotation", ctypes.c_int, [c_p, c_p, c_p]),
+    ("oscar_calibrate_workspace_bytes", ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),
+    ("oscar_calib_accumulate_workspace_bytes", ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),
+    ("oscar_calib_rotations_workspace_bytes", ctypes.c_size_t, []),
+    ("oscar_clip_threshold_workspace_bytes", ctypes.c_size_t, [ctypes.c_int64]),
     ("oscar_calibrate_rotation", ctypes.c_int,
      [c_p, c_p, c_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
-      c_p, c_p, c_p, c_p, c_p]),
+      c_p, c_p, c_p, c_p, c_p, ctypes.c_size_t, c_p]),
     ("oscar_calib_accumulate", ctypes.c_int,
-     [c_p, c_p, c_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, c_p, c_p]),
-    ("oscar_calib_rotations", ctypes.c_int, [c_p, ctypes.c_double, c_p, c_p, c_p]),
+     [c_p, c_p, c_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, c_p, c_p, ctypes.c_size_t, c_p]),
+    ("oscar_calib_rotations", ctypes.c_int, [c_p, ctypes.c_double, c_p, c_p, c_p, ctypes.c_size_t, c_p]),
     ("oscar_clip_threshold", ctypes.c_int,
-     [c_p, ctypes.c_int64, c_p, ctypes.c_double, c_p, c_p]),
+     [c_p, ctypes.c_int64, c_p, ctypes.c_double, c_p, c_p, ctypes.c_size_t, c_p]),
     ("oscar_write_kv", ctypes.c_int,
      [ctypes.POINTER(LayerCacheC), ctypes.POINTER(RotationC), ctypes.POINTER(RotationC),
       c_p, c_p, c_p, c_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, c_p]),

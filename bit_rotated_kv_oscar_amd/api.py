@@ -298,8 +298,10 @@ def calib_accumulate(q_cal: torch.Tensor, k_cal: torch.Tensor, v_cal: torch.Tens
     _need(sums, "sums", (torch.float64,), dev)
     if tuple(sums.shape) != (2, HEAD_DIM, HEAD_DIM):
         raise ValueError("sums must be [2, 128, 128]")
+    n = int(load().oscar_calib_accumulate_workspace_bytes(q_cal.shape[0], q_cal.shape[1], k_cal.shape[1]))
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
     check(load().oscar_calib_accumulate(_ptr(q_cal), _ptr(k_cal), _ptr(v_cal), q_cal.shape[0], q_cal.shape[1],
-                                        k_cal.shape[1], _ptr(sums), _stream(dev)))
+                                        k_cal.shape[1], _ptr(sums), _ptr(ws), ws.numel(), _stream(dev)))
     return int(q_cal.shape[0] * q_cal.shape[1])
 
 
@@ -310,7 +312,9 @@ def calib_rotations(sums: torch.Tensor, count: float):
     _need(sums, "sums", (torch.float64,), dev)
     R_K = torch.empty((HEAD_DIM, HEAD_DIM), dtype=torch.float64)
     R_V = torch.empty((HEAD_DIM, HEAD_DIM), dtype=torch.float64)
-    check(load().oscar_calib_rotations(_ptr(sums), float(count), _ptr(R_K), _ptr(R_V), _stream(dev)))
+    ws = torch.empty(int(load().oscar_calib_rotations_workspace_bytes()), dtype=torch.uint8, device=dev)
+    check(load().oscar_calib_rotations(_ptr(sums), float(count), _ptr(R_K), _ptr(R_V), _ptr(ws), ws.numel(),
+                                       _stream(dev)))
     return R_K, R_V
 
 
@@ -323,8 +327,10 @@ def clip_threshold(x_cal: torch.Tensor, R: torch.Tensor, clip_quantile: float = 
     if R.shape != (HEAD_DIM, HEAD_DIM):
         raise ValueError("R must be [128, 128]")
     out = ctypes.c_float(0)
-    check(load().oscar_clip_threshold(_ptr(x_cal), x_cal.numel() // HEAD_DIM, _ptr(R), float(clip_quantile),
-                                      ctypes.byref(out), _stream(dev)))
+    n_vec = x_cal.numel() // HEAD_DIM
+    ws = torch.empty(max(int(load().oscar_clip_threshold_workspace_bytes(n_vec)), 1), dtype=torch.uint8, device=dev)
+    check(load().oscar_clip_threshold(_ptr(x_cal), n_vec, _ptr(R), float(clip_quantile),
+                                      ctypes.byref(out), _ptr(ws), ws.numel(), _stream(dev)))
     return out.value
 
 
@@ -338,8 +344,10 @@ def calibrate_rotation(q_cal: torch.Tensor, k_cal: torch.Tensor, v_cal: torch.Te
     R_K = torch.empty((HEAD_DIM, HEAD_DIM), dtype=torch.float64)
     R_V = torch.empty((HEAD_DIM, HEAD_DIM), dtype=torch.float64)
     ck, cv = ctypes.c_float(0), ctypes.c_float(0)
+    n = int(load().oscar_calibrate_workspace_bytes(q_cal.shape[0], q_cal.shape[1], k_cal.shape[1]))
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
     check(load().oscar_calibrate_rotation(_ptr(q_cal), _ptr(k_cal), _ptr(v_cal), q_cal.shape[0],
                                           q_cal.shape[1], k_cal.shape[1], float(clip_quantile),
                                           _ptr(R_K), _ptr(R_V), ctypes.byref(ck), ctypes.byref(cv),
-                                          _stream(dev)))
+                                          _ptr(ws), ws.numel(), _stream(dev)))
     return R_K, R_V, ck.value, cv.value

@@ -1,5 +1,6 @@
 // extern "C" entry points of liboscar: argument validation, workspace sizing,
 // error reporting, and the host side of calibration.
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -29,18 +30,19 @@ int hip_fail(hipError_t e, const char *where) {
   return fail(OSCAR_EHIP, "%s: HIP error %d (%s)", where, int(e), hipGetErrorString(e));
 }
 
-// The current device must be gfx950; the answer is cached per device id.
+// The current device must be gfx950; the answer (an immutable property of
+// the device) is cached per device id.
 int check_device() {
-  static int cached[64] = {0};  // 0 unknown, 1 ok, -1 not gfx950
+  static std::atomic<int> cached[64];  // 0 unknown, 1 ok, -1 not gfx950
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess || dev < 0) return fail(OSCAR_ENODEV, "no HIP device (%s)", hipGetErrorString(e));
-  if (dev < 64 && cached[dev] == 1) return OSCAR_OK;
+  if (dev < 64 && cached[dev].load(std::memory_order_relaxed) == 1) return OSCAR_OK;
   hipDeviceProp_t prop;
   e = hipGetDeviceProperties(&prop, dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
   const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-  if (dev < 64) cached[dev] = ok ? 1 : -1;
+  if (dev < 64) cached[dev].store(ok ? 1 : -1, std::memory_order_relaxed);
   if (!ok) return fail(OSCAR_ENODEV, "device %d is %s, this library is built for gfx950", dev, prop.gcnArchName);
   return OSCAR_OK;
 }
@@ -82,24 +84,105 @@ KernelEvents &profile_events() { return g_events; }
 
 namespace {
 
+constexpr int kJacobiSweeps = oscar::JACOBI_MAX_SWEEPS;
+
 // Eigenbasis (sorted, signed) of the symmetric 128 x 128 matrix at mat (device,
 // destroyed) by the device Jacobi iteration; work: device scratch of
-// 128 * 128 doubles + one int.
-hipError_t device_eigenbasis(double *mat, double *work, hipStream_t s, std::vector<double> &U) {
+// 128 * 128 doubles + one int.  *converged: whether the iteration met its
+// tolerance within kJacobiSweeps sweeps.
+hipError_t device_eigenbasis(double *mat, double *work, hipStream_t s, std::vector<double> &U, bool *converged) {
   const int D = oscar::D;
   int *sweeps = reinterpret_cast<int *>(work + D * D);
   hipError_t e = oscar::launch_jacobi(mat, work, sweeps, s);
   std::vector<double> VT(D * D), V(D * D), A(D * D), w(D);
+  int n_sweeps = 0;
   if (e == hipSuccess) e = hipMemcpyAsync(VT.data(), work, VT.size() * sizeof(double), hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipMemcpyAsync(A.data(), mat, A.size() * sizeof(double), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(&n_sweeps, sweeps, sizeof(int), hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return e;
+  *converged = n_sweeps < kJacobiSweeps;
   for (int i = 0; i < D; ++i) {
     w[i] = A[size_t(i) * D + i];
     for (int j = 0; j < D; ++j) V[size_t(i) * D + j] = VT[size_t(j) * D + i];
   }
   oscar::sorted_basis(V, w, D, U);
   return hipSuccess;
+}
+
+// The p quantile (linear interpolation between order statistics, type 7) of
+// n non-negative doubles y on the device: the two order statistics by radix
+// selection (host memory independent of n), the interpolation as numpy's.
+hipError_t device_quantile(const double *y, int64_t n, double p, void *scratch, hipStream_t s, double *q) {
+  const double h = double(n - 1) * p;
+  int64_t lo = int64_t(std::floor(h));
+  if (lo > n - 1) lo = n - 1;
+  double a = 0.0, b = 0.0;
+  hipError_t e = oscar::select_order_stats(y, n, lo, scratch, s, &a, &b);
+  if (e != hipSuccess) return e;
+  if (lo >= n - 1) {
+    *q = a;
+    return hipSuccess;
+  }
+  const double t = h - double(lo);
+  *q = t >= 0.5 ? b - (b - a) * (1.0 - t) : a + (b - a) * t;
+  return hipSuccess;
+}
+
+size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct CalibLayout {
+  size_t cov, o, rd, y, part, sel, total;
+};
+CalibLayout calib_layout(int64_t n_tokens, int32_t hq, int32_t hkv) {
+  const size_t D = oscar::D;
+  CalibLayout l;
+  l.cov = 0;
+  l.o = l.cov + al256(2 * D * D * sizeof(double));
+  l.rd = l.o + al256(size_t(n_tokens) * hq * D * sizeof(double));
+  l.y = l.rd + al256(D * D * sizeof(double));
+  l.part = l.y + al256(size_t(n_tokens) * hkv * D * sizeof(double));
+  const size_t part = oscar::calib_outer_part_bytes() > D * D * sizeof(double) + 256
+                          ? oscar::calib_outer_part_bytes() : D * D * sizeof(double) + 256;
+  l.sel = l.part + al256(part);
+  l.total = l.sel + al256(oscar::select_scratch_bytes());
+  return l;
+}
+
+struct AccumLayout {
+  size_t o, part, total;
+};
+AccumLayout accum_layout(int64_t n_tokens, int32_t hq) {
+  AccumLayout l;
+  l.o = 0;
+  l.part = al256(size_t(n_tokens) * hq * oscar::D * sizeof(double));
+  l.total = l.part + al256(oscar::calib_outer_part_bytes());
+  return l;
+}
+
+struct RotationsLayout {
+  size_t mat, work, total;
+};
+RotationsLayout rotations_layout() {
+  const size_t D = oscar::D;
+  RotationsLayout l;
+  l.mat = 0;
+  l.work = al256(2 * D * D * sizeof(double));
+  l.total = l.work + al256(D * D * sizeof(double) + 256);
+  return l;
+}
+
+struct ClipLayout {
+  size_t rd, y, sel, total;
+};
+ClipLayout clip_layout(int64_t n_vec) {
+  const size_t D = oscar::D;
+  ClipLayout l;
+  l.rd = 0;
+  l.y = al256(D * D * sizeof(double));
+  l.sel = l.y + al256(size_t(n_vec) * D * sizeof(double));
+  l.total = l.sel + al256(oscar::select_scratch_bytes());
+  return l;
 }
 
 }  // namespace
@@ -330,53 +413,68 @@ int oscar_bf16_paged_decode(const uint16_t *q, const uint16_t *kv_pages, int64_t
   return OSCAR_OK;
 }
 
+// ---------------------------------------------------------------- calibration
+// Every calibration call works in a caller workspace (no allocation in the
+// library): the layouts below, each region 256-byte aligned.
+
+size_t oscar_calibrate_workspace_bytes(int64_t n_tokens, int32_t n_q_heads, int32_t n_kv_heads) {
+  if (n_tokens < 1 || n_q_heads < 1 || n_kv_heads < 1) return 0;
+  return calib_layout(n_tokens, n_q_heads, n_kv_heads).total;
+}
+
+size_t oscar_calib_accumulate_workspace_bytes(int64_t n_tokens, int32_t n_q_heads, int32_t n_kv_heads) {
+  if (n_tokens < 1 || n_q_heads < 1 || n_kv_heads < 1) return 0;
+  return accum_layout(n_tokens, n_q_heads).total;
+}
+
+size_t oscar_calib_rotations_workspace_bytes(void) { return rotations_layout().total; }
+
+size_t oscar_clip_threshold_workspace_bytes(int64_t n_vec) {
+  if (n_vec < 1) return 0;
+  return clip_layout(n_vec).total;
+}
+
 int oscar_calibrate_rotation(const uint16_t *q_cal, const uint16_t *k_cal, const uint16_t *v_cal,
                              int64_t n_tokens, int32_t n_q_heads, int32_t n_kv_heads,
                              double clip_quantile, double *R_K, double *R_V, float *clip_K,
-                             float *clip_V, oscar_stream_t stream) {
+                             float *clip_V, void *workspace, size_t workspace_bytes, oscar_stream_t stream) {
   if (!q_cal || !k_cal || !v_cal) return fail(OSCAR_EINVAL, "calibration inputs NULL");
   if (!R_K || !R_V || !clip_K || !clip_V) return fail(OSCAR_EINVAL, "outputs NULL");
   if (n_tokens < 1 || n_tokens > 65536) return fail(OSCAR_EINVAL, "n_tokens %lld outside [1, 65536]", (long long)n_tokens);
   if (n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || n_q_heads > 256)
     return fail(OSCAR_EUNSUPPORTED, "head counts %d/%d unsupported", n_q_heads, n_kv_heads);
   if (!(clip_quantile > 0.0 && clip_quantile <= 1.0)) return fail(OSCAR_EINVAL, "clip_quantile must be in (0, 1]");
+  const CalibLayout lay = calib_layout(n_tokens, n_q_heads, n_kv_heads);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(OSCAR_EWORKSPACE, "calibrate: workspace of %zu bytes needed, %zu given", lay.total,
+                workspace ? workspace_bytes : 0);
   if (int rc = check_device()) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int D = oscar::D;
+  char *w = static_cast<char *>(workspace);
+  double *cov = reinterpret_cast<double *>(w + lay.cov), *o = reinterpret_cast<double *>(w + lay.o);
+  double *Rd = reinterpret_cast<double *>(w + lay.rd), *y = reinterpret_cast<double *>(w + lay.y);
+  double *part = reinterpret_cast<double *>(w + lay.part);
+  void *sel = w + lay.sel;
   const int64_t nq = n_tokens * n_q_heads, nkv = n_tokens * n_kv_heads;
-  double *cov = nullptr, *o = nullptr, *Rd = nullptr, *y = nullptr, *part = nullptr;
-  int rc = OSCAR_OK;
   hipError_t e;
-  auto cleanup = [&]() {
-    if (cov) (void)hipFree(cov);
-    if (o) (void)hipFree(o);
-    if (Rd) (void)hipFree(Rd);
-    if (y) (void)hipFree(y);
-    if (part) (void)hipFree(part);
-  };
-#define CHECK_HIP(expr, where)       \
-  do {                               \
-    e = (expr);                      \
-    if (e != hipSuccess) {           \
-      rc = hip_fail(e, where);       \
-      cleanup();                     \
-      return rc;                     \
-    }                                \
+#define CHECK_HIP(expr, where)             \
+  do {                                     \
+    e = (expr);                            \
+    if (e != hipSuccess) return hip_fail(e, where); \
   } while (0)
-  CHECK_HIP(hipMalloc(&cov, 2 * D * D * sizeof(double)), "hipMalloc");
-  CHECK_HIP(hipMalloc(&o, size_t(nq) * D * sizeof(double)), "hipMalloc");
-  CHECK_HIP(hipMalloc(&Rd, D * D * sizeof(double)), "hipMalloc");
-  CHECK_HIP(hipMalloc(&y, size_t(nkv) * D * sizeof(double)), "hipMalloc");
-  CHECK_HIP(hipMalloc(&part, oscar::calib_outer_part_bytes()), "hipMalloc");
   CHECK_HIP(oscar::launch_calib_outer(q_cal, nullptr, nq, cov, part, s), "calib C_Q");
   CHECK_HIP(oscar::launch_calib_attention(q_cal, k_cal, v_cal, n_tokens, n_q_heads, n_kv_heads, o, s), "calib attention");
   CHECK_HIP(oscar::launch_calib_outer(nullptr, o, nq, cov + D * D, part, s), "calib C_S");
   // eigenbases of the sums (the 1/(N Hq) scale changes no eigenvector);
   // the Jacobi work area reuses the first partials of the moment step
-  std::vector<double> U, Rk, Rv, absv(size_t(nkv) * D);
-  CHECK_HIP(device_eigenbasis(cov, part, s, U), "eigenbasis C_Q");
+  std::vector<double> U, Rk, Rv;
+  bool conv = true;
+  CHECK_HIP(device_eigenbasis(cov, part, s, U, &conv), "eigenbasis C_Q");
+  if (!conv) return fail(OSCAR_EINVAL, "calibrate: the eigen-iteration of C_Q did not converge in %d sweeps", kJacobiSweeps);
   oscar::compose_rotation(U, Rk);
-  CHECK_HIP(device_eigenbasis(cov + D * D, part, s, U), "eigenbasis C_S");
+  CHECK_HIP(device_eigenbasis(cov + D * D, part, s, U, &conv), "eigenbasis C_S");
+  if (!conv) return fail(OSCAR_EINVAL, "calibrate: the eigen-iteration of C_S did not converge in %d sweeps", kJacobiSweeps);
   oscar::compose_rotation(U, Rv);
   double clips[2];
   const uint16_t *xs[2] = {k_cal, v_cal};
@@ -384,12 +482,9 @@ int oscar_calibrate_rotation(const uint16_t *q_cal, const uint16_t *k_cal, const
   for (int t = 0; t < 2; ++t) {
     CHECK_HIP(hipMemcpyAsync(Rd, Rs[t]->data(), D * D * sizeof(double), hipMemcpyHostToDevice, s), "copy R");
     CHECK_HIP(oscar::launch_calib_rotate_abs(xs[t], nkv, Rd, y, s), "calib |x R|");
-    CHECK_HIP(hipMemcpyAsync(absv.data(), y, absv.size() * sizeof(double), hipMemcpyDeviceToHost, s), "copy |x R|");
-    CHECK_HIP(hipStreamSynchronize(s), "sync");
-    clips[t] = oscar::quantile_linear(absv, clip_quantile);
+    CHECK_HIP(device_quantile(y, nkv * D, clip_quantile, sel, s, &clips[t]), "clip quantile");
   }
 #undef CHECK_HIP
-  cleanup();
   std::memcpy(R_K, Rk.data(), D * D * sizeof(double));
   std::memcpy(R_V, Rv.data(), D * D * sizeof(double));
   *clip_K = float(clips[0]);
@@ -399,31 +494,37 @@ int oscar_calibrate_rotation(const uint16_t *q_cal, const uint16_t *k_cal, const
 
 int oscar_calib_accumulate(const uint16_t *q_cal, const uint16_t *k_cal, const uint16_t *v_cal,
                            int64_t n_tokens, int32_t n_q_heads, int32_t n_kv_heads, double *sums,
-                           oscar_stream_t stream) {
+                           void *workspace, size_t workspace_bytes, oscar_stream_t stream) {
   if (!q_cal || !k_cal || !v_cal || !sums) return fail(OSCAR_EINVAL, "calib_accumulate: NULL argument");
   if (n_tokens < 1 || n_tokens > 65536) return fail(OSCAR_EINVAL, "n_tokens %lld outside [1, 65536]", (long long)n_tokens);
   if (n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || n_q_heads > 256)
     return fail(OSCAR_EUNSUPPORTED, "head counts %d/%d unsupported", n_q_heads, n_kv_heads);
+  const AccumLayout lay = accum_layout(n_tokens, n_q_heads);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(OSCAR_EWORKSPACE, "calib_accumulate: workspace of %zu bytes needed, %zu given", lay.total,
+                workspace ? workspace_bytes : 0);
   if (int rc = check_device()) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int D = oscar::D;
   const int64_t nq = n_tokens * n_q_heads;
-  double *o = nullptr, *part = nullptr;
-  hipError_t e = hipMalloc(&o, size_t(nq) * D * sizeof(double));
-  if (e == hipSuccess) e = hipMalloc(&part, oscar::calib_outer_part_bytes());
-  if (e == hipSuccess) e = oscar::launch_calib_outer(q_cal, nullptr, nq, sums, part, s, true);
+  char *w = static_cast<char *>(workspace);
+  double *o = reinterpret_cast<double *>(w + lay.o), *part = reinterpret_cast<double *>(w + lay.part);
+  hipError_t e = oscar::launch_calib_outer(q_cal, nullptr, nq, sums, part, s, true);
   if (e == hipSuccess) e = oscar::launch_calib_attention(q_cal, k_cal, v_cal, n_tokens, n_q_heads, n_kv_heads, o, s);
   if (e == hipSuccess) e = oscar::launch_calib_outer(nullptr, o, nq, sums + D * D, part, s, true);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
-  if (o) (void)hipFree(o);
-  if (part) (void)hipFree(part);
   if (e != hipSuccess) return hip_fail(e, "calib_accumulate");
   return OSCAR_OK;
 }
 
-int oscar_calib_rotations(const double *sums, double count, double *R_K, double *R_V, oscar_stream_t stream) {
+int oscar_calib_rotations(const double *sums, double count, double *R_K, double *R_V, void *workspace,
+                          size_t workspace_bytes, oscar_stream_t stream) {
   if (!sums || !R_K || !R_V) return fail(OSCAR_EINVAL, "calib_rotations: NULL argument");
   if (!(count > 0.0) || !std::isfinite(count)) return fail(OSCAR_EINVAL, "count must be positive and finite");
+  const RotationsLayout lay = rotations_layout();
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(OSCAR_EWORKSPACE, "calib_rotations: workspace of %zu bytes needed, %zu given", lay.total,
+                workspace ? workspace_bytes : 0);
   if (int rc = check_device()) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int D = oscar::D;
@@ -435,43 +536,45 @@ int oscar_calib_rotations(const double *sums, double count, double *R_K, double 
     if (!std::isfinite(x / count)) return fail(OSCAR_EINVAL, "calib_rotations: non-finite moments");
   // the caller's sums stay intact: the iteration runs on a copy (the 1/count
   // scale changes no eigenvector)
-  double *mat = nullptr, *work = nullptr;
+  char *w = static_cast<char *>(workspace);
+  double *mat = reinterpret_cast<double *>(w + lay.mat), *work = reinterpret_cast<double *>(w + lay.work);
   std::vector<double> U, Rk, Rv;
-  e = hipMalloc(&mat, 2 * D * D * sizeof(double));
-  if (e == hipSuccess) e = hipMalloc(&work, D * D * sizeof(double) + 256);
-  if (e == hipSuccess) e = hipMemcpyAsync(mat, sums, 2 * D * D * sizeof(double), hipMemcpyDeviceToDevice, s);
-  if (e == hipSuccess) e = device_eigenbasis(mat, work, s, U);
+  bool conv_k = true, conv_v = true;
+  e = hipMemcpyAsync(mat, sums, 2 * D * D * sizeof(double), hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = device_eigenbasis(mat, work, s, U, &conv_k);
   if (e == hipSuccess) oscar::compose_rotation(U, Rk);
-  if (e == hipSuccess) e = device_eigenbasis(mat + D * D, work, s, U);
+  if (e == hipSuccess) e = device_eigenbasis(mat + D * D, work, s, U, &conv_v);
   if (e == hipSuccess) oscar::compose_rotation(U, Rv);
-  if (mat) (void)hipFree(mat);
-  if (work) (void)hipFree(work);
   if (e != hipSuccess) return hip_fail(e, "calib_rotations");
+  if (!conv_k || !conv_v)
+    return fail(OSCAR_EINVAL, "calib_rotations: the eigen-iteration of %s did not converge in %d sweeps",
+                conv_k ? "C_S" : "C_Q", kJacobiSweeps);
   std::memcpy(R_K, Rk.data(), D * D * sizeof(double));
   std::memcpy(R_V, Rv.data(), D * D * sizeof(double));
   return OSCAR_OK;
 }
 
 int oscar_clip_threshold(const uint16_t *x_cal, int64_t n_vec, const double *R, double clip_quantile,
-                         float *clip, oscar_stream_t stream) {
+                         float *clip, void *workspace, size_t workspace_bytes, oscar_stream_t stream) {
   if (!x_cal || !R || !clip) return fail(OSCAR_EINVAL, "clip_threshold: NULL argument");
-  if (n_vec < 1 || n_vec > (int64_t(1) << 20)) return fail(OSCAR_EINVAL, "n_vec %lld outside [1, 2^20]", (long long)n_vec);
+  if (n_vec < 1 || n_vec > (int64_t(1) << 31) - 1)
+    return fail(OSCAR_EINVAL, "n_vec %lld outside [1, 2^31 - 1]", (long long)n_vec);
   if (!(clip_quantile > 0.0 && clip_quantile <= 1.0)) return fail(OSCAR_EINVAL, "clip_quantile must be in (0, 1]");
+  const ClipLayout lay = clip_layout(n_vec);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(OSCAR_EWORKSPACE, "clip_threshold: workspace of %zu bytes needed, %zu given", lay.total,
+                workspace ? workspace_bytes : 0);
   if (int rc = check_device()) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int D = oscar::D;
-  double *Rd = nullptr, *y = nullptr;
-  std::vector<double> absv(size_t(n_vec) * D);
-  hipError_t e = hipMalloc(&Rd, D * D * sizeof(double));
-  if (e == hipSuccess) e = hipMalloc(&y, absv.size() * sizeof(double));
-  if (e == hipSuccess) e = hipMemcpyAsync(Rd, R, D * D * sizeof(double), hipMemcpyHostToDevice, s);
+  char *w = static_cast<char *>(workspace);
+  double *Rd = reinterpret_cast<double *>(w + lay.rd), *y = reinterpret_cast<double *>(w + lay.y);
+  double q = 0.0;
+  hipError_t e = hipMemcpyAsync(Rd, R, D * D * sizeof(double), hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = oscar::launch_calib_rotate_abs(x_cal, n_vec, Rd, y, s);
-  if (e == hipSuccess) e = hipMemcpyAsync(absv.data(), y, absv.size() * sizeof(double), hipMemcpyDeviceToHost, s);
-  if (e == hipSuccess) e = hipStreamSynchronize(s);
-  if (Rd) (void)hipFree(Rd);
-  if (y) (void)hipFree(y);
+  if (e == hipSuccess) e = device_quantile(y, n_vec * D, clip_quantile, w + lay.sel, s, &q);
   if (e != hipSuccess) return hip_fail(e, "clip_threshold");
-  *clip = float(oscar::quantile_linear(absv, clip_quantile));
+  *clip = float(q);
   return OSCAR_OK;
 }
 

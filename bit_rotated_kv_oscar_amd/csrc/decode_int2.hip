@@ -92,6 +92,16 @@ struct Rows {
   __device__ static constexpr int head_slot(int h) { return NG == 1 ? (h % HC) % 2 : 0; }
 };
 
+// Compute units of the current device (256 on MI355X; 256 when it cannot
+// be queried, e.g. while sizing a workspace on a host without a GPU).
+static int64_t device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      n > 0)
+    return n;
+  return 256;
+}
+
 SplitPlan plan_int2_splits(int batch, int n_kv_heads, int max_seq_len) {
   const int pages = n_hist_pages(max_seq_len);
   SplitPlan p;
@@ -101,7 +111,7 @@ SplitPlan plan_int2_splits(int batch, int n_kv_heads, int max_seq_len) {
     p.fused = true;
     return p;
   }
-  // One round of attend workgroups, one per CU on 256 CUs (measured faster
+  // One round of attend workgroups, one per CU (measured faster
   // at batch 1 than two per CU: each workgroup's fixed work, the q fragment
   // and the epilogue, is paid half as often and the merge reads half the
   // partials).  When every unit (request, KV head) fits in that round with
@@ -114,7 +124,7 @@ SplitPlan plan_int2_splits(int batch, int n_kv_heads, int max_seq_len) {
   // rounds, the election and the merge hold workgroup slots that other units
   // need, and a separate merge kernel is faster (~6 % at batch 64).
   const int64_t units = int64_t(batch) * n_kv_heads;
-  const int64_t slots = 256;
+  const int64_t slots = device_cus();
   int64_t pps;
   if (slots - units >= units) {
     const int64_t per_unit = (slots - units) / units;

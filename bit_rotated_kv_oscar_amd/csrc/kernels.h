@@ -92,11 +92,19 @@ hipError_t launch_calib_attention(const uint16_t *q, const uint16_t *k, const ui
                                   double *o, hipStream_t s);
 // Jacobi eigen-decomposition of the symmetric 128 x 128 matrix a (device,
 // overwritten: eigenvalues on its diagonal); vt: device [128][128] out, the
-// eigenvectors as rows, unsorted; sweeps: device int out
+// eigenvectors as rows, unsorted; sweeps: device int out, the sweeps done
+// (JACOBI_MAX_SWEEPS: stopped before reaching the tolerance)
+constexpr int JACOBI_MAX_SWEEPS = 60;
 hipError_t launch_jacobi(double *a, double *vt, int *sweeps, hipStream_t s);
 // y[n][128] = |x[n] R| (fp64), x bf16 [n][128]
 hipError_t launch_calib_rotate_abs(const uint16_t *x, int64_t n_vec, const double *R,
                                    double *y, hipStream_t s);
+// The k-th and (k+1)-th smallest (0-based; the (k+1)-th is the k-th when k
+// is the last) of n non-negative doubles y (device), by radix selection;
+// scratch: select_scratch_bytes() of device memory.  Synchronises s.
+size_t select_scratch_bytes();
+hipError_t select_order_stats(const double *y, int64_t n, int64_t k, void *scratch, hipStream_t s, double *vk,
+                              double *vk1);
 
 // Read probe: sums (mod 2^32) the words of n_blocks blocks of block_bytes
 // bytes into *sink; block i is slot ids[i] of buf (ids null: slot i), slots

@@ -5,6 +5,8 @@
 // query second moment C_Q and the attention-output second moment C_S, and the
 // magnitudes |x R| from which the per-layer clip is taken.  Everything here is
 // fp64 so the eigenbases match a double-precision reference to ~1e-14.
+#include <cstring>
+
 #include "kernels.h"
 
 namespace oscar {
@@ -236,6 +238,96 @@ hipError_t launch_calib_rotate_abs(const uint16_t *x, int64_t n_vec, const doubl
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- order statistics
+// Exact order statistics of non-negative fp64 values (the |x R| of a clip
+// quantile) by radix selection on the device, in memory independent of the
+// number of values: non-negative IEEE doubles order like their 64-bit
+// patterns, so the k-th smallest is found 8 bits at a time, each pass
+// counting, among the values whose leading bits equal the prefix found so
+// far, how many carry each value of the next 8 bits (a 256-bucket histogram:
+// per workgroup in LDS, then added to the global one).
+
+__global__ void __launch_bounds__(256) fill_u64_kernel(unsigned long long *p, int n, unsigned long long v) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = v;
+}
+
+__global__ void __launch_bounds__(256) radix_hist_kernel(const unsigned long long *__restrict__ y, int64_t n,
+                                                         unsigned long long prefix, int shift,
+                                                         unsigned long long *__restrict__ hist) {
+  __shared__ unsigned int h[256];
+  h[threadIdx.x] = 0;
+  __syncthreads();
+  const int hi_shift = shift + 8;  // bits above the digit must equal the prefix
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
+    const unsigned long long v = y[i];
+    const bool match = hi_shift >= 64 || (v >> hi_shift) == prefix;
+    if (match) atomicAdd(&h[(v >> shift) & 255u], 1u);
+  }
+  __syncthreads();
+  if (h[threadIdx.x]) atomicAdd(&hist[threadIdx.x], (unsigned long long)h[threadIdx.x]);
+}
+
+// *out = min over the values above v (bit patterns), or all ones if none
+__global__ void __launch_bounds__(256) next_above_kernel(const unsigned long long *__restrict__ y, int64_t n,
+                                                         unsigned long long v, unsigned long long *out) {
+  unsigned long long m = ~0ull;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
+    const unsigned long long x = y[i];
+    if (x > v && x < m) m = x;
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    const unsigned long long o = __shfl_xor(m, off);
+    m = o < m ? o : m;
+  }
+  if ((threadIdx.x & 63) == 0) atomicMin(out, m);
+}
+
+size_t select_scratch_bytes() { return 257 * sizeof(unsigned long long); }
+
+static unsigned select_grid(int64_t n) {
+  const int64_t g = (n + 255) / 256;
+  return unsigned(g < 4096 ? (g > 0 ? g : 1) : 4096);
+}
+
+hipError_t select_order_stats(const double *y, int64_t n, int64_t k, void *scratch, hipStream_t s, double *vk,
+                              double *vk1) {
+  const unsigned long long *yy = reinterpret_cast<const unsigned long long *>(y);
+  unsigned long long *hist = static_cast<unsigned long long *>(scratch);
+  unsigned long long prefix = 0, hh[256];
+  int64_t rank = k, in_bucket = 0;
+  hipError_t e = hipSuccess;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    hipLaunchKernelGGL(fill_u64_kernel, dim3(1), dim3(256), 0, s, hist, 256, 0ull);
+    hipLaunchKernelGGL(radix_hist_kernel, dim3(select_grid(n)), dim3(256), 0, s, yy, n, prefix, shift, hist);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = hipMemcpyAsync(hh, hist, sizeof hh, hipMemcpyDeviceToHost, s)) != hipSuccess) return e;
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
+    int d = 0;
+    while (d < 255 && rank >= int64_t(hh[d])) rank -= int64_t(hh[d++]);
+    in_bucket = int64_t(hh[d]);
+    prefix = (prefix << 8) | unsigned(d);
+  }
+  // prefix: the bit pattern of the k-th smallest; `in_bucket` values equal it
+  double v;
+  std::memcpy(&v, &prefix, sizeof v);
+  *vk = v;
+  if (rank + 1 < in_bucket) {
+    *vk1 = v;
+    return hipSuccess;
+  }
+  unsigned long long *mn = hist + 256;
+  hipLaunchKernelGGL(fill_u64_kernel, dim3(1), dim3(256), 0, s, mn, 1, ~0ull);
+  hipLaunchKernelGGL(next_above_kernel, dim3(select_grid(n)), dim3(256), 0, s, yy, n, prefix, mn);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  unsigned long long nx = 0;
+  if ((e = hipMemcpyAsync(&nx, mn, sizeof nx, hipMemcpyDeviceToHost, s)) != hipSuccess) return e;
+  if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
+  if (nx == ~0ull) nx = prefix;  // k is the largest
+  std::memcpy(&v, &nx, sizeof v);
+  *vk1 = v;
+  return hipSuccess;
+}
+
 }  // namespace oscar
 
 namespace oscar {
@@ -279,7 +371,7 @@ __global__ void __launch_bounds__(JACOBI_THREADS) jacobi_kernel(double *__restri
   };
   fro = sqrt(block_sum(fro));
   int sweep = 0;
-  for (; sweep < 60; ++sweep) {
+  for (; sweep < JACOBI_MAX_SWEEPS; ++sweep) {
     double off = 0.0;
     for (int e = tid; e < D * D; e += JACOBI_THREADS)
       if (e % D > e / D) off += A[(e / D) * JS + e % D] * A[(e / D) * JS + e % D];

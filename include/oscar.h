@@ -11,11 +11,12 @@
  *
  * Every pointer argument is a plain pointer; "device" means memory the HIP
  * runtime can address on the current device, "host" means CPU memory.
- * The caller owns every buffer.  The library allocates device memory only in
- * the calibration calls (oscar_calibrate_rotation, oscar_calib_accumulate,
- * oscar_calib_rotations, oscar_clip_threshold; freed before they return)
- * and keeps no state besides a thread-local error string.  All calls except
- * those calibration calls are asynchronous on the given stream.
+ * The caller owns every buffer; the library allocates no memory on the device
+ * (work areas are caller workspaces, sized by the *_workspace_bytes calls,
+ * or the fixed scratch array of oscar_decode_attn_noalloc).  Its state is a
+ * thread-local error string, a per-device cache of the device check and the
+ * scratch array's address.  All calls except the calibration calls are
+ * asynchronous on the given stream.
  *
  * Return value: OSCAR_OK (0) or a negative code; oscar_last_error() then
  * holds a message.  Arguments are validated on the host before any launch;
@@ -152,6 +153,21 @@ OSCAR_API size_t oscar_rotation_bytes(void);
  * forms: device buffer of oscar_rotation_bytes(). */
 OSCAR_API int oscar_prepare_rotation(const double *R, void *forms, oscar_stream_t stream);
 
+/* Calibration workspaces.  Every calibration call works in a device
+ * workspace the caller provides (any alignment >= 256 B, contents on entry
+ * irrelevant); these give its size in bytes (0 for invalid sizes):
+ *   oscar_calibrate_workspace_bytes: fp64 moments, the causal attention
+ *     outputs (n_tokens * Hq * 1 KiB), |k R| / |v R| (n_tokens * Hkv *
+ *     1 KiB), the moment partials (32 MiB) and the quantile's selection;
+ *   oscar_calib_accumulate_workspace_bytes: attention outputs and partials;
+ *   oscar_calib_rotations_workspace_bytes: two 128 x 128 fp64 matrices;
+ *   oscar_clip_threshold_workspace_bytes: R and |x R| (n_vec * 1 KiB). */
+OSCAR_API size_t oscar_calibrate_workspace_bytes(int64_t n_tokens, int32_t n_q_heads, int32_t n_kv_heads);
+OSCAR_API size_t oscar_calib_accumulate_workspace_bytes(int64_t n_tokens, int32_t n_q_heads,
+                                                        int32_t n_kv_heads);
+OSCAR_API size_t oscar_calib_rotations_workspace_bytes(void);
+OSCAR_API size_t oscar_clip_threshold_workspace_bytes(int64_t n_vec);
+
 /* Calibration over many sequences ([nl]/[fr] §2.2.A; the moments are sums,
  * so they accumulate over any number of calibration sequences):
  * oscar_calib_accumulate adds one sequence's second-moment sums to sums,
@@ -165,16 +181,18 @@ OSCAR_API int oscar_prepare_rotation(const double *R, void *forms, oscar_stream_
  * oscar_clip_threshold over the calibration K and V vectors.
  * q_cal: device bf16 [n_tokens][Hq][128]; k_cal, v_cal: device bf16
  * [n_tokens][Hkv][128]; sums: device fp64 [2][128][128], zeroed by the
- * caller before the first sequence; R_K, R_V: host fp64 [128][128] out.
- * Both calls allocate temporary device memory and synchronise the stream.
+ * caller before the first sequence; R_K, R_V: host fp64 [128][128] out;
+ * workspace: device, the sizes above.  Both calls synchronise the stream.
  * Errors: OSCAR_EINVAL (NULL pointers, n_tokens outside [1, 65536], count
- * not positive, non-finite moments), OSCAR_EUNSUPPORTED (head counts),
+ * not positive, non-finite moments, an eigen-iteration that did not reach
+ * its tolerance), OSCAR_EUNSUPPORTED (head counts), OSCAR_EWORKSPACE,
  * OSCAR_EHIP. */
 OSCAR_API int oscar_calib_accumulate(const uint16_t *q_cal, const uint16_t *k_cal,
                            const uint16_t *v_cal, int64_t n_tokens, int32_t n_q_heads,
-                           int32_t n_kv_heads, double *sums, oscar_stream_t stream);
+                           int32_t n_kv_heads, double *sums, void *workspace,
+                           size_t workspace_bytes, oscar_stream_t stream);
 OSCAR_API int oscar_calib_rotations(const double *sums, double count, double *R_K, double *R_V,
-                          oscar_stream_t stream);
+                          void *workspace, size_t workspace_bytes, oscar_stream_t stream);
 
 /* Clip threshold of one fixed rotation ([nl]/[fr] §2.2.A "clipping
  * thresholds"): the clip_quantile quantile (linear interpolation between
@@ -182,15 +200,17 @@ OSCAR_API int oscar_calib_rotations(const double *sums, double count, double *R_
  * same rule oscar_calibrate_rotation applies to its own R_K and R_V.  It
  * serves rotations chosen by the caller, such as the Hadamard-only
  * (QuaRot-style) R = H P_br and the identity of plain INT2 that the pages
- * compare OSCAR with ([abs]; [nl]/[fr] §2.1).
+ * compare OSCAR with ([abs]; [nl]/[fr] §2.1).  The order statistics are
+ * selected on the device (radix selection over the fp64 bit patterns): host
+ * memory does not grow with n_vec.
  * x_cal: device bf16 [n_vec][128]; R: host fp64 [128][128] (row-vector
- * convention, x R); clip: host float out.  Allocates and frees temporary
- * device memory and synchronises the stream.  Errors: OSCAR_EINVAL for
- * NULL pointers, n_vec outside [1, 2^20] (2^20 vectors take 1 GiB of
- * temporary device and host memory) or clip_quantile outside (0, 1];
- * OSCAR_EHIP for runtime failures. */
+ * convention, x R); clip: host float out; workspace: device,
+ * oscar_clip_threshold_workspace_bytes(n_vec).  Synchronises the stream.
+ * Errors: OSCAR_EINVAL for NULL pointers, n_vec outside [1, 2^31 - 1] or
+ * clip_quantile outside (0, 1]; OSCAR_EWORKSPACE; OSCAR_EHIP. */
 OSCAR_API int oscar_clip_threshold(const uint16_t *x_cal, int64_t n_vec, const double *R,
-                         double clip_quantile, float *clip, oscar_stream_t stream);
+                         double clip_quantile, float *clip, void *workspace,
+                         size_t workspace_bytes, oscar_stream_t stream);
 
 /* Offline calibration ([nl] §2.2.A, [fr] §2.2.A, [abs]):
  *   C_Q = mean over tokens and query heads of the outer product q q^T;
@@ -206,14 +226,16 @@ OSCAR_API int oscar_clip_threshold(const uint16_t *x_cal, int64_t n_vec, const d
  *         calibration token, KV head and channel.
  * q_cal: device bf16 [n_tokens][Hq][128]; k_cal, v_cal: device bf16
  * [n_tokens][Hkv][128].  Outputs R_K, R_V (host fp64 [128][128]) and
- * clip_K, clip_V (host).  Synchronises the stream; allocates and frees its
- * own device scratch.  n_tokens in [1, 65536], clip_quantile in (0, 1]. */
+ * clip_K, clip_V (host).  workspace: device,
+ * oscar_calibrate_workspace_bytes(n_tokens, Hq, Hkv).  Synchronises the
+ * stream.  n_tokens in [1, 65536], clip_quantile in (0, 1].  Errors as
+ * oscar_calib_accumulate. */
 OSCAR_API int oscar_calibrate_rotation(const uint16_t *q_cal, const uint16_t *k_cal,
                              const uint16_t *v_cal, int64_t n_tokens,
                              int32_t n_q_heads, int32_t n_kv_heads,
                              double clip_quantile, double *R_K, double *R_V,
-                             float *clip_K, float *clip_V,
-                             oscar_stream_t stream);
+                             float *clip_K, float *clip_V, void *workspace,
+                             size_t workspace_bytes, oscar_stream_t stream);
 
 /* Fused KV write ([abs] "fused ... write ... kernels", [nl]/[fr] §2.2.B):
  * appends new tokens to every request of the batch.  Request b gets

@@ -167,25 +167,40 @@ def test_calibrate_and_prepare_validation_codes():
     E = _lib
     R = (ctypes.c_double * (128 * 128))()
     f = ctypes.c_float()
-    assert lib.oscar_calibrate_rotation(0, 0x1, 0x1, 16, 8, 2, 0.999, R, R, ctypes.byref(f), ctypes.byref(f),
-                                        None) == E.OSCAR_EINVAL
-    assert lib.oscar_calibrate_rotation(0x1, 0x1, 0x1, 0, 8, 2, 0.999, R, R, ctypes.byref(f), ctypes.byref(f),
-                                        None) == E.OSCAR_EINVAL
-    assert lib.oscar_calibrate_rotation(0x1, 0x1, 0x1, 16, 8, 3, 0.999, R, R, ctypes.byref(f), ctypes.byref(f),
-                                        None) == E.OSCAR_EUNSUPPORTED
-    assert lib.oscar_calibrate_rotation(0x1, 0x1, 0x1, 16, 8, 2, 1.5, R, R, ctypes.byref(f), ctypes.byref(f),
-                                        None) == E.OSCAR_EINVAL
+    W, WB = 0xE000, 1 << 40   # a workspace pointer and size that pass the size checks
+
+    def cal(q=0x1, n=16, hq=8, hkv=2, p=0.999, ws=W, wb=WB):
+        return lib.oscar_calibrate_rotation(q, 0x1, 0x1, n, hq, hkv, p, R, R, ctypes.byref(f), ctypes.byref(f),
+                                            ws, wb, None)
+    assert cal(q=0) == E.OSCAR_EINVAL
+    assert cal(n=0) == E.OSCAR_EINVAL
+    assert cal(hkv=3) == E.OSCAR_EUNSUPPORTED
+    assert cal(p=1.5) == E.OSCAR_EINVAL
+    assert cal(ws=0) == E.OSCAR_EWORKSPACE
+    need = lib.oscar_calibrate_workspace_bytes(16, 8, 2)
+    assert cal(wb=need - 1) == E.OSCAR_EWORKSPACE and "workspace" in _err()
     assert lib.oscar_prepare_rotation(0, 0x1, None) == E.OSCAR_EINVAL
-    assert lib.oscar_calib_accumulate(0, 0x1, 0x1, 16, 8, 2, 0x1, None) == E.OSCAR_EINVAL
-    assert lib.oscar_calib_accumulate(0x1, 0x1, 0x1, 0, 8, 2, 0x1, None) == E.OSCAR_EINVAL
-    assert lib.oscar_calib_accumulate(0x1, 0x1, 0x1, 16, 8, 3, 0x1, None) == E.OSCAR_EUNSUPPORTED
-    assert lib.oscar_calib_rotations(0x1, 0.0, R, R, None) == E.OSCAR_EINVAL
-    assert lib.oscar_calib_rotations(0x1, float("nan"), R, R, None) == E.OSCAR_EINVAL
-    assert lib.oscar_calib_rotations(0, 10.0, R, R, None) == E.OSCAR_EINVAL
-    assert lib.oscar_clip_threshold(0, 16, R, 0.999, ctypes.byref(f), None) == E.OSCAR_EINVAL
-    assert lib.oscar_clip_threshold(0x1, 0, R, 0.999, ctypes.byref(f), None) == E.OSCAR_EINVAL
-    assert lib.oscar_clip_threshold(0x1, 16, R, 0.0, ctypes.byref(f), None) == E.OSCAR_EINVAL
-    assert lib.oscar_clip_threshold(0x1, 16, None, 0.999, ctypes.byref(f), None) == E.OSCAR_EINVAL
+    assert lib.oscar_calib_accumulate(0, 0x1, 0x1, 16, 8, 2, 0x1, W, WB, None) == E.OSCAR_EINVAL
+    assert lib.oscar_calib_accumulate(0x1, 0x1, 0x1, 0, 8, 2, 0x1, W, WB, None) == E.OSCAR_EINVAL
+    assert lib.oscar_calib_accumulate(0x1, 0x1, 0x1, 16, 8, 3, 0x1, W, WB, None) == E.OSCAR_EUNSUPPORTED
+    assert lib.oscar_calib_accumulate(0x1, 0x1, 0x1, 16, 8, 2, 0x1, W, 1024, None) == E.OSCAR_EWORKSPACE
+    assert lib.oscar_calib_rotations(0x1, 0.0, R, R, W, WB, None) == E.OSCAR_EINVAL
+    assert lib.oscar_calib_rotations(0x1, float("nan"), R, R, W, WB, None) == E.OSCAR_EINVAL
+    assert lib.oscar_calib_rotations(0, 10.0, R, R, W, WB, None) == E.OSCAR_EINVAL
+    assert lib.oscar_calib_rotations(0x1, 10.0, R, R, 0, WB, None) == E.OSCAR_EWORKSPACE
+    assert lib.oscar_clip_threshold(0, 16, R, 0.999, ctypes.byref(f), W, WB, None) == E.OSCAR_EINVAL
+    assert lib.oscar_clip_threshold(0x1, 0, R, 0.999, ctypes.byref(f), W, WB, None) == E.OSCAR_EINVAL
+    assert lib.oscar_clip_threshold(0x1, 16, R, 0.0, ctypes.byref(f), W, WB, None) == E.OSCAR_EINVAL
+    assert lib.oscar_clip_threshold(0x1, 16, None, 0.999, ctypes.byref(f), W, WB, None) == E.OSCAR_EINVAL
+    assert lib.oscar_clip_threshold(0x1, 16, R, 0.999, ctypes.byref(f), W, 100, None) == E.OSCAR_EWORKSPACE
+    # no cap on the number of vectors beyond the int32 grid limit
+    assert lib.oscar_clip_threshold(0x1, 1 << 31, R, 0.999, ctypes.byref(f), W, WB, None) == E.OSCAR_EINVAL
+    # workspace sizes: monotone in the sizes they depend on, 0 for invalid ones
+    assert lib.oscar_clip_threshold_workspace_bytes(1 << 22) > lib.oscar_clip_threshold_workspace_bytes(1 << 20) > 0
+    assert lib.oscar_clip_threshold_workspace_bytes(0) == 0
+    assert lib.oscar_calibrate_workspace_bytes(2048, 32, 8) > lib.oscar_calibrate_workspace_bytes(1024, 32, 8) > 0
+    assert lib.oscar_calib_accumulate_workspace_bytes(0, 8, 2) == 0
+    assert lib.oscar_calib_rotations_workspace_bytes() >= 3 * 128 * 128 * 8
 
 
 def test_errors_raise_in_binding():

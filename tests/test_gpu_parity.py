@@ -15,7 +15,7 @@ import torch
 import synth
 from oracle import oscar_ref as o
 from tests.parity_tools import (Scenario, assert_decode_close, assert_history_ok, bf16_pool_bits,
-                                compare_history, decode_error, to_dev_bf16)
+                                compare_history, decode_error, random_rotation, to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -504,3 +504,37 @@ def test_bf16_decode_more_than_64_pages_per_wave(oscar):
     pick = [0, 21, 39]
     expect = o.bf16_paged_decode(q[pick], pages, pt[:len(pick)], [L] * len(pick), SCALE)
     assert_decode_close(out.cpu().numpy()[pick], expect, "bf16 long split")
+
+
+def test_clip_threshold_exact_order_statistics_past_2_20_vectors(oscar):
+    # R = I and integer values 0..250 (exact in bf16): the 0.999 and 0.5
+    # quantiles (type 7) follow from the value counts in closed form; 2^20 + 3
+    # vectors (134M values, past the former host-sort cap) go through the
+    # device radix selection, and ties (each value ~535K times) exercise the
+    # equal-neighbour case
+    n = (1 << 20) + 3
+    idx = torch.arange(n * 128, device="cuda", dtype=torch.int64)
+    vals = (idx % 251).to(torch.float32)
+    x = vals.to(torch.bfloat16).view(n, 128)
+    counts = np.bincount((np.arange(n * 128, dtype=np.int64) % 251), minlength=251)
+    cum = np.cumsum(counts)
+
+    def order_stat(r):  # 0-based rank -> value
+        return float(np.searchsorted(cum, r, side="right"))
+
+    for p in (0.999, 0.5, 1.0, 1e-9):
+        h = (n * 128 - 1) * p
+        lo = int(np.floor(h))
+        a = order_stat(lo)
+        b = order_stat(min(lo + 1, n * 128 - 1))
+        t = h - lo
+        want = b - (b - a) * (1 - t) if t >= 0.5 else a + (b - a) * t
+        got = oscar.clip_threshold(x, torch.eye(128, dtype=torch.float64), p)
+        assert got == np.float32(want), (p, got, want)
+    # a general rotation on a smaller set: the oracle's numpy quantile
+    R = random_rotation(77)
+    xs = to_dev_bf16(synth.bf16_bits(np.random.default_rng(3).standard_normal((3000, 128)).astype(np.float32) * 3))
+    xf = synth.bf16_to_f64(xs.view(torch.int16).cpu().numpy().view(np.uint16))
+    want = o.clip_threshold(xf, R, 0.999)
+    got = oscar.clip_threshold(xs, torch.from_numpy(R), 0.999)
+    assert abs(got - want) <= 1e-6 * want
