@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -84,16 +85,28 @@ KernelEvents &profile_events() { return g_events; }
 
 namespace {
 
-constexpr int kJacobiSweeps = oscar::JACOBI_MAX_SWEEPS;
+// Sweep limit of the eigen-iteration: JACOBI_MAX_SWEEPS (far more than the
+// 6-10 sweeps a 128 x 128 moment matrix takes), or the value of the
+// environment variable OSCAR_JACOBI_SWEEPS (1..1000), a diagnostic hook that
+// lets a test make the iteration stop early and see the error it reports.
+int jacobi_sweep_limit() {
+  const char *env = std::getenv("OSCAR_JACOBI_SWEEPS");
+  if (env) {
+    const int v = std::atoi(env);
+    if (v >= 1 && v <= 1000) return v;
+  }
+  return oscar::JACOBI_MAX_SWEEPS;
+}
 
 // Eigenbasis (sorted, signed) of the symmetric 128 x 128 matrix at mat (device,
 // destroyed) by the device Jacobi iteration; work: device scratch of
 // 128 * 128 doubles + one int.  *converged: whether the iteration met its
-// tolerance within kJacobiSweeps sweeps.
+// tolerance within the sweep limit.
 hipError_t device_eigenbasis(double *mat, double *work, hipStream_t s, std::vector<double> &U, bool *converged) {
   const int D = oscar::D;
   int *sweeps = reinterpret_cast<int *>(work + D * D);
-  hipError_t e = oscar::launch_jacobi(mat, work, sweeps, s);
+  const int limit = jacobi_sweep_limit();
+  hipError_t e = oscar::launch_jacobi(mat, work, sweeps, limit, s);
   std::vector<double> VT(D * D), V(D * D), A(D * D), w(D);
   int n_sweeps = 0;
   if (e == hipSuccess) e = hipMemcpyAsync(VT.data(), work, VT.size() * sizeof(double), hipMemcpyDeviceToHost, s);
@@ -101,7 +114,7 @@ hipError_t device_eigenbasis(double *mat, double *work, hipStream_t s, std::vect
   if (e == hipSuccess) e = hipMemcpyAsync(&n_sweeps, sweeps, sizeof(int), hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return e;
-  *converged = n_sweeps < kJacobiSweeps;
+  *converged = n_sweeps < limit;
   for (int i = 0; i < D; ++i) {
     w[i] = A[size_t(i) * D + i];
     for (int j = 0; j < D; ++j) V[size_t(i) * D + j] = VT[size_t(j) * D + i];
@@ -471,10 +484,10 @@ int oscar_calibrate_rotation(const uint16_t *q_cal, const uint16_t *k_cal, const
   std::vector<double> U, Rk, Rv;
   bool conv = true;
   CHECK_HIP(device_eigenbasis(cov, part, s, U, &conv), "eigenbasis C_Q");
-  if (!conv) return fail(OSCAR_EINVAL, "calibrate: the eigen-iteration of C_Q did not converge in %d sweeps", kJacobiSweeps);
+  if (!conv) return fail(OSCAR_EINVAL, "calibrate: the eigen-iteration of C_Q did not converge in %d sweeps", jacobi_sweep_limit());
   oscar::compose_rotation(U, Rk);
   CHECK_HIP(device_eigenbasis(cov + D * D, part, s, U, &conv), "eigenbasis C_S");
-  if (!conv) return fail(OSCAR_EINVAL, "calibrate: the eigen-iteration of C_S did not converge in %d sweeps", kJacobiSweeps);
+  if (!conv) return fail(OSCAR_EINVAL, "calibrate: the eigen-iteration of C_S did not converge in %d sweeps", jacobi_sweep_limit());
   oscar::compose_rotation(U, Rv);
   double clips[2];
   const uint16_t *xs[2] = {k_cal, v_cal};
@@ -548,7 +561,7 @@ int oscar_calib_rotations(const double *sums, double count, double *R_K, double 
   if (e != hipSuccess) return hip_fail(e, "calib_rotations");
   if (!conv_k || !conv_v)
     return fail(OSCAR_EINVAL, "calib_rotations: the eigen-iteration of %s did not converge in %d sweeps",
-                conv_k ? "C_S" : "C_Q", kJacobiSweeps);
+                conv_k ? "C_S" : "C_Q", jacobi_sweep_limit());
   std::memcpy(R_K, Rk.data(), D * D * sizeof(double));
   std::memcpy(R_V, Rv.data(), D * D * sizeof(double));
   return OSCAR_OK;

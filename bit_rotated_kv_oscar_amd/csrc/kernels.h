@@ -93,9 +93,9 @@ hipError_t launch_calib_attention(const uint16_t *q, const uint16_t *k, const ui
 // Jacobi eigen-decomposition of the symmetric 128 x 128 matrix a (device,
 // overwritten: eigenvalues on its diagonal); vt: device [128][128] out, the
 // eigenvectors as rows, unsorted; sweeps: device int out, the sweeps done
-// (JACOBI_MAX_SWEEPS: stopped before reaching the tolerance)
+// (max_sweeps: stopped before reaching the tolerance)
 constexpr int JACOBI_MAX_SWEEPS = 60;
-hipError_t launch_jacobi(double *a, double *vt, int *sweeps, hipStream_t s);
+hipError_t launch_jacobi(double *a, double *vt, int *sweeps, int max_sweeps, hipStream_t s);
 // y[n][128] = |x[n] R| (fp64), x bf16 [n][128]
 hipError_t launch_calib_rotate_abs(const uint16_t *x, int64_t n_vec, const double *R,
                                    double *y, hipStream_t s);

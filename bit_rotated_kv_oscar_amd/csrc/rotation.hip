@@ -348,7 +348,7 @@ constexpr int JACOBI_THREADS = 1024;
 constexpr int JS = D + 1;  // LDS row stride of the matrix (doubles)
 
 __global__ void __launch_bounds__(JACOBI_THREADS) jacobi_kernel(double *__restrict__ a, double *__restrict__ vt,
-                                                               int *__restrict__ sweeps_out) {
+                                                               int *__restrict__ sweeps_out, int max_sweeps) {
   __shared__ double A[D * JS];  // rows padded to JS doubles (no bank conflicts down a column)
   __shared__ double cs[D / 2], sn[D / 2];
   __shared__ int pp[D / 2], qq[D / 2];
@@ -371,7 +371,7 @@ __global__ void __launch_bounds__(JACOBI_THREADS) jacobi_kernel(double *__restri
   };
   fro = sqrt(block_sum(fro));
   int sweep = 0;
-  for (; sweep < JACOBI_MAX_SWEEPS; ++sweep) {
+  for (; sweep < max_sweeps; ++sweep) {
     double off = 0.0;
     for (int e = tid; e < D * D; e += JACOBI_THREADS)
       if (e % D > e / D) off += A[(e / D) * JS + e % D] * A[(e / D) * JS + e % D];
@@ -431,8 +431,8 @@ __global__ void __launch_bounds__(JACOBI_THREADS) jacobi_kernel(double *__restri
   if (tid == 0) *sweeps_out = sweep;
 }
 
-hipError_t launch_jacobi(double *a, double *vt, int *sweeps, hipStream_t s) {
-  hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(JACOBI_THREADS), 0, s, a, vt, sweeps);
+hipError_t launch_jacobi(double *a, double *vt, int *sweeps, int max_sweeps, hipStream_t s) {
+  hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(JACOBI_THREADS), 0, s, a, vt, sweeps, max_sweeps);
   return hipGetLastError();
 }
 

@@ -538,3 +538,23 @@ def test_clip_threshold_exact_order_statistics_past_2_20_vectors(oscar):
     want = o.clip_threshold(xf, R, 0.999)
     got = oscar.clip_threshold(xs, torch.from_numpy(R), 0.999)
     assert abs(got - want) <= 1e-6 * want
+
+
+def test_calibration_reports_an_unconverged_eigen_iteration(oscar, monkeypatch):
+    # the sweep limit forced to 1 (diagnostic hook): the iteration stops
+    # before its tolerance and both calibration entry points say so
+    ld = synth.LayerData(41, 0, 8, 2)
+    qc, kc, vc = (to_dev_bf16(x) for x in ld.calibration(256))
+    monkeypatch.setenv("OSCAR_JACOBI_SWEEPS", "1")
+    with pytest.raises(oscar.OscarError) as ei:
+        oscar.calibrate_rotation(qc, kc, vc, 0.999)
+    assert ei.value.code == oscar._lib.OSCAR_EINVAL and "converge" in str(ei.value)
+    sums = torch.zeros((2, 128, 128), dtype=torch.float64, device="cuda")
+    count = oscar.calib_accumulate(qc, kc, vc, sums)
+    with pytest.raises(oscar.OscarError) as ei:
+        oscar.calib_rotations(sums, count)
+    assert "converge" in str(ei.value)
+    # back at the default limit the same inputs calibrate
+    monkeypatch.delenv("OSCAR_JACOBI_SWEEPS")
+    R_K, R_V, ck, cv = oscar.calibrate_rotation(qc, kc, vc, 0.999)
+    assert np.abs(R_K.numpy().T @ R_K.numpy() - np.eye(128)).max() < 1e-12
