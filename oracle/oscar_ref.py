@@ -27,7 +27,8 @@ notes of this repository):
   * clip first, then per-token groups of G consecutive rotated channels,
     asymmetric min-max INT2 with fp16 scale and zero, codes from the stored
     (fp16-rounded) scale and zero, round half to even, all codes 0 when the
-    fp16 scale is 0;
+    fp16 scale is 0; the INT4 variant is the same with 16 levels
+    (scale = (max - min)/15), the bit width being the only difference;
   * sink = first 16 tokens, recent = last 128 tokens (exact sliding window),
     both raw bf16 and unrotated; history in between;
   * decode: one query per request over all cached tokens, no mask, fp64;
@@ -247,14 +248,23 @@ def relative_l2(x: np.ndarray, ref: np.ndarray) -> float:
 
 # --------------------------------------------------------------------------
 # the INT2 quantiser  ([nl]/[fr] §1 four levels, §2.2.B rotate + clip + INT2)
+# and its INT4 variant (16 levels; the INT4 baseline the pages compare
+# against, [nl] §4 / [fr] §4)
 # --------------------------------------------------------------------------
 
-def quantize(x: np.ndarray, R: np.ndarray, clip: float, G: int) -> dict:
+def levels(bits: int) -> int:
+    """Highest code of a bits-wide quantiser: 3 (INT2) or 15 (INT4)."""
+    assert bits in (2, 4)
+    return (1 << bits) - 1
+
+
+def quantize(x: np.ndarray, R: np.ndarray, clip: float, G: int, bits: int = 2) -> dict:
     """Rotate, clip and quantise vectors.
 
     x: float64 [n][128] (bf16 values).  Returns codes uint8 [n][128], scale
     and zero float16 [n][128/G], the clipped rotated values xc [n][128] and
-    t = (xc - zero)/scale in code units (NaN where scale == 0).
+    t = (xc - zero)/scale in code units (NaN where scale == 0).  The scale
+    spreads a group's range over levels(bits) steps.
     """
     n = x.shape[0]
     ng = D // G
@@ -263,14 +273,14 @@ def quantize(x: np.ndarray, R: np.ndarray, clip: float, G: int) -> dict:
     lo = g.min(axis=2)
     hi = g.max(axis=2)
     zero = f16_round(lo)
-    scale = f16_round((hi - lo) / 3.0)
-    codes, t = codes_from_meta(xc, scale, zero, G)
+    scale = f16_round((hi - lo) / float(levels(bits)))
+    codes, t = codes_from_meta(xc, scale, zero, G, bits)
     return {"codes": codes, "scale": scale, "zero": zero, "xc": xc, "t": t}
 
 
-def codes_from_meta(xc: np.ndarray, scale: np.ndarray, zero: np.ndarray, G: int):
+def codes_from_meta(xc: np.ndarray, scale: np.ndarray, zero: np.ndarray, G: int, bits: int = 2):
     """Codes of clipped rotated values for a given fp16 (scale, zero):
-    clamp(rint((xc - z)/s), 0, 3), 0 where s == 0."""
+    clamp(rint((xc - z)/s), 0, levels(bits)), 0 where s == 0."""
     n = xc.shape[0]
     ng = D // G
     s = scale.astype(np.float64)[:, :, None]
@@ -278,7 +288,7 @@ def codes_from_meta(xc: np.ndarray, scale: np.ndarray, zero: np.ndarray, G: int)
     g = xc.reshape(n, ng, G)
     with np.errstate(divide="ignore", invalid="ignore"):
         t = np.where(s > 0, (g - z) / np.where(s > 0, s, 1.0), np.nan)
-    c = np.where(s > 0, np.clip(np.rint(np.nan_to_num(t)), 0, 3), 0).astype(np.uint8)
+    c = np.where(s > 0, np.clip(np.rint(np.nan_to_num(t)), 0, levels(bits)), 0).astype(np.uint8)
     return c.reshape(n, D), t.reshape(n, D)
 
 
@@ -298,8 +308,39 @@ LO_BIT = (8, 6, 12, 10, 4, 2, 16, 14)
 HI_BIT = (24, 22, 28, 26, 20, 18, 0, 30)
 
 
-def hist_block_bytes(G: int) -> int:
-    return 1024 + 128 * (D // G)
+def code_area_bytes(bits: int = 2) -> int:
+    """Bytes of one code area: 16 tokens x 128 channels x bits."""
+    return PAGE * D * bits // 8
+
+
+def hist_block_bytes(G: int, bits: int = 2) -> int:
+    return 2 * code_area_bytes(bits) + 128 * (D // G)
+
+
+def _code_bit_tables_int4(kind: str):
+    """(byte index, shift) [16 rows][128 channels] of every 4-bit code of an
+    INT4 code area (1024 bytes, 256 dwords; dword w = 4 l + i of lane l,
+    a = l % 16, q = l / 16; code at bits 4 e .. 4 e + 3 of its dword):
+      K: a = token t; dword i = kb (0..3) holds channels 32 kb + 8 q + e,
+         e = 0..7, of token t;
+      V: a = channel offset m; dword i = d (0..3), half h = e / 4 (16 bits
+         each) holds channel 16 (2 d + h) + m, token 4 q + e % 4."""
+    byte_idx = np.full((PAGE, D), -1, dtype=np.int64)
+    shift = np.full((PAGE, D), -1, dtype=np.int64)
+    for lane in range(64):
+        a, q = lane % 16, lane // 16
+        for i in range(4):
+            word = 4 * lane + i
+            for e in range(8):
+                if kind == "K":
+                    t, c = a, 32 * i + 8 * q + e
+                else:
+                    t, c = 4 * q + e % 4, 16 * (2 * i + e // 4) + a
+                assert byte_idx[t, c] < 0
+                byte_idx[t, c] = 4 * word + e // 2
+                shift[t, c] = 4 * (e % 2)
+    assert (byte_idx >= 0).all()
+    return byte_idx, shift
 
 
 def _code_bit_tables(kind: str):
@@ -325,27 +366,29 @@ def _code_bit_tables(kind: str):
     return byte_idx, shift
 
 
-_K_TABLES = _code_bit_tables("K")
-_V_TABLES = _code_bit_tables("V")
+_TABLES = {(2, "K"): _code_bit_tables("K"), (2, "V"): _code_bit_tables("V"),
+           (4, "K"): _code_bit_tables_int4("K"), (4, "V"): _code_bit_tables_int4("V")}
 
 
-def pack_codes(codes: np.ndarray, kind: str) -> np.ndarray:
-    """codes uint8 [..., 16, 128] (0..3) -> code areas uint8 [..., 512]."""
-    byte_idx, shift = _K_TABLES if kind == "K" else _V_TABLES
+def pack_codes(codes: np.ndarray, kind: str, bits: int = 2) -> np.ndarray:
+    """codes uint8 [..., 16, 128] (0..levels(bits)) -> code areas uint8
+    [..., code_area_bytes(bits)]."""
+    byte_idx, shift = _TABLES[(bits, kind)]
+    nb, mask = code_area_bytes(bits), levels(bits)
     lead = codes.shape[:-2]
-    out = np.zeros(lead + (512,), dtype=np.uint8)
-    flat_out = out.reshape(-1, 512)
+    out = np.zeros(lead + (nb,), dtype=np.uint8)
+    flat_out = out.reshape(-1, nb)
     flat_c = codes.reshape(-1, PAGE, D).astype(np.uint8)
     for t in range(PAGE):
         for c in range(D):
-            flat_out[:, byte_idx[t, c]] |= ((flat_c[:, t, c] & 3) << np.uint8(shift[t, c])).astype(np.uint8)
+            flat_out[:, byte_idx[t, c]] |= ((flat_c[:, t, c] & mask) << np.uint8(shift[t, c])).astype(np.uint8)
     return out
 
 
-def unpack_codes(area: np.ndarray, kind: str) -> np.ndarray:
-    """code areas uint8 [..., 512] -> codes uint8 [..., 16, 128]."""
-    byte_idx, shift = _K_TABLES if kind == "K" else _V_TABLES
-    return (area[..., byte_idx] >> shift.astype(np.uint8)) & 3
+def unpack_codes(area: np.ndarray, kind: str, bits: int = 2) -> np.ndarray:
+    """code areas uint8 [..., code_area_bytes(bits)] -> codes uint8 [..., 16, 128]."""
+    byte_idx, shift = _TABLES[(bits, kind)]
+    return (area[..., byte_idx] >> shift.astype(np.uint8)) & levels(bits)
 
 
 def pack_meta(scale: np.ndarray, zero: np.ndarray) -> np.ndarray:
@@ -364,11 +407,12 @@ def unpack_meta(area: np.ndarray, G: int):
     return np.swapaxes(pair[..., 0], -1, -2), np.swapaxes(pair[..., 1], -1, -2)
 
 
-def split_block(block: np.ndarray, G: int) -> dict:
-    """Views of the four areas of history blocks uint8 [..., B_hist(G)]."""
+def split_block(block: np.ndarray, G: int, bits: int = 2) -> dict:
+    """Views of the four areas of history blocks uint8 [..., B_hist(G, bits)]."""
     m = 64 * (D // G)
-    return {"k_codes": block[..., 0:512], "k_meta": block[..., 512:512 + m],
-            "v_codes": block[..., 512 + m:1024 + m], "v_meta": block[..., 1024 + m:1024 + 2 * m]}
+    a = code_area_bytes(bits)
+    return {"k_codes": block[..., 0:a], "k_meta": block[..., a:a + m],
+            "v_codes": block[..., a + m:2 * a + m], "v_meta": block[..., 2 * a + m:2 * a + 2 * m]}
 
 
 # --------------------------------------------------------------------------
@@ -386,12 +430,13 @@ def storage_of(p: int, L: int):
 
 
 class LayerCacheRef:
-    """One layer's cache as numpy pools with page tables (formats of oscar.h)."""
+    """One layer's cache as numpy pools with page tables (formats of oscar.h);
+    bits = 2 (INT2 history) or 4 (INT4)."""
 
     def __init__(self, n_kv_heads: int, G: int, n_hist_pages: int, n_bf16_pages: int,
-                 hist_pt: np.ndarray, bf16_pt: np.ndarray):
-        self.hkv, self.G = n_kv_heads, G
-        self.hist = np.zeros((n_hist_pages, n_kv_heads, hist_block_bytes(G)), dtype=np.uint8)
+                 hist_pt: np.ndarray, bf16_pt: np.ndarray, bits: int = 2):
+        self.hkv, self.G, self.bits = n_kv_heads, G, bits
+        self.hist = np.zeros((n_hist_pages, n_kv_heads, hist_block_bytes(G, bits)), dtype=np.uint8)
         self.bf16 = np.zeros((n_bf16_pages, n_kv_heads, 2, PAGE, D), dtype=np.uint16)
         self.hist_pt = np.asarray(hist_pt, dtype=np.int32)
         self.bf16_pt = np.asarray(bf16_pt, dtype=np.int32)
@@ -452,17 +497,17 @@ class LayerCacheRef:
             rot = {"k": (rot_k, clip_k), "v": (rot_v, clip_v)}
             for h in range(self.hkv):
                 blocks = self.hist[pids, h].copy()          # [P][block]
-                areas = split_block(blocks, G)
+                areas = split_block(blocks, G, self.bits)
                 for kind in ("k", "v"):
                     R, clip = rot[kind]
-                    qq = quantize(xs[kind][:, h, :], R, clip, G)
-                    codes = unpack_codes(areas[kind + "_codes"], kind.upper())
+                    qq = quantize(xs[kind][:, h, :], R, clip, G, self.bits)
+                    codes = unpack_codes(areas[kind + "_codes"], kind.upper(), self.bits)
                     sc, zr = unpack_meta(areas[kind + "_meta"], G)
                     sc, zr = sc.copy(), zr.copy()
                     codes[slot, rows] = qq["codes"]
                     sc[slot, rows] = qq["scale"]
                     zr[slot, rows] = qq["zero"]
-                    areas[kind + "_codes"][:] = pack_codes(codes, kind.upper())
+                    areas[kind + "_codes"][:] = pack_codes(codes, kind.upper(), self.bits)
                     areas[kind + "_meta"][:] = pack_meta(sc, zr)
                 self.hist[pids, h] = blocks
 
@@ -490,9 +535,9 @@ class LayerCacheRef:
             slot = np.searchsorted(upages, pages)
             pids = self.hist_pt[b, upages]
             for h in range(self.hkv):
-                areas = split_block(self.hist[pids, h], G)
+                areas = split_block(self.hist[pids, h], G, self.bits)
                 for kind, R, out in (("k", rot_k, K), ("v", rot_v, V)):
-                    c = unpack_codes(areas[kind + "_codes"], kind.upper())      # [P][16][128]
+                    c = unpack_codes(areas[kind + "_codes"], kind.upper(), self.bits)      # [P][16][128]
                     sc, zr = unpack_meta(areas[kind + "_meta"], G)             # [P][16][NG]
                     n = c.shape[0] * PAGE
                     x = dequantize(c.reshape(n, D), sc.reshape(n, -1), zr.reshape(n, -1), G) @ R.T

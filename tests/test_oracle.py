@@ -353,6 +353,104 @@ def test_pack_hand_derived_bytes():
 
 def test_block_sizes():
     assert [o.hist_block_bytes(G) for G in (32, 64, 128)] == [1536, 1280, 1152]
+    assert [o.hist_block_bytes(G, 4) for G in (32, 64, 128)] == [2560, 2304, 2176]
+
+
+# ------------------------------------------------------------- INT4 variant
+
+
+def test_int4_quantizer_hand_cases():
+    I = np.eye(128)
+    # sixteen levels, each value its own code
+    q = o.quantize(_group_input(np.tile(np.arange(16.0), 2)), I, 1000.0, 32, bits=4)
+    assert q["zero"][0, 0] == 0 and q["scale"][0, 0] == 1
+    assert q["codes"][0, :32].tolist() == list(range(16)) * 2
+    # the INT2 quantiser on the same group spreads the range over 3 steps
+    q2 = o.quantize(_group_input(np.tile(np.arange(16.0), 2)), I, 1000.0, 32)
+    assert q2["scale"][0, 0] == 5 and q2["codes"][0, :16].tolist() == [0] * 3 + [1] * 5 + [2] * 5 + [3] * 3
+    # ties round to even: range 0..15 gives step 1; 2.5 -> 2, 3.5 -> 4, 14.5 -> 14
+    q = o.quantize(_group_input(np.array([0.0, 15.0, 2.5, 3.5, 14.5] + [1.0] * 27)), I, 1000.0, 32, bits=4)
+    assert q["codes"][0, 2:5].tolist() == [2, 4, 14]
+    # clipped maximum: range [0, 4] over 15 steps, fp16 step 0.26660156...
+    vals = np.array([50.0] + [float(i % 3) for i in range(31)])
+    q = o.quantize(_group_input(vals), I, 4.0, 32, bits=4)
+    assert float(q["scale"][0, 0]) == float(np.float16(4.0 / 15.0)) == 0.2666015625
+    assert q["codes"][0, 0] == 15
+    # x = 1 sits at 1/0.2666015625 = 3.7509... steps -> 4; x = 2 at 7.50183 -> 8
+    assert q["codes"][0, 1:4].tolist() == [0, 4, 8]
+    # constant group
+    q = o.quantize(_group_input(np.full(32, -0.25)), I, 1000.0, 32, bits=4)
+    assert q["scale"][0, 0] == 0 and q["codes"][0, :32].tolist() == [0] * 32
+    assert np.all(o.dequantize(q["codes"], q["scale"], q["zero"], 32)[0, :32] == -0.25)
+
+
+def test_int4_quantizer_invariants_random():
+    x = synth.bf16_to_f64(synth.bf16_bits(RNG.standard_normal((400, 128)).astype(np.float32) * 3))
+    R, _ = np.linalg.qr(RNG.standard_normal((128, 128)))
+    for G in (32, 64, 128):
+        q = o.quantize(x, R, 5.0, G, bits=4)
+        c, s = q["codes"], q["scale"].astype(float)
+        assert c.min() == 0 and c.max() == 15
+        xh = o.dequantize(c, q["scale"], q["zero"], G)
+        ng = 128 // G
+        err = np.abs(q["xc"] - xh).reshape(-1, ng, G)
+        slack = np.abs(q["xc"]).reshape(-1, ng, G).max(axis=2) * 2.0 ** -10
+        assert np.all(err.max(axis=2) <= s / 2 + 16 * slack + 1e-12)
+        g = q["xc"].reshape(-1, ng, G)
+        cg = c.reshape(-1, ng, G)
+        assert np.all(np.take_along_axis(cg, np.argmin(g, axis=2)[..., None], 2) == 0)
+        assert np.all(np.take_along_axis(cg, np.argmax(g, axis=2)[..., None], 2) == 15)
+        # four bits quantise the same rotated values more finely than two
+        q2 = o.quantize(x, R, 5.0, G)
+        e4 = np.linalg.norm(q["xc"] - xh)
+        e2 = np.linalg.norm(q2["xc"] - o.dequantize(q2["codes"], q2["scale"], q2["zero"], G))
+        assert e4 < 0.3 * e2
+
+
+def test_int4_quantizer_identity_is_textbook_minmax():
+    x = synth.bf16_to_f64(synth.bf16_bits(RNG.standard_normal((6, 128)).astype(np.float32)))
+    for G in (32, 128):
+        q = o.quantize(x, np.eye(128), 1e9, G, bits=4)
+        for n in range(x.shape[0]):
+            for g in range(128 // G):
+                vals = [float(v) for v in x[n, g * G:(g + 1) * G]]
+                lo, hi = min(vals), max(vals)
+                z = float(np.float16(lo))
+                s = float(np.float16((hi - lo) / 15))
+                for i, val in enumerate(vals):
+                    t = (val - z) / s
+                    r = math.floor(t + 0.5)
+                    if t + 0.5 == r and r % 2 == 1:
+                        r -= 1
+                    assert q["codes"][n, g * G + i] == min(15, max(0, r))
+
+
+def test_int4_pack_roundtrip_and_bijection():
+    c = RNG.integers(0, 16, size=(7, 16, 128)).astype(np.uint8)
+    for kind in "KV":
+        area = o.pack_codes(c, kind, 4)
+        assert area.shape == (7, 1024)
+        assert np.array_equal(o.unpack_codes(area, kind, 4), c)
+        assert np.all(o.pack_codes(np.full((1, 16, 128), 15, dtype=np.uint8), kind, 4) == 0xFF)
+
+
+def test_int4_pack_hand_derived_bytes():
+    g = _golden("pack_bytes_int4.json")
+    for case in g["cases"]:
+        c = np.zeros((16, 128), dtype=np.uint8)
+        c[case["row"], case["channel"]] = case["code"]
+        expect = np.zeros(1024, dtype=np.uint8)
+        for k, v in case["bytes"].items():
+            expect[int(k)] = v
+        assert np.array_equal(o.pack_codes(c, case["kind"], 4), expect), case["derivation"]
+    for case in g["dword_cases"]:
+        c = np.zeros((16, 128), dtype=np.uint8)
+        for row, ch, code in case["codes"]:
+            c[row, ch] = code
+        expect = np.zeros(1024, dtype=np.uint8)
+        for k, v in case["bytes"].items():
+            expect[int(k)] = v
+        assert np.array_equal(o.pack_codes(c, case["kind"], 4), expect), case["derivation"]
 
 
 # ------------------------------------------------------------------- layout
@@ -378,11 +476,11 @@ def test_storage_of_boundaries():
         assert len(set(slots)) == len(slots)
 
 
-def _make_cache(L_max, hkv=2, G=32, batch=1, seed=3):
+def _make_cache(L_max, hkv=2, G=32, batch=1, seed=3, bits=2):
     n_hist = max(1, (max(0, L_max - 144) + 15) // 16)
     pt, npool = synth.shuffled_page_tables(seed, 0, [L_max] * batch, n_pool_pages=n_hist * batch + 3)
     bpt = synth.bf16_page_tables(batch, shuffle_seed=seed)
-    return o.LayerCacheRef(hkv, G, npool, 9 * batch, pt, bpt)
+    return o.LayerCacheRef(hkv, G, npool, 9 * batch, pt, bpt, bits=bits)
 
 
 def _rot(seed=5):
@@ -390,14 +488,15 @@ def _rot(seed=5):
     return R
 
 
-@pytest.mark.parametrize("L", [1, 16, 17, 144, 145, 160, 161, 300])
-def test_prefill_equals_token_by_token(L):
+@pytest.mark.parametrize("L,bits", [(1, 2), (16, 2), (17, 2), (144, 2), (145, 2), (160, 2), (161, 2),
+                                    (300, 2), (145, 4), (300, 4)])
+def test_prefill_equals_token_by_token(L, bits):
     ld = synth.LayerData(21, 0, 4, 2)
     k, v = ld.cache_kv(L)
     R = _rot()
-    a = _make_cache(L)
+    a = _make_cache(L, bits=bits)
     a.write(R, R.T, 4.0, 3.0, k, v, [0, L], [0])
-    b = _make_cache(L)
+    b = _make_cache(L, bits=bits)
     for p in range(L):
         b.write(R, R.T, 4.0, 3.0, k[p:p + 1], v[p:p + 1], [0, 1], [p])
     assert np.array_equal(a.hist, b.hist)
@@ -468,12 +567,12 @@ def test_attention_brute_force_tiny():
             np.testing.assert_allclose(out[h], ref, rtol=1e-12, atol=1e-12)
 
 
-def _filled(L, batch=1, hkv=2, hq=8, G=32, seed=31, R=None, Rv=None, clip=(6.0, 6.0)):
+def _filled(L, batch=1, hkv=2, hq=8, G=32, seed=31, R=None, Rv=None, clip=(6.0, 6.0), bits=2):
     ld = synth.LayerData(seed, 0, hq, hkv)
     k, v = ld.cache_kv(L * batch)
     R = _rot(8) if R is None else R
     Rv = R if Rv is None else Rv
-    c = _make_cache(L, hkv=hkv, G=G, batch=batch, seed=seed)
+    c = _make_cache(L, hkv=hkv, G=G, batch=batch, seed=seed, bits=bits)
     cu = [L * i for i in range(batch + 1)]
     c.write(R, Rv, clip[0], clip[1], k, v, cu, [0] * batch)
     return c, k, v, ld.decode_q(batch), R, Rv
@@ -640,6 +739,99 @@ def test_decode_brute_force_with_history():
     for h in range(2):
         ref = _brute_attention(qf[h].tolist(), Ks, Vs, 0.1)
         np.testing.assert_allclose(out[0, h], ref, rtol=1e-11, atol=1e-11)
+
+
+def test_int4_decode_lossless_history_pins_rotation_direction():
+    # as for INT2, with sixteen levels per group: each rotated group holds
+    # only z + k s, k = 0..15, with both ends present, so INT4 storage is
+    # lossless and the decode equals the BF16 decode of the same tokens
+    L = 200
+    shift = np.roll(np.eye(128), 9, axis=1)
+    rng = np.random.default_rng(98)
+    k = np.zeros((L, 2, 128), dtype=np.float32)
+    v = np.zeros((L, 2, 128), dtype=np.float32)
+    for X in (k, v):
+        lv = rng.integers(0, 16, size=(L, 2, 128)).astype(np.float32)
+        lv[..., 0::64] = 0
+        lv[..., 1::64] = 15
+        X[:] = (lv * 0.25 - 2.0) @ shift.T
+    kb, vb = synth.bf16_bits(k), synth.bf16_bits(v)
+    c = _make_cache(L, G=64, bits=4)
+    c.write(shift, shift, 100.0, 100.0, kb, vb, [0, L], [0])
+    q = synth.LayerData(6, 0, 8, 2).decode_q(1)
+    out = o.decode_attn(c, shift, shift, q, [L], 0.088)
+    pages = np.zeros(((L + 15) // 16, 2, 2, 16, 128), dtype=np.uint16)
+    for p in range(L):
+        pages[p // 16, :, 0, p % 16] = kb[p]
+        pages[p // 16, :, 1, p % 16] = vb[p]
+    ref = o.bf16_paged_decode(q, pages, np.arange(pages.shape[0], dtype=np.int32)[None], [L], 0.088)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+    bad = o.decode_attn(c, shift.T, shift.T, q, [L], 0.088)
+    assert np.abs(bad - ref).max() > 0.1
+
+
+def test_int4_decode_brute_force_with_history():
+    # INT4 decode against a plain-Python evaluation that finds each 4-bit
+    # code by scanning the layout's (lane, dword, nibble) enumeration
+    L = 166
+    c, k, v, q, R, Rv = _filled(L, hkv=1, hq=2, G=32, clip=(3.0, 2.5), bits=4)
+    out = o.decode_attn(c, R, Rv, q, [L], 0.1)
+    qf = synth.bf16_to_f64(q)[0]
+    kf, vf = synth.bf16_to_f64(k), synth.bf16_to_f64(v)
+
+    def code_at(area, kind, t, ch):
+        for lane in range(64):
+            a, qq = lane % 16, lane // 16
+            for i in range(4):
+                for e in range(8):
+                    if kind == "K":
+                        tt, c2 = a, 32 * i + 8 * qq + e
+                    else:
+                        tt, c2 = 4 * qq + e % 4, 16 * (2 * i + e // 4) + a
+                    if tt == t and c2 == ch:
+                        word = int.from_bytes(bytes(area[16 * lane + 4 * i:16 * lane + 4 * i + 4]), "little")
+                        return (word >> (4 * e)) & 15
+        raise AssertionError
+
+    def vec(kind, p):
+        h = p - 16
+        blk = c.hist[c.hist_pt[0, h // 16], 0]
+        off = 0 if kind == "K" else 1024 + 256
+        meta = blk[off + 1024: off + 1024 + 256].view(np.float16)
+        xr = []
+        for ch in range(128):
+            g = ch // 32
+            s, z = float(meta[2 * (16 * g + h % 16)]), float(meta[2 * (16 * g + h % 16) + 1])
+            xr.append(code_at(blk[off:off + 1024], kind, h % 16, ch) * s + z)
+        Rm = R if kind == "K" else Rv
+        return [sum(xr[j] * Rm[i, j] for j in range(128)) for i in range(128)]
+
+    Ks, Vs = [], []
+    for p in range(L):
+        if o.storage_of(p, L)[0] == "hist":
+            Ks.append(vec("K", p))
+            Vs.append(vec("V", p))
+        else:
+            Ks.append(kf[p, 0].tolist())
+            Vs.append(vf[p, 0].tolist())
+    for h in range(2):
+        ref = _brute_attention(qf[h].tolist(), Ks, Vs, 0.1)
+        np.testing.assert_allclose(out[0, h], ref, rtol=1e-11, atol=1e-11)
+
+
+def test_int4_history_closer_than_int2():
+    # the same tokens stored at four bits (no clipping) decode closer to the
+    # unquantised attention than at two bits
+    L = 400
+    outs = {}
+    for bits in (2, 4):
+        c, k, v, q, R, Rv = _filled(L, bits=bits, seed=33, clip=(1e4, 1e4))
+        outs[bits] = o.decode_attn(c, R, Rv, q, [L], 0.088)
+    kf, vf = synth.bf16_to_f64(k), synth.bf16_to_f64(v)
+    ref = o.attention(synth.bf16_to_f64(q)[0], kf, vf, 0.088)
+    e2 = np.abs(outs[2][0] - ref).max()
+    e4 = np.abs(outs[4][0] - ref).max()
+    assert e4 < 0.5 * e2
 
 
 # ------------------------------------------------------- rotation variants
