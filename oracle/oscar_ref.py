@@ -320,11 +320,12 @@ def hist_block_bytes(G: int, bits: int = 2) -> int:
 def _code_bit_tables_int4(kind: str):
     """(byte index, shift) [16 rows][128 channels] of every 4-bit code of an
     INT4 code area (1024 bytes, 256 dwords; dword w = 4 l + i of lane l,
-    a = l % 16, q = l / 16; code at bits 4 e .. 4 e + 3 of its dword):
-      K: a = token t; dword i = kb (0..3) holds channels 32 kb + 8 q + e,
-         e = 0..7, of token t;
-      V: a = channel offset m; dword i = d (0..3), half h = e / 4 (16 bits
-         each) holds channel 16 (2 d + h) + m, token 4 q + e % 4."""
+    a = l % 16, q = l / 16; nibble e = 0..7 of a dword at bits 4 e .. 4 e + 3):
+      K: a = token t; dword i = kb (0..3), nibble e holds channel
+         32 kb + 8 q + 2 (e % 4) + e / 4 of token t;
+      V: a = channel offset m; dword i = d (0..3), nibble e holds channel
+         16 (2 d + (e / 2) % 2) + m, token 4 q + 2 (e % 2) + e / 4.
+    Nibbles e and e + 4 thus hold neighbouring channels (K) or tokens (V)."""
     byte_idx = np.full((PAGE, D), -1, dtype=np.int64)
     shift = np.full((PAGE, D), -1, dtype=np.int64)
     for lane in range(64):
@@ -333,9 +334,9 @@ def _code_bit_tables_int4(kind: str):
             word = 4 * lane + i
             for e in range(8):
                 if kind == "K":
-                    t, c = a, 32 * i + 8 * q + e
+                    t, c = a, 32 * i + 8 * q + 2 * (e % 4) + e // 4
                 else:
-                    t, c = 4 * q + e % 4, 16 * (2 * i + e // 4) + a
+                    t, c = 4 * q + 2 * (e % 2) + e // 4, 16 * (2 * i + (e // 2) % 2) + a
                 assert byte_idx[t, c] < 0
                 byte_idx[t, c] = 4 * word + e // 2
                 shift[t, c] = 4 * (e % 2)

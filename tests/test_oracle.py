@@ -785,9 +785,9 @@ def test_int4_decode_brute_force_with_history():
             for i in range(4):
                 for e in range(8):
                     if kind == "K":
-                        tt, c2 = a, 32 * i + 8 * qq + e
+                        tt, c2 = a, 32 * i + 8 * qq + 2 * (e % 4) + e // 4
                     else:
-                        tt, c2 = 4 * qq + e % 4, 16 * (2 * i + e // 4) + a
+                        tt, c2 = 4 * qq + 2 * (e % 2) + e // 4, 16 * (2 * i + (e // 2) % 2) + a
                     if tt == t and c2 == ch:
                         word = int.from_bytes(bytes(area[16 * lane + 4 * i:16 * lane + 4 * i + 4]), "little")
                         return (word >> (4 * e)) & 15
