@@ -35,7 +35,8 @@ class LayerCacheC(ctypes.Structure):
                 ("hist_pt", c_p),
                 ("hist_pt_stride", ctypes.c_int32),
                 ("bf16_pt", c_p),
-                ("status", c_p)]
+                ("status", c_p),
+                ("code_bits", ctypes.c_int32)]
 
 
 class RotationC(ctypes.Structure):
@@ -47,6 +48,7 @@ SIGNATURES = [
     ("oscar_last_error", ctypes.c_char_p, []),
     ("oscar_version", ctypes.c_char_p, []),
     ("oscar_hist_block_bytes", ctypes.c_size_t, [ctypes.c_int32]),
+    ("oscar_hist_block_bytes_bits", ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32]),
     ("oscar_rotation_bytes", ctypes.c_size_t, []),
     ("oscar_prepare_rotation", ctypes.c_int, [c_p, c_p, c_p]),
     ("oscar_calibrate_workspace_bytes", ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),

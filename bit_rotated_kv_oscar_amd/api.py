@@ -39,8 +39,8 @@ def _need(t: torch.Tensor, name: str, dtypes, device=None) -> None:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
-def hist_block_bytes(group: int) -> int:
-    return int(load().oscar_hist_block_bytes(group))
+def hist_block_bytes(group: int, code_bits: int = 2) -> int:
+    return int(load().oscar_hist_block_bytes_bits(group, code_bits))
 
 
 def rotation_bytes() -> int:
@@ -67,20 +67,23 @@ class Rotation:
 class LayerCache:
     """One layer's paged cache in the formats of include/oscar.h.
 
-    hist:   uint8 [n_hist_pages, Hkv, hist_block_bytes(group)]
+    hist:   uint8 [n_hist_pages, Hkv, hist_block_bytes(group, code_bits)]
     bf16:   bfloat16 [n_bf16_pages, Hkv, 2, 16, 128]
     hist_pt int32 [B, stride], bf16_pt int32 [B, 9], status int32 [1].
+    code_bits: 2 (INT2 history) or 4 (INT4).
     """
 
     def __init__(self, n_kv_heads: int, group: int, n_hist_pages: int, n_bf16_pages: int,
                  hist_pt: torch.Tensor, bf16_pt: torch.Tensor, device="cuda",
-                 hist: torch.Tensor | None = None, bf16: torch.Tensor | None = None):
+                 hist: torch.Tensor | None = None, bf16: torch.Tensor | None = None, code_bits: int = 2):
         device = torch.device(device)
         self.device = device
-        self.n_kv_heads, self.group = int(n_kv_heads), int(group)
-        blk = hist_block_bytes(group)
+        self.n_kv_heads, self.group, self.code_bits = int(n_kv_heads), int(group), int(code_bits)
+        blk = hist_block_bytes(group, code_bits)
         if blk == 0:
-            raise ValueError(f"unsupported group {group}")
+            raise ValueError(f"unsupported group {group} / code_bits {code_bits}")
+        if hist is not None and (hist.dim() != 3 or hist.shape[2] != blk):
+            raise ValueError(f"hist must be [pages, Hkv, {blk}]")
         self.hist = hist if hist is not None else torch.zeros(
             (max(n_hist_pages, 0), n_kv_heads, blk), dtype=torch.uint8, device=device)
         self.bf16 = bf16 if bf16 is not None else torch.zeros(
@@ -94,7 +97,8 @@ class LayerCache:
     def c(self) -> LayerCacheC:
         return LayerCacheC(self.n_kv_heads, self.group, self.hist.data_ptr(), self.hist.shape[0],
                            self.bf16.data_ptr(), self.bf16.shape[0], self.hist_pt.data_ptr(),
-                           self.hist_pt.shape[1], self.bf16_pt.data_ptr(), self.status.data_ptr())
+                           self.hist_pt.shape[1], self.bf16_pt.data_ptr(), self.status.data_ptr(),
+                           self.code_bits)
 
 
 def write_kv(cache: LayerCache, rot_k: Rotation, rot_v: Rotation, k_new: torch.Tensor,

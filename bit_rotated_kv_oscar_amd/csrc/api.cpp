@@ -55,6 +55,8 @@ int check_cache(const oscar_layer_cache *c) {
   if (c->n_kv_heads < 1 || c->n_kv_heads > 256)
     return fail(OSCAR_EINVAL, "n_kv_heads %d outside [1, 256]", c->n_kv_heads);
   if (!group_ok(c->group)) return fail(OSCAR_EUNSUPPORTED, "group %d not in {32, 64, 128}", c->group);
+  if (c->code_bits != 0 && c->code_bits != 2 && c->code_bits != 4)
+    return fail(OSCAR_EUNSUPPORTED, "code_bits %d not in {0 (= 2), 2, 4}", c->code_bits);
   if (c->n_hist_pages < 0 || c->n_bf16_pages < 1)
     return fail(OSCAR_EINVAL, "page counts must be n_hist_pages >= 0 and n_bf16_pages >= 1");
   if (c->n_hist_pages > (int64_t(1) << 31) - 1 || c->n_bf16_pages > (int64_t(1) << 31) - 1)
@@ -63,6 +65,12 @@ int check_cache(const oscar_layer_cache *c) {
   if (!c->bf16) return fail(OSCAR_EINVAL, "bf16 pool is NULL");
   if (!c->hist_pt || c->hist_pt_stride < 1) return fail(OSCAR_EINVAL, "hist_pt NULL or hist_pt_stride < 1");
   if (!c->bf16_pt) return fail(OSCAR_EINVAL, "bf16_pt is NULL");
+  return OSCAR_OK;
+}
+
+// Entry points that handle INT2 caches only.
+int check_int2(const oscar_layer_cache *c, const char *what) {
+  if (oscar::cache_bits(*c) != 2) return fail(OSCAR_EUNSUPPORTED, "%s supports INT2 caches only (code_bits 2)", what);
   return OSCAR_OK;
 }
 
@@ -234,6 +242,11 @@ size_t oscar_hist_block_bytes(int32_t group) {
   return group_ok(group) ? size_t(oscar::hist_block_bytes(group)) : 0;
 }
 
+size_t oscar_hist_block_bytes_bits(int32_t group, int32_t code_bits) {
+  if (!group_ok(group) || (code_bits != 2 && code_bits != 4)) return 0;
+  return size_t(oscar::hist_block_bytes(group, code_bits));
+}
+
 size_t oscar_rotation_bytes(void) { return oscar::FORM_BYTES; }
 
 int oscar_prepare_rotation(const double *R, void *forms, oscar_stream_t stream) {
@@ -347,6 +360,7 @@ int oscar_decode_step(const oscar_layer_cache *cache, const oscar_rotation *rot_
                       float sm_scale, float *out, void *workspace, size_t workspace_bytes,
                       oscar_stream_t stream) {
   if (int rc = check_cache(cache)) return rc;
+  if (int rc = check_int2(cache, "decode_step")) return rc;
   if (int rc = check_rot(rot_k, "rot_k")) return rc;
   if (int rc = check_rot(rot_v, "rot_v")) return rc;
   if (int rc = check_heads(n_q_heads, cache->n_kv_heads)) return rc;
@@ -374,6 +388,7 @@ int oscar_extend_attn(const oscar_layer_cache *cache, const oscar_rotation *rot_
                       const int32_t *cu_new, const int32_t *len_before, int32_t batch, int64_t total_tokens,
                       int32_t max_new, int32_t max_prefix, float sm_scale, float *out, oscar_stream_t stream) {
   if (int rc = check_cache(cache)) return rc;
+  if (int rc = check_int2(cache, "extend_attn")) return rc;
   if (int rc = check_rot(rot_k, "rot_k")) return rc;
   if (int rc = check_rot(rot_v, "rot_v")) return rc;
   if (int rc = check_heads(n_q_heads, cache->n_kv_heads)) return rc;

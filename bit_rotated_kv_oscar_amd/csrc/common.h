@@ -16,7 +16,7 @@ constexpr int N_SINK = OSCAR_N_SINK;  // 16
 constexpr int N_RECENT = OSCAR_N_RECENT;
 constexpr int N_RAW = N_SINK + N_RECENT;  // 144 raw bf16 tokens at most
 constexpr int BF16_PT = OSCAR_BF16_PAGES_PER_REQ;
-constexpr int CODE_BYTES = 512;       // one code area: 16 rows x 128 codes x 2 bits
+constexpr int CODE_BYTES = 512;       // one INT2 code area: 16 rows x 128 codes x 2 bits
 
 // Byte offsets inside the forms buffer of one rotation.
 constexpr size_t FORM_R = 0;                        // fp32 R[i][j]
@@ -25,13 +25,21 @@ constexpr size_t FORM_RT_HI = FORM_RT + D * D * 4;  // fp16 hi(R[i][j]) at [j][i
 constexpr size_t FORM_RT_LO = FORM_RT_HI + D * D * 2;  // fp16 2^11 * (R - hi)
 constexpr size_t FORM_BYTES = FORM_RT_LO + D * D * 2;
 
+// History blocks of both code widths: [K codes | K meta | V codes | V meta],
+// a code area being 16 rows x 128 codes x bits (512 B for INT2, 1 KB for
+// INT4).
 __host__ __device__ constexpr int n_groups(int G) { return D / G; }
 __host__ __device__ constexpr int meta_bytes(int G) { return 64 * (D / G); }
-__host__ __device__ constexpr int hist_block_bytes(int G) { return 1024 + 128 * (D / G); }
-__host__ __device__ constexpr int k_codes_off(int) { return 0; }
-__host__ __device__ constexpr int k_meta_off(int) { return CODE_BYTES; }
-__host__ __device__ constexpr int v_codes_off(int G) { return CODE_BYTES + meta_bytes(G); }
-__host__ __device__ constexpr int v_meta_off(int G) { return 2 * CODE_BYTES + meta_bytes(G); }
+__host__ __device__ constexpr int code_area_bytes(int bits) { return PAGE * D * bits / 8; }
+__host__ __device__ constexpr int hist_block_bytes(int G, int bits = 2) {
+  return 2 * code_area_bytes(bits) + 128 * (D / G);
+}
+__host__ __device__ constexpr int k_codes_off(int, int = 2) { return 0; }
+__host__ __device__ constexpr int k_meta_off(int, int bits = 2) { return code_area_bytes(bits); }
+__host__ __device__ constexpr int v_codes_off(int G, int bits = 2) { return code_area_bytes(bits) + meta_bytes(G); }
+__host__ __device__ constexpr int v_meta_off(int G, int bits = 2) { return 2 * code_area_bytes(bits) + meta_bytes(G); }
+// the code width of a cache (0 in a zero-initialised struct means INT2)
+__host__ __device__ inline int cache_bits(const oscar_layer_cache &c) { return c.code_bits == 4 ? 4 : 2; }
 
 // Slot bit tables of a code dword (first code at LO[u], second at HI[u]).
 __host__ __device__ inline int slot_lo(int u) {

@@ -23,7 +23,7 @@
 //     appended is read from k_new / v_new); splits s >= 1 over history pages
 //     (wave w takes every 8th page of the split; its first 64 page ids are
 //     loaded at entry with the other loads that need no request length;
-//     pages are copied straight into a per-wave LDS ring DEPTH pages ahead of
+//     pages are copied straight into a per-wave LDS ring 4 pages ahead of
 //     the one being computed).  While the first pages fly, each history
 //     workgroup computes q_rot = q R_K * sm_scale * log2(e) for the query
 //     heads of its group and lays it out as the A operand of the score
@@ -175,6 +175,7 @@ struct StepArgs {
   float pv_scale, pv_unscale;     // 2^k and 2^-k applied to the PV operand
   float pk01, pk23;               // log2(4 * 2^k), log2(16 * 2^k): PV factors of tokens 4q+{0,1}, 4q+{2,3}
   uint32_t ex_m4, ex_m16, ex_e;   // code expansion constants 0x03000300, 0x00C000C0, 0x3C003C00
+  uint32_t ex_mn;                 // INT4 expansion mask 0x03C003C0
   float *parts;                   // [B][Hq][part_slots][PART_STRIDE]
   int part_slots;                 // partials per query head: 1 + max(n_splits, merge window)
   uint32_t *counters;             // [B][Hkv][COUNTER_STRIDE]: word 0 = workgroups done (zero between calls)
@@ -449,7 +450,7 @@ __device__ inline void build_q_issue(const StepArgs &a, int b, int hk, int tid, 
 
 // Workgroup-wide, from the loads above: q' = q R_K and the A-operand
 // fragment block of the score product in frag_lds (layout of Rows).
-template <int GQA, int NG>
+template <int GQA, int NG, int BITS>
 __device__ __forceinline__ void build_q(const StepArgs &a, int tid, QWork<GQA, NG> &w, uint32_t *frag_lds, const QLoads<GQA> &ql) {
   using R = Rows<GQA, NG>;
   constexpr int G = R::G, SEG = QWork<GQA, NG>::SEG, NT = AW * 64;
@@ -504,7 +505,8 @@ __device__ __forceinline__ void build_q(const StepArgs &a, int tid, QWork<GQA, N
   float kq = 1.f;  // keeps |q' * 16 * kq| <= 2^14 (fp16 operands)
   while (gmax * 16.f * kq > 16384.f) kq *= 0.5f;
   // A operand values q' * w_c * kq as fp16 high part and low part x 2^11
-  // (w_c = 4 or 16, the weight that the K code expansion puts on channel c),
+  // (w_c, the weight that the K code expansion puts on channel c: INT2 4 or
+  // 16, INT4 16 on every channel),
   // and their sums over each scale group by wave reductions: a wave covers
   // 64 consecutive channels of one head (uniform loop bounds)
   for (int e0 = 0; e0 < GQA * D; e0 += NT) {
@@ -514,7 +516,7 @@ __device__ __forceinline__ void build_q(const StepArgs &a, int tid, QWork<GQA, N
     float vh = 0.f, vl = 0.f, vq = 0.f;
     if (in) {
       const float y = w.y[h][ch] * sc;
-      const float x = y * (((ch & 3) < 2) ? 4.f : 16.f) * kq;
+      const float x = y * ((BITS == 2 && (ch & 3) < 2) ? 4.f : 16.f) * kq;
       const _Float16 hi = _Float16(x), lo = _Float16((x - float(hi)) * 2048.f);
       w.qa[0][h][ch] = hi;
       w.qa[1][h][ch] = lo;
@@ -570,14 +572,18 @@ __device__ __forceinline__ void build_q(const StepArgs &a, int tid, QWork<GQA, N
 // ------------------------------------------------------------------ attend
 
 // History pages reach LDS by direct global->LDS copies (global_load_lds):
-// DEPTH pages per wave in flight without holding registers.  One page block
-// is 1024 + 128 NG bytes: one 16-byte-per-lane copy of the first 1 KB, one
-// of the rest on the first 8 NG lanes.  The compiler does not order LDS
-// reads after these copies, so the page loop waits for them itself (vmcnt
-// counts per instruction; loads complete in issue order).
-constexpr int DEPTH = 4;
-constexpr int RP = 3;  // pages loaded through registers before the q build (at most DEPTH - 1)
-static_assert(RP <= DEPTH - 1, "register pages fit the ring");
+// several pages per wave in flight without holding registers.  One INT2
+// page block is 1024 + 128 NG bytes: one 16-byte-per-lane copy of the first
+// 1 KB, one of the rest on the first 8 NG lanes (INT4: two copies of 1 KB,
+// then the rest).  The compiler does not order LDS reads after these copies,
+// so the page loop waits for them itself (vmcnt counts per instruction;
+// loads complete in issue order).
+// Pages in flight per wave (the ring's depth): 4 INT2 pages; INT4 blocks are
+// 1.7-1.9 times larger, and three of them hold more bytes than four INT2
+// pages while two workgroups' rings still fit a CU's LDS.  The first
+// depth - 1 pages are loaded through registers before the q build.
+template <int BITS>
+constexpr int depth_of() { return BITS == 2 ? 4 : 3; }
 
 __device__ inline void lds_copy16(const void *src, void *lds_base) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
@@ -588,17 +594,17 @@ __device__ inline void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// wait until at most `pages` page copies (2 instructions each) are pending
-template <int P = DEPTH - 1>
+// wait until at most `pages` page copies (IPP instructions each) are pending
+template <int IPP, int P>
 __device__ inline void wait_pages(int pages) {
-  static_assert(2 * P <= 63, "vmcnt range");
+  static_assert(IPP * P <= 63, "vmcnt range");
   if constexpr (P == 0) {
     wait_vmem<0>();
   } else {
     if (pages >= P)
-      wait_vmem<2 * P>();
+      wait_vmem<IPP * P>();
     else
-      wait_pages<P - 1>(pages);
+      wait_pages<IPP, P - 1>(pages);
   }
 }
 
@@ -651,6 +657,42 @@ struct RingRead {
   }
 };
 
+// The same for INT4 pages: 16 code bytes per lane and tensor.
+template <int VCODE, int KMETA, int VMETA, int POFF>
+struct RingRead4 {
+  u32x4 kc, vc;
+  uint32_t km0, km1, vm0, vm1;
+  template <int NG>
+  __device__ void load(uint32_t a_code, uint32_t a_meta) {
+    if constexpr (NG == 1) {
+      asm volatile(
+          "ds_read_b128 %0, %4\n\t"
+          "ds_read_b128 %1, %4 offset:%6\n\t"
+          "ds_read_b32 %2, %5 offset:%7\n\t"
+          "ds_read_b32 %3, %5 offset:%8\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(kc), "=&v"(vc), "=&v"(km0), "=&v"(vm0)
+          : "v"(a_code), "v"(a_meta), "n"(VCODE), "n"(KMETA), "n"(VMETA)
+          : "memory");
+      km1 = km0;
+      vm1 = vm0;
+    } else {
+      asm volatile(
+          "ds_read_b128 %0, %6\n\t"
+          "ds_read_b128 %1, %6 offset:%8\n\t"
+          "ds_read_b32 %2, %7 offset:%9\n\t"
+          "ds_read_b32 %3, %7 offset:%10\n\t"
+          "ds_read_b32 %4, %7 offset:%11\n\t"
+          "ds_read_b32 %5, %7 offset:%12\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(kc), "=&v"(vc), "=&v"(km0), "=&v"(km1), "=&v"(vm0), "=&v"(vm1)
+          : "v"(a_code), "v"(a_meta), "n"(VCODE), "n"(KMETA), "n"(KMETA + POFF), "n"(VMETA),
+            "n"(VMETA + POFF)
+          : "memory");
+    }
+  }
+};
+
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 __device__ inline h2v as_h2(uint32_t w) { return __builtin_bit_cast(h2v, w); }
 
@@ -675,6 +717,21 @@ struct Expander {
     const uint32_t x = s == 0 ? w : s == 1 ? (w >> 4) : s == 2 ? (w << 4) : rotr8(w);
     return as_f16x4(and_or(x, m4, e), and_or(x, m16, e));
   }
+};
+
+// INT4 codes as fp16 1 + c/16: a nibble moved to mantissa bits 6-9 (and
+// 22-25 for the high half) under the exponent of 1.0.  Pair p of a dword
+// holds nibbles p and p + 4, so the four pairs of a K dword are channels
+// 0..7 of its block in order, and pairs 0, 1 (2, 3) of a V dword are rows
+// 0..3 of its first (second) channel.
+struct Expander4 {
+  uint32_t m, e;  // 0x03C003C0, 0x3C003C00
+  __device__ uint32_t pair(uint32_t x, int p) const {
+    const uint32_t y = p == 0 ? (x << 6) : p == 1 ? (x << 2) : p == 2 ? (x >> 2) : (x >> 6);
+    return and_or(y, m, e);
+  }
+  __device__ f16x8 k(uint32_t x) const { return as_f16x8(pair(x, 0), pair(x, 1), pair(x, 2), pair(x, 3)); }
+  __device__ f16x4 v(uint32_t x, int h) const { return as_f16x4(pair(x, 2 * h), pair(x, 2 * h + 1)); }
 };
 
 // x[ch][sl] of lane src (a byte address, 4 * lane) where (ch, sl) is this
@@ -726,14 +783,18 @@ __device__ inline uint32_t halves(uint32_t a, uint32_t b, uint32_t sel) { return
 // forms B_g = fp16(pw s_tg) for each scale group g; acc[r] += Vexp_r B_g(r)
 // with Vexp = 1 + code/w_t, and cacc[g] += 1 B_g, whose rows all equal the
 // column sums of B_g: acc - cacc is then exactly sum_t B code / w_t.
-template <int GQA, int NG, class Prep>
+template <int GQA, int NG, int BITS, class Prep>
 __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, int j1, int wave, int lane,
                              int pid_pre, Prep &&prep, const uint32_t *frag_lds, uint8_t *ring, float *zs,
                              float *o_lds, float *m_lds, float *l_lds) {
   using R = Rows<GQA, NG>;
   constexpr int NCH = R::NCH, SPL = R::SPL, G = R::G, HC = R::HC;
-  constexpr int SB = hist_block_bytes(G);
-  constexpr int kmeta = k_meta_off(G), vcode = v_codes_off(G), vmeta = v_meta_off(G);
+  constexpr int SB = hist_block_bytes(G, BITS);
+  constexpr int kmeta = k_meta_off(G, BITS), vcode = v_codes_off(G, BITS), vmeta = v_meta_off(G, BITS);
+  // a block is HB = 2 code areas' worth of bytes (1 or 2 KB) copied 1 KB
+  // per instruction, then 128 NG bytes of tail: IPP copy instructions per page
+  constexpr int HB = 2 * code_area_bytes(BITS), NHB = HB / 1024, IPP = NHB + 1;
+  constexpr int DP = depth_of<BITS>(), RPB = DP - 1;
   const oscar_layer_cache &c = a.c;
   const int t = lane & 15, qd = lane >> 4;  // score side: token, lane group
   const int hp = t % GQA;                   // PV side: head of column n = l%16 (tq = qd)
@@ -747,7 +808,7 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
   f32x4 dinit[NCH];
   float qz[NCH][2];
   float inv_kq = 1.f, kq = 1.f;
-  const bool w16 = (t & 3) >= 2;
+  const bool w16 = BITS == 4 || (t & 3) >= 2;
   const float lw_t = w16 ? a.pk23 : a.pk01;  // log2(w_t 2^kpv)
   const float inv_w = w16 ? 0.0625f : 0.25f;
   // K/V meta dword of (token t, group of pair 0); pair 1 sits 16 dwords on
@@ -761,6 +822,9 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
   // keep the exponent pattern in a VGPR (the mask stays in an SGPR): then one
   // v_and_or_b32 per expanded register.  The empty asm emits no instruction.
   asm volatile("" : "+v"(ex.e));
+  Expander4 ex4;
+  ex4.m = a.ex_mn;
+  ex4.e = ex.e;
   const f16x4 ones = as_f16x4(0x3C003C00u, 0x3C003C00u);
 
   bool started = false;  // wave-uniform: a max has been set
@@ -787,7 +851,7 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
   // page is skipped), so every page costs the same two copy instructions
   uint32_t ok_slots = 0;
   const uint32_t lane16 = 16u * uint32_t(lane);
-  constexpr int N2 = (SB - 1024) / 16;  // lanes of the second copy
+  constexpr int N2 = (SB - HB) / 16;  // lanes of the tail copy
   static_assert((N2 & (N2 - 1)) == 0 && N2 <= 64, "second copy part: a power of two of lanes");
   auto page_block = [&](int i, int sl) {
     if ((i & 63) == 0 && i > 0) {
@@ -806,8 +870,9 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
   auto issue = [&](int i, int sl) {
     const uint8_t *blk = page_block(i, sl);
     uint8_t *dst = ring + sl * SB;
-    lds_copy16(blk + lane16, dst);
-    if (lane < N2) lds_copy16(blk + 1024u + lane16, dst + 1024);
+#pragma unroll
+    for (int k = 0; k < NHB; ++k) lds_copy16(blk + 1024u * k + lane16, dst + 1024 * k);
+    if (lane < N2) lds_copy16(blk + uint32_t(HB) + lane16, dst + HB);
   };
   // the first DEPTH - 1 pages go through registers: no copy into LDS is in
   // flight while the workgroup builds the q fragment (the compiler would
@@ -816,33 +881,41 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
   // per lane.  Both loads are issued in every lane and on every path (lanes
   // past the tail re-read it; with no pages the rotation forms stand in), so
   // the compiler's waits count them exactly.
-  typedef typename std::conditional<(SB - 1024 > 256), u32x2, uint32_t>::type Tail;
-  constexpr int TB = sizeof(Tail), NT2 = (SB - 1024) / TB;  // tail lanes
+  typedef typename std::conditional<(SB - HB > 256), u32x2, uint32_t>::type Tail;
+  constexpr int TB = sizeof(Tail), NT2 = (SB - HB) / TB;  // tail lanes
   static_assert((NT2 & (NT2 - 1)) == 0 && NT2 <= 64, "tail: a power of two of lanes");
   typedef const __attribute__((address_space(1))) u32x4 *gp4;
   typedef const __attribute__((address_space(1))) Tail *gpt;
-  u32x4 preg[RP];
-  Tail ptail[RP];
+  u32x4 preg[RPB][NHB];
+  Tail ptail[RPB];
   auto issue_reg = [&](int i, bool on) {
     const uint8_t *blk = on ? page_block(i, i) : a.fk;
-    preg[i] = *(gp4)(blk + lane16);
-    ptail[i] = *(gpt)(blk + 1024u + TB * uint32_t(lane & (NT2 - 1)));
+#pragma unroll
+    for (int k = 0; k < NHB; ++k) preg[i][k] = *(gp4)(blk + 1024u * k + lane16);
+    ptail[i] = *(gpt)(blk + uint32_t(HB) + TB * uint32_t(lane & (NT2 - 1)));
   };
 
   // one page from the ring; PARTIAL: rows >= nvalid are absent (any bits)
   auto page = [&](const uint8_t *src, int nvalid, auto partial_tag) {
     constexpr bool PARTIAL = decltype(partial_tag)::value;
     const uint32_t base = lds_addr(src);
-    RingRead<vcode, kmeta, vmeta, POFF> rd;
-    rd.template load<NG>(base + 8 * lane, base + moff);
-    const u32x2 kc = rd.kc, vc = rd.vc;
+    typedef typename std::conditional<BITS == 2, RingRead<vcode, kmeta, vmeta, POFF>,
+                                      RingRead4<vcode, kmeta, vmeta, POFF>>::type Rd;
+    Rd rd;
+    rd.template load<NG>(base + (BITS == 2 ? 8 : 16) * lane, base + moff);
+    const auto kc = rd.kc, vc = rd.vc;
     const h2v km0 = as_h2(rd.km0), km1 = as_h2(rd.km1);
     const h2v vm0 = as_h2(rd.vm0), vm1 = as_h2(rd.vm1);
     const bool tok_ok = !PARTIAL || t < nvalid;
     // ---- scores (kq units)
     f16x8 kx[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) kx[kb] = ex.k(kc[0], kc[1], kb);
+    for (int kb = 0; kb < 4; ++kb) {
+      if constexpr (BITS == 2)
+        kx[kb] = ex.k(kc[0], kc[1], kb);
+      else
+        kx[kb] = ex4.k(kc[kb]);
+    }
     float S[NCH][SPL];
     bool up = false;
 #pragma unroll
@@ -965,13 +1038,18 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
 #pragma unroll
     for (int g = 0; g < NG; ++g) cacc[g] = mfma_v(ones, bp[g], cacc[g]);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) acc[r] = mfma_v(ex.v(vc[0], vc[1], r), bp[(16 * r) / G], acc[r]);
+    for (int r = 0; r < 8; ++r) {
+      if constexpr (BITS == 2)
+        acc[r] = mfma_v(ex.v(vc[0], vc[1], r), bp[(16 * r) / G], acc[r]);
+      else
+        acc[r] = mfma_v(ex4.v(vc[r >> 1], r & 1), bp[(16 * r) / G], acc[r]);
+    }
   };
 
   auto step = [&](int i, auto partial_tag) {
-    if (i + DEPTH - 1 < npw) issue(i + DEPTH - 1, (i + DEPTH - 1) % DEPTH);
-    wait_pages(min(DEPTH - 1, npw - 1 - i));
-    const int sl = i % DEPTH;
+    if (i + DP - 1 < npw) issue(i + DP - 1, (i + DP - 1) % DP);
+    wait_pages<IPP, DP - 1>(min(DP - 1, npw - 1 - i));
+    const int sl = i % DP;
     // tested as a per-lane value (the same in every lane): as a scalar branch
     // the compiler copies the accumulators at its merge point every page
     uint32_t okv = ok_slots;
@@ -989,13 +1067,14 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
     const int pid = __builtin_amdgcn_readlane(my_pid, i);
     const uint8_t *blk = c.hist + (int64_t(pid) * c.n_kv_heads + hk) * SB;
     uint8_t *dst = ring + sl * SB;
-    lds_copy16(blk + lane16, dst);
-    if (lane < N2) lds_copy16(blk + 1024u + lane16, dst + 1024);
+#pragma unroll
+    for (int k = 0; k < NHB; ++k) lds_copy16(blk + 1024u * k + lane16, dst + 1024 * k);
+    if (lane < N2) lds_copy16(blk + uint32_t(HB) + lane16, dst + HB);
   };
   auto step_fast = [&](int i, auto partial_tag) {
-    if (i + DEPTH - 1 < npw) issue_fast(i + DEPTH - 1, (i + DEPTH - 1) % DEPTH);
-    wait_pages(min(DEPTH - 1, npw - 1 - i));
-    page(ring + (i % DEPTH) * SB, nh - PAGE * (j0 + wave + AW * i), partial_tag);
+    if (i + DP - 1 < npw) issue_fast(i + DP - 1, (i + DP - 1) % DP);
+    wait_pages<IPP, DP - 1>(min(DP - 1, npw - 1 - i));
+    page(ring + (i % DP) * SB, nh - PAGE * (j0 + wave + AW * i), partial_tag);
   };
 
   // the page ids (loaded by the caller, with the loads of the q fragment
@@ -1005,19 +1084,20 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
   my_pid = pid_pre;
   asm volatile("" : "+v"(my_pid));
 #pragma unroll
-  for (int i = 0; i < RP; ++i) issue_reg(i, any_pages);
+  for (int i = 0; i < RPB; ++i) issue_reg(i, any_pages);
   prep();
   // stored on every path, used or not: a load still in flight into a
   // register at the loop entry would make the compiler wait for every load
   // in flight (the prefetched pages) wherever the loop reuses that register
 #pragma unroll
-  for (int i = 0; i < RP; ++i) {
-    *reinterpret_cast<u32x4 *>(ring + i * SB + lane16) = preg[i];
-    if (lane < NT2) *reinterpret_cast<Tail *>(ring + i * SB + 1024u + TB * lane) = ptail[i];
+  for (int i = 0; i < RPB; ++i) {
+#pragma unroll
+    for (int k = 0; k < NHB; ++k) *reinterpret_cast<u32x4 *>(ring + i * SB + 1024u * k + lane16) = preg[i][k];
+    if (lane < NT2) *reinterpret_cast<Tail *>(ring + i * SB + uint32_t(HB) + TB * lane) = ptail[i];
   }
   // the rest of the ring fills by direct copies from here
   if (any_pages)
-    for (int i = RP; i < DEPTH - 1 && i < npw; ++i) issue(i, i);
+    for (int i = RPB; i < DP - 1 && i < npw; ++i) issue(i, i);
 #pragma unroll
   for (int r = 0; r < 8; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1394,7 +1474,7 @@ __global__ void __launch_bounds__(merge_threads<GQA>()) merge_kernel(StepArgs a)
 template <int GQA, int NG>
 constexpr int attend_waves() { return (GQA <= 4 && NG <= 2) ? 4 : 1; }
 
-template <int GQA, int NG, bool FUSED>
+template <int GQA, int NG, bool FUSED, int BITS>
 __global__ void __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(attend_waves<GQA, NG>())))
 attend_kernel(StepArgs a) {
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
@@ -1420,8 +1500,8 @@ attend_kernel(StepArgs a) {
   asm volatile("" ::: "memory");
   const int L = append ? L0 + 1 : L0;
   // per wave: its page ring, reused for its o[GQA][128] once the pages are done
-  constexpr int SB = hist_block_bytes(D / NG);
-  constexpr int WREG = DEPTH * SB > GQA * D * 4 ? DEPTH * SB : GQA * D * 4;
+  constexpr int SB = hist_block_bytes(D / NG, BITS);
+  constexpr int WREG = depth_of<BITS>() * SB > GQA * D * 4 ? depth_of<BITS>() * SB : GQA * D * 4;
   __shared__ __attribute__((aligned(16))) uint8_t wave_lds[AW * WREG];
   __shared__ float ml_lds[2 * AW * GQA];
   __shared__ float zs_lds[AW * GQA * NG];  // per wave: z sums per (head, group)
@@ -1483,24 +1563,27 @@ attend_kernel(StepArgs a) {
       st.compute(ld, valid, lane);
     }
     st.finish(o_w, m_lds + wave * GQA, l_lds + wave * GQA, lane);
-    if (append && ap.evict && ap.raw_page >= 0) {
-      const int pid = c.hist_pt[int64_t(b) * c.hist_pt_stride + ap.evict_j];
-      uint8_t *blk = nullptr;
-      if (pid >= 0 && pid < c.n_hist_pages)
-        blk = c.hist + (int64_t(pid) * c.n_kv_heads + hk) * hist_block_bytes(D / NG);
-      else if (tid == 0)
-        flag_status(c.status, OSCAR_STATUS_BAD_PAGE);
-      evict_token<GQA, D / NG>(a, b, hk, tid, wave, ap, blk, work.e);
-      extra = true;
+    // (appends reach only INT2 caches: the host refuses them for INT4)
+    if constexpr (BITS == 2) {
+      if (append && ap.evict && ap.raw_page >= 0) {
+        const int pid = c.hist_pt[int64_t(b) * c.hist_pt_stride + ap.evict_j];
+        uint8_t *blk = nullptr;
+        if (pid >= 0 && pid < c.n_hist_pages)
+          blk = c.hist + (int64_t(pid) * c.n_kv_heads + hk) * hist_block_bytes(D / NG);
+        else if (tid == 0)
+          flag_status(c.status, OSCAR_STATUS_BAD_PAGE);
+        evict_token<GQA, D / NG>(a, b, hk, tid, wave, ap, blk, work.e);
+        extra = true;
+      }
     }
   } else {
     // the newest history token has just left the recent window in an
     // append: the raw workgroup attends it
     const int nh = n_hist_tokens(L) - (append && L0 >= N_RAW ? 1 : 0);
     const int j1 = min((nh + PAGE - 1) / PAGE, j0 + a.pages_per_split);
-    auto prep = [&] { build_q<GQA, NG>(a, tid, work.q, frag_lds, ql); };
+    auto prep = [&] { build_q<GQA, NG, BITS>(a, tid, work.q, frag_lds, ql); };
     // every wave of the workgroup calls this (it holds workgroup barriers)
-    history_wave<GQA, NG>(a, b, hk, nh, j0, j1, wave, lane, pid_pre, prep, frag_lds, wave_lds + wave * WREG,
+    history_wave<GQA, NG, BITS>(a, b, hk, nh, j0, j1, wave, lane, pid_pre, prep, frag_lds, wave_lds + wave * WREG,
                           zs_lds + wave * GQA * NG, o_w, m_lds + wave * GQA, l_lds + wave * GQA);
   }
   const int64_t head_stride = int64_t(a.part_slots) * PART_STRIDE;
@@ -1555,28 +1638,34 @@ attend_kernel(StepArgs a) {
 
 // ------------------------------------------------------------------ launch
 
-template <int GQA, int NG>
+template <int GQA, int NG, int BITS>
 static hipError_t launch_t(const StepArgs &a, bool fused, int batch, int hkv, hipStream_t s) {
   const KernelEvents ev = take_profile_events();
   const dim3 grid(1 + a.n_splits, hkv, batch);
   if (fused) {
-    hipExtLaunchKernelGGL((attend_kernel<GQA, NG, true>), grid, dim3(AW * 64), 0, s, ev.before, ev.after, 0, a);
+    hipExtLaunchKernelGGL((attend_kernel<GQA, NG, true, BITS>), grid, dim3(AW * 64), 0, s, ev.before, ev.after, 0, a);
     return hipGetLastError();
   }
-  hipExtLaunchKernelGGL((attend_kernel<GQA, NG, false>), grid, dim3(AW * 64), 0, s, ev.before, ev.after, 0, a);
+  hipExtLaunchKernelGGL((attend_kernel<GQA, NG, false, BITS>), grid, dim3(AW * 64), 0, s, ev.before, ev.after, 0, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((merge_kernel<GQA>), dim3(hkv, batch), dim3(merge_threads<GQA>()), 0, s, a);
   return hipGetLastError();
 }
 
+template <int GQA, int BITS>
+static hipError_t launch_gb(const StepArgs &a, bool fused, int G, int batch, int hkv, hipStream_t s) {
+  switch (G) {
+    case 32: return launch_t<GQA, 4, BITS>(a, fused, batch, hkv, s);
+    case 64: return launch_t<GQA, 2, BITS>(a, fused, batch, hkv, s);
+    default: return launch_t<GQA, 1, BITS>(a, fused, batch, hkv, s);
+  }
+}
+
 template <int GQA>
 static hipError_t launch_g(const StepArgs &a, bool fused, int G, int batch, int hkv, hipStream_t s) {
-  switch (G) {
-    case 32: return launch_t<GQA, 4>(a, fused, batch, hkv, s);
-    case 64: return launch_t<GQA, 2>(a, fused, batch, hkv, s);
-    default: return launch_t<GQA, 1>(a, fused, batch, hkv, s);
-  }
+  return cache_bits(a.c) == 4 ? launch_gb<GQA, 4>(a, fused, G, batch, hkv, s)
+                              : launch_gb<GQA, 2>(a, fused, G, batch, hkv, s);
 }
 
 static float pv_scale_for(float clip_v) {
@@ -1612,6 +1701,7 @@ hipError_t launch_decode_step(const oscar_layer_cache &c, RotArg rk, RotArg rv, 
   a.ex_m4 = 0x03000300u;
   a.ex_m16 = 0x00C000C0u;
   a.ex_e = 0x3C003C00u;
+  a.ex_mn = 0x03C003C0u;
   a.pk01 = std::log2(4.f * a.pv_scale);
   a.pk23 = std::log2(16.f * a.pv_scale);
   const SplitPlan p = plan_int2_splits(batch, c.n_kv_heads, max_seq_len);

@@ -1,5 +1,5 @@
-// Fused KV write: rotate, clip, INT2-pack and page-store history tokens; store
-// sink / recent tokens raw.  OSCAR online phase (gist.science nl/fr technical
+// Fused KV write: rotate, clip, INT2- (or INT4-) pack and page-store history
+// tokens; store sink / recent tokens raw.  OSCAR online phase (gist.science nl/fr technical
 // summaries, section 2.2.B: history kept as INT2 after the fixed rotation and
 // clipping, sink and recent tokens in BF16; arXiv:2605.17757 v2 abstract:
 // fused write kernel over a paged cache).
@@ -96,6 +96,16 @@ __device__ inline uint32_t pack16(uint32_t w0, uint32_t w1, uint32_t w2, uint32_
   return p0 | (p2 << 2) | (p4 << 4) | (p6 << 6);
 }
 
+// One INT4 code dword from eight code bytes x0 (codes a0..a3), x1 (b0..b3):
+// nibbles 0..7 = a0, a2, b0, b2, a1, a3, b1, b3.  For K, x0 / x1 are channels
+// j = 0..3 / 4..7 of a token (nibble e then holds channel 2 (e % 4) + e / 4);
+// for V, rows 0..3 of channel 16 (2d) + m / 16 (2d + 1) + m.  x | x >> 12
+// puts a0 | a2 << 4 in byte 0 and a1 | a3 << 4 in byte 1 (codes < 16).
+__device__ inline uint32_t pack8(uint32_t x0, uint32_t x1) {
+  const uint32_t e0 = x0 | (x0 >> 12), e1 = x1 | (x1 >> 12);
+  return __builtin_amdgcn_perm(e1, e0, 0x05010400u);
+}
+
 // K code rows in LDS: 136 bytes apart (34 dwords), so the 16 tokens of a
 // row-group write and read distinct banks
 constexpr int KROW = D + 8;
@@ -155,9 +165,11 @@ __device__ inline void token_source(const WriteArgs &a, int ids, int tensor, int
 // meta (kept in the other LDS buffer) are stored, then page j is computed.
 // The next wait for loads comes at page j+1's staging, a whole page later.
 // All page ids of the workgroup are loaded once, into lanes of one register.
-template <int G, int TENSOR>
+template <int G, int TENSOR, int BITS>
 __device__ __forceinline__ void write_hist_body(const WriteArgs &a, WriteShared<G> &sh) {
   constexpr int NG = D / G, WPG = G / 32;
+  constexpr int LEVELS = (1 << BITS) - 1;     // highest code
+  constexpr uint32_t CMASK = 0x01010101u * LEVELS;  // one code per byte
   // workgroup and work-item ids through the builtins: in an inlined body,
   // blockIdx / threadIdx may become calls that return vector registers
   const int bx = __builtin_amdgcn_workgroup_id_x(), by = __builtin_amdgcn_workgroup_id_y();
@@ -253,12 +265,15 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a, WriteShared<
   }
 
   // ---- packed store of a computed page (codes and meta in LDS buffer buf):
-  // 128 code dwords per head, then the meta entries.  K dword (token t, q,
-  // d): channels 64d + 8q .. +7 and 64d + 32 + 8q .. +7 of token t; V dword
-  // (q, m, d): tokens 4q .. 4q+3 of channels 16 (4d + r) + m, r < 4.  Rows
+  // the code dwords of each head (INT2: 128, one per thread; INT4: 256, two
+  // per thread), then the meta entries.  INT2 K dword (token t, q, d):
+  // channels 64d + 8q .. +7 and 64d + 32 + 8q .. +7 of token t; V dword
+  // (q, m, d): tokens 4q .. 4q+3 of channels 16 (4d + r) + m, r < 4.  INT4 K
+  // dword (t, q, i): channels 32i + 8q .. +7 of token t; V dword (q, m, i):
+  // tokens 4q .. 4q+3 of channels 16 (2i) + m and 16 (2i + 1) + m.  Rows
   // below hlo are already in history and are kept (read-modify-write); rows
   // at or past hhi are not yet and may be overwritten.
-  const int hbb = hist_block_bytes(G);
+  const int hbb = hist_block_bytes(G, BITS);
   // Heads are wave-uniform (waves 2i, 2i+1 take head 2k + i of the codes,
   // wave w head w of the meta), so block addresses stay scalar.
   auto store_page = [&](int pid, int pos0, int buf) {
@@ -268,7 +283,44 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a, WriteShared<
       const int w = tid & 127;
       const int ln = w >> 1, d = w & 1, lq = ln >> 4, la = ln & 15;
       uint8_t *blk = c.hist + (int64_t(pid) * hkv + h0 + hh) * hbb;
-      if constexpr (tensor == 0) {
+      if constexpr (BITS == 4) {
+        // dwords 4 ln + 2 d and 4 ln + 2 d + 1 of the head's code area
+        if constexpr (tensor == 0) {
+          const int t = la, p = pos0 + t;
+          if (p < hlo || p >= hhi) continue;
+          const uint8_t *src = &sh.codes[buf][hh][t * KROW + 64 * d + 8 * lq];
+          const u32x2w x0 = *reinterpret_cast<const u32x2w *>(src);
+          const u32x2w x1 = *reinterpret_cast<const u32x2w *>(src + 32);
+          reinterpret_cast<u32x2w *>(blk + k_codes_off(G, 4))[w] = u32x2w{pack8(x0[0], x0[1]), pack8(x1[0], x1[1])};
+        } else {
+          uint32_t keep = 0, on = 0;  // code bytes of kept / written tokens 4lq + byte
+#pragma unroll
+          for (int by = 0; by < 4; ++by) {
+            const int p = pos0 + 4 * lq + by;
+            if (p < hlo) keep |= 0x0Fu << (8 * by);
+            else if (p < hhi) on |= 0x0Fu << (8 * by);
+          }
+          if (!on) continue;
+          uint32_t word[2];
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const int i = 2 * d + s2;
+            const uint32_t xa =
+                *reinterpret_cast<const uint32_t *>(&sh.codes[buf][hh][(16 * (2 * i) + la) * PAGE + 4 * lq]) & on;
+            const uint32_t xb =
+                *reinterpret_cast<const uint32_t *>(&sh.codes[buf][hh][(16 * (2 * i + 1) + la) * PAGE + 4 * lq]) & on;
+            word[s2] = pack8(xa, xb);
+          }
+          u32x2w *dst = reinterpret_cast<u32x2w *>(blk + v_codes_off(G, 4)) + w;
+          if (keep) {
+            const uint32_t km = pack8(keep, keep);
+            const u32x2w old = *dst;
+            *dst = u32x2w{(old[0] & km) | word[0], (old[1] & km) | word[1]};
+          } else {
+            *dst = u32x2w{word[0], word[1]};
+          }
+        }
+      } else if constexpr (tensor == 0) {
         const int t = la, p = pos0 + t;
         if (p < hlo || p >= hhi) continue;
         const uint8_t *src = &sh.codes[buf][hh][t * KROW + 64 * d + 8 * lq];
@@ -303,7 +355,7 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a, WriteShared<
       const int p = pos0 + t;
       if (p >= hlo && p < hhi) {
         uint8_t *blk = c.hist + (int64_t(pid) * hkv + h0 + hh) * hbb;
-        __half2 *meta = reinterpret_cast<__half2 *>(blk + (tensor ? v_meta_off(G) : k_meta_off(G)));
+        __half2 *meta = reinterpret_cast<__half2 *>(blk + (tensor ? v_meta_off(G, BITS) : k_meta_off(G, BITS)));
         meta[PAGE * gg + t] =
             __halves2half2(__float2half_rn(sh.sz[buf][hh][gg][t][0]), __float2half_rn(sh.sz[buf][hh][gg][t][1]));
       }
@@ -381,10 +433,10 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a, WriteShared<
         hi = lanes4_max(hi) * (1.0f / 2048.0f);
       };
       auto quantise = [&](int hh, const f32x4w (&yc)[2], float lo, float hi) {
-        // (max - min) / 3 by a product with fp32(1/3) and the code step by a
-        // hardware reciprocal: each within two fp32 ulps, far inside the
-        // error bound of the rotated values they come from
-        const float sq = __half2float(__float2half_rn((hi - lo) * (1.0f / 3.0f)));
+        // (max - min) / LEVELS by a product with fp32(1 / LEVELS) and the
+        // code step by a hardware reciprocal: each within three fp32 ulps,
+        // far inside the error bound of the rotated values they come from
+        const float sq = __half2float(__float2half_rn((hi - lo) * (1.0f / float(LEVELS))));
         const float zq = __half2float(__float2half_rn(lo));
         szv[hh][0] = sq;
         szv[hh][1] = zq;
@@ -406,7 +458,7 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a, WriteShared<
             const float d = yc[ct][i] - zs;
             const float t0 = d * inv;
             const float t = fmaf(fmaf(-t0, ss, d), inv, t0);
-            cd[i] = __float_as_uint(__builtin_amdgcn_fmed3f(t, 0.f, 3.f) + 12582912.0f);
+            cd[i] = __float_as_uint(__builtin_amdgcn_fmed3f(t, 0.f, float(LEVELS)) + 12582912.0f);
           }
           const int ch = 32 * wave + 16 * ct + 4 * qd;
           // the four codes (channels ch .. ch+3 of the lane's token) as bytes
@@ -497,21 +549,21 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a, WriteShared<
 // min / max partials held across a barrier); wider groups keep two.
 // K and V workgroups (the low bit of blockIdx.y) run separate instances of
 // the body, so the tensor's branches are resolved at compile time.
-template <int G>
+template <int G, int BITS>
 __global__ void __launch_bounds__(256) write_hist_kernel(WriteArgs a) {
   __shared__ __attribute__((aligned(16))) WriteShared<G> sh;
   if (__builtin_amdgcn_workgroup_id_y() & 1)
-    write_hist_body<G, 1>(a, sh);
+    write_hist_body<G, 1, BITS>(a, sh);
   else
-    write_hist_body<G, 0>(a, sh);
+    write_hist_body<G, 0, BITS>(a, sh);
 }
-template <>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) write_hist_kernel<32>(WriteArgs a) {
+template <int BITS>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) write_hist_kernel_g32(WriteArgs a) {
   __shared__ __attribute__((aligned(16))) WriteShared<32> sh;
   if (__builtin_amdgcn_workgroup_id_y() & 1)
-    write_hist_body<32, 1>(a, sh);
+    write_hist_body<32, 1, BITS>(a, sh);
   else
-    write_hist_body<32, 0>(a, sh);
+    write_hist_body<32, 0, BITS>(a, sh);
 }
 
 // New tokens that land in the sink or the recent ring: raw bf16 copies.
@@ -571,11 +623,14 @@ hipError_t launch_write_kv(const oscar_layer_cache &c, RotArg rk, RotArg rv,
   const int tiles = (max_new + PAGE - 1) / PAGE + 2;
   const dim3 grid((tiles + WPP - 1) / WPP, 2 * ((c.n_kv_heads + WHC - 1) / WHC), batch);
   const KernelEvents ev = take_profile_events();
+  const bool int4 = cache_bits(c) == 4;
+#define OSCAR_WRITE_LAUNCH(K_) hipExtLaunchKernelGGL((K_), grid, dim3(256), 0, s, ev.before, ev.after, 0, a)
   switch (c.group) {
-    case 32: hipExtLaunchKernelGGL(write_hist_kernel<32>, grid, dim3(256), 0, s, ev.before, ev.after, 0, a); break;
-    case 64: hipExtLaunchKernelGGL(write_hist_kernel<64>, grid, dim3(256), 0, s, ev.before, ev.after, 0, a); break;
-    default: hipExtLaunchKernelGGL(write_hist_kernel<128>, grid, dim3(256), 0, s, ev.before, ev.after, 0, a); break;
+    case 32: if (int4) OSCAR_WRITE_LAUNCH(write_hist_kernel_g32<4>); else OSCAR_WRITE_LAUNCH(write_hist_kernel_g32<2>); break;
+    case 64: if (int4) OSCAR_WRITE_LAUNCH((write_hist_kernel<64, 4>)); else OSCAR_WRITE_LAUNCH((write_hist_kernel<64, 2>)); break;
+    default: if (int4) OSCAR_WRITE_LAUNCH((write_hist_kernel<128, 4>)); else OSCAR_WRITE_LAUNCH((write_hist_kernel<128, 2>)); break;
   }
+#undef OSCAR_WRITE_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(write_raw_kernel, dim3(N_SINK + N_RECENT, batch), dim3(256), 0, s, a);

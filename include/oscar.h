@@ -87,11 +87,12 @@ enum {
  * BF16 pool: uint16 (bf16 bits) [n_bf16_pages][Hkv][2][16][128]; index 0 of
  * the "2" axis is K, 1 is V.  Rows hold raw, unrotated vectors.
  *
- * History pool: uint8 [n_hist_pages][Hkv][B_hist(G)], one block per
+ * History pool: uint8 [n_hist_pages][Hkv][B_hist(G, bits)], one block per
  * (page, KV head):
- *     [ K codes 512 B | K meta 64*NG B | V codes 512 B | V meta 64*NG B ]
- *   NG = 128/G groups; B_hist(G) = 1024 + 128*NG  (1536, 1280, 1152 B for
- *   G = 32, 64, 128).
+ *     [ K codes A B | K meta 64*NG B | V codes A B | V meta 64*NG B ]
+ *   NG = 128/G groups; A = 512 B for INT2 codes (code_bits 2), 1024 B for
+ *   INT4 (code_bits 4); B_hist = 2A + 128*NG  (INT2: 1536, 1280, 1152 B,
+ *   INT4: 2560, 2304, 2176 B for G = 32, 64, 128).
  *
  * Meta: entry (group g, row t) at byte 4*(16*g + t) of the meta area:
  *   fp16 scale s at +0, fp16 zero z at +2.  Dequantised value of a code c:
@@ -114,6 +115,17 @@ enum {
  * AND-OR each (after at most one shift), in exactly the register order the
  * gfx950 matrix-core instructions read: K as 16x16x32 operands (16 tokens,
  * 32 channels per block), V as 16x16x16 operands (16 channels x 16 tokens).
+ *
+ * INT4 codes (code_bits 4): 4-bit values 0..15, asymmetric min-max over 15
+ * steps (the INT4 comparison point of [nl] §4 / [fr] §4), meta as above.  A
+ * code area is 256 dwords; lane l = w/4 owns dwords 4l..4l+3 (i = w%4), with
+ * a = l%16, q = l/16; nibble e (0..7) of a dword sits at bits 4e..4e+3.
+ *   K: a = row (token) t; dword i holds channels 32i + 8q + j of token t,
+ *      channel offset j = 2*(e%4) + e/4 in nibble e.
+ *   V: a = channel offset m; dword i holds channels 16*(2i + h) + m, h =
+ *      (e/2)%2, rows 4q + k, k = 2*(e%2) + e/4, in nibble e.
+ * Nibbles e and e+4 hold neighbouring channels (K) or rows (V), so one
+ * shift and one AND-OR place them in the two halves of an fp16 pair.
  * ------------------------------------------------------------------------- */
 
 typedef struct oscar_layer_cache {
@@ -127,6 +139,8 @@ typedef struct oscar_layer_cache {
   int32_t hist_pt_stride;  /* >= history pages of the longest request       */
   const int32_t *bf16_pt;  /* device int32 [batch][9]                        */
   uint32_t *status;        /* device, may be NULL: OSCAR_STATUS_* bits       */
+  int32_t code_bits;       /* history code width: 2 (INT2; 0 also means 2)
+                              or 4 (INT4: write and decode_attn only)      */
 } oscar_layer_cache;
 
 /* Device forms of one fixed per-layer rotation R = U*H*P ([nl] §2.2.A
@@ -141,8 +155,12 @@ typedef struct oscar_rotation {
 OSCAR_API const char *oscar_last_error(void);
 OSCAR_API const char *oscar_version(void);
 
-/* Bytes of one history block for group size G (0 if G is unsupported). */
+/* Bytes of one INT2 history block for group size G (0 if G is unsupported). */
 OSCAR_API size_t oscar_hist_block_bytes(int32_t group);
+
+/* Bytes of one history block for group size G and code width code_bits
+ * (2 or 4); 0 if either is unsupported. */
+OSCAR_API size_t oscar_hist_block_bytes_bits(int32_t group, int32_t code_bits);
 
 /* Bytes of the device buffer that holds the forms of one rotation. */
 OSCAR_API size_t oscar_rotation_bytes(void);
@@ -246,7 +264,8 @@ OSCAR_API int oscar_calibrate_rotation(const uint16_t *q_cal, const uint16_t *k_
  * ring tokens pushed out by this call, are rotated by R (x*R), clamped to
  * [-clip, clip], split into groups of G consecutive rotated channels, and
  * stored as codes c = clamp(rint((x - z)/s), 0, 3) with z = fp16(min),
- * s = fp16((max - min)/3) (all codes 0 when s == 0).  The rotation keeps
+ * s = fp16((max - min)/3) (all codes 0 when s == 0); with code_bits 4 the
+ * same over 15 steps: c in 0..15, s = fp16((max - min)/15).  The rotation keeps
  * fp32 dot-product accuracy with fp16 operands on the matrix cores: entries
  * of k_new / v_new beyond the fp16 range (|x| > 65504) are saturated to
  * +-65504 before rotating.
@@ -280,7 +299,8 @@ OSCAR_API size_t oscar_decode_workspace_bytes(int32_t batch, int32_t n_q_heads,
  * KV head h / (Hq/Hkv).
  * q: device bf16 [batch][Hq][128]; seq_lens: device int32 [batch], each in
  * [1, max_seq_len]; out: device fp32 [batch][Hq][128]; workspace: see
- * oscar_decode_workspace_bytes (zero-filled before its first use). */
+ * oscar_decode_workspace_bytes (zero-filled before its first use).  Reads
+ * INT2 or INT4 history (cache->code_bits). */
 OSCAR_API int oscar_decode_attn(const oscar_layer_cache *cache,
                       const oscar_rotation *rot_k, const oscar_rotation *rot_v,
                       const uint16_t *q, int32_t n_q_heads,
@@ -320,7 +340,8 @@ OSCAR_API int oscar_decode_attn_noalloc(const oscar_layer_cache *cache,
  * must be <= max_seq_len.  Same result as oscar_write_kv with one token per
  * request followed by oscar_decode_attn, in one kernel launch.  The
  * workspace is the one of oscar_decode_attn (oscar_decode_workspace_bytes,
- * zero-filled before its first use). */
+ * zero-filled before its first use).  INT2 caches only (code_bits 4:
+ * OSCAR_EUNSUPPORTED). */
 OSCAR_API int oscar_decode_step(const oscar_layer_cache *cache,
                                 const oscar_rotation *rot_k,
                                 const oscar_rotation *rot_v,
@@ -348,7 +369,7 @@ OSCAR_API int oscar_decode_step(const oscar_layer_cache *cache,
  * [total_tokens][Hq][128].  Needs no workspace.  A request whose length or
  * chunk is out of range sets OSCAR_STATUS_BAD_LEN and leaves its rows
  * unwritten; a page id out of range sets OSCAR_STATUS_BAD_PAGE and that
- * page is left out. */
+ * page is left out.  INT2 caches only (code_bits 4: OSCAR_EUNSUPPORTED). */
 OSCAR_API int oscar_extend_attn(const oscar_layer_cache *cache,
                                 const oscar_rotation *rot_k,
                                 const oscar_rotation *rot_v,

@@ -19,6 +19,12 @@ Write parity (two levels):
   2. codes equal the oracle's codes recomputed with the GPU's scale and zero,
      except where the oracle's t = (xc - z)/s lies within 1e-4 code units of
      a rounding boundary k + 1/2; at most 1e-5 of all codes may differ.
+INT4 history (15 steps per group instead of 3): the same rules with the
+scale's bound divided by 15 (the kernel multiplies by fp32(1/15), which
+carries one more rounding of up to one ulp than fp32(1/3): three roundings
+of (max - min)/15 instead of two) and a code band 5 times wider, since a
+step 5 times smaller turns the same rotation error into 5 times as many
+code units.
 Decode parity: max |gpu - oracle| <= 2e-2 and ||gpu - oracle||_2 /
 ||oracle||_2 <= 5e-3 over all (request, head, channel).
 """
@@ -84,12 +90,16 @@ def _f16_neighbours_ok(gpu: np.ndarray, ref: np.ndarray, unrounded: np.ndarray, 
 
 
 def compare_history(gpu_hist: np.ndarray, hist_pt: np.ndarray, tokens_k, tokens_v, lens,
-                    R_K, R_V, clip_k, clip_v, G: int, positions=None) -> dict:
+                    R_K, R_V, clip_k, clip_v, G: int, positions=None, bits: int = 2) -> dict:
     """Two-level comparison of every history row of every request.
 
     tokens_k/v[b]: bf16 bits [L_b][Hkv][128] of request b (all positions).
     positions[b] (optional): subset of history positions to check.
+    bits: code width of the pool (2 or 4).
     """
+    steps = float(o.levels(bits))
+    band = CODE_BAND * steps / 3.0
+    n_round = 2 if bits == 2 else 3
     stats = {"codes": 0, "raw_code_mismatch": 0, "code_out_of_band": 0, "meta": 0,
              "meta_differ": 0, "meta_out_of_tol": 0}
     hkv = gpu_hist.shape[1]
@@ -105,9 +115,9 @@ def compare_history(gpu_hist: np.ndarray, hist_pt: np.ndarray, tokens_k, tokens_
         for kind, toks, R, clip in (("K", tokens_k[b], R_K, clip_k), ("V", tokens_v[b], R_V, clip_v)):
             for h in range(hkv):
                 x = o.bf16_to_f64(toks[hist_p, h, :])
-                q = o.quantize(x, R, clip, G)
-                areas = o.split_block(gpu_hist[pids, h], G)
-                codes_all = o.unpack_codes(areas[kind.lower() + "_codes"], kind)   # [n][16][128]
+                q = o.quantize(x, R, clip, G, bits)
+                areas = o.split_block(gpu_hist[pids, h], G, bits)
+                codes_all = o.unpack_codes(areas[kind.lower() + "_codes"], kind, bits)   # [n][16][128]
                 s_all, z_all = o.unpack_meta(areas[kind.lower() + "_meta"], G)
                 ar = np.arange(len(rows))
                 gc, gs, gz = codes_all[ar, rows], s_all[ar, rows], z_all[ar, rows]
@@ -117,15 +127,15 @@ def compare_history(gpu_hist: np.ndarray, hist_pt: np.ndarray, tokens_k, tokens_
                 err = (ROT_BOUND * (np.abs(x) @ np.abs(R))).reshape(-1, ng, G).max(axis=2)
                 u = 2.0 ** -24
                 ok_z = _f16_neighbours_ok(gz, q["zero"], lo, err)
-                ok_s = _f16_neighbours_ok(gs, q["scale"], (hi - lo) / 3.0,
-                                          (2 * err + u * (hi - lo)) / 3.0 + u * (hi - lo) / 3.0)
+                ok_s = _f16_neighbours_ok(gs, q["scale"], (hi - lo) / steps,
+                                          (2 * err + u * (hi - lo)) / steps + (n_round - 1) * u * (hi - lo) / steps)
                 stats["meta"] += 2 * gs.size
                 stats["meta_differ"] += int((gs != q["scale"]).sum() + (gz != q["zero"]).sum())
                 stats["meta_out_of_tol"] += int((~ok_s).sum() + (~ok_z).sum())
-                ref_codes, t = o.codes_from_meta(q["xc"], gs, gz, G)
+                ref_codes, t = o.codes_from_meta(q["xc"], gs, gz, G, bits)
                 diff = gc != ref_codes
                 frac = t - np.floor(t)
-                near = np.abs(frac - 0.5) < CODE_BAND
+                near = np.abs(frac - 0.5) < band
                 stats["codes"] += gc.size
                 stats["raw_code_mismatch"] += int((gc != q["codes"]).sum())
                 stats["code_out_of_band"] += int((diff & ~np.nan_to_num(near, nan=False)).sum())
@@ -154,8 +164,8 @@ class Scenario:
     """Seeded requests written by the oracle (numpy pools) with shuffled page tables."""
 
     def __init__(self, seed: int, hq: int, hkv: int, G: int, lens, rot="random", n_cal=2048, layer=0,
-                 spare_pages=3, dense_q=False):
-        self.seed, self.hq, self.hkv, self.G = seed, hq, hkv, G
+                 spare_pages=3, dense_q=False, bits=2):
+        self.seed, self.hq, self.hkv, self.G, self.bits = seed, hq, hkv, G, bits
         self.lens = [int(x) for x in lens]
         self.ld = synth.LayerData(seed, layer, hq, hkv, dense_q=dense_q)
         if rot == "calibrated":
@@ -185,7 +195,8 @@ class Scenario:
         self.q = self.ld.decode_q(len(self.lens))
 
     def oracle_cache(self, chunks=None) -> o.LayerCacheRef:
-        ref = o.LayerCacheRef(self.hkv, self.G, self.n_hist_pages, self.n_bf16_pages, self.hist_pt, self.bf16_pt)
+        ref = o.LayerCacheRef(self.hkv, self.G, self.n_hist_pages, self.n_bf16_pages, self.hist_pt, self.bf16_pt,
+                              bits=self.bits)
         for cu, lb, k, v in self.write_calls(chunks):
             ref.write(self.R_K, self.R_V, self.clip_k, self.clip_v, k, v, cu, lb)
         return ref

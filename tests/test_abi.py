@@ -50,12 +50,13 @@ def test_struct_layout_matches_c():
     #include <stddef.h>
     #include "oscar.h"
     int main(void) {
-      printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(oscar_layer_cache),
+      printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(oscar_layer_cache),
         offsetof(oscar_layer_cache, group), offsetof(oscar_layer_cache, hist),
         offsetof(oscar_layer_cache, n_hist_pages), offsetof(oscar_layer_cache, bf16),
         offsetof(oscar_layer_cache, n_bf16_pages), offsetof(oscar_layer_cache, hist_pt),
         offsetof(oscar_layer_cache, hist_pt_stride), offsetof(oscar_layer_cache, bf16_pt),
-        offsetof(oscar_layer_cache, status), sizeof(oscar_rotation));
+        offsetof(oscar_layer_cache, status), offsetof(oscar_layer_cache, code_bits),
+        sizeof(oscar_rotation));
       return 0;
     }
     """
@@ -68,13 +69,15 @@ def test_struct_layout_matches_c():
     L = _lib.LayerCacheC
     expect = [ctypes.sizeof(L), L.group.offset, L.hist.offset, L.n_hist_pages.offset, L.bf16.offset,
               L.n_bf16_pages.offset, L.hist_pt.offset, L.hist_pt_stride.offset, L.bf16_pt.offset,
-              L.status.offset, ctypes.sizeof(_lib.RotationC)]
+              L.status.offset, L.code_bits.offset, ctypes.sizeof(_lib.RotationC)]
     assert vals == expect
 
 
 def test_sizes():
     assert [oscar.hist_block_bytes(g) for g in (32, 64, 128)] == [1536, 1280, 1152]
     assert oscar.hist_block_bytes(48) == 0
+    assert [oscar.hist_block_bytes(g, 4) for g in (32, 64, 128)] == [2560, 2304, 2176]
+    assert oscar.hist_block_bytes(32, 3) == 0 and oscar.hist_block_bytes(32, 8) == 0
     assert oscar.rotation_bytes() == 196608
     assert oscar.decode_workspace_bytes(1, 32, 8, 32768) > 0
     assert oscar.decode_workspace_bytes(0, 32, 8, 32768) == 0
@@ -226,6 +229,7 @@ def test_extend_validation_codes():
                                      cu, 0x9000, batch, total, max_new, max_prefix, scale, 0xD000, None)
     assert call(hq=6) == E.OSCAR_EUNSUPPORTED
     assert call(c=_cache(group=48)) == E.OSCAR_EUNSUPPORTED
+    assert call(c=_cache(code_bits=4)) == E.OSCAR_EUNSUPPORTED and "INT2 caches only" in _err()
     assert call(batch=0) == E.OSCAR_EINVAL
     assert call(max_new=32, total=16) == E.OSCAR_EINVAL
     assert call(max_prefix=-1) == E.OSCAR_EINVAL
@@ -270,3 +274,22 @@ def test_decode_noalloc_validation_codes():
     assert _decode_noalloc(c=big, batch=300, max_len=60000) == E.OSCAR_EWORKSPACE
     if NO_GPU:
         assert _decode_noalloc() == E.OSCAR_ENODEV
+
+
+def test_code_bits_validation():
+    E = _lib
+    # INT2 (0 or 2) and INT4 caches pass the cache checks of write and
+    # decode (valid arguments are only sent where no device can run them)
+    if NO_GPU:
+        for bits in (0, 2, 4):
+            assert _write(c=_cache(code_bits=bits)) == E.OSCAR_ENODEV, (bits, _err())
+            assert _decode(c=_cache(code_bits=bits)) == E.OSCAR_ENODEV, (bits, _err())
+    for bits in (1, 3, 8, -2):
+        assert _write(c=_cache(code_bits=bits)) == E.OSCAR_EUNSUPPORTED and "code_bits" in _err()
+        assert _decode(c=_cache(code_bits=bits)) == E.OSCAR_EUNSUPPORTED
+    # the append step handles INT2 caches only
+    lib = _lib.load()
+    c = _cache(code_bits=4)
+    rc = lib.oscar_decode_step(ctypes.byref(c), ctypes.byref(ROT), ctypes.byref(ROT), 0x6000, 0x7000, 0x9000, 0xB000,
+                               8, 1, 150, 0.088, 0xD000, 0xA000, 1 << 30, None)
+    assert rc == E.OSCAR_EUNSUPPORTED and "INT2 caches only" in _err()

@@ -31,7 +31,7 @@ def oscar():
 def gpu_cache(oscar, sc: Scenario, hist=None, bf16=None):
     dev = torch.device("cuda:0")
     c = oscar.LayerCache(sc.hkv, sc.G, sc.n_hist_pages, sc.n_bf16_pages, torch.from_numpy(sc.hist_pt),
-                         torch.from_numpy(sc.bf16_pt), device=dev)
+                         torch.from_numpy(sc.bf16_pt), device=dev, code_bits=sc.bits)
     if hist is not None:
         c.hist.copy_(torch.from_numpy(hist))
     if bf16 is not None:
