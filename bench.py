@@ -27,12 +27,16 @@ token are timed as well.  Its line names its own metric (write GB/s).
 
 `--workload 28x100k` runs the capacity workload (Qwen3-32B-shaped, 64 layers,
 28 requests x 100000 tokens, GQA 8, G = 128, ~104 GB of INT2 cache; its
-all-BF16 copy does not fit one GPU) and `--workload config0` the single-layer
-4096-token correctness configuration (8 query / 2 KV heads, G = 32).
+all-BF16 copy does not fit one GPU), `--workload int4_28x100k` the same
+tokens from an INT4 cache (~195 GB: the 4-bit comparison point of the
+capacity result; one step per layer is the write of the new token followed by
+the decode, since the fused append step is INT2-only), and `--workload
+config0` the single-layer 4096-token correctness configuration (8 query / 2
+KV heads, G = 32).
 
 The default run (no --workload) times bs1 -- its `value` -- and adds every
-other workload's line under its name ("bs64", "28x100k", "write", "extend",
-"config0"), each with its own roofline and CPU oracle baseline, plus the
+other workload's line under its name ("bs64", "28x100k", "int4_28x100k",
+"write", "extend", "config0"), each with its own roofline and CPU oracle baseline, plus the
 measured read ceilings of the device ("read_ceiling": streaming and
 page-gather reads by oscar_read_probe), against which each bandwidth-bound
 roofline also reports `frac_of_measured_ceiling`.
@@ -65,7 +69,8 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", choices=["bs1", "bs64", "write", "28x100k", "extend", "config0"], default=None,
+    p.add_argument("--workload", choices=["bs1", "bs64", "write", "28x100k", "int4_28x100k", "extend", "config0"],
+                   default=None,
                    help="default: bs1, with every other workload's figures added to its line")
     p.add_argument("--no-companion", action="store_true", help="default run: bs1 alone")
     p.add_argument("--layers", type=int, default=None, help="override the layer count (testing only)")
@@ -96,6 +101,7 @@ DOMINANT = {"bs1": ("attend_kernel", ["decode_int2.hip", "attn_common.h", "commo
             "write": ("write_hist_kernel", ["write.hip", "common.h"]),
             "extend": ("extend_kernel", ["extend.hip", "attn_common.h", "common.h"]),
             "28x100k": ("attend_kernel", ["decode_int2.hip", "attn_common.h", "common.h"]),
+            "int4_28x100k": ("attend_kernel", ["decode_int2.hip", "attn_common.h", "common.h"]),
             "config0": ("attend_kernel", ["decode_int2.hip", "attn_common.h", "common.h"])}
 
 
@@ -169,6 +175,12 @@ WORKLOADS = {
                     layers=64, hq=64, hkv=8, G=128, batch=28, len_lo=100000, len_hi=100000,
                     bf16_bytes_note="all-BF16 cache of the same tokens: 734 GB, beyond one GPU's 288 GB"),
 }
+# the same tokens from an INT4 cache (~195 GB): the pages' 4-bit comparison
+# point of the capacity result, which fits the 288 GB of one MI355X
+WORKLOADS["int4_28x100k"] = dict(
+    name="qwen3-32b-shaped attention decode from an INT4 cache, 64 layers, 28 requests x 100000-token context, "
+         "G 128", layers=64, hq=64, hkv=8, G=128, batch=28, len_lo=100000, len_hi=100000, bits=4,
+    bf16_bytes_note="all-BF16 cache of the same tokens: 734 GB, beyond one GPU's 288 GB")
 # the single-layer correctness configuration (cache-resident: a latency
 # figure, not a bandwidth result); pages contiguous
 WORKLOADS["config0"] = dict(name="single layer, batch 1, 8 q / 2 KV heads, context 4096 (16 sink + 128 recent BF16 + "
@@ -187,11 +199,11 @@ def n_hist_tokens(L):
     return max(0, L - 144)
 
 
-def decode_bytes(lens, hq, hkv, G):
-    """Algorithmic bytes of one decode call: INT2 codes + fp16 meta of every
-    history token, raw bf16 sink/recent tokens, page-table entries, q, out,
-    and R_K / R_V (fp32) once."""
-    per_tok_int2 = 2 * (32 + 4 * (128 // G))
+def decode_bytes(lens, hq, hkv, G, bits=2):
+    """Algorithmic bytes of one decode call: INT2 (or INT4) codes + fp16 meta
+    of every history token, raw bf16 sink/recent tokens, page-table entries,
+    q, out, and R_K / R_V (fp32) once."""
+    per_tok_int2 = 2 * (16 * bits + 4 * (128 // G))
     b = 0
     for L in lens:
         nh = n_hist_tokens(L)
@@ -203,11 +215,11 @@ def decode_bytes(lens, hq, hkv, G):
     return b
 
 
-def attend_bytes(lens, hkv, G):
+def attend_bytes(lens, hkv, G, bits=2):
     """Algorithmic bytes of the split-K attention kernel of one decode call:
-    INT2 codes + fp16 meta of every history token, raw bf16 sink/recent
-    tokens and the page-table entries it follows."""
-    per_tok_int2 = 2 * (32 + 4 * (128 // G))
+    INT2 (or INT4) codes + fp16 meta of every history token, raw bf16
+    sink/recent tokens and the page-table entries it follows."""
+    per_tok_int2 = 2 * (16 * bits + 4 * (128 // G))
     b = 0
     for L in lens:
         nh = n_hist_tokens(L)
@@ -215,11 +227,11 @@ def attend_bytes(lens, hkv, G):
     return b
 
 
-def append_bytes(batch, hkv, G):
+def append_bytes(batch, hkv, G, bits=2):
     """Algorithmic bytes of one append call: the evicted ring token is read
     and written to history, the new token is read and stored raw, R_K and
     R_V (fp32) are read once."""
-    per_tok_int2 = 32 + 4 * (128 // G)
+    per_tok_int2 = 16 * bits + 4 * (128 // G)
     return batch * hkv * 2 * (256 + per_tok_int2 + 256 + 256) + 2 * 128 * 128 * 4
 
 
@@ -291,7 +303,7 @@ def main():
         # every other workload, one after another (each frees its memory
         # before the next starts), then the device's read ceilings
         import gc
-        for name in ("bs64", "28x100k", "write", "extend", "config0"):
+        for name in ("bs64", "28x100k", "int4_28x100k", "write", "extend", "config0"):
             gc.collect()
             torch.cuda.empty_cache()
             a2 = argparse.Namespace(**vars(args))
@@ -314,7 +326,7 @@ def main():
         ceil = read_ceiling(dev)
         line["read_ceiling"] = ceil
         attach_ceiling(line, ceil)
-        for name in ("bs64", "28x100k", "write", "config0"):
+        for name in ("bs64", "28x100k", "int4_28x100k", "write", "config0"):
             attach_ceiling(line[name], ceil)
     elif args.workload != "config0":
         ceil = read_ceiling(dev)
@@ -324,14 +336,15 @@ def main():
 
 
 # gather block of each workload's history pages, and which ceiling bounds it
-CEILING_OF = {"bs1": "gather_1280", "bs64": "gather_1280", "28x100k": "gather_1152", "write": "stream"}
+CEILING_OF = {"bs1": "gather_1280", "bs64": "gather_1280", "28x100k": "gather_1152", "int4_28x100k": "gather_2176",
+              "write": "stream"}
 
 
 def read_ceiling(dev, reps=5):
     """Measured read ceilings (oscar_read_probe, median of `reps` timed
     launches): streaming 4 KB blocks of a 4 GiB buffer, and gathers of
-    history-page-sized blocks (1152 / 1280 / 1536 B: G = 128 / 64 / 32) in a
-    seeded random order from a 4 GiB pool."""
+    history-page-sized blocks (INT2: 1152 / 1280 / 1536 B for G = 128 / 64 /
+    32; INT4 G = 128: 2176 B) in a seeded random order from a 4 GiB pool."""
     import numpy as np
     import torch
 
@@ -356,7 +369,7 @@ def read_ceiling(dev, reps=5):
         return n_blocks * bb / float(np.median(ts)) / 1e9
 
     out["stream"] = round(timed(nbytes // 4096, 4096), 1)
-    for bb in (1152, 1280, 1536):
+    for bb in (1152, 1280, 1536, 2176):
         n_slots = nbytes // bb
         ids = torch.from_numpy(np.random.default_rng(bb).permutation(n_slots)[: n_slots * 3 // 4].astype(np.int32))
         out[f"gather_{bb}"] = round(timed(ids.numel(), bb, ids.to(dev)), 1)
@@ -442,6 +455,7 @@ def decode_main(args, W, dev, workload):
     if args.layers:
         W["layers"] = args.layers
     nl, hq, hkv, G, B = W["layers"], W["hq"], W["hkv"], W["G"], W["batch"]
+    bits = W.get("bits", 2)
     steps, warm = args.steps, args.warmup
     headroom = steps + warm + 1
     if W["batch"] == 1:
@@ -479,7 +493,7 @@ def decode_main(args, W, dev, workload):
                                                          n_pool_pages=sum(pages_per_req) + 1)
             bf16_pt = synth.bf16_page_tables(B, shuffle_seed=args.seed + l)
         ly.cache = oscar.LayerCache(hkv, G, n_pool, 9 * B, torch.from_numpy(hist_pt), torch.from_numpy(bf16_pt),
-                                    device=dev)
+                                    device=dev, code_bits=bits)
         # prefill: every request's first start_len tokens in one write call
         tot = int(start_lens.sum())
         k = synth.kv_device(synth.device_generator(args.seed, l, synth.S_CACHE_K), tot, ld.outliers, dev)
@@ -488,7 +502,13 @@ def decode_main(args, W, dev, workload):
         oscar.write_kv(ly.cache, ly.rk, ly.rv, k, v, cu, torch.zeros(B, dtype=torch.int32, device=dev),
                        int(start_lens.max()))
         if "bf16_bytes_note" in W:
-            torch.cuda.synchronize()   # free the bulk tokens before the next layer draws its own
+            # free the bulk tokens (and hand their segments back) before the
+            # next layer allocates its pool and draws its own: otherwise the
+            # caching allocator fragments ~100-200 GB of pools
+            torch.cuda.synchronize()
+            del k, v
+            torch.cuda.empty_cache()
+            k = v = None
         # per-step inputs (the same new token and query every step)
         ly.k_new = synth.kv_device(synth.device_generator(args.seed, l, synth.S_NEW_K), B, ld.outliers, dev)
         ly.v_new = synth.kv_device(synth.device_generator(args.seed, l, synth.S_NEW_V), B, ld.outliers, dev)
@@ -530,11 +550,18 @@ def decode_main(args, W, dev, workload):
     # ---------------------------------------------------------------- the step
     lens_before = torch.from_numpy(start_lens.astype(np.int32)).to(dev)   # before this step's append
     lens_after = lens_before + 1
+    cu_one = torch.arange(B + 1, dtype=torch.int32, device=dev)           # one new token per request
 
     def step():
         for ly in layers:
-            oscar.decode_step(ly.cache, ly.rk, ly.rv, ly.k_new, ly.v_new, lens_before, ly.q, max_len,
-                              1 / math.sqrt(HEAD_DIM), out=ly.out, workspace=ly.ws)
+            if bits == 2:
+                oscar.decode_step(ly.cache, ly.rk, ly.rv, ly.k_new, ly.v_new, lens_before, ly.q, max_len,
+                                  1 / math.sqrt(HEAD_DIM), out=ly.out, workspace=ly.ws)
+            else:
+                # INT4: the write of the new token, then the decode
+                oscar.write_kv(ly.cache, ly.rk, ly.rv, ly.k_new, ly.v_new, cu_one, lens_before, 1)
+                oscar.decode_attn(ly.cache, ly.rk, ly.rv, ly.q, lens_after, max_len, 1 / math.sqrt(HEAD_DIM),
+                                  out=ly.out, workspace=ly.ws)
         lens_before.add_(1)
         lens_after.add_(1)
 
@@ -572,9 +599,9 @@ def decode_main(args, W, dev, workload):
     dec_bytes_mean = 0.0
     for s in range(steps):
         lens_s = (lens_at_timing + s + 1).tolist()
-        db = decode_bytes(lens_s, hq, hkv, G)
+        db = decode_bytes(lens_s, hq, hkv, G, bits)
         dec_bytes_mean += db / steps
-        step_bytes += nl * (db + append_bytes(B, hkv, G)) / steps
+        step_bytes += nl * (db + append_bytes(B, hkv, G, bits)) / steps
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     tokens_per_s = B / (ms_per_step * 1e-3)
 
@@ -596,7 +623,7 @@ def decode_main(args, W, dev, workload):
     torch.cuda.synchronize()
     attend_us = float(np.mean([a.elapsed_time(b) for a, b in pairs])) * 1e3
     lens_now0 = lens_before.cpu().numpy().tolist()
-    attend_b = attend_bytes(lens_now0, hkv, G)
+    attend_b = attend_bytes(lens_now0, hkv, G, bits)
     achieved = attend_b / (attend_us * 1e-6) / 1e9
 
     # ---------------------------------------------------------------- BF16
@@ -645,7 +672,8 @@ def decode_main(args, W, dev, workload):
     if not args.no_cpu_baseline:
         # 28 x 100K: one KV head (with its query heads) of one request per
         # layer sample; the others: every head
-        cpu = cpu_baseline(args, W, final_lens, step_bytes, kv_sample=1 if W["hkv"] * W["len_hi"] > 400000 else None)
+        cpu = cpu_baseline(args, W, final_lens, step_bytes, kv_sample=1 if W["hkv"] * W["len_hi"] > 400000 else None,
+                           bits=bits)
 
     line = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warm,
@@ -653,12 +681,15 @@ def decode_main(args, W, dev, workload):
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": W["name"], "layers": nl, "batch": B, "q_heads": hq, "kv_heads": hkv, "group": G,
                    "context": int(max_len) if B == 1 else [int(W["len_lo"]), int(W["len_hi"])],
-                   "step": "per layer: oscar_decode_step (write-on-append of one token + INT2 paged decode)"},
+                   "code_bits": bits,
+                   "step": "per layer: oscar_decode_step (write-on-append of one token + INT2 paged decode)"
+                           if bits == 2 else
+                           "per layer: oscar_write_kv of one token per request + oscar_decode_attn (INT4)"},
         "tokens_per_s": round(tokens_per_s, 1),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(workload),
-                     "kernel": f"oscar::attend_kernel<{hq // hkv}, {128 // G}> (split-K INT2 + BF16 decode)",
+                     "kernel": f"oscar::attend_kernel<{hq // hkv}, {128 // G}> (split-K INT{bits} + BF16 decode)",
                      "avg_launch_us": round(attend_us, 2), "bytes_per_launch": int(attend_b)},
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
@@ -974,7 +1005,7 @@ def write_cpu_baseline(args, W, bytes_per_token):
     return out
 
 
-def cpu_baseline(args, W, final_lens, step_bytes, kv_sample=None):
+def cpu_baseline(args, W, final_lens, step_bytes, kv_sample=None, bits=2):
     """The fp64 oracle timed on the host on a bounded sample of the step: one
     layer of the first request (kv_sample: only that many KV heads, with their
     query heads), prefilled untimed, then rounds of (append one token +
@@ -996,7 +1027,7 @@ def cpu_baseline(args, W, final_lens, step_bytes, kv_sample=None):
     rng = np.random.default_rng(args.seed)
     R = np.linalg.qr(rng.standard_normal((128, 128)))[0]
     pt, npool = synth.shuffled_page_tables(args.seed, 0, [L + 16])
-    ref = o.LayerCacheRef(hkv_s, G, npool, 9, pt, synth.bf16_page_tables(1))
+    ref = o.LayerCacheRef(hkv_s, G, npool, 9, pt, synth.bf16_page_tables(1), bits=bits)
     t_pre = time.time()
     ref.write(R, R, 6.0, 6.0, k[:L - 8], v[:L - 8], [0, L - 8], [0])
     prefill_s = time.time() - t_pre
@@ -1008,7 +1039,7 @@ def cpu_baseline(args, W, final_lens, step_bytes, kv_sample=None):
         ref.write(R, R, 6.0, 6.0, k[cur:cur + 1], v[cur:cur + 1], [0, 1], [cur])
         cur += 1
         o.decode_attn(ref, R, R, q, [cur], 1 / math.sqrt(128))
-        sample_bytes += decode_bytes([cur], hq_s, hkv_s, G) + append_bytes(1, hkv_s, G)
+        sample_bytes += decode_bytes([cur], hq_s, hkv_s, G, bits) + append_bytes(1, hkv_s, G, bits)
         rounds += 1
     dt = time.time() - t0
     rate = sample_bytes / dt
@@ -1016,7 +1047,7 @@ def cpu_baseline(args, W, final_lens, step_bytes, kv_sample=None):
     exact = W["layers"] == 1 and len(final_lens) == 1 and hkv_s == hkv
     out = {"value": round(rate / 1e9, 4), "unit": "GB/s", "kind": "oracle",
            "sample": f"{rounds} rounds of (append 1 token + decode) on one layer of one {L}-token request "
-                     f"({heads}, {gqa} query heads each, G {G}): {dt / rounds:.2f} s per round; value = "
+                     f"({heads}, {gqa} query heads each, G {G}, INT{bits}): {dt / rounds:.2f} s per round; value = "
                      f"algorithmic bytes of those rounds / their time",
            "measured" if exact else "s_per_step_extrapolated": round(step_bytes / rate, 3),
            "prefill_untimed_s": round(prefill_s, 1)}
