@@ -254,8 +254,8 @@ def bf16_paged_decode(q: torch.Tensor, kv_pages: torch.Tensor, pt: torch.Tensor,
     if out is None:
         out = torch.empty((batch, hq, HEAD_DIM), dtype=torch.float32, device=dev)
     need = bf16_decode_workspace_bytes(batch, hq, hkv, max_seq_len)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace is None:  # zero-filled: it holds the merge counters
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
     check(load().oscar_bf16_paged_decode(_ptr(q), _ptr(kv_pages), kv_pages.shape[0], _ptr(pt), pt.shape[1],
                                          _ptr(seq_lens), batch, int(max_seq_len), hq, hkv, float(sm_scale),
                                          _ptr(out), _ptr(status), _ptr(workspace), workspace.numel(),

@@ -310,6 +310,112 @@ __device__ inline float load_agent(const float *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ------------------------------------------------------------ split merge
+constexpr int MAX_MERGE_SPLITS = 256;  // partials per query head one merge combines
+constexpr int MERGE_WINDOW = 32;       // slots per head the merge loads without bounds checks
+constexpr int COUNTER_STRIDE = 64;     // uint32 words per merge counter (one 256-byte line)
+
+// Merge of one (request, KV head), run inside a split-K decode kernel by
+// the workgroup (NT threads) that finishes last: LSE-combines the `used`
+// partials (o[128], m, l; PART_STRIDE floats apart, head_stride apart per
+// query head, at least MERGE_WINDOW slots per head) of each query head of the
+// group, normalises, and writes out0 [GQA][128].  Built for latency: thread (h, c)
+// issues the loads of all its partial values and the (m, l) pairs at once,
+// so the workgroup waits on memory about once.  The partials of other
+// workgroups are read with agent-scope loads (they may sit in the L2 of
+// another XCD until written through).
+template <int GQA>
+struct MergeWork {
+  float w[GQA][MAX_MERGE_SPLITS];  // m, then the weight of each split (0 past `used`)
+  float l[GQA][MAX_MERGE_SPLITS];
+  float lsum[GQA];
+};
+
+// partials per (head, channel) a merging thread holds in registers at a time
+template <int GQA>
+constexpr int merge_ch() { return GQA >= 8 ? 16 : 32; }
+
+template <int GQA, int NT>
+__device__ void merge_partials(const float *parts0, int64_t head_stride, int used, float *out0, int tid,
+                               MergeWork<GQA> &mw) {
+  constexpr int KH = (GQA * D + NT - 1) / NT;  // (head, channel) pairs per thread
+  constexpr int MCH = merge_ch<GQA>();
+  static_assert(MCH <= MERGE_WINDOW && MCH <= MAX_MERGE_SPLITS, "the first register window fits");
+
+  // ---- loads, all issued before any use: partial values of splits
+  // 0..MCH-1 (every head has at least MCH slots, so these loads need no
+  // bounds; slots >= used are never summed), then the (m, l) pairs
+  float ov[KH][MCH];
+#pragma unroll
+  for (int k = 0; k < KH; ++k) {
+    const int idx = tid + NT * k, h = idx / D, c = idx % D;
+    const float *ph = parts0 + (h < GQA ? h : 0) * head_stride + c;
+#pragma unroll
+    for (int j = 0; j < MCH; ++j) ov[k][j] = load_agent(ph + j * PART_STRIDE);
+  }
+  for (int e = tid; e < GQA * used; e += NT) {
+    const int hh = e / used, sp = e % used;
+    const float *pm = parts0 + hh * head_stride + sp * PART_STRIDE + D;
+    mw.w[hh][sp] = load_agent(pm);
+    mw.l[hh][sp] = load_agent(pm + 1);
+  }
+  __syncthreads();
+  // ---- per head: max over splits, split weights, total l (wave hh; DPP
+  // reductions)
+  {
+    const int wave = wave_id(), lane = tid & 63;
+    const int nw = used > MCH ? used : MCH;
+    for (int hh = wave; hh < GQA; hh += NT / 64) {
+      float m = -INFINITY;
+      for (int sp = lane; sp < used; sp += 64) m = fmaxf(m, mw.w[hh][sp]);
+      m = wave_max(m);
+      float l = 0.f;
+      for (int sp = lane; sp < nw; sp += 64) {
+        float w = 0.f;
+        if (sp < used) {
+          const float ms = mw.w[hh][sp];
+          w = (ms == -INFINITY) ? 0.f : fast_exp2(ms - m);
+          l = fmaf(w, mw.l[hh][sp], l);
+        }
+        mw.w[hh][sp] = w;
+      }
+      l = wave_sum(l);
+      if (lane == 0) mw.lsum[hh] = l;
+    }
+  }
+  __syncthreads();
+  // ---- output channel c of head h
+#pragma unroll
+  for (int k = 0; k < KH; ++k) {
+    const int idx = tid + NT * k, h = idx / D, c = idx % D;
+    if (h < GQA) {
+      float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+      for (int j = 0; j < MCH; ++j) {
+        const float t = fmaf(mw.w[h][j], ov[k][j], j & 1 ? acc1 : acc0);
+        if (j & 1)
+          acc1 = (j < used) ? t : acc1;
+        else
+          acc0 = (j < used) ? t : acc0;
+      }
+      // the first window is summed here, before the later windows' loads
+      asm volatile("" : "+v"(acc0), "+v"(acc1));
+      const float *ph = parts0 + h * head_stride + c;
+      for (int s0 = MCH; s0 < used; s0 += MCH) {
+        float o2[MCH];
+#pragma unroll
+        for (int j = 0; j < MCH; ++j) o2[j] = (s0 + j < used) ? load_agent(ph + (s0 + j) * PART_STRIDE) : 0.f;
+#pragma unroll
+        for (int j = 0; j < MCH; ++j) {
+          const float w = (s0 + j < used) ? mw.w[h][s0 + j] : 0.f;
+          acc0 = fmaf(w, o2[j], acc0);
+        }
+      }
+      out0[h * D + c] = (acc0 + acc1) / mw.lsum[h];
+    }
+  }
+}
+
 // Combines the NW per-wave states in LDS (o [NW][GQA][128], m, l [NW][GQA])
 // and writes one unnormalised partial (o[128], m, l) per query head
 // (AGENT: with agent-scope stores).  With xm, one more token joins: value

@@ -86,6 +86,9 @@ struct SplitPlan {
   bool fused = false;   // INT2: the attend kernel merges (last workgroup of each unit)
 };
 
+// Compute units of the current device (256 when it cannot be queried).
+int64_t device_cus();
+
 SplitPlan plan_int2_splits(int batch, int n_kv_heads, int max_seq_len);
 SplitPlan plan_bf16_splits(int batch, int n_kv_heads, int max_seq_len);
 

@@ -5,8 +5,13 @@
 // next page's loads issued into a second register set before the current
 // page computes).  Scores on the bf16 matrix
 // cores, PV on the vector ALUs, fp32 accumulation.  Each workgroup writes an
-// unnormalised partial per query head; a merge kernel (one block per
-// (request, KV head)) LSE-combines them and normalises.
+// unnormalised partial per query head.  The split plan and the merge are
+// those of the INT2 decode: when every (request, KV head) fits one round of
+// one workgroup per CU, its pages are spread over as many splits as that
+// round holds and the last workgroup of each unit to finish merges the
+// partials inside the kernel (agent-scope stores and loads, a counter per
+// unit); otherwise splits of 64 pages and a merge kernel (one block per
+// (request, KV head)) that LSE-combines them and normalises.
 #include "attn_common.h"
 
 namespace oscar {
@@ -14,27 +19,41 @@ namespace oscar {
 constexpr int BW = 8;  // waves per workgroup
 
 SplitPlan plan_bf16_splits(int batch, int n_kv_heads, int max_seq_len) {
-  // as for the INT2 decode: fill one round of resident workgroups (two per
-  // CU) when the batch is small, else splits of 8 pages per wave
+  // as for the INT2 decode: one round of workgroups, one per CU (the
+  // kernel's registers hold one 8-wave workgroup per CU), when every unit
+  // gets at least one; else splits of 8 pages per wave
   const int pages = (max_seq_len + PAGE - 1) / PAGE;
   const int64_t units = int64_t(batch) * n_kv_heads;
-  int64_t pps = units <= 512 ? (pages + 512 / units - 1) / (512 / units) : 8 * BW;
-  if (pps < BW) pps = BW;
-  const int64_t min_pps = (pages + 255 - 1) / 255;
-  if (pps < min_pps) pps = min_pps;
+  const int64_t slots = device_cus();
   SplitPlan p;
+  int64_t pps;
+  if (units <= slots) {
+    const int64_t per_unit = slots / units;
+    pps = (pages + per_unit - 1) / per_unit;
+    p.fused = true;
+  } else {
+    pps = 8 * BW;
+  }
+  if (pps < BW) pps = BW;
+  const int64_t min_pps = (pages + MAX_MERGE_SPLITS - 2) / (MAX_MERGE_SPLITS - 1);
+  if (pps < min_pps) pps = min_pps;
   p.pages_per_split = int(pps);
   p.n_splits = int((pages + pps - 1) / pps);
   return p;
 }
 
-static size_t count_off(int batch, int n_q_heads, int n_splits) {
-  return (size_t(batch) * n_q_heads * n_splits * PART_STRIDE * sizeof(float) + 255) & ~size_t(255);
+// Partial slots per query head: one per split, and at least the fused
+// merge's first register window (loaded without bounds checks).
+static int bf16_part_slots(const SplitPlan &p) { return p.n_splits > MERGE_WINDOW ? p.n_splits : MERGE_WINDOW; }
+
+// Workspace: the partials, then one merge counter per (request, KV head)
+static size_t count_off(int batch, int n_q_heads, const SplitPlan &p) {
+  return (size_t(batch) * n_q_heads * bf16_part_slots(p) * PART_STRIDE * sizeof(float) + 255) & ~size_t(255);
 }
 
 size_t decode_bf16_ws_bytes(int batch, int n_q_heads, int n_kv_heads, int max_seq_len) {
   const SplitPlan p = plan_bf16_splits(batch, n_kv_heads, max_seq_len);
-  return count_off(batch, n_q_heads, p.n_splits);
+  return count_off(batch, n_q_heads, p) + size_t(batch) * n_kv_heads * COUNTER_STRIDE * sizeof(uint32_t);
 }
 
 struct Bf16Args {
@@ -47,7 +66,9 @@ struct Bf16Args {
   float sm_scale;
   float *out;
   uint32_t *status;
-  float *parts;     // [B][Hq][n_splits][PART_STRIDE]
+  float *parts;     // [B][Hq][part_slots][PART_STRIDE]
+  int part_slots;
+  uint32_t *counters;  // [B][Hkv][COUNTER_STRIDE]: word 0 = workgroups done (zero between calls)
 };
 
 template <int GQA>
@@ -58,7 +79,7 @@ __global__ void __launch_bounds__(1024) bf16_merge_kernel(Bf16Args a) {
   if (L < 1 || L > a.max_seq_len) return;  // output zeroed by the split kernel
   const int pages = (L + PAGE - 1) / PAGE;
   const int used = (pages + a.pages_per_split - 1) / a.pages_per_split;
-  const int64_t head_stride = int64_t(a.n_splits) * PART_STRIDE;
+  const int64_t head_stride = int64_t(a.part_slots) * PART_STRIDE;
   const float *parts0 = a.parts + (int64_t(b) * a.n_q_heads + hk * GQA) * head_stride;
   __shared__ float w_lds[GQA][256];
   __shared__ float lsum[GQA];
@@ -101,7 +122,7 @@ __global__ void __launch_bounds__(1024) bf16_merge_kernel(Bf16Args a) {
   }
 }
 
-template <int GQA>
+template <int GQA, bool FUSED>
 __global__ void __launch_bounds__(BW * 64) bf16_decode_kernel(Bf16Args a) {
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
@@ -160,16 +181,44 @@ __global__ void __launch_bounds__(BW * 64) bf16_decode_kernel(Bf16Args a) {
   }
   st.finish(o_lds + wave * GQA * D, m_lds + wave * GQA, l_lds + wave * GQA, lane);
   __syncthreads();
-  const int64_t head_stride = int64_t(a.n_splits) * PART_STRIDE;
-  float *part0 = a.parts + (int64_t(b) * a.n_q_heads + hk * GQA) * head_stride + split * PART_STRIDE;
-  combine_waves<GQA, BW>(o_lds, m_lds, l_lds, part0, head_stride, tid);
+  const int64_t head_stride = int64_t(a.part_slots) * PART_STRIDE;
+  float *parts0 = a.parts + (int64_t(b) * a.n_q_heads + hk * GQA) * head_stride;
+  float *part0 = parts0 + split * PART_STRIDE;
+  if constexpr (!FUSED) {
+    combine_waves<GQA, BW>(o_lds, m_lds, l_lds, part0, head_stride, tid);
+  } else {
+    combine_waves<GQA, BW, true>(o_lds, m_lds, l_lds, part0, head_stride, tid);
+    // the last workgroup of (b, hk) to finish merges: its partial stores
+    // have completed (agent scope) before the counter counts it in; the
+    // counter is left at zero for the next call
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (used > 1) {
+      __shared__ int last;
+      if (tid == 0) {
+        uint32_t *cnt = a.counters + COUNTER_STRIDE * (b * a.n_kv_heads + hk);
+        const uint32_t done = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = done == uint32_t(used - 1);
+        if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
+      if (!last) return;
+    }
+    static_assert(sizeof(MergeWork<GQA>) <= sizeof(lds), "merge work area fits the wave states");
+    merge_partials<GQA, BW * 64>(parts0, head_stride, used, a.out + (int64_t(b) * a.n_q_heads + hk * GQA) * D,
+                                 tid, *reinterpret_cast<MergeWork<GQA> *>(lds));
+  }
 }
 
 template <int GQA>
-static hipError_t launch_t(const Bf16Args &a, int batch, hipStream_t s) {
+static hipError_t launch_t(const Bf16Args &a, bool fused, int batch, hipStream_t s) {
   const KernelEvents ev = take_profile_events();
-  hipExtLaunchKernelGGL((bf16_decode_kernel<GQA>), dim3(a.n_splits, a.n_kv_heads, batch), dim3(BW * 64), 0, s,
-                        ev.before, ev.after, 0, a);
+  const dim3 grid(a.n_splits, a.n_kv_heads, batch);
+  if (fused) {
+    hipExtLaunchKernelGGL((bf16_decode_kernel<GQA, true>), grid, dim3(BW * 64), 0, s, ev.before, ev.after, 0, a);
+    return hipGetLastError();
+  }
+  hipExtLaunchKernelGGL((bf16_decode_kernel<GQA, false>), grid, dim3(BW * 64), 0, s, ev.before, ev.after, 0, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bf16_merge_kernel<GQA>), dim3(a.n_kv_heads, batch), dim3(1024), 0, s, a);
@@ -197,11 +246,13 @@ hipError_t launch_decode_bf16(const uint16_t *q, const uint16_t *kv, int64_t n_p
   a.out = out;
   a.status = status;
   a.parts = static_cast<float *>(ws);
+  a.part_slots = bf16_part_slots(p);
+  a.counters = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + count_off(batch, n_q_heads, p));
   switch (n_q_heads / n_kv_heads) {
-    case 1: return launch_t<1>(a, batch, s);
-    case 2: return launch_t<2>(a, batch, s);
-    case 4: return launch_t<4>(a, batch, s);
-    case 8: return launch_t<8>(a, batch, s);
+    case 1: return launch_t<1>(a, p.fused, batch, s);
+    case 2: return launch_t<2>(a, p.fused, batch, s);
+    case 4: return launch_t<4>(a, p.fused, batch, s);
+    case 8: return launch_t<8>(a, p.fused, batch, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -94,7 +94,7 @@ struct Rows {
 
 // Compute units of the current device (256 on MI355X; 256 when it cannot
 // be queried, e.g. while sizing a workspace on a host without a GPU).
-static int64_t device_cus() {
+int64_t device_cus() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
       n > 0)
@@ -145,12 +145,12 @@ static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Partial slots per query head: one per split (raw + history), and at least
 // the merge's first register window, which it loads without bounds checks.
-constexpr int MERGE_WINDOW = 32;
+static_assert(MAX_SPLITS + 1 <= MAX_MERGE_SPLITS, "the merge holds every split's weight");
 static int part_slots(const SplitPlan &p) { return 1 + (p.n_splits > MERGE_WINDOW ? p.n_splits : MERGE_WINDOW); }
 
 // Workspace: the partials, then one merge counter per (request, KV head),
-// each on a 256-byte line of its own (atomics on one line serialise)
-constexpr int COUNTER_STRIDE = 64;  // uint32 words
+// each on a 256-byte line of its own (COUNTER_STRIDE words: atomics on one
+// line serialise)
 static size_t parts_bytes(int batch, int n_q_heads, const SplitPlan &p) {
   return align256(size_t(batch) * n_q_heads * part_slots(p) * PART_STRIDE * sizeof(float));
 }
@@ -578,10 +578,12 @@ __device__ __forceinline__ void build_q(const StepArgs &a, int tid, QWork<GQA, N
 // then the rest).  The compiler does not order LDS reads after these copies,
 // so the page loop waits for them itself (vmcnt counts per instruction;
 // loads complete in issue order).
-// Pages in flight per wave (the ring's depth): 4 INT2 pages; INT4 blocks are
-// 1.7-1.9 times larger, and three of them hold more bytes than four INT2
-// pages while two workgroups' rings still fit a CU's LDS.  The first
-// depth - 1 pages are loaded through registers before the q build.
+// Pages in flight per wave (the ring's depth): 4 INT2 pages; INT4 blocks
+// are 1.7-1.9 times larger, and three of them hold more bytes than four INT2
+// pages while two workgroups' rings still fit a CU's LDS.  (A ring of 8 INT2
+// pages, every page of a batch-1 wave requested at once, measured slower:
+// 18.5 against 17.3 us per layer at 32K.)  Up to 3 pages are loaded through
+// registers before the q build, the rest by direct copies after it.
 template <int BITS>
 constexpr int depth_of() { return BITS == 2 ? 4 : 3; }
 
@@ -783,7 +785,7 @@ __device__ inline uint32_t halves(uint32_t a, uint32_t b, uint32_t sel) { return
 // forms B_g = fp16(pw s_tg) for each scale group g; acc[r] += Vexp_r B_g(r)
 // with Vexp = 1 + code/w_t, and cacc[g] += 1 B_g, whose rows all equal the
 // column sums of B_g: acc - cacc is then exactly sum_t B code / w_t.
-template <int GQA, int NG, int BITS, class Prep>
+template <int GQA, int NG, int BITS, int DP, class Prep>
 __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, int j1, int wave, int lane,
                              int pid_pre, Prep &&prep, const uint32_t *frag_lds, uint8_t *ring, float *zs,
                              float *o_lds, float *m_lds, float *l_lds) {
@@ -794,7 +796,7 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
   // a block is HB = 2 code areas' worth of bytes (1 or 2 KB) copied 1 KB
   // per instruction, then 128 NG bytes of tail: IPP copy instructions per page
   constexpr int HB = 2 * code_area_bytes(BITS), NHB = HB / 1024, IPP = NHB + 1;
-  constexpr int DP = depth_of<BITS>(), RPB = DP - 1;
+  constexpr int RPB = DP - 1 < 3 ? DP - 1 : 3;
   const oscar_layer_cache &c = a.c;
   const int t = lane & 15, qd = lane >> 4;  // score side: token, lane group
   const int hp = t % GQA;                   // PV side: head of column n = l%16 (tq = qd)
@@ -1244,106 +1246,14 @@ __device__ void combine_rotate(const float *o_lds, const float *m_lds, const flo
   }
 }
 
-// Merge of one (request, KV head), run inside the attend kernel by the
-// workgroup that finishes last: LSE-combines the `used` partials of each
-// query head of the group (all in the plain basis: the history workgroups
-// rotated theirs back) and normalises.  Built for latency: thread (h, c)
-// issues the loads of all its partial values and the (m, l) pairs at once,
-// so the workgroup waits on memory about once.  The partials of other
-// workgroups are read with agent-scope loads (they may sit in the L2 of
-// another XCD until written through).
-template <int GQA>
-struct MergeWork {
-  float w[GQA][MAX_SPLITS + 1];  // m, then the weight of each split (0 past `used`)
-  float l[GQA][MAX_SPLITS + 1];
-  float lsum[GQA];
-};
-
-// partials per (head, channel) a merging thread holds in registers at a time
-template <int GQA>
-constexpr int merge_ch() { return GQA >= 8 ? 16 : 32; }
-
+// Merge of one (request, KV head) inside the attend kernel (the partials
+// are all in the plain basis: the history workgroups rotated theirs back).
 template <int GQA>
 __device__ void merge_unit(const StepArgs &a, int b, int hk, int used, int tid, MergeWork<GQA> &mw) {
-  constexpr int NT = AW * 64;
-  constexpr int KH = (GQA * D + NT - 1) / NT;  // (head, channel) pairs per thread
-  constexpr int MCH = merge_ch<GQA>();
-  static_assert(MCH <= MERGE_WINDOW && MCH <= MAX_SPLITS + 1, "the first register window fits");
   const int64_t head_stride = int64_t(a.part_slots) * PART_STRIDE;
   const float *parts0 = a.parts + (int64_t(b) * a.n_q_heads + hk * GQA) * head_stride;
-
-  // ---- loads, all issued before any use: partial values of splits
-  // 0..MCH-1 (every head has at least MCH slots, so these loads need no
-  // bounds; slots >= used are never summed), then the (m, l) pairs
-  float ov[KH][MCH];
-#pragma unroll
-  for (int k = 0; k < KH; ++k) {
-    const int idx = tid + NT * k, h = idx / D, c = idx % D;
-    const float *ph = parts0 + (h < GQA ? h : 0) * head_stride + c;
-#pragma unroll
-    for (int j = 0; j < MCH; ++j) ov[k][j] = load_agent(ph + j * PART_STRIDE);
-  }
-  for (int e = tid; e < GQA * used; e += NT) {
-    const int hh = e / used, sp = e % used;
-    const float *pm = parts0 + hh * head_stride + sp * PART_STRIDE + D;
-    mw.w[hh][sp] = load_agent(pm);
-    mw.l[hh][sp] = load_agent(pm + 1);
-  }
-  __syncthreads();
-  // ---- per head: max over splits, split weights, total l (wave hh; DPP
-  // reductions)
-  {
-    const int wave = wave_id(), lane = tid & 63;
-    const int nw = used > MCH ? used : MCH;
-    for (int hh = wave; hh < GQA; hh += NT / 64) {
-      float m = -INFINITY;
-      for (int sp = lane; sp < used; sp += 64) m = fmaxf(m, mw.w[hh][sp]);
-      m = wave_max(m);
-      float l = 0.f;
-      for (int sp = lane; sp < nw; sp += 64) {
-        float w = 0.f;
-        if (sp < used) {
-          const float ms = mw.w[hh][sp];
-          w = (ms == -INFINITY) ? 0.f : fast_exp2(ms - m);
-          l = fmaf(w, mw.l[hh][sp], l);
-        }
-        mw.w[hh][sp] = w;
-      }
-      l = wave_sum(l);
-      if (lane == 0) mw.lsum[hh] = l;
-    }
-  }
-  __syncthreads();
-  // ---- output channel c of head h
-#pragma unroll
-  for (int k = 0; k < KH; ++k) {
-    const int idx = tid + NT * k, h = idx / D, c = idx % D;
-    if (h < GQA) {
-      float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll
-      for (int j = 0; j < MCH; ++j) {
-        const float t = fmaf(mw.w[h][j], ov[k][j], j & 1 ? acc1 : acc0);
-        if (j & 1)
-          acc1 = (j < used) ? t : acc1;
-        else
-          acc0 = (j < used) ? t : acc0;
-      }
-      // the first window is summed here, before the later windows' loads
-      asm volatile("" : "+v"(acc0), "+v"(acc1));
-      const float *ph = parts0 + h * head_stride + c;
-      for (int s0 = MCH; s0 < used; s0 += MCH) {
-        float o2[MCH];
-#pragma unroll
-        for (int j = 0; j < MCH; ++j) o2[j] = (s0 + j < used) ? load_agent(ph + (s0 + j) * PART_STRIDE) : 0.f;
-#pragma unroll
-        for (int j = 0; j < MCH; ++j) {
-          const float w = (s0 + j < used) ? mw.w[h][s0 + j] : 0.f;
-          acc0 = fmaf(w, o2[j], acc0);
-        }
-      }
-      a.out[(int64_t(b) * a.n_q_heads + hk * GQA + h) * D + c] = (acc0 + acc1) / mw.lsum[h];
-    }
-  }
+  merge_partials<GQA, AW * 64>(parts0, head_stride, used, a.out + (int64_t(b) * a.n_q_heads + hk * GQA) * D, tid,
+                               mw);
 }
 
 // Separate merge kernel (large batches, where the attend workgroups run in
@@ -1501,7 +1411,8 @@ attend_kernel(StepArgs a) {
   const int L = append ? L0 + 1 : L0;
   // per wave: its page ring, reused for its o[GQA][128] once the pages are done
   constexpr int SB = hist_block_bytes(D / NG, BITS);
-  constexpr int WREG = depth_of<BITS>() * SB > GQA * D * 4 ? depth_of<BITS>() * SB : GQA * D * 4;
+  constexpr int DPK = depth_of<BITS>();
+  constexpr int WREG = DPK * SB > GQA * D * 4 ? DPK * SB : GQA * D * 4;
   __shared__ __attribute__((aligned(16))) uint8_t wave_lds[AW * WREG];
   __shared__ float ml_lds[2 * AW * GQA];
   __shared__ float zs_lds[AW * GQA * NG];  // per wave: z sums per (head, group)
@@ -1583,7 +1494,7 @@ attend_kernel(StepArgs a) {
     const int j1 = min((nh + PAGE - 1) / PAGE, j0 + a.pages_per_split);
     auto prep = [&] { build_q<GQA, NG, BITS>(a, tid, work.q, frag_lds, ql); };
     // every wave of the workgroup calls this (it holds workgroup barriers)
-    history_wave<GQA, NG, BITS>(a, b, hk, nh, j0, j1, wave, lane, pid_pre, prep, frag_lds, wave_lds + wave * WREG,
+    history_wave<GQA, NG, BITS, DPK>(a, b, hk, nh, j0, j1, wave, lane, pid_pre, prep, frag_lds, wave_lds + wave * WREG,
                           zs_lds + wave * GQA * NG, o_w, m_lds + wave * GQA, l_lds + wave * GQA);
   }
   const int64_t head_stride = int64_t(a.part_slots) * PART_STRIDE;

@@ -381,7 +381,10 @@ OSCAR_API int oscar_extend_attn(const oscar_layer_cache *cache,
                                 float sm_scale, float *out,
                                 oscar_stream_t stream);
 
-/* Workspace for oscar_bf16_paged_decode. */
+/* Workspace for oscar_bf16_paged_decode (device, any alignment >= 256 B):
+ * the partials of the splits, then one merge counter per (request, KV head),
+ * with the contract of oscar_decode_workspace_bytes: zero-filled before its
+ * first use, left with zero counters by every call that completes. */
 OSCAR_API size_t oscar_bf16_decode_workspace_bytes(int32_t batch, int32_t n_q_heads,
                                          int32_t n_kv_heads,
                                          int32_t max_seq_len);
@@ -391,9 +394,11 @@ OSCAR_API size_t oscar_bf16_decode_workspace_bytes(int32_t batch, int32_t n_q_he
  * kv_pages: device bf16 [n_pages][Hkv][2][16][128] (same page format as
  * the BF16 pool); pt: device int32 [batch][pt_stride] — token p of request
  * b is row p%16 of page pt[b][p/16]; other arguments as oscar_decode_attn.
- * status: device uint32 or NULL (OSCAR_STATUS_* bits).
- * The workspace (oscar_bf16_decode_workspace_bytes) may hold anything on
- * entry; calls that share a workspace must not run concurrently. */
+ * status: device uint32 or NULL (OSCAR_STATUS_* bits).  Split plan and
+ * merge as in oscar_decode_attn (one round of one workgroup per CU with the
+ * merge inside the kernel when the batch allows).  The workspace
+ * (oscar_bf16_decode_workspace_bytes) is zero-filled before its first use;
+ * calls that share a workspace must not run concurrently. */
 OSCAR_API int oscar_bf16_paged_decode(const uint16_t *q, const uint16_t *kv_pages,
                             int64_t n_pages, const int32_t *pt,
                             int32_t pt_stride, const int32_t *seq_lens,

@@ -443,6 +443,29 @@ def test_bf16_decode_reuses_workspace(oscar):
         out = oscar.bf16_paged_decode(*args, workspace=ws)
         torch.cuda.synchronize()
         assert_decode_close(out.cpu().numpy(), ref, "bf16 repeated")
+        assert int(ws[-256:].count_nonzero().item()) == 0   # merge counters back at zero
+
+
+def test_bf16_decode_one_round_many_splits(oscar):
+    # one request at 20K over 2 KV heads: one round of workgroups, 125
+    # splits per head, merged inside the kernel in several register windows
+    L, hq, hkv = 20000, 8, 2
+    ld = synth.LayerData(1350, 0, hq, hkv)
+    k, v = ld.cache_kv(L)
+    pt, npages = synth.shuffled_page_tables(1350, 0, [L], n_pages_fn=lambda n: (n + 15) // 16)
+    pages = np.zeros((npages, hkv, 2, 16, 128), dtype=np.uint16)
+    p = np.arange(L)
+    pages[pt[0, p // 16], :, 0, p % 16] = k
+    pages[pt[0, p // 16], :, 1, p % 16] = v
+    q = ld.decode_q(1)
+    ref = o.bf16_paged_decode(q, pages, pt, [L], SCALE)
+    ws = torch.zeros(oscar.bf16_decode_workspace_bytes(1, hq, hkv, L), dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        out = oscar.bf16_paged_decode(to_dev_bf16(q), to_dev_bf16(pages), torch.from_numpy(pt).cuda(),
+                                      torch.tensor([L], dtype=torch.int32, device="cuda"), L, SCALE, workspace=ws)
+        torch.cuda.synchronize()
+        assert_decode_close(out.cpu().numpy(), ref, "bf16 one round")
+        assert int(ws[-256:].count_nonzero().item()) == 0
 
 
 # ------------------------------------------------------------------ long splits
