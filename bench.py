@@ -473,6 +473,14 @@ def decode_main(args, W, dev, workload):
     layers = []
     bf16_layers = []
     pages_per_req = [synth.hist_pages_needed(int(L)) for L in final_lens]
+    bulk = None
+    if "bf16_bytes_note" in W:
+        # the capacity workloads draw every layer's prefill tokens into the
+        # same buffers (per-layer allocations of ~17 GB between the pools
+        # fragment the caching allocator)
+        nel = int(start_lens.sum()) * hkv * HEAD_DIM
+        bulk = (torch.empty(nel, dtype=torch.bfloat16, device=dev), torch.empty(nel, dtype=torch.bfloat16, device=dev),
+                torch.empty(nel, dtype=torch.float32, device=dev))
     for l in range(nl):
         ly = Layer()
         ld = synth.LayerData(args.seed, l, hq, hkv)
@@ -496,19 +504,15 @@ def decode_main(args, W, dev, workload):
                                     device=dev, code_bits=bits)
         # prefill: every request's first start_len tokens in one write call
         tot = int(start_lens.sum())
-        k = synth.kv_device(synth.device_generator(args.seed, l, synth.S_CACHE_K), tot, ld.outliers, dev)
-        v = synth.kv_device(synth.device_generator(args.seed, l, synth.S_CACHE_V), tot, ld.outliers, dev)
+        kw = dict(out=bulk[0], work=bulk[2]) if bulk else {}
+        vw = dict(out=bulk[1], work=bulk[2]) if bulk else {}
+        k = synth.kv_device(synth.device_generator(args.seed, l, synth.S_CACHE_K), tot, ld.outliers, dev, **kw)
+        v = synth.kv_device(synth.device_generator(args.seed, l, synth.S_CACHE_V), tot, ld.outliers, dev, **vw)
         cu = torch.from_numpy(np.concatenate([[0], np.cumsum(start_lens)]).astype(np.int32)).to(dev)
         oscar.write_kv(ly.cache, ly.rk, ly.rv, k, v, cu, torch.zeros(B, dtype=torch.int32, device=dev),
                        int(start_lens.max()))
-        if "bf16_bytes_note" in W:
-            # free the bulk tokens (and hand their segments back) before the
-            # next layer allocates its pool and draws its own: otherwise the
-            # caching allocator fragments ~100-200 GB of pools
-            torch.cuda.synchronize()
-            del k, v
-            torch.cuda.empty_cache()
-            k = v = None
+        if bulk:
+            torch.cuda.synchronize()   # the write has read the bulk tokens before the next layer redraws them
         # per-step inputs (the same new token and query every step)
         ly.k_new = synth.kv_device(synth.device_generator(args.seed, l, synth.S_NEW_K), B, ld.outliers, dev)
         ly.v_new = synth.kv_device(synth.device_generator(args.seed, l, synth.S_NEW_V), B, ld.outliers, dev)
@@ -543,6 +547,8 @@ def decode_main(args, W, dev, workload):
             print(f"setup: {l + 1}/{nl} layers calibrated and prefilled ({time.time() - t_setup:.0f} s)",
                   file=sys.stderr, flush=True)
     torch.cuda.synchronize()
+    bulk = None
+    torch.cuda.empty_cache()
     for ly in layers:
         assert int(ly.cache.status.item()) == 0, "prefill flagged bad data"
     setup_s = time.time() - t_setup

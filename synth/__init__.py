@@ -163,15 +163,26 @@ def device_generator(base_seed: int, layer: int, stream: int, device="cuda"):
     return g
 
 
-def kv_device(gen, n: int, outliers: np.ndarray, device="cuda"):
-    """bf16 [n][Hkv][128] ~ N(0, 1) with the outlier channels scaled x20."""
+def kv_device(gen, n: int, outliers: np.ndarray, device="cuda", out=None, work=None):
+    """bf16 [n][Hkv][128] ~ N(0, 1) with the outlier channels scaled x20.
+    out (bf16) and work (fp32), both with at least n * Hkv * 128 elements,
+    optionally receive the values and hold the fp32 draw (no allocation)."""
     import torch
     hkv = outliers.shape[0]
     scale = torch.ones((hkv, HEAD_DIM), dtype=torch.float32)
     for h in range(hkv):
         scale[h, torch.as_tensor(outliers[h])] = 20.0
-    x = torch.randn((n, hkv, HEAD_DIM), generator=gen, device=device, dtype=torch.float32)
+    shape = (n, hkv, HEAD_DIM)
+    if work is not None:
+        x = work.view(-1)[: n * hkv * HEAD_DIM].view(shape)
+        torch.randn(shape, generator=gen, device=device, dtype=torch.float32, out=x)
+    else:
+        x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
     x.mul_(scale.to(device))
+    if out is not None:
+        y = out.view(-1)[: n * hkv * HEAD_DIM].view(shape)
+        y.copy_(x)
+        return y
     return x.to(torch.bfloat16)
 
 
