@@ -145,8 +145,6 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // bits 8-9 / 24-25) and 1 + c/16 (mask 0x00C0, bits 6-7 / 22-23) after one of
 // four shifts (none, >>4, <<4, rotate right 8).  The constant 1 and the 1/4,
 // 1/16 weights are undone by the operand on the other side of the product.
-__device__ inline uint32_t ex4(uint32_t x) { return (x & 0x03000300u) | 0x3C003C00u; }
-__device__ inline uint32_t ex16(uint32_t x) { return (x & 0x00C000C0u) | 0x3C003C00u; }
 __device__ inline uint32_t rotr8(uint32_t x) { return __builtin_amdgcn_alignbit(x, x, 8); }
 
 __device__ inline f16x8 as_f16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -158,21 +156,28 @@ __device__ inline f16x4 as_f16x4(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(f16x4, u);
 }
 
-// K code block k (channels 32k..32k+31) as the A operand of a 16x16x32 MFMA
-__device__ inline f16x8 expand_k(uint32_t w0, uint32_t w1, int k) {
-  const uint32_t w = (k < 2) ? w0 : w1;
-  const uint32_t x0 = (k & 1) ? (w << 4) : w;
-  const uint32_t x1 = (k & 1) ? rotr8(w) : (w >> 4);
-  return as_f16x8(ex4(x0), ex16(x0), ex4(x1), ex16(x1));
-}
+// (x & m) | e.  m and e arrive as kernel arguments, so the compiler cannot
+// fold them into literals and forms one v_and_or_b32 (a VOP3 instruction,
+// which takes no literal on gfx950) instead of an AND and an OR; plain C++
+// keeps the compiler's hazard tracking between these writes and the matrix
+// instructions that read them.
+__device__ inline uint32_t and_or(uint32_t x, uint32_t m, uint32_t e) { return (x & m) | e; }
 
-// V code row-block r (channels 16r..16r+15) as the A operand of a 16x16x16 MFMA
-__device__ inline f16x4 expand_v(uint32_t w0, uint32_t w1, int r) {
-  const uint32_t w = (r < 4) ? w0 : w1;
-  const int s = r & 3;
-  const uint32_t x = s == 0 ? w : s == 1 ? (w >> 4) : s == 2 ? (w << 4) : rotr8(w);
-  return as_f16x4(ex4(x), ex16(x));
-}
+struct Expander {
+  uint32_t m4, m16, e;  // 0x03000300, 0x00C000C0, 0x3C003C00
+  __device__ f16x8 k(uint32_t w0, uint32_t w1, int kb) const {
+    const uint32_t w = (kb < 2) ? w0 : w1;
+    const uint32_t x0 = (kb & 1) ? (w << 4) : w;
+    const uint32_t x1 = (kb & 1) ? rotr8(w) : (w >> 4);
+    return as_f16x8(and_or(x0, m4, e), and_or(x0, m16, e), and_or(x1, m4, e), and_or(x1, m16, e));
+  }
+  __device__ f16x4 v(uint32_t w0, uint32_t w1, int r) const {
+    const uint32_t w = (r < 4) ? w0 : w1;
+    const int s = r & 3;
+    const uint32_t x = s == 0 ? w : s == 1 ? (w >> 4) : s == 2 ? (w << 4) : rotr8(w);
+    return as_f16x4(and_or(x, m4, e), and_or(x, m16, e));
+  }
+};
 
 __device__ inline f32x4 mfma_k(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);

@@ -698,29 +698,6 @@ struct RingRead4 {
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 __device__ inline h2v as_h2(uint32_t w) { return __builtin_bit_cast(h2v, w); }
 
-// (x & m) | e.  m and e arrive as kernel arguments, so the compiler cannot
-// fold them into literals and forms one v_and_or_b32 (a VOP3 instruction,
-// which takes no literal on gfx950) instead of an AND and an OR; plain C++
-// keeps the compiler's hazard tracking between these writes and the matrix
-// instructions that read them.
-__device__ inline uint32_t and_or(uint32_t x, uint32_t m, uint32_t e) { return (x & m) | e; }
-
-struct Expander {
-  uint32_t m4, m16, e;  // 0x03000300, 0x00C000C0, 0x3C003C00
-  __device__ f16x8 k(uint32_t w0, uint32_t w1, int kb) const {
-    const uint32_t w = (kb < 2) ? w0 : w1;
-    const uint32_t x0 = (kb & 1) ? (w << 4) : w;
-    const uint32_t x1 = (kb & 1) ? rotr8(w) : (w >> 4);
-    return as_f16x8(and_or(x0, m4, e), and_or(x0, m16, e), and_or(x1, m4, e), and_or(x1, m16, e));
-  }
-  __device__ f16x4 v(uint32_t w0, uint32_t w1, int r) const {
-    const uint32_t w = (r < 4) ? w0 : w1;
-    const int s = r & 3;
-    const uint32_t x = s == 0 ? w : s == 1 ? (w >> 4) : s == 2 ? (w << 4) : rotr8(w);
-    return as_f16x4(and_or(x, m4, e), and_or(x, m16, e));
-  }
-};
-
 // INT4 codes as fp16 1 + c/16: a nibble moved to mantissa bits 6-9 (and
 // 22-25 for the high half) under the exponent of 1.0.  Pair p of a dword
 // holds nibbles p and p + 4, so the four pairs of a K dword are channels

@@ -50,6 +50,7 @@ struct ExtendArgs {
   int64_t total_tokens;  // rows of q / k_new / v_new / out
   float scale_log2;  // sm_scale * log2(e)
   float pv_scale;    // power of two: p s_V pv_scale stays below 2^15 (fp16 operand)
+  uint32_t ex_m4, ex_m16, ex_e;  // code expansion constants 0x03000300, 0x00C000C0, 0x3C003C00
   float *out;
 };
 
@@ -89,42 +90,52 @@ __device__ inline void split_bf16(const float (&x)[4], s16x4 &hi, s16x4 &lo) {
 
 // Online-softmax state of one part of the keys: the BF16 keys (sink, window,
 // chunk; acc = O^T in the original basis) or the INT2 history (acc = O^T in
-// the rotated basis, plus the zero-point sums per group).  The two parts are
-// merged at the end, so only one part's accumulators are live at a time.
+// the rotated basis, cacc = the column sums of the PV operands per group,
+// which the expansion's constant 1 adds to acc, and the zero-point sums per
+// group).  The two parts are merged at the end, so only one part's
+// accumulators are live at a time.
 template <int NZ>
 struct SoftState {
   f32x4 acc[8];
+  f32x4 cacc[NZ > 0 ? NZ : 1];
   float zacc[NZ > 0 ? NZ : 1];  // sum_t p_t z_t of the lane's keys, per group
   float m, l;                   // running max (log2 units) of the lane's query; lane-partial sum
   __device__ void init() {
     for (int b = 0; b < 8; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int g = 0; g < (NZ > 0 ? NZ : 1); ++g) zacc[g] = 0.f;
+    for (int g = 0; g < (NZ > 0 ? NZ : 1); ++g) {
+      cacc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+      zacc[g] = 0.f;
+    }
     m = -INFINITY;
     l = 0.f;
   }
 };
 
-// Online softmax over one tile: s[r] = scaled score of key 4(l/16)+r for the
-// lane's query (-inf where masked); p[r] receives the probabilities relative
-// to the running max.  The running max is raised only when a score exceeds it
-// by more than 2^LAZY_TH (so p <= 2^LAZY_TH); the accumulators are rescaled
-// only in the waves where some query's max was raised.
+// Online softmax over one tile: s[r] * sc = score of key 4(l/16)+r for the
+// lane's query in log2 units (-inf where masked; sc > 0); p[r] receives the
+// probabilities relative to the running max.  The running max is raised
+// only when a score exceeds it by more than 2^LAZY_TH (so p <= 2^LAZY_TH);
+// the accumulators are rescaled only in the waves where some query's max was
+// raised.
 template <int NZ>
-__device__ inline void softmax_tile(SoftState<NZ> &st, const float (&s)[4], float (&p)[4]) {
-  const float mx = lanes4_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+__device__ inline void softmax_tile(SoftState<NZ> &st, const float (&s)[4], float (&p)[4], float sc = 1.f) {
+  const float mx = lanes4_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))) * sc;
   const bool raise = mx > st.m + LAZY_TH;  // false while both are -inf
   if (__builtin_amdgcn_ballot_w64(raise)) {
     const float mn = raise ? mx : st.m;
     const float alpha = raise ? __builtin_amdgcn_exp2f(st.m - mn) : 1.f;  // st.m = -inf: 0
     st.l *= alpha;
     for (int b = 0; b < 8; ++b) st.acc[b] *= alpha;
-    for (int g = 0; g < NZ; ++g) st.zacc[g] *= alpha;
+    for (int g = 0; g < NZ; ++g) {
+      st.cacc[g] *= alpha;
+      st.zacc[g] *= alpha;
+    }
     st.m = mn;
   }
   const float ref = st.m == -INFINITY ? 0.f : st.m;
   float sum = 0.f;
   for (int r = 0; r < 4; ++r) {
-    p[r] = __builtin_amdgcn_exp2f(s[r] - ref);
+    p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sc, -ref));
     sum += p[r];
   }
   st.l += sum;
@@ -195,47 +206,60 @@ __device__ inline void hist_load(HistData<D / G> &hd, const uint8_t *blk, int la
   }
 }
 
-// Attention over one loaded history page, rows < n_valid.
+// Attention over one loaded history page: only rows < n_valid exist (the
+// others, and their meta, may hold anything).  (A second instance for full
+// pages, without the masks, raises the kernel's registers past two waves per
+// SIMD.)
 template <int G>
 __device__ inline void hist_tile(SoftState<D / G> &st, const HistData<D / G> &hd, int n_valid, const f16x8 (&qh)[4],
                                  const f16x8 (&ql)[4], const float (&qs)[D / G], const float (&qoff)[D / G],
-                                 float inv_kqs, float pv_scale, float pv_unscale, int lane) {
+                                 float inv_kqs, float pv_scale, const Expander &ex, int lane) {
   constexpr int NG = D / G;
   const int kq = lane >> 4;
-  float s[4] = {0.f, 0.f, 0.f, 0.f};
+  float s[4];
   for (int g = 0; g < NG; ++g) {
-    f32x4 d = {0.f, 0.f, 0.f, 0.f};
+    // starts at minus the sum of the operands: the expansion's constant 1
+    // comes off in the accumulator, d = sum_c c q_c (q carries 1/w, the
+    // softmax scale and kqs)
+    f32x4 d = {-qoff[g], -qoff[g], -qoff[g], -qoff[g]};
     for (int kb = g * G / 32; kb < (g + 1) * G / 32; ++kb) {
-      const f16x8 x = expand_k(hd.kc[0], hd.kc[1], kb);  // 1 + c w, w = 1/4 or 1/16
+      const f16x8 x = ex.k(hd.kc[0], hd.kc[1], kb);  // 1 + c w, w = 1/4 or 1/16
       d = mfma_k(x, ql[kb], d);
       d = mfma_k(x, qh[kb], d);
     }
-    // d - qoff = sum_c c q_c (q carries 1/w and the softmax scale)
-    for (int r = 0; r < 4; ++r) s[r] += lo_f16(hd.km[g][r]) * (d[r] - qoff[g]) + hi_f16(hd.km[g][r]) * qs[g];
+    for (int r = 0; r < 4; ++r) {
+      const float v = fmaf(lo_f16(hd.km[g][r]), d[r], hi_f16(hd.km[g][r]) * qs[g]);
+      s[r] = g == 0 ? v : s[r] + v;
+    }
   }
   bool ok[4];
   float p[4];
   for (int r = 0; r < 4; ++r) {
     ok[r] = 4 * kq + r < n_valid;
-    s[r] = ok[r] ? s[r] * inv_kqs : -INFINITY;
+    s[r] = ok[r] ? s[r] : -INFINITY;
   }
-  softmax_tile(st, s, p);
+  softmax_tile(st, s, p, inv_kqs);  // scores in kqs units
   // A = 1 + c w (w = 1/4 for rows 0, 1 of the lane's four keys, 1/16 for
-  // rows 2, 3), B = fp16(p s k / w): the product is B + c p s k; the sum of
-  // the B as rounded leaves through the zero-point accumulator
+  // rows 2, 3), B = fp16(p s k / w): the product is B + c p s k; the column
+  // sums of B come off at the end (cacc: the same B against an all-ones
+  // operand), the zero points enter as sum_t p_t z_t
+  const f16x4 ones = as_f16x4(0x3C003C00u, 0x3C003C00u);
+  float pw[4];
+  for (int r = 0; r < 4; ++r) pw[r] = p[r] * (pv_scale * (r < 2 ? 4.f : 16.f));
   for (int g = 0; g < NG; ++g) {
     f16x4 bp;
     for (int r = 0; r < 4; ++r) {
-      const float wi = r < 2 ? 4.f : 16.f;
-      bp[r] = _Float16(ok[r] ? p[r] * (pv_scale * wi) * lo_f16(hd.vm[g][r]) : 0.f);
-      st.zacc[g] += ok[r] ? fmaf(p[r], hi_f16(hd.vm[g][r]), -float(bp[r]) * pv_unscale) : 0.f;
+      bp[r] = _Float16(ok[r] ? pw[r] * lo_f16(hd.vm[g][r]) : 0.f);
+      st.zacc[g] = ok[r] ? fmaf(p[r], hi_f16(hd.vm[g][r]), st.zacc[g]) : st.zacc[g];
     }
-    for (int b = g * G / 16; b < (g + 1) * G / 16; ++b) st.acc[b] = mfma_v(expand_v(hd.vc[0], hd.vc[1], b), bp, st.acc[b]);
+    st.cacc[g] = mfma_v(ones, bp, st.cacc[g]);
+    for (int b = g * G / 16; b < (g + 1) * G / 16; ++b) st.acc[b] = mfma_v(ex.v(hd.vc[0], hd.vc[1], b), bp, st.acc[b]);
   }
 }
 
 template <int GQA, int G>
-__global__ void __launch_bounds__(64 * (GQA < 4 ? GQA : 4)) extend_kernel(ExtendArgs a) {
+__global__ void __launch_bounds__(64 * (GQA < 4 ? GQA : 4)) __attribute__((amdgpu_waves_per_eu(2)))
+extend_kernel(ExtendArgs a) {
   constexpr int WAVES = GQA < 4 ? GQA : 4;
   constexpr int NG = D / G;
   __shared__ float buf_all[WAVES][2][EXT_TILE * D];
@@ -392,6 +416,13 @@ __global__ void __launch_bounds__(64 * (GQA < 4 ? GQA : 4)) extend_kernel(Extend
   const float pv_unscale = 1.f / a.pv_scale;
   SoftState<NG> sh;
   sh.init();
+  Expander ex;
+  ex.m4 = a.ex_m4;
+  ex.m16 = a.ex_m16;
+  ex.e = a.ex_e;
+  // the exponent pattern in a VGPR, the masks in SGPRs: one v_and_or_b32
+  // per expanded register (the empty asm emits nothing)
+  asm volatile("" : "+v"(ex.e));
   const int nht = n_hist_tokens(L0), nhp = n_hist_pages(L0);
   const int32_t *hpt = a.hist_pt + int64_t(b) * a.hist_pt_stride;
   const int blk_bytes = hist_block_bytes(G);
@@ -412,7 +443,7 @@ __global__ void __launch_bounds__(64 * (GQA < 4 ? GQA : 4)) extend_kernel(Extend
         return;
       }
       const int nv = nht - PAGE * j < PAGE ? nht - PAGE * j : PAGE;
-      hist_tile<G>(sh, hd, nv, qh, ql, qs, qoff, inv_kqs, a.pv_scale, pv_unscale, lane);
+      hist_tile<G>(sh, hd, nv, qh, ql, qs, qoff, inv_kqs, a.pv_scale, ex, lane);
     };
     HistData<NG> d0, d1;
     int p0 = page_id(0), p1 = -1;
@@ -443,7 +474,7 @@ __global__ void __launch_bounds__(64 * (GQA < 4 ? GQA : 4)) extend_kernel(Extend
   for (int bb = 0; bb < 8; ++bb)
     for (int r = 0; r < 4; ++r) {
       const int c = 16 * bb + 4 * kq + r;
-      buf[c * EXT_TILE + m] = fmaf(sh.acc[bb][r], pv_unscale, sh.zacc[c / G]) * f2;
+      buf[c * EXT_TILE + m] = fmaf(sh.acc[bb][r] - sh.cacc[c / G][r], pv_unscale, sh.zacc[c / G]) * f2;
     }
   __syncthreads();
   float o[EXT_TILE][2];
@@ -518,6 +549,9 @@ hipError_t launch_extend(const oscar_layer_cache &c, RotArg rk, RotArg rv, const
   while (vmax * k > 32768.f) k *= 0.5f;
   while (vmax * k * 2.f <= 32768.f && k < 65536.f) k *= 2.f;
   a.pv_scale = k;
+  a.ex_m4 = 0x03000300u;
+  a.ex_m16 = 0x00C000C0u;
+  a.ex_e = 0x3C003C00u;
   a.out = out;
   switch (n_q_heads / c.n_kv_heads) {
     case 1: return launch_gqa<1>(a, c.group, batch, max_new, s);
