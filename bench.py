@@ -29,8 +29,7 @@ token are timed as well.  Its line names its own metric (write GB/s).
 28 requests x 100000 tokens, GQA 8, G = 128, ~104 GB of INT2 cache; its
 all-BF16 copy does not fit one GPU), `--workload int4_28x100k` the same
 tokens from an INT4 cache (~195 GB: the 4-bit comparison point of the
-capacity result; one step per layer is the write of the new token followed by
-the decode, since the fused append step is INT2-only), and `--workload
+capacity result), and `--workload
 config0` the single-layer 4096-token correctness configuration (8 query / 2
 KV heads, G = 32).
 
@@ -67,8 +66,8 @@ HEAD_DIM = 128
 def parse_args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=30)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", choices=["bs1", "bs64", "write", "28x100k", "int4_28x100k", "extend", "config0"],
                    default=None,
                    help="default: bs1, with every other workload's figures added to its line")
@@ -556,18 +555,11 @@ def decode_main(args, W, dev, workload):
     # ---------------------------------------------------------------- the step
     lens_before = torch.from_numpy(start_lens.astype(np.int32)).to(dev)   # before this step's append
     lens_after = lens_before + 1
-    cu_one = torch.arange(B + 1, dtype=torch.int32, device=dev)           # one new token per request
 
     def step():
         for ly in layers:
-            if bits == 2:
-                oscar.decode_step(ly.cache, ly.rk, ly.rv, ly.k_new, ly.v_new, lens_before, ly.q, max_len,
-                                  1 / math.sqrt(HEAD_DIM), out=ly.out, workspace=ly.ws)
-            else:
-                # INT4: the write of the new token, then the decode
-                oscar.write_kv(ly.cache, ly.rk, ly.rv, ly.k_new, ly.v_new, cu_one, lens_before, 1)
-                oscar.decode_attn(ly.cache, ly.rk, ly.rv, ly.q, lens_after, max_len, 1 / math.sqrt(HEAD_DIM),
-                                  out=ly.out, workspace=ly.ws)
+            oscar.decode_step(ly.cache, ly.rk, ly.rv, ly.k_new, ly.v_new, lens_before, ly.q, max_len,
+                              1 / math.sqrt(HEAD_DIM), out=ly.out, workspace=ly.ws)
         lens_before.add_(1)
         lens_after.add_(1)
 
@@ -688,9 +680,7 @@ def decode_main(args, W, dev, workload):
         "config": {"workload": W["name"], "layers": nl, "batch": B, "q_heads": hq, "kv_heads": hkv, "group": G,
                    "context": int(max_len) if B == 1 else [int(W["len_lo"]), int(W["len_hi"])],
                    "code_bits": bits,
-                   "step": "per layer: oscar_decode_step (write-on-append of one token + INT2 paged decode)"
-                           if bits == 2 else
-                           "per layer: oscar_write_kv of one token per request + oscar_decode_attn (INT4)"},
+                   "step": f"per layer: oscar_decode_step (write-on-append of one token + INT{bits} paged decode)"},
         "tokens_per_s": round(tokens_per_s, 1),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -360,7 +360,6 @@ int oscar_decode_step(const oscar_layer_cache *cache, const oscar_rotation *rot_
                       float sm_scale, float *out, void *workspace, size_t workspace_bytes,
                       oscar_stream_t stream) {
   if (int rc = check_cache(cache)) return rc;
-  if (int rc = check_int2(cache, "decode_step")) return rc;
   if (int rc = check_rot(rot_k, "rot_k")) return rc;
   if (int rc = check_rot(rot_v, "rot_v")) return rc;
   if (int rc = check_heads(n_q_heads, cache->n_kv_heads)) return rc;

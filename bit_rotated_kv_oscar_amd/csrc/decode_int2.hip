@@ -245,7 +245,8 @@ struct EvictWork {
 
 // Append, raw workgroup: the token at position L0 - 128 leaves the recent
 // window (OSCAR write path, gist.science technical summaries section 2.2:
-// rotate, clip, quantise per group into the paged INT2 history).  Its K and
+// rotate, clip, quantise per group into the paged INT2 -- or INT4 --
+// history).  Its K and
 // V are read from their ring row and rotated by R_K / R_V, clipped and
 // quantised (G channels per group), and its row of history block `blk` (null:
 // bad page id) is written: the K codes and the meta are dwords of its own; the
@@ -254,9 +255,10 @@ struct EvictWork {
 // dequantised and rotated back (e.u; q.k is the same in either basis) with its
 // score per query head (e.sc): the history workgroups leave its row out,
 // since their copy of the page may predate this write.  Workgroup-wide.
-template <int GQA, int G>
+template <int GQA, int G, int BITS>
 __device__ void evict_token(const StepArgs &a, int b, int hk, int tid, int wave, const AppendPlan &ap, uint8_t *blk,
                             EvictWork &e) {
+  constexpr int LEVELS = (1 << BITS) - 1;
   const oscar_layer_cache &c = a.c;
   const int hkv = c.n_kv_heads, lane = tid & 63;
   const int jr = tid >> 3, qq = tid & 7;  // rows jr, jr + 64; inputs 32k + 4qq .. + 3
@@ -341,9 +343,9 @@ __device__ void evict_token(const StepArgs &a, int b, int hk, int tid, int wave,
     lo = seg_min<G>(xc, lane);
     hi = seg_max<G>(xc, lane);
   }
-  const float sq = __half2float(__float2half_rn((hi - lo) / 3.0f));
+  const float sq = __half2float(__float2half_rn((hi - lo) / float(LEVELS)));
   const float zq = __half2float(__float2half_rn(lo));
-  const int code = sq > 0.f ? min(3, max(0, int(rintf((xc - zq) / sq)))) : 0;
+  const int code = sq > 0.f ? min(LEVELS, max(0, int(rintf((xc - zq) / sq)))) : 0;
   if (tid < 2 * D) {
     e.codes[v][ch] = uint8_t(code);
     e.d[v][ch] = fmaf(sq, float(code), zq);
@@ -354,7 +356,33 @@ __device__ void evict_token(const StepArgs &a, int b, int hk, int tid, int wave,
   }
   __syncthreads();
   // ---- the row in history (layouts of the code dwords: include/oscar.h)
-  if (blk) {
+  if (blk && BITS == 4) {
+    const int row = ap.evict_row;
+    if (tid < 16) {
+      // K: dwords i of lanes 16q + row hold channels 32i + 8q + j of token
+      // `row`, channel offset j = 2 (e % 4) + e / 4 in nibble e
+      const int q = tid >> 2, i = tid & 3;
+      uint32_t w = 0;
+      for (int ee = 0; ee < 8; ++ee) w |= uint32_t(e.codes[0][32 * i + 8 * q + 2 * (ee % 4) + ee / 4]) << (4 * ee);
+      *reinterpret_cast<uint32_t *>(blk + k_codes_off(G, 4) + 4 * (4 * (16 * q + row) + i)) = w;
+    } else if (tid >= 64 && tid < 128) {
+      // V: token `row` (quad q = row / 4, k = row % 4) is nibble e0 (channel
+      // 16 (2d) + m) and e0 + 2 (channel 16 (2d + 1) + m) of dword d of lane
+      // 16 q + m, with k = 2 (e0 % 2) + e0 / 4
+      const int t = tid - 64, m = t & 15, d = t >> 4, q = row >> 2, k = row & 3;
+      const int e0 = (k & 1) * 4 + (k >> 1);
+      const uint32_t w = (uint32_t(e.codes[1][16 * (2 * d) + m]) << (4 * e0)) |
+                         (uint32_t(e.codes[1][16 * (2 * d + 1) + m]) << (4 * (e0 + 2)));
+      const uint32_t mask = (0xFu << (4 * e0)) | (0xFu << (4 * (e0 + 2)));
+      uint32_t *p = reinterpret_cast<uint32_t *>(blk + v_codes_off(G, 4) + 4 * (4 * (16 * q + m) + d));
+      *p = (*p & ~mask) | w;
+    } else if (tid >= 128 && tid < 128 + 2 * (D / G)) {
+      const int vec = (tid - 128) / (D / G), g = (tid - 128) % (D / G);
+      const uint32_t w = uint32_t(__half_as_ushort(__float2half_rn(e.sz[vec][2 * g]))) |
+                         (uint32_t(__half_as_ushort(__float2half_rn(e.sz[vec][2 * g + 1]))) << 16);
+      *reinterpret_cast<uint32_t *>(blk + (vec ? v_meta_off(G, 4) : k_meta_off(G, 4)) + 4 * (PAGE * g + row)) = w;
+    }
+  } else if (blk) {
     const int row = ap.evict_row;
     if (tid < 8) {
       // K: the 8 dwords of token `row` (lanes 16q + row, halves d)
@@ -1451,18 +1479,15 @@ attend_kernel(StepArgs a) {
       st.compute(ld, valid, lane);
     }
     st.finish(o_w, m_lds + wave * GQA, l_lds + wave * GQA, lane);
-    // (appends reach only INT2 caches: the host refuses them for INT4)
-    if constexpr (BITS == 2) {
-      if (append && ap.evict && ap.raw_page >= 0) {
-        const int pid = c.hist_pt[int64_t(b) * c.hist_pt_stride + ap.evict_j];
-        uint8_t *blk = nullptr;
-        if (pid >= 0 && pid < c.n_hist_pages)
-          blk = c.hist + (int64_t(pid) * c.n_kv_heads + hk) * hist_block_bytes(D / NG);
-        else if (tid == 0)
-          flag_status(c.status, OSCAR_STATUS_BAD_PAGE);
-        evict_token<GQA, D / NG>(a, b, hk, tid, wave, ap, blk, work.e);
-        extra = true;
-      }
+    if (append && ap.evict && ap.raw_page >= 0) {
+      const int pid = c.hist_pt[int64_t(b) * c.hist_pt_stride + ap.evict_j];
+      uint8_t *blk = nullptr;
+      if (pid >= 0 && pid < c.n_hist_pages)
+        blk = c.hist + (int64_t(pid) * c.n_kv_heads + hk) * hist_block_bytes(D / NG, BITS);
+      else if (tid == 0)
+        flag_status(c.status, OSCAR_STATUS_BAD_PAGE);
+      evict_token<GQA, D / NG, BITS>(a, b, hk, tid, wave, ap, blk, work.e);
+      extra = true;
     }
   } else {
     // the newest history token has just left the recent window in an

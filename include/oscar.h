@@ -140,7 +140,7 @@ typedef struct oscar_layer_cache {
   const int32_t *bf16_pt;  /* device int32 [batch][9]                        */
   uint32_t *status;        /* device, may be NULL: OSCAR_STATUS_* bits       */
   int32_t code_bits;       /* history code width: 2 (INT2; 0 also means 2)
-                              or 4 (INT4: write and decode_attn only)      */
+                              or 4 (INT4: every entry point but extend)    */
 } oscar_layer_cache;
 
 /* Device forms of one fixed per-layer rotation R = U*H*P ([nl] §2.2.A
@@ -340,8 +340,7 @@ OSCAR_API int oscar_decode_attn_noalloc(const oscar_layer_cache *cache,
  * must be <= max_seq_len.  Same result as oscar_write_kv with one token per
  * request followed by oscar_decode_attn, in one kernel launch.  The
  * workspace is the one of oscar_decode_attn (oscar_decode_workspace_bytes,
- * zero-filled before its first use).  INT2 caches only (code_bits 4:
- * OSCAR_EUNSUPPORTED). */
+ * zero-filled before its first use).  INT2 or INT4 caches. */
 OSCAR_API int oscar_decode_step(const oscar_layer_cache *cache,
                                 const oscar_rotation *rot_k,
                                 const oscar_rotation *rot_v,

@@ -16,7 +16,7 @@ import torch
 from oracle import oscar_ref as o
 from tests.parity_tools import (Scenario, assert_decode_close, assert_history_ok, bf16_pool_bits,
                                 compare_history, decode_error, to_dev_bf16)
-from tests.test_gpu_parity import check_raw_rows, gpu_cache, gpu_decode, gpu_rotations, gpu_write
+from tests.test_gpu_parity import _prefix_cache, check_raw_rows, gpu_cache, gpu_decode, gpu_rotations, gpu_write
 
 pytestmark = pytest.mark.gpu
 
@@ -191,15 +191,72 @@ def test_int4_bad_page_flagged_not_followed(oscar):
     assert np.isfinite(out).all()
 
 
-def test_int4_refused_by_append_and_extend(oscar):
+def test_int4_extend_refused(oscar):
     sc = Scenario(3100, 8, 2, 64, [300], bits=4)
     cache = gpu_cache(oscar, sc)
     rk, rv = gpu_rotations(oscar, sc)
     k1 = torch.zeros((1, 2, 128), dtype=torch.bfloat16, device="cuda")
     q1 = torch.zeros((1, 8, 128), dtype=torch.bfloat16, device="cuda")
     lb = torch.tensor([300], dtype=torch.int32, device="cuda")
-    with pytest.raises(RuntimeError, match="INT2 caches only"):
-        oscar.decode_step(cache, rk, rv, k1, k1, lb, q1, 301, SCALE)
     cu = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
     with pytest.raises(RuntimeError, match="INT2 caches only"):
         oscar.extend_attn(cache, rk, rv, q1, k1, k1, cu, lb, 1, 300, SCALE)
+
+
+# ------------------------------------------------------------------ append + decode
+
+
+def _last_tokens(sc, s):
+    k = np.stack([t[L - s] for t, L in zip(sc.tok_k, sc.lens)])
+    v = np.stack([t[L - s] for t, L in zip(sc.tok_v, sc.lens)])
+    return to_dev_bf16(k), to_dev_bf16(v)
+
+
+@pytest.mark.parametrize("G,rot", [(32, "random"), (64, "random"), (128, "random"), (32, "identity")])
+def test_int4_decode_step_appends_then_decodes(oscar, G, rot):
+    # the token at position L-129 leaves the window into an INT4 page
+    # whenever L - 1 >= 144 (its K dwords written whole, its V nibbles
+    # merged into dwords shared with three other rows); with the identity
+    # rotation many steps fall exactly halfway between levels
+    lens = [1, 16, 17, 143, 144, 145, 146, 160, 161, 500, 1201]
+    sc = Scenario(3200 + G, 8, 2, G, lens, rot=rot, bits=4)
+    pre = _prefix_cache(sc, 1)
+    full = sc.oracle_cache()
+    cache = gpu_cache(oscar, sc, hist=pre.hist, bf16=pre.bf16)
+    rk, rv = gpu_rotations(oscar, sc)
+    k1, v1 = _last_tokens(sc, 1)
+    before = torch.tensor([L - 1 for L in lens], dtype=torch.int32, device="cuda")
+    out = oscar.decode_step(cache, rk, rv, k1, v1, before, to_dev_bf16(sc.q), max(lens), SCALE)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) == 0
+    stats = compare_history(cache.hist.cpu().numpy(), sc.hist_pt, sc.tok_k, sc.tok_v, sc.lens,
+                            sc.R_K, sc.R_V, sc.clip_k, sc.clip_v, G, bits=4)
+    assert_history_ok(stats)
+    if rot == "identity":
+        assert stats.get("code_in_band", 0) == 0, stats
+    check_raw_rows(sc, bf16_pool_bits(cache.bf16), full)
+    assert_decode_close(out.cpu().numpy(), sc.oracle_decode(full), f"int4 decode_step G={G} {rot}")
+
+
+def test_int4_decode_step_many_steps(oscar):
+    # 40 consecutive steps: evicted tokens fill INT4 history pages row by row
+    lens = [330, 200, 150]
+    steps = 40
+    sc = Scenario(3300, 8, 2, 64, lens, bits=4)
+    pre = _prefix_cache(sc, steps)
+    full = sc.oracle_cache()
+    cache = gpu_cache(oscar, sc, hist=pre.hist, bf16=pre.bf16)
+    rk, rv = gpu_rotations(oscar, sc)
+    ws = torch.zeros(oscar.decode_workspace_bytes(len(lens), 8, 2, max(lens)), dtype=torch.uint8, device="cuda")
+    q = to_dev_bf16(sc.q)
+    for s in range(steps, 0, -1):
+        k_s, v_s = _last_tokens(sc, s)
+        before = torch.tensor([L - s for L in lens], dtype=torch.int32, device="cuda")
+        out = oscar.decode_step(cache, rk, rv, k_s, v_s, before, q, max(lens), SCALE, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) == 0
+    stats = compare_history(cache.hist.cpu().numpy(), sc.hist_pt, sc.tok_k, sc.tok_v, sc.lens,
+                            sc.R_K, sc.R_V, sc.clip_k, sc.clip_v, 64, bits=4)
+    assert_history_ok(stats)
+    check_raw_rows(sc, bf16_pool_bits(cache.bf16), full)
+    assert_decode_close(out.cpu().numpy(), sc.oracle_decode(full), "int4 decode_step x40")

@@ -336,7 +336,7 @@ def test_calibration_over_sequences_matches_oracle(oscar):
 
 def _prefix_cache(sc: Scenario, drop: int):
     """Oracle cache holding all but the last `drop` tokens of every request."""
-    ref = o.LayerCacheRef(sc.hkv, sc.G, sc.n_hist_pages, sc.n_bf16_pages, sc.hist_pt, sc.bf16_pt)
+    ref = o.LayerCacheRef(sc.hkv, sc.G, sc.n_hist_pages, sc.n_bf16_pages, sc.hist_pt, sc.bf16_pt, bits=sc.bits)
     keep = [max(0, L - drop) for L in sc.lens]
     kp = np.concatenate([t[:n] for t, n in zip(sc.tok_k, keep)])
     vp = np.concatenate([t[:n] for t, n in zip(sc.tok_v, keep)])
