@@ -68,12 +68,6 @@ int check_cache(const oscar_layer_cache *c) {
   return OSCAR_OK;
 }
 
-// Entry points that handle INT2 caches only.
-int check_int2(const oscar_layer_cache *c, const char *what) {
-  if (oscar::cache_bits(*c) != 2) return fail(OSCAR_EUNSUPPORTED, "%s supports INT2 caches only (code_bits 2)", what);
-  return OSCAR_OK;
-}
-
 int check_rot(const oscar_rotation *r, const char *name) {
   if (!r || !r->forms) return fail(OSCAR_EINVAL, "%s: rotation or its forms is NULL", name);
   if (!std::isfinite(r->clip) || r->clip <= 0.f || r->clip > 65504.f)
@@ -387,7 +381,6 @@ int oscar_extend_attn(const oscar_layer_cache *cache, const oscar_rotation *rot_
                       const int32_t *cu_new, const int32_t *len_before, int32_t batch, int64_t total_tokens,
                       int32_t max_new, int32_t max_prefix, float sm_scale, float *out, oscar_stream_t stream) {
   if (int rc = check_cache(cache)) return rc;
-  if (int rc = check_int2(cache, "extend_attn")) return rc;
   if (int rc = check_rot(rot_k, "rot_k")) return rc;
   if (int rc = check_rot(rot_v, "rot_v")) return rc;
   if (int rc = check_heads(n_q_heads, cache->n_kv_heads)) return rc;

@@ -726,21 +726,6 @@ struct RingRead4 {
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 __device__ inline h2v as_h2(uint32_t w) { return __builtin_bit_cast(h2v, w); }
 
-// INT4 codes as fp16 1 + c/16: a nibble moved to mantissa bits 6-9 (and
-// 22-25 for the high half) under the exponent of 1.0.  Pair p of a dword
-// holds nibbles p and p + 4, so the four pairs of a K dword are channels
-// 0..7 of its block in order, and pairs 0, 1 (2, 3) of a V dword are rows
-// 0..3 of its first (second) channel.
-struct Expander4 {
-  uint32_t m, e;  // 0x03C003C0, 0x3C003C00
-  __device__ uint32_t pair(uint32_t x, int p) const {
-    const uint32_t y = p == 0 ? (x << 6) : p == 1 ? (x << 2) : p == 2 ? (x >> 2) : (x >> 6);
-    return and_or(y, m, e);
-  }
-  __device__ f16x8 k(uint32_t x) const { return as_f16x8(pair(x, 0), pair(x, 1), pair(x, 2), pair(x, 3)); }
-  __device__ f16x4 v(uint32_t x, int h) const { return as_f16x4(pair(x, 2 * h), pair(x, 2 * h + 1)); }
-};
-
 // x[ch][sl] of lane src (a byte address, 4 * lane) where (ch, sl) is this
 // lane's (chain, slot) pair; ds_bpermute moves registers between lanes
 // without touching memory.

@@ -1,6 +1,7 @@
 // Extend (chunked-prefill) attention over the mixed-precision cache: the new
 // tokens of a request attend to its cached prefix -- BF16 sink and recent
-// window, INT2 history read through dequantisation in the rotated basis -- and
+// window, INT2 (or INT4) history read through dequantisation in the rotated
+// basis -- and
 // causally to the chunk's own tokens at bf16 ([abs]: paged KV layouts with
 // prefix caching; [nl]/[fr] §2.2.B: the fused kernel unpacks, dequantises
 // and inverse-rotates the INT2 history inside the attention).
@@ -24,6 +25,7 @@
 // The history accumulator stays in the rotated basis and is brought back with
 // R_V^T once per query at the end.
 #include <cmath>
+#include <type_traits>
 
 #include "attn_common.h"
 
@@ -51,6 +53,8 @@ struct ExtendArgs {
   float scale_log2;  // sm_scale * log2(e)
   float pv_scale;    // power of two: p s_V pv_scale stays below 2^15 (fp16 operand)
   uint32_t ex_m4, ex_m16, ex_e;  // code expansion constants 0x03000300, 0x00C000C0, 0x3C003C00
+  uint32_t ex_mn;                // INT4 expansion mask 0x03C003C0
+  int bits;                      // history code width (2 or 4)
   float *out;
 };
 
@@ -187,22 +191,25 @@ __device__ inline void bf16_tile(SoftState<0> &st, const uint16_t *kp, const uin
   }
 }
 
-// One INT2 history page (block of one KV head): the lane's code dwords and
-// the scale / zero entries of its four keys per group.
-template <int NG>
+// One history page (block of one KV head): the lane's code dwords (INT2: 8
+// bytes per tensor, INT4: 16) and the scale / zero entries of its four keys
+// per group.
+template <int NG, int BITS>
 struct HistData {
-  u32x2 kc, vc;
+  typedef typename std::conditional<BITS == 2, u32x2, u32x4>::type Codes;
+  Codes kc, vc;
   u32x4 km[NG], vm[NG];
 };
 
-template <int G>
-__device__ inline void hist_load(HistData<D / G> &hd, const uint8_t *blk, int lane) {
+template <int G, int BITS>
+__device__ inline void hist_load(HistData<D / G, BITS> &hd, const uint8_t *blk, int lane) {
+  typedef typename HistData<D / G, BITS>::Codes Codes;
   const int kq = lane >> 4;
-  hd.kc = *reinterpret_cast<const u32x2 *>(blk + k_codes_off(G) + 8 * lane);
-  hd.vc = *reinterpret_cast<const u32x2 *>(blk + v_codes_off(G) + 8 * lane);
+  hd.kc = *reinterpret_cast<const Codes *>(blk + k_codes_off(G, BITS) + sizeof(Codes) * lane);
+  hd.vc = *reinterpret_cast<const Codes *>(blk + v_codes_off(G, BITS) + sizeof(Codes) * lane);
   for (int g = 0; g < D / G; ++g) {
-    hd.km[g] = *reinterpret_cast<const u32x4 *>(blk + k_meta_off(G) + 4 * (16 * g + 4 * kq));
-    hd.vm[g] = *reinterpret_cast<const u32x4 *>(blk + v_meta_off(G) + 4 * (16 * g + 4 * kq));
+    hd.km[g] = *reinterpret_cast<const u32x4 *>(blk + k_meta_off(G, BITS) + 4 * (16 * g + 4 * kq));
+    hd.vm[g] = *reinterpret_cast<const u32x4 *>(blk + v_meta_off(G, BITS) + 4 * (16 * g + 4 * kq));
   }
 }
 
@@ -210,10 +217,11 @@ __device__ inline void hist_load(HistData<D / G> &hd, const uint8_t *blk, int la
 // others, and their meta, may hold anything).  (A second instance for full
 // pages, without the masks, raises the kernel's registers past two waves per
 // SIMD.)
-template <int G>
-__device__ inline void hist_tile(SoftState<D / G> &st, const HistData<D / G> &hd, int n_valid, const f16x8 (&qh)[4],
-                                 const f16x8 (&ql)[4], const float (&qs)[D / G], const float (&qoff)[D / G],
-                                 float inv_kqs, float pv_scale, const Expander &ex, int lane) {
+template <int G, int BITS>
+__device__ inline void hist_tile(SoftState<D / G> &st, const HistData<D / G, BITS> &hd, int n_valid,
+                                 const f16x8 (&qh)[4], const f16x8 (&ql)[4], const float (&qs)[D / G],
+                                 const float (&qoff)[D / G], float inv_kqs, float pv_scale, const Expander &ex,
+                                 const Expander4 &ex4, int lane) {
   constexpr int NG = D / G;
   const int kq = lane >> 4;
   float s[4];
@@ -223,7 +231,12 @@ __device__ inline void hist_tile(SoftState<D / G> &st, const HistData<D / G> &hd
     // softmax scale and kqs)
     f32x4 d = {-qoff[g], -qoff[g], -qoff[g], -qoff[g]};
     for (int kb = g * G / 32; kb < (g + 1) * G / 32; ++kb) {
-      const f16x8 x = ex.k(hd.kc[0], hd.kc[1], kb);  // 1 + c w, w = 1/4 or 1/16
+      // 1 + c w: INT2 w = 1/4 or 1/16, INT4 w = 1/16
+      f16x8 x;
+      if constexpr (BITS == 2)
+        x = ex.k(hd.kc[0], hd.kc[1], kb);
+      else
+        x = ex4.k(hd.kc[kb]);
       d = mfma_k(x, ql[kb], d);
       d = mfma_k(x, qh[kb], d);
     }
@@ -239,13 +252,13 @@ __device__ inline void hist_tile(SoftState<D / G> &st, const HistData<D / G> &hd
     s[r] = ok[r] ? s[r] : -INFINITY;
   }
   softmax_tile(st, s, p, inv_kqs);  // scores in kqs units
-  // A = 1 + c w (w = 1/4 for rows 0, 1 of the lane's four keys, 1/16 for
-  // rows 2, 3), B = fp16(p s k / w): the product is B + c p s k; the column
+  // A = 1 + c w (INT2: w = 1/4 for rows 0, 1 of the lane's four keys, 1/16
+  // for rows 2, 3; INT4: 1/16), B = fp16(p s k / w): the product is B + c p s k; the column
   // sums of B come off at the end (cacc: the same B against an all-ones
   // operand), the zero points enter as sum_t p_t z_t
   const f16x4 ones = as_f16x4(0x3C003C00u, 0x3C003C00u);
   float pw[4];
-  for (int r = 0; r < 4; ++r) pw[r] = p[r] * (pv_scale * (r < 2 ? 4.f : 16.f));
+  for (int r = 0; r < 4; ++r) pw[r] = p[r] * (pv_scale * ((BITS == 2 && r < 2) ? 4.f : 16.f));
   for (int g = 0; g < NG; ++g) {
     f16x4 bp;
     for (int r = 0; r < 4; ++r) {
@@ -253,11 +266,16 @@ __device__ inline void hist_tile(SoftState<D / G> &st, const HistData<D / G> &hd
       st.zacc[g] = ok[r] ? fmaf(p[r], hi_f16(hd.vm[g][r]), st.zacc[g]) : st.zacc[g];
     }
     st.cacc[g] = mfma_v(ones, bp, st.cacc[g]);
-    for (int b = g * G / 16; b < (g + 1) * G / 16; ++b) st.acc[b] = mfma_v(ex.v(hd.vc[0], hd.vc[1], b), bp, st.acc[b]);
+    for (int b = g * G / 16; b < (g + 1) * G / 16; ++b) {
+      if constexpr (BITS == 2)
+        st.acc[b] = mfma_v(ex.v(hd.vc[0], hd.vc[1], b), bp, st.acc[b]);
+      else
+        st.acc[b] = mfma_v(ex4.v(hd.vc[b >> 1], b & 1), bp, st.acc[b]);
+    }
   }
 }
 
-template <int GQA, int G>
+template <int GQA, int G, int BITS>
 __global__ void __launch_bounds__(64 * (GQA < 4 ? GQA : 4)) __attribute__((amdgpu_waves_per_eu(2)))
 extend_kernel(ExtendArgs a) {
   constexpr int WAVES = GQA < 4 ? GQA : 4;
@@ -341,7 +359,7 @@ extend_kernel(ExtendArgs a) {
   for (int kb = 0; kb < 4; ++kb) {
     for (int e = 0; e < 8; ++e) {
       const float x = buf[m * D + 32 * kb + 8 * kq + e] * a.scale_log2 * kqs;
-      const float y = x * ((e & 2) ? 16.f : 4.f);
+      const float y = x * ((BITS == 4 || (e & 2)) ? 16.f : 4.f);
       const _Float16 hi = _Float16(y);
       const _Float16 lo = _Float16(y - float(hi));
       qh[kb][e] = hi;
@@ -412,7 +430,7 @@ extend_kernel(ExtendArgs a) {
     }
   const float m1 = sp.m, l1 = lanes4_sum(sp.l);
 
-  // ======== INT2 history pages
+  // ======== history pages (INT2 or INT4)
   const float pv_unscale = 1.f / a.pv_scale;
   SoftState<NG> sh;
   sh.init();
@@ -423,9 +441,12 @@ extend_kernel(ExtendArgs a) {
   // the exponent pattern in a VGPR, the masks in SGPRs: one v_and_or_b32
   // per expanded register (the empty asm emits nothing)
   asm volatile("" : "+v"(ex.e));
+  Expander4 ex4;
+  ex4.m = a.ex_mn;
+  ex4.e = ex.e;
   const int nht = n_hist_tokens(L0), nhp = n_hist_pages(L0);
   const int32_t *hpt = a.hist_pt + int64_t(b) * a.hist_pt_stride;
-  const int blk_bytes = hist_block_bytes(G);
+  const int blk_bytes = hist_block_bytes(G, BITS);
   // page ids 64 at a time (lane i: page j0 + i, -1 past the end); the next
   // page's data is loaded while the current one is computed
   auto page_block = [&](int pid) -> const uint8_t * { return a.hist + (int64_t(pid) * a.hkv + kh) * blk_bytes; };
@@ -437,28 +458,28 @@ extend_kernel(ExtendArgs a) {
       if (j > 0 && (j & 63) == 0) ids = j + lane < nhp ? hpt[j + lane] : -1;
       return __builtin_amdgcn_readlane(ids, j & 63);
     };
-    auto run = [&](int j, int pid, const HistData<NG> &hd) {
+    auto run = [&](int j, int pid, const HistData<NG, BITS> &hd) {
       if (bad_page(pid)) {
         if (lane == 0) flag_status(a.status, OSCAR_STATUS_BAD_PAGE);
         return;
       }
       const int nv = nht - PAGE * j < PAGE ? nht - PAGE * j : PAGE;
-      hist_tile<G>(sh, hd, nv, qh, ql, qs, qoff, inv_kqs, a.pv_scale, ex, lane);
+      hist_tile<G, BITS>(sh, hd, nv, qh, ql, qs, qoff, inv_kqs, a.pv_scale, ex, ex4, lane);
     };
-    HistData<NG> d0, d1;
+    HistData<NG, BITS> d0, d1;
     int p0 = page_id(0), p1 = -1;
-    if (!bad_page(p0)) hist_load<G>(d0, page_block(p0), lane);
+    if (!bad_page(p0)) hist_load<G, BITS>(d0, page_block(p0), lane);
 #pragma unroll 1
     for (int j = 0; j < nhp; j += 2) {
       if (j + 1 < nhp) {
         p1 = page_id(j + 1);
-        if (!bad_page(p1)) hist_load<G>(d1, page_block(p1), lane);
+        if (!bad_page(p1)) hist_load<G, BITS>(d1, page_block(p1), lane);
       }
       run(j, p0, d0);
       if (j + 1 >= nhp) break;
       if (j + 2 < nhp) {
         p0 = page_id(j + 2);
-        if (!bad_page(p0)) hist_load<G>(d0, page_block(p0), lane);
+        if (!bad_page(p0)) hist_load<G, BITS>(d0, page_block(p0), lane);
       }
       run(j + 1, p1, d1);
     }
@@ -508,9 +529,10 @@ hipError_t launch_gqa(const ExtendArgs &a, int G, int batch, int max_new, hipStr
   auto go = [&](auto kern) {
     hipExtLaunchKernelGGL(kern, grid, dim3(64 * WAVES), 0, s, ev.before, ev.after, 0, a);
   };
-  if (G == 32) go(extend_kernel<GQA, 32>);
-  else if (G == 64) go(extend_kernel<GQA, 64>);
-  else go(extend_kernel<GQA, 128>);
+  const bool int4 = a.bits == 4;
+  if (G == 32) int4 ? go(extend_kernel<GQA, 32, 4>) : go(extend_kernel<GQA, 32, 2>);
+  else if (G == 64) int4 ? go(extend_kernel<GQA, 64, 4>) : go(extend_kernel<GQA, 64, 2>);
+  else int4 ? go(extend_kernel<GQA, 128, 4>) : go(extend_kernel<GQA, 128, 2>);
   return hipGetLastError();
 }
 
@@ -552,6 +574,8 @@ hipError_t launch_extend(const oscar_layer_cache &c, RotArg rk, RotArg rv, const
   a.ex_m4 = 0x03000300u;
   a.ex_m16 = 0x00C000C0u;
   a.ex_e = 0x3C003C00u;
+  a.ex_mn = 0x03C003C0u;
+  a.bits = cache_bits(c);
   a.out = out;
   switch (n_q_heads / c.n_kv_heads) {
     case 1: return launch_gqa<1>(a, c.group, batch, max_new, s);

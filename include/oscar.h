@@ -60,7 +60,7 @@ typedef struct ihipStream_t *oscar_stream_t;
 enum {
   OSCAR_OK = 0,
   OSCAR_EINVAL = -1,       /* null pointer, negative or inconsistent size    */
-  OSCAR_EUNSUPPORTED = -2, /* G not in {32,64,128}, Hq/Hkv not in {1,2,4,8} */
+  OSCAR_EUNSUPPORTED = -2, /* G, code_bits or Hq/Hkv outside what is built */
   OSCAR_EWORKSPACE = -3,   /* workspace smaller than the *_workspace_bytes() */
   OSCAR_EHIP = -4,         /* HIP runtime or launch error (text appended)    */
   OSCAR_ENODEV = -5        /* no usable gfx950 device                        */
@@ -140,7 +140,7 @@ typedef struct oscar_layer_cache {
   const int32_t *bf16_pt;  /* device int32 [batch][9]                        */
   uint32_t *status;        /* device, may be NULL: OSCAR_STATUS_* bits       */
   int32_t code_bits;       /* history code width: 2 (INT2; 0 also means 2)
-                              or 4 (INT4: every entry point but extend)    */
+                              or 4 (INT4)                                  */
 } oscar_layer_cache;
 
 /* Device forms of one fixed per-layer rotation R = U*H*P ([nl] §2.2.A
@@ -368,7 +368,7 @@ OSCAR_API int oscar_decode_step(const oscar_layer_cache *cache,
  * [total_tokens][Hq][128].  Needs no workspace.  A request whose length or
  * chunk is out of range sets OSCAR_STATUS_BAD_LEN and leaves its rows
  * unwritten; a page id out of range sets OSCAR_STATUS_BAD_PAGE and that
- * page is left out.  INT2 caches only (code_bits 4: OSCAR_EUNSUPPORTED). */
+ * page is left out.  INT2 or INT4 caches. */
 OSCAR_API int oscar_extend_attn(const oscar_layer_cache *cache,
                                 const oscar_rotation *rot_k,
                                 const oscar_rotation *rot_v,

@@ -229,7 +229,7 @@ def test_extend_validation_codes():
                                      cu, 0x9000, batch, total, max_new, max_prefix, scale, 0xD000, None)
     assert call(hq=6) == E.OSCAR_EUNSUPPORTED
     assert call(c=_cache(group=48)) == E.OSCAR_EUNSUPPORTED
-    assert call(c=_cache(code_bits=4)) == E.OSCAR_EUNSUPPORTED and "INT2 caches only" in _err()
+    assert call(c=_cache(code_bits=3)) == E.OSCAR_EUNSUPPORTED and "code_bits" in _err()
     assert call(batch=0) == E.OSCAR_EINVAL
     assert call(max_new=32, total=16) == E.OSCAR_EINVAL
     assert call(max_prefix=-1) == E.OSCAR_EINVAL

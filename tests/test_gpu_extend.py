@@ -25,10 +25,10 @@ def oscar():
     return m
 
 
-def _setup(oscar, seed, hq, hkv, G, prefix, chunk, rot="random", layer=0):
+def _setup(oscar, seed, hq, hkv, G, prefix, chunk, rot="random", layer=0, bits=2):
     lens = [p + c for p, c in zip(prefix, chunk)]
-    sc = Scenario(seed, hq, hkv, G, lens, rot=rot, layer=layer)
-    ref = o.LayerCacheRef(hkv, G, sc.n_hist_pages, sc.n_bf16_pages, sc.hist_pt, sc.bf16_pt)
+    sc = Scenario(seed, hq, hkv, G, lens, rot=rot, layer=layer, bits=bits)
+    ref = o.LayerCacheRef(hkv, G, sc.n_hist_pages, sc.n_bf16_pages, sc.hist_pt, sc.bf16_pt, bits=bits)
     kp = np.concatenate([t[:n] for t, n in zip(sc.tok_k, prefix)])
     vp = np.concatenate([t[:n] for t, n in zip(sc.tok_v, prefix)])
     cu_p = np.concatenate([[0], np.cumsum(prefix)]).astype(np.int32)
@@ -39,7 +39,7 @@ def _setup(oscar, seed, hq, hkv, G, prefix, chunk, rot="random", layer=0):
     q = sc.ld.decode_q(int(cu[-1]), stream=synth.S_EVAL_Q)
     dev = torch.device("cuda:0")
     cache = oscar.LayerCache(hkv, G, sc.n_hist_pages, sc.n_bf16_pages, torch.from_numpy(sc.hist_pt),
-                             torch.from_numpy(sc.bf16_pt), device=dev)
+                             torch.from_numpy(sc.bf16_pt), device=dev, code_bits=bits)
     cache.hist.copy_(torch.from_numpy(ref.hist))
     cache.bf16.view(torch.int16).copy_(torch.from_numpy(ref.bf16.view(np.int16)))
     rk, rv = oscar.Rotation(sc.R_K, sc.clip_k), oscar.Rotation(sc.R_V, sc.clip_v)
@@ -67,6 +67,28 @@ def test_extend_ragged_prefixes_and_chunks(oscar, G):
     assert int(cache.status.item()) == 0
     exp = o.extend_attn(ref, sc.R_K, sc.R_V, q, kn, vn, cu, prefix, SCALE)
     assert_decode_close(out, exp, f"extend G={G}")
+
+
+@pytest.mark.parametrize("G", [32, 64, 128])
+def test_extend_int4_ragged_prefixes_and_chunks(oscar, G):
+    # the same shapes over an INT4 history (16-level codes, 1 KB code areas)
+    prefix = [0, 5, 16, 100, 144, 145, 300, 700]
+    chunk = [37, 16, 1, 50, 17, 33, 64, 20]
+    sc, ref, cache, rk, rv, q, kn, vn, cu = _setup(oscar, 2050 + G, 8, 2, G, prefix, chunk, bits=4)
+    out = _run(oscar, cache, rk, rv, q, kn, vn, cu, prefix)
+    assert int(cache.status.item()) == 0
+    exp = o.extend_attn(ref, sc.R_K, sc.R_V, q, kn, vn, cu, prefix, SCALE)
+    mx, rel = assert_decode_close(out, exp, f"extend INT4 G={G}")
+    print(f"extend INT4 G={G} max abs {mx:.2e} rel {rel:.2e}")
+
+
+def test_extend_int4_gqa8_calibrated(oscar):
+    prefix, chunk = [2500, 170], [48, 33]
+    sc, ref, cache, rk, rv, q, kn, vn, cu = _setup(oscar, 2060, 16, 2, 64, prefix, chunk, rot="calibrated", bits=4)
+    out = _run(oscar, cache, rk, rv, q, kn, vn, cu, prefix)
+    assert int(cache.status.item()) == 0
+    exp = o.extend_attn(ref, sc.R_K, sc.R_V, q, kn, vn, cu, prefix, SCALE)
+    assert_decode_close(out, exp, "extend INT4 GQA 8 calibrated")
 
 
 @pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 2), (16, 2)])

@@ -191,18 +191,6 @@ def test_int4_bad_page_flagged_not_followed(oscar):
     assert np.isfinite(out).all()
 
 
-def test_int4_extend_refused(oscar):
-    sc = Scenario(3100, 8, 2, 64, [300], bits=4)
-    cache = gpu_cache(oscar, sc)
-    rk, rv = gpu_rotations(oscar, sc)
-    k1 = torch.zeros((1, 2, 128), dtype=torch.bfloat16, device="cuda")
-    q1 = torch.zeros((1, 8, 128), dtype=torch.bfloat16, device="cuda")
-    lb = torch.tensor([300], dtype=torch.int32, device="cuda")
-    cu = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
-    with pytest.raises(RuntimeError, match="INT2 caches only"):
-        oscar.extend_attn(cache, rk, rv, q1, k1, k1, cu, lb, 1, 300, SCALE)
-
-
 # ------------------------------------------------------------------ append + decode
 
 
