@@ -39,12 +39,12 @@ def oscar():
 class FullCase:
     """Shared host tokens, rotations and per-request page tables."""
 
-    def __init__(self, seed, hq, hkv, G, lens, shared_pages=0, offset_step=37):
+    def __init__(self, seed, hq, hkv, G, lens, shared_pages=0, offset_step=37, bits=2):
         """shared_pages = n > 0: requests 0 .. B-n hold the pages of request 0
         (a shared prefix); the last n - 1 requests and request 0 have pages
         of their own.  Request b's tokens are rows off[b] .. off[b] + L_b of
         one seeded host array (off[b] = offset_step * b, request 0 at 0)."""
-        self.hq, self.hkv, self.G = hq, hkv, G
+        self.hq, self.hkv, self.G, self.bits = hq, hkv, G, bits
         self.lens = np.asarray(lens, dtype=np.int64)
         B = len(self.lens)
         self.shared = int(shared_pages)
@@ -79,7 +79,8 @@ class FullCase:
         """Write every request's tokens through the GPU write kernel."""
         dev = torch.device("cuda:0")
         cache = oscar.LayerCache(self.hkv, self.G, self.n_hist_pages, self.n_bf16_pages,
-                                 torch.from_numpy(self.hist_pt), torch.from_numpy(self.bf16_pt), device=dev)
+                                 torch.from_numpy(self.hist_pt), torch.from_numpy(self.bf16_pt), device=dev,
+                                 code_bits=self.bits)
         rk, rv = oscar.Rotation(self.R_K, CLIP, dev), oscar.Rotation(self.R_V, CLIP, dev)
         kd, vd = to_dev_bf16(self.k), to_dev_bf16(self.v)
         own = self.own_requests()
@@ -91,7 +92,7 @@ class FullCase:
             # the write addresses the own requests' rows of the page tables
             wcache = oscar.LayerCache(self.hkv, self.G, self.n_hist_pages, self.n_bf16_pages,
                                       torch.from_numpy(self.hist_pt[own]), torch.from_numpy(self.bf16_pt[own]),
-                                      device=dev, hist=cache.hist, bf16=cache.bf16)
+                                      device=dev, hist=cache.hist, bf16=cache.bf16, code_bits=self.bits)
             wcache.status = cache.status
         oscar.write_kv(wcache, rk, rv, kd.index_select(0, idx).contiguous(), vd.index_select(0, idx).contiguous(),
                        cu, torch.zeros(len(lens), dtype=torch.int32, device=dev), int(lens.max()))
@@ -105,7 +106,7 @@ class FullCase:
         gqa = self.hq // self.hkv
         nh = synth.hist_pages_needed(L)
         ref = o.LayerCacheRef(1, self.G, nh, 9, np.arange(nh, dtype=np.int32)[None],
-                              np.arange(9, dtype=np.int32)[None])
+                              np.arange(9, dtype=np.int32)[None], bits=self.bits)
         kb, vb = self.tokens(b, h)
         ref.write(self.R_K, self.R_V, CLIP, CLIP, kb, vb, np.array([0, L], np.int32), np.zeros(1, np.int32))
         qb = (self.q if q is None else q)[b:b + 1, h * gqa:(h + 1) * gqa]
@@ -160,6 +161,25 @@ def test_28_requests_100k_gqa8_g128(oscar):
     out = _decode(oscar, fc, cache, rk, rv)
     assert np.isfinite(out).all()
     _check(fc, out, [(0, 2), (13, 7), (26, 5), (27, 2)], "28 x 100K")
+
+
+def test_int4_28_requests_100k_gqa8_g128(oscar):
+    # the INT4 capacity layer (the same shape from an INT4 cache, as
+    # bench.py's int4_28x100k times it): the decode of sampled pairs, and the
+    # history pages of two (request, KV head) pairs against the oracle's
+    # codes and meta
+    fc = FullCase(2106, 64, 8, 128, [100000] * 28, shared_pages=3, offset_step=1000, bits=4)
+    cache, rk, rv = fc.gpu(oscar)
+    out = _decode(oscar, fc, cache, rk, rv)
+    assert np.isfinite(out).all()
+    _check(fc, out, [(0, 1), (14, 6), (26, 3), (27, 0)], "INT4 28 x 100K")
+    hist = cache.hist.cpu().numpy()
+    for b, h in ((0, 4), (27, 7)):
+        kb, vb = fc.tokens(b, h)
+        stats = compare_history(hist[:, h:h + 1], fc.hist_pt[b:b + 1], [kb], [vb],
+                                [int(fc.lens[b])], fc.R_K, fc.R_V, CLIP, CLIP, fc.G, bits=4)
+        assert_history_ok(stats)
+        print(f"INT4 write b={b} h={h}: {stats}", flush=True)
 
 
 def test_write_prefill_8x32k_g32(oscar):
