@@ -1377,7 +1377,11 @@ constexpr int attend_waves() { return (GQA <= 4 && NG <= 2) ? 4 : 1; }
 template <int GQA, int NG, bool FUSED, int BITS>
 __global__ void __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(attend_waves<GQA, NG>())))
 attend_kernel(StepArgs a) {
-  const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  // several rounds: the split index varies slowest, so every unit's first
+  // splits are dispatched before any unit's (shorter) last one, and the
+  // final round holds the short work; one round: splits of a unit together
+  const int split = FUSED ? blockIdx.x : blockIdx.z;
+  const int hk = FUSED ? blockIdx.y : blockIdx.x, b = FUSED ? blockIdx.z : blockIdx.y;
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const oscar_layer_cache &c = a.c;
   const bool append = a.k_new != nullptr;
@@ -1539,7 +1543,7 @@ attend_kernel(StepArgs a) {
 template <int GQA, int NG, int BITS>
 static hipError_t launch_t(const StepArgs &a, bool fused, int batch, int hkv, hipStream_t s) {
   const KernelEvents ev = take_profile_events();
-  const dim3 grid(1 + a.n_splits, hkv, batch);
+  const dim3 grid = fused ? dim3(1 + a.n_splits, hkv, batch) : dim3(hkv, batch, 1 + a.n_splits);
   if (fused) {
     hipExtLaunchKernelGGL((attend_kernel<GQA, NG, true, BITS>), grid, dim3(AW * 64), 0, s, ev.before, ev.after, 0, a);
     return hipGetLastError();
