@@ -116,9 +116,11 @@ SplitPlan plan_int2_splits(int batch, int n_kv_heads, int max_seq_len) {
   // and the epilogue, is paid half as often and the merge reads half the
   // partials).  When every unit (request, KV head) fits in that round with
   // at least one history split, spread each unit's pages over as many splits
-  // as it holds (its raw workgroup included); otherwise use splits of 48
-  // pages per wave (measured at batch 64: 2 % faster than 32, as fast as 64,
-  // whose longer splits leave more of the last round idle).
+  // as it holds (its raw workgroup included); otherwise use splits of 64
+  // pages per wave (measured with the split index slowest in the grid: at
+  // batch 64 / 28 x 100K, 24, 32 and 48 pages lose 8 / 26, 4 / 15 and 1 / 4 %
+  // to 64 in per-workgroup fixed work, 96 and 128 lose 4-13 % to the last
+  // round's imbalance).
   // In the one-round case the last workgroup of each unit merges inside the
   // attend kernel (measured: ~2.5 us less per call at batch 1); with several
   // rounds, the election and the merge hold workgroup slots that other units
@@ -131,7 +133,7 @@ SplitPlan plan_int2_splits(int batch, int n_kv_heads, int max_seq_len) {
     pps = (pages + per_unit - 1) / per_unit;
     p.fused = true;
   } else {
-    pps = 48 * AW;
+    pps = 64 * AW;
   }
   if (pps < AW) pps = AW;
   const int64_t min_pps = (pages + MAX_SPLITS - 1) / MAX_SPLITS;  // bounds the merge's LDS
