@@ -213,11 +213,11 @@ __device__ inline void hist_load(HistData<D / G, BITS> &hd, const uint8_t *blk, 
   }
 }
 
-// Attention over one loaded history page: only rows < n_valid exist (the
-// others, and their meta, may hold anything).  (A second instance for full
-// pages, without the masks, raises the kernel's registers past two waves per
-// SIMD.)
-template <int G, int BITS>
+// Attention over one loaded history page.  MASKED: only rows < n_valid
+// exist (the others, and their meta, may hold anything), so their scores are
+// -inf and their value operands zero; a full page (every row written) runs
+// without the masks.
+template <int G, int BITS, bool MASKED>
 __device__ inline void hist_tile(SoftState<D / G> &st, const HistData<D / G, BITS> &hd, int n_valid,
                                  const f16x8 (&qh)[4], const f16x8 (&ql)[4], const float (&qs)[D / G],
                                  const float (&qoff)[D / G], float inv_kqs, float pv_scale, const Expander &ex,
@@ -240,15 +240,16 @@ __device__ inline void hist_tile(SoftState<D / G> &st, const HistData<D / G, BIT
       d = mfma_k(x, ql[kb], d);
       d = mfma_k(x, qh[kb], d);
     }
+    // s += z_g qs_g + s_g d (two mixed-precision FMAs on the packed meta)
     for (int r = 0; r < 4; ++r) {
-      const float v = fmaf(lo_f16(hd.km[g][r]), d[r], hi_f16(hd.km[g][r]) * qs[g]);
-      s[r] = g == 0 ? v : s[r] + v;
+      const float t = fmaf(hi_f16(hd.km[g][r]), qs[g], g == 0 ? 0.f : s[r]);
+      s[r] = fmaf(lo_f16(hd.km[g][r]), d[r], t);
     }
   }
   bool ok[4];
   float p[4];
   for (int r = 0; r < 4; ++r) {
-    ok[r] = 4 * kq + r < n_valid;
+    ok[r] = !MASKED || 4 * kq + r < n_valid;
     s[r] = ok[r] ? s[r] : -INFINITY;
   }
   softmax_tile(st, s, p, inv_kqs);  // scores in kqs units
@@ -458,30 +459,53 @@ extend_kernel(ExtendArgs a) {
       if (j > 0 && (j & 63) == 0) ids = j + lane < nhp ? hpt[j + lane] : -1;
       return __builtin_amdgcn_readlane(ids, j & 63);
     };
-    auto run = [&](int j, int pid, const HistData<NG, BITS> &hd) {
+    // full pages (every row written) run unmasked; only the last page can
+    // be partial, and it runs after the loop
+    auto run_full = [&](int pid, const HistData<NG, BITS> &hd) {
       if (bad_page(pid)) {
         if (lane == 0) flag_status(a.status, OSCAR_STATUS_BAD_PAGE);
         return;
       }
-      const int nv = nht - PAGE * j < PAGE ? nht - PAGE * j : PAGE;
-      hist_tile<G, BITS>(sh, hd, nv, qh, ql, qs, qoff, inv_kqs, a.pv_scale, ex, ex4, lane);
+      hist_tile<G, BITS, false>(sh, hd, PAGE, qh, ql, qs, qoff, inv_kqs, a.pv_scale, ex, ex4, lane);
     };
+    const int nfull = nht / PAGE;
     HistData<NG, BITS> d0, d1;
     int p0 = page_id(0), p1 = -1;
     if (!bad_page(p0)) hist_load<G, BITS>(d0, page_block(p0), lane);
+    int j = 0;
 #pragma unroll 1
-    for (int j = 0; j < nhp; j += 2) {
+    for (; j + 2 <= nfull; j += 2) {
+      // d0 holds page j; page j + 1 goes to d1, page j + 2 to d0
       if (j + 1 < nhp) {
         p1 = page_id(j + 1);
         if (!bad_page(p1)) hist_load<G, BITS>(d1, page_block(p1), lane);
       }
-      run(j, p0, d0);
-      if (j + 1 >= nhp) break;
+      run_full(p0, d0);
       if (j + 2 < nhp) {
         p0 = page_id(j + 2);
         if (!bad_page(p0)) hist_load<G, BITS>(d0, page_block(p0), lane);
       }
-      run(j + 1, p1, d1);
+      run_full(p1, d1);
+    }
+    // the partial last page, if any
+    auto run_last = [&](int jj, int pid, const HistData<NG, BITS> &hd) {
+      if (bad_page(pid)) {
+        if (lane == 0) flag_status(a.status, OSCAR_STATUS_BAD_PAGE);
+        return;
+      }
+      hist_tile<G, BITS, true>(sh, hd, nht - PAGE * jj, qh, ql, qs, qoff, inv_kqs, a.pv_scale, ex, ex4, lane);
+    };
+    if (j < nfull) {
+      // one full page left (in d0), maybe followed by the partial page (d1)
+      const bool more = j + 1 < nhp;
+      if (more) {
+        p1 = page_id(j + 1);
+        if (!bad_page(p1)) hist_load<G, BITS>(d1, page_block(p1), lane);
+      }
+      run_full(p0, d0);
+      if (more) run_last(j + 1, p1, d1);
+    } else if (j < nhp) {
+      run_last(j, p0, d0);  // in d0
     }
   }
 
