@@ -263,7 +263,7 @@ __device__ inline void hist_tile(SoftState<D / G> &st, const HistData<D / G, BIT
   for (int g = 0; g < NG; ++g) {
     f16x4 bp;
     for (int r = 0; r < 4; ++r) {
-      bp[r] = _Float16(ok[r] ? pw[r] * lo_f16(hd.vm[g][r]) : 0.f);
+      bp[r] = _Float16(ok[r] ? fmaf(pw[r], lo_f16(hd.vm[g][r]), 0.f) : 0.f);  // one v_fma_mixlo_f16
       st.zacc[g] = ok[r] ? fmaf(p[r], hi_f16(hd.vm[g][r]), st.zacc[g]) : st.zacc[g];
     }
     st.cacc[g] = mfma_v(ones, bp, st.cacc[g]);
