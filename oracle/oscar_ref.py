@@ -24,6 +24,9 @@ notes of this repository):
   * one symmetric clip per layer and tensor: the 0.999 quantile (linear
     interpolation, "type 7") of |x R| over calibration tokens, heads and
     channels;
+  * per-layer R and clip, as the pages fix them; per-KV-head R and clip is
+    an optional extension, the same rules applied to each KV head's own
+    data (its query heads' moments, its vectors' quantile);
   * clip first, then per-token groups of G consecutive rotated channels,
     asymmetric min-max INT2 with fp16 scale and zero, codes from the stored
     (fp16-rounded) scale and zero, round half to even, all codes 0 when the
@@ -188,6 +191,38 @@ def calibrate(q, k, v, clip_quantile: float = 0.999) -> dict:
     return {"R_K": R_K, "R_V": R_V,
             "clip_K": clip_threshold(k, R_K, clip_quantile),
             "clip_V": clip_threshold(v, R_V, clip_quantile)}
+
+
+def calibrate_per_head(q, k, v, clip_quantile: float = 0.999) -> dict:
+    """Per-KV-head calibration (an extension of the per-layer rule): KV head
+    h gets R_K[h], R_V[h] from C_Q and C_S over the query heads that read it
+    (h * Hq/Hkv .. +Hq/Hkv-1, each attending to KV head h as in the layer),
+    and clips from its own K and V vectors.  Returns R_K, R_V [Hkv][128][128]
+    and clip_K, clip_V [Hkv]."""
+    hq, hkv = q.shape[1], k.shape[1]
+    gqa = hq // hkv
+    o = causal_attention_outputs(q, k, v)
+    out = {"R_K": [], "R_V": [], "clip_K": [], "clip_V": []}
+    for h in range(hkv):
+        qs = q[:, h * gqa:(h + 1) * gqa]
+        os_ = o[:, h * gqa:(h + 1) * gqa].reshape(-1, D)
+        R_K = compose_rotation(eigenbasis(query_covariance(qs)))
+        R_V = compose_rotation(eigenbasis(os_.T @ os_ / os_.shape[0]))
+        out["R_K"].append(R_K)
+        out["R_V"].append(R_V)
+        out["clip_K"].append(clip_threshold(k[:, h], R_K, clip_quantile))
+        out["clip_V"].append(clip_threshold(v[:, h], R_V, clip_quantile))
+    return {key: np.asarray(val) for key, val in out.items()}
+
+
+def head_rotation(R, clip, h: int):
+    """KV head h's rotation and clip: R [128][128] and a scalar clip are
+    shared by every head (the per-layer rotation); R [Hkv][128][128] with
+    clip [Hkv] give head h its own."""
+    R = np.asarray(R, dtype=np.float64)
+    if R.ndim == 2:
+        return R, None if clip is None else float(clip)
+    return R[h], None if clip is None else float(np.asarray(clip, dtype=np.float64)[h])
 
 
 def calibrate_sequences(seqs, clip_quantile: float = 0.999) -> dict:
@@ -452,6 +487,8 @@ class LayerCacheRef:
               k_new: np.ndarray, v_new: np.ndarray, cu_new, len_before) -> None:
         """Append tokens (the write of [abs] and [nl]/[fr] §2.2.B).
 
+        rot_k / rot_v with clip_k / clip_v: one R [128][128] and clip for
+        the layer, or per KV head R [Hkv][128][128] and clips [Hkv].
         k_new, v_new: bf16 bits [T][Hkv][128].  Request b receives rows
         cu_new[b]..cu_new[b+1]-1 at positions len_before[b]... .  Ring tokens
         that leave the recent window are quantised into history.
@@ -500,7 +537,7 @@ class LayerCacheRef:
                 blocks = self.hist[pids, h].copy()          # [P][block]
                 areas = split_block(blocks, G, self.bits)
                 for kind in ("k", "v"):
-                    R, clip = rot[kind]
+                    R, clip = head_rotation(*rot[kind], h)
                     qq = quantize(xs[kind][:, h, :], R, clip, G, self.bits)
                     codes = unpack_codes(areas[kind + "_codes"], kind.upper(), self.bits)
                     sc, zr = unpack_meta(areas[kind + "_meta"], G)
@@ -515,7 +552,8 @@ class LayerCacheRef:
     # ---- reconstruction for the decode
     def gather(self, b: int, L: int, rot_k: np.ndarray, rot_v: np.ndarray):
         """K, V float64 [L][Hkv][128] of request b, history inverse-rotated
-        back to the original basis (dequantise, then x_rot R^T)."""
+        back to the original basis (dequantise, then x_rot R^T; R per layer
+        [128][128] or per KV head [Hkv][128][128])."""
         G = self.G
         K = np.empty((L, self.hkv, D))
         V = np.empty((L, self.hkv, D))
@@ -537,7 +575,8 @@ class LayerCacheRef:
             pids = self.hist_pt[b, upages]
             for h in range(self.hkv):
                 areas = split_block(self.hist[pids, h], G, self.bits)
-                for kind, R, out in (("k", rot_k, K), ("v", rot_v, V)):
+                for kind, Rh, out in (("k", rot_k, K), ("v", rot_v, V)):
+                    R, _ = head_rotation(Rh, None, h)
                     c = unpack_codes(areas[kind + "_codes"], kind.upper(), self.bits)      # [P][16][128]
                     sc, zr = unpack_meta(areas[kind + "_meta"], G)             # [P][16][NG]
                     n = c.shape[0] * PAGE

@@ -1134,3 +1134,121 @@ def test_calibrate_clip_wiring():
     assert abs(q999(k.reshape(-1, 128) @ cal["R_V"]) - cal["clip_K"]) > 1e-2 * cal["clip_K"]
     assert abs(q999(v.reshape(-1, 128) @ cal["R_K"]) - cal["clip_V"]) > 1e-2 * cal["clip_V"]
     assert cal["clip_V"] > 2.0 * cal["clip_K"]
+
+
+# ---- per-KV-head rotations (an extension of the per-layer rule): each head
+# must behave exactly as a one-head layer with that head's R and clip
+
+def _one_head_cache(ref, h, L):
+    """A one-head cache with request 0's page tables of ref."""
+    return o.LayerCacheRef(1, ref.G, ref.hist.shape[0], ref.bf16.shape[0], ref.hist_pt, ref.bf16_pt, bits=ref.bits)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_per_head_rotation_with_equal_heads_matches_shared(bits):
+    L, hkv, hq = 400, 2, 8
+    ld = synth.LayerData(41, 0, hq, hkv)
+    k, v = ld.cache_kv(L)
+    R, Rv = _rot(11), _rot(12)
+    a = _make_cache(L, hkv=hkv, G=64, bits=bits)
+    a.write(R, Rv, 4.0, 3.0, k, v, [0, L], [0])
+    b = _make_cache(L, hkv=hkv, G=64, bits=bits)
+    b.write(np.stack([R, R]), np.stack([Rv, Rv]), [4.0, 4.0], [3.0, 3.0], k, v, [0, L], [0])
+    assert np.array_equal(a.hist, b.hist) and np.array_equal(a.bf16, b.bf16)
+    q = ld.decode_q(1)
+    assert np.array_equal(o.decode_attn(a, R, Rv, q, [L], 0.1), o.decode_attn(b, np.stack([R, R]),
+                                                                               np.stack([Rv, Rv]), q, [L], 0.1))
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_per_head_rotation_is_each_head_as_its_own_layer(bits):
+    # heads with different R and clips: head h's bytes and decode equal those
+    # of a one-head layer that holds only head h's tokens, written with the
+    # shared (per-layer) rule and R[h], clip[h]
+    L, hkv, hq = 420, 3, 6
+    gqa = hq // hkv
+    ld = synth.LayerData(42, 0, hq, hkv)
+    k, v = ld.cache_kv(L)
+    RK = np.stack([_rot(20 + h) for h in range(hkv)])
+    RV = np.stack([_rot(30 + h) for h in range(hkv)])
+    ck, cv = [3.0, 5.0, 7.0], [2.5, 4.0, 6.5]
+    ref = _make_cache(L, hkv=hkv, G=32, bits=bits)
+    ref.write(RK, RV, ck, cv, k, v, [0, L], [0])
+    q = ld.decode_q(1)
+    out = o.decode_attn(ref, RK, RV, q, [L], 0.09)
+    for h in range(hkv):
+        one = _one_head_cache(ref, h, L)
+        one.write(RK[h], RV[h], ck[h], cv[h], k[:, h:h + 1], v[:, h:h + 1], [0, L], [0])
+        assert np.array_equal(one.hist[:, 0], ref.hist[:, h])
+        assert np.array_equal(one.bf16[:, 0], ref.bf16[:, h])
+        exp = o.decode_attn(one, RK[h], RV[h], q[:, h * gqa:(h + 1) * gqa], [L], 0.09)
+        assert np.array_equal(out[:, h * gqa:(h + 1) * gqa], exp)
+    # and another head's R would not do: head 1 written with R[0] differs
+    wrong = _one_head_cache(ref, 1, L)
+    wrong.write(RK[0], RV[0], ck[1], cv[1], k[:, 1:2], v[:, 1:2], [0, L], [0])
+    assert not np.array_equal(wrong.hist[:, 0], ref.hist[:, 1])
+
+
+def test_per_head_extend_is_each_head_as_its_own_layer():
+    L0, n, hkv, hq = 300, 7, 2, 4
+    gqa = hq // hkv
+    ld = synth.LayerData(43, 0, hq, hkv)
+    k, v = ld.cache_kv(L0 + n)
+    RK = np.stack([_rot(50 + h) for h in range(hkv)])
+    RV = np.stack([_rot(60 + h) for h in range(hkv)])
+    ck, cv = [4.0, 6.0], [3.0, 5.0]
+    ref = _make_cache(L0 + n, hkv=hkv, G=64)
+    ref.write(RK, RV, ck, cv, k[:L0], v[:L0], [0, L0], [0])
+    q = ld.decode_q(n)
+    out = o.extend_attn(ref, RK, RV, q, k[L0:], v[L0:], [0, n], [L0], 0.1)
+    for h in range(hkv):
+        one = _one_head_cache(ref, h, L0)
+        one.write(RK[h], RV[h], ck[h], cv[h], k[:L0, h:h + 1], v[:L0, h:h + 1], [0, L0], [0])
+        exp = o.extend_attn(one, RK[h], RV[h], q[:, h * gqa:(h + 1) * gqa], k[L0:, h:h + 1], v[L0:, h:h + 1],
+                            [0, n], [L0], 0.1)
+        assert np.array_equal(out[:, h * gqa:(h + 1) * gqa], exp)
+
+
+def test_calibrate_per_head_one_kv_head_is_the_layer_rule():
+    ld = synth.LayerData(44, 0, 4, 1)
+    q, k, v = (synth.bf16_to_f64(x) for x in ld.calibration(96))
+    a = o.calibrate(q, k, v)
+    b = o.calibrate_per_head(q, k, v)
+    assert np.allclose(b["R_K"][0], a["R_K"], atol=1e-12) and np.allclose(b["R_V"][0], a["R_V"], atol=1e-12)
+    assert b["clip_K"][0] == pytest.approx(a["clip_K"], rel=1e-13)
+    assert b["clip_V"][0] == pytest.approx(a["clip_V"], rel=1e-13)
+
+
+def test_calibrate_per_head_uses_each_groups_queries_and_vectors():
+    # two KV heads, two query heads each.  Group 0's queries carry most of
+    # their energy in channel 3, group 1's in channel 70: the leading
+    # eigenvector of head h's C_Q is e_3 / e_70, so R_K[h] (H P_br)^T has that
+    # first column.  KV head 1's vectors are three times head 0's: with equal
+    # R_K (queries of equal moments) its clip is exactly three times larger.
+    rng = np.random.default_rng(7)
+    N = 64
+    q = rng.standard_normal((N, 4, 128)) * 0.1
+    q[:, 0:2, 3] += rng.standard_normal((N, 2)) * 5.0
+    q[:, 2:4, 70] += rng.standard_normal((N, 2)) * 5.0
+    k0 = rng.standard_normal((N, 1, 128))
+    k = np.concatenate([k0, 3.0 * k0], axis=1)
+    v = rng.standard_normal((N, 2, 128))
+    c = o.calibrate_per_head(q, k, v)
+    HP = o.hadamard() @ o.bitrev_permutation()
+    for h, ch in ((0, 3), (1, 70)):
+        U = c["R_K"][h] @ HP.T
+        assert np.argmax(np.abs(U[:, 0])) == ch and U[ch, 0] > 0.99
+    # equal query moments for both groups: equal R_K, clips in ratio 3
+    q2 = q.copy()
+    q2[:, 2:4] = q2[:, 0:2]
+    c2 = o.calibrate_per_head(q2, k, v)
+    assert np.allclose(c2["R_K"][0], c2["R_K"][1], atol=1e-12)
+    assert c2["clip_K"][1] == pytest.approx(3.0 * c2["clip_K"][0], rel=1e-12)
+    # C_S of a group comes from its own outputs: with V of head 1 zero, its
+    # outputs are zero and every head-1 moment vanishes (R_V[1] is then the
+    # eigenbasis of the zero matrix, the identity order), head 0 unaffected
+    v3 = v.copy()
+    v3[:, 1] = 0.0
+    c3 = o.calibrate_per_head(q, k, v3)
+    assert np.allclose(c3["R_V"][0], c["R_V"][0], atol=1e-12)
+    assert c3["clip_V"][1] == 0.0
