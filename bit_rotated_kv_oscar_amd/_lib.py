@@ -39,8 +39,12 @@ class LayerCacheC(ctypes.Structure):
                 ("code_bits", ctypes.c_int32)]
 
 
+MAX_HEAD_ROTATIONS = 32  # OSCAR_MAX_HEAD_ROTATIONS
+
+
 class RotationC(ctypes.Structure):
-    _fields_ = [("forms", c_p), ("clip", ctypes.c_float)]
+    _fields_ = [("forms", c_p), ("clip", ctypes.c_float), ("n_heads", ctypes.c_int32),
+                ("head_clips", ctypes.POINTER(ctypes.c_float))]
 
 
 # (name, restype, argtypes) of every exported function
@@ -59,6 +63,8 @@ SIGNATURES = [
      [c_p, c_p, c_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
       c_p, c_p, c_p, c_p, c_p, ctypes.c_size_t, c_p]),
     ("oscar_calib_accumulate", ctypes.c_int,
+     [c_p, c_p, c_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, c_p, c_p, ctypes.c_size_t, c_p]),
+    ("oscar_calib_accumulate_heads", ctypes.c_int,
      [c_p, c_p, c_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, c_p, c_p, ctypes.c_size_t, c_p]),
     ("oscar_calib_rotations", ctypes.c_int, [c_p, ctypes.c_double, c_p, c_p, c_p, ctypes.c_size_t, c_p]),
     ("oscar_clip_threshold", ctypes.c_int,

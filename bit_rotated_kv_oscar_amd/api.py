@@ -11,7 +11,7 @@ import math
 
 import torch
 
-from ._lib import LayerCacheC, RotationC, check, load
+from ._lib import MAX_HEAD_ROTATIONS, LayerCacheC, RotationC, check, load
 
 HEAD_DIM = 128
 PAGE = 16
@@ -48,20 +48,40 @@ def rotation_bytes() -> int:
 
 
 class Rotation:
-    """Device forms of one fixed per-layer rotation R (fp64 [128,128], x_rot = x R)
-    and its clip threshold; built by oscar_prepare_rotation."""
+    """Device forms of a fixed rotation and its clip threshold, built by
+    oscar_prepare_rotation: one per-layer R (fp64 [128, 128], x_rot = x R)
+    with a scalar clip, or one R per KV head ([Hkv, 128, 128], Hkv <= 32)
+    with a clip per head (the optional per-head extension)."""
 
-    def __init__(self, R, clip: float, device: torch.device | str = "cuda"):
+    def __init__(self, R, clip, device: torch.device | str = "cuda"):
         device = torch.device(device)
-        self.R64 = torch.as_tensor(R, dtype=torch.float64).to(device).contiguous()
-        if tuple(self.R64.shape) != (HEAD_DIM, HEAD_DIM):
-            raise ValueError("R must be [128, 128]")
-        self.forms = torch.empty(rotation_bytes(), dtype=torch.uint8, device=device)
-        self.clip = float(clip)
-        check(load().oscar_prepare_rotation(_ptr(self.R64), _ptr(self.forms), _stream(device)))
+        R64 = torch.as_tensor(R, dtype=torch.float64)
+        per_head = R64.dim() == 3
+        if (R64.dim() not in (2, 3)) or tuple(R64.shape[-2:]) != (HEAD_DIM, HEAD_DIM):
+            raise ValueError("R must be [128, 128] or [Hkv, 128, 128]")
+        self.R64 = R64.to(device).contiguous()
+        self.n_heads = int(R64.shape[0]) if per_head else 0
+        if per_head:
+            clips = [float(c) for c in clip]
+            if len(clips) != self.n_heads or not 1 <= self.n_heads <= MAX_HEAD_ROTATIONS:
+                raise ValueError("per-head rotations: one clip per head, at most 32 heads")
+            self._clips = (ctypes.c_float * self.n_heads)(*clips)
+            self.clip = max(clips)
+        else:
+            self._clips = None
+            self.clip = float(clip)
+        nb = rotation_bytes()
+        self.forms = torch.empty(max(self.n_heads, 1) * nb, dtype=torch.uint8, device=device)
+        lib = load()
+        for h in range(max(self.n_heads, 1)):
+            Rh = self.R64[h] if per_head else self.R64
+            check(lib.oscar_prepare_rotation(_ptr(Rh), self.forms.data_ptr() + h * nb, _stream(device)))
 
     def c(self) -> RotationC:
-        return RotationC(self.forms.data_ptr(), self.clip)
+        if self.n_heads:
+            return RotationC(self.forms.data_ptr(), self.clip, self.n_heads,
+                             ctypes.cast(self._clips, ctypes.POINTER(ctypes.c_float)))
+        return RotationC(self.forms.data_ptr(), self.clip, 0, None)
 
 
 class LayerCache:
@@ -307,6 +327,46 @@ def calib_accumulate(q_cal: torch.Tensor, k_cal: torch.Tensor, v_cal: torch.Tens
     check(load().oscar_calib_accumulate(_ptr(q_cal), _ptr(k_cal), _ptr(v_cal), q_cal.shape[0], q_cal.shape[1],
                                         k_cal.shape[1], _ptr(sums), _ptr(ws), ws.numel(), _stream(dev)))
     return int(q_cal.shape[0] * q_cal.shape[1])
+
+
+def calib_accumulate_heads(q_cal: torch.Tensor, k_cal: torch.Tensor, v_cal: torch.Tensor,
+                           sums: torch.Tensor) -> int:
+    """oscar_calib_accumulate_heads: adds one calibration sequence's per-KV-head
+    moment sums to sums (float64 [Hkv, 2, 128, 128] on the device); returns
+    n_tokens * Hq/Hkv, each head's count increment."""
+    dev = q_cal.device
+    for t, n in ((q_cal, "q_cal"), (k_cal, "k_cal"), (v_cal, "v_cal")):
+        _need(t, n, (torch.bfloat16,), dev)
+    _need(sums, "sums", (torch.float64,), dev)
+    hkv = k_cal.shape[1]
+    if tuple(sums.shape) != (hkv, 2, HEAD_DIM, HEAD_DIM):
+        raise ValueError("sums must be [Hkv, 2, 128, 128]")
+    n = int(load().oscar_calib_accumulate_workspace_bytes(q_cal.shape[0], q_cal.shape[1], hkv))
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    check(load().oscar_calib_accumulate_heads(_ptr(q_cal), _ptr(k_cal), _ptr(v_cal), q_cal.shape[0],
+                                              q_cal.shape[1], hkv, _ptr(sums), _ptr(ws), ws.numel(),
+                                              _stream(dev)))
+    return int(q_cal.shape[0] * (q_cal.shape[1] // hkv))
+
+
+def calibrate_per_head(q_cal: torch.Tensor, k_cal: torch.Tensor, v_cal: torch.Tensor,
+                       clip_quantile: float = 0.999):
+    """Per-KV-head calibration of one sequence (the optional per-head
+    extension): per-head moments, then each head's R_K, R_V
+    (oscar_calib_rotations) and clips over its own K and V vectors
+    (oscar_clip_threshold).  Returns R_K, R_V float64 CPU [Hkv, 128, 128] and
+    clip lists [Hkv]."""
+    hkv = k_cal.shape[1]
+    sums = torch.zeros((hkv, 2, HEAD_DIM, HEAD_DIM), dtype=torch.float64, device=q_cal.device)
+    count = calib_accumulate_heads(q_cal, k_cal, v_cal, sums)
+    RK, RV, ck, cv = [], [], [], []
+    for h in range(hkv):
+        rk, rv = calib_rotations(sums[h], count)
+        RK.append(rk)
+        RV.append(rv)
+        ck.append(clip_threshold(k_cal[:, h].contiguous(), rk, clip_quantile))
+        cv.append(clip_threshold(v_cal[:, h].contiguous(), rv, clip_quantile))
+    return torch.stack(RK), torch.stack(RV), ck, cv
 
 
 def calib_rotations(sums: torch.Tensor, count: float):

@@ -1,5 +1,6 @@
 // extern "C" entry points of liboscar: argument validation, workspace sizing,
 // error reporting, and the host side of calibration.
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -68,15 +69,43 @@ int check_cache(const oscar_layer_cache *c) {
   return OSCAR_OK;
 }
 
-int check_rot(const oscar_rotation *r, const char *name) {
+bool clip_ok(float c) { return std::isfinite(c) && c > 0.f && c <= 65504.f; }
+
+// One rotation for the layer (n_heads 0 or 1), or one per KV head (n_heads =
+// hkv, at most OSCAR_MAX_HEAD_ROTATIONS, with a host clip per head).
+int check_rot(const oscar_rotation *r, const char *name, int32_t hkv) {
   if (!r || !r->forms) return fail(OSCAR_EINVAL, "%s: rotation or its forms is NULL", name);
-  if (!std::isfinite(r->clip) || r->clip <= 0.f || r->clip > 65504.f)
+  if (r->n_heads > 1) {
+    if (r->n_heads != hkv || r->n_heads > OSCAR_MAX_HEAD_ROTATIONS)
+      return fail(OSCAR_EINVAL, "%s: n_heads %d must be 0, 1 or n_kv_heads %d (at most %d)", name, r->n_heads, hkv,
+                  OSCAR_MAX_HEAD_ROTATIONS);
+    if (!r->head_clips) return fail(OSCAR_EINVAL, "%s: head_clips is NULL", name);
+    for (int h = 0; h < r->n_heads; ++h)
+      if (!clip_ok(r->head_clips[h]))
+        return fail(OSCAR_EINVAL, "%s: head_clips[%d] = %g must be finite, > 0 and <= 65504", name, h,
+                    double(r->head_clips[h]));
+    return OSCAR_OK;
+  }
+  if (r->n_heads < 0) return fail(OSCAR_EINVAL, "%s: n_heads %d < 0", name, r->n_heads);
+  if (!clip_ok(r->clip))
     return fail(OSCAR_EINVAL, "%s: clip %g must be finite, > 0 and <= 65504", name, double(r->clip));
   return OSCAR_OK;
 }
 
 oscar::RotArg rot_arg(const oscar_rotation *r) {
-  return oscar::RotArg{static_cast<const uint8_t *>(r->forms), r->clip};
+  oscar::RotArg a{};
+  a.forms = static_cast<const uint8_t *>(r->forms);
+  a.clip = r->clip;
+  if (r->n_heads > 1) {
+    a.n_heads = r->n_heads;
+    a.stride = int64_t(oscar::FORM_BYTES);
+    a.clip = 0.f;
+    for (int h = 0; h < r->n_heads; ++h) {
+      a.head_clip[h] = r->head_clips[h];
+      a.clip = std::max(a.clip, r->head_clips[h]);  // the largest: bounds for every head
+    }
+  }
+  return a;
 }
 
 }  // namespace
@@ -256,8 +285,8 @@ int oscar_write_kv(const oscar_layer_cache *cache, const oscar_rotation *rot_k,
                    const int32_t *cu_new, const int32_t *len_before, int32_t batch,
                    int64_t total_tokens, int32_t max_new, oscar_stream_t stream) {
   if (int rc = check_cache(cache)) return rc;
-  if (int rc = check_rot(rot_k, "rot_k")) return rc;
-  if (int rc = check_rot(rot_v, "rot_v")) return rc;
+  if (int rc = check_rot(rot_k, "rot_k", cache->n_kv_heads)) return rc;
+  if (int rc = check_rot(rot_v, "rot_v", cache->n_kv_heads)) return rc;
   if (batch < 1 || batch > 65535) return fail(OSCAR_EINVAL, "batch %d outside [1, 65535]", batch);
   if (total_tokens < 0 || max_new < 0) return fail(OSCAR_EINVAL, "negative token counts");
   if (int64_t(max_new) > total_tokens) return fail(OSCAR_EINVAL, "max_new %d > total_tokens %lld", max_new, (long long)total_tokens);
@@ -293,8 +322,8 @@ int oscar_decode_attn(const oscar_layer_cache *cache, const oscar_rotation *rot_
                       const int32_t *seq_lens, int32_t batch, int32_t max_seq_len, float sm_scale,
                       float *out, void *workspace, size_t workspace_bytes, oscar_stream_t stream) {
   if (int rc = check_cache(cache)) return rc;
-  if (int rc = check_rot(rot_k, "rot_k")) return rc;
-  if (int rc = check_rot(rot_v, "rot_v")) return rc;
+  if (int rc = check_rot(rot_k, "rot_k", cache->n_kv_heads)) return rc;
+  if (int rc = check_rot(rot_v, "rot_v", cache->n_kv_heads)) return rc;
   if (int rc = check_heads(n_q_heads, cache->n_kv_heads)) return rc;
   if (batch < 1 || batch > 65535) return fail(OSCAR_EINVAL, "batch %d outside [1, 65535]", batch);
   if (max_seq_len < 1) return fail(OSCAR_EINVAL, "max_seq_len %d < 1", max_seq_len);
@@ -321,8 +350,8 @@ int oscar_decode_attn_noalloc(const oscar_layer_cache *cache, const oscar_rotati
                               const int32_t *seq_lens, int32_t batch, int32_t max_seq_len, float sm_scale,
                               float *out, oscar_stream_t stream) {
   if (int rc = check_cache(cache)) return rc;
-  if (int rc = check_rot(rot_k, "rot_k")) return rc;
-  if (int rc = check_rot(rot_v, "rot_v")) return rc;
+  if (int rc = check_rot(rot_k, "rot_k", cache->n_kv_heads)) return rc;
+  if (int rc = check_rot(rot_v, "rot_v", cache->n_kv_heads)) return rc;
   if (int rc = check_heads(n_q_heads, cache->n_kv_heads)) return rc;
   if (batch < 1 || batch > 65535) return fail(OSCAR_EINVAL, "batch %d outside [1, 65535]", batch);
   if (max_seq_len < 1) return fail(OSCAR_EINVAL, "max_seq_len %d < 1", max_seq_len);
@@ -354,8 +383,8 @@ int oscar_decode_step(const oscar_layer_cache *cache, const oscar_rotation *rot_
                       float sm_scale, float *out, void *workspace, size_t workspace_bytes,
                       oscar_stream_t stream) {
   if (int rc = check_cache(cache)) return rc;
-  if (int rc = check_rot(rot_k, "rot_k")) return rc;
-  if (int rc = check_rot(rot_v, "rot_v")) return rc;
+  if (int rc = check_rot(rot_k, "rot_k", cache->n_kv_heads)) return rc;
+  if (int rc = check_rot(rot_v, "rot_v", cache->n_kv_heads)) return rc;
   if (int rc = check_heads(n_q_heads, cache->n_kv_heads)) return rc;
   if (batch < 1 || batch > 65535) return fail(OSCAR_EINVAL, "batch %d outside [1, 65535]", batch);
   if (max_seq_len < 1) return fail(OSCAR_EINVAL, "max_seq_len %d < 1", max_seq_len);
@@ -381,8 +410,8 @@ int oscar_extend_attn(const oscar_layer_cache *cache, const oscar_rotation *rot_
                       const int32_t *cu_new, const int32_t *len_before, int32_t batch, int64_t total_tokens,
                       int32_t max_new, int32_t max_prefix, float sm_scale, float *out, oscar_stream_t stream) {
   if (int rc = check_cache(cache)) return rc;
-  if (int rc = check_rot(rot_k, "rot_k")) return rc;
-  if (int rc = check_rot(rot_v, "rot_v")) return rc;
+  if (int rc = check_rot(rot_k, "rot_k", cache->n_kv_heads)) return rc;
+  if (int rc = check_rot(rot_v, "rot_v", cache->n_kv_heads)) return rc;
   if (int rc = check_heads(n_q_heads, cache->n_kv_heads)) return rc;
   if (batch < 1 || batch > 65535) return fail(OSCAR_EINVAL, "batch %d outside [1, 65535]", batch);
   if (total_tokens < 0 || max_new < 0 || max_prefix < 0) return fail(OSCAR_EINVAL, "negative token counts");
@@ -534,6 +563,38 @@ int oscar_calib_accumulate(const uint16_t *q_cal, const uint16_t *k_cal, const u
   if (e == hipSuccess) e = oscar::launch_calib_outer(nullptr, o, nq, sums + D * D, part, s, true);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "calib_accumulate");
+  return OSCAR_OK;
+}
+
+int oscar_calib_accumulate_heads(const uint16_t *q_cal, const uint16_t *k_cal, const uint16_t *v_cal,
+                                 int64_t n_tokens, int32_t n_q_heads, int32_t n_kv_heads, double *sums,
+                                 void *workspace, size_t workspace_bytes, oscar_stream_t stream) {
+  if (!q_cal || !k_cal || !v_cal || !sums) return fail(OSCAR_EINVAL, "calib_accumulate_heads: NULL argument");
+  if (n_tokens < 1 || n_tokens > 65536) return fail(OSCAR_EINVAL, "n_tokens %lld outside [1, 65536]", (long long)n_tokens);
+  if (n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || n_q_heads > 256)
+    return fail(OSCAR_EUNSUPPORTED, "head counts %d/%d unsupported", n_q_heads, n_kv_heads);
+  const AccumLayout lay = accum_layout(n_tokens, n_q_heads);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(OSCAR_EWORKSPACE, "calib_accumulate_heads: workspace of %zu bytes needed, %zu given", lay.total,
+                workspace ? workspace_bytes : 0);
+  if (int rc = check_device()) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int D = oscar::D;
+  const int gqa = n_q_heads / n_kv_heads;
+  const int64_t nv = n_tokens * gqa;  // vectors per KV head
+  char *w = static_cast<char *>(workspace);
+  double *o = reinterpret_cast<double *>(w + lay.o), *part = reinterpret_cast<double *>(w + lay.part);
+  // the attention outputs of every query head once, then per KV head the
+  // rows of its query heads (gqa consecutive rows in each token's Hq rows)
+  hipError_t e = oscar::launch_calib_attention(q_cal, k_cal, v_cal, n_tokens, n_q_heads, n_kv_heads, o, s);
+  for (int h = 0; h < n_kv_heads && e == hipSuccess; ++h) {
+    double *sh = sums + int64_t(h) * 2 * D * D;
+    e = oscar::launch_calib_outer(q_cal, nullptr, nv, sh, part, s, true, gqa, n_q_heads, int64_t(h) * gqa);
+    if (e == hipSuccess)
+      e = oscar::launch_calib_outer(nullptr, o, nv, sh + D * D, part, s, true, gqa, n_q_heads, int64_t(h) * gqa);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "calib_accumulate_heads");
   return OSCAR_OK;
 }
 

@@ -166,6 +166,8 @@ struct StepArgs {
   oscar_layer_cache c;
   const uint8_t *fk, *fv;
   float clip_k, clip_v;
+  int64_t fstride_k, fstride_v;  // bytes between KV heads' forms (0: one rotation for the layer)
+  float hclip_k[MAX_HEAD_ROT], hclip_v[MAX_HEAD_ROT];  // per-head clips (fstride != 0)
   // append (may be null: no append)
   const uint16_t *k_new, *v_new;  // [B][Hkv][128]
   const int32_t *len_before;      // [B]: the new token goes to position len_before[b]
@@ -185,6 +187,12 @@ struct StepArgs {
 };
 
 __device__ inline bool valid_len(int L, int max_len) { return L >= 1 && L <= max_len; }
+
+// KV head hk's rotation forms and clips (the layer's when the stride is 0)
+__device__ inline const uint8_t *forms_k(const StepArgs &a, int hk) { return a.fk + hk * a.fstride_k; }
+__device__ inline const uint8_t *forms_v(const StepArgs &a, int hk) { return a.fv + hk * a.fstride_v; }
+__device__ inline float head_clip_k(const StepArgs &a, int hk) { return a.fstride_k ? a.hclip_k[hk] : a.clip_k; }
+__device__ inline float head_clip_v(const StepArgs &a, int hk) { return a.fstride_v ? a.hclip_v[hk] : a.clip_v; }
 
 // ------------------------------------------------------------------ q and append
 
@@ -277,7 +285,7 @@ __device__ void evict_token(const StepArgs &a, int b, int hk, int tid, int wave,
   f32x4 rf[2][8];
 #pragma unroll
   for (int vec = 0; vec < 2; ++vec) {
-    const float *RT = reinterpret_cast<const float *>((vec ? a.fv : a.fk) + FORM_RT) + jr * D + 4 * qq;
+    const float *RT = reinterpret_cast<const float *>((vec ? forms_v(a, hk) : forms_k(a, hk)) + FORM_RT) + jr * D + 4 * qq;
 #pragma unroll
     for (int k = 0; k < 8; ++k) rf[vec][k] = *reinterpret_cast<const f32x4 *>(RT + (k >> 2) * 64 * D + 32 * (k & 3));
   }
@@ -321,14 +329,14 @@ __device__ void evict_token(const StepArgs &a, int b, int hk, int tid, int wave,
   f32x4 rb[2][8];
 #pragma unroll
   for (int vec = 0; vec < 2; ++vec) {
-    const float *Rr = reinterpret_cast<const float *>((vec ? a.fv : a.fk) + FORM_R) + jr * D + 4 * qq;
+    const float *Rr = reinterpret_cast<const float *>((vec ? forms_v(a, hk) : forms_k(a, hk)) + FORM_R) + jr * D + 4 * qq;
 #pragma unroll
     for (int k = 0; k < 8; ++k) rb[vec][k] = *reinterpret_cast<const f32x4 *>(Rr + (k >> 2) * 64 * D + 32 * (k & 3));
   }
   __syncthreads();
   // ---- clip and quantise: group min / max over G consecutive channels (all
   // threads take part; threads >= 256 repeat the work of threads < 256)
-  const float clip = v ? a.clip_v : a.clip_k;
+  const float clip = v ? head_clip_v(a, hk) : head_clip_k(a, hk);
   const float xc = fminf(fmaxf(e.y[v][ch], -clip), clip);
   float lo, hi;
   if constexpr (G == 128) {
@@ -469,7 +477,7 @@ __device__ inline void build_q_issue(const StepArgs &a, int b, int hk, int tid, 
   constexpr int NT = AW * 64;
   // eight consecutive lanes read one 128-byte line of a row
   const int jr = tid >> 3, qq = tid & 7;
-  const float *RT = reinterpret_cast<const float *>(a.fk + FORM_RT) + (hist ? jr * D : 0) + 4 * qq;
+  const float *RT = reinterpret_cast<const float *>(forms_k(a, hk) + FORM_RT) + (hist ? jr * D : 0) + 4 * qq;
   const int s_hi = hist ? 64 * D : 0, s_k = hist ? 32 : 0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) ql.rk[k] = *reinterpret_cast<const f32x4 *>(RT + (k >> 2) * s_hi + s_k * (k & 3));
@@ -1279,7 +1287,7 @@ __global__ void __launch_bounds__(merge_threads<GQA>()) merge_kernel(StepArgs a)
   // read 128 contiguous bytes
   constexpr int NR = 1024 / NT;  // rows per thread: 128 rows x 8 lanes over NT threads
   const int cr = tid >> 3, qq = tid & 7;
-  const float *Rc = reinterpret_cast<const float *>(a.fv + FORM_R) + cr * D + 4 * qq;
+  const float *Rc = reinterpret_cast<const float *>(forms_v(a, hk) + FORM_R) + cr * D + 4 * qq;
   f32x4 rv[4 * NR];
 #pragma unroll
   for (int m = 0; m < NR; ++m)
@@ -1507,7 +1515,7 @@ attend_kernel(StepArgs a) {
       // computed here, not hoisted above the page loop (register pressure)
       int t = tid;
       asm volatile("" : "+v"(t));
-      if (split > 0) rv.load(a.fv, t);
+      if (split > 0) rv.load(forms_v(a, hk), t);
     }
     __syncthreads();
     if (split > 0)
@@ -1590,7 +1598,13 @@ hipError_t launch_decode_step(const oscar_layer_cache &c, RotArg rk, RotArg rv, 
   a.fk = rk.forms;
   a.fv = rv.forms;
   a.clip_k = rk.clip;
-  a.clip_v = rv.clip;
+  a.clip_v = rv.clip;  // with a rotation per head, the largest head clip (bounds the PV operand)
+  a.fstride_k = rk.stride;
+  a.fstride_v = rv.stride;
+  for (int h = 0; h < MAX_HEAD_ROT; ++h) {
+    a.hclip_k[h] = rk.head_clip[h];
+    a.hclip_v[h] = rv.head_clip[h];
+  }
   a.k_new = k_new;
   a.v_new = v_new;
   a.len_before = len_before;

@@ -46,6 +46,7 @@ struct ExtendArgs {
   uint32_t *status;
   const float *rk;   // fp32 R_K[i][j] at i*128 + j
   const float *rvt;  // fp32 R_V[j][c] at c*128 + j
+  int64_t rk_stride, rv_stride;  // floats between KV heads' forms (0: one rotation for the layer)
   const uint16_t *q, *k_new, *v_new;
   const int32_t *cu_new, *len_before;
   int hq, hkv, max_new, max_prefix;
@@ -322,7 +323,7 @@ extend_kernel(ExtendArgs a) {
   for (int i = 0; i < EXT_TILE; ++i) qr[i][0] = qr[i][1] = 0.f;
 #pragma unroll 2
   for (int c = 0; c < D; ++c) {
-    const float2 r = *reinterpret_cast<const float2 *>(a.rk + c * D + 2 * lane);
+    const float2 r = *reinterpret_cast<const float2 *>(a.rk + kh * a.rk_stride + c * D + 2 * lane);
     for (int i4 = 0; i4 < EXT_TILE / 4; ++i4) {
       const float4 x = *reinterpret_cast<const float4 *>(buf + c * EXT_TILE + 4 * i4);
       const float xs[4] = {x.x, x.y, x.z, x.w};
@@ -526,7 +527,7 @@ extend_kernel(ExtendArgs a) {
   for (int i = 0; i < EXT_TILE; ++i) o[i][0] = o[i][1] = 0.f;
 #pragma unroll 2
   for (int c = 0; c < D; ++c) {
-    const float2 r = *reinterpret_cast<const float2 *>(a.rvt + c * D + 2 * lane);
+    const float2 r = *reinterpret_cast<const float2 *>(a.rvt + kh * a.rv_stride + c * D + 2 * lane);
     for (int i4 = 0; i4 < EXT_TILE / 4; ++i4) {
       const float4 x = *reinterpret_cast<const float4 *>(buf + c * EXT_TILE + 4 * i4);
       const float xs[4] = {x.x, x.y, x.z, x.w};
@@ -577,6 +578,8 @@ hipError_t launch_extend(const oscar_layer_cache &c, RotArg rk, RotArg rv, const
   a.status = c.status;
   a.rk = reinterpret_cast<const float *>(rk.forms + FORM_R);
   a.rvt = reinterpret_cast<const float *>(rv.forms + FORM_RT);
+  a.rk_stride = rk.stride / 4;
+  a.rv_stride = rv.stride / 4;
   a.q = q;
   a.k_new = k_new;
   a.v_new = v_new;

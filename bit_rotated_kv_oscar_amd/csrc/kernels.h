@@ -8,9 +8,16 @@
 
 namespace oscar {
 
+// A rotation as the kernels take it: one form for the layer (stride 0), or
+// one per KV head (head h's forms at forms + h * stride, its clip
+// head_clip[h]); clip is then the largest head clip.
+constexpr int MAX_HEAD_ROT = OSCAR_MAX_HEAD_ROTATIONS;
 struct RotArg {
-  const uint8_t *forms;  // device forms of one rotation (FORM_* offsets)
+  const uint8_t *forms;  // device forms (FORM_* offsets)
   float clip;
+  int n_heads;           // 0: one rotation for every head
+  int64_t stride;        // bytes between heads' forms (0: shared)
+  float head_clip[MAX_HEAD_ROT];
 };
 
 // Events that the next decode launch records around its split-K attention
@@ -84,8 +91,11 @@ hipError_t launch_extend(const oscar_layer_cache &c, RotArg rk, RotArg rv, const
 // cov[128][128] = (accumulate ? cov : 0) + sum over the n_vec vectors of
 // x x^T (not divided); part: calib_outer_part_bytes() of device scratch
 size_t calib_outer_part_bytes();
+// (vector n: row (n / grp) * rstride + roff + n % grp of x; the defaults
+// take the rows in order).
 hipError_t launch_calib_outer(const uint16_t *x_bf16, const double *x_f64, int64_t n_vec,
-                              double *cov, double *part, hipStream_t s, bool accumulate = false);
+                              double *cov, double *part, hipStream_t s, bool accumulate = false, int grp = 1,
+                              int64_t rstride = 1, int64_t roff = 0);
 // o[N][Hq][128] (fp64) = causal softmax(q k^T / sqrt(128)) v per query head
 hipError_t launch_calib_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                   int64_t n_tokens, int n_q_heads, int n_kv_heads,

@@ -44,19 +44,29 @@ hipError_t launch_prepare_rotation(const double *R, void *forms, hipStream_t s) 
 // products and sums, four rows per step in a fixed order); wave I owns the
 // 16-row block I of cov and all eight column blocks.  outer_reduce_kernel
 // adds the partials in workgroup order.  Exactly one of xb (bf16) / xd
-// (fp64) is non-null.
+// (fp64) is non-null.  Vector n is row (n / grp) * rstride + roff + n % grp
+// of x (grp = 1, rstride = 1, roff = 0: the rows in order; per KV head: the
+// grp = Hq/Hkv query-head rows of that head in each token's Hq rows).
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 constexpr int OUTER_WAVES = D / 16;  // one wave per 16-row block
 constexpr int OUTER_MAX_PARTS = 256;
 
-__device__ inline double outer_load(const uint16_t *xb, const double *xd, int64_t n, int64_t n_end, int col) {
+struct RowMap {
+  int grp;
+  int64_t rstride, roff;
+  __device__ int64_t row(int64_t n) const { return grp == 1 ? n * rstride + roff : (n / grp) * rstride + roff + n % grp; }
+};
+
+__device__ inline double outer_load(const uint16_t *xb, const double *xd, const RowMap &m, int64_t n, int64_t n_end,
+                                    int col) {
   if (n >= n_end) return 0.0;
-  return xb ? double(bf16_to_f32(xb[n * D + col])) : xd[n * D + col];
+  const int64_t r = m.row(n);
+  return xb ? double(bf16_to_f32(xb[r * D + col])) : xd[r * D + col];
 }
 
 __global__ void __launch_bounds__(OUTER_WAVES * 64) outer_partial_kernel(const uint16_t *__restrict__ xb,
                                                                        const double *__restrict__ xd,
-                                                                       int64_t n_vec, int64_t rows,
+                                                                       int64_t n_vec, int64_t rows, RowMap map,
                                                                        double *__restrict__ part) {
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int c = lane & 15, kq = lane >> 4;  // column in a block; row in a step of four
@@ -68,10 +78,10 @@ __global__ void __launch_bounds__(OUTER_WAVES * 64) outer_partial_kernel(const u
   for (int64_t n0 = r0; n0 < r1; n0 += 4) {
     const int64_t n = n0 + kq;
     // A: x[n0 + k][16 wave + i] at (i = c, k = kq); B: x[n0 + k][16 jb + j]
-    const double a = outer_load(xb, xd, n, r1, 16 * wave + c);
+    const double a = outer_load(xb, xd, map, n, r1, 16 * wave + c);
     double b[D / 16];
 #pragma unroll
-    for (int jb = 0; jb < D / 16; ++jb) b[jb] = outer_load(xb, xd, n, r1, 16 * jb + c);
+    for (int jb = 0; jb < D / 16; ++jb) b[jb] = outer_load(xb, xd, map, n, r1, 16 * jb + c);
 #pragma unroll
     for (int jb = 0; jb < D / 16; ++jb) acc[jb] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b[jb], acc[jb], 0, 0, 0);
   }
@@ -95,13 +105,14 @@ __global__ void __launch_bounds__(256) outer_reduce_kernel(const double *__restr
 size_t calib_outer_part_bytes() { return size_t(OUTER_MAX_PARTS) * D * D * sizeof(double); }
 
 hipError_t launch_calib_outer(const uint16_t *x_bf16, const double *x_f64, int64_t n_vec,
-                              double *cov, double *part, hipStream_t s, bool accumulate) {
+                              double *cov, double *part, hipStream_t s, bool accumulate, int grp,
+                              int64_t rstride, int64_t roff) {
   // rows per workgroup: a multiple of four, at least 64, at most 256 workgroups
   int64_t rows = (n_vec + OUTER_MAX_PARTS - 1) / OUTER_MAX_PARTS;
   rows = rows < 64 ? 64 : (rows + 3) / 4 * 4;
   const int n_parts = int((n_vec + rows - 1) / rows);
   hipLaunchKernelGGL(outer_partial_kernel, dim3(n_parts), dim3(OUTER_WAVES * 64), 0, s, x_bf16, x_f64, n_vec,
-                     rows, part);
+                     rows, RowMap{grp, rstride, roff}, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(outer_reduce_kernel, dim3(D * D / 256), dim3(256), 0, s, part, n_parts, cov, accumulate);

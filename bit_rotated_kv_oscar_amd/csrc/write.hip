@@ -22,6 +22,8 @@ struct WriteArgs {
   oscar_layer_cache c;
   const uint8_t *forms[2];
   float clip[2];
+  int64_t fstride[2];              // bytes between KV heads' forms (0: one rotation for the layer)
+  float hclip[2][MAX_HEAD_ROT];    // per-head clips (fstride != 0)
   const uint16_t *src[2];  // k_new, v_new
   const int32_t *cu_new;
   const int32_t *len_before;
@@ -43,9 +45,13 @@ __device__ inline bool request_ok(const WriteArgs &a, int b, int &L0, int &n) {
          int64_t(L0) + n < (int64_t(1) << 30);
 }
 
-constexpr int WHC = 4;   // KV heads per write workgroup
+constexpr int WHC = 4;   // KV heads per write workgroup (one rotation for the layer)
 constexpr int WPP = 16;  // history pages per write workgroup (the R pieces stay in registers)
-constexpr int XSTR = WHC * D * 2 + 16;  // LDS bytes per staged token row (all WHC heads; padded)
+// LDS bytes per staged token row (all HC heads of a workgroup; padded).  With
+// a rotation per KV head a workgroup takes one head (HC = 1): its R pieces
+// are the ones in registers.
+template <int HC>
+constexpr int xstr() { return HC * D * 2 + 16; }
 
 typedef _Float16 f16x8w __attribute__((ext_vector_type(8)));
 typedef float f32x4w __attribute__((ext_vector_type(4)));
@@ -110,12 +116,12 @@ __device__ inline uint32_t pack8(uint32_t x0, uint32_t x1) {
 // row-group write and read distinct banks
 constexpr int KROW = D + 8;
 
-template <int G>
+template <int G, int HC>
 struct WriteShared {
-  uint8_t xs[PAGE * XSTR];                  // the page's rows, all heads of the chunk (bf16)
-  uint8_t codes[2][WHC][PAGE * KROW];       // per buffer -- K: [token][channel] (rows KROW bytes apart); V: [channel][token]
-  float pmin[WHC][PAGE][4], pmax[WHC][PAGE][4];  // per wave (groups wider than a wave)
-  float sz[2][WHC][D / G][PAGE][2];         // per buffer: (scale, zero) after fp16 rounding
+  uint8_t xs[PAGE * xstr<HC>()];            // the page's rows, all heads of the chunk (bf16)
+  uint8_t codes[2][HC][PAGE * KROW];        // per buffer -- K: [token][channel] (rows KROW bytes apart); V: [channel][token]
+  float pmin[HC][PAGE][4], pmax[HC][PAGE][4];  // per wave (groups wider than a wave)
+  float sz[2][HC][D / G][PAGE][2];          // per buffer: (scale, zero) after fp16 rounding
   int bad[2][4];                            // per page parity: a wave met a bad ring page id
 };
 
@@ -148,7 +154,7 @@ __device__ inline void token_source(const WriteArgs &a, int ids, int tensor, int
 }
 
 // One workgroup (4 waves) per (request, WPP consecutive history pages, K|V,
-// up to WHC KV heads).  Per page: the rows that enter history in this call
+// up to HC KV heads).  Per page: the rows that enter history in this call
 // -- new tokens, or ring tokens pushed out of the recent window -- are staged
 // in LDS for all heads of the chunk as fp16 (exact in fp16's normal range),
 // rotated on the matrix cores as 2^11 Y = X (2^11 R_hi) + X R_lo with
@@ -165,8 +171,9 @@ __device__ inline void token_source(const WriteArgs &a, int ids, int tensor, int
 // meta (kept in the other LDS buffer) are stored, then page j is computed.
 // The next wait for loads comes at page j+1's staging, a whole page later.
 // All page ids of the workgroup are loaded once, into lanes of one register.
-template <int G, int TENSOR, int BITS>
-__device__ __forceinline__ void write_hist_body(const WriteArgs &a, WriteShared<G> &sh) {
+template <int G, int TENSOR, int BITS, int HC>
+__device__ __forceinline__ void write_hist_body(const WriteArgs &a, WriteShared<G, HC> &sh) {
+  constexpr int XSTR = xstr<HC>();
   constexpr int NG = D / G, WPG = G / 32;
   constexpr int LEVELS = (1 << BITS) - 1;     // highest code
   constexpr uint32_t CMASK = 0x01010101u * LEVELS;  // one code per byte
@@ -180,9 +187,9 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a, WriteShared<
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const oscar_layer_cache &c = a.c;
   const int hkv = c.n_kv_heads;
-  const int h0 = hc * WHC;
+  const int h0 = hc * HC;
   if (h0 >= hkv) return;
-  const int nh = min(WHC, hkv - h0);
+  const int nh = min(HC, hkv - h0);
 
   int L0, n;
   if (!request_ok(a, b, L0, n)) {
@@ -196,7 +203,9 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a, WriteShared<
   const int jfirst = (hlo - N_SINK) / PAGE + bx * WPP;
   if (N_SINK + PAGE * jfirst >= hhi) return;
   const int jend = min((hhi - N_SINK + PAGE - 1) / PAGE, jfirst + WPP);
-  const float clip_s = a.clip[tensor] * 2048.0f;  // the clip in the accumulators' 2^11 scale
+  // the clip (the chunk's head's own with a rotation per head) in the
+  // accumulators' 2^11 scale
+  const float clip_s = (a.fstride[tensor] ? a.hclip[tensor][h0] : a.clip[tensor]) * 2048.0f;
   const int r_a = lane & 15, qd = lane >> 4;  // MFMA: token row (A) / column (B, D); k sub-block / row group
 
   // page ids: lane i < WPP holds hist_pt[b][jfirst + i] (-1 past the table),
@@ -251,8 +260,9 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a, WriteShared<
   // as 2^11 y.
   f16x8w rh[2][4], rl[2][4];
   {
-    const uint16_t *RH = reinterpret_cast<const uint16_t *>(a.forms[tensor] + FORM_RT_HI);
-    const uint16_t *RL = reinterpret_cast<const uint16_t *>(a.forms[tensor] + FORM_RT_LO);
+    const uint8_t *F = a.forms[tensor] + h0 * a.fstride[tensor];
+    const uint16_t *RH = reinterpret_cast<const uint16_t *>(F + FORM_RT_HI);
+    const uint16_t *RL = reinterpret_cast<const uint16_t *>(F + FORM_RT_LO);
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
@@ -371,7 +381,7 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a, WriteShared<
     for (int k = 0; k < 4; ++k) {
       const int t = wave + 4 * k, hh = lane >> 4, c16 = lane & 15;
       const u32x4w v = bf16x8_to_f16x8(xr[k]);
-      *reinterpret_cast<u32x4w *>(sh.xs + t * XSTR + hh * (D * 2) + 16 * c16) = v;
+      if (hh < HC) *reinterpret_cast<u32x4w *>(sh.xs + t * XSTR + hh * (D * 2) + 16 * c16) = v;
     }
     if (lane == 0) sh.bad[j & 1][wave] = __ballot(bad_next) != 0;
     __syncthreads();
@@ -399,7 +409,7 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a, WriteShared<
       // the partner's)
       const uint32_t selA = (tok & 2) ? 0x03020706u : 0x05040100u;
       const uint32_t selB = (tok & 1) ? 0x03070105u : 0x06020400u;
-      float szv[WHC][2];  // (scale, zero) of each head's group; stored after the heads
+      float szv[HC][2];  // (scale, zero) of each head's group; stored after the heads
       auto products = [&](int hh, f32x4w (&acc2)[2]) {
         f16x8w xb[4];
 #pragma unroll
@@ -484,13 +494,13 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a, WriteShared<
         f32x4w acc_cur[2], acc_next[2];
         products(0, acc_cur);
 #pragma unroll
-        for (int hh = 0; hh < WHC; ++hh) {
-          if (hh + 1 < WHC) products(hh + 1, acc_next);
+        for (int hh = 0; hh < HC; ++hh) {
+          if (hh + 1 < HC) products(hh + 1, acc_next);
           f32x4w yc[2];
           float lo, hi;
           finish(acc_cur, yc, lo, hi);
           quantise(hh, yc, lo, hi);
-          if (hh + 1 < WHC) {
+          if (hh + 1 < HC) {
             acc_cur[0] = acc_next[0];
             acc_cur[1] = acc_next[1];
             // spread the next head's sixteen products over this head's
@@ -503,10 +513,10 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a, WriteShared<
           }
         }
       } else {
-        f32x4w yc[WHC][2];
-        float lo[WHC], hi[WHC];
+        f32x4w yc[HC][2];
+        float lo[HC], hi[HC];
 #pragma unroll
-        for (int hh = 0; hh < WHC; ++hh) {
+        for (int hh = 0; hh < HC; ++hh) {
           f32x4w acc2[2];
           products(hh, acc2);
           finish(acc2, yc[hh], lo[hh], hi[hh]);
@@ -518,7 +528,7 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a, WriteShared<
         __syncthreads();
         const int w0 = (wave / WPG) * WPG;
 #pragma unroll
-        for (int hh = 0; hh < WHC; ++hh) {
+        for (int hh = 0; hh < HC; ++hh) {
           float l2 = sh.pmin[hh][tok][w0], h2 = sh.pmax[hh][tok][w0];
 #pragma unroll
           for (int w = 1; w < WPG; ++w) {
@@ -530,7 +540,7 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a, WriteShared<
       }
       if (qd == 0 && wave % WPG == 0) {
 #pragma unroll
-        for (int hh = 0; hh < WHC; ++hh) {
+        for (int hh = 0; hh < HC; ++hh) {
           sh.sz[buf][hh][g][tok][0] = szv[hh][0];
           sh.sz[buf][hh][g][tok][1] = szv[hh][1];
         }
@@ -549,21 +559,21 @@ __device__ __forceinline__ void write_hist_body(const WriteArgs &a, WriteShared<
 // min / max partials held across a barrier); wider groups keep two.
 // K and V workgroups (the low bit of blockIdx.y) run separate instances of
 // the body, so the tensor's branches are resolved at compile time.
-template <int G, int BITS>
+template <int G, int BITS, int HC>
 __global__ void __launch_bounds__(256) write_hist_kernel(WriteArgs a) {
-  __shared__ __attribute__((aligned(16))) WriteShared<G> sh;
+  __shared__ __attribute__((aligned(16))) WriteShared<G, HC> sh;
   if (__builtin_amdgcn_workgroup_id_y() & 1)
-    write_hist_body<G, 1, BITS>(a, sh);
+    write_hist_body<G, 1, BITS, HC>(a, sh);
   else
-    write_hist_body<G, 0, BITS>(a, sh);
+    write_hist_body<G, 0, BITS, HC>(a, sh);
 }
-template <int BITS>
+template <int BITS, int HC>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) write_hist_kernel_g32(WriteArgs a) {
-  __shared__ __attribute__((aligned(16))) WriteShared<32> sh;
+  __shared__ __attribute__((aligned(16))) WriteShared<32, HC> sh;
   if (__builtin_amdgcn_workgroup_id_y() & 1)
-    write_hist_body<32, 1, BITS>(a, sh);
+    write_hist_body<32, 1, BITS, HC>(a, sh);
   else
-    write_hist_body<32, 0, BITS>(a, sh);
+    write_hist_body<32, 0, BITS, HC>(a, sh);
 }
 
 // New tokens that land in the sink or the recent ring: raw bf16 copies.
@@ -613,24 +623,39 @@ hipError_t launch_write_kv(const oscar_layer_cache &c, RotArg rk, RotArg rv,
   a.forms[1] = rv.forms;
   a.clip[0] = rk.clip;
   a.clip[1] = rv.clip;
+  a.fstride[0] = rk.stride;
+  a.fstride[1] = rv.stride;
+  for (int h = 0; h < MAX_HEAD_ROT; ++h) {
+    a.hclip[0][h] = rk.head_clip[h];
+    a.hclip[1][h] = rv.head_clip[h];
+  }
   a.src[0] = k_new;
   a.src[1] = v_new;
   a.cu_new = cu_new;
   a.len_before = len_before;
   a.total_tokens = total_tokens;
   a.max_new = max_new;
-  // history positions entering in one call span at most max_new + 16 rows
+  // history positions entering in one call span at most max_new + 16 rows;
+  // a rotation per KV head: one head per workgroup
+  const bool per_head = rk.stride != 0 || rv.stride != 0;
+  const int hc = per_head ? 1 : WHC;
   const int tiles = (max_new + PAGE - 1) / PAGE + 2;
-  const dim3 grid((tiles + WPP - 1) / WPP, 2 * ((c.n_kv_heads + WHC - 1) / WHC), batch);
+  const dim3 grid((tiles + WPP - 1) / WPP, 2 * ((c.n_kv_heads + hc - 1) / hc), batch);
   const KernelEvents ev = take_profile_events();
   const bool int4 = cache_bits(c) == 4;
-#define OSCAR_WRITE_LAUNCH(K_) hipExtLaunchKernelGGL((K_), grid, dim3(256), 0, s, ev.before, ev.after, 0, a)
-  switch (c.group) {
-    case 32: if (int4) OSCAR_WRITE_LAUNCH(write_hist_kernel_g32<4>); else OSCAR_WRITE_LAUNCH(write_hist_kernel_g32<2>); break;
-    case 64: if (int4) OSCAR_WRITE_LAUNCH((write_hist_kernel<64, 4>)); else OSCAR_WRITE_LAUNCH((write_hist_kernel<64, 2>)); break;
-    default: if (int4) OSCAR_WRITE_LAUNCH((write_hist_kernel<128, 4>)); else OSCAR_WRITE_LAUNCH((write_hist_kernel<128, 2>)); break;
-  }
-#undef OSCAR_WRITE_LAUNCH
+  auto go = [&](auto kern) { hipExtLaunchKernelGGL(kern, grid, dim3(256), 0, s, ev.before, ev.after, 0, a); };
+  auto pick = [&](auto hc_tag) {
+    constexpr int H = decltype(hc_tag)::value;
+    switch (c.group) {
+      case 32: int4 ? go(write_hist_kernel_g32<4, H>) : go(write_hist_kernel_g32<2, H>); break;
+      case 64: int4 ? go(write_hist_kernel<64, 4, H>) : go(write_hist_kernel<64, 2, H>); break;
+      default: int4 ? go(write_hist_kernel<128, 4, H>) : go(write_hist_kernel<128, 2, H>); break;
+    }
+  };
+  if (per_head)
+    pick(std::integral_constant<int, 1>{});
+  else
+    pick(std::integral_constant<int, WHC>{});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(write_raw_kernel, dim3(N_SINK + N_RECENT, batch), dim3(256), 0, s, a);

@@ -146,10 +146,25 @@ typedef struct oscar_layer_cache {
 /* Device forms of one fixed per-layer rotation R = U*H*P ([nl] §2.2.A
  * "Formule", [fr] §2.2.A.3; row-vector convention x_rot = x*R) and its clip
  * threshold ([nl]/[fr] §2.2.A, [abs] "fixed per-layer rotations and clipping
- * thresholds").  `forms` is written by oscar_prepare_rotation. */
+ * thresholds").  `forms` is written by oscar_prepare_rotation.
+ *
+ * Per-KV-head rotations (optional, an extension of the pages' per-layer
+ * rule): n_heads equal to the cache's n_kv_heads (at most
+ * OSCAR_MAX_HEAD_ROTATIONS) gives each KV head h its own rotation, whose
+ * forms start h * oscar_rotation_bytes() bytes into `forms` (each written
+ * by oscar_prepare_rotation), and its own clip head_clips[h] (host array,
+ * read during the call only; each as `clip` below, which is then unused).
+ * n_heads 0 or 1: one rotation for every head (head_clips unused).  Both
+ * rotations of a call may use either form independently.  Errors:
+ * OSCAR_EINVAL for another n_heads, a NULL head_clips or a clip outside
+ * (0, 65504]. */
+#define OSCAR_MAX_HEAD_ROTATIONS 32
 typedef struct oscar_rotation {
-  const void *forms;       /* device, oscar_rotation_bytes() bytes           */
+  const void *forms;       /* device, n_heads (at least 1) consecutive forms
+                              of oscar_rotation_bytes() bytes each        */
   float clip;              /* > 0 and finite; values clamp to [-clip, clip]  */
+  int32_t n_heads;         /* 0 or 1: one rotation; else n_kv_heads         */
+  const float *head_clips; /* host float[n_heads] when n_heads > 1         */
 } oscar_rotation;
 
 OSCAR_API const char *oscar_last_error(void);
@@ -211,6 +226,22 @@ OSCAR_API int oscar_calib_accumulate(const uint16_t *q_cal, const uint16_t *k_ca
                            size_t workspace_bytes, oscar_stream_t stream);
 OSCAR_API int oscar_calib_rotations(const double *sums, double count, double *R_K, double *R_V,
                           void *workspace, size_t workspace_bytes, oscar_stream_t stream);
+
+/* Per-KV-head moments, for per-head rotations (an extension of the pages'
+ * per-layer rule): as oscar_calib_accumulate, but KV head h's sums only
+ * take the Hq/Hkv query heads that read it (h*Hq/Hkv ..), each with its
+ * causal attention output over KV head h:
+ *   sums[h][0] += sum over tokens and those query heads of q q^T,
+ *   sums[h][1] += the same of o o^T.
+ * sums: device fp64 [Hkv][2][128][128], zeroed by the caller before the
+ * first sequence; KV head h's count grows by n_tokens * Hq/Hkv.  Then
+ * oscar_calib_rotations on sums + h * 2*128*128 gives head h's R_K and R_V,
+ * and oscar_clip_threshold over head h's K and V vectors its clips.
+ * Workspace, synchronisation and errors as oscar_calib_accumulate. */
+OSCAR_API int oscar_calib_accumulate_heads(const uint16_t *q_cal, const uint16_t *k_cal,
+                                           const uint16_t *v_cal, int64_t n_tokens, int32_t n_q_heads,
+                                           int32_t n_kv_heads, double *sums, void *workspace,
+                                           size_t workspace_bytes, oscar_stream_t stream);
 
 /* Clip threshold of one fixed rotation ([nl]/[fr] §2.2.A "clipping
  * thresholds"): the clip_quantile quantile (linear interpolation between

@@ -94,6 +94,8 @@ def compare_history(gpu_hist: np.ndarray, hist_pt: np.ndarray, tokens_k, tokens_
     """Two-level comparison of every history row of every request.
 
     tokens_k/v[b]: bf16 bits [L_b][Hkv][128] of request b (all positions).
+    R_K / R_V with clip_k / clip_v: the layer's rotation and clip, or one per
+    KV head ([Hkv][128][128] and [Hkv]).
     positions[b] (optional): subset of history positions to check.
     bits: code width of the pool (2 or 4).
     """
@@ -112,8 +114,9 @@ def compare_history(gpu_hist: np.ndarray, hist_pt: np.ndarray, tokens_k, tokens_
         hidx = hist_p - o.N_SINK
         pids = hist_pt[b, hidx // o.PAGE]
         rows = hidx % o.PAGE
-        for kind, toks, R, clip in (("K", tokens_k[b], R_K, clip_k), ("V", tokens_v[b], R_V, clip_v)):
+        for kind, toks, R_all, clip_all in (("K", tokens_k[b], R_K, clip_k), ("V", tokens_v[b], R_V, clip_v)):
             for h in range(hkv):
+                R, clip = o.head_rotation(R_all, clip_all, h)  # the layer's, or head h's own
                 x = o.bf16_to_f64(toks[hist_p, h, :])
                 q = o.quantize(x, R, clip, G, bits)
                 areas = o.split_block(gpu_hist[pids, h], G, bits)
@@ -178,6 +181,18 @@ class Scenario:
             self.R_K = self.R_V = R
             self.clip_k = float(np.float32(o.clip_threshold(o.bf16_to_f64(kc), R)))
             self.clip_v = float(np.float32(o.clip_threshold(o.bf16_to_f64(vc), R)))
+        elif rot == "per_head":
+            # a random rotation and a clip of its own for every KV head
+            self.R_K = np.stack([random_rotation(seed + 10 * h) for h in range(hkv)])
+            self.R_V = np.stack([random_rotation(seed + 10 * h + 1) for h in range(hkv)])
+            self.clip_k = [4.5 + 0.75 * h for h in range(hkv)]
+            self.clip_v = [3.5 + 0.5 * h for h in range(hkv)]
+        elif rot == "per_head_calibrated":
+            qc, kc, vc = self.ld.calibration(n_cal)
+            cal = o.calibrate_per_head(*(o.bf16_to_f64(x) for x in (qc, kc, vc)))
+            self.R_K, self.R_V = cal["R_K"], cal["R_V"]
+            self.clip_k = [float(np.float32(c)) for c in cal["clip_K"]]
+            self.clip_v = [float(np.float32(c)) for c in cal["clip_V"]]
         else:
             self.R_K, self.R_V = random_rotation(seed), random_rotation(seed + 1)
             self.clip_k = self.clip_v = 6.0

@@ -50,13 +50,14 @@ def test_struct_layout_matches_c():
     #include <stddef.h>
     #include "oscar.h"
     int main(void) {
-      printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(oscar_layer_cache),
+      printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %d\n", sizeof(oscar_layer_cache),
         offsetof(oscar_layer_cache, group), offsetof(oscar_layer_cache, hist),
         offsetof(oscar_layer_cache, n_hist_pages), offsetof(oscar_layer_cache, bf16),
         offsetof(oscar_layer_cache, n_bf16_pages), offsetof(oscar_layer_cache, hist_pt),
         offsetof(oscar_layer_cache, hist_pt_stride), offsetof(oscar_layer_cache, bf16_pt),
         offsetof(oscar_layer_cache, status), offsetof(oscar_layer_cache, code_bits),
-        sizeof(oscar_rotation));
+        sizeof(oscar_rotation), offsetof(oscar_rotation, clip), offsetof(oscar_rotation, n_heads),
+        offsetof(oscar_rotation, head_clips), OSCAR_MAX_HEAD_ROTATIONS);
       return 0;
     }
     """
@@ -69,7 +70,8 @@ def test_struct_layout_matches_c():
     L = _lib.LayerCacheC
     expect = [ctypes.sizeof(L), L.group.offset, L.hist.offset, L.n_hist_pages.offset, L.bf16.offset,
               L.n_bf16_pages.offset, L.hist_pt.offset, L.hist_pt_stride.offset, L.bf16_pt.offset,
-              L.status.offset, L.code_bits.offset, ctypes.sizeof(_lib.RotationC)]
+              L.status.offset, L.code_bits.offset, ctypes.sizeof(_lib.RotationC), _lib.RotationC.clip.offset,
+              _lib.RotationC.n_heads.offset, _lib.RotationC.head_clips.offset, _lib.MAX_HEAD_ROTATIONS]
     assert vals == expect
 
 
@@ -118,12 +120,27 @@ def test_write_validation_codes():
     assert _write(rv=_lib.RotationC(0, 1.0)) == E.OSCAR_EINVAL
     assert _write(batch=0) == E.OSCAR_EINVAL
     assert _write(max_new=32, total=16) == E.OSCAR_EINVAL
+    # per-KV-head rotations: n_heads must be the cache's n_kv_heads (2 here),
+    # with a valid host clip per head
+    clips = (ctypes.c_float * 2)(3.0, 4.0)
+    cp = ctypes.cast(clips, ctypes.POINTER(ctypes.c_float))
+    assert _write(rk=_lib.RotationC(0x5000, 0.0, 3, cp)) == E.OSCAR_EINVAL and "n_heads" in _err()
+    assert _write(rk=_lib.RotationC(0x5000, 0.0, -1, None)) == E.OSCAR_EINVAL and "n_heads" in _err()
+    assert _write(rv=_lib.RotationC(0x5000, 0.0, 2, None)) == E.OSCAR_EINVAL and "head_clips" in _err()
+    bad = (ctypes.c_float * 2)(3.0, float("inf"))
+    assert _write(rv=_lib.RotationC(0x5000, 0.0, 2, ctypes.cast(bad, ctypes.POINTER(ctypes.c_float)))) == \
+        E.OSCAR_EINVAL and "head_clips[1]" in _err()
+    big = _cache(n_kv_heads=40)
+    clips40 = (ctypes.c_float * 40)(*([2.0] * 40))
+    assert _write(c=big, rk=_lib.RotationC(0x5000, 0.0, 40, ctypes.cast(clips40, ctypes.POINTER(ctypes.c_float)))) \
+        == E.OSCAR_EINVAL and "at most 32" in _err()
     assert _write(k=0) == E.OSCAR_EINVAL
     assert _write(cu=0) == E.OSCAR_EINVAL
     # nothing to write: success without touching a device
     assert _write(max_new=0, total=0, k=0, v=0) == E.OSCAR_OK
     if NO_GPU:  # valid arguments, no device: refused before any launch
         assert _write() == E.OSCAR_ENODEV
+        assert _write(rk=_lib.RotationC(0x5000, 0.0, 2, cp)) == E.OSCAR_ENODEV  # per-head: valid
 
 
 def _decode(c=None, hq=8, batch=1, max_len=150, ws=0xA000, ws_bytes=1 << 30, scale=0.088, q=0xB000):
@@ -187,6 +204,10 @@ def test_calibrate_and_prepare_validation_codes():
     assert lib.oscar_calib_accumulate(0x1, 0x1, 0x1, 0, 8, 2, 0x1, W, WB, None) == E.OSCAR_EINVAL
     assert lib.oscar_calib_accumulate(0x1, 0x1, 0x1, 16, 8, 3, 0x1, W, WB, None) == E.OSCAR_EUNSUPPORTED
     assert lib.oscar_calib_accumulate(0x1, 0x1, 0x1, 16, 8, 2, 0x1, W, 1024, None) == E.OSCAR_EWORKSPACE
+    assert lib.oscar_calib_accumulate_heads(0, 0x1, 0x1, 16, 8, 2, 0x1, W, WB, None) == E.OSCAR_EINVAL
+    assert lib.oscar_calib_accumulate_heads(0x1, 0x1, 0x1, 70000, 8, 2, 0x1, W, WB, None) == E.OSCAR_EINVAL
+    assert lib.oscar_calib_accumulate_heads(0x1, 0x1, 0x1, 16, 8, 3, 0x1, W, WB, None) == E.OSCAR_EUNSUPPORTED
+    assert lib.oscar_calib_accumulate_heads(0x1, 0x1, 0x1, 16, 8, 2, 0x1, W, 1024, None) == E.OSCAR_EWORKSPACE
     assert lib.oscar_calib_rotations(0x1, 0.0, R, R, W, WB, None) == E.OSCAR_EINVAL
     assert lib.oscar_calib_rotations(0x1, float("nan"), R, R, W, WB, None) == E.OSCAR_EINVAL
     assert lib.oscar_calib_rotations(0, 10.0, R, R, W, WB, None) == E.OSCAR_EINVAL
