@@ -166,8 +166,6 @@ struct StepArgs {
   oscar_layer_cache c;
   const uint8_t *fk, *fv;
   float clip_k, clip_v;
-  int64_t fstride_k, fstride_v;  // bytes between KV heads' forms (0: one rotation for the layer)
-  float hclip_k[MAX_HEAD_ROT], hclip_v[MAX_HEAD_ROT];  // per-head clips (fstride != 0)
   // append (may be null: no append)
   const uint16_t *k_new, *v_new;  // [B][Hkv][128]
   const int32_t *len_before;      // [B]: the new token goes to position len_before[b]
@@ -184,15 +182,28 @@ struct StepArgs {
   int part_slots;                 // partials per query head: 1 + max(n_splits, merge window)
   uint32_t *counters;             // [B][Hkv][COUNTER_STRIDE]: word 0 = workgroups done (zero between calls)
   float *out;                     // [B][Hq][128]
+  // per-KV-head rotations (last, so the fields above keep their offsets)
+  int64_t fstride_k, fstride_v;   // bytes between KV heads' forms (0: one rotation for the layer)
+  float hclip_k[MAX_HEAD_ROT], hclip_v[MAX_HEAD_ROT];  // per-head clips (fstride != 0)
 };
 
 __device__ inline bool valid_len(int L, int max_len) { return L >= 1 && L <= max_len; }
 
-// KV head hk's rotation forms and clips (the layer's when the stride is 0)
-__device__ inline const uint8_t *forms_k(const StepArgs &a, int hk) { return a.fk + hk * a.fstride_k; }
-__device__ inline const uint8_t *forms_v(const StepArgs &a, int hk) { return a.fv + hk * a.fstride_v; }
-__device__ inline float head_clip_k(const StepArgs &a, int hk) { return a.fstride_k ? a.hclip_k[hk] : a.clip_k; }
-__device__ inline float head_clip_v(const StepArgs &a, int hk) { return a.fstride_v ? a.hclip_v[hk] : a.clip_v; }
+// KV head hk's rotation forms and clips.  PH (a rotation per KV head) is a
+// template parameter: the per-layer instances read neither the strides nor
+// the head clips, and compile as they would without them.
+template <bool PH>
+__device__ inline const uint8_t *forms_k(const StepArgs &a, int hk) { return PH ? a.fk + hk * a.fstride_k : a.fk; }
+template <bool PH>
+__device__ inline const uint8_t *forms_v(const StepArgs &a, int hk) { return PH ? a.fv + hk * a.fstride_v : a.fv; }
+template <bool PH>
+__device__ inline float head_clip_k(const StepArgs &a, int hk) {
+  return (PH && a.fstride_k) ? a.hclip_k[hk] : a.clip_k;
+}
+template <bool PH>
+__device__ inline float head_clip_v(const StepArgs &a, int hk) {
+  return (PH && a.fstride_v) ? a.hclip_v[hk] : a.clip_v;
+}
 
 // ------------------------------------------------------------------ q and append
 
@@ -265,7 +276,7 @@ struct EvictWork {
 // dequantised and rotated back (e.u; q.k is the same in either basis) with its
 // score per query head (e.sc): the history workgroups leave its row out,
 // since their copy of the page may predate this write.  Workgroup-wide.
-template <int GQA, int G, int BITS>
+template <int GQA, int G, int BITS, bool PH>
 __device__ void evict_token(const StepArgs &a, int b, int hk, int tid, int wave, const AppendPlan &ap, uint8_t *blk,
                             EvictWork &e) {
   constexpr int LEVELS = (1 << BITS) - 1;
@@ -285,7 +296,7 @@ __device__ void evict_token(const StepArgs &a, int b, int hk, int tid, int wave,
   f32x4 rf[2][8];
 #pragma unroll
   for (int vec = 0; vec < 2; ++vec) {
-    const float *RT = reinterpret_cast<const float *>((vec ? forms_v(a, hk) : forms_k(a, hk)) + FORM_RT) + jr * D + 4 * qq;
+    const float *RT = reinterpret_cast<const float *>((vec ? forms_v<PH>(a, hk) : forms_k<PH>(a, hk)) + FORM_RT) + jr * D + 4 * qq;
 #pragma unroll
     for (int k = 0; k < 8; ++k) rf[vec][k] = *reinterpret_cast<const f32x4 *>(RT + (k >> 2) * 64 * D + 32 * (k & 3));
   }
@@ -329,14 +340,14 @@ __device__ void evict_token(const StepArgs &a, int b, int hk, int tid, int wave,
   f32x4 rb[2][8];
 #pragma unroll
   for (int vec = 0; vec < 2; ++vec) {
-    const float *Rr = reinterpret_cast<const float *>((vec ? forms_v(a, hk) : forms_k(a, hk)) + FORM_R) + jr * D + 4 * qq;
+    const float *Rr = reinterpret_cast<const float *>((vec ? forms_v<PH>(a, hk) : forms_k<PH>(a, hk)) + FORM_R) + jr * D + 4 * qq;
 #pragma unroll
     for (int k = 0; k < 8; ++k) rb[vec][k] = *reinterpret_cast<const f32x4 *>(Rr + (k >> 2) * 64 * D + 32 * (k & 3));
   }
   __syncthreads();
   // ---- clip and quantise: group min / max over G consecutive channels (all
   // threads take part; threads >= 256 repeat the work of threads < 256)
-  const float clip = v ? head_clip_v(a, hk) : head_clip_k(a, hk);
+  const float clip = v ? head_clip_v<PH>(a, hk) : head_clip_k<PH>(a, hk);
   const float xc = fminf(fmaxf(e.y[v][ch], -clip), clip);
   float lo, hi;
   if constexpr (G == 128) {
@@ -472,12 +483,12 @@ struct QLoads {
 // Every load is issued on every path (`hist` false: every lane re-reads one
 // line of R_K), so the compiler can count exactly how many loads its waits
 // may leave in flight.
-template <int GQA>
+template <int GQA, bool PH>
 __device__ inline void build_q_issue(const StepArgs &a, int b, int hk, int tid, bool hist, QLoads<GQA> &ql) {
   constexpr int NT = AW * 64;
   // eight consecutive lanes read one 128-byte line of a row
   const int jr = tid >> 3, qq = tid & 7;
-  const float *RT = reinterpret_cast<const float *>(forms_k(a, hk) + FORM_RT) + (hist ? jr * D : 0) + 4 * qq;
+  const float *RT = reinterpret_cast<const float *>(forms_k<PH>(a, hk) + FORM_RT) + (hist ? jr * D : 0) + 4 * qq;
   const int s_hi = hist ? 64 * D : 0, s_k = hist ? 32 : 0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) ql.rk[k] = *reinterpret_cast<const f32x4 *>(RT + (k >> 2) * s_hi + s_k * (k & 3));
@@ -1266,7 +1277,7 @@ __device__ void merge_unit(const StepArgs &a, int b, int hk, int used, int tid, 
 template <int GQA>
 constexpr int merge_threads() { return D * (GQA < 2 ? 2 : GQA); }
 
-template <int GQA>
+template <int GQA, bool PH>
 __global__ void __launch_bounds__(merge_threads<GQA>()) merge_kernel(StepArgs a) {
   constexpr int NT = merge_threads<GQA>(), MCH = merge_ch<GQA>();
   const int hk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
@@ -1287,7 +1298,7 @@ __global__ void __launch_bounds__(merge_threads<GQA>()) merge_kernel(StepArgs a)
   // read 128 contiguous bytes
   constexpr int NR = 1024 / NT;  // rows per thread: 128 rows x 8 lanes over NT threads
   const int cr = tid >> 3, qq = tid & 7;
-  const float *Rc = reinterpret_cast<const float *>(forms_v(a, hk) + FORM_R) + cr * D + 4 * qq;
+  const float *Rc = reinterpret_cast<const float *>(forms_v<PH>(a, hk) + FORM_R) + cr * D + 4 * qq;
   f32x4 rv[4 * NR];
 #pragma unroll
   for (int m = 0; m < NR; ++m)
@@ -1384,7 +1395,7 @@ __global__ void __launch_bounds__(merge_threads<GQA>()) merge_kernel(StepArgs a)
 template <int GQA, int NG>
 constexpr int attend_waves() { return (GQA <= 4 && NG <= 2) ? 4 : 1; }
 
-template <int GQA, int NG, bool FUSED, int BITS>
+template <int GQA, int NG, bool FUSED, int BITS, bool PH>
 __global__ void __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(attend_waves<GQA, NG>())))
 attend_kernel(StepArgs a) {
   // several rounds: the split index varies slowest, so every unit's first
@@ -1408,7 +1419,7 @@ attend_kernel(StepArgs a) {
     pid_pre = c.hist_pt[int64_t(b) * c.hist_pt_stride + j];
   }
   QLoads<GQA> ql;
-  build_q_issue<GQA>(a, b, hk, tid, split > 0, ql);
+  build_q_issue<GQA, PH>(a, b, hk, tid, split > 0, ql);
   // keeps these loads ahead of the length checks below (otherwise the
   // compiler sinks them past the early exits, behind the wait for L0)
   asm volatile("" ::: "memory");
@@ -1485,7 +1496,7 @@ attend_kernel(StepArgs a) {
         blk = c.hist + (int64_t(pid) * c.n_kv_heads + hk) * hist_block_bytes(D / NG, BITS);
       else if (tid == 0)
         flag_status(c.status, OSCAR_STATUS_BAD_PAGE);
-      evict_token<GQA, D / NG, BITS>(a, b, hk, tid, wave, ap, blk, work.e);
+      evict_token<GQA, D / NG, BITS, PH>(a, b, hk, tid, wave, ap, blk, work.e);
       extra = true;
     }
   } else {
@@ -1515,7 +1526,7 @@ attend_kernel(StepArgs a) {
       // computed here, not hoisted above the page loop (register pressure)
       int t = tid;
       asm volatile("" : "+v"(t));
-      if (split > 0) rv.load(forms_v(a, hk), t);
+      if (split > 0) rv.load(forms_v<PH>(a, hk), t);
     }
     __syncthreads();
     if (split > 0)
@@ -1554,15 +1565,22 @@ template <int GQA, int NG, int BITS>
 static hipError_t launch_t(const StepArgs &a, bool fused, int batch, int hkv, hipStream_t s) {
   const KernelEvents ev = take_profile_events();
   const dim3 grid = fused ? dim3(1 + a.n_splits, hkv, batch) : dim3(hkv, batch, 1 + a.n_splits);
-  if (fused) {
-    hipExtLaunchKernelGGL((attend_kernel<GQA, NG, true, BITS>), grid, dim3(AW * 64), 0, s, ev.before, ev.after, 0, a);
+  auto go = [&](auto ph_tag) -> hipError_t {
+    constexpr bool PH = decltype(ph_tag)::value;
+    if (fused) {
+      hipExtLaunchKernelGGL((attend_kernel<GQA, NG, true, BITS, PH>), grid, dim3(AW * 64), 0, s, ev.before, ev.after,
+                            0, a);
+      return hipGetLastError();
+    }
+    hipExtLaunchKernelGGL((attend_kernel<GQA, NG, false, BITS, PH>), grid, dim3(AW * 64), 0, s, ev.before, ev.after,
+                          0, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((merge_kernel<GQA, PH>), dim3(hkv, batch), dim3(merge_threads<GQA>()), 0, s, a);
     return hipGetLastError();
-  }
-  hipExtLaunchKernelGGL((attend_kernel<GQA, NG, false, BITS>), grid, dim3(AW * 64), 0, s, ev.before, ev.after, 0, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((merge_kernel<GQA>), dim3(hkv, batch), dim3(merge_threads<GQA>()), 0, s, a);
-  return hipGetLastError();
+  };
+  // a rotation per KV head (either tensor) runs the instances that index them
+  return (a.fstride_k || a.fstride_v) ? go(std::true_type{}) : go(std::false_type{});
 }
 
 template <int GQA, int BITS>
