@@ -607,8 +607,12 @@ def decode_main(args, W, dev, workload):
     # The split-K attention kernel dominates the step.  The library records a
     # pair of HIP events on the decode stream right around that one kernel
     # (oscar_profile_events); eager decode calls of every layer, three rounds.
+    # A bounded spin kernel goes first, so that the calls queue up behind it
+    # and run back to back, as in the replayed step (otherwise the device
+    # idles between short kernels while the host issues the next call).
     pairs = []
     with torch.cuda.stream(stream):
+        torch.cuda._sleep(20_000_000)
         for rep in range(3):
             for ly in layers:
                 a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
