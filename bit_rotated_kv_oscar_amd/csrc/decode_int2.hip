@@ -936,13 +936,15 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
       f32x4 d = dinit[ch];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) d = mfma_k(aq[ch][kb], kx[kb], d);
-      const float v0 = fmaf(float(km0.x), fmaf(d[1], 0x1p-11f, d[0]), float(km0.y) * qz[ch][0]);
-      const float v1 = fmaf(float(km1.x), fmaf(d[3], 0x1p-11f, d[2]), float(km1.y) * qz[ch][1]);
+      // s_g (d_hi + 2^-11 d_lo) + z_g qz_g per pair, as mixed-precision
+      // FMAs on the packed meta (fp16 operands taken as they are)
+      const float d0 = fmaf(d[1], 0x1p-11f, d[0]), d1 = fmaf(d[3], 0x1p-11f, d[2]);
       if constexpr (NG == 1) {
-        S[ch][0] = v0;
-        S[ch][1] = v1;
+        S[ch][0] = fmaf(float(km0.x), d0, fmaf(float(km0.y), qz[ch][0], 0.f));
+        S[ch][1] = fmaf(float(km1.x), d1, fmaf(float(km1.y), qz[ch][1], 0.f));
       } else {
-        float sv = v0 + v1;
+        const float z = fmaf(float(km1.y), qz[ch][1], fmaf(float(km0.y), qz[ch][0], 0.f));
+        float sv = fmaf(float(km1.x), d1, fmaf(float(km0.x), d0, z));
         if constexpr (NG == 4) sv += __shfl_xor(sv, 16);
         S[ch][0] = sv;
       }
@@ -1011,20 +1013,20 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
     uint32_t ps[NCH];
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
-      float x0, x1;
+      // each half one mixed-precision FMA (fp16 scale in, fp16 product out)
+      _Float16 x0, x1;
       if constexpr (NG == 1) {
-        const float sv = float(vm0.x);
-        x0 = pw[ch][0] * sv;
-        x1 = pw[ch][1] * sv;
+        x0 = _Float16(fmaf(pw[ch][0], float(vm0.x), 0.f));
+        x1 = _Float16(fmaf(pw[ch][1], float(vm0.x), 0.f));
       } else {
-        x0 = pw[ch][0] * float(vm0.x);
-        x1 = pw[ch][0] * float(vm1.x);
+        x0 = _Float16(fmaf(pw[ch][0], float(vm0.x), 0.f));
+        x1 = _Float16(fmaf(pw[ch][0], float(vm1.x), 0.f));
       }
       if constexpr (PARTIAL) {  // absent rows: their meta may be anything
-        x0 = tok_ok ? x0 : 0.f;
-        x1 = tok_ok ? x1 : 0.f;
+        x0 = tok_ok ? x0 : _Float16(0.f);
+        x1 = tok_ok ? x1 : _Float16(0.f);
       }
-      const h2v hv = {_Float16(x0), _Float16(x1)};
+      const h2v hv = {x0, x1};
       ps[ch] = __builtin_bit_cast(uint32_t, hv);
     }
     // lane (n, tq) = head hp, tokens 4tq..4tq+3: B_g from the dwords of its

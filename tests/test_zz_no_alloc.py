@@ -39,16 +39,17 @@ def _noalloc_c(oscar, cache, rk, rv, q, lens, max_len, out):
                                          q.shape[0], max_len, SCALE, ctypes.c_void_p(out.data_ptr()), stream)
 
 
-@pytest.mark.parametrize("hq,hkv,G,first", [
-    (32, 8, 64, [9000, 4000, 200]),          # one round of workgroups: merged in the attend kernel
-    (8, 2, 32, [9000, 4000, 200]),
-    (32, 8, 64, [300 + 97 * i for i in range(20)]),  # 160 units: several rounds, separate merge kernel
+@pytest.mark.parametrize("hq,hkv,G,first,rot", [
+    (32, 8, 64, [9000, 4000, 200], "random"),          # one round of workgroups: merged in the attend kernel
+    (8, 2, 32, [9000, 4000, 200], "random"),
+    (32, 8, 64, [300 + 97 * i for i in range(20)], "random"),  # 160 units: several rounds, separate merge kernel
+    (16, 4, 64, [5000, 1200], "per_head"),             # a rotation and clip per KV head
 ])
-def test_noalloc_decode_matches_workspace_decode_twice(hq, hkv, G, first):
+def test_noalloc_decode_matches_workspace_decode_twice(hq, hkv, G, first, rot):
     import bit_rotated_kv_oscar_amd as oscar
     # first call as given; second call: 1 request of 700 tokens
     for seed, lens in ((3100 + G, first), (3200 + G, [700])):
-        sc = Scenario(seed, hq, hkv, G, lens)
+        sc = Scenario(seed, hq, hkv, G, lens, rot=rot)
         ref, cache, rk, rv = _gpu_case(oscar, sc)
         q = to_dev_bf16(sc.q)
         L = torch.tensor(sc.lens, dtype=torch.int32, device="cuda")
