@@ -124,9 +124,13 @@ struct SoftState {
 // raised.
 template <int NZ>
 __device__ inline void softmax_tile(SoftState<NZ> &st, const float (&s)[4], float (&p)[4], float sc = 1.f) {
-  const float mx = lanes4_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))) * sc;
-  const bool raise = mx > st.m + LAZY_TH;  // false while both are -inf
-  if (__builtin_amdgcn_ballot_w64(raise)) {
+  // the lane's own four keys decide whether any query may need a new max
+  // (the four lanes of a query share its running max); the query's max over
+  // its 16 keys is formed only then
+  const float lmx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])) * sc;
+  if (__builtin_amdgcn_ballot_w64(lmx > st.m + LAZY_TH)) {  // false while both are -inf
+    const float mx = lanes4_max(lmx);
+    const bool raise = mx > st.m + LAZY_TH;
     const float mn = raise ? mx : st.m;
     const float alpha = raise ? __builtin_amdgcn_exp2f(st.m - mn) : 1.f;  // st.m = -inf: 0
     st.l *= alpha;
