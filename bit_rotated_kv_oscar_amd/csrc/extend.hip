@@ -37,9 +37,9 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 struct ExtendArgs {
   const uint8_t *hist;
-  int64_t n_hist_pages;
+  int n_hist_pages;  // below 2^31 (page ids are int32): scalar compares
   const uint16_t *bf16;
-  int64_t n_bf16_pages;
+  int n_bf16_pages;
   const int32_t *hist_pt;
   int hist_pt_stride;
   const int32_t *bf16_pt;
@@ -105,6 +105,7 @@ struct SoftState {
   f32x4 cacc[NZ > 0 ? NZ : 1];
   float zacc[NZ > 0 ? NZ : 1];  // sum_t p_t z_t of the lane's keys, per group
   float m, l;                   // running max (log2 units) of the lane's query; lane-partial sum
+  float thr, nref;              // m + LAZY_TH (the raise test) and -m (0 while m = -inf)
   __device__ void init() {
     for (int b = 0; b < 8; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int g = 0; g < (NZ > 0 ? NZ : 1); ++g) {
@@ -113,6 +114,8 @@ struct SoftState {
     }
     m = -INFINITY;
     l = 0.f;
+    thr = -INFINITY;
+    nref = 0.f;
   }
 };
 
@@ -128,9 +131,9 @@ __device__ inline void softmax_tile(SoftState<NZ> &st, const float (&s)[4], floa
   // (the four lanes of a query share its running max); the query's max over
   // its 16 keys is formed only then
   const float lmx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])) * sc;
-  if (__builtin_amdgcn_ballot_w64(lmx > st.m + LAZY_TH)) {  // false while both are -inf
+  if (__builtin_amdgcn_ballot_w64(lmx > st.thr)) {  // false while both are -inf
     const float mx = lanes4_max(lmx);
-    const bool raise = mx > st.m + LAZY_TH;
+    const bool raise = mx > st.thr;
     const float mn = raise ? mx : st.m;
     const float alpha = raise ? __builtin_amdgcn_exp2f(st.m - mn) : 1.f;  // st.m = -inf: 0
     st.l *= alpha;
@@ -140,14 +143,11 @@ __device__ inline void softmax_tile(SoftState<NZ> &st, const float (&s)[4], floa
       st.zacc[g] *= alpha;
     }
     st.m = mn;
+    st.thr = mn + LAZY_TH;
+    st.nref = mn == -INFINITY ? 0.f : -mn;
   }
-  const float ref = st.m == -INFINITY ? 0.f : st.m;
-  float sum = 0.f;
-  for (int r = 0; r < 4; ++r) {
-    p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sc, -ref));
-    sum += p[r];
-  }
-  st.l += sum;
+  for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sc, st.nref));
+  st.l += (p[0] + p[1]) + (p[2] + p[3]);
 }
 
 // One tile of 16 raw bf16 keys: key t's K row at kp + t * stride (elements),
@@ -573,9 +573,9 @@ hipError_t launch_extend(const oscar_layer_cache &c, RotArg rk, RotArg rv, const
                          int max_prefix, float sm_scale, float *out, hipStream_t s) {
   ExtendArgs a;
   a.hist = c.hist;
-  a.n_hist_pages = c.n_hist_pages;
+  a.n_hist_pages = int(c.n_hist_pages);
   a.bf16 = c.bf16;
-  a.n_bf16_pages = c.n_bf16_pages;
+  a.n_bf16_pages = int(c.n_bf16_pages);
   a.hist_pt = c.hist_pt;
   a.hist_pt_stride = c.hist_pt_stride;
   a.bf16_pt = c.bf16_pt;
