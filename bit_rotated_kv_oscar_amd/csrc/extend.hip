@@ -53,6 +53,7 @@ struct ExtendArgs {
   int64_t total_tokens;  // rows of q / k_new / v_new / out
   float scale_log2;  // sm_scale * log2(e)
   float pv_scale;    // power of two: p s_V pv_scale stays below 2^15 (fp16 operand)
+  float pk4, pk16;   // log2(4 pv_scale), log2(16 pv_scale): the PV weights of the history rows
   uint32_t ex_m4, ex_m16, ex_e;  // code expansion constants 0x03000300, 0x00C000C0, 0x3C003C00
   uint32_t ex_mn;                // INT4 expansion mask 0x03C003C0
   int bits;                      // history code width (2 or 4)
@@ -99,23 +100,33 @@ __device__ inline void split_bf16(const float (&x)[4], s16x4 &hi, s16x4 &lo) {
 // which the expansion's constant 1 adds to acc, and the zero-point sums per
 // group).  The two parts are merged at the end, so only one part's
 // accumulators are live at a time.
+// History tiles (NZ > 0) keep two classes of the lane's four keys, rows 0, 1
+// and rows 2, 3: their probabilities come out of the exponential already
+// multiplied by the PV operand's power-of-two weight 2^off_a / 2^off_b (INT2:
+// pv_scale * 4 / pv_scale * 16; INT4: pv_scale * 16 for both), and their
+// sums (l / lb, zacc / zb) are taken per class and unweighted at the end.
 template <int NZ>
 struct SoftState {
+  static constexpr int NZ1 = NZ > 0 ? NZ : 1;
   f32x4 acc[8];
-  f32x4 cacc[NZ > 0 ? NZ : 1];
-  float zacc[NZ > 0 ? NZ : 1];  // sum_t p_t z_t of the lane's keys, per group
-  float m, l;                   // running max (log2 units) of the lane's query; lane-partial sum
-  float thr, nref;              // m + LAZY_TH (the raise test) and -m (0 while m = -inf)
-  __device__ void init() {
+  f32x4 cacc[NZ1];
+  float zacc[NZ1], zb[NZ1];     // sum_t p_t z_t of the lane's keys, per group (rows 0, 1 / 2, 3)
+  float m, l, lb;               // running max (log2 units) of the lane's query; lane-partial sums
+  float thr, nref, nrb;         // m + LAZY_TH (the raise test); off_a - m and off_b - m (off - 0 while m = -inf)
+  float offa, offb;             // the classes' weights, log2
+  __device__ void init(float off_a = 0.f, float off_b = 0.f) {
     for (int b = 0; b < 8; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int g = 0; g < (NZ > 0 ? NZ : 1); ++g) {
+    for (int g = 0; g < NZ1; ++g) {
       cacc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-      zacc[g] = 0.f;
+      zacc[g] = zb[g] = 0.f;
     }
     m = -INFINITY;
-    l = 0.f;
+    l = lb = 0.f;
     thr = -INFINITY;
-    nref = 0.f;
+    offa = off_a;
+    offb = off_b;
+    nref = off_a;
+    nrb = off_b;
   }
 };
 
@@ -137,17 +148,27 @@ __device__ inline void softmax_tile(SoftState<NZ> &st, const float (&s)[4], floa
     const float mn = raise ? mx : st.m;
     const float alpha = raise ? __builtin_amdgcn_exp2f(st.m - mn) : 1.f;  // st.m = -inf: 0
     st.l *= alpha;
+    if constexpr (NZ > 0) st.lb *= alpha;
     for (int b = 0; b < 8; ++b) st.acc[b] *= alpha;
     for (int g = 0; g < NZ; ++g) {
       st.cacc[g] *= alpha;
       st.zacc[g] *= alpha;
+      st.zb[g] *= alpha;
     }
     st.m = mn;
     st.thr = mn + LAZY_TH;
-    st.nref = mn == -INFINITY ? 0.f : -mn;
+    const float base = mn == -INFINITY ? 0.f : -mn;
+    st.nref = base + st.offa;
+    st.nrb = base + st.offb;
   }
-  for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sc, st.nref));
-  st.l += (p[0] + p[1]) + (p[2] + p[3]);
+  if constexpr (NZ > 0) {
+    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sc, r < 2 ? st.nref : st.nrb));
+    st.l += p[0] + p[1];
+    st.lb += p[2] + p[3];
+  } else {
+    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sc, st.nref));
+    st.l += (p[0] + p[1]) + (p[2] + p[3]);
+  }
 }
 
 // One tile of 16 raw bf16 keys: key t's K row at kp + t * stride (elements),
@@ -262,14 +283,14 @@ __device__ inline void hist_tile(SoftState<D / G> &st, const HistData<D / G, BIT
   // for rows 2, 3; INT4: 1/16), B = fp16(p s k / w): the product is B + c p s k; the column
   // sums of B come off at the end (cacc: the same B against an all-ones
   // operand), the zero points enter as sum_t p_t z_t
+  // (p carries the weight already: the softmax state's class offsets)
   const f16x4 ones = as_f16x4(0x3C003C00u, 0x3C003C00u);
-  float pw[4];
-  for (int r = 0; r < 4; ++r) pw[r] = p[r] * (pv_scale * ((BITS == 2 && r < 2) ? 4.f : 16.f));
   for (int g = 0; g < NG; ++g) {
     f16x4 bp;
     for (int r = 0; r < 4; ++r) {
-      bp[r] = _Float16(ok[r] ? fmaf(pw[r], lo_f16(hd.vm[g][r]), 0.f) : 0.f);  // one v_fma_mixlo_f16
-      st.zacc[g] = ok[r] ? fmaf(p[r], hi_f16(hd.vm[g][r]), st.zacc[g]) : st.zacc[g];
+      bp[r] = _Float16(ok[r] ? fmaf(p[r], lo_f16(hd.vm[g][r]), 0.f) : 0.f);  // one v_fma_mixlo_f16
+      float &z = r < 2 ? st.zacc[g] : st.zb[g];
+      z = ok[r] ? fmaf(p[r], hi_f16(hd.vm[g][r]), z) : z;
     }
     st.cacc[g] = mfma_v(ones, bp, st.cacc[g]);
     for (int b = g * G / 16; b < (g + 1) * G / 16; ++b) {
@@ -439,7 +460,9 @@ extend_kernel(ExtendArgs a) {
   // ======== history pages (INT2 or INT4)
   const float pv_unscale = 1.f / a.pv_scale;
   SoftState<NG> sh;
-  sh.init();
+  // rows 0, 1 of an INT2 page carry weight 4 pv_scale, rows 2, 3 (and every
+  // INT4 row) 16 pv_scale
+  sh.init(BITS == 2 ? a.pk4 : a.pk16, a.pk16);
   Expander ex;
   ex.m4 = a.ex_m4;
   ex.m16 = a.ex_m16;
@@ -515,8 +538,10 @@ extend_kernel(ExtendArgs a) {
   }
 
   // ======== merge: o = (f2 (acc_r + z) R_V^T + f1 acc_p) / (f1 l1 + f2 l2)
-  const float l2 = lanes4_sum(sh.l);
-  for (int g = 0; g < NG; ++g) sh.zacc[g] = lanes4_sum(sh.zacc[g]);
+  // the two classes' sums without their weights
+  const float ua = exp2f(-sh.offa), ub = exp2f(-sh.offb);
+  const float l2 = lanes4_sum(fmaf(sh.l, ua, sh.lb * ub));
+  for (int g = 0; g < NG; ++g) sh.zacc[g] = lanes4_sum(fmaf(sh.zacc[g], ua, sh.zb[g] * ub));
   const float mm = fmaxf(m1, sh.m);  // finite: every query sees at least itself
   const float f1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
   const float f2 = sh.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sh.m - mm);
@@ -602,6 +627,8 @@ hipError_t launch_extend(const oscar_layer_cache &c, RotArg rk, RotArg rv, const
   while (vmax * k > 32768.f) k *= 0.5f;
   while (vmax * k * 2.f <= 32768.f && k < 65536.f) k *= 2.f;
   a.pv_scale = k;
+  a.pk4 = std::log2(4.f * k);
+  a.pk16 = std::log2(16.f * k);
   a.ex_m4 = 0x03000300u;
   a.ex_m16 = 0x00C000C0u;
   a.ex_e = 0x3C003C00u;
