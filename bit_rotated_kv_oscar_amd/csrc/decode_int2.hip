@@ -620,7 +620,7 @@ __device__ __forceinline__ void build_q(const StepArgs &a, int tid, QWork<GQA, N
 
 // ------------------------------------------------------------------ attend
 
-// History pages reach LDS by direct global->LDS copies (global_load_lds):
+// History pages reach LDS by direct buffer->LDS copies (buffer_load ... lds):
 // several pages per wave in flight without holding registers.  One INT2
 // page block is 1024 + 128 NG bytes: one 16-byte-per-lane copy of the first
 // 1 KB, one of the rest on the first 8 NG lanes (INT4: two copies of 1 KB,
@@ -636,8 +636,17 @@ __device__ __forceinline__ void build_q(const StepArgs &a, int tid, QWork<GQA, N
 template <int BITS>
 constexpr int depth_of() { return BITS == 2 ? 4 : 3; }
 
-__device__ inline void lds_copy16(const void *src, void *lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+// Copies of one page block (wave-uniform address, `bytes` long) through a
+// buffer resource built in scalar registers: each copy takes the lane's
+// 32-bit offset, with no 64-bit address arithmetic per lane
+__device__ inline __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t *p, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(a)), hi = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
+  asm volatile("" : "+s"(lo), "+s"(hi));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>((uint64_t(hi) << 32) | lo), 0, bytes, 0x00020000);
+}
+__device__ inline void lds_copy16(__amdgpu_buffer_rsrc_t r, uint32_t off, void *lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_base, 16, off, 0, 0, 0);
 }
 
 template <int N>
@@ -881,11 +890,11 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
     return c.hist + (int64_t(pid) * c.n_kv_heads + hk) * SB;
   };
   auto issue = [&](int i, int sl) {
-    const uint8_t *blk = page_block(i, sl);
+    const auto rs = block_rsrc(page_block(i, sl), SB);
     uint8_t *dst = ring + sl * SB;
 #pragma unroll
-    for (int k = 0; k < NHB; ++k) lds_copy16(blk + 1024u * k + lane16, dst + 1024 * k);
-    if (lane < N2) lds_copy16(blk + uint32_t(HB) + lane16, dst + HB);
+    for (int k = 0; k < NHB; ++k) lds_copy16(rs, 1024u * k + lane16, dst + 1024 * k);
+    if (lane < N2) lds_copy16(rs, uint32_t(HB) + lane16, dst + HB);
   };
   // the first DEPTH - 1 pages go through registers: no copy into LDS is in
   // flight while the workgroup builds the q fragment (the compiler would
@@ -1080,11 +1089,11 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
   // range (checked once), so no per-page checks or bookkeeping
   auto issue_fast = [&](int i, int sl) {
     const int pid = __builtin_amdgcn_readlane(my_pid, i);
-    const uint8_t *blk = c.hist + (int64_t(pid) * c.n_kv_heads + hk) * SB;
+    const auto rs = block_rsrc(c.hist + (int64_t(pid) * c.n_kv_heads + hk) * SB, SB);
     uint8_t *dst = ring + sl * SB;
 #pragma unroll
-    for (int k = 0; k < NHB; ++k) lds_copy16(blk + 1024u * k + lane16, dst + 1024 * k);
-    if (lane < N2) lds_copy16(blk + uint32_t(HB) + lane16, dst + HB);
+    for (int k = 0; k < NHB; ++k) lds_copy16(rs, 1024u * k + lane16, dst + 1024 * k);
+    if (lane < N2) lds_copy16(rs, uint32_t(HB) + lane16, dst + HB);
   };
   auto step_fast = [&](int i, auto partial_tag) {
     if (i + DP - 1 < npw) issue_fast(i + DP - 1, (i + DP - 1) % DP);
