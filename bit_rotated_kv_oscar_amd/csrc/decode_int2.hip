@@ -92,6 +92,66 @@ struct Rows {
   __device__ static constexpr int head_slot(int h) { return NG == 1 ? (h % HC) % 2 : 0; }
 };
 
+// INT2 with one or two scale groups per head (F4 below): the score product
+// runs on the fp8 x fp4 matrix core instead (16x16x128, one instruction per
+// 16 rows over all 128 channels).  The stored 2-bit codes become fp4 (e2m1)
+// values c/2 by masking alone (nibble 00cc), and q' goes in as four fp8
+// (e4m3) parts whose sum carries it to 2^-16 of its group's largest value,
+// each part scaled back by the product's per-row power-of-two scale.  Per
+// chain two products: product j row 4qd + p is part p of pair (2qd + j) of
+// that chain (head and group as above), so lane (t, qd) again holds the
+// whole score of its pairs for token t.
+// Used where each wave's pages run long (the several-round plan): the
+// fragment build costs about what the shorter page loop saves over the
+// eight pages per wave of a batch-1 round.
+template <int BITS, int NG, bool FUSED>
+constexpr bool f4_scores() { return BITS == 2 && NG <= 2 && !FUSED; }
+
+// Bit position of the K code of channel c in its code dword (the slot
+// tables: u = 4 (k & 1) + (c & 7) / 2 for k = c / 32, low slot for even c,
+// high slot for odd), as shifts of two packed tables.  Spread to nibbles
+// (the dword masked with 0x33333333 after a right shift by 0 or 2), it
+// lands in nibble pos / 4 of spread register 2 (k / 2) + (pos / 2) % 2.
+__device__ inline int f4_code_bit(int c) {
+  constexpr uint64_t LO = 8ull | 6ull << 5 | 12ull << 10 | 10ull << 15 | 4ull << 20 | 2ull << 25 | 16ull << 30 | 14ull << 35;
+  constexpr uint64_t HI = 24ull | 22ull << 5 | 28ull << 10 | 26ull << 15 | 20ull << 20 | 18ull << 25 | 0ull << 30 | 30ull << 35;
+  const int u = 4 * ((c >> 5) & 1) + ((c & 7) >> 1);
+  return int((((c & 1) ? HI : LO) >> (5 * u)) & 31u);
+}
+
+// 2^n for -126 <= n <= 127, exactly
+__device__ inline float pow2i(int n) { return __uint_as_float(uint32_t(127 + n) << 23); }
+
+// fp8 e4m3 (bias 7, subnormal step 2^-9) round-to-nearest-even of t,
+// |t| < 448: the byte, and its value in val
+__device__ inline uint32_t fp8_rne(float t, float &val) {
+  const float a = fabsf(t);
+  const int e = max(int((__float_as_uint(a) >> 23) & 255u) - 127, -6);  // floor(log2 a), at least -6
+  const float q = rintf(a * pow2i(3 - e));                                // 0 .. 16
+  val = copysignf(q * pow2i(e - 3), t);
+  return (t < 0.f && q > 0.f ? 0x80u : 0u) | uint32_t(((e + 7) << 3) + int(q) - 8);
+}
+
+// The four fp8 part bytes of y (byte p = part p) for a group whose largest
+// |y| has exponent E: part 0 is y 2^(7-E) rounded (below 256 in magnitude),
+// each later part the remainder times 16 rounded (below 128)
+__device__ inline uint32_t fp8_parts(float y, int E) {
+  float t = y * pow2i(7 - E), val;
+  uint32_t w = 0;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    w |= fp8_rne(t, val) << (8 * p);
+    t = (t - val) * 16.f;
+  }
+  return w;
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+// the 32 fp8 bytes of an F4 A operand, held as two f16x8 fragment registers
+__device__ inline i32x8 f4_operand(f16x8 lo, f16x8 hi) {
+  return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15));
+}
+
 // Compute units of the current device (256 on MI355X; 256 when it cannot
 // be queried, e.g. while sizing a workspace on a host without a GPU).
 int64_t device_cus() {
@@ -499,7 +559,7 @@ __device__ inline void build_q_issue(const StepArgs &a, int b, int hk, int tid, 
 
 // Workgroup-wide, from the loads above: q' = q R_K and the A-operand
 // fragment block of the score product in frag_lds (layout of Rows).
-template <int GQA, int NG, int BITS>
+template <int GQA, int NG, int BITS, bool F4>
 __device__ __forceinline__ void build_q(const StepArgs &a, int tid, QWork<GQA, NG> &w, uint32_t *frag_lds, const QLoads<GQA> &ql) {
   using R = Rows<GQA, NG>;
   constexpr int G = R::G, SEG = QWork<GQA, NG>::SEG, NT = AW * 64;
@@ -552,12 +612,15 @@ __device__ __forceinline__ void build_q(const StepArgs &a, int tid, QWork<GQA, N
   for (int i = 0; i < AW; ++i) gmax = fmaxf(gmax, w.red[i]);
   gmax *= sc;
   float kq = 1.f;  // keeps |q' * 16 * kq| <= 2^14 (fp16 operands)
-  while (gmax * 16.f * kq > 16384.f) kq *= 0.5f;
+  if constexpr (!F4)
+    while (gmax * 16.f * kq > 16384.f) kq *= 0.5f;
   // A operand values q' * w_c * kq as fp16 high part and low part x 2^11
   // (w_c, the weight that the K code expansion puts on channel c: INT2 4 or
   // 16, INT4 16 on every channel),
   // and their sums over each scale group by wave reductions: a wave covers
   // 64 consecutive channels of one head (uniform loop bounds)
+  if constexpr (F4)  // the A operand bytes are scattered into place below
+    for (int i = tid; i < 16 * R::NCH * 64; i += NT) frag_lds[R::FR_A * 64 + i] = 0u;
   for (int e0 = 0; e0 < GQA * D; e0 += NT) {
     const int e = e0 + tid;
     const bool in = e < GQA * D;
@@ -565,16 +628,24 @@ __device__ __forceinline__ void build_q(const StepArgs &a, int tid, QWork<GQA, N
     float vh = 0.f, vl = 0.f, vq = 0.f;
     if (in) {
       const float y = w.y[h][ch] * sc;
-      const float x = y * ((BITS == 2 && (ch & 3) < 2) ? 4.f : 16.f) * kq;
-      const _Float16 hi = _Float16(x), lo = _Float16((x - float(hi)) * 2048.f);
-      w.qa[0][h][ch] = hi;
-      w.qa[1][h][ch] = lo;
-      vh = float(hi);
-      vl = float(lo);
+      if constexpr (F4) {
+        vh = fabsf(y);  // the group's largest |y| sets its part scales
+      } else {
+        const float x = y * ((BITS == 2 && (ch & 3) < 2) ? 4.f : 16.f) * kq;
+        const _Float16 hi = _Float16(x), lo = _Float16((x - float(hi)) * 2048.f);
+        w.qa[0][h][ch] = hi;
+        w.qa[1][h][ch] = lo;
+        vh = float(hi);
+        vl = float(lo);
+      }
       vq = y * kq;
     }
-    vh = seg_sum<SEG>(vh, tid & 63);
-    vl = seg_sum<SEG>(vl, tid & 63);
+    if constexpr (F4) {
+      vh = seg_max<SEG>(vh, tid & 63);
+    } else {
+      vh = seg_sum<SEG>(vh, tid & 63);
+      vl = seg_sum<SEG>(vl, tid & 63);
+    }
     vq = seg_sum<SEG>(vq, tid & 63);
     if (in && ch % SEG == 0) {
       w.gpart[0][h][ch / SEG] = vh;
@@ -588,9 +659,67 @@ __device__ __forceinline__ void build_q(const StepArgs &a, int tid, QWork<GQA, N
     for (int k = 0; k < G / SEG; ++k) sum += w.gpart[which][h][g * (G / SEG) + k];
     return sum;
   };
+  // F4: the exponent E of the largest |y| of (head, group) (y < 2^(E+1)),
+  // and every y's four fp8 part bytes, into the fp16 staging area
+  auto f4_exp = [&](int h, int g, bool &live) {
+    float mx = 0.f;
+    for (int k = 0; k < G / SEG; ++k) mx = fmaxf(mx, w.gpart[0][h][g * (G / SEG) + k]);
+    const int E = int((__float_as_uint(mx) >> 23) & 255u) - 127;
+    live = E > -90;  // zero (or negligible) groups keep zero parts
+    return E;
+  };
+  if constexpr (F4) {
+    // each y's four part bytes straight to their A operand bytes: pair P of
+    // chain ch (row 4 (P / 2) + part of product P % 2), and the lane group
+    // and byte whose fp8 slot meets the fp4 nibble of channel c
+    uint8_t *fb = reinterpret_cast<uint8_t *>(frag_lds);
+    for (int e = tid; e < GQA * D; e += NT) {
+      const int h = e / D, c = e % D, g = c / G;
+      bool live;
+      const int E = f4_exp(h, g, live);
+      if (!live) continue;
+      const uint32_t parts = fp8_parts(w.y[h][c] * sc, E);
+      const int P = NG == 1 ? h % R::HC : 2 * (h % R::HC) + g, ch = h / R::HC;
+      const int qr = P >> 1, j = P & 1;
+      const int pos = f4_code_bit(c), kk = c >> 5;
+      const int sB = 8 * (2 * (kk >> 1) + ((pos >> 1) & 1)) + (pos >> 2);
+      const int K = 32 * ((c & 31) >> 3) + sB;
+      const int gA = (K & 63) >> 4, sA = (K & 15) + (K >= 64 ? 16 : 0);
+      const int dw = R::FR_A + 16 * ch + 8 * j + (sA >> 2);
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) fb[4 * (dw * 64 + 16 * gA + 4 * qr + pp) + (sA & 3)] = uint8_t(parts >> (8 * pp));
+    }
+  }
   for (int idx = tid; idx < R::FR_DW * 64; idx += NT) {
     const int d = idx / 64, lane = idx % 64, r = lane & 15, qd = lane >> 4;
     uint32_t fw;
+    if constexpr (F4) {
+      // (product j of chain ch, row r = 4 qr + part): pair 2 qr + j
+      const int qr = r >> 2, part = r & 3;
+      if (d < R::FR_INIT) {
+        continue;  // the A operand, scattered above
+      } else if (d < R::FR_Q) {
+        // dword 0 of each chain: byte j = the E8M0 scale 2^(E - 7 - 4 part)
+        // of this lane's row in product j
+        const int ch = (d - R::FR_INIT) / 4, i = (d - R::FR_INIT) % 4;
+        fw = 0u;
+        if (i == 0)
+          for (int j = 0; j < 2; ++j) {
+            const int h = R::HC * ch + R::pair_head(qr, j), g = R::pair_group(qr, j);
+            bool live = false;
+            const int E = h < GQA ? f4_exp(h, g, live) : 0;
+            fw |= uint32_t(live ? 127 + E - 7 - 4 * part : 127) << (8 * j);
+          }
+      } else if (d < R::FR_INVKQ) {
+        const int ch = (d - R::FR_Q) / 2, k = (d - R::FR_Q) % 2;
+        const int h = R::HC * ch + R::pair_head(qd, k), g = R::pair_group(qd, k);
+        fw = __float_as_uint(h < GQA ? gsum(2, h, g) : 0.f);
+      } else {
+        fw = __float_as_uint(1.f);
+      }
+      frag_lds[idx] = fw;
+      continue;
+    }
     if (d < R::FR_INIT) {
       // A operand: row r of chain ch, k-block kb, dword v (channels c0, c0+1)
       const int ch = d / 16, kb = (d % 16) / 4, v = d % 4;
@@ -805,7 +934,7 @@ __device__ inline uint32_t halves(uint32_t a, uint32_t b, uint32_t sel) { return
 // forms B_g = fp16(pw s_tg) for each scale group g; acc[r] += Vexp_r B_g(r)
 // with Vexp = 1 + code/w_t, and cacc[g] += 1 B_g, whose rows all equal the
 // column sums of B_g: acc - cacc is then exactly sum_t B code / w_t.
-template <int GQA, int NG, int BITS, int DP, class Prep>
+template <int GQA, int NG, int BITS, int DP, bool F4, class Prep>
 __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, int j1, int wave, int lane,
                              int pid_pre, Prep &&prep, const uint32_t *frag_lds, uint8_t *ring, float *zs,
                              float *o_lds, float *m_lds, float *l_lds) {
@@ -931,23 +1060,45 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
     const bool tok_ok = !PARTIAL || t < nvalid;
     // ---- scores (kq units)
     f16x8 kx[4];
+    i32x8 k4;  // F4: the codes as fp4 c/2, nibbles of the spread dwords
+    if constexpr (F4) {
+      const uint32_t M = 0x33333333u;
+      k4 = i32x8{int(kc[0] & M), int((kc[0] >> 2) & M), int(kc[1] & M), int((kc[1] >> 2) & M), 0, 0, 0, 0};
+    } else {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      if constexpr (BITS == 2)
-        kx[kb] = ex.k(kc[0], kc[1], kb);
-      else
-        kx[kb] = ex4.k(kc[kb]);
+      for (int kb = 0; kb < 4; ++kb) {
+        if constexpr (BITS == 2)
+          kx[kb] = ex.k(kc[0], kc[1], kb);
+        else
+          kx[kb] = ex4.k(kc[kb]);
+      }
     }
     float S[NCH][SPL];
     bool up = false;
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
-      f32x4 d = dinit[ch];
+      float d0, d1;
+      if constexpr (F4) {
+        // the four parts of the lane's pairs (2qd, 2qd + 1), each product's
+        // rows scaled by their own power of two (byte j of the chain's scale
+        // dword); the fp4 operand scaled by 2 (c/2 -> c)
+        const int scl = int(__float_as_uint(dinit[ch][0]));
+        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 e0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            f4_operand(aq[ch][0], aq[ch][1]), k4, z4, 0, 4, 0, scl, 0, 128);
+        const f32x4 e1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            f4_operand(aq[ch][2], aq[ch][3]), k4, z4, 0, 4, 1, scl, 0, 128);
+        d0 = (e0[0] + e0[1]) + (e0[2] + e0[3]);
+        d1 = (e1[0] + e1[1]) + (e1[2] + e1[3]);
+      } else {
+        f32x4 d = dinit[ch];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) d = mfma_k(aq[ch][kb], kx[kb], d);
-      // s_g (d_hi + 2^-11 d_lo) + z_g qz_g per pair, as mixed-precision
-      // FMAs on the packed meta (fp16 operands taken as they are)
-      const float d0 = fmaf(d[1], 0x1p-11f, d[0]), d1 = fmaf(d[3], 0x1p-11f, d[2]);
+        for (int kb = 0; kb < 4; ++kb) d = mfma_k(aq[ch][kb], kx[kb], d);
+        // s_g (d_hi + 2^-11 d_lo) + z_g qz_g per pair, as mixed-precision
+        // FMAs on the packed meta (fp16 operands taken as they are)
+        d0 = fmaf(d[1], 0x1p-11f, d[0]);
+        d1 = fmaf(d[3], 0x1p-11f, d[2]);
+      }
       if constexpr (NG == 1) {
         S[ch][0] = fmaf(float(km0.x), d0, fmaf(float(km0.y), qz[ch][0], 0.f));
         S[ch][1] = fmaf(float(km1.x), d1, fmaf(float(km1.y), qz[ch][1], 0.f));
@@ -1515,9 +1666,10 @@ attend_kernel(StepArgs a) {
     // append: the raw workgroup attends it
     const int nh = n_hist_tokens(L) - (append && L0 >= N_RAW ? 1 : 0);
     const int j1 = min((nh + PAGE - 1) / PAGE, j0 + a.pages_per_split);
-    auto prep = [&] { build_q<GQA, NG, BITS>(a, tid, work.q, frag_lds, ql); };
+    constexpr bool F4 = f4_scores<BITS, NG, FUSED>();
+    auto prep = [&] { build_q<GQA, NG, BITS, F4>(a, tid, work.q, frag_lds, ql); };
     // every wave of the workgroup calls this (it holds workgroup barriers)
-    history_wave<GQA, NG, BITS, DPK>(a, b, hk, nh, j0, j1, wave, lane, pid_pre, prep, frag_lds, wave_lds + wave * WREG,
+    history_wave<GQA, NG, BITS, DPK, F4>(a, b, hk, nh, j0, j1, wave, lane, pid_pre, prep, frag_lds, wave_lds + wave * WREG,
                           zs_lds + wave * GQA * NG, o_w, m_lds + wave * GQA, l_lds + wave * GQA);
   }
   const int64_t head_stride = int64_t(a.part_slots) * PART_STRIDE;

@@ -505,6 +505,37 @@ def test_decode_more_than_64_pages_per_wave(oscar):
     assert_decode_close(got[pick], expect, "int2 long split")
 
 
+@pytest.mark.parametrize("hq,hkv,G", [(32, 8, 64), (64, 8, 128), (16, 8, 64), (8, 8, 128)])
+def test_decode_several_rounds_fp4_scores(oscar, hq, hkv, G):
+    # 24 requests x 8 KV heads = 192 (request, head) units, more than one
+    # round holds: the several-round plan, whose INT2 scores (one or two
+    # scale groups per head) run on the fp8 x fp4 matrix-core products.
+    # Requests read request 0's pages as prefixes of ragged lengths (partial
+    # last pages, one or no history page), each with its own query.
+    L, B = 2500, 24
+    sc = Scenario(1700 + hq + G, hq, hkv, G, [L])
+    ref = sc.oracle_cache()
+    hist_pt, bf16_pt, q = _shared_page_batch(sc, ref, B)
+    rng = np.random.default_rng(1701)
+    lens = np.concatenate([[L, 2049, 160, 161, 144, 150, 1000], rng.integers(145, L, B - 7)]).astype(np.int32)
+    dev = torch.device("cuda:0")
+    cache = oscar.LayerCache(sc.hkv, sc.G, sc.n_hist_pages, sc.n_bf16_pages, torch.from_numpy(hist_pt),
+                             torch.from_numpy(bf16_pt), device=dev)
+    cache.hist.copy_(torch.from_numpy(ref.hist))
+    cache.bf16.view(torch.int16).copy_(torch.from_numpy(ref.bf16.view(np.int16)))
+    rk, rv = gpu_rotations(oscar, sc)
+    out = oscar.decode_attn(cache, rk, rv, to_dev_bf16(q), torch.from_numpy(lens).to(dev), L, SCALE)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) == 0
+    got = out.cpu().numpy()
+    pick = [0, 1, 2, 3, 5, 6, 11, 23]
+    ref.hist_pt = hist_pt[:len(pick)]
+    ref.bf16_pt = bf16_pt[:len(pick)]
+    expect = o.decode_attn(ref, sc.R_K, sc.R_V, q[pick], [int(lens[b]) for b in pick], SCALE)
+    mx, rel = assert_decode_close(got[pick], expect, f"several rounds {hq}/{hkv} G {G}")
+    print(f"several rounds {hq}/{hkv} G={G}: max abs {mx:.2e} rel {rel:.2e}")
+
+
 def test_bf16_decode_more_than_64_pages_per_wave(oscar):
     # 40 requests x 8 KV heads = 320 units: one split per unit, 563 / 8 > 64
     # pages per wave; all requests read the same pages
