@@ -811,7 +811,7 @@ __device__ inline uint32_t lds_addr(const void *p) {
 // one asm block that also waits for them: loads the compiler sees would each
 // get a wait for every LDS copy in flight, the prefetched pages included.
 // kc/vc: K/V code dwords of the lane; km/vm: K/V meta of (token, pair 0/1).
-template <int VCODE, int KMETA, int VMETA, int POFF>
+template <int VCODE, int KMETA, int VMETA, int POFF, int SOFF = 0>
 struct RingRead {
   u32x2 kc, vc;
   uint32_t km0, km1, vm0, vm1;
@@ -819,19 +819,19 @@ struct RingRead {
   __device__ void load(uint32_t a_code, uint32_t a_meta) {
     if constexpr (NG == 1) {
       asm volatile(
-          "ds_read_b64 %0, %4\n\t"
+          "ds_read_b64 %0, %4 offset:%9\n\t"
           "ds_read_b64 %1, %4 offset:%6\n\t"
           "ds_read_b32 %2, %5 offset:%7\n\t"
           "ds_read_b32 %3, %5 offset:%8\n\t"
           "s_waitcnt lgkmcnt(0)"
           : "=&v"(kc), "=&v"(vc), "=&v"(km0), "=&v"(vm0)
-          : "v"(a_code), "v"(a_meta), "n"(VCODE), "n"(KMETA), "n"(VMETA)
+          : "v"(a_code), "v"(a_meta), "n"(VCODE + SOFF), "n"(KMETA + SOFF), "n"(VMETA + SOFF), "n"(SOFF)
           : "memory");
       km1 = km0;
       vm1 = vm0;
     } else {
       asm volatile(
-          "ds_read_b64 %0, %6\n\t"
+          "ds_read_b64 %0, %6 offset:%13\n\t"
           "ds_read_b64 %1, %6 offset:%8\n\t"
           "ds_read_b32 %2, %7 offset:%9\n\t"
           "ds_read_b32 %3, %7 offset:%10\n\t"
@@ -839,15 +839,15 @@ struct RingRead {
           "ds_read_b32 %5, %7 offset:%12\n\t"
           "s_waitcnt lgkmcnt(0)"
           : "=&v"(kc), "=&v"(vc), "=&v"(km0), "=&v"(km1), "=&v"(vm0), "=&v"(vm1)
-          : "v"(a_code), "v"(a_meta), "n"(VCODE), "n"(KMETA), "n"(KMETA + POFF), "n"(VMETA),
-            "n"(VMETA + POFF)
+          : "v"(a_code), "v"(a_meta), "n"(VCODE + SOFF), "n"(KMETA + SOFF), "n"(KMETA + POFF + SOFF),
+            "n"(VMETA + SOFF), "n"(VMETA + POFF + SOFF), "n"(SOFF)
           : "memory");
     }
   }
 };
 
 // The same for INT4 pages: 16 code bytes per lane and tensor.
-template <int VCODE, int KMETA, int VMETA, int POFF>
+template <int VCODE, int KMETA, int VMETA, int POFF, int SOFF = 0>
 struct RingRead4 {
   u32x4 kc, vc;
   uint32_t km0, km1, vm0, vm1;
@@ -855,19 +855,19 @@ struct RingRead4 {
   __device__ void load(uint32_t a_code, uint32_t a_meta) {
     if constexpr (NG == 1) {
       asm volatile(
-          "ds_read_b128 %0, %4\n\t"
+          "ds_read_b128 %0, %4 offset:%9\n\t"
           "ds_read_b128 %1, %4 offset:%6\n\t"
           "ds_read_b32 %2, %5 offset:%7\n\t"
           "ds_read_b32 %3, %5 offset:%8\n\t"
           "s_waitcnt lgkmcnt(0)"
           : "=&v"(kc), "=&v"(vc), "=&v"(km0), "=&v"(vm0)
-          : "v"(a_code), "v"(a_meta), "n"(VCODE), "n"(KMETA), "n"(VMETA)
+          : "v"(a_code), "v"(a_meta), "n"(VCODE + SOFF), "n"(KMETA + SOFF), "n"(VMETA + SOFF), "n"(SOFF)
           : "memory");
       km1 = km0;
       vm1 = vm0;
     } else {
       asm volatile(
-          "ds_read_b128 %0, %6\n\t"
+          "ds_read_b128 %0, %6 offset:%13\n\t"
           "ds_read_b128 %1, %6 offset:%8\n\t"
           "ds_read_b32 %2, %7 offset:%9\n\t"
           "ds_read_b32 %3, %7 offset:%10\n\t"
@@ -875,8 +875,8 @@ struct RingRead4 {
           "ds_read_b32 %5, %7 offset:%12\n\t"
           "s_waitcnt lgkmcnt(0)"
           : "=&v"(kc), "=&v"(vc), "=&v"(km0), "=&v"(km1), "=&v"(vm0), "=&v"(vm1)
-          : "v"(a_code), "v"(a_meta), "n"(VCODE), "n"(KMETA), "n"(KMETA + POFF), "n"(VMETA),
-            "n"(VMETA + POFF)
+          : "v"(a_code), "v"(a_meta), "n"(VCODE + SOFF), "n"(KMETA + SOFF), "n"(KMETA + POFF + SOFF),
+            "n"(VMETA + SOFF), "n"(VMETA + POFF + SOFF), "n"(SOFF)
           : "memory");
     }
   }
@@ -1047,11 +1047,14 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
   };
 
   // one page from the ring; PARTIAL: rows >= nvalid are absent (any bits)
-  auto page = [&](const uint8_t *src, int nvalid, auto partial_tag) {
+  // soff_tag: a ring slot's byte offset known at compile time (the unrolled
+  // loop: immediate offsets of the ring reads), else 0 with src at the slot
+  auto page = [&](const uint8_t *src, int nvalid, auto partial_tag, auto soff_tag) {
     constexpr bool PARTIAL = decltype(partial_tag)::value;
+    constexpr int SOFF = decltype(soff_tag)::value;
     const uint32_t base = lds_addr(src);
-    typedef typename std::conditional<BITS == 2, RingRead<vcode, kmeta, vmeta, POFF>,
-                                      RingRead4<vcode, kmeta, vmeta, POFF>>::type Rd;
+    typedef typename std::conditional<BITS == 2, RingRead<vcode, kmeta, vmeta, POFF, SOFF>,
+                                      RingRead4<vcode, kmeta, vmeta, POFF, SOFF>>::type Rd;
     Rd rd;
     rd.template load<NG>(base + (BITS == 2 ? 8 : 16) * lane, base + moff);
     const auto kc = rd.kc, vc = rd.vc;
@@ -1232,7 +1235,7 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
     if (!((okv >> sl) & 1u)) {
       if (lane == 0) flag_status(c.status, OSCAR_STATUS_BAD_PAGE);
     } else {
-      page(ring + sl * SB, nh - PAGE * (j0 + wave + AW * i), partial_tag);
+      page(ring + sl * SB, nh - PAGE * (j0 + wave + AW * i), partial_tag, std::integral_constant<int, 0>{});
     }
   };
 
@@ -1249,7 +1252,14 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
   auto step_fast = [&](int i, auto partial_tag) {
     if (i + DP - 1 < npw) issue_fast(i + DP - 1, (i + DP - 1) % DP);
     wait_pages<IPP, DP - 1>(min(DP - 1, npw - 1 - i));
-    page(ring + (i % DP) * SB, nh - PAGE * (j0 + wave + AW * i), partial_tag);
+    page(ring + (i % DP) * SB, nh - PAGE * (j0 + wave + AW * i), partial_tag, std::integral_constant<int, 0>{});
+  };
+  // page i known to sit in ring slot S (i % DP == S)
+  auto step_slot = [&](int i, auto slot_tag) {
+    constexpr int S = decltype(slot_tag)::value;
+    if (i + DP - 1 < npw) issue_fast(i + DP - 1, (S + DP - 1) % DP);
+    wait_pages<IPP, DP - 1>(min(DP - 1, npw - 1 - i));
+    page(ring, nh - PAGE * (j0 + wave + AW * i), std::false_type{}, std::integral_constant<int, S * SB>{});
   };
 
   // the page ids (loaded by the caller, with the loads of the q fragment
@@ -1301,7 +1311,23 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
     const int nfull = npw - (last_partial ? 1 : 0);
     const bool fast = npw <= 64 && __ballot(lane < npw && !(my_pid >= 0 && my_pid < c.n_hist_pages)) == 0;
     if (fast) {
-      for (int i = 0; i < nfull; ++i) step_fast(i, std::false_type{});
+      // long page runs (the fp4-score instances of the several-round plan
+      // with 8 or more score rows per lane group): DP pages per trip, each
+      // ring slot's reads at immediate offsets (a batch-1 round's 8 pages
+      // per wave gain nothing from the longer code; smaller instances would
+      // spill)
+      constexpr bool UNR = F4 && GQA * NG >= 8;
+      static_assert(DP == 3 || DP == 4, "ring depth");
+      int i = 0;
+      if constexpr (UNR) {
+        for (; i + DP <= nfull; i += DP) {
+          step_slot(i, std::integral_constant<int, 0>{});
+          step_slot(i + 1, std::integral_constant<int, 1>{});
+          step_slot(i + 2, std::integral_constant<int, 2>{});
+          if constexpr (DP == 4) step_slot(i + 3, std::integral_constant<int, 3>{});
+        }
+      }
+      for (; i < nfull; ++i) step_fast(i, std::false_type{});
       if (last_partial) step_fast(npw - 1, std::true_type{});
     } else {
       for (int i = 0; i < nfull; ++i) step(i, std::false_type{});
