@@ -107,16 +107,17 @@ struct Rows {
 template <int BITS, int NG, bool FUSED>
 constexpr bool f4_scores() { return BITS == 2 && NG <= 2 && !FUSED; }
 
-// Bit position of the K code of channel c in its code dword (the slot
-// tables: u = 4 (k & 1) + (c & 7) / 2 for k = c / 32, low slot for even c,
-// high slot for odd), as shifts of two packed tables.  Spread to nibbles
-// (the dword masked with 0x33333333 after a right shift by 0 or 2), it
-// lands in nibble pos / 4 of spread register 2 (k / 2) + (pos / 2) % 2.
-__device__ inline int f4_code_bit(int c) {
-  constexpr uint64_t LO = 8ull | 6ull << 5 | 12ull << 10 | 10ull << 15 | 4ull << 20 | 2ull << 25 | 16ull << 30 | 14ull << 35;
-  constexpr uint64_t HI = 24ull | 22ull << 5 | 28ull << 10 | 26ull << 15 | 20ull << 20 | 18ull << 25 | 0ull << 30 | 30ull << 35;
-  const int u = 4 * ((c >> 5) & 1) + ((c & 7) >> 1);
-  return int((((c & 1) ? HI : LO) >> (5 * u)) & 31u);
+// Channel of the K code in nibble s of fp4 operand lane group gB, once the
+// lane's two code dwords are spread to nibbles (register v = s / 8 is dword
+// v / 2 masked with 0x33333333 after a right shift by 2 (v % 2)): the code
+// at bit pos of dword d is slot u of the code slot tables (low slot for
+// even channels, high for odd), channel 32 (2d + u / 4) + 8 gB + 2 (u % 4)
+// (+ 1 when high).
+__device__ inline int f4_channel(int gB, int s) {
+  const int v = s >> 3, pos = 4 * (s & 7) + 2 * (v & 1), hp = pos >> 1;
+  const int u = int((0xE9832Eu >> (3 * (hp & 7))) & 7u);  // slots 6 5 4 1 0 3 2 7 at bits 0 2 4 .. 14 (mod 16)
+  const int par = (hp >= 8) != ((hp & 7) == 0);
+  return 32 * (2 * (v >> 1) + (u >> 2)) + 8 * gB + 2 * (u & 3) + par;
 }
 
 // 2^n for -126 <= n <= 127, exactly
@@ -619,8 +620,8 @@ __device__ __forceinline__ void build_q(const StepArgs &a, int tid, QWork<GQA, N
   // 16, INT4 16 on every channel),
   // and their sums over each scale group by wave reductions: a wave covers
   // 64 consecutive channels of one head (uniform loop bounds)
-  if constexpr (F4)  // the A operand bytes are scattered into place below
-    for (int i = tid; i < 16 * R::NCH * 64; i += NT) frag_lds[R::FR_A * 64 + i] = 0u;
+  if constexpr (F4)  // the A operand and scale bytes are scattered into place below
+    for (int i = tid; i < R::FR_Q * 64; i += NT) frag_lds[R::FR_A * 64 + i] = 0u;
   for (int e0 = 0; e0 < GQA * D; e0 += NT) {
     const int e = e0 + tid;
     const bool in = e < GQA * D;
@@ -628,9 +629,7 @@ __device__ __forceinline__ void build_q(const StepArgs &a, int tid, QWork<GQA, N
     float vh = 0.f, vl = 0.f, vq = 0.f;
     if (in) {
       const float y = w.y[h][ch] * sc;
-      if constexpr (F4) {
-        vh = fabsf(y);  // the group's largest |y| sets its part scales
-      } else {
+      if constexpr (!F4) {
         const float x = y * ((BITS == 2 && (ch & 3) < 2) ? 4.f : 16.f) * kq;
         const _Float16 hi = _Float16(x), lo = _Float16((x - float(hi)) * 2048.f);
         w.qa[0][h][ch] = hi;
@@ -640,9 +639,7 @@ __device__ __forceinline__ void build_q(const StepArgs &a, int tid, QWork<GQA, N
       }
       vq = y * kq;
     }
-    if constexpr (F4) {
-      vh = seg_max<SEG>(vh, tid & 63);
-    } else {
+    if constexpr (!F4) {
       vh = seg_sum<SEG>(vh, tid & 63);
       vl = seg_sum<SEG>(vl, tid & 63);
     }
@@ -659,35 +656,40 @@ __device__ __forceinline__ void build_q(const StepArgs &a, int tid, QWork<GQA, N
     for (int k = 0; k < G / SEG; ++k) sum += w.gpart[which][h][g * (G / SEG) + k];
     return sum;
   };
-  // F4: the exponent E of the largest |y| of (head, group) (y < 2^(E+1)),
-  // and every y's four fp8 part bytes, into the fp16 staging area
-  auto f4_exp = [&](int h, int g, bool &live) {
-    float mx = 0.f;
-    for (int k = 0; k < G / SEG; ++k) mx = fmaxf(mx, w.gpart[0][h][g * (G / SEG) + k]);
-    const int E = int((__float_as_uint(mx) >> 23) & 255u) - 127;
-    live = E > -90;  // zero (or negligible) groups keep zero parts
-    return E;
-  };
   if constexpr (F4) {
-    // each y's four part bytes straight to their A operand bytes: pair P of
-    // chain ch (row 4 (P / 2) + part of product P % 2), and the lane group
-    // and byte whose fp8 slot meets the fp4 nibble of channel c
+    // Thread (h, b, s) takes K = 32 b + s: the channel c whose code is
+    // nibble s of fp4 lane group b, and the fp8 slot of that K.  A row's
+    // E8M0 scale from lane group b applies to K block b (K = 32 b .. 32 b +
+    // 31, read off the hardware), so each block of each row gets its own
+    // exponent E (of its group's largest |y| in the block; the block's 32
+    // K are 32 consecutive lanes here): its four fp8 part bytes and the
+    // block's scales go straight into the fragment.
     uint8_t *fb = reinterpret_cast<uint8_t *>(frag_lds);
     for (int e = tid; e < GQA * D; e += NT) {
-      const int h = e / D, c = e % D, g = c / G;
-      bool live;
-      const int E = f4_exp(h, g, live);
-      if (!live) continue;
-      const uint32_t parts = fp8_parts(w.y[h][c] * sc, E);
-      const int P = NG == 1 ? h % R::HC : 2 * (h % R::HC) + g, ch = h / R::HC;
-      const int qr = P >> 1, j = P & 1;
-      const int pos = f4_code_bit(c), kk = c >> 5;
-      const int sB = 8 * (2 * (kk >> 1) + ((pos >> 1) & 1)) + (pos >> 2);
-      const int K = 32 * ((c & 31) >> 3) + sB;
-      const int gA = (K & 63) >> 4, sA = (K & 15) + (K >= 64 ? 16 : 0);
-      const int dw = R::FR_A + 16 * ch + 8 * j + (sA >> 2);
+      const int h = e / D, K = e % D, b = K >> 5;
+      const int c = f4_channel(b, K & 31), g = c / G;
+      const float y = w.y[h][c] * sc;
+      int E = 0;
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) fb[4 * (dw * 64 + 16 * gA + 4 * qr + pp) + (sA & 3)] = uint8_t(parts >> (8 * pp));
+      for (int gg = 0; gg < NG; ++gg) {
+        const float mx = seg_max<32>(g == gg ? fabsf(y) : 0.f, tid & 63);
+        const int Eg = int((__float_as_uint(mx) >> 23) & 255u) - 127;  // mx < 2^(Eg+1)
+        if (gg == g) E = Eg;
+        // pair P of chain ch: row 4 (P / 2) + part of product P % 2
+        const int P = NG == 1 ? h % R::HC : 2 * (h % R::HC) + gg, ch = h / R::HC;
+        if ((K & 31) == 0 && Eg > -90)
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp)
+            fb[4 * ((R::FR_INIT + 4 * ch) * 64 + 16 * b + 4 * (P >> 1) + pp) + (P & 1)] = uint8_t(127 + Eg - 7 - 4 * pp);
+      }
+      if (E <= -90) continue;  // zero (or negligible) block: zero parts
+      const uint32_t parts = fp8_parts(y, E);
+      const int P = NG == 1 ? h % R::HC : 2 * (h % R::HC) + g, ch = h / R::HC;
+      // fp8 slot of K: lane group gA, byte sA (K = 16 gA + sA, or 64 + 16 gA + sA - 16)
+      const int gA = (K & 63) >> 4, sA = (K & 15) + (K >= 64 ? 16 : 0);
+      const int dw = R::FR_A + 16 * ch + 8 * (P & 1) + (sA >> 2);
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) fb[4 * (dw * 64 + 16 * gA + 4 * (P >> 1) + pp) + (sA & 3)] = uint8_t(parts >> (8 * pp));
     }
   }
   for (int idx = tid; idx < R::FR_DW * 64; idx += NT) {
@@ -699,17 +701,7 @@ __device__ __forceinline__ void build_q(const StepArgs &a, int tid, QWork<GQA, N
       if (d < R::FR_INIT) {
         continue;  // the A operand, scattered above
       } else if (d < R::FR_Q) {
-        // dword 0 of each chain: byte j = the E8M0 scale 2^(E - 7 - 4 part)
-        // of this lane's row in product j
-        const int ch = (d - R::FR_INIT) / 4, i = (d - R::FR_INIT) % 4;
-        fw = 0u;
-        if (i == 0)
-          for (int j = 0; j < 2; ++j) {
-            const int h = R::HC * ch + R::pair_head(qr, j), g = R::pair_group(qr, j);
-            bool live = false;
-            const int E = h < GQA ? f4_exp(h, g, live) : 0;
-            fw |= uint32_t(live ? 127 + E - 7 - 4 * part : 127) << (8 * j);
-          }
+        continue;  // the E8M0 scales, written above
       } else if (d < R::FR_INVKQ) {
         const int ch = (d - R::FR_Q) / 2, k = (d - R::FR_Q) % 2;
         const int h = R::HC * ch + R::pair_head(qd, k), g = R::pair_group(qd, k);

@@ -536,6 +536,41 @@ def test_decode_several_rounds_fp4_scores(oscar, hq, hkv, G):
     print(f"several rounds {hq}/{hkv} G={G}: max abs {mx:.2e} rel {rel:.2e}")
 
 
+@pytest.mark.parametrize("q_mult,sm_scale", [(400.0, 1.0), (1e-3, SCALE), (0.0, SCALE)])
+def test_decode_several_rounds_fp4_scores_query_norms(oscar, q_mult, sm_scale):
+    # the fp8 parts of q R_K take their exponents from each (head, group)'s
+    # largest value: scores far beyond the fp16 range (x400 at sm_scale 1),
+    # tiny queries, and every third query head all zero (no parts: uniform
+    # attention) beside normal ones
+    L, B = 1200, 24
+    sc = Scenario(1800, 32, 8, 64, [L])
+    ref = sc.oracle_cache()
+    hist_pt, bf16_pt, q = _shared_page_batch(sc, ref, B)
+    qf = synth.bf16_to_f64(q) * (q_mult if q_mult else 1.0)
+    if q_mult == 0.0:
+        qf[:, ::3] = 0.0  # every third query head all zero
+    q = synth.bf16_bits(qf.astype(np.float32))
+    lens = np.full(B, L, dtype=np.int32)
+    lens[1::2] = 700
+    dev = torch.device("cuda:0")
+    cache = oscar.LayerCache(sc.hkv, sc.G, sc.n_hist_pages, sc.n_bf16_pages, torch.from_numpy(hist_pt),
+                             torch.from_numpy(bf16_pt), device=dev)
+    cache.hist.copy_(torch.from_numpy(ref.hist))
+    cache.bf16.view(torch.int16).copy_(torch.from_numpy(ref.bf16.view(np.int16)))
+    rk, rv = gpu_rotations(oscar, sc)
+    out = oscar.decode_attn(cache, rk, rv, to_dev_bf16(q), torch.from_numpy(lens).to(dev), L, sm_scale)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) == 0
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    pick = [0, 1, 7, 22]
+    ref.hist_pt = hist_pt[:len(pick)]
+    ref.bf16_pt = bf16_pt[:len(pick)]
+    expect = o.decode_attn(ref, sc.R_K, sc.R_V, q[pick], [int(lens[b]) for b in pick], sm_scale)
+    mx, rel = assert_decode_close(got[pick], expect, f"several rounds q x{q_mult} sm_scale {sm_scale}")
+    print(f"several rounds q x{q_mult}: max abs {mx:.2e} rel {rel:.2e}")
+
+
 def test_bf16_decode_more_than_64_pages_per_wave(oscar):
     # 40 requests x 8 KV heads = 320 units: one split per unit, 563 / 8 > 64
     # pages per wave; all requests read the same pages
