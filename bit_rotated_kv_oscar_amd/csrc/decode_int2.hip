@@ -775,17 +775,18 @@ __device__ inline void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// wait until at most `pages` page copies (IPP instructions each) are pending
-template <int IPP, int P>
+// wait until at most `pages` page copies (IPP instructions each) are pending,
+// with EXTRA younger loads issued after the last page copy
+template <int IPP, int P, int EXTRA = 0>
 __device__ inline void wait_pages(int pages) {
-  static_assert(IPP * P <= 63, "vmcnt range");
+  static_assert(IPP * P + EXTRA <= 63, "vmcnt range");
   if constexpr (P == 0) {
-    wait_vmem<0>();
+    wait_vmem<EXTRA>();
   } else {
     if (pages >= P)
-      wait_vmem<IPP * P>();
+      wait_vmem<IPP * P + EXTRA>();
     else
-      wait_pages<IPP, P - 1>(pages);
+      wait_pages<IPP, P - 1, EXTRA>(pages);
   }
 }
 
@@ -926,10 +927,14 @@ __device__ inline uint32_t halves(uint32_t a, uint32_t b, uint32_t sel) { return
 // forms B_g = fp16(pw s_tg) for each scale group g; acc[r] += Vexp_r B_g(r)
 // with Vexp = 1 + code/w_t, and cacc[g] += 1 B_g, whose rows all equal the
 // column sums of B_g: acc - cacc is then exactly sum_t B code / w_t.
-template <int GQA, int NG, int BITS, int DP, bool F4, class Prep>
-__device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, int j1, int wave, int lane,
-                             int pid_pre, Prep &&prep, const uint32_t *frag_lds, uint8_t *ring, float *zs,
-                             float *o_lds, float *m_lds, float *l_lds) {
+// LATE (N_LATE > 0): late() issues N_LATE loads into registers once the
+// wave has issued its last page copy (the fast page path); the waits of the
+// remaining pages count them.  Returns whether late() was called.
+template <int GQA, int NG, int BITS, int DP, bool F4, int N_LATE, class Prep, class Late>
+__device__ bool history_wave(const StepArgs &a, int b, int hk, int nh, int j0, int j1, int wave, int lane,
+                             int pid_pre, Prep &&prep, Late &&late, const uint32_t *frag_lds, uint8_t *ring,
+                             float *zs, float *o_lds, float *m_lds, float *l_lds) {
+  bool late_done = false;
   using R = Rows<GQA, NG>;
   constexpr int NCH = R::NCH, SPL = R::SPL, G = R::G, HC = R::HC;
   constexpr int SB = hist_block_bytes(G, BITS);
@@ -1319,8 +1324,23 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
           if constexpr (DP == 4) step_slot(i + 3, std::integral_constant<int, 3>{});
         }
       }
-      for (; i < nfull; ++i) step_fast(i, std::false_type{});
-      if (last_partial) step_fast(npw - 1, std::true_type{});
+      if constexpr (N_LATE > 0) {
+        // from the first page whose step issues no copy on, the late loads
+        // are in flight behind the last copies
+        const int i0 = max(0, npw - DP + 1);
+        for (; i < i0; ++i) step_fast(i, std::false_type{});
+        late();
+        late_done = true;
+        auto step_late = [&](int ii, auto partial_tag) {
+          wait_pages<IPP, DP - 1, N_LATE>(min(DP - 1, npw - 1 - ii));
+          page(ring + (ii % DP) * SB, nh - PAGE * (j0 + wave + AW * ii), partial_tag, std::integral_constant<int, 0>{});
+        };
+        for (; i < nfull; ++i) step_late(i, std::false_type{});
+        if (last_partial) step_late(npw - 1, std::true_type{});
+      } else {
+        for (; i < nfull; ++i) step_fast(i, std::false_type{});
+        if (last_partial) step_fast(npw - 1, std::true_type{});
+      }
     } else {
       for (int i = 0; i < nfull; ++i) step(i, std::false_type{});
       if (last_partial) step(npw - 1, std::true_type{});
@@ -1374,12 +1394,14 @@ __device__ void history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
         o_lds[t * D + 16 * r + 4 * qd + i] = (acc[r][i] - cacc[g][i] + zg) * a.pv_unscale;
     }
   }
+  return late_done;
 }
 
 // R_V rows of a workgroup thread for the way back to the plain basis: rows
 // cr + 64 m (m < 2), inputs 32 k + 4 qq .. + 3 (cr = tid / 8, qq = tid % 8);
 // eight lanes per row read 128 contiguous bytes.
 struct RvRows {
+  static constexpr int N_LOADS = 8;  // load instructions of load()
   f32x4 r[8];
   __device__ void load(const uint8_t *fv, int tid) {
     const float *Rc = reinterpret_cast<const float *>(fv + FORM_R) + (tid >> 3) * D + 4 * (tid & 7);
@@ -1571,12 +1593,14 @@ __global__ void __launch_bounds__(merge_threads<GQA>()) merge_kernel(StepArgs a)
 }
 
 // Waves per SIMD the register budget is set for: 4 (two workgroups per CU,
-// at most 128 registers) where the page loop fits, else whatever it needs.
-template <int GQA, int NG>
-constexpr int attend_waves() { return (GQA <= 4 && NG <= 2) ? 4 : 1; }
+// at most 128 registers) where the page loop fits, else whatever it needs;
+// the one-round plan runs one workgroup per CU (two waves per SIMD), and
+// its waves hold the R_V rows through their last pages.
+template <int GQA, int NG, bool FUSED>
+constexpr int attend_waves() { return (GQA <= 4 && NG <= 2) ? (FUSED ? 2 : 4) : 1; }
 
 template <int GQA, int NG, bool FUSED, int BITS, bool PH>
-__global__ void __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(attend_waves<GQA, NG>())))
+__global__ void __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(attend_waves<GQA, NG, FUSED>())))
 attend_kernel(StepArgs a) {
   // several rounds: the split index varies slowest, so every unit's first
   // splits are dispatched before any unit's (shorter) last one, and the
@@ -1636,6 +1660,8 @@ attend_kernel(StepArgs a) {
   float *l_lds = m_lds + AW * GQA;
   float *o_w = o_lds + wave * (WREG / 4);
   bool extra = false;  // the raw workgroup attends the token leaving the window
+  RvRows rv;             // history workgroups of the one-round plan: R_V rows
+  bool rv_loaded = false;
   if (split == 0) {
     AppendPlan ap{};
     if (append) ap = plan_append(a, L0, bpt_lane);
@@ -1686,9 +1712,18 @@ attend_kernel(StepArgs a) {
     const int j1 = min((nh + PAGE - 1) / PAGE, j0 + a.pages_per_split);
     constexpr bool F4 = f4_scores<BITS, NG, FUSED>();
     auto prep = [&] { build_q<GQA, NG, BITS, F4>(a, tid, work.q, frag_lds, ql); };
+    // one round: the R_V rows for the partial's way back are loaded behind
+    // the wave's last page copies, in flight during its last pages (not at
+    // GQA 8 with four scale groups, whose registers are full already)
+    auto late = [&] {
+      asm volatile("" ::: "memory");
+      rv.load(forms_v<PH>(a, hk), tid);
+      asm volatile("" ::: "memory");
+    };
     // every wave of the workgroup calls this (it holds workgroup barriers)
-    history_wave<GQA, NG, BITS, DPK, F4>(a, b, hk, nh, j0, j1, wave, lane, pid_pre, prep, frag_lds, wave_lds + wave * WREG,
-                          zs_lds + wave * GQA * NG, o_w, m_lds + wave * GQA, l_lds + wave * GQA);
+    rv_loaded = history_wave<GQA, NG, BITS, DPK, F4, (FUSED && GQA * NG <= 16) ? RvRows::N_LOADS : 0>(
+        a, b, hk, nh, j0, j1, wave, lane, pid_pre, prep, late, frag_lds, wave_lds + wave * WREG,
+        zs_lds + wave * GQA * NG, o_w, m_lds + wave * GQA, l_lds + wave * GQA);
   }
   const int64_t head_stride = int64_t(a.part_slots) * PART_STRIDE;
   float *part0 = a.parts + (int64_t(b) * a.n_q_heads + hk * GQA) * head_stride + split * PART_STRIDE;
@@ -1700,15 +1735,9 @@ attend_kernel(StepArgs a) {
     else
       combine_waves<GQA, AW>(o_lds, m_lds, l_lds, part0, head_stride, tid, WREG / 4);
   } else {
-    // R_V rows for the history partial's way back, in flight during the
-    // barrier (the page loop's registers are free)
-    RvRows rv;
-    {
-      // computed here, not hoisted above the page loop (register pressure)
-      int t = tid;
-      asm volatile("" : "+v"(t));
-      if (split > 0) rv.load(forms_v<PH>(a, hk), t);
-    }
+    // R_V rows for the history partial's way back, unless the page loop
+    // loaded them already (in flight during the barrier)
+    if (split > 0 && !rv_loaded) rv.load(forms_v<PH>(a, hk), tid);
     __syncthreads();
     if (split > 0)
       combine_rotate<GQA>(o_lds, m_lds, l_lds, part0, head_stride, tid, WREG / 4, rv, work.q.y);
