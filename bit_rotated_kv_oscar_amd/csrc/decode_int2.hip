@@ -101,11 +101,11 @@ struct Rows {
 // chain two products: product j row 4qd + p is part p of pair (2qd + j) of
 // that chain (head and group as above), so lane (t, qd) again holds the
 // whole score of its pairs for token t.
-// Used where each wave's pages run long (the several-round plan): the
-// fragment build costs about what the shorter page loop saves over the
-// eight pages per wave of a batch-1 round.
+// Both plans (with the one-round plan's two-wave register budget the
+// batch-1 kernel gains 2.5 % from it; FUSED is kept as a parameter for
+// the choice).
 template <int BITS, int NG, bool FUSED>
-constexpr bool f4_scores() { return BITS == 2 && NG <= 2 && !FUSED; }
+constexpr bool f4_scores() { return BITS == 2 && NG <= 2; }
 
 // Channel of the K code in nibble s of fp4 operand lane group gB, once the
 // lane's two code dwords are spread to nibbles (register v = s / 8 is dword
@@ -1308,11 +1308,9 @@ __device__ bool history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
     const int nfull = npw - (last_partial ? 1 : 0);
     const bool fast = npw <= 64 && __ballot(lane < npw && !(my_pid >= 0 && my_pid < c.n_hist_pages)) == 0;
     if (fast) {
-      // long page runs (the fp4-score instances of the several-round plan
-      // with 8 or more score rows per lane group): DP pages per trip, each
-      // ring slot's reads at immediate offsets (a batch-1 round's 8 pages
-      // per wave gain nothing from the longer code; smaller instances would
-      // spill)
+      // the fp4-score instances with 8 or more score rows per lane group:
+      // DP pages per trip, each ring slot's reads at immediate offsets
+      // (smaller instances would spill)
       constexpr bool UNR = F4 && GQA * NG >= 8;
       static_assert(DP == 3 || DP == 4, "ring depth");
       int i = 0;
