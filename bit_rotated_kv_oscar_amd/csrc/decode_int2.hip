@@ -930,7 +930,7 @@ __device__ inline uint32_t halves(uint32_t a, uint32_t b, uint32_t sel) { return
 // LATE (N_LATE > 0): late() issues N_LATE loads into registers once the
 // wave has issued its last page copy (the fast page path); the waits of the
 // remaining pages count them.  Returns whether late() was called.
-template <int GQA, int NG, int BITS, int DP, bool F4, int N_LATE, class Prep, class Late>
+template <int GQA, int NG, int BITS, int DP, bool F4, int N_LATE, int RP, class Prep, class Late>
 __device__ bool history_wave(const StepArgs &a, int b, int hk, int nh, int j0, int j1, int wave, int lane,
                              int pid_pre, Prep &&prep, Late &&late, const uint32_t *frag_lds, uint8_t *ring,
                              float *zs, float *o_lds, float *m_lds, float *l_lds) {
@@ -942,7 +942,7 @@ __device__ bool history_wave(const StepArgs &a, int b, int hk, int nh, int j0, i
   // a block is HB = 2 code areas' worth of bytes (1 or 2 KB) copied 1 KB
   // per instruction, then 128 NG bytes of tail: IPP copy instructions per page
   constexpr int HB = 2 * code_area_bytes(BITS), NHB = HB / 1024, IPP = NHB + 1;
-  constexpr int RPB = DP - 1 < 3 ? DP - 1 : 3;
+  constexpr int RPB = DP - 1 < RP ? DP - 1 : RP;  // pages loaded through registers
   const oscar_layer_cache &c = a.c;
   const int t = lane & 15, qd = lane >> 4;  // score side: token, lane group
   const int hp = t % GQA;                   // PV side: head of column n = l%16 (tq = qd)
@@ -1719,7 +1719,10 @@ attend_kernel(StepArgs a) {
       asm volatile("" ::: "memory");
     };
     // every wave of the workgroup calls this (it holds workgroup barriers)
-    rv_loaded = history_wave<GQA, NG, BITS, DPK, F4, (FUSED && GQA * NG <= 16) ? RvRows::N_LOADS : 0>(
+    // pages per wave loaded through registers before the q build: 3, or 2 in
+    // the one-round plan (its 64 KB of R_K per workgroup lands sooner; A/B:
+    // batch-1 step -0.6 %, batch 64 +1 % with 2)
+    rv_loaded = history_wave<GQA, NG, BITS, DPK, F4, (FUSED && GQA * NG <= 16) ? RvRows::N_LOADS : 0, FUSED ? 2 : 3>(
         a, b, hk, nh, j0, j1, wave, lane, pid_pre, prep, late, frag_lds, wave_lds + wave * WREG,
         zs_lds + wave * GQA * NG, o_w, m_lds + wave * GQA, l_lds + wave * GQA);
   }
