@@ -149,6 +149,35 @@ def test_extend_bad_page_and_length_are_flagged(oscar):
     assert_decode_close(s[cu[1]:], exp[cu[1]:], "extend request beside a bad length")
 
 
+@pytest.mark.parametrize("G", [64, 128])
+def test_extend_history_page_counts(oscar, G):
+    # histories of 1 to 7 full pages, with and without a partial last page,
+    # and a longer one: every phase of the history loop's page slots
+    prefix = [144 + 16 * k + r for k, r in [(1, 0), (2, 5), (3, 0), (4, 15), (5, 0), (6, 1), (7, 0), (13, 9)]]
+    chunk = [16, 3, 20, 1, 33, 16, 7, 25]
+    sc, ref, cache, rk, rv, q, kn, vn, cu = _setup(oscar, 2450 + G, 8, 2, G, prefix, chunk)
+    out = _run(oscar, cache, rk, rv, q, kn, vn, cu, prefix)
+    assert int(cache.status.item()) == 0
+    exp = o.extend_attn(ref, sc.R_K, sc.R_V, q, kn, vn, cu, prefix, SCALE)
+    assert_decode_close(out, exp, f"extend page counts G={G}")
+
+
+def test_extend_bad_page_in_each_slot(oscar):
+    # request r < 7 has a bad id at history page r of its 6 full pages and
+    # a partial seventh; request 7 is untouched and exact
+    prefix, chunk = [144 + 16 * 6 + 3] * 8, [5] * 8
+    sc, ref, cache, rk, rv, q, kn, vn, cu = _setup(oscar, 2470, 8, 2, 64, prefix, chunk)
+    pt = sc.hist_pt.copy()
+    for r in range(7):
+        pt[r, r] = sc.n_hist_pages + 1 + r
+    cache.hist_pt.copy_(torch.from_numpy(pt))
+    out = _run(oscar, cache, rk, rv, q, kn, vn, cu, prefix)
+    assert int(cache.status.item()) & oscar._lib.STATUS_BAD_PAGE
+    exp = o.extend_attn(ref, sc.R_K, sc.R_V, q, kn, vn, cu, prefix, SCALE)
+    assert np.all(np.isfinite(out))
+    assert_decode_close(out[cu[7]:], exp[cu[7]:], "extend request beside bad pages")
+
+
 def test_extend_bench_shape_sampled_rows(oscar):
     # the timed shape of the extend workload (one layer): Hq 32 / Hkv 8, G 64,
     # prefix 28672 + chunk 4096, in the launch the benchmark uses; rows at the
