@@ -510,6 +510,22 @@ def test_decode_several_rounds_fp4_scores(oscar, hq, hkv, G):
     # 24 requests x 8 KV heads = 192 (request, head) units, more than one
     # round holds: the several-round plan, whose INT2 scores (one or two
     # scale groups per head) run on the fp8 x fp4 matrix-core products.
+    _several_rounds_case(oscar, hq, hkv, G)
+
+
+def test_decode_gqa8_g32(oscar):
+    # GQA 8 with four scale groups per head: 32 (head, group) pairs per KV
+    # head, the widest score fragment (fp16 products; these instances keep
+    # part of their state in scratch), in one round and in several rounds
+    sc = Scenario(1750, 16, 2, 32, [300, 1500])
+    ref = sc.oracle_cache()
+    cache = gpu_cache(oscar, sc, hist=ref.hist, bf16=ref.bf16)
+    rk, rv = gpu_rotations(oscar, sc)
+    assert_decode_close(gpu_decode(oscar, sc, cache, rk, rv), sc.oracle_decode(ref), "16/2 G 32")
+    _several_rounds_case(oscar, 64, 8, 32)
+
+
+def _several_rounds_case(oscar, hq, hkv, G):
     # Requests read request 0's pages as prefixes of ragged lengths (partial
     # last pages, one or no history page), each with its own query.
     L, B = 2500, 24
